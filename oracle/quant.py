@@ -1,0 +1,57 @@
+"""Quantization and rounding steps of the method, emulated exactly in float32.
+
+Sources:
+* cpu-attn kernel card (phanerozoic/cpu-attn), section "Method": K and V are
+  quantized per token and per head with an absmax int8 rule at append time;
+  section "Requirements and limits": per-token per-head absmax only.
+* The same card's logit formula uses a quantized query (``q_i8``, ``q_scale``);
+  it does not say how q is quantized.  Reading taken: the same per-row absmax
+  rule, one scale per query head.
+* opencoti-llamafile sparse_attn.md, section "Method: Quest-style min/max block
+  bounds": the side cache stores kmin/kmax as f16.  When the pre-quantization
+  keys are float32 (int8 cache), the reading taken is: round kmin toward -inf
+  and kmax toward +inf so the stored envelope still contains every key.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+QMAX = 127  # symmetric int8 range [-127, 127]
+
+
+def quantize_rows(x: np.ndarray):
+    """Absmax int8 quantization of each row (last axis) of a float32 array.
+
+    For a row x: a = max_d |x_d| (exact); if a == 0 the scale is 0 and all
+    codes are 0; otherwise scale = fl32(a / 127) and
+    code_d = clamp(rint(fl32(x_d / scale)), -127, 127), rint rounding half to
+    even.  Returns (codes int8 [..., D], scales float32 [...]).
+    """
+    x = np.asarray(x, dtype=np.float32)
+    a = np.max(np.abs(x), axis=-1)                       # float32, exact
+    scale = (a / np.float32(QMAX)).astype(np.float32)    # correctly rounded fl32 division
+    safe = np.where(scale == 0, np.float32(1), scale).astype(np.float32)
+    r = np.rint((x / safe[..., None]).astype(np.float32))
+    r = np.clip(r, -QMAX, QMAX)
+    r = np.where((scale == 0)[..., None], 0, r)
+    return r.astype(np.int8), scale.astype(np.float32)
+
+
+def f16_round_down(x: np.ndarray) -> np.ndarray:
+    """Largest float16 value <= x (x float32).  Values below -65504 become -inf."""
+    x = np.asarray(x, dtype=np.float32)
+    with np.errstate(over="ignore"):
+        r = x.astype(np.float16)                          # round to nearest even
+        too_big = r.astype(np.float32) > x
+        r = np.where(too_big, np.nextafter(r, np.float16(-np.inf)), r)
+    return r.astype(np.float16)
+
+
+def f16_round_up(x: np.ndarray) -> np.ndarray:
+    """Smallest float16 value >= x (x float32).  Values above 65504 become +inf."""
+    x = np.asarray(x, dtype=np.float32)
+    with np.errstate(over="ignore"):
+        r = x.astype(np.float16)
+        too_small = r.astype(np.float32) < x
+        r = np.where(too_small, np.nextafter(r, np.float16(np.inf)), r)
+    return r.astype(np.float16)
