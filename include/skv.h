@@ -1,0 +1,243 @@
+/*
+ * skv.h — decode-step attention over dense, int8 and Quest block-sparse KV
+ * caches on AMD MI355X (gfx950).  C ABI.
+ *
+ * The library computes, for one new query token per sequence, attention of
+ * each query head h against the cached keys/values of KV head
+ * g = h / (H / Hkv) (grouped-query attention; cpu-attn kernel card, "Usage").
+ * Three variants share the same calls:
+ *   - dense split-K flash-decode over an f16 cache;
+ *   - the same over an int8 cache quantized per token and per head with an
+ *     absmax scale at append time, with exact integer q.k logit dots
+ *     (cpu-attn kernel card, "Method");
+ *   - Quest block-sparse decode: per-(KV head, block) kmin/kmax side cache,
+ *     a channel-wise upper bound per block, fixed top-K blocks plus the sink
+ *     block(s) and the recent window, attention over the selected blocks only
+ *     (opencoti-llamafile sparse_attn.md, "Method: Quest-style min/max block
+ *     bounds" and "S2/S3 engineering design").
+ *
+ * Conventions for every call:
+ *   - All tensor arguments are DEVICE pointers to memory the caller allocated
+ *     and owns.  The library allocates nothing, keeps no state between calls
+ *     and never synchronizes: every call only enqueues kernels on `stream`
+ *     (NULL = the default stream) and returns.  Calls on one stream execute in
+ *     order, so append -> bounds -> select -> decode -> combine needs no
+ *     further synchronization.
+ *   - Arguments are validated on the host before anything is enqueued; a
+ *     failed check returns a negative skv_status and enqueues nothing.  No
+ *     call aborts.  Values that live in device memory (positions, lengths,
+ *     budgets, selected indices) cannot be checked on the host; the kernels
+ *     clamp them so that every access stays inside the buffers described
+ *     below, and each call documents what it does with out-of-range values.
+ *   - Layouts are dense, row-major, with the last dimension contiguous.
+ *     f16 means IEEE binary16 bit patterns (uint16_t storage).
+ *   - Supported in this version: head_dim D = 128; GQA group size
+ *     G = H / Hkv in {1, 2, 4, 8}; block a multiple of 16.  Other values that
+ *     are otherwise valid return SKV_EUNSUPPORTED.
+ */
+#ifndef SKV_H
+#define SKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum skv_status {
+  SKV_OK = 0,
+  SKV_EINVAL = -1,       /* malformed argument: NULL pointer, bad shape, H % Hkv != 0,
+                            D not a multiple of 16 or above 1024, negative counts */
+  SKV_ERANGE = -2,       /* a size exceeds what the buffers or the cache can hold */
+  SKV_EWORKSPACE = -3,   /* workspace missing or smaller than skv_workspace_bytes() */
+  SKV_EUNSUPPORTED = -4, /* valid but not built in this version (see above) */
+  SKV_EDEVICE = -5       /* the HIP runtime reported an error at launch */
+} skv_status;
+
+typedef enum skv_dtype {
+  SKV_F16 = 1,
+  SKV_F32 = 2,
+  SKV_I8 = 3
+} skv_dtype;
+
+/*
+ * Cache descriptor (plain data; the caller fills it and owns every buffer).
+ *   k, v      : [batch][n_kv_heads][max_seq][head_dim]; f16 when kv_dtype is
+ *               SKV_F16, int8 codes when kv_dtype is SKV_I8.
+ *   k_scale,
+ *   v_scale   : [batch][n_kv_heads][max_seq] float32 absmax scales (SKV_I8
+ *               only; ignored for SKV_F16).
+ *   kmin, kmax: [batch][n_kv_heads][max_blocks][head_dim] f16, where
+ *               max_blocks = ceil(max_seq / block).  The Quest side cache:
+ *               channel-wise min and max of the keys of each block, taken
+ *               before quantization (sparse_attn.md, "Method" and
+ *               "All-KV-types composition").  Both NULL = no side cache
+ *               (dense only; appends then skip the bounds update).
+ * Token t of sequence b lives at position t (0-based) of its row.
+ */
+typedef struct skv_cache {
+  int32_t batch;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t max_seq;
+  int32_t block;
+  int32_t kv_dtype;
+  void* k;
+  void* v;
+  float* k_scale;
+  float* v_scale;
+  uint16_t* kmin;
+  uint16_t* kmax;
+} skv_cache;
+
+/* Number of blocks per sequence row of the side cache: ceil(max_seq/block). */
+int32_t skv_max_blocks(const skv_cache* c);
+
+/*
+ * skv_kv_append — write n_new consecutive tokens into every sequence.
+ * Defines: cpu-attn kernel card, "Method" (int8 cache: per token and per KV
+ * head, a = max_d |x_d|, scale = a / 127 in float32, code_d =
+ * rint(x_d / scale) clamped to [-127, 127], a == 0 giving scale 0 and codes 0);
+ * sparse_attn.md, "All-KV-types composition" and "S2/S3 engineering design"
+ * item 1 (side cache: per block, channel min/max of the new pre-quantization
+ * keys, min/max-merged into a block that already holds earlier tokens,
+ * overwriting a block whose first position is >= pos0).
+ *   pos0   : device int32 [batch]; sequence b receives positions
+ *            pos0[b] .. pos0[b] + n_new - 1.  Tokens before pos0[b] must
+ *            already be in the cache (the bounds merge assumes a filled
+ *            prefix).  Rows at positions >= max_seq (or a negative pos0) are
+ *            not written.
+ *   n_new  : >= 1 tokens per sequence.
+ *   k_new,
+ *   v_new  : device [batch][n_new][n_kv_heads][head_dim] of src_dtype:
+ *            SKV_F16 for an f16 cache (copied bit for bit), SKV_F32 for an
+ *            int8 cache (quantized; side-cache bounds are the float32 min
+ *            rounded toward -inf and max rounded toward +inf into f16).
+ * Errors: SKV_EINVAL (NULL, n_new < 1), SKV_ERANGE (n_new > max_seq),
+ * SKV_EUNSUPPORTED (other dtype pairs), SKV_EDEVICE.
+ */
+skv_status skv_kv_append(const skv_cache* c, const int32_t* pos0, int32_t n_new,
+                         const void* k_new, const void* v_new, int32_t src_dtype,
+                         hipStream_t stream);
+
+/*
+ * skv_block_bounds — Quest upper bound per block, reduced over the GQA group.
+ * Defines: sparse_attn.md, "Method" (UB = sum_d max(q_d * kmin_d,
+ * q_d * kmax_d)) and "S2/S3 engineering design" item 2 / "Open questions"
+ * (max of UB over the query heads of a KV head gives one score per block).
+ * A channel with q_d == 0 contributes 0.  Computed in float32.
+ *   q       : device float32 [batch][n_heads][head_dim], the query as given
+ *             (no softmax scale; the bound only ranks blocks).
+ *   seq_len : device int32 [batch]; sequence b has L_b tokens, clamped to
+ *             [0, max_len]; blocks j < ceil(L_b / block) are scored.
+ *   max_len : host upper bound of every L_b, <= max_seq.
+ *   score   : device float32 [batch][n_kv_heads][max_blocks]; entries of
+ *             blocks >= ceil(L_b / block) are not written.
+ * Errors: SKV_EINVAL (NULL, no side cache, H % Hkv), SKV_ERANGE (max_len),
+ * SKV_EUNSUPPORTED, SKV_EDEVICE.
+ */
+skv_status skv_block_bounds(const skv_cache* c, const float* q, int32_t n_heads,
+                            const int32_t* seq_len, int32_t max_len, float* score,
+                            hipStream_t stream);
+
+/*
+ * skv_select_topk — fixed top-K block selection per (sequence, KV head).
+ * Defines: sparse_attn.md, "Method" (top-K_SEL blocks by bound plus the
+ * recent window and the attention-sink block) and "Budget policy" (fixed K).
+ * Forced blocks F = [0, n_sink) and [NB - n_recent, NB), NB =
+ * ceil(L_b / block).  The k_sel[b] highest-scoring blocks among the others are
+ * added (scores compare by value, -0 == +0; exact ties go to the lower block
+ * index); if k_sel[b] covers every other block, all NB blocks are selected.
+ * The selected set is written in ascending block order.
+ *   score    : device float32 [batch][n_kv_heads][max_blocks] (from
+ *              skv_block_bounds).
+ *   seq_len  : device int32 [batch], clamped to [0, max_blocks * block].
+ *   k_sel    : device int32 [batch]; negative values count as 0.
+ *   max_sel  : capacity of each selected list; should be >= k_sel[b] + n_sink
+ *              + n_recent.  At most max_sel indices are written.
+ *   sel_idx  : device int32 [batch][n_kv_heads][max_sel]; entries past the
+ *              set are filled with -1.
+ *   sel_cnt  : device int32 [batch][n_kv_heads]: |S| = min(NB, k + |F|),
+ *              reported in full even when it exceeds max_sel (that signals a
+ *              truncated list; skv_decode_attn reads at most max_sel).
+ *   sel_mask : optional (NULL = none) device uint32
+ *              [batch][n_kv_heads][ceil(max_blocks / 32)]: bit (j % 32) of
+ *              word j / 32 set iff block j is selected.
+ * Errors: SKV_EINVAL (NULL, negative n_sink/n_recent, max_sel < 1),
+ * SKV_EUNSUPPORTED (max_blocks > 16384), SKV_EDEVICE.
+ */
+skv_status skv_select_topk(const float* score, const int32_t* seq_len, int32_t batch,
+                           int32_t n_kv_heads, int32_t max_blocks, int32_t block,
+                           const int32_t* k_sel, int32_t n_sink, int32_t n_recent,
+                           int32_t max_sel, int32_t* sel_idx, int32_t* sel_cnt,
+                           uint32_t* sel_mask, hipStream_t stream);
+
+/*
+ * skv_decode_attn — split-K partial attention (first half of a flash-decode).
+ * Defines: for every query head, the softmax over the attended tokens of
+ * s_t = (q . k_t) * softmax_scale and the weighted sum of v_t.
+ *   f16 cache: s_t from float32 products of the query and the f16 keys;
+ *   int8 cache: the query head is quantized with the absmax rule of
+ *     skv_kv_append, dot_t = sum_d q_code_d * k_code_{t,d} exactly in int32,
+ *     s_t = dot_t * q_scale * k_scale_t * softmax_scale; v_t = v_scale_t *
+ *     v_code_t (cpu-attn kernel card, "Method").
+ * Softmax and accumulation are float32.  Attended tokens: all of
+ * [0, L_b) (dense, sel_idx == NULL), or the tokens of the selected blocks
+ * with the last block clipped at L_b (sparse; sparse_attn.md "Method",
+ * kernel skip).  Selected indices outside [0, NB) are ignored.
+ * The tokens of (sequence, KV head) are cut into n_split contiguous parts
+ * (dense: runs of blocks; sparse: runs of the selected list); each part
+ * writes one partial state per query head into the workspace:
+ *   workspace = float m[batch][n_heads][n_split],
+ *               float l[batch][n_heads][n_split],
+ *               float o[batch][n_heads][n_split][head_dim]
+ *   with, over the part's tokens T: m = max_t s_t * log2(e), l = sum_t
+ *   2^(s_t log2 e - m), o = sum_t 2^(s_t log2 e - m) v_t; an empty part has
+ *   m = -inf, l = 0, o = 0.
+ *   q          : device float32 [batch][n_heads][head_dim].
+ *   seq_len    : device int32 [batch], clamped to [0, max_len].
+ *   max_len    : host upper bound of every L_b, <= max_seq.
+ *   sel_idx,
+ *   sel_cnt    : from skv_select_topk, or both NULL for dense.
+ *   max_sel    : row length of sel_idx (ignored for dense).
+ *   n_split    : 1 .. 4096 parts per (sequence, KV head).
+ *   dbg_logits : optional (NULL = none), int8 cache only: device int32
+ *                [batch][n_heads][max_len] receiving the exact integer dots
+ *                of the attended tokens (others untouched).
+ * Errors: SKV_EINVAL, SKV_ERANGE, SKV_EWORKSPACE, SKV_EUNSUPPORTED,
+ * SKV_EDEVICE.
+ */
+skv_status skv_decode_attn(const skv_cache* c, const float* q, int32_t n_heads,
+                           const int32_t* seq_len, int32_t max_len,
+                           const int32_t* sel_idx, const int32_t* sel_cnt, int32_t max_sel,
+                           float softmax_scale, int32_t n_split,
+                           void* workspace, size_t workspace_bytes,
+                           int32_t* dbg_logits, hipStream_t stream);
+
+/*
+ * skv_combine — merge the split-K partial states into the output.
+ * Defines: M = max_i m_i; out = sum_i 2^(m_i - M) o_i / sum_i 2^(m_i - M) l_i
+ * over the non-empty parts (the numerator/mass form of a split softmax).  A
+ * query head whose parts are all empty (L_b == 0) gets zeros.
+ *   workspace : as written by skv_decode_attn with the same batch, n_heads,
+ *               head_dim, n_split.
+ *   out       : device float32 [batch][n_heads][head_dim].
+ * Errors: SKV_EINVAL, SKV_EUNSUPPORTED, SKV_EDEVICE.
+ */
+skv_status skv_combine(const void* workspace, int32_t batch, int32_t n_heads,
+                       int32_t head_dim, int32_t n_split, float* out, hipStream_t stream);
+
+/* Bytes of workspace skv_decode_attn needs: 4 * batch * n_heads * n_split *
+ * (head_dim + 2); 0 for invalid arguments. */
+size_t skv_workspace_bytes(int32_t batch, int32_t n_heads, int32_t head_dim, int32_t n_split);
+
+/* Static, human-readable name of a status code. */
+const char* skv_status_str(int32_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SKV_H */

@@ -61,6 +61,10 @@ def block_bounds(keys: np.ndarray, L: int, block: int):
 def upper_bounds(q: np.ndarray, kmin: np.ndarray, kmax: np.ndarray) -> np.ndarray:
     """UB[h][j] = sum_d max(q[h,d]*kmin[g,j,d], q[h,d]*kmax[g,j,d]), g = h//G.
 
+    A channel with q_d == 0 contributes 0 (reading taken: the page's max of
+    two products would be 0 * inf = NaN for an infinite bound, which only an
+    int8 cache with |key| > 65504 can produce).
+
     Every product of a float32 q and a float16 bound is exact in float64, and
     the sum is ``math.fsum`` (correctly rounded), so UB is the exact bound
     rounded once; correctly rounded sums are monotone, which makes
@@ -73,9 +77,10 @@ def upper_bounds(q: np.ndarray, kmin: np.ndarray, kmax: np.ndarray) -> np.ndarra
     ub = np.empty((H, nb), dtype=np.float64)
     for h in range(H):
         g = h // G
-        lo = kmin[g].astype(np.float64) * q[h]
-        hi = kmax[g].astype(np.float64) * q[h]
-        terms = np.maximum(lo, hi)                     # [NB][D]
+        with np.errstate(invalid="ignore"):
+            lo = kmin[g].astype(np.float64) * q[h]
+            hi = kmax[g].astype(np.float64) * q[h]
+            terms = np.where(q[h] == 0, 0.0, np.maximum(lo, hi))     # [NB][D]
         ub[h] = [math.fsum(row) for row in terms]
     return ub
 

@@ -1,0 +1,233 @@
+"""Decode-step attention over dense, int8 and Quest block-sparse KV caches on
+AMD MI355X (gfx950).
+
+Python binding of ``libskv.so`` (declared in ``include/skv.h``).  This module
+only marshals arguments: tensors become device pointers, the current torch
+stream becomes the HIP stream, status codes become exceptions.  Every step of
+the computation runs in the library's HIP kernels; there is no Python or CPU
+fallback, and :func:`load` raises if the library is missing.
+
+The five calls keep the C names: :func:`kv_append`, :func:`block_bounds`,
+:func:`select_topk`, :func:`decode_attn`, :func:`combine` (plus
+:func:`workspace_bytes` and :func:`status_str`).  :class:`Cache` owns the
+cache tensors and the C descriptor; :func:`decode` chains the calls for one
+decode step (dense, or Quest when ``k_sel`` is given), the shape of the
+``Int8KVCache.append`` / ``decode`` interface on the cpu-attn kernel card
+("Usage").
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+__all__ = ["load", "Cache", "SkvError", "kv_append", "block_bounds", "select_topk",
+           "decode_attn", "combine", "workspace_bytes", "status_str", "decode",
+           "SKV_F16", "SKV_F32", "SKV_I8", "LIB_PATH", "EXPORTS"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libskv.so")
+
+SKV_OK, SKV_EINVAL, SKV_ERANGE, SKV_EWORKSPACE, SKV_EUNSUPPORTED, SKV_EDEVICE = 0, -1, -2, -3, -4, -5
+SKV_F16, SKV_F32, SKV_I8 = 1, 2, 3
+
+EXPORTS = ("skv_max_blocks", "skv_kv_append", "skv_block_bounds", "skv_select_topk",
+           "skv_decode_attn", "skv_combine", "skv_workspace_bytes", "skv_status_str")
+
+
+class SkvCacheDesc(ctypes.Structure):
+    """Mirror of ``skv_cache`` in include/skv.h."""
+    _fields_ = [("batch", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("max_seq", ctypes.c_int32),
+                ("block", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
+                ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
+                ("kmin", ctypes.c_void_p), ("kmax", ctypes.c_void_p)]
+
+
+class SkvError(RuntimeError):
+    def __init__(self, call: str, status: int):
+        super().__init__(f"{call} failed: {status_str(status)} ({status})")
+        self.status = status
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Load libskv.so once and declare the C signatures.  Raises if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with "
+                           "`python -m sparse_kv_cache_append_amd.build` (no fallback exists)")
+    lib = ctypes.CDLL(path)
+    P, I32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    desc = ctypes.POINTER(SkvCacheDesc)
+    sig = {
+        "skv_max_blocks": (I32, [desc]),
+        "skv_kv_append": (I32, [desc, P, I32, P, P, I32, P]),
+        "skv_block_bounds": (I32, [desc, P, I32, P, I32, P, P]),
+        "skv_select_topk": (I32, [P, P, I32, I32, I32, I32, P, I32, I32, I32, P, P, P, P]),
+        "skv_decode_attn": (I32, [desc, P, I32, P, I32, P, P, I32, ctypes.c_float, I32, P, SZ, P, P]),
+        "skv_combine": (I32, [P, I32, I32, I32, I32, P, P]),
+        "skv_workspace_bytes": (SZ, [I32, I32, I32, I32]),
+        "skv_status_str": (ctypes.c_char_p, [I32]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def status_str(status: int) -> str:
+    return load().skv_status_str(int(status)).decode()
+
+
+def workspace_bytes(batch: int, n_heads: int, head_dim: int, n_split: int) -> int:
+    return int(load().skv_workspace_bytes(batch, n_heads, head_dim, n_split))
+
+
+def _check(call: str, status: int):
+    if status != SKV_OK:
+        raise SkvError(call, status)
+
+
+def _ptr(t) -> Optional[int]:
+    """Device pointer of a CUDA tensor (None passes NULL)."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensor must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+class Cache:
+    """KV cache tensors plus the C descriptor.
+
+    k, v: [batch][n_kv_heads][max_seq][head_dim] (float16 or int8);
+    k_scale, v_scale: [batch][n_kv_heads][max_seq] float32 (int8 only);
+    kmin, kmax: [batch][n_kv_heads][max_blocks][head_dim] float16 (Quest side
+    cache, allocated when ``bounds``)."""
+
+    def __init__(self, batch: int, n_kv_heads: int, max_seq: int, head_dim: int = 128,
+                 kv_dtype: str = "f16", block: int = 64, bounds: bool = True, device="cuda"):
+        import torch
+        if kv_dtype not in ("f16", "i8"):
+            raise ValueError("kv_dtype must be 'f16' or 'i8'")
+        self.batch, self.n_kv_heads, self.max_seq = batch, n_kv_heads, max_seq
+        self.head_dim, self.block, self.kv_dtype = head_dim, block, kv_dtype
+        self.max_blocks = -(-max_seq // block)
+        shape = (batch, n_kv_heads, max_seq, head_dim)
+        dt = torch.float16 if kv_dtype == "f16" else torch.int8
+        self.k = torch.zeros(shape, dtype=dt, device=device)
+        self.v = torch.zeros(shape, dtype=dt, device=device)
+        self.k_scale = self.v_scale = None
+        if kv_dtype == "i8":
+            self.k_scale = torch.zeros(shape[:3], dtype=torch.float32, device=device)
+            self.v_scale = torch.zeros(shape[:3], dtype=torch.float32, device=device)
+        self.kmin = self.kmax = None
+        if bounds:
+            bshape = (batch, n_kv_heads, self.max_blocks, head_dim)
+            self.kmin = torch.zeros(bshape, dtype=torch.float16, device=device)
+            self.kmax = torch.zeros(bshape, dtype=torch.float16, device=device)
+        self.desc = SkvCacheDesc(batch, n_kv_heads, head_dim, max_seq, block,
+                                 SKV_F16 if kv_dtype == "f16" else SKV_I8,
+                                 _ptr(self.k), _ptr(self.v), _ptr(self.k_scale),
+                                 _ptr(self.v_scale), _ptr(self.kmin), _ptr(self.kmax))
+
+    def src_dtype(self) -> int:
+        return SKV_F16 if self.kv_dtype == "f16" else SKV_F32
+
+
+def kv_append(cache: Cache, pos0, k_new, v_new, stream=None):
+    """Append n_new tokens per sequence: k_new, v_new [batch][n_new][Hkv][D]
+    (float16 for an f16 cache, float32 for an int8 cache); pos0 int32 [batch]."""
+    n_new = int(k_new.shape[1])
+    _check("skv_kv_append", load().skv_kv_append(
+        ctypes.byref(cache.desc), _ptr(pos0), n_new, _ptr(k_new), _ptr(v_new),
+        cache.src_dtype(), _stream(stream)))
+
+
+def block_bounds(cache: Cache, q, seq_len, max_len: int, score, stream=None):
+    """score [batch][Hkv][max_blocks] <- group-max Quest bound of every block."""
+    _check("skv_block_bounds", load().skv_block_bounds(
+        ctypes.byref(cache.desc), _ptr(q), int(q.shape[1]), _ptr(seq_len), int(max_len),
+        _ptr(score), _stream(stream)))
+
+
+def select_topk(score, seq_len, block: int, k_sel, n_sink: int, n_recent: int,
+                sel_idx, sel_cnt, sel_mask=None, stream=None):
+    """Fixed top-K + sink + recent; sel_idx [batch][Hkv][max_sel] int32 ascending."""
+    B, Hkv, max_blocks = (int(x) for x in score.shape)
+    _check("skv_select_topk", load().skv_select_topk(
+        _ptr(score), _ptr(seq_len), B, Hkv, max_blocks, int(block), _ptr(k_sel), int(n_sink),
+        int(n_recent), int(sel_idx.shape[2]), _ptr(sel_idx), _ptr(sel_cnt), _ptr(sel_mask),
+        _stream(stream)))
+
+
+def decode_attn(cache: Cache, q, seq_len, max_len: int, softmax_scale: float, n_split: int,
+                workspace, sel_idx=None, sel_cnt=None, dbg_logits=None, stream=None):
+    """Split-K partial states into ``workspace`` (uint8/float tensor of at least
+    workspace_bytes(...) bytes)."""
+    max_sel = int(sel_idx.shape[2]) if sel_idx is not None else 0
+    _check("skv_decode_attn", load().skv_decode_attn(
+        ctypes.byref(cache.desc), _ptr(q), int(q.shape[1]), _ptr(seq_len), int(max_len),
+        _ptr(sel_idx), _ptr(sel_cnt), max_sel, float(softmax_scale), int(n_split),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(dbg_logits),
+        _stream(stream)))
+
+
+def combine(workspace, batch: int, n_heads: int, head_dim: int, n_split: int, out, stream=None):
+    """out [batch][n_heads][head_dim] float32 from the split-K partials."""
+    _check("skv_combine", load().skv_combine(
+        _ptr(workspace), int(batch), int(n_heads), int(head_dim), int(n_split), _ptr(out),
+        _stream(stream)))
+
+
+def default_split(batch: int, n_kv_heads: int, n_units: int, target_wgs: int = 1024) -> int:
+    """Parts per (sequence, KV head) so the grid has about ``target_wgs``
+    workgroups, at least one block (or selected entry) per part."""
+    n = max(1, math.ceil(target_wgs / max(1, batch * n_kv_heads)))
+    return int(max(1, min(n, n_units, 4096)))
+
+
+def decode(cache: Cache, q, seq_len, max_len: int, softmax_scale: Optional[float] = None,
+           k_sel=None, n_sink: int = 1, n_recent: int = 2, max_sel: Optional[int] = None,
+           n_split: Optional[int] = None, stream=None):
+    """One decode step: dense (k_sel None) or Quest (k_sel int32 [batch]).
+    Returns out [batch][H][D] float32.  Allocates its scratch tensors."""
+    import torch
+    B, H, D = (int(x) for x in q.shape)
+    dev = q.device
+    scale = 1.0 / math.sqrt(D) if softmax_scale is None else softmax_scale
+    sel_idx = sel_cnt = None
+    nb_max = -(-max_len // cache.block)
+    if k_sel is not None:
+        if max_sel is None:
+            max_sel = int(k_sel.max().item()) + n_sink + n_recent
+        max_sel = max(1, min(max_sel, nb_max if nb_max > 0 else 1))
+        score = torch.empty((B, cache.n_kv_heads, cache.max_blocks), dtype=torch.float32, device=dev)
+        sel_idx = torch.empty((B, cache.n_kv_heads, max_sel), dtype=torch.int32, device=dev)
+        sel_cnt = torch.empty((B, cache.n_kv_heads), dtype=torch.int32, device=dev)
+        block_bounds(cache, q, seq_len, max_len, score, stream)
+        select_topk(score, seq_len, cache.block, k_sel, n_sink, n_recent, sel_idx, sel_cnt,
+                    stream=stream)
+    units = max_sel if k_sel is not None else max(nb_max, 1)
+    S = n_split or default_split(B, cache.n_kv_heads, units)
+    ws = torch.empty(workspace_bytes(B, H, D, S), dtype=torch.uint8, device=dev)
+    out = torch.empty((B, H, D), dtype=torch.float32, device=dev)
+    decode_attn(cache, q, seq_len, max_len, scale, S, ws, sel_idx, sel_cnt, stream=stream)
+    combine(ws, B, H, D, S, out, stream)
+    return out

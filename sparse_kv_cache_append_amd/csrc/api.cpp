@@ -1,0 +1,158 @@
+// C entry points: argument validation (host only, before anything is
+// enqueued) and dispatch to the kernel launchers.
+#include <hip/hip_runtime.h>
+
+#include "launch.h"
+#include "skv.h"
+
+namespace {
+
+constexpr int32_t kMaxSplit = 4096;
+constexpr int32_t kMaxSelectBlocks = 16384;
+
+bool valid_head_dim(int32_t d) { return d >= 16 && d <= 1024 && d % 16 == 0; }
+bool supported_group(int32_t g) { return g == 1 || g == 2 || g == 4 || g == 8; }
+
+int32_t blocks_of(int32_t n, int32_t block) {
+  return int32_t((int64_t(n) + block - 1) / block);
+}
+
+skv_status check_cache(const skv_cache* c, bool need_bounds) {
+  if (c == nullptr) return SKV_EINVAL;
+  if (c->batch < 1 || c->n_kv_heads < 1 || c->max_seq < 1) return SKV_EINVAL;
+  if (!valid_head_dim(c->head_dim)) return SKV_EINVAL;
+  if (c->block < 16 || c->block % 16 != 0) return SKV_EINVAL;
+  if (c->kv_dtype != SKV_F16 && c->kv_dtype != SKV_I8) return SKV_EINVAL;
+  if (c->k == nullptr || c->v == nullptr) return SKV_EINVAL;
+  if (c->kv_dtype == SKV_I8 && (c->k_scale == nullptr || c->v_scale == nullptr)) return SKV_EINVAL;
+  if ((c->kmin == nullptr) != (c->kmax == nullptr)) return SKV_EINVAL;
+  if (need_bounds && c->kmin == nullptr) return SKV_EINVAL;
+  // element counts must fit comfortably in int64 address arithmetic
+  const double elems = double(c->batch) * c->n_kv_heads * double(c->max_seq) * c->head_dim;
+  if (elems > 4.0e18) return SKV_ERANGE;
+  if (c->head_dim != 128) return SKV_EUNSUPPORTED;
+  return SKV_OK;
+}
+
+skv_status check_heads(const skv_cache* c, int32_t n_heads) {
+  if (n_heads < 1 || n_heads % c->n_kv_heads != 0) return SKV_EINVAL;
+  if (!supported_group(n_heads / c->n_kv_heads)) return SKV_EUNSUPPORTED;
+  return SKV_OK;
+}
+
+skv_status device_status(hipError_t e) { return e == hipSuccess ? SKV_OK : SKV_EDEVICE; }
+
+}  // namespace
+
+extern "C" {
+
+int32_t skv_max_blocks(const skv_cache* c) {
+  if (c == nullptr || c->block < 1 || c->max_seq < 0) return 0;
+  return blocks_of(c->max_seq, c->block);
+}
+
+size_t skv_workspace_bytes(int32_t batch, int32_t n_heads, int32_t head_dim, int32_t n_split) {
+  if (batch < 1 || n_heads < 1 || !valid_head_dim(head_dim) || n_split < 1 || n_split > kMaxSplit)
+    return 0;
+  return sizeof(float) * size_t(batch) * size_t(n_heads) * size_t(n_split) * size_t(head_dim + 2);
+}
+
+const char* skv_status_str(int32_t s) {
+  switch (s) {
+    case SKV_OK: return "SKV_OK";
+    case SKV_EINVAL: return "SKV_EINVAL: malformed argument";
+    case SKV_ERANGE: return "SKV_ERANGE: size out of range";
+    case SKV_EWORKSPACE: return "SKV_EWORKSPACE: workspace missing or too small";
+    case SKV_EUNSUPPORTED: return "SKV_EUNSUPPORTED: valid but not built in this version";
+    case SKV_EDEVICE: return "SKV_EDEVICE: HIP runtime error";
+    default: return "unknown skv_status";
+  }
+}
+
+skv_status skv_kv_append(const skv_cache* c, const int32_t* pos0, int32_t n_new,
+                         const void* k_new, const void* v_new, int32_t src_dtype,
+                         hipStream_t stream) {
+  skv_status st = check_cache(c, false);
+  if (st != SKV_OK) return st;
+  if (pos0 == nullptr || k_new == nullptr || v_new == nullptr || n_new < 1) return SKV_EINVAL;
+  if (n_new > c->max_seq) return SKV_ERANGE;
+  const bool ok = (c->kv_dtype == SKV_F16 && src_dtype == SKV_F16) ||
+                  (c->kv_dtype == SKV_I8 && src_dtype == SKV_F32);
+  if (!ok) return (src_dtype == SKV_F16 || src_dtype == SKV_F32) ? SKV_EUNSUPPORTED : SKV_EINVAL;
+  return device_status(skv::launch_append(*c, pos0, n_new, k_new, v_new, stream));
+}
+
+skv_status skv_block_bounds(const skv_cache* c, const float* q, int32_t n_heads,
+                            const int32_t* seq_len, int32_t max_len, float* score,
+                            hipStream_t stream) {
+  skv_status st = check_cache(c, true);
+  if (st != SKV_OK) return st;
+  if (q == nullptr || seq_len == nullptr || score == nullptr) return SKV_EINVAL;
+  st = check_heads(c, n_heads);
+  if (st != SKV_OK) return st;
+  if (max_len < 0 || max_len > c->max_seq) return SKV_ERANGE;
+  return device_status(skv::launch_bounds(*c, q, n_heads, seq_len, max_len, score, stream));
+}
+
+skv_status skv_select_topk(const float* score, const int32_t* seq_len, int32_t batch,
+                           int32_t n_kv_heads, int32_t max_blocks, int32_t block,
+                           const int32_t* k_sel, int32_t n_sink, int32_t n_recent,
+                           int32_t max_sel, int32_t* sel_idx, int32_t* sel_cnt,
+                           uint32_t* sel_mask, hipStream_t stream) {
+  if (score == nullptr || seq_len == nullptr || k_sel == nullptr || sel_idx == nullptr ||
+      sel_cnt == nullptr)
+    return SKV_EINVAL;
+  if (batch < 1 || n_kv_heads < 1 || max_blocks < 1 || block < 16 || block % 16 != 0)
+    return SKV_EINVAL;
+  if (n_sink < 0 || n_recent < 0 || max_sel < 1) return SKV_EINVAL;
+  if (max_blocks > kMaxSelectBlocks) return SKV_EUNSUPPORTED;
+  return device_status(skv::launch_select(score, seq_len, batch, n_kv_heads, max_blocks, block,
+                                          k_sel, n_sink, n_recent, max_sel, sel_idx, sel_cnt,
+                                          sel_mask, stream));
+}
+
+skv_status skv_decode_attn(const skv_cache* c, const float* q, int32_t n_heads,
+                           const int32_t* seq_len, int32_t max_len,
+                           const int32_t* sel_idx, const int32_t* sel_cnt, int32_t max_sel,
+                           float softmax_scale, int32_t n_split,
+                           void* workspace, size_t workspace_bytes,
+                           int32_t* dbg_logits, hipStream_t stream) {
+  skv_status st = check_cache(c, false);
+  if (st != SKV_OK) return st;
+  if (q == nullptr || seq_len == nullptr) return SKV_EINVAL;
+  st = check_heads(c, n_heads);
+  if (st != SKV_OK) return st;
+  if ((sel_idx == nullptr) != (sel_cnt == nullptr)) return SKV_EINVAL;
+  if (sel_idx != nullptr && max_sel < 1) return SKV_EINVAL;
+  if (n_split < 1 || n_split > kMaxSplit) return SKV_EINVAL;
+  if (!(softmax_scale == softmax_scale) || softmax_scale < 0.0f) return SKV_EINVAL;
+  if (dbg_logits != nullptr && c->kv_dtype != SKV_I8) return SKV_EINVAL;
+  if (max_len < 0 || max_len > c->max_seq) return SKV_ERANGE;
+  const size_t need = skv_workspace_bytes(c->batch, n_heads, c->head_dim, n_split);
+  if (workspace == nullptr || workspace_bytes < need) return SKV_EWORKSPACE;
+  skv::DecodeParams p;
+  p.c = c;
+  p.q = q;
+  p.n_heads = n_heads;
+  p.seq_len = seq_len;
+  p.max_len = max_len;
+  p.sel_idx = sel_idx;
+  p.sel_cnt = sel_cnt;
+  p.max_sel = max_sel;
+  p.softmax_scale = softmax_scale;
+  p.n_split = n_split;
+  p.ws = static_cast<float*>(workspace);
+  p.dbg_logits = dbg_logits;
+  return device_status(skv::launch_decode(p, stream));
+}
+
+skv_status skv_combine(const void* workspace, int32_t batch, int32_t n_heads, int32_t head_dim,
+                       int32_t n_split, float* out, hipStream_t stream) {
+  if (workspace == nullptr || out == nullptr) return SKV_EINVAL;
+  if (batch < 1 || n_heads < 1 || !valid_head_dim(head_dim)) return SKV_EINVAL;
+  if (n_split < 1 || n_split > kMaxSplit) return SKV_EINVAL;
+  return device_status(skv::launch_combine(static_cast<const float*>(workspace), batch, n_heads,
+                                           head_dim, n_split, out, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,121 @@
+// Device-side helpers shared by the gfx950 kernels: cross-lane reductions on
+// 64-wide wavefronts, f16 bit handling, directed f32 -> f16 rounding, the
+// absmax int8 row quantizer and order-preserving radix keys.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+#include <stdint.h>
+
+namespace skv {
+
+constexpr int kWave = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ---------------------------------------------------------------- DPP lanes
+// DPP control codes (GFX9 encoding).
+constexpr int kDppQuadXor1 = 0xB1;      // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowMirror = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xF, 0xF, false);
+}
+
+// Sum / max over aligned groups of 8 lanes; every lane of the group gets the
+// same bits (each step combines a lane with its mirror, a commutative op).
+__device__ __forceinline__ float group8_sum(float x) {
+  x += dpp_f<kDppQuadXor1>(x);
+  x += dpp_f<kDppQuadXor2>(x);
+  x += dpp_f<kDppRowHalfMirror>(x);
+  return x;
+}
+__device__ __forceinline__ int group8_sum_i(int x) {
+  x += dpp_i<kDppQuadXor1>(x);
+  x += dpp_i<kDppQuadXor2>(x);
+  x += dpp_i<kDppRowHalfMirror>(x);
+  return x;
+}
+__device__ __forceinline__ float group8_max(float x) {
+  x = fmaxf(x, dpp_f<kDppQuadXor1>(x));
+  x = fmaxf(x, dpp_f<kDppQuadXor2>(x));
+  x = fmaxf(x, dpp_f<kDppRowHalfMirror>(x));
+  return x;
+}
+// Sum over aligned groups of 16 lanes (one DPP row).
+__device__ __forceinline__ float group16_sum(float x) {
+  x = group8_sum(x);
+  x += dpp_f<kDppRowMirror>(x);
+  return x;
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+__device__ __forceinline__ int wave_sum_i(int x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+// ---------------------------------------------------------------- f16 bits
+__device__ __forceinline__ float h2f(uint16_t b) {
+  return __half2float(__ushort_as_half(b));
+}
+__device__ __forceinline__ float h2f_lo(uint32_t w) { return h2f(uint16_t(w & 0xFFFFu)); }
+__device__ __forceinline__ float h2f_hi(uint32_t w) { return h2f(uint16_t(w >> 16)); }
+
+// Next f16 toward -inf / +inf of a non-NaN bit pattern.
+__device__ __forceinline__ uint16_t f16_next_down(uint16_t u) {
+  if ((u & 0x7FFFu) == 0) return 0x8001u;          // +-0 -> smallest negative subnormal
+  return (u & 0x8000u) ? uint16_t(u + 1) : uint16_t(u - 1);
+}
+__device__ __forceinline__ uint16_t f16_next_up(uint16_t u) {
+  if ((u & 0x7FFFu) == 0) return 0x0001u;
+  return (u & 0x8000u) ? uint16_t(u - 1) : uint16_t(u + 1);
+}
+// Largest f16 <= x and smallest f16 >= x (x finite float32 or +-inf).
+__device__ __forceinline__ uint16_t f32_to_f16_down(float x) {
+  uint16_t r = __half_as_ushort(__float2half_rn(x));
+  return (h2f(r) > x) ? f16_next_down(r) : r;
+}
+__device__ __forceinline__ uint16_t f32_to_f16_up(float x) {
+  uint16_t r = __half_as_ushort(__float2half_rn(x));
+  return (h2f(r) < x) ? f16_next_up(r) : r;
+}
+__device__ __forceinline__ uint16_t f16_min_bits(uint16_t a, uint16_t b) {
+  return h2f(a) <= h2f(b) ? a : b;
+}
+__device__ __forceinline__ uint16_t f16_max_bits(uint16_t a, uint16_t b) {
+  return h2f(a) >= h2f(b) ? a : b;
+}
+
+// ------------------------------------------------------- absmax int8 quant
+// scale = a / 127 and x / scale are IEEE correctly rounded float32 divisions
+// (this code is built without fast-math), rintf rounds half to even.
+__device__ __forceinline__ float absmax_scale(float a) { return a / 127.0f; }
+__device__ __forceinline__ int quant_code(float x, float scale) {
+  if (scale == 0.0f) return 0;
+  float r = rintf(x / scale);
+  r = fminf(fmaxf(r, -127.0f), 127.0f);
+  return int(r);
+}
+
+// ------------------------------------------------------ radix select keys
+// Order-preserving map float32 -> uint32 (larger float -> larger key), with
+// -0 canonicalized to +0 so that the two compare equal.
+__device__ __forceinline__ uint32_t float_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+}  // namespace skv

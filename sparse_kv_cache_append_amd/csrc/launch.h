@@ -1,0 +1,51 @@
+// Internal launchers, one per kernel family.  The C entry points in api.cpp
+// validate every argument and then call these; the launchers only size the
+// grid and enqueue on the given stream.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "skv.h"
+
+namespace skv {
+
+struct DecodeParams {
+  const skv_cache* c;
+  const float* q;
+  int32_t n_heads;
+  const int32_t* seq_len;
+  int32_t max_len;
+  const int32_t* sel_idx;  // nullptr = dense
+  const int32_t* sel_cnt;
+  int32_t max_sel;
+  float softmax_scale;
+  int32_t n_split;
+  float* ws;
+  int32_t* dbg_logits;
+};
+
+hipError_t launch_append(const skv_cache& c, const int32_t* pos0, int32_t n_new,
+                         const void* k_new, const void* v_new, hipStream_t stream);
+
+hipError_t launch_bounds(const skv_cache& c, const float* q, int32_t n_heads,
+                         const int32_t* seq_len, int32_t max_len, float* score,
+                         hipStream_t stream);
+
+hipError_t launch_select(const float* score, const int32_t* seq_len, int32_t batch,
+                         int32_t n_kv_heads, int32_t max_blocks, int32_t block,
+                         const int32_t* k_sel, int32_t n_sink, int32_t n_recent,
+                         int32_t max_sel, int32_t* sel_idx, int32_t* sel_cnt,
+                         uint32_t* sel_mask, hipStream_t stream);
+
+hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
+
+hipError_t launch_combine(const float* ws, int32_t batch, int32_t n_heads, int32_t head_dim,
+                          int32_t n_split, float* out, hipStream_t stream);
+
+// Workspace layout of the split-K partial states (see skv_decode_attn).
+inline size_t ws_m_offset(int32_t, int32_t, int32_t) { return 0; }
+inline size_t ws_l_offset(int32_t B, int32_t H, int32_t S) { return size_t(B) * H * S; }
+inline size_t ws_o_offset(int32_t B, int32_t H, int32_t S) { return 2 * size_t(B) * H * S; }
+
+}  // namespace skv

@@ -1,0 +1,140 @@
+"""Helpers for the GPU parity tests: move a workload into a device cache
+through the library's own append, run the library's calls, compare with the
+oracle.  Imported only by ``-m gpu`` tests."""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+import sparse_kv_cache_append_amd as skv
+
+DEV = "cuda:0"
+
+
+def rel_err(got, ref) -> float:
+    """Frobenius-relative error ||got - ref|| / ||ref|| in float64."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    den = np.linalg.norm(ref)
+    return float(np.linalg.norm(got - ref) / (den if den > 0 else 1.0))
+
+
+def padded_rows(w, b_rows: int):
+    """[B][b_rows][Hkv][D] source tensors for a one-call prefill of every
+    sequence; sequence b is padded past L_b with copies of its last row, which
+    leaves every block's min/max unchanged (rows past L_b are never read)."""
+    B, Hkv, D = w.B, w.Hkv, w.D
+    dt = np.float16 if w.kv_dtype == "f16" else np.float32
+    k = np.empty((B, b_rows, Hkv, D), dt)
+    v = np.empty((B, b_rows, Hkv, D), dt)
+    for b in range(B):
+        L = w.lens[b]
+        k[b, :L] = np.transpose(w.k[b], (1, 0, 2))
+        v[b, :L] = np.transpose(w.v[b], (1, 0, 2))
+        if L < b_rows and L > 0:
+            k[b, L:] = k[b, L - 1]
+            v[b, L:] = v[b, L - 1]
+        elif L == 0:
+            k[b] = 0
+            v[b] = 0
+    return k, v
+
+
+def build_cache(w, max_seq: int | None = None, bounds: bool = True, chunk: int | None = None):
+    """Device cache holding the workload's tokens, filled by skv.kv_append
+    (in chunks of ``chunk`` rows when given)."""
+    Lmax = max(w.lens)
+    max_seq = max_seq or max(Lmax, 1)
+    cache = skv.Cache(w.B, w.Hkv, max_seq, w.D, w.kv_dtype, w.block, bounds=bounds, device=DEV)
+    if Lmax == 0:
+        return cache
+    k, v = padded_rows(w, Lmax)
+    kt = torch.from_numpy(k).to(DEV)
+    vt = torch.from_numpy(v).to(DEV)
+    step = chunk or Lmax
+    for p0 in range(0, Lmax, step):
+        n = min(step, Lmax - p0)
+        pos0 = torch.full((w.B,), p0, dtype=torch.int32, device=DEV)
+        skv.kv_append(cache, pos0, kt[:, p0:p0 + n].contiguous(), vt[:, p0:p0 + n].contiguous())
+    torch.cuda.synchronize()
+    return cache
+
+
+def device_inputs(w):
+    q = torch.from_numpy(np.ascontiguousarray(w.q)).to(DEV)
+    seq_len = torch.tensor(w.lens, dtype=torch.int32, device=DEV)
+    return q, seq_len
+
+
+def run_dense(cache, w, n_split=None, dbg=False):
+    q, seq_len = device_inputs(w)
+    max_len = max(max(w.lens), 0)
+    nb = -(-max_len // w.block)
+    S = n_split or skv.default_split(w.B, w.Hkv, max(nb, 1))
+    ws = torch.empty(skv.workspace_bytes(w.B, w.H, w.D, S), dtype=torch.uint8, device=DEV)
+    out = torch.empty((w.B, w.H, w.D), dtype=torch.float32, device=DEV)
+    dl = None
+    if dbg:
+        dl = torch.full((w.B, w.H, max(max_len, 1)), -2 ** 31, dtype=torch.int32, device=DEV)
+    skv.decode_attn(cache, q, seq_len, max_len, w.softmax_scale, S, ws, dbg_logits=dl)
+    skv.combine(ws, w.B, w.H, w.D, S, out)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), (dl.cpu().numpy() if dbg else None)
+
+
+def run_select(cache, w, k_sel=None, max_sel=None, with_mask=False):
+    q, seq_len = device_inputs(w)
+    max_len = max(w.lens)
+    k_sel = list(w.k_sel if k_sel is None else k_sel)
+    ks = torch.tensor(k_sel, dtype=torch.int32, device=DEV)
+    max_sel = max_sel or (max(k_sel) + w.n_sink + w.n_recent)
+    score = torch.full((w.B, w.Hkv, cache.max_blocks), float("nan"), device=DEV)
+    sel = torch.empty((w.B, w.Hkv, max_sel), dtype=torch.int32, device=DEV)
+    cnt = torch.empty((w.B, w.Hkv), dtype=torch.int32, device=DEV)
+    mask = None
+    if with_mask:
+        mask = torch.zeros((w.B, w.Hkv, -(-cache.max_blocks // 32)), dtype=torch.int32, device=DEV)
+    skv.block_bounds(cache, q, seq_len, max_len, score)
+    skv.select_topk(score, seq_len, w.block, ks, w.n_sink, w.n_recent, sel, cnt, mask)
+    torch.cuda.synchronize()
+    return (score.cpu().numpy(), sel, cnt,
+            (mask.cpu().numpy().view(np.uint32) if with_mask else None))
+
+
+def run_sparse(cache, w, sel, cnt, n_split=None):
+    q, seq_len = device_inputs(w)
+    max_len = max(w.lens)
+    max_sel = int(sel.shape[2])
+    S = n_split or skv.default_split(w.B, w.Hkv, max_sel)
+    ws = torch.empty(skv.workspace_bytes(w.B, w.H, w.D, S), dtype=torch.uint8, device=DEV)
+    out = torch.empty((w.B, w.H, w.D), dtype=torch.float32, device=DEV)
+    skv.decode_attn(cache, q, seq_len, max_len, w.softmax_scale, S, ws, sel, cnt)
+    skv.combine(ws, w.B, w.H, w.D, S, out)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def sel_tensor_from_lists(lists, B, Hkv, max_sel):
+    """Host-built selected lists (oracle sets) as device sel_idx / sel_cnt."""
+    idx = np.full((B, Hkv, max_sel), -1, np.int32)
+    cnt = np.zeros((B, Hkv), np.int32)
+    for b in range(B):
+        for g in range(Hkv):
+            s = np.asarray(lists[b][g], np.int32)
+            idx[b, g, :len(s)] = s
+            cnt[b, g] = len(s)
+    return torch.from_numpy(idx).to(DEV), torch.from_numpy(cnt).to(DEV)
+
+
+def quantized_host(w, b):
+    """Oracle quantization of sequence b's float32 rows (codes, scales)."""
+    import oracle
+    kc, ks = oracle.quantize_rows(w.k[b])
+    vc, vs = oracle.quantize_rows(w.v[b])
+    return kc, ks, vc, vs
+
+
+def softmax_scale(D: int) -> float:
+    return 1.0 / math.sqrt(D)

@@ -183,3 +183,10 @@ def test_sparse_with_every_block_selected_equals_dense_bit_for_bit():
         toks = oracle.selected_tokens(sel, 333, 64)
         sp = oracle.attend_f16(w.q[0], w.k[0], w.v[0], w.softmax_scale, tokens=toks)
         assert np.array_equal(sp[g * 4:(g + 1) * 4], dense[g * 4:(g + 1) * 4])
+
+
+def test_zero_query_channel_contributes_zero_even_against_infinite_bounds():
+    kmin = np.array([[[-np.inf, -1.0]]], np.float16)
+    kmax = np.array([[[np.inf, 2.0]]], np.float16)
+    q = np.array([[0.0, 3.0]], np.float32)
+    assert oracle.upper_bounds(q, kmin, kmax)[0, 0] == 6.0

@@ -36,8 +36,10 @@ The five named workloads mirror GQA decode shapes (D = 128):
 """
 from __future__ import annotations
 
+import concurrent.futures as cf
 import dataclasses
 import math
+import os
 from typing import List, Optional
 
 import numpy as np
@@ -126,11 +128,21 @@ def clustered(seeds, H: int, Hkv: int, D: int, lens, kv_dtype: str,
     """Clustered keys, one generator per sequence (``seeds[b]``)."""
     lens = [int(x) for x in lens]
     B = len(lens)
-    ks, vs, qs = [], [], []
-    for b in range(B):
+
+    def one(b):
         rng = np.random.default_rng(seeds[b])
-        k, v, q = _clustered_sequence(rng, H, Hkv, D, lens[b], n_dirs, amp, block, kv_dtype)
-        ks.append(k); vs.append(v); qs.append(q)
+        return _clustered_sequence(rng, H, Hkv, D, lens[b], n_dirs, amp, block, kv_dtype)
+
+    # Sequences draw from independent generators, so threads change no byte.
+    workers = max(1, min(B, 8, os.cpu_count() or 1))
+    if workers > 1:
+        with cf.ThreadPoolExecutor(workers) as ex:
+            seqs = list(ex.map(one, range(B)))
+    else:
+        seqs = [one(0)]
+    ks = [s[0] for s in seqs]
+    vs = [s[1] for s in seqs]
+    qs = [s[2] for s in seqs]
     return Workload(name, B, H, Hkv, D, lens, kv_dtype, ks, vs, np.stack(qs),
                     block=block, **kw)
 
