@@ -6,8 +6,8 @@
 // Quest decode (sparse_attn.md, "Method", kernel skip: unselected blocks are
 // never read).
 //
-// Streaming: LPR lanes share one cache row (LPR = 8 for G <= 4, 16 for
-// G = 8, which halves the per-lane query and accumulator registers), so one
+// Streaming: LPR lanes share one cache row (LPR = 8 for G <= 2, 16 for
+// G >= 4, which halves the per-lane query and accumulator registers), so one
 // wavefront instruction reads 64/LPR full rows.  A workgroup step covers
 // 4 * 64 / LPR rows.  Each lane keeps its slice of K and V in registers and
 // applies it to all G query heads of the group, so every K/V byte crosses
@@ -48,19 +48,33 @@ __device__ __forceinline__ int group_sum_i(int x) {
   return x;
 }
 
+// The blocks of one part, walked in 32- or 16-row steps by an incremental
+// cursor (no division per step).  For Quest decode the part's selected block
+// indices are loaded once, one per lane, and read back with readlane, so a
+// step's address never waits on a memory load.
 struct Part {
   const int32_t* sel;  // row of sel_idx for (b, g); nullptr = dense
   int32_t u0, n_units, spb, block, L, nb, rows_per_step;
+  int32_t jl;          // lane k: selected block of unit k (k < 64), sparse only
 
   __device__ __forceinline__ int32_t n_steps() const { return n_units * spb; }
-  // First row and number of valid rows of step i (nvalid = 0: nothing valid).
-  __device__ __forceinline__ void step(int32_t i, int32_t& r0, int32_t& nvalid) const {
-    const int32_t unit = i / spb, sub = i - unit * spb;
-    int32_t j = u0 + unit;
-    if (sel != nullptr) j = sel[j];
-    if (j < 0 || j >= nb) { r0 = 0; nvalid = 0; return; }
-    r0 = j * block + sub * rows_per_step;
-    nvalid = min(min(rows_per_step, block - sub * rows_per_step), L - r0);
+};
+
+struct Cursor {
+  int32_t unit = 0, sub = 0;
+  // First row and number of valid rows of the cursor's step; then advance.
+  __device__ __forceinline__ void next(const Part& pt, int32_t& r0, int32_t& nvalid) {
+    int32_t j = pt.u0 + unit;
+    if (pt.sel != nullptr)
+      j = unit < kWave ? __builtin_amdgcn_readlane(pt.jl, unit) : pt.sel[j];
+    if (j < 0 || j >= pt.nb) {
+      r0 = 0;
+      nvalid = 0;
+    } else {
+      r0 = j * pt.block + sub * pt.rows_per_step;
+      nvalid = min(min(pt.rows_per_step, pt.block - sub * pt.rows_per_step), pt.L - r0);
+    }
+    if (++sub == pt.spb) { sub = 0; ++unit; }
   }
 };
 
@@ -76,12 +90,17 @@ __device__ __forceinline__ Part make_part(const int32_t* sel_idx, const int32_t*
   pt.spb = (block + rows_per_step - 1) / rows_per_step;
   int32_t total = pt.nb;
   pt.sel = nullptr;
+  pt.jl = -1;
   if (sel_idx != nullptr) {
     pt.sel = sel_idx + bg * max_sel;
     total = min(max(sel_cnt[bg], 0), max_sel);
   }
   pt.u0 = split * units_per_split;
   pt.n_units = max(0, min(units_per_split, total - pt.u0));
+  if (pt.sel != nullptr) {
+    const int lane = threadIdx.x % kWave;
+    if (lane < pt.n_units) pt.jl = pt.sel[pt.u0 + lane];
+  }
   return pt;
 }
 
@@ -144,23 +163,40 @@ __device__ __forceinline__ void finish_part(float (&m)[G], float (&l)[G], float 
   }
 }
 
-// Online-softmax update of one head with logit s (base 2) of a row whose value
-// slice is produced by vget(e); `valid` masks rows past the part.
-template <int EPL, typename VGet>
-__device__ __forceinline__ void softmax_row(float s, bool valid, float wscale, float& m, float& l,
-                                            float (&o)[EPL], VGet vget) {
-  if (valid && s > m) {
-    const float cr = __builtin_amdgcn_exp2f(m - s);
-    l *= cr;
+// Online softmax of one row for all G heads (logits s[h] in base 2).  The
+// reference max m[h] is raised only when a logit exceeds it by more than
+// kLazy (weights stay <= 2^kLazy, far from float32 overflow), and the rescale
+// sits behind a wavefront-uniform branch, so it runs only in the rare steps
+// where some lane needs it.  The final o / l is unchanged by the choice of
+// reference.
+constexpr float kLazy = 8.0f;
+
+template <int G, int EPL, bool SCALED, typename VGet>
+__device__ __forceinline__ void softmax_rows(const float (&s)[G], bool valid, float wscale,
+                                             float (&m)[G], float (&l)[G], float (&o)[G][EPL],
+                                             VGet vget) {
+  bool need = false;
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) o[e] *= cr;
-    m = s;
+  for (int h = 0; h < G; ++h) need |= valid && (s[h] > m[h] + kLazy);
+  if (__ballot(need)) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const bool r = valid && (s[h] > m[h] + kLazy);
+      const float cr = r ? __builtin_amdgcn_exp2f(m[h] - s[h]) : 1.0f;
+      m[h] = r ? s[h] : m[h];
+      l[h] *= cr;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) o[h][e] *= cr;
+    }
   }
-  const float p = valid ? __builtin_amdgcn_exp2f(s - m) : 0.0f;
-  l += p;
-  const float pw = p * wscale;
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) o[e] = fmaf(pw, vget(e), o[e]);
+  for (int h = 0; h < G; ++h) {
+    float p = valid ? __builtin_amdgcn_exp2f(s[h] - m[h]) : 0.0f;
+    l[h] += p;
+    if (SCALED) p *= wscale;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) o[h][e] = fmaf(p, vget(e), o[h][e]);
+  }
 }
 
 // ------------------------------------------------------------------ f16
@@ -194,7 +230,14 @@ decode_f16_kernel(const uint16_t* __restrict__ kc, const uint16_t* __restrict__ 
   for (int h = 0; h < G; ++h) {
     const float* qp = q + (int64_t(b) * H + g * G + h) * kD;
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) qv[h][e] = qp[dmap(c, e)] * qscale2;
+    for (int k = 0; k < EPL / 8; ++k) {
+      const float4* q4 = reinterpret_cast<const float4*>(qp + dmap(c, 8 * k));
+      const float4 a = q4[0], bq = q4[1];
+      qv[h][8 * k + 0] = a.x * qscale2; qv[h][8 * k + 1] = a.y * qscale2;
+      qv[h][8 * k + 2] = a.z * qscale2; qv[h][8 * k + 3] = a.w * qscale2;
+      qv[h][8 * k + 4] = bq.x * qscale2; qv[h][8 * k + 5] = bq.y * qscale2;
+      qv[h][8 * k + 6] = bq.z * qscale2; qv[h][8 * k + 7] = bq.w * qscale2;
+    }
   }
   float m[G], l[G], o[G][EPL];
 #pragma unroll
@@ -207,47 +250,47 @@ decode_f16_kernel(const uint16_t* __restrict__ kc, const uint16_t* __restrict__ 
   const uint4* kbase = reinterpret_cast<const uint4*>(kc + bg * max_seq * kD);
   const uint4* vbase = reinterpret_cast<const uint4*>(vc + bg * max_seq * kD);
   const int32_t last = max(L - 1, 0);
-  struct Frag { uint4 k[NV], v[NV]; };
-  auto issue = [&](int32_t i, Frag& f, int32_t& nvalid) {
+  struct Frag { uint32_t k[NW], v[NW]; };
+  Cursor cur;
+  auto issue = [&](Frag& f, int32_t& nvalid) {
     int32_t r0;
-    pt.step(i, r0, nvalid);
+    cur.next(pt, r0, nvalid);
     const int32_t row = min(r0 + rsub, last);
     const uint4* kp = kbase + int64_t(row) * (kD / 8);
     const uint4* vp = vbase + int64_t(row) * (kD / 8);
 #pragma unroll
-    for (int v = 0; v < NV; ++v) { f.k[v] = kp[c + LPR * v]; f.v[v] = vp[c + LPR * v]; }
+    for (int v = 0; v < NV; ++v) {
+      const uint4 a = kp[c + LPR * v], bb = vp[c + LPR * v];
+      f.k[4 * v] = a.x; f.k[4 * v + 1] = a.y; f.k[4 * v + 2] = a.z; f.k[4 * v + 3] = a.w;
+      f.v[4 * v] = bb.x; f.v[4 * v + 1] = bb.y; f.v[4 * v + 2] = bb.z; f.v[4 * v + 3] = bb.w;
+    }
   };
 
   Frag ring[P];
   int32_t rnv[P];
 #pragma unroll
   for (int p = 0; p < P; ++p)
-    if (p < n_steps) issue(p, ring[p], rnv[p]);
+    if (p < n_steps) issue(ring[p], rnv[p]);
 
   for (int32_t base = 0; base < n_steps; base += P) {
 #pragma unroll
     for (int p = 0; p < P; ++p) {
       const int32_t i = base + p;
       if (i < n_steps) {
-        const Frag f = ring[p];
         const bool valid = rsub < rnv[p];
-        if (i + P < n_steps) issue(i + P, ring[p], rnv[p]);
-        uint32_t kw[NW], vw[NW];
-#pragma unroll
-        for (int v = 0; v < NV; ++v) {
-          kw[4 * v] = f.k[v].x; kw[4 * v + 1] = f.k[v].y; kw[4 * v + 2] = f.k[v].z; kw[4 * v + 3] = f.k[v].w;
-          vw[4 * v] = f.v[v].x; vw[4 * v + 1] = f.v[v].y; vw[4 * v + 2] = f.v[v].z; vw[4 * v + 3] = f.v[v].w;
-        }
-        auto kget = [&](int e) { return (e & 1) ? h2f_hi(kw[e >> 1]) : h2f_lo(kw[e >> 1]); };
-        auto vget = [&](int e) { return (e & 1) ? h2f_hi(vw[e >> 1]) : h2f_lo(vw[e >> 1]); };
+        const Frag& f = ring[p];
+        auto kget = [&](int e) { return (e & 1) ? h2f_hi(f.k[e >> 1]) : h2f_lo(f.k[e >> 1]); };
+        auto vget = [&](int e) { return (e & 1) ? h2f_hi(f.v[e >> 1]) : h2f_lo(f.v[e >> 1]); };
+        float sc[G];
 #pragma unroll
         for (int h = 0; h < G; ++h) {
           float acc = 0.0f;
 #pragma unroll
           for (int e = 0; e < EPL; ++e) acc = fmaf(qv[h][e], kget(e), acc);
-          const float s = group_sum<LPR>(acc);
-          softmax_row<EPL>(s, valid, 1.0f, m[h], l[h], o[h], vget);
+          sc[h] = group_sum<LPR>(acc);
         }
+        softmax_rows<G, EPL, false>(sc, valid, 1.0f, m, l, o, vget);
+        if (i + P < n_steps) issue(ring[p], rnv[p]);
       }
     }
   }
@@ -291,14 +334,14 @@ decode_i8_kernel(const int8_t* __restrict__ kc, const int8_t* __restrict__ vc,
     const float2 two = reinterpret_cast<const float2*>(qp)[lane];
     const float a = wave_max(fmaxf(fabsf(two.x), fabsf(two.y)));
     const float qs = absmax_scale(a);
+    const float4* q4 = reinterpret_cast<const float4*>(qp + dmap(c, 0));
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
-      uint32_t packed = 0;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int code = quant_code(qp[dmap(c, 4 * w + e)], qs);
-        packed |= (uint32_t(code) & 0xFFu) << (8 * e);
-      }
+      const float4 x = q4[w];
+      const uint32_t packed = (uint32_t(quant_code(x.x, qs)) & 0xFFu) |
+                              ((uint32_t(quant_code(x.y, qs)) & 0xFFu) << 8) |
+                              ((uint32_t(quant_code(x.z, qs)) & 0xFFu) << 16) |
+                              ((uint32_t(quant_code(x.w, qs)) & 0xFFu) << 24);
       qc[h][w] = int32_t(packed);
     }
     coef[h] = qs * scale2;
@@ -317,9 +360,10 @@ decode_i8_kernel(const int8_t* __restrict__ kc, const int8_t* __restrict__ vc,
   const float* vsb = vsc + bg * max_seq;
   const int32_t last = max(L - 1, 0);
   struct Frag { uint32_t k[NW], v[NW]; float ks, vs; int32_t row; };
-  auto issue = [&](int32_t i, Frag& f, int32_t& nvalid) {
+  Cursor cur;
+  auto issue = [&](Frag& f, int32_t& nvalid) {
     int32_t r0;
-    pt.step(i, r0, nvalid);
+    cur.next(pt, r0, nvalid);
     const int32_t row = min(r0 + rsub, last);
     f.row = r0 + rsub;
     const int8_t* kp = kbase + int64_t(row) * kD + EPL * c;
@@ -341,17 +385,17 @@ decode_i8_kernel(const int8_t* __restrict__ kc, const int8_t* __restrict__ vc,
   int32_t rnv[P];
 #pragma unroll
   for (int p = 0; p < P; ++p)
-    if (p < n_steps) issue(p, ring[p], rnv[p]);
+    if (p < n_steps) issue(ring[p], rnv[p]);
 
   for (int32_t base = 0; base < n_steps; base += P) {
 #pragma unroll
     for (int p = 0; p < P; ++p) {
       const int32_t i = base + p;
       if (i < n_steps) {
-        const Frag f = ring[p];
+        const Frag& f = ring[p];
         const bool valid = rsub < rnv[p];
-        if (i + P < n_steps) issue(i + P, ring[p], rnv[p]);
         auto vget = [&](int e) { return float(int8_t((f.v[e >> 2] >> (8 * (e & 3))) & 0xFFu)); };
+        float sc[G];
 #pragma unroll
         for (int h = 0; h < G; ++h) {
           int32_t dot = 0;
@@ -361,9 +405,10 @@ decode_i8_kernel(const int8_t* __restrict__ kc, const int8_t* __restrict__ vc,
           dot = group_sum_i<LPR>(dot);
           if (dbg != nullptr && valid && c == 0)
             dbg[(int64_t(b) * H + g * G + h) * max_len + f.row] = dot;
-          const float s = float(dot) * coef[h] * f.ks;
-          softmax_row<EPL>(s, valid, f.vs, m[h], l[h], o[h], vget);
+          sc[h] = float(dot) * coef[h] * f.ks;
         }
+        softmax_rows<G, EPL, true>(sc, valid, f.vs, m, l, o, vget);
+        if (i + P < n_steps) issue(ring[p], rnv[p]);
       }
     }
   }
@@ -387,15 +432,15 @@ void launch_decode_g(const DecodeParams& p, hipStream_t stream) {
   }
   dim3 grid(S, c.n_kv_heads, B);
   const float scale2 = p.softmax_scale * kLog2e;
-  constexpr int LPR = G <= 4 ? 8 : 16;
+  constexpr int LPR = G <= 2 ? 8 : 16;
   if (c.kv_dtype == SKV_F16) {
-    constexpr int P = LPR == 8 ? 3 : 6;
+    constexpr int P = LPR == 8 ? 4 : 5;
     decode_f16_kernel<G, LPR, P><<<grid, kDecThreads, 0, stream>>>(
         static_cast<const uint16_t*>(c.k), static_cast<const uint16_t*>(c.v), p.q, p.seq_len,
         p.sel_idx, p.sel_cnt, p.max_sel, c.n_kv_heads, c.max_seq, c.block, p.max_len, S, ups,
         scale2, ws_m, ws_l, ws_o);
   } else {
-    constexpr int P = LPR == 8 ? 5 : 8;
+    constexpr int P = LPR == 8 ? 6 : 8;
     decode_i8_kernel<G, LPR, P><<<grid, kDecThreads, 0, stream>>>(
         static_cast<const int8_t*>(c.k), static_cast<const int8_t*>(c.v), c.k_scale, c.v_scale,
         p.q, p.seq_len, p.sel_idx, p.sel_cnt, p.max_sel, c.n_kv_heads, c.max_seq, c.block,
@@ -406,6 +451,7 @@ void launch_decode_g(const DecodeParams& p, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
+  if (launch_decode_mfma(p, stream)) return hipGetLastError();
   switch (p.n_heads / p.c->n_kv_heads) {
     case 1: launch_decode_g<1>(p, stream); break;
     case 2: launch_decode_g<2>(p, stream); break;

@@ -1,0 +1,367 @@
+// decode_attn on the matrix cores (gfx950 MFMA).
+//
+// The per-step contractions of decode attention for one KV head are small
+// dense products: S = K_tile q^T (tokens x GQA heads, reduced over the head
+// dimension) and O += P V_tile (heads x channels, reduced over tokens).  Both
+// run on MFMA; the vector ALUs only do the online softmax.  The query heads of
+// a GQA group fill the N = 16 columns of the MFMA tile (zero-padded past G),
+// so every K/V byte is read once for the whole group.
+//
+// Layouts (verified lane maps of the gfx950 instructions):
+//   v_mfma_f32_16x16x32_f16 / _16x16x16f16 / _i32_16x16x64_i8:
+//     A: lane l holds row l%16, k-chunk l/16;  B: column l%16, k-chunk l/16;
+//     C: column l%16, rows 4*(l/16) .. +3.
+//   ds_read_b64_tr_b16: in each 16-lane group, lane j receives element j%4 of
+//     the 4-element rows read by lanes j/4, 4+j/4, 8+j/4, 12+j/4.
+//   ds_read_b64_tr_b8: lane j receives byte j%8 of the 8-byte rows read by
+//     lanes j/8, 2+j/8, ..., 14+j/8.
+//
+// Data flow per wavefront and tile (f16: 16 tokens, int8: 32 tokens):
+//   global -> registers: coalesced 16-byte loads, 4 rows per instruction,
+//     prefetched P tiles ahead (register ring);
+//   registers -> LDS: row-major tile with the 16-byte chunks of row r XOR-
+//     swizzled by r % 16, so both the row reads of the q.K operand and the
+//     transposing reads of the P.V operand are free of bank conflicts;
+//   q.K: A = K rows from LDS, B = query (f16: split into an f16 high and low
+//     part, two MFMAs, ~22-bit query precision; int8: the absmax codes, an
+//     exact int32 product);
+//   softmax: per-head tile max across the 4 lane groups, running max/mass,
+//     one rescale of the accumulators per tile;
+//   P.V: A = P (f16 high + low parts, straight from the q.K output registers),
+//     B = V^T via the transposing LDS read (int8 codes widened to f16, exact).
+#include <type_traits>
+
+#include "device_common.h"
+#include "launch.h"
+
+namespace skv {
+namespace {
+
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef int int4_t __attribute__((ext_vector_type(4)));
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef int int2_t __attribute__((ext_vector_type(2)));
+#define SKV_LDS __attribute__((address_space(3)))
+
+constexpr int kMWaves = 4;
+constexpr int kMThreads = kMWaves * kWave;
+constexpr int kD = 128;
+constexpr int kRowBytesF16 = kD * 2;   // 256
+constexpr int kRowBytesI8 = kD;        // 128
+
+__device__ __forceinline__ int swz(int row) { return row & 15; }
+
+__device__ __forceinline__ float4_t mfma_f16_32(half8_t a, half8_t b, float4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ float4_t mfma_f16_16(half4_t a, half4_t b, float4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+}
+
+// Tile walk of one wavefront: tiles w, w + kMWaves, ... of the part's
+// sequence of T-row tiles (each block holds block / T tiles).
+struct TileWalk {
+  const int32_t* sel;
+  int32_t jl, u0, n_units, tpb, block, L, nb;
+  int32_t unit, sub;
+
+  __device__ __forceinline__ void init(int w) {
+    unit = w / tpb;
+    sub = w - unit * tpb;
+  }
+  __device__ __forceinline__ bool more() const { return unit < n_units; }
+  // first row and valid-row count of the current tile, then advance by kMWaves tiles
+  template <int T>
+  __device__ __forceinline__ void next(int32_t& r0, int32_t& nvalid) {
+    int32_t j = u0 + unit;
+    if (sel != nullptr) j = unit < kWave ? __builtin_amdgcn_readlane(jl, unit) : sel[j];
+    if (j < 0 || j >= nb) {
+      r0 = 0;
+      nvalid = 0;
+    } else {
+      r0 = j * block + sub * T;
+      nvalid = min(min(T, block - sub * T), L - r0);
+    }
+    sub += kMWaves;
+    while (sub >= tpb) { sub -= tpb; ++unit; }
+  }
+};
+
+template <int T>
+__device__ __forceinline__ TileWalk make_walk(const int32_t* sel_idx, const int32_t* sel_cnt,
+                                              int32_t max_sel, int64_t bg, int32_t L,
+                                              int32_t block, int32_t split,
+                                              int32_t units_per_split) {
+  TileWalk tw;
+  tw.block = block;
+  tw.L = L;
+  tw.nb = (L + block - 1) / block;
+  tw.tpb = block / T;
+  int32_t total = tw.nb;
+  tw.sel = nullptr;
+  tw.jl = -1;
+  if (sel_idx != nullptr) {
+    tw.sel = sel_idx + bg * max_sel;
+    total = min(max(sel_cnt[bg], 0), max_sel);
+  }
+  tw.u0 = split * units_per_split;
+  tw.n_units = max(0, min(units_per_split, total - tw.u0));
+  if (tw.sel != nullptr) {
+    const int lane = threadIdx.x % kWave;
+    if (lane < tw.n_units) tw.jl = tw.sel[tw.u0 + lane];
+  }
+  return tw;
+}
+
+// Softmax bookkeeping of one tile for the 16 MFMA columns (heads): lane l
+// owns head l%16 and rows 4*(l/16) + r of the tile.  s[r] are base-2 logits
+// (-inf for masked rows); returns the weights p[r] and rescales O.
+template <int NT>
+__device__ __forceinline__ void tile_softmax(float (&s)[4 * NT], float& m_run, float& l_run,
+                                             float4_t (&O)[8]) {
+  const int lane = threadIdx.x % kWave;
+  float mx = s[0];
+#pragma unroll
+  for (int i = 1; i < 4 * NT; ++i) mx = fmaxf(mx, s[i]);
+  mx = fmaxf(mx, __shfl_xor(mx, 16));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  const float m_new = fmaxf(m_run, mx);
+  const bool live = m_new != -INFINITY;
+  const float cr = (live && m_run != -INFINITY) ? __builtin_amdgcn_exp2f(m_run - m_new)
+                                                : (live ? 0.0f : 1.0f);
+  float ps = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4 * NT; ++i) {
+    s[i] = (s[i] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(s[i] - m_new);
+    ps += s[i];
+  }
+  ps += __shfl_xor(ps, 16);
+  ps += __shfl_xor(ps, 32);
+  l_run = l_run * cr + ps;
+  m_run = m_new;
+  // O rows are heads 4*(lane/16) + r; their factors live in lanes 4*(lane/16) + r
+  const int g4 = 4 * (lane / 16);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const float c = __shfl(cr, g4 + r);
+#pragma unroll
+    for (int n = 0; n < 8; ++n) O[n][r] *= c;
+  }
+}
+
+__device__ __forceinline__ void split_hi_lo4(const float* p, half4_t& hi, half4_t& lo) {
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const _Float16 h = (_Float16)p[s];
+    hi[s] = h;
+    lo[s] = (_Float16)(p[s] - (float)h);
+  }
+}
+
+// Merge the 4 wavefronts' states (heads < G) through LDS and write the
+// part's partial softmax state.
+template <int G>
+__device__ __forceinline__ void finish_mfma(float m_run, float l_run, const float4_t (&O)[8],
+                                            float* lds, float* __restrict__ ws_m,
+                                            float* __restrict__ ws_l, float* __restrict__ ws_o,
+                                            int64_t head0, int32_t n_split, int32_t split) {
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  float* lo = lds;                          // [waves][G][D]
+  float* lm = lds + kMWaves * G * kD;       // [waves][G]
+  float* ll = lm + kMWaves * G;
+  __syncthreads();                          // tile buffers are reused
+  const int g4 = 4 * (lane / 16);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int h = g4 + r;
+    if (h < G) {
+#pragma unroll
+      for (int n = 0; n < 8; ++n) lo[(wave * G + h) * kD + 16 * n + lane % 16] = O[n][r];
+    }
+  }
+  if (lane < G) { lm[wave * G + lane] = m_run; ll[wave * G + lane] = l_run; }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < G * kD; idx += kMThreads) {
+    const int h = idx / kD, d = idx % kD;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kMWaves; ++w) M = fmaxf(M, lm[w * G + h]);
+    float so = 0.0f, sl = 0.0f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < kMWaves; ++w) {
+        const float mw = lm[w * G + h];
+        const float a = (mw == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mw - M);
+        so += a * lo[(w * G + h) * kD + d];
+        sl += a * ll[w * G + h];
+      }
+    }
+    const int64_t ps = (head0 + h) * n_split + split;
+    ws_o[ps * kD + d] = so;
+    if (d == 0) { ws_m[ps] = M; ws_l[ps] = sl; }
+  }
+}
+
+// ------------------------------------------------------------------ f16
+// Tile = 16 tokens: K and V tiles are 4 KiB each (4 load instructions).
+template <int G, int P>
+__global__ void __launch_bounds__(kMThreads, 2)
+decode_f16_mfma(const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
+                const float* __restrict__ q, const int32_t* __restrict__ seq_len,
+                const int32_t* __restrict__ sel_idx, const int32_t* __restrict__ sel_cnt,
+                int32_t max_sel, int32_t Hkv, int32_t max_seq, int32_t block, int32_t max_len,
+                int32_t n_split, int32_t units_per_split, float qscale2,
+                float* __restrict__ ws_m, float* __restrict__ ws_l, float* __restrict__ ws_o) {
+  constexpr int T = 16;
+  constexpr int kTileBytes = T * kRowBytesF16;              // 4096
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kMWaves][2][2 * kTileBytes];
+  const int32_t split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int lg = lane / 16, lc = lane % 16;
+  const int32_t H = Hkv * G;
+  const int32_t L = min(max(seq_len[b], 0), max_len);
+  const int64_t bg = int64_t(b) * Hkv + g;
+  TileWalk tw = make_walk<T>(sel_idx, sel_cnt, max_sel, bg, L, block, split, units_per_split);
+  tw.init(wave);
+
+  // query as the B operand of q.K: column = head lc, k-chunk = lg; f16 hi + lo
+  half8_t qhi[4], qlo[4];
+  {
+    const bool hv = lc < G;
+    const float* qp = q + (int64_t(b) * H + g * G + (hv ? lc : 0)) * kD;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const float4 a = *reinterpret_cast<const float4*>(qp + 32 * kk + 8 * lg);
+      const float4 c = *reinterpret_cast<const float4*>(qp + 32 * kk + 8 * lg + 4);
+      const float x[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const float v = hv ? x[s] * qscale2 : 0.0f;
+        const _Float16 h = (_Float16)v;
+        qhi[kk][s] = h;
+        qlo[kk][s] = (_Float16)(v - (float)h);
+      }
+    }
+  }
+  float m_run = -INFINITY, l_run = 0.0f;
+  float4_t O[8];
+#pragma unroll
+  for (int n = 0; n < 8; ++n) O[n] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+  const uint8_t* kbase = reinterpret_cast<const uint8_t*>(kc + bg * int64_t(max_seq) * kD);
+  const uint8_t* vbase = reinterpret_cast<const uint8_t*>(vc + bg * int64_t(max_seq) * kD);
+  const int32_t last = max(L - 1, 0);
+  struct Frag { int4_t k[4], v[4]; int32_t nvalid; };
+  // lane loads row 4*i + lane/16 (i = 0..3) of the tile, 16-byte chunk lane%16
+  auto issue = [&](Frag& f) {
+    int32_t r0, nv;
+    tw.next<T>(r0, nv);
+    f.nvalid = nv;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int32_t row = min(r0 + 4 * i + lg, last);
+      const int64_t off = int64_t(row) * kRowBytesF16 + 16 * lc;
+      f.k[i] = *reinterpret_cast<const int4_t*>(kbase + off);
+      f.v[i] = *reinterpret_cast<const int4_t*>(vbase + off);
+    }
+  };
+
+  // Process one tile held in registers: stage it in LDS buffer `buf`, refill
+  // the fragment with the tile two steps ahead, then q.K, softmax and P.V.
+  auto process = [&](auto bufc, Frag& fr, bool& have) {
+    constexpr int kBuf = decltype(bufc)::value;
+    uint8_t* kt = smem[wave][kBuf];
+    uint8_t* vt = kt + kTileBytes;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 4 * i + lg;
+      const int off = row * kRowBytesF16 + 16 * (lc ^ swz(row));
+      *reinterpret_cast<int4_t*>(kt + off) = fr.k[i];
+      *reinterpret_cast<int4_t*>(vt + off) = fr.v[i];
+    }
+    const int32_t nvalid = fr.nvalid;
+    have = tw.more();
+    if (have) issue(fr);
+    // LDS writes above and reads below touch the same array: they stay in
+    // program order, and LDS executes one wavefront's accesses in order.
+    // q.K: A = K row lc, logical chunk lg + 4kk
+    float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const half8_t a = *reinterpret_cast<const half8_t*>(
+          kt + lc * kRowBytesF16 + 16 * ((lg + 4 * kk) ^ swz(lc)));
+      acc = mfma_f16_32(a, qhi[kk], acc);
+      acc = mfma_f16_32(a, qlo[kk], acc);
+    }
+    float sc[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sc[r] = (4 * lg + r < nvalid) ? acc[r] : -INFINITY;
+    tile_softmax<1>(sc, m_run, l_run, O);
+    half4_t phi, plo;
+    split_hi_lo4(sc, phi, plo);
+    // P.V: B = V^T rows 4lg..4lg+3 via the transposing read; 16 channels per n
+    const int tr_row = 4 * lg + (lc >> 2);
+#pragma unroll
+    for (int n = 0; n < 8; ++n) {
+      const int chunk = 2 * n + ((lc & 3) >> 1);
+      const int off = tr_row * kRowBytesF16 + 16 * (chunk ^ swz(tr_row)) + 8 * (lc & 1);
+      const short4_t raw =
+          __builtin_amdgcn_ds_read_tr16_b64_v4i16((SKV_LDS short4_t*)(vt + off));
+      const half4_t bv = __builtin_bit_cast(half4_t, raw);
+      O[n] = mfma_f16_16(phi, bv, O[n]);
+      O[n] = mfma_f16_16(plo, bv, O[n]);
+    }
+  };
+
+  Frag f0, f1;
+  bool h0 = tw.more();
+  if (h0) issue(f0);
+  bool h1 = tw.more();
+  if (h1) issue(f1);
+  while (h0) {
+    process(std::integral_constant<int, 0>{}, f0, h0);
+    if (!h1) break;
+    process(std::integral_constant<int, 1>{}, f1, h1);
+  }
+  finish_mfma<G>(m_run, l_run, O, reinterpret_cast<float*>(&smem[0][0][0]), ws_m, ws_l, ws_o,
+                 int64_t(b) * H + g * G, n_split, split);
+}
+
+}  // namespace
+
+bool launch_decode_mfma(const DecodeParams& p, hipStream_t stream) {
+  const skv_cache& c = *p.c;
+  if (c.kv_dtype != SKV_F16 || c.block % 16 != 0) return false;
+  const int32_t B = c.batch, H = p.n_heads, S = p.n_split;
+  const int G = H / c.n_kv_heads;
+  float* ws_m = p.ws + ws_m_offset(B, H, S);
+  float* ws_l = p.ws + ws_l_offset(B, H, S);
+  float* ws_o = p.ws + ws_o_offset(B, H, S);
+  int32_t ups;
+  if (p.sel_idx != nullptr) {
+    ups = (p.max_sel + S - 1) / S;
+  } else {
+    const int32_t nb_max = (p.max_len + c.block - 1) / c.block;
+    ups = (nb_max + S - 1) / S;
+  }
+  dim3 grid(S, c.n_kv_heads, B);
+  const float scale2 = p.softmax_scale * kLog2e;
+#define SKV_LAUNCH_F16(GG)                                                                      \
+  decode_f16_mfma<GG, 2><<<grid, kMThreads, 0, stream>>>(                                      \
+      static_cast<const uint16_t*>(c.k), static_cast<const uint16_t*>(c.v), p.q, p.seq_len,    \
+      p.sel_idx, p.sel_cnt, p.max_sel, c.n_kv_heads, c.max_seq, c.block, p.max_len, S, ups,    \
+      scale2, ws_m, ws_l, ws_o)
+  switch (G) {
+    case 1: SKV_LAUNCH_F16(1); break;
+    case 2: SKV_LAUNCH_F16(2); break;
+    case 4: SKV_LAUNCH_F16(4); break;
+    case 8: SKV_LAUNCH_F16(8); break;
+    default: return false;
+  }
+#undef SKV_LAUNCH_F16
+  return true;
+}
+
+}  // namespace skv
