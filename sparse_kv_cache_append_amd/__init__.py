@@ -196,7 +196,7 @@ def combine(workspace, batch: int, n_heads: int, head_dim: int, n_split: int, ou
         _stream(stream)))
 
 
-def default_split(batch: int, n_kv_heads: int, n_units: int, target_wgs: int = 1024) -> int:
+def default_split(batch: int, n_kv_heads: int, n_units: int, target_wgs: int = 256) -> int:
     """Parts per (sequence, KV head) so the grid has about ``target_wgs``
     workgroups, at least one block (or selected entry) per part."""
     n = max(1, math.ceil(target_wgs / max(1, batch * n_kv_heads)))

@@ -52,4 +52,5 @@ inline size_t ws_m_offset(int32_t, int32_t, int32_t) { return 0; }
 inline size_t ws_l_offset(int32_t B, int32_t H, int32_t S) { return size_t(B) * H * S; }
 inline size_t ws_o_offset(int32_t B, int32_t H, int32_t S) { return 2 * size_t(B) * H * S; }
 
+
 }  // namespace skv

@@ -178,13 +178,15 @@ hipError_t launch_select(const float* score, const int32_t* seq_len, int32_t bat
                          int32_t max_sel, int32_t* sel_idx, int32_t* sel_cnt,
                          uint32_t* sel_mask, hipStream_t stream) {
   const size_t lds = (size_t(max_blocks) + (max_blocks + 31) / 32) * sizeof(uint32_t);
-  static bool attr_set = false;
-  if (!attr_set) {
+  static bool attr_set[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
+  if (dev >= 0 && dev < 64 && !attr_set[dev]) {
     const size_t most = (size_t(kMaxSelectBlocks) + kMaxSelectBlocks / 32) * sizeof(uint32_t);
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&select_kernel),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, int(most));
     if (e != hipSuccess) return e;
-    attr_set = true;
+    attr_set[dev] = true;
   }
   dim3 grid(n_kv_heads, batch);
   select_kernel<<<grid, kSelThreads, lds, stream>>>(score, seq_len, n_kv_heads, max_blocks, block,

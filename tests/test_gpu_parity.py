@@ -395,3 +395,48 @@ def test_decode_helper_chains_the_calls(gpu_lib):
                                 w.softmax_scale, tokens=toks)
         if len(r["near"]) == 0:
             assert rel_err(outq[0, 4 * g:4 * g + 4], ref) < F16_TOL
+
+
+# ------------------------------------------------------------------ HIP graphs
+def test_step_replays_in_a_hip_graph(gpu_lib):
+    """A captured decode step (append + bounds + select + decode + combine)
+    replayed several times, with eager work between replays, gives the eager
+    result every time."""
+    _print("graph replay")
+    w = workloads.clustered([93], 32, 8, 128, [2048], "f16", n_dirs=16, k_sel=[8])
+    cache = build_cache(w, max_seq=2048)
+    q, seq_len = device_inputs(w)
+    L = 2048
+    from gpu_harness import padded_rows
+    k, v = padded_rows(w, L)
+    nk = torch.from_numpy(k[:, L - 1:L].copy()).to(DEV)
+    nv = torch.from_numpy(v[:, L - 1:L].copy()).to(DEV)
+    pos = torch.full((1,), L - 1, dtype=torch.int32, device=DEV)
+    ks = torch.tensor([8], dtype=torch.int32, device=DEV)
+    score = torch.empty((1, 8, cache.max_blocks), device=DEV)
+    sel = torch.empty((1, 8, 11), dtype=torch.int32, device=DEV)
+    cnt = torch.empty((1, 8), dtype=torch.int32, device=DEV)
+    S = 4
+    ws = torch.empty(skv.workspace_bytes(1, 32, 128, S), dtype=torch.uint8, device=DEV)
+    out = torch.empty((1, 32, 128), device=DEV)
+
+    def step():
+        skv.kv_append(cache, pos, nk, nv)
+        skv.block_bounds(cache, q, seq_len, L, score)
+        skv.select_topk(score, seq_len, 64, ks, 1, 2, sel, cnt)
+        skv.decode_attn(cache, q, seq_len, L, w.softmax_scale, S, ws, sel, cnt)
+        skv.combine(ws, 1, 32, 128, S, out)
+
+    step()
+    torch.cuda.synchronize()
+    eager = out.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for i in range(4):
+        out.zero_()
+        junk = torch.randn(1 << 20, device=DEV).sum()   # eager work between replays
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), i
+        assert float(junk) == float(junk)
