@@ -75,6 +75,39 @@ def step_bytes(lens, Hkv, H, D, kv_dtype, block, attended_blocks=None):
     return {"kv": kv, "bounds": bounds, "q_out": q_out, "total": kv + bounds + q_out}
 
 
+# ------------------------------------------------------------- HBM traffic
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic_quest32k.txt")
+KERNEL_SOURCES = [os.path.join(ROOT, "sparse_kv_cache_append_amd", "csrc", f)
+                  for f in ("decode_mfma.hip", "device_common.h", "launch.h")]
+
+
+def kernel_source_digest() -> str:
+    """sha256 over the sources the decode kernel is compiled from."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
+
+
+def recorded_traffic(kernel: str):
+    """HBM bytes per launch of the timed kernel from the committed rocprofv3
+    counter summary (FETCH_SIZE + WRITE_SIZE, scaled by the copy-kernel
+    factors recorded there), or None when the summary is missing, is for
+    another kernel, or the kernel source changed since it was taken."""
+    try:
+        fields = {}
+        for line in open(TRAFFIC_FILE):
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip()
+        if fields.get("kernel_source_sha256") != kernel_source_digest() or fields.get("kernel") != kernel:
+            return None
+        return int(float(fields["traffic_bytes_per_launch"]))
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 # ------------------------------------------------------------- cpu baseline
 def cpu_baseline(w, budget_s: float = 12.0):
     """The oracle's Quest step (append the token, bounds, selection, sparse
@@ -136,6 +169,11 @@ def main():
     ap.add_argument("--n-split", type=int, default=0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--mode", choices=("both", "quest", "dense"), default="both",
+                    help="which step to time (profiling runs use one)")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="after timing, copy a buffer of this many MiB three times "
+                         "(a plain copy of known size that scales HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the path has no "
@@ -226,13 +264,16 @@ def main():
         return (time.perf_counter() - t0) / (reps * R), reps * R
 
     K, W = args.steps, args.warmup
-    quest_stream = time_stream(quest_step, K, W)
-    dense_stream = time_stream(dense_step, K, W)
+    do_q, do_d = args.mode in ("both", "quest"), args.mode in ("both", "dense")
+    quest_stream = time_stream(quest_step, K, W) if do_q else None
+    dense_stream = time_stream(dense_step, K, W) if do_d else None
     quest_graph = dense_graph = None
     steps_done = K
     if not args.no_graph:
-        quest_graph, steps_done = time_graph(quest_step, K, W)
-        dense_graph, _ = time_graph(dense_step, K, W)
+        if do_q:
+            quest_graph, steps_done = time_graph(quest_step, K, W)
+        if do_d:
+            dense_graph, steps_done = time_graph(dense_step, K, W)
 
     # selected sets of this workload (for the byte accounting)
     quest_step(0)
@@ -247,6 +288,17 @@ def main():
     # HIP events on the replay stream bracket K launches
     def time_kernel(fn):
         st = torch.cuda.Stream()
+        if args.no_graph:
+            with torch.cuda.stream(st):
+                for i in range(R):
+                    fn(i)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(st)
+                for i in range(K):
+                    fn(i)
+                e1.record(st)
+            st.synchronize()
+            return e0.elapsed_time(e1) * 1e3 / K
         with torch.cuda.stream(st):
             for i in range(R):
                 fn(i)
@@ -266,51 +318,76 @@ def main():
         st.synchronize()
         return e0.elapsed_time(e1) * 1e3 / (reps * R)
 
-    dec_us = time_kernel(lambda i: skv.decode_attn(caches[i % R], q, seq_len, L, w.softmax_scale,
-                                                   S_q, ws_q, sel, cnt))
     dec_bytes = qb["kv"] + H * D * 4
-    dense_dec_us = time_kernel(lambda i: skv.decode_attn(caches[i % R], q, seq_len, L,
-                                                         w.softmax_scale, S_d, ws_d))
     dense_dec_bytes = db["kv"] + H * D * 4
+    dec_us = time_kernel(lambda i: skv.decode_attn(caches[i % R], q, seq_len, L, w.softmax_scale,
+                                                   S_q, ws_q, sel, cnt)) if do_q else None
+    dense_dec_us = time_kernel(lambda i: skv.decode_attn(caches[i % R], q, seq_len, L,
+                                                         w.softmax_scale, S_d, ws_d)) if do_d else None
 
-    quest_us = (quest_graph if quest_graph is not None else quest_stream) * 1e6
-    dense_us = (dense_graph if dense_graph is not None else dense_stream) * 1e6
-    gbps = qb["total"] / (quest_us * 1e-6) / 1e9
-    ach = dec_bytes / (dec_us * 1e-6) / 1e9
+    def us(graph_t, stream_t):
+        t = graph_t if graph_t is not None else stream_t
+        return None if t is None else t * 1e6
+
+    def rnd(x, n=3):
+        return None if x is None else round(x, n)
+
+    quest_us = us(quest_graph, quest_stream)
+    dense_us = us(dense_graph, dense_stream)
+    head_us = quest_us if quest_us is not None else dense_us
+    head_bytes = qb["total"] if quest_us is not None else db["total"]
+    gbps = head_bytes / (head_us * 1e-6) / 1e9
+    if dec_us is not None:
+        rk, rb, rus = "decode_f16_mfma (decode_attn over the selected blocks)", dec_bytes, dec_us
+    else:
+        rk, rb, rus = "decode_f16_mfma (decode_attn, dense)", dense_dec_bytes, dense_dec_us
+    ach = rb / (rus * 1e-6) / 1e9
+    traffic = recorded_traffic(rk)
     res = {
         "metric": METRIC,
-        "value": round(quest_us, 3),
+        "value": round(head_us, 3),
         "unit": "us/step",
         "n_gpus": 1,
         "steps": steps_done,
         "warmup": W,
-        "ms_per_step": round(quest_us / 1e3, 6),
+        "ms_per_step": round(head_us / 1e3, 6),
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f16",
         "data": "synthetic",
-        "config": {"workload": w.name, "step": "kv_append + block_bounds + select_topk + "
-                   "decode_attn(selected blocks) + combine", "cache_copies": R,
-                   "launch": "hipgraph" if quest_graph is not None else "stream",
-                   "n_split": S_q},
+        "config": {"workload": w.name,
+                   "step": ("kv_append + block_bounds + select_topk + decode_attn(selected blocks)"
+                            " + combine") if quest_us is not None else
+                           "kv_append + decode_attn(dense) + combine",
+                   "cache_copies": R,
+                   "launch": "hipgraph" if not args.no_graph else "stream",
+                   "n_split": S_q if quest_us is not None else S_d},
         "achieved_GBps": round(gbps, 1),
         "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
-        "bytes_per_step": qb,
-        "dense": {"us_per_step": round(dense_us, 3), "bytes_per_step": db,
-                  "achieved_GBps": round(db["total"] / (dense_us * 1e-6) / 1e9, 1),
-                  "pct_hbm_peak": round(100 * db["total"] / (dense_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 2),
-                  "n_split": S_d,
-                  "decode_attn_us": round(dense_dec_us, 3),
-                  "decode_attn_GBps": round(dense_dec_bytes / (dense_dec_us * 1e-6) / 1e9, 1)},
-        "quest_over_dense_time": round(quest_us / dense_us, 4),
-        "stream_launch_us": {"quest": round(quest_stream * 1e6, 3), "dense": round(dense_stream * 1e6, 3)},
+        "bytes_per_step": qb if quest_us is not None else db,
+        "dense": None if dense_us is None else {
+            "us_per_step": rnd(dense_us), "bytes_per_step": db,
+            "achieved_GBps": round(db["total"] / (dense_us * 1e-6) / 1e9, 1),
+            "pct_hbm_peak": round(100 * db["total"] / (dense_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 2),
+            "n_split": S_d, "decode_attn_us": rnd(dense_dec_us),
+            "decode_attn_GBps": round(dense_dec_bytes / (dense_dec_us * 1e-6) / 1e9, 1)},
+        "quest_over_dense_time": (round(quest_us / dense_us, 4)
+                                  if quest_us is not None and dense_us is not None else None),
+        "stream_launch_us": {"quest": rnd(None if quest_stream is None else quest_stream * 1e6),
+                             "dense": rnd(None if dense_stream is None else dense_stream * 1e6)},
         "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": None,
-                     "kernel": "decode_f16_mfma (decode_attn over the selected blocks)",
-                     "avg_launch_us": round(dec_us, 3),
-                     "bytes_per_launch": dec_bytes},
+                     "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                     "kernel": rk, "avg_launch_us": round(rus, 3), "bytes_per_launch": rb},
     }
+    if args.copy_probe_mib > 0:
+        a = torch.ones(args.copy_probe_mib * 2 ** 18, dtype=torch.float32, device=dev)
+        b2 = torch.empty_like(a)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            b2.copy_(a)
+        torch.cuda.synchronize()
+        res["copy_probe_bytes"] = {"read": a.numel() * 4, "written": a.numel() * 4}
     if not args.no_cpu:
         res["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(res), flush=True)

@@ -98,20 +98,22 @@ __device__ __forceinline__ TileWalk make_walk(const int32_t* sel_idx, const int3
   tw.block = block;
   tw.L = L;
   tw.nb = (L + block - 1) / block;
-  tw.tpb = block / T;
+  tw.tpb = (block + T - 1) / T;
   int32_t total = tw.nb;
   tw.sel = nullptr;
   tw.jl = -1;
-  if (sel_idx != nullptr) {
-    tw.sel = sel_idx + bg * max_sel;
-    total = min(max(sel_cnt[bg], 0), max_sel);
-  }
   tw.u0 = split * units_per_split;
-  tw.n_units = max(0, min(units_per_split, total - tw.u0));
-  if (tw.sel != nullptr) {
+  if (sel_idx != nullptr) {
+    // the count and this part's list entries are loaded together (one round
+    // trip); entries past the count are ignored through n_units
+    tw.sel = sel_idx + bg * max_sel;
     const int lane = threadIdx.x % kWave;
-    if (lane < tw.n_units) tw.jl = tw.sel[tw.u0 + lane];
+    const int32_t e = tw.u0 + lane;
+    const int32_t cnt = sel_cnt[bg];
+    if (lane < units_per_split && e < max_sel) tw.jl = tw.sel[e];
+    total = min(max(cnt, 0), max_sel);
   }
+  tw.n_units = max(0, min(units_per_split, total - tw.u0));
   return tw;
 }
 
