@@ -3,24 +3,26 @@
 A step is one pass of the whole hot path over one batch: append the new
 token (kv_append), Quest upper bounds (block_bounds), top-K selection
 (select_topk), attention over the selected blocks (decode_attn) and the
-split-K merge (combine).  The workload is the 32K-context GQA decode
-(B=1, H=32, Hkv=8, D=128, f16 KV, block 64, K_SEL=128 + sink + 2 recent);
-the same cache is also timed with dense decode (append + decode_attn +
-combine) for the sparse/dense ratio.
+split-K merge (combine).  The headline workload is the 32K-context GQA
+decode (B=1, H=32, Hkv=8, D=128, f16 KV, block 64, K_SEL=128 + sink + 2
+recent); the same cache is also timed with dense decode (append +
+decode_attn + combine) for the sparse/dense ratio.  The other named
+workloads (512-token dense f16, 8K int8, the 16-sequence 16K-64K batch,
+262K int8 Quest) are timed the same way and reported under "workloads".
 
 Timing protocol:
 * Inputs are resident in HBM before the timed region.
-* Cold cache: every step reads one of R cache copies, R chosen so the copies
-  a ring touches exceed 2x the 256 MB last-level cache, so steps read HBM.
-* W warmup steps, then exactly K timed steps between synchronizations;
-  the steps are captured once in a HIP graph (torch.cuda.CUDAGraph over the
-  library's launches on the capture stream) and replayed; the stream-launch
-  time is reported too.
-* The dominant kernel (decode_attn) is timed alone: R launches (one per cache
-  copy) captured in a HIP graph, replayed, HIP events on the replay stream;
-  achieved GB/s = algorithmic bytes per launch / average launch time.
+* Cold cache: step i reads copy i % R of the cache, R chosen so that R
+  consecutive steps touch more than twice the 256 MB last-level cache.
+* W warmup steps, then exactly K steps captured in one HIP graph
+  (torch.cuda.CUDAGraph over the library's launches), replayed once
+  untimed and once timed between synchronizations; the stream-launch time
+  of K eager steps is reported too.
+* The dominant kernel (decode_attn) is timed alone the same way (K launches
+  in one graph), with HIP events on the replay stream; achieved GB/s =
+  algorithmic bytes per launch / average launch time.
 
-Prints ONE JSON line (rank 0, one GPU).
+Prints ONE JSON line (one GPU).
 """
 from __future__ import annotations
 
@@ -160,17 +162,232 @@ def cpu_baseline(w, budget_s: float = 12.0):
 
 
 # ------------------------------------------------------------- GPU bench
+class Timer:
+    """Graph- and stream-timed replays of a step function f(i) over a ring of
+    R cache copies (step i reads copy i % R)."""
+
+    def __init__(self, torch, R, steps, warmup, use_graph):
+        self.torch, self.R, self.K, self.W, self.use_graph = torch, R, steps, warmup, use_graph
+
+    def stream(self, fn):
+        torch = self.torch
+        for i in range(self.W):
+            fn(i)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(self.K):
+            fn(i)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / self.K
+
+    def graph(self, fn):
+        """Wall time per step of exactly K steps captured in one HIP graph
+        (step i reads copy i % R), replayed once untimed, then once timed.
+        Returns (None, K) when graphs are off."""
+        if not self.use_graph:
+            return None, self.K
+        torch, R, K = self.torch, self.R, self.K
+        for i in range(max(self.W, R)):
+            fn(i)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(K):
+                fn(i)
+        g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        g.replay()
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t0) / K
+        del g
+        return dt, K
+
+    def kernel(self, fn):
+        """Average duration of one launch of fn, HIP events on the launch
+        stream around K launches (graph-replayed when graphs are on)."""
+        torch, R, K = self.torch, self.R, self.K
+        st = torch.cuda.Stream()
+        with torch.cuda.stream(st):
+            for i in range(R):
+                fn(i)
+        st.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        if not self.use_graph:
+            with torch.cuda.stream(st):
+                e0.record(st)
+                for i in range(K):
+                    fn(i)
+                e1.record(st)
+            st.synchronize()
+            return e0.elapsed_time(e1) * 1e3 / K
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=st):
+            for i in range(K):
+                fn(i)
+        with torch.cuda.stream(st):
+            g.replay()
+            e0.record(st)
+            g.replay()
+            e1.record(st)
+        st.synchronize()
+        del g
+        return e0.elapsed_time(e1) * 1e3 / K
+
+
+def padded_prefill(w, rows):
+    """[B][rows][Hkv][D] rows 0..L_b-2 of every sequence, padded past L_b - 2
+    with copies of that row (the pad never changes a block's min/max and is
+    never attended: positions >= L_b - 1 are rewritten or unread)."""
+    dt = np.float16 if w.kv_dtype == "f16" else np.float32
+    k = np.empty((w.B, rows, w.Hkv, w.D), dt)
+    v = np.empty((w.B, rows, w.Hkv, w.D), dt)
+    for b, L in enumerate(w.lens):
+        n = L - 1
+        k[b, :n] = np.transpose(w.k[b][:, :n], (1, 0, 2))
+        v[b, :n] = np.transpose(w.v[b][:, :n], (1, 0, 2))
+        k[b, n:] = k[b, n - 1]
+        v[b, n:] = v[b, n - 1]
+    return k, v
+
+
+def measure(w, args, quest: bool, dense: bool, detail: bool = False):
+    """Time the dense and/or Quest decode step of workload w on a cold ring of
+    cache copies.  Returns a dict of per-step figures (and, with detail, the
+    device state used for the roofline kernel timing)."""
+    import torch
+    import sparse_kv_cache_append_amd as skv
+    dev = torch.device("cuda:0")
+    B, H, Hkv, D, blk = w.B, w.H, w.Hkv, w.D, w.block
+    Lmax = max(w.lens)
+    src_dt = torch.float16 if w.kv_dtype == "f16" else torch.float32
+    base = skv.Cache(B, Hkv, Lmax, D, w.kv_dtype, blk, bounds=True, device=dev)
+    k0, v0 = padded_prefill(w, Lmax - 1)
+    skv.kv_append(base, torch.zeros(B, dtype=torch.int32, device=dev),
+                  torch.from_numpy(k0).to(dev), torch.from_numpy(v0).to(dev))
+    del k0, v0
+    new_k = torch.from_numpy(np.stack([w.k[b][:, L - 1] for b, L in enumerate(w.lens)])[:, None]
+                             .copy()).to(dev).to(src_dt).contiguous()
+    new_v = torch.from_numpy(np.stack([w.v[b][:, L - 1] for b, L in enumerate(w.lens)])[:, None]
+                             .copy()).to(dev).to(src_dt).contiguous()
+    pos_last = torch.tensor([L - 1 for L in w.lens], dtype=torch.int32, device=dev)
+    seq_len = torch.tensor(w.lens, dtype=torch.int32, device=dev)
+    q = torch.from_numpy(np.ascontiguousarray(w.q)).to(dev)
+    nb_max = -(-Lmax // blk)
+    per_tok = kv_bytes_per_token(w.kv_dtype, D)
+
+    k_sel = list(w.k_sel) if (quest and w.k_sel) else None
+    max_sel = (max(k_sel) + w.n_sink + w.n_recent) if k_sel else 0
+    # bytes one step touches; the ring is sized for the smaller step so that
+    # R consecutive steps of either kind exceed twice the last-level cache
+    touches = []
+    if dense:
+        touches.append(sum(w.lens) * Hkv * per_tok)
+    if k_sel:
+        touches.append(B * Hkv * max_sel * blk * per_tok + B * Hkv * nb_max * 512)
+    per_copy = sum(t.numel() * t.element_size() for t in
+                   (base.k, base.v, base.k_scale, base.v_scale, base.kmin, base.kmax)
+                   if t is not None)
+    R = args.ring or min(256, max(2, math.ceil(2 * LLC_BYTES / max(min(touches), 1)) + 1))
+    R = max(1, min(R, int(args.ring_budget_gb * 2 ** 30 // max(per_copy, 1))))
+    caches = [base] + [base.clone() for _ in range(R - 1)]
+    torch.cuda.synchronize()
+    T = Timer(torch, R, args.steps, args.warmup, not args.no_graph)
+    res = {"workload": w.name, "cache_copies": R}
+
+    if dense:
+        S_d = args.n_split or skv.default_split(B, Hkv, nb_max)
+        ws_d = torch.empty(skv.workspace_bytes(B, H, D, S_d), dtype=torch.uint8, device=dev)
+        out_d = torch.empty((B, H, D), dtype=torch.float32, device=dev)
+
+        def dense_step(i):
+            c = caches[i % R]
+            skv.kv_append(c, pos_last, new_k, new_v)
+            skv.decode_attn(c, q, seq_len, Lmax, w.softmax_scale, S_d, ws_d)
+            skv.combine(ws_d, B, H, D, S_d, out_d)
+
+        st = T.stream(dense_step)
+        gr, n = T.graph(dense_step)
+        us = (gr if gr is not None else st) * 1e6
+        dec_us = T.kernel(lambda i: skv.decode_attn(caches[i % R], q, seq_len, Lmax,
+                                                    w.softmax_scale, S_d, ws_d))
+        db = step_bytes(w.lens, Hkv, H, D, w.kv_dtype, blk, None)
+        dec_bytes = db["kv"] + B * H * D * 4
+        res["dense"] = {"us_per_step": round(us, 3), "stream_us_per_step": round(st * 1e6, 3),
+                        "steps": n, "n_split": S_d, "bytes_per_step": db["total"],
+                        "GBps": round(db["total"] / us / 1e3, 1),
+                        "pct_hbm_peak": round(100 * db["total"] / us / 1e3 / HBM_PEAK_GBPS, 2),
+                        "decode_attn_us": round(dec_us, 3),
+                        "decode_attn_GBps": round(dec_bytes / dec_us / 1e3, 1),
+                        "decode_attn_pct_peak": round(100 * dec_bytes / dec_us / 1e3
+                                                      / HBM_PEAK_GBPS, 2)}
+
+    if k_sel:
+        ks = torch.tensor(k_sel, dtype=torch.int32, device=dev)
+        score = torch.empty((B, Hkv, base.max_blocks), dtype=torch.float32, device=dev)
+        sel = torch.empty((B, Hkv, max_sel), dtype=torch.int32, device=dev)
+        cnt = torch.empty((B, Hkv), dtype=torch.int32, device=dev)
+        S_q = args.n_split or skv.default_split(B, Hkv, max_sel)
+        ws_q = torch.empty(skv.workspace_bytes(B, H, D, S_q), dtype=torch.uint8, device=dev)
+        out_q = torch.empty((B, H, D), dtype=torch.float32, device=dev)
+
+        def quest_step(i):
+            c = caches[i % R]
+            skv.kv_append(c, pos_last, new_k, new_v)
+            skv.block_bounds(c, q, seq_len, Lmax, score)
+            skv.select_topk(score, seq_len, blk, ks, w.n_sink, w.n_recent, sel, cnt)
+            skv.decode_attn(c, q, seq_len, Lmax, w.softmax_scale, S_q, ws_q, sel, cnt)
+            skv.combine(ws_q, B, H, D, S_q, out_q)
+
+        st = T.stream(quest_step)
+        gr, n = T.graph(quest_step)
+        us = (gr if gr is not None else st) * 1e6
+        quest_step(0)
+        torch.cuda.synchronize()
+        sel_h, cnt_h = sel.cpu().numpy(), cnt.cpu().numpy()
+        attended = {(b, g): sel_h[b, g, :cnt_h[b, g]].tolist() for b in range(B) for g in range(Hkv)}
+        qb = step_bytes(w.lens, Hkv, H, D, w.kv_dtype, blk, attended)
+        dec_bytes = qb["kv"] + B * H * D * 4
+        dec_us = T.kernel(lambda i: skv.decode_attn(caches[i % R], q, seq_len, Lmax,
+                                                    w.softmax_scale, S_q, ws_q, sel, cnt))
+        n_att = sum(len(x) for x in attended.values())
+        n_all = sum(-(-L // blk) for L in w.lens) * Hkv
+        res["quest"] = {"us_per_step": round(us, 3), "stream_us_per_step": round(st * 1e6, 3),
+                        "steps": n, "n_split": S_q, "bytes_per_step": qb["total"],
+                        "kv_bytes": qb["kv"], "bounds_bytes": qb["bounds"],
+                        "blocks_attended_frac": round(n_att / n_all, 4),
+                        "GBps": round(qb["total"] / us / 1e3, 1),
+                        "pct_hbm_peak": round(100 * qb["total"] / us / 1e3 / HBM_PEAK_GBPS, 2),
+                        "decode_attn_us": round(dec_us, 3),
+                        "decode_attn_GBps": round(dec_bytes / dec_us / 1e3, 1),
+                        "decode_attn_pct_peak": round(100 * dec_bytes / dec_us / 1e3
+                                                      / HBM_PEAK_GBPS, 2)}
+        if detail:
+            res["_roofline"] = (dec_bytes, dec_us)
+        if "dense" in res:
+            res["quest_over_dense"] = round(res["quest"]["us_per_step"]
+                                            / res["dense"]["us_per_step"], 4)
+    del caches
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--ring", type=int, default=0, help="cache copies (0 = auto, cold cache)")
+    ap.add_argument("--ring-budget-gb", type=float, default=24.0,
+                    help="upper bound on the memory of the cache copies of one workload")
     ap.add_argument("--n-split", type=int, default=0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--mode", choices=("both", "quest", "dense"), default="both",
-                    help="which step to time (profiling runs use one)")
+                    help="which step of the 32K workload to time (profiling runs use one)")
+    ap.add_argument("--workloads", default="1,2,4,5",
+                    help="other workloads to time besides the 32K headline ('' = none)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after timing, copy a buffer of this many MiB three times "
                          "(a plain copy of known size that scales HBM byte counters)")
@@ -185,203 +402,63 @@ def main():
     import workloads
 
     skv.load()
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    w = workloads.named(3)
-    B, H, Hkv, D, blk = w.B, w.H, w.Hkv, w.D, w.block
-    L = w.lens[0]
-    k_sel = w.k_sel[0]
-    max_sel = k_sel + w.n_sink + w.n_recent
-    nb = -(-L // blk)
-
-    # ring of cache copies, each holding L-1 tokens; every step appends token L-1
-    src_k = torch.from_numpy(np.ascontiguousarray(np.transpose(w.k[0], (1, 0, 2))[None])).to(dev)
-    src_v = torch.from_numpy(np.ascontiguousarray(np.transpose(w.v[0], (1, 0, 2))[None])).to(dev)
-    quest_touch = max_sel * blk * Hkv * kv_bytes_per_token("f16", D) + nb * Hkv * 512
-    R = args.ring or max(2, math.ceil(2 * LLC_BYTES / quest_touch) + 1)
-    caches = []
-    zero = torch.zeros(1, dtype=torch.int32, device=dev)
-    for _ in range(R):
-        c = skv.Cache(B, Hkv, L, D, "f16", blk, bounds=True, device=dev)
-        skv.kv_append(c, zero, src_k[:, :L - 1].contiguous(), src_v[:, :L - 1].contiguous())
-        caches.append(c)
-    new_k = src_k[:, L - 1:L].contiguous()
-    new_v = src_v[:, L - 1:L].contiguous()
-    pos_last = torch.full((B,), L - 1, dtype=torch.int32, device=dev)
-    q = torch.from_numpy(w.q).to(dev)
-    seq_len = torch.full((B,), L, dtype=torch.int32, device=dev)
-    ks = torch.full((B,), k_sel, dtype=torch.int32, device=dev)
-    score = torch.empty((B, Hkv, caches[0].max_blocks), dtype=torch.float32, device=dev)
-    sel = torch.empty((B, Hkv, max_sel), dtype=torch.int32, device=dev)
-    cnt = torch.empty((B, Hkv), dtype=torch.int32, device=dev)
-    S_q = args.n_split or skv.default_split(B, Hkv, max_sel)
-    S_d = args.n_split or skv.default_split(B, Hkv, nb)
-    ws_q = torch.empty(skv.workspace_bytes(B, H, D, S_q), dtype=torch.uint8, device=dev)
-    ws_d = torch.empty(skv.workspace_bytes(B, H, D, S_d), dtype=torch.uint8, device=dev)
-    out = torch.empty((B, H, D), dtype=torch.float32, device=dev)
-    torch.cuda.synchronize()
-
-    def quest_step(i):
-        c = caches[i % R]
-        skv.kv_append(c, pos_last, new_k, new_v)
-        skv.block_bounds(c, q, seq_len, L, score)
-        skv.select_topk(score, seq_len, blk, ks, w.n_sink, w.n_recent, sel, cnt)
-        skv.decode_attn(c, q, seq_len, L, w.softmax_scale, S_q, ws_q, sel, cnt)
-        skv.combine(ws_q, B, H, D, S_q, out)
-
-    def dense_step(i):
-        c = caches[i % R]
-        skv.kv_append(c, pos_last, new_k, new_v)
-        skv.decode_attn(c, q, seq_len, L, w.softmax_scale, S_d, ws_d)
-        skv.combine(ws_d, B, H, D, S_d, out)
-
-    def time_stream(fn, steps, warmup):
-        for i in range(warmup):
-            fn(i)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for i in range(steps):
-            fn(i)
-        torch.cuda.synchronize()
-        return (time.perf_counter() - t0) / steps
-
-    def time_graph(fn, steps, warmup):
-        for i in range(max(warmup, R)):
-            fn(i)
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for i in range(R):
-                fn(i)
-        for _ in range(2):
-            g.replay()
-        torch.cuda.synchronize()
-        reps = max(1, steps // R)
-        t0 = time.perf_counter()
-        for _ in range(reps):
-            g.replay()
-        torch.cuda.synchronize()
-        return (time.perf_counter() - t0) / (reps * R), reps * R
-
-    K, W = args.steps, args.warmup
+    torch.cuda.set_device(0)
+    w3 = workloads.named(3)
     do_q, do_d = args.mode in ("both", "quest"), args.mode in ("both", "dense")
-    quest_stream = time_stream(quest_step, K, W) if do_q else None
-    dense_stream = time_stream(dense_step, K, W) if do_d else None
-    quest_graph = dense_graph = None
-    steps_done = K
-    if not args.no_graph:
-        if do_q:
-            quest_graph, steps_done = time_graph(quest_step, K, W)
-        if do_d:
-            dense_graph, steps_done = time_graph(dense_step, K, W)
+    head = measure(w3, args, quest=do_q, dense=do_d, detail=True)
+    others = []
+    for tok in [t for t in args.workloads.split(",") if t.strip()]:
+        cfg = int(tok)
+        if cfg == 3:
+            continue
+        w = workloads.named(cfg)
+        others.append(measure(w, args, quest=bool(w.k_sel), dense=True))
+        del w
 
-    # selected sets of this workload (for the byte accounting)
-    quest_step(0)
-    torch.cuda.synchronize()
-    sel_h, cnt_h = sel.cpu().numpy(), cnt.cpu().numpy()
-    attended = {(0, g): sel_h[0, g, :cnt_h[0, g]].tolist() for g in range(Hkv)}
-    qb = step_bytes([L], Hkv, H, D, "f16", blk, attended)
-    db = step_bytes([L], Hkv, H, D, "f16", blk, None)
-
-    # dominant kernel alone: the fused decode over the selected blocks, R
-    # launches (one per cache copy) captured in a HIP graph and replayed;
-    # HIP events on the replay stream bracket K launches
-    def time_kernel(fn):
-        st = torch.cuda.Stream()
-        if args.no_graph:
-            with torch.cuda.stream(st):
-                for i in range(R):
-                    fn(i)
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record(st)
-                for i in range(K):
-                    fn(i)
-                e1.record(st)
-            st.synchronize()
-            return e0.elapsed_time(e1) * 1e3 / K
-        with torch.cuda.stream(st):
-            for i in range(R):
-                fn(i)
-        st.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=st):
-            for i in range(R):
-                fn(i)
-        reps = max(1, K // R)
-        with torch.cuda.stream(st):
-            g.replay()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(st)
-            for _ in range(reps):
-                g.replay()
-            e1.record(st)
-        st.synchronize()
-        return e0.elapsed_time(e1) * 1e3 / (reps * R)
-
-    dec_bytes = qb["kv"] + H * D * 4
-    dense_dec_bytes = db["kv"] + H * D * 4
-    dec_us = time_kernel(lambda i: skv.decode_attn(caches[i % R], q, seq_len, L, w.softmax_scale,
-                                                   S_q, ws_q, sel, cnt)) if do_q else None
-    dense_dec_us = time_kernel(lambda i: skv.decode_attn(caches[i % R], q, seq_len, L,
-                                                         w.softmax_scale, S_d, ws_d)) if do_d else None
-
-    def us(graph_t, stream_t):
-        t = graph_t if graph_t is not None else stream_t
-        return None if t is None else t * 1e6
-
-    def rnd(x, n=3):
-        return None if x is None else round(x, n)
-
-    quest_us = us(quest_graph, quest_stream)
-    dense_us = us(dense_graph, dense_stream)
-    head_us = quest_us if quest_us is not None else dense_us
-    head_bytes = qb["total"] if quest_us is not None else db["total"]
-    gbps = head_bytes / (head_us * 1e-6) / 1e9
-    if dec_us is not None:
-        rk, rb, rus = "decode_f16_mfma (decode_attn over the selected blocks)", dec_bytes, dec_us
+    hq, hd = head.get("quest"), head.get("dense")
+    top = hq if hq is not None else hd
+    if hq is not None:
+        rk = "decode_f16_mfma (decode_attn over the selected blocks)"
+        rb, rus = head["_roofline"]
     else:
-        rk, rb, rus = "decode_f16_mfma (decode_attn, dense)", dense_dec_bytes, dense_dec_us
+        rk = "decode_f16_mfma (decode_attn, dense)"
+        rus = hd["decode_attn_us"]
+        rb = step_bytes(w3.lens, w3.Hkv, w3.H, w3.D, "f16", w3.block, None)["kv"] + w3.H * w3.D * 4
     ach = rb / (rus * 1e-6) / 1e9
-    traffic = recorded_traffic(rk)
+    us = top["us_per_step"]
     res = {
         "metric": METRIC,
-        "value": round(head_us, 3),
+        "value": us,
         "unit": "us/step",
         "n_gpus": 1,
-        "steps": steps_done,
-        "warmup": W,
-        "ms_per_step": round(head_us / 1e3, 6),
+        "steps": top["steps"],
+        "warmup": args.warmup,
+        "ms_per_step": round(us / 1e3, 6),
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f16",
         "data": "synthetic",
-        "config": {"workload": w.name,
+        "config": {"workload": w3.name,
                    "step": ("kv_append + block_bounds + select_topk + decode_attn(selected blocks)"
-                            " + combine") if quest_us is not None else
+                            " + combine") if hq is not None else
                            "kv_append + decode_attn(dense) + combine",
-                   "cache_copies": R,
+                   "cache_copies": head["cache_copies"],
                    "launch": "hipgraph" if not args.no_graph else "stream",
-                   "n_split": S_q if quest_us is not None else S_d},
-        "achieved_GBps": round(gbps, 1),
-        "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
-        "bytes_per_step": qb if quest_us is not None else db,
-        "dense": None if dense_us is None else {
-            "us_per_step": rnd(dense_us), "bytes_per_step": db,
-            "achieved_GBps": round(db["total"] / (dense_us * 1e-6) / 1e9, 1),
-            "pct_hbm_peak": round(100 * db["total"] / (dense_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 2),
-            "n_split": S_d, "decode_attn_us": rnd(dense_dec_us),
-            "decode_attn_GBps": round(dense_dec_bytes / (dense_dec_us * 1e-6) / 1e9, 1)},
-        "quest_over_dense_time": (round(quest_us / dense_us, 4)
-                                  if quest_us is not None and dense_us is not None else None),
-        "stream_launch_us": {"quest": rnd(None if quest_stream is None else quest_stream * 1e6),
-                             "dense": rnd(None if dense_stream is None else dense_stream * 1e6)},
+                   "n_split": top["n_split"]},
+        "achieved_GBps": top["GBps"],
+        "pct_hbm_peak": top["pct_hbm_peak"],
+        "quest": hq,
+        "dense": hd,
+        "quest_over_dense_time": head.get("quest_over_dense"),
         "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                     "kernel": rk, "avg_launch_us": round(rus, 3), "bytes_per_launch": rb},
+                     "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4),
+                     "traffic": recorded_traffic(rk), "kernel": rk,
+                     "avg_launch_us": round(rus, 3), "bytes_per_launch": rb},
+        "workloads": others,
     }
     if args.copy_probe_mib > 0:
-        a = torch.ones(args.copy_probe_mib * 2 ** 18, dtype=torch.float32, device=dev)
+        a = torch.ones(args.copy_probe_mib * 2 ** 18, dtype=torch.float32, device="cuda:0")
         b2 = torch.empty_like(a)
         torch.cuda.synchronize()
         for _ in range(3):
@@ -389,7 +466,7 @@ def main():
         torch.cuda.synchronize()
         res["copy_probe_bytes"] = {"read": a.numel() * 4, "written": a.numel() * 4}
     if not args.no_cpu:
-        res["cpu_baseline"] = cpu_baseline(w)
+        res["cpu_baseline"] = cpu_baseline(w3)
     print(json.dumps(res), flush=True)
 
 

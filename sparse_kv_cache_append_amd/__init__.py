@@ -150,6 +150,18 @@ class Cache:
     def src_dtype(self) -> int:
         return SKV_F16 if self.kv_dtype == "f16" else SKV_F32
 
+    def clone(self) -> "Cache":
+        """A second cache with copies of every tensor (same geometry)."""
+        c = Cache.__new__(Cache)
+        c.__dict__.update(self.__dict__)
+        for name in ("k", "v", "k_scale", "v_scale", "kmin", "kmax"):
+            t = getattr(self, name)
+            setattr(c, name, None if t is None else t.clone())
+        c.desc = SkvCacheDesc(self.batch, self.n_kv_heads, self.head_dim, self.max_seq,
+                              self.block, self.desc.kv_dtype, _ptr(c.k), _ptr(c.v),
+                              _ptr(c.k_scale), _ptr(c.v_scale), _ptr(c.kmin), _ptr(c.kmax))
+        return c
+
 
 def kv_append(cache: Cache, pos0, k_new, v_new, stream=None):
     """Append n_new tokens per sequence: k_new, v_new [batch][n_new][Hkv][D]
