@@ -22,7 +22,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libskv.so")
 
-SOURCES = ["api.cpp", "append.hip", "bounds.hip", "select.hip", "decode.hip", "decode_mfma.hip",
+SOURCES = ["api.cpp", "append.hip", "bounds.hip", "select.hip", "decode_mfma.hip",
            "combine.hip"]
 ARCH = "gfx950"
 

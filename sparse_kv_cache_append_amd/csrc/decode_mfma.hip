@@ -331,13 +331,232 @@ decode_f16_mfma(const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc
                  int64_t(b) * H + g * G, n_split, split);
 }
 
+// ------------------------------------------------------------------ int8
+// Tile = 32 tokens: K and V tiles are 4 KiB each (4 load instructions of 8
+// rows) plus their 32 K scales and 32 V scales (one load instruction).
+//
+// Token order inside a tile.  q.K runs as two 16-token halves, so lane
+// (group lg, head lc) holds the logits of tokens 4 lg + r and 16 + 4 lg + r
+// (r = 0..3).  P.V contracts all 32 tokens in one 16x16x32 f16 MFMA per 16
+// channels, with element e of lane group lg standing for token
+// tok(lg, e) = 16 (e / 4) + 4 lg + e % 4 in both operands (a permutation of
+// the reduction index leaves the sum unchanged).  The transposing byte read
+// delivers that order: lane i of group lg reads the 8 bytes of token
+// tok(lg, i / 2) at channel 16 n + 8 (i % 2), and lane j then holds channel
+// 16 n + j of tokens tok(lg, 0..7).  The codes are widened to f16 exactly
+// (1152 + c is exact in f16, minus 1152).
+//
+// The V scales are folded into the weights: P' = p * v_scale * 2^-e with
+// 2^e the tile's largest V scale rounded to a power of two, so P' <= 1 keeps
+// full f16 (high + low) precision whatever the scale; the tile's product is
+// then added to the accumulator times 2^e (exact).
+__device__ __forceinline__ half8_t widen_codes(int2_t w) {
+  typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+  half8_t r;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const uint32_t x = uint32_t(w[k]) ^ 0x80808080u;         // c + 128 per byte
+    const uint32_t lo = (x & 0xFFu) | ((x & 0xFF00u) << 8) | 0x64006400u;
+    const uint32_t hi = ((x >> 16) & 0xFFu) | ((x >> 8) & 0xFF0000u) | 0x64006400u;
+    const half2_t a = __builtin_bit_cast(half2_t, lo) - half2_t{(_Float16)1152.0f, (_Float16)1152.0f};
+    const half2_t b = __builtin_bit_cast(half2_t, hi) - half2_t{(_Float16)1152.0f, (_Float16)1152.0f};
+    r[4 * k + 0] = a[0];
+    r[4 * k + 1] = a[1];
+    r[4 * k + 2] = b[0];
+    r[4 * k + 3] = b[1];
+  }
+  return r;
+}
+
+template <int G>
+__global__ void __launch_bounds__(kMThreads, 2)
+decode_i8_mfma(const int8_t* __restrict__ kc, const int8_t* __restrict__ vc,
+               const float* __restrict__ ksc, const float* __restrict__ vsc,
+               const float* __restrict__ q, const int32_t* __restrict__ seq_len,
+               const int32_t* __restrict__ sel_idx, const int32_t* __restrict__ sel_cnt,
+               int32_t max_sel, int32_t Hkv, int32_t max_seq, int32_t block, int32_t max_len,
+               int32_t n_split, int32_t units_per_split, float scale2,
+               float* __restrict__ ws_m, float* __restrict__ ws_l, float* __restrict__ ws_o,
+               int32_t* __restrict__ dbg) {
+  constexpr int T = 32;
+  constexpr int kTileBytes = T * kRowBytesI8;               // 4096
+  constexpr int kScaleOff = 2 * kTileBytes;                 // 32 K scales, 32 V scales
+  constexpr int kBufBytes = 2 * kTileBytes + 2 * T * 4;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kMWaves][2][kBufBytes];
+  const int32_t split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int lg = lane / 16, lc = lane % 16;
+  const int32_t H = Hkv * G;
+  const int32_t L = min(max(seq_len[b], 0), max_len);
+  const int64_t bg = int64_t(b) * Hkv + g;
+  TileWalk tw = make_walk<T>(sel_idx, sel_cnt, max_sel, bg, L, block, split, units_per_split);
+  tw.init(wave);
+
+  // Query codes as the B operand of q.K (column = head lc, k-chunk lg): the
+  // head's absmax scale over all 128 channels (the 4 lanes of a column hold
+  // 32 channels each), then the codes of channels 64 kk + 16 lg + 0..15.
+  int4_t qb[2];
+  float coef;
+  {
+    const bool hv = lc < G;
+    const float* qp = q + (int64_t(b) * H + g * G + (hv ? lc : 0)) * kD;
+    float x[2][16];
+    float a = 0.0f;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float4 v4 = *reinterpret_cast<const float4*>(qp + 64 * kk + 16 * lg + 4 * i);
+        x[kk][4 * i + 0] = v4.x; x[kk][4 * i + 1] = v4.y;
+        x[kk][4 * i + 2] = v4.z; x[kk][4 * i + 3] = v4.w;
+        a = fmaxf(a, fmaxf(fmaxf(fabsf(v4.x), fabsf(v4.y)), fmaxf(fabsf(v4.z), fabsf(v4.w))));
+      }
+    }
+    a = fmaxf(a, __shfl_xor(a, 16));
+    a = fmaxf(a, __shfl_xor(a, 32));
+    const float qs = absmax_scale(a);
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        uint32_t packed = 0u;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          packed |= (uint32_t(quant_code(x[kk][4 * w + e], qs)) & 0xFFu) << (8 * e);
+        qb[kk][w] = hv ? int32_t(packed) : 0;
+      }
+    }
+    coef = hv ? qs * scale2 : 0.0f;
+  }
+  float m_run = -INFINITY, l_run = 0.0f;
+  float4_t O[8];
+#pragma unroll
+  for (int n = 0; n < 8; ++n) O[n] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+  const uint8_t* kbase = reinterpret_cast<const uint8_t*>(kc + bg * int64_t(max_seq) * kD);
+  const uint8_t* vbase = reinterpret_cast<const uint8_t*>(vc + bg * int64_t(max_seq) * kD);
+  const float* ksb = ksc + bg * int64_t(max_seq);
+  const float* vsb = vsc + bg * int64_t(max_seq);
+  int32_t* dbg_h = (dbg != nullptr && lc < G)
+                       ? dbg + (int64_t(b) * H + g * G + lc) * int64_t(max_len) : nullptr;
+  const int32_t last = max(L - 1, 0);
+  struct Frag { int4_t k[4], v[4]; float sc; int32_t r0, nvalid; };
+  // lane loads row 8 i + lane / 8 (i = 0..3) of the tile, 16-byte chunk
+  // lane % 8; lanes < 32 load the K scale of token lane, the others the V
+  // scale of token lane - 32
+  auto issue = [&](Frag& f) {
+    int32_t r0, nv;
+    tw.next<T>(r0, nv);
+    f.r0 = r0;
+    f.nvalid = nv;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int32_t row = min(r0 + 8 * i + lane / 8, last);
+      const int64_t off = int64_t(row) * kRowBytesI8 + 16 * (lane % 8);
+      f.k[i] = *reinterpret_cast<const int4_t*>(kbase + off);
+      f.v[i] = *reinterpret_cast<const int4_t*>(vbase + off);
+    }
+    const int32_t srow = min(r0 + lane % 32, last);
+    f.sc = lane < 32 ? ksb[srow] : vsb[srow];
+  };
+  auto sw = [](int row, int chunk) { return row * kRowBytesI8 + 16 * (chunk ^ (row & 7)); };
+
+  auto process = [&](auto bufc, Frag& fr, bool& have) {
+    constexpr int kBuf = decltype(bufc)::value;
+    uint8_t* kt = smem[wave][kBuf];
+    uint8_t* vt = kt + kTileBytes;
+    float* st = reinterpret_cast<float*>(kt + kScaleOff);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 8 * i + lane / 8;
+      *reinterpret_cast<int4_t*>(kt + sw(row, lane % 8)) = fr.k[i];
+      *reinterpret_cast<int4_t*>(vt + sw(row, lane % 8)) = fr.v[i];
+    }
+    st[lane] = fr.sc;
+    const int32_t nvalid = fr.nvalid, r0 = fr.r0;
+    have = tw.more();
+    if (have) issue(fr);
+    // q.K, exact: two 16-token halves, 128 channels as two k = 64 steps
+    int4_t acc[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      acc[s] = int4_t{0, 0, 0, 0};
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const int4_t a = *reinterpret_cast<const int4_t*>(kt + sw(16 * s + lc, lg + 4 * kk));
+        acc[s] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, qb[kk], acc[s], 0, 0, 0);
+      }
+    }
+    const float4 ks0 = *reinterpret_cast<const float4*>(st + 4 * lg);
+    const float4 ks1 = *reinterpret_cast<const float4*>(st + 16 + 4 * lg);
+    const float4 vs0 = *reinterpret_cast<const float4*>(st + 32 + 4 * lg);
+    const float4 vs1 = *reinterpret_cast<const float4*>(st + 48 + 4 * lg);
+    const float ks[8] = {ks0.x, ks0.y, ks0.z, ks0.w, ks1.x, ks1.y, ks1.z, ks1.w};
+    const float vs[8] = {vs0.x, vs0.y, vs0.z, vs0.w, vs1.x, vs1.y, vs1.z, vs1.w};
+    float sc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int t = 16 * (e / 4) + 4 * lg + e % 4;
+      const int32_t dot = acc[e / 4][e % 4];
+      const bool ok = t < nvalid;
+      if (dbg_h != nullptr && ok) dbg_h[r0 + t] = dot;
+      sc[e] = ok ? float(dot) * coef * ks[e] : -INFINITY;
+    }
+    tile_softmax<2>(sc, m_run, l_run, O);
+    // fold the V scales into the weights, normalized by the tile's largest
+    float vmax = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) vmax = fmaxf(vmax, vs[e]);
+    vmax = fmaxf(vmax, __shfl_xor(vmax, 16));
+    vmax = fmaxf(vmax, __shfl_xor(vmax, 32));
+    const int ex = __builtin_amdgcn_frexp_expf(vmax);
+    float pw[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pw[e] = sc[e] * ldexpf(vs[e], -ex);
+    half8_t phi, plo;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const _Float16 h = (_Float16)pw[e];
+      phi[e] = h;
+      plo[e] = (_Float16)(pw[e] - (float)h);
+    }
+    const float back = ldexpf(1.0f, ex);
+    // P.V: B = V codes of channels 16 n + lc for tokens tok(lg, 0..7)
+    const int tr_row = 16 * ((lc / 2) / 4) + 4 * lg + (lc / 2) % 4;
+#pragma unroll
+    for (int n = 0; n < 8; ++n) {
+      const int off = sw(tr_row, n) + 8 * (lc & 1);
+      const int2_t raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32((SKV_LDS int2_t*)(vt + off));
+      const half8_t bv = widen_codes(raw);
+      float4_t t4 = mfma_f16_32(phi, bv, float4_t{0.0f, 0.0f, 0.0f, 0.0f});
+      t4 = mfma_f16_32(plo, bv, t4);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) O[n][r] = fmaf(t4[r], back, O[n][r]);
+    }
+  };
+
+  Frag f0, f1;
+  bool h0 = tw.more();
+  if (h0) issue(f0);
+  bool h1 = tw.more();
+  if (h1) issue(f1);
+  while (h0) {
+    process(std::integral_constant<int, 0>{}, f0, h0);
+    if (!h1) break;
+    process(std::integral_constant<int, 1>{}, f1, h1);
+  }
+  finish_mfma<G>(m_run, l_run, O, reinterpret_cast<float*>(&smem[0][0][0]), ws_m, ws_l, ws_o,
+                 int64_t(b) * H + g * G, n_split, split);
+}
+
 }  // namespace
 
-bool launch_decode_mfma(const DecodeParams& p, hipStream_t stream) {
+hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   const skv_cache& c = *p.c;
-  if (c.kv_dtype != SKV_F16 || c.block % 16 != 0) return false;
+  if (c.block % 16 != 0) return hipErrorInvalidValue;
   const int32_t B = c.batch, H = p.n_heads, S = p.n_split;
   const int G = H / c.n_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return hipErrorInvalidValue;
   float* ws_m = p.ws + ws_m_offset(B, H, S);
   float* ws_l = p.ws + ws_l_offset(B, H, S);
   float* ws_o = p.ws + ws_o_offset(B, H, S);
@@ -350,20 +569,35 @@ bool launch_decode_mfma(const DecodeParams& p, hipStream_t stream) {
   }
   dim3 grid(S, c.n_kv_heads, B);
   const float scale2 = p.softmax_scale * kLog2e;
+  if (c.kv_dtype == SKV_F16) {
 #define SKV_LAUNCH_F16(GG)                                                                      \
   decode_f16_mfma<GG, 2><<<grid, kMThreads, 0, stream>>>(                                      \
       static_cast<const uint16_t*>(c.k), static_cast<const uint16_t*>(c.v), p.q, p.seq_len,    \
       p.sel_idx, p.sel_cnt, p.max_sel, c.n_kv_heads, c.max_seq, c.block, p.max_len, S, ups,    \
       scale2, ws_m, ws_l, ws_o)
-  switch (G) {
-    case 1: SKV_LAUNCH_F16(1); break;
-    case 2: SKV_LAUNCH_F16(2); break;
-    case 4: SKV_LAUNCH_F16(4); break;
-    case 8: SKV_LAUNCH_F16(8); break;
-    default: return false;
-  }
+    switch (G) {
+      case 1: SKV_LAUNCH_F16(1); break;
+      case 2: SKV_LAUNCH_F16(2); break;
+      case 4: SKV_LAUNCH_F16(4); break;
+      default: SKV_LAUNCH_F16(8); break;
+    }
 #undef SKV_LAUNCH_F16
-  return true;
+    return hipGetLastError();
+  }
+  if (c.kv_dtype != SKV_I8) return hipErrorInvalidValue;
+#define SKV_LAUNCH_I8(GG)                                                                       \
+  decode_i8_mfma<GG><<<grid, kMThreads, 0, stream>>>(                                          \
+      static_cast<const int8_t*>(c.k), static_cast<const int8_t*>(c.v), c.k_scale, c.v_scale,  \
+      p.q, p.seq_len, p.sel_idx, p.sel_cnt, p.max_sel, c.n_kv_heads, c.max_seq, c.block,       \
+      p.max_len, S, ups, scale2, ws_m, ws_l, ws_o, p.dbg_logits)
+  switch (G) {
+    case 1: SKV_LAUNCH_I8(1); break;
+    case 2: SKV_LAUNCH_I8(2); break;
+    case 4: SKV_LAUNCH_I8(4); break;
+    default: SKV_LAUNCH_I8(8); break;
+  }
+#undef SKV_LAUNCH_I8
+  return hipGetLastError();
 }
 
 }  // namespace skv

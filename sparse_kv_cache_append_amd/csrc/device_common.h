@@ -23,29 +23,13 @@ template <int CTRL>
 __device__ __forceinline__ float dpp_f(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
 }
-template <int CTRL>
-__device__ __forceinline__ int dpp_i(int x) {
-  return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xF, 0xF, false);
-}
 
-// Sum / max over aligned groups of 8 lanes; every lane of the group gets the
-// same bits (each step combines a lane with its mirror, a commutative op).
+// Sum over an aligned group of 8 lanes; every lane of the group gets the same
+// bits (each step combines a lane with its mirror, a commutative op).
 __device__ __forceinline__ float group8_sum(float x) {
   x += dpp_f<kDppQuadXor1>(x);
   x += dpp_f<kDppQuadXor2>(x);
   x += dpp_f<kDppRowHalfMirror>(x);
-  return x;
-}
-__device__ __forceinline__ int group8_sum_i(int x) {
-  x += dpp_i<kDppQuadXor1>(x);
-  x += dpp_i<kDppQuadXor2>(x);
-  x += dpp_i<kDppRowHalfMirror>(x);
-  return x;
-}
-__device__ __forceinline__ float group8_max(float x) {
-  x = fmaxf(x, dpp_f<kDppQuadXor1>(x));
-  x = fmaxf(x, dpp_f<kDppQuadXor2>(x));
-  x = fmaxf(x, dpp_f<kDppRowHalfMirror>(x));
   return x;
 }
 // Sum over aligned groups of 16 lanes (one DPP row).
@@ -58,11 +42,6 @@ __device__ __forceinline__ float group16_sum(float x) {
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
-  return x;
-}
-__device__ __forceinline__ int wave_sum_i(int x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
   return x;
 }
 

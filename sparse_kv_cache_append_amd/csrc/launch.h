@@ -40,10 +40,6 @@ hipError_t launch_select(const float* score, const int32_t* seq_len, int32_t bat
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
 
-// Matrix-core decode; returns false (nothing launched) for caches it does not
-// cover, which then take launch_decode's vector-ALU kernels.
-bool launch_decode_mfma(const DecodeParams& p, hipStream_t stream);
-
 hipError_t launch_combine(const float* ws, int32_t batch, int32_t n_heads, int32_t head_dim,
                           int32_t n_split, float* out, hipStream_t stream);
 
