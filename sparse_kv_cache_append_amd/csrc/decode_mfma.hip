@@ -120,15 +120,14 @@ __device__ __forceinline__ TileWalk make_walk(const int32_t* sel_idx, const int3
 // Softmax bookkeeping of one tile for the 16 MFMA columns (heads): lane l
 // owns head l%16 and rows 4*(l/16) + r of the tile.  s[r] are base-2 logits
 // (-inf for masked rows); returns the weights p[r] and rescales O.
-template <int NT>
+template <int G, int NT>
 __device__ __forceinline__ void tile_softmax(float (&s)[4 * NT], float& m_run, float& l_run,
                                              float4_t (&O)[8]) {
   const int lane = threadIdx.x % kWave;
   float mx = s[0];
 #pragma unroll
   for (int i = 1; i < 4 * NT; ++i) mx = fmaxf(mx, s[i]);
-  mx = fmaxf(mx, __shfl_xor(mx, 16));
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  mx = rows_max(mx);
   const float m_new = fmaxf(m_run, mx);
   const bool live = m_new != -INFINITY;
   const float cr = (live && m_run != -INFINITY) ? __builtin_amdgcn_exp2f(m_run - m_new)
@@ -139,15 +138,20 @@ __device__ __forceinline__ void tile_softmax(float (&s)[4 * NT], float& m_run, f
     s[i] = (s[i] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(s[i] - m_new);
     ps += s[i];
   }
-  ps += __shfl_xor(ps, 16);
-  ps += __shfl_xor(ps, 32);
+  ps = rows_sum(ps);
   l_run = l_run * cr + ps;
   m_run = m_new;
-  // O rows are heads 4*(lane/16) + r; their factors live in lanes 4*(lane/16) + r
-  const int g4 = 4 * (lane / 16);
+  // O rows are heads 4*(lane/16) + r; head h's factor is in lane h (column
+  // h of every row holds it).  Only heads < G matter: rows past them hold
+  // padding and may take any finite factor.
+  const bool upper = G > 4 && lane >= 16;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    const float c = __shfl(cr, g4 + r);
+    float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cr), r));
+    if (G > 4) {
+      const float c4 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cr), 4 + r));
+      c = upper ? c4 : c;
+    }
 #pragma unroll
     for (int n = 0; n < 8; ++n) O[n][r] *= c;
   }
@@ -300,7 +304,7 @@ decode_f16_mfma(const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc
     float sc[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) sc[r] = (4 * lg + r < nvalid) ? acc[r] : -INFINITY;
-    tile_softmax<1>(sc, m_run, l_run, O);
+    tile_softmax<G, 1>(sc, m_run, l_run, O);
     half4_t phi, plo;
     split_hi_lo4(sc, phi, plo);
     // P.V: B = V^T rows 4lg..4lg+3 via the transposing read; 16 channels per n
@@ -412,8 +416,7 @@ decode_i8_mfma(const int8_t* __restrict__ kc, const int8_t* __restrict__ vc,
         a = fmaxf(a, fmaxf(fmaxf(fabsf(v4.x), fabsf(v4.y)), fmaxf(fabsf(v4.z), fabsf(v4.w))));
       }
     }
-    a = fmaxf(a, __shfl_xor(a, 16));
-    a = fmaxf(a, __shfl_xor(a, 32));
+    a = rows_max(a);
     const float qs = absmax_scale(a);
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
@@ -502,13 +505,12 @@ decode_i8_mfma(const int8_t* __restrict__ kc, const int8_t* __restrict__ vc,
       if (dbg_h != nullptr && ok) dbg_h[r0 + t] = dot;
       sc[e] = ok ? float(dot) * coef * ks[e] : -INFINITY;
     }
-    tile_softmax<2>(sc, m_run, l_run, O);
+    tile_softmax<G, 2>(sc, m_run, l_run, O);
     // fold the V scales into the weights, normalized by the tile's largest
     float vmax = 0.0f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) vmax = fmaxf(vmax, vs[e]);
-    vmax = fmaxf(vmax, __shfl_xor(vmax, 16));
-    vmax = fmaxf(vmax, __shfl_xor(vmax, 32));
+    vmax = rows_max(vmax);
     const int ex = __builtin_amdgcn_frexp_expf(vmax);
     float pw[8];
 #pragma unroll

@@ -39,9 +39,78 @@ __device__ __forceinline__ float group16_sum(float x) {
   return x;
 }
 
+
+// ------------------------------------------------------- across the 4 rows
+// gfx950 lane swaps (verified lane maps): permlane16_swap(x, x) returns, in
+// every lane, the values of its row pair {row 2i, row 2i+1} as (row 2i,
+// row 2i+1); permlane32_swap(x, x) returns (lower half, upper half).  So
+// op(first, second) is the same bits in all lanes of the pair, and two steps
+// reduce lanes l, l ^ 16, l ^ 32, l ^ 48 with VALU instructions only.
+__device__ __forceinline__ uint32_t rows_pair_lo(uint32_t x, uint32_t& hi) {
+  const auto p = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  hi = p[1];
+  return p[0];
+}
+__device__ __forceinline__ uint32_t halves_lo(uint32_t x, uint32_t& hi) {
+  const auto p = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  hi = p[1];
+  return p[0];
+}
+__device__ __forceinline__ float rows_max(float x) {
+  uint32_t h;
+  float l = __uint_as_float(rows_pair_lo(__float_as_uint(x), h));
+  x = fmaxf(l, __uint_as_float(h));
+  l = __uint_as_float(halves_lo(__float_as_uint(x), h));
+  return fmaxf(l, __uint_as_float(h));
+}
+__device__ __forceinline__ float rows_sum(float x) {
+  uint32_t h;
+  float l = __uint_as_float(rows_pair_lo(__float_as_uint(x), h));
+  x = l + __uint_as_float(h);
+  l = __uint_as_float(halves_lo(__float_as_uint(x), h));
+  return l + __uint_as_float(h);
+}
+
 __device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  x = fmaxf(x, dpp_f<kDppQuadXor1>(x));
+  x = fmaxf(x, dpp_f<kDppQuadXor2>(x));
+  x = fmaxf(x, dpp_f<kDppRowHalfMirror>(x));
+  x = fmaxf(x, dpp_f<kDppRowMirror>(x));
+  return rows_max(x);
+}
+
+// ------------------------------------------------------ wavefront integers
+// Inclusive prefix sum over the 64 lanes: DPP row shifts by 1, 2, 4, 8 scan
+// each row of 16, then the row-15 and row-31 broadcasts carry the row totals
+// into the rows above (verified on gfx950).
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, true);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, true);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, true);   // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31
+  return x;
+}
+// AND / OR over the 64 lanes (every lane gets the result).
+__device__ __forceinline__ uint32_t wave_and(uint32_t x) {
+  x &= uint32_t(__builtin_amdgcn_update_dpp(0, int(x), kDppQuadXor1, 0xF, 0xF, false));
+  x &= uint32_t(__builtin_amdgcn_update_dpp(0, int(x), kDppQuadXor2, 0xF, 0xF, false));
+  x &= uint32_t(__builtin_amdgcn_update_dpp(0, int(x), kDppRowHalfMirror, 0xF, 0xF, false));
+  x &= uint32_t(__builtin_amdgcn_update_dpp(0, int(x), kDppRowMirror, 0xF, 0xF, false));
+  uint32_t h;
+  x = rows_pair_lo(x, h) & h;
+  x = halves_lo(x, h) & h;
+  return x;
+}
+__device__ __forceinline__ uint32_t wave_or(uint32_t x) {
+  x |= uint32_t(__builtin_amdgcn_update_dpp(0, int(x), kDppQuadXor1, 0xF, 0xF, false));
+  x |= uint32_t(__builtin_amdgcn_update_dpp(0, int(x), kDppQuadXor2, 0xF, 0xF, false));
+  x |= uint32_t(__builtin_amdgcn_update_dpp(0, int(x), kDppRowHalfMirror, 0xF, 0xF, false));
+  x |= uint32_t(__builtin_amdgcn_update_dpp(0, int(x), kDppRowMirror, 0xF, 0xF, false));
+  uint32_t h;
+  x = rows_pair_lo(x, h) | h;
+  x = halves_lo(x, h) | h;
   return x;
 }
 

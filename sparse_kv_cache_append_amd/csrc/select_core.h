@@ -1,0 +1,236 @@
+// Exact fixed top-K of one row of block scores, computed by one workgroup of
+// kSelThreads threads: the selection rule of sparse_attn.md, "Method" (the
+// K highest upper bounds) and "Budget policy" (fixed K), with exact ties
+// going to the lower block index.
+//
+// Order.  Candidate i with score key k_i (float_key: order-preserving, -0
+// and +0 equal) has the 64-bit order value v_i = k_i * 2^32 + (2^32 - 1 - i):
+// a larger score wins, and among equal scores the lower index.  The v_i are
+// distinct, so "the K best candidates" is exactly {i : v_i >= V*} for the
+// K-th largest value V*; computing V* is the whole selection.
+//
+// Thread t holds the keys of candidates t, t + 256, ... in registers (RMAX
+// of them), loaded in one round trip.  V* is found by
+//   * fixing the leading key bits that every candidate shares (a DPP AND/OR
+//     reduction): the bounds of one row share sign and most exponent bits,
+//     and a histogram of those bits would pile every key into one or two bins;
+//   * most-significant-digit radix passes (LDS histogram of 256 bins filled
+//     straight from registers, DPP prefix sum over the bins) fixing 8 more
+//     bits of the K-th key each, until at most 64 candidates share its prefix;
+//   * ranking those pairwise (LDS broadcast reads of their order values);
+//   * or, if more than 64 keys equal the K-th key exactly, taking its
+//     occurrence of the right rank in index order.
+// Index order of flagged candidates (ascending output positions) comes from
+// per-(chunk, wavefront) ballot counts, one workgroup scan of those counts,
+// and the set ballot bits below each lane.
+#pragma once
+
+#include "device_common.h"
+
+namespace skv {
+
+constexpr int kSelThreads = 256;
+constexpr int kSelWaves = kSelThreads / kWave;
+constexpr int kSelMaxChunks = 64;                 // candidates <= 64 * 256 = 16384
+
+struct __attribute__((aligned(16))) SelectShared {
+  uint32_t hist[256];
+  uint64_t slot[kWave];                           // order values tied on the prefix
+  int32_t part[kSelMaxChunks * kSelWaves];        // (chunk, wave) counts -> prefixes
+  uint32_t red_and[kSelWaves], red_or[kSelWaves];
+  int scan_tmp[kSelWaves];
+  uint64_t cut;
+  uint32_t digit;
+  int above, count, n_active;
+};
+
+__device__ __forceinline__ int lanes_below(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi(uint32_t(mask >> 32),
+                                   __builtin_amdgcn_mbcnt_lo(uint32_t(mask), 0u));
+}
+__device__ __forceinline__ uint64_t order_value(uint32_t key, int32_t i) {
+  return (uint64_t(key) << 32) | uint64_t(~uint32_t(i));
+}
+
+// Exclusive scan of one int per thread over the workgroup; also returns the
+// total.
+__device__ __forceinline__ int sel_exclusive_scan(int v, int* tmp, int& total) {
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int x = wave_incl_scan(v);
+  if (lane == kWave - 1) tmp[wave] = x;
+  __syncthreads();
+  int off = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < kSelWaves; ++w) {
+    const int t = tmp[w];
+    off += (w < wave) ? t : 0;
+    tot += t;
+  }
+  __syncthreads();
+  total = tot;
+  return off + x - v;
+}
+
+// Keys of candidates threadIdx.x + 256 r, r < RMAX, of a row of n.
+template <int RMAX>
+struct SelKeys {
+  uint32_t k[RMAX];
+  int32_t n;
+  __device__ __forceinline__ bool valid(int r) const {
+    return int32_t(threadIdx.x) + kSelThreads * r < n;
+  }
+  __device__ __forceinline__ int32_t index(int r) const {
+    return int32_t(threadIdx.x) + kSelThreads * r;
+  }
+  // Every load is issued before any key is formed (one round trip).
+  __device__ __forceinline__ void load(const float* __restrict__ score_row, int32_t n_cand) {
+    n = n_cand;
+    float v[RMAX];
+#pragma unroll
+    for (int r = 0; r < RMAX; ++r) v[r] = valid(r) ? score_row[index(r)] : 0.0f;
+#pragma unroll
+    for (int r = 0; r < RMAX; ++r) k[r] = float_key(v[r]);
+  }
+};
+
+// Index order of flagged candidates.  Bit r of `flags` flags candidate
+// threadIdx.x + 256 r.  Afterwards sel_order_pos(flags, r) is a flagged
+// candidate's number of flagged candidates with a smaller index.  Returns the
+// total.  Called by the whole workgroup (R = chunks in use, <= 64).
+__device__ __forceinline__ int sel_order_prepare(uint64_t flags, int R, SelectShared& s) {
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  for (int r = 0; r < R; ++r) {
+    const uint64_t bal = __ballot(int((flags >> r) & 1u));
+    if (lane == 0) s.part[r * kSelWaves + wave] = __popcll(bal);
+  }
+  __syncthreads();
+  const int v = tid < R * kSelWaves ? s.part[tid] : 0;   // R * 4 <= 256 entries
+  int tot;
+  const int ex = sel_exclusive_scan(v, s.scan_tmp, tot);
+  if (tid < R * kSelWaves) s.part[tid] = ex;
+  __syncthreads();
+  return tot;
+}
+__device__ __forceinline__ int sel_order_pos(uint64_t flags, int r, const SelectShared& s) {
+  const uint64_t bal = __ballot(int((flags >> r) & 1u));
+  return s.part[r * kSelWaves + threadIdx.x / kWave] + lanes_below(bal);
+}
+
+// 0 < K < n.  Returns V* in every thread: candidate i is among the K best iff
+// order_value(key_i, i) >= V*.
+template <int RMAX>
+__device__ __forceinline__ uint64_t sel_cut(const SelKeys<RMAX>& kk, int32_t K, SelectShared& s) {
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int32_t n = kk.n;
+
+  uint32_t a = ~0u, o = 0u;
+#pragma unroll
+  for (int r = 0; r < RMAX; ++r) {
+    const bool ok = kk.valid(r);
+    a &= ok ? kk.k[r] : ~0u;
+    o |= ok ? kk.k[r] : 0u;
+  }
+  a = wave_and(a);
+  o = wave_or(o);
+  if (lane == 0) { s.red_and[wave] = a; s.red_or[wave] = o; }
+  __syncthreads();
+  a = s.red_and[0]; o = s.red_or[0];
+#pragma unroll
+  for (int w = 1; w < kSelWaves; ++w) { a &= s.red_and[w]; o |= s.red_or[w]; }
+  const uint32_t diff = a ^ o;
+  uint32_t pmask = diff == 0u ? ~0u : (__clz(diff) == 0 ? 0u : ~0u << (32 - __clz(diff)));
+  uint32_t prefix = a & pmask;
+  int remaining = K;
+  int active = n;
+
+  while (active > kWave && pmask != ~0u) {
+    const int free_bits = __popc(~pmask);
+    const int width = free_bits < 8 ? free_bits : 8;
+    const int shift = free_bits - width;
+    const uint32_t dmask = (1u << width) - 1u;
+    s.hist[tid] = 0u;                      // kSelThreads == 256 bins
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < RMAX; ++r) {
+      const uint32_t k = kk.k[r];
+      if (kk.valid(r) && (k & pmask) == prefix) atomicAdd(&s.hist[(k >> shift) & dmask], 1u);
+    }
+    __syncthreads();
+    if (wave == 0) {
+      // lane l owns digits 255-4l .. 252-4l (descending)
+      const uint4 h4 = *reinterpret_cast<const uint4*>(&s.hist[252 - 4 * lane]);
+      const int cnt[4] = {int(h4.w), int(h4.z), int(h4.y), int(h4.x)};
+      const int sum = cnt[0] + cnt[1] + cnt[2] + cnt[3];
+      int above = wave_incl_scan(sum) - sum;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (above < remaining && remaining <= above + cnt[q]) {
+          s.digit = uint32_t(255 - 4 * lane - q);
+          s.above = above;
+          s.count = cnt[q];
+        }
+        above += cnt[q];
+      }
+    }
+    __syncthreads();
+    remaining -= s.above;
+    active = s.count;
+    prefix |= s.digit << shift;
+    pmask |= dmask << shift;
+  }
+
+  if (active <= kWave) {
+    // pairwise ranks of the (at most 64) candidates tied on the prefix
+    if (tid == 0) s.n_active = 0;
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < RMAX; ++r) {
+      const uint32_t k = kk.k[r];
+      if (kk.valid(r) && (k & pmask) == prefix)
+        s.slot[atomicAdd(&s.n_active, 1)] = order_value(k, kk.index(r));
+    }
+    __syncthreads();
+    if (wave == 0) {
+      const int m = active;
+      const uint64_t v = lane < m ? s.slot[lane] : 0u;
+      int rank = 0;
+#pragma unroll 8
+      for (int j = 0; j < m; j += 2) {
+        const ulonglong2 p = *reinterpret_cast<const ulonglong2*>(&s.slot[j]);
+        rank += (p.x > v ? 1 : 0) + ((j + 1 < m && p.y > v) ? 1 : 0);
+      }
+      if (lane < m && rank == remaining - 1) s.cut = v;
+    }
+    __syncthreads();
+    return s.cut;
+  }
+  // every bit fixed and more than 64 keys equal the K-th key: its occurrence
+  // number `remaining` in index order is the cut
+  uint64_t eq = 0u;
+#pragma unroll
+  for (int r = 0; r < RMAX; ++r)
+    if (kk.valid(r) && kk.k[r] == prefix) eq |= uint64_t(1) << r;
+  const int R = (n + kSelThreads - 1) / kSelThreads;
+  sel_order_prepare(eq, R, s);
+#pragma unroll
+  for (int r = 0; r < RMAX; ++r) {
+    if (r < R) {
+      const int pos = sel_order_pos(eq, r, s);
+      if (((eq >> r) & 1u) && pos == remaining - 1) s.cut = order_value(prefix, kk.index(r));
+    }
+  }
+  __syncthreads();
+  return s.cut;
+}
+
+// Bit r set iff candidate threadIdx.x + 256 r is among the K best.
+template <int RMAX>
+__device__ __forceinline__ uint64_t sel_taken_mask(const SelKeys<RMAX>& kk, uint64_t cut) {
+  uint64_t m = 0u;
+#pragma unroll
+  for (int r = 0; r < RMAX; ++r)
+    if (kk.valid(r) && order_value(kk.k[r], kk.index(r)) >= cut) m |= uint64_t(1) << r;
+  return m;
+}
+
+}  // namespace skv

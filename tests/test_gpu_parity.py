@@ -316,6 +316,77 @@ def test_sparse_attention_over_oracle_selection(gpu_lib, seeds, H, Hkv, lens, kv
                     assert rel_err(out[b, hs], con) < contract_bar(meth, con)
 
 
+def _score_pattern(kind, nb, rng):
+    if kind == "distinct":
+        return rng.standard_normal(nb).astype(np.float32)
+    if kind == "shared-exponent":          # one binade: the leading key bits agree
+        return (100.0 + rng.random(nb)).astype(np.float32)
+    if kind == "few-values":               # large tie classes at the cut-off
+        return rng.integers(0, 10, nb).astype(np.float32)
+    if kind == "all-equal":
+        return np.full(nb, 3.5, np.float32)
+    if kind == "signed-zeros":             # -0 == +0, ties to the lower index
+        x = np.where(rng.random(nb) < 0.5, np.float32(-0.0), np.float32(0.0))
+        x[rng.random(nb) < 0.1] = 1e-30
+        return x.astype(np.float32)
+    if kind == "infinities":
+        x = rng.standard_normal(nb).astype(np.float32)
+        x[rng.random(nb) < 0.05] = np.inf
+        x[rng.random(nb) < 0.05] = -np.inf
+        return x
+    if kind == "near-ties":                # neighbours one ulp apart
+        base = np.float32(7.25)
+        steps = rng.integers(-300, 300, nb)
+        return np.array([np.nextafter(base, np.float32(np.inf * np.sign(t)) if t else base)
+                         if abs(t) == 1 else base + np.float32(t) * np.float32(1e-6)
+                         for t in steps], np.float32)
+    raise ValueError(kind)
+
+
+SELECT_CASES = [
+    # (pattern, n_blocks, k_sel per sequence, n_sink, n_recent)
+    ("distinct", 4096, [512, 1000], 1, 4),
+    ("shared-exponent", 4096, [512, 7], 1, 2),
+    ("few-values", 5000, [1500, 20], 2, 3),
+    ("all-equal", 1000, [300, 999], 1, 2),
+    ("signed-zeros", 3000, [700, 1], 1, 2),
+    ("infinities", 2000, [100, 1900], 0, 0),
+    ("near-ties", 3000, [900, 64], 1, 2),
+    ("distinct", 16384, [4096, 16000], 1, 4),
+    ("few-values", 300, [150, 1], 1, 1),
+    ("distinct", 5, [1, 2], 1, 1),
+]
+
+
+@pytest.mark.parametrize("kind,nb,k_sel,ns,nr", SELECT_CASES)
+def test_select_topk_on_given_scores(gpu_lib, kind, nb, k_sel, ns, nr):
+    """select_topk alone on host-made scores (every pattern of ties the
+    radix passes and the pairwise ranks meet) equals the oracle's rule, bit
+    for bit, on the same float32 scores."""
+    _print("select on given scores", kind, nb, k_sel)
+    rng = np.random.default_rng(nb * 31 + len(kind))
+    B, Hkv, blk = 2, 3, 16
+    score = np.stack([np.stack([_score_pattern(kind, nb, rng) for _ in range(Hkv)])
+                      for _ in range(B)])
+    lens = [nb * blk, nb * blk - blk // 2]          # second sequence: partial last block
+    max_sel = max(k_sel) + ns + nr
+    st = torch.from_numpy(score).to(DEV)
+    seq_len = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    ks = torch.tensor(k_sel, dtype=torch.int32, device=DEV)
+    sel = torch.empty((B, Hkv, max_sel), dtype=torch.int32, device=DEV)
+    cnt = torch.empty((B, Hkv), dtype=torch.int32, device=DEV)
+    skv.select_topk(st, seq_len, blk, ks, ns, nr, sel, cnt)
+    torch.cuda.synchronize()
+    sel, cnt = sel.cpu().numpy(), cnt.cpu().numpy()
+    for b in range(B):
+        n_blocks = -(-lens[b] // blk)
+        for g in range(Hkv):
+            ref = oracle.select_blocks(score[b, g], n_blocks, k_sel[b], ns, nr)["sel"]
+            assert cnt[b, g] == len(ref), (b, g)
+            assert np.array_equal(sel[b, g, :cnt[b, g]], ref), (b, g)
+            assert np.all(sel[b, g, cnt[b, g]:] == -1)
+
+
 def test_select_all_equals_dense(gpu_lib):
     """K_SEL = n_blocks makes sparse equal dense (sparse_attn.md, 'Gate
     ladder').  Same part boundaries => bit-identical output."""
