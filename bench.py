@@ -3,7 +3,9 @@
 A step is one pass of the whole hot path over one batch: append the new
 token (kv_append), Quest upper bounds (block_bounds), top-K selection
 (select_topk), attention over the selected blocks (decode_attn) and the
-split-K merge (combine).  The headline workload is the 32K-context GQA
+split-K merge (combine), issued as one skv_decode_step (three launches:
+append folded into the bounds pass, selection into the attention
+prologue); the same five calls issued one by one are timed too.  The headline workload is the 32K-context GQA
 decode (B=1, H=32, Hkv=8, D=128, f16 KV, block 64, K_SEL=128 + sink + 2
 recent); the same cache is also timed with dense decode (append +
 decode_attn + combine) for the sparse/dense ratio.  The other named
@@ -301,10 +303,8 @@ def measure(w, args, quest: bool, dense: bool, detail: bool = False):
         out_d = torch.empty((B, H, D), dtype=torch.float32, device=dev)
 
         def dense_step(i):
-            c = caches[i % R]
-            skv.kv_append(c, pos_last, new_k, new_v)
-            skv.decode_attn(c, q, seq_len, Lmax, w.softmax_scale, S_d, ws_d)
-            skv.combine(ws_d, B, H, D, S_d, out_d)
+            skv.decode_step(caches[i % R], q, seq_len, Lmax, w.softmax_scale, S_d, ws_d, out_d,
+                            pos0=pos_last, k_new=new_k, v_new=new_v)
 
         st = T.stream(dense_step)
         gr, n = T.graph(dense_step)
@@ -332,6 +332,12 @@ def measure(w, args, quest: bool, dense: bool, detail: bool = False):
         out_q = torch.empty((B, H, D), dtype=torch.float32, device=dev)
 
         def quest_step(i):
+            skv.decode_step(caches[i % R], q, seq_len, Lmax, w.softmax_scale, S_q, ws_q, out_q,
+                            pos0=pos_last, k_new=new_k, v_new=new_v, k_sel=ks,
+                            n_sink=w.n_sink, n_recent=w.n_recent, score=score, sel_idx=sel,
+                            sel_cnt=cnt)
+
+        def quest_calls(i):
             c = caches[i % R]
             skv.kv_append(c, pos_last, new_k, new_v)
             skv.block_bounds(c, q, seq_len, Lmax, score)
@@ -342,6 +348,8 @@ def measure(w, args, quest: bool, dense: bool, detail: bool = False):
         st = T.stream(quest_step)
         gr, n = T.graph(quest_step)
         us = (gr if gr is not None else st) * 1e6
+        gr_c, _ = T.graph(quest_calls)
+        calls_us = (gr_c if gr_c is not None else T.stream(quest_calls)) * 1e6
         quest_step(0)
         torch.cuda.synchronize()
         sel_h, cnt_h = sel.cpu().numpy(), cnt.cpu().numpy()
@@ -353,6 +361,7 @@ def measure(w, args, quest: bool, dense: bool, detail: bool = False):
         n_att = sum(len(x) for x in attended.values())
         n_all = sum(-(-L // blk) for L in w.lens) * Hkv
         res["quest"] = {"us_per_step": round(us, 3), "stream_us_per_step": round(st * 1e6, 3),
+                        "five_calls_us_per_step": round(calls_us, 3),
                         "steps": n, "n_split": S_q, "bytes_per_step": qb["total"],
                         "kv_bytes": qb["kv"], "bounds_bytes": qb["bounds"],
                         "blocks_attended_frac": round(n_att / n_all, 4),
@@ -440,9 +449,10 @@ def main():
         "dtype": "f16",
         "data": "synthetic",
         "config": {"workload": w3.name,
-                   "step": ("kv_append + block_bounds + select_topk + decode_attn(selected blocks)"
-                            " + combine") if hq is not None else
-                           "kv_append + decode_attn(dense) + combine",
+                   "step": ("decode_step: kv_append + block_bounds + select_topk + "
+                            "decode_attn(selected blocks) + combine in 3 launches")
+                           if hq is not None else
+                           "decode_step: kv_append + decode_attn(dense) + combine",
                    "cache_copies": head["cache_copies"],
                    "launch": "hipgraph" if not args.no_graph else "stream",
                    "n_split": top["n_split"]},

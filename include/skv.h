@@ -229,6 +229,49 @@ skv_status skv_decode_attn(const skv_cache* c, const float* q, int32_t n_heads,
 skv_status skv_combine(const void* workspace, int32_t batch, int32_t n_heads,
                        int32_t head_dim, int32_t n_split, float* out, hipStream_t stream);
 
+/*
+ * skv_decode_step — one whole decode step in three kernel launches.
+ * Defines: the composition of the calls above, in the order the pages run
+ * them (cpu-attn kernel card, "Usage": append the token, then decode;
+ * sparse_attn.md, "S2/S3 engineering design": fill the side cache, select,
+ * attend over the selected blocks).  The results -- out, the cache rows,
+ * scales and bounds, score, sel_idx, sel_cnt -- are bit-identical to
+ *     skv_kv_append(c, pos0, 1, k_new, v_new, src_dtype)        if k_new
+ *     skv_block_bounds(c, q, n_heads, seq_len, max_len, score)   if k_sel
+ *     skv_select_topk(score, seq_len, batch, n_kv_heads, max_blocks, block,
+ *                     k_sel, n_sink, n_recent, max_sel, sel_idx, sel_cnt,
+ *                     NULL)                                       if k_sel
+ *     skv_decode_attn(c, q, n_heads, seq_len, max_len, sel_idx | NULL,
+ *                     sel_cnt | NULL, max_sel, softmax_scale, n_split,
+ *                     workspace, workspace_bytes, NULL)
+ *     skv_combine(workspace, batch, n_heads, head_dim, n_split, out)
+ * with max_blocks = skv_max_blocks(c).  The append runs inside the bounds
+ * pass (Quest), and the selection inside the attention kernel's prologue
+ * (each part of a row recomputes it) when max_blocks <= 4096 and
+ * ceil(max_sel / n_split) <= 64; otherwise they run as their own kernels.
+ *   pos0, k_new, v_new, src_dtype : as skv_kv_append with n_new = 1
+ *            (k_new, v_new: [batch][1][n_kv_heads][head_dim]); k_new == NULL
+ *            skips the append (pos0, v_new, src_dtype ignored).
+ *   q, n_heads, seq_len, max_len : as skv_decode_attn; seq_len counts the
+ *            appended token.
+ *   k_sel  : device int32 [batch] Quest budget; NULL = dense decode (then
+ *            n_sink, n_recent, max_sel, score, sel_idx, sel_cnt are ignored).
+ *   n_sink, n_recent, max_sel, score, sel_idx, sel_cnt : as
+ *            skv_block_bounds / skv_select_topk; all required for Quest
+ *            (score is scratch the caller owns; sel_idx, sel_cnt are outputs).
+ *   softmax_scale, n_split, workspace, workspace_bytes : as skv_decode_attn.
+ *   out    : device float32 [batch][n_heads][head_dim].
+ * Errors: those of the composed calls (SKV_EINVAL, SKV_ERANGE,
+ * SKV_EWORKSPACE, SKV_EUNSUPPORTED, SKV_EDEVICE), checked before any launch.
+ */
+skv_status skv_decode_step(const skv_cache* c, const int32_t* pos0, const void* k_new,
+                           const void* v_new, int32_t src_dtype, const float* q,
+                           int32_t n_heads, const int32_t* seq_len, int32_t max_len,
+                           const int32_t* k_sel, int32_t n_sink, int32_t n_recent,
+                           int32_t max_sel, float* score, int32_t* sel_idx, int32_t* sel_cnt,
+                           float softmax_scale, int32_t n_split, void* workspace,
+                           size_t workspace_bytes, float* out, hipStream_t stream);
+
 /* Bytes of workspace skv_decode_attn needs: 4 * batch * n_heads * n_split *
  * (head_dim + 2); 0 for invalid arguments. */
 size_t skv_workspace_bytes(int32_t batch, int32_t n_heads, int32_t head_dim, int32_t n_split);

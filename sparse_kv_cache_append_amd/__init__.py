@@ -8,8 +8,9 @@ the computation runs in the library's HIP kernels; there is no Python or CPU
 fallback, and :func:`load` raises if the library is missing.
 
 The five calls keep the C names: :func:`kv_append`, :func:`block_bounds`,
-:func:`select_topk`, :func:`decode_attn`, :func:`combine` (plus
-:func:`workspace_bytes` and :func:`status_str`).  :class:`Cache` owns the
+:func:`select_topk`, :func:`decode_attn`, :func:`combine`, and so does the
+whole-step call :func:`decode_step` (plus :func:`workspace_bytes` and
+:func:`status_str`).  :class:`Cache` owns the
 cache tensors and the C descriptor; :func:`decode` chains the calls for one
 decode step (dense, or Quest when ``k_sel`` is given), the shape of the
 ``Int8KVCache.append`` / ``decode`` interface on the cpu-attn kernel card
@@ -23,7 +24,7 @@ import os
 from typing import Optional
 
 __all__ = ["load", "Cache", "SkvError", "kv_append", "block_bounds", "select_topk",
-           "decode_attn", "combine", "workspace_bytes", "status_str", "decode",
+           "decode_attn", "decode_step", "combine", "workspace_bytes", "status_str", "decode",
            "SKV_F16", "SKV_F32", "SKV_I8", "LIB_PATH", "EXPORTS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libskv.so")
@@ -32,7 +33,8 @@ SKV_OK, SKV_EINVAL, SKV_ERANGE, SKV_EWORKSPACE, SKV_EUNSUPPORTED, SKV_EDEVICE = 
 SKV_F16, SKV_F32, SKV_I8 = 1, 2, 3
 
 EXPORTS = ("skv_max_blocks", "skv_kv_append", "skv_block_bounds", "skv_select_topk",
-           "skv_decode_attn", "skv_combine", "skv_workspace_bytes", "skv_status_str")
+           "skv_decode_attn", "skv_decode_step", "skv_combine", "skv_workspace_bytes",
+           "skv_status_str")
 
 
 class SkvCacheDesc(ctypes.Structure):
@@ -71,6 +73,8 @@ def load(path: str = LIB_PATH):
         "skv_block_bounds": (I32, [desc, P, I32, P, I32, P, P]),
         "skv_select_topk": (I32, [P, P, I32, I32, I32, I32, P, I32, I32, I32, P, P, P, P]),
         "skv_decode_attn": (I32, [desc, P, I32, P, I32, P, P, I32, ctypes.c_float, I32, P, SZ, P, P]),
+        "skv_decode_step": (I32, [desc, P, P, P, I32, P, I32, P, I32, P, I32, I32, I32, P, P, P,
+                                   ctypes.c_float, I32, P, SZ, P, P]),
         "skv_combine": (I32, [P, I32, I32, I32, I32, P, P]),
         "skv_workspace_bytes": (SZ, [I32, I32, I32, I32]),
         "skv_status_str": (ctypes.c_char_p, [I32]),
@@ -199,6 +203,22 @@ def decode_attn(cache: Cache, q, seq_len, max_len: int, softmax_scale: float, n_
         _ptr(sel_idx), _ptr(sel_cnt), max_sel, float(softmax_scale), int(n_split),
         _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(dbg_logits),
         _stream(stream)))
+
+
+def decode_step(cache: Cache, q, seq_len, max_len: int, softmax_scale: float, n_split: int,
+                workspace, out, pos0=None, k_new=None, v_new=None, k_sel=None, n_sink: int = 1,
+                n_recent: int = 2, score=None, sel_idx=None, sel_cnt=None, stream=None):
+    """One decode step in three launches (skv_decode_step): optional one-token
+    append (k_new, v_new [batch][1][Hkv][D] at pos0), dense or Quest (k_sel)
+    attention, combine into ``out``.  Quest needs score [batch][Hkv][max_blocks]
+    scratch and sel_idx [batch][Hkv][max_sel] / sel_cnt [batch][Hkv] outputs."""
+    max_sel = int(sel_idx.shape[2]) if sel_idx is not None else 0
+    _check("skv_decode_step", load().skv_decode_step(
+        ctypes.byref(cache.desc), _ptr(pos0), _ptr(k_new), _ptr(v_new), cache.src_dtype(),
+        _ptr(q), int(q.shape[1]), _ptr(seq_len), int(max_len), _ptr(k_sel), int(n_sink),
+        int(n_recent), max_sel, _ptr(score), _ptr(sel_idx), _ptr(sel_cnt),
+        float(softmax_scale), int(n_split), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _ptr(out), _stream(stream)))
 
 
 def combine(workspace, batch: int, n_heads: int, head_dim: int, n_split: int, out, stream=None):

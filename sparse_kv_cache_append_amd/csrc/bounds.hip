@@ -11,6 +11,9 @@
 // D = 128), so it is spread over as many workgroups as there are 16-block
 // tiles: 16 lanes per block, each lane holding 8 channels (one 16-byte load of
 // kmin and one of kmax), a 16-lane DPP sum per head, then the group max.
+//
+// A decode step may fold its one-token append into this pass
+// (launch_append_bounds), which saves a launch and a dependent round trip.
 #include "device_common.h"
 #include "launch.h"
 
@@ -21,14 +24,94 @@ constexpr int kBoundsThreads = 256;
 constexpr int kLanesPerBlock = 16;
 constexpr int kBlocksPerWG = kBoundsThreads / kLanesPerBlock;  // 16
 
-template <int D, int G>
+enum AppendMode { kNoAppend = 0, kAppendF16 = 1, kAppendI8 = 2 };
+
+// Write the new token of (sequence b, KV head g) at position p0 -- the
+// one-token case of skv_kv_append, same arithmetic -- and its block's bounds.
+template <int D, int MODE>
+__device__ __forceinline__ void append_one(const AppendOne& ap, uint16_t* __restrict__ kmin,
+                                           uint16_t* __restrict__ kmax, int32_t b, int32_t g,
+                                           int32_t Hkv, int32_t p0, int32_t jn, bool fresh,
+                                           int32_t max_blocks) {
+  const int tid = threadIdx.x;
+  const int64_t bg = int64_t(b) * Hkv + g;
+  const int64_t row = bg * ap.max_seq + p0;
+  const int64_t bo = (bg * max_blocks + jn) * D;
+  if constexpr (MODE == kAppendF16) {
+    constexpr int kVec = D * 2 / 16;
+    const uint4* ks = reinterpret_cast<const uint4*>(ap.k_new) + bg * kVec;
+    const uint4* vs = reinterpret_cast<const uint4*>(ap.v_new) + bg * kVec;
+    if (tid < kVec) reinterpret_cast<uint4*>(ap.k)[row * kVec + tid] = ks[tid];
+    else if (tid < 2 * kVec) reinterpret_cast<uint4*>(ap.v)[row * kVec + tid - kVec] = vs[tid - kVec];
+    const uint16_t* kn = static_cast<const uint16_t*>(ap.k_new) + bg * D;
+    for (int d = tid; d < D; d += kBoundsThreads) {
+      const uint16_t x = kn[d];
+      uint16_t bmn = x, bmx = x;
+      if (!fresh) {
+        bmn = f16_min_bits(kmin[bo + d], bmn);
+        bmx = f16_max_bits(kmax[bo + d], bmx);
+      }
+      kmin[bo + d] = bmn;
+      kmax[bo + d] = bmx;
+    }
+  } else {
+    static_assert(D % kWave == 0, "D must be a multiple of 64");
+    constexpr int E = D / kWave;
+    const int lane = tid % kWave, wave = tid / kWave;
+    if (wave < 2) {
+      const float* x = static_cast<const float*>(wave == 0 ? ap.k_new : ap.v_new) + bg * D;
+      float xv[E];
+      float am = 0.0f;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        xv[e] = x[lane * E + e];
+        am = fmaxf(am, fabsf(xv[e]));
+      }
+      am = wave_max(am);
+      const float scale = absmax_scale(am);
+      int8_t* dst = static_cast<int8_t*>(wave == 0 ? ap.k : ap.v) + row * D + lane * E;
+#pragma unroll
+      for (int e = 0; e < E; ++e) dst[e] = int8_t(quant_code(xv[e], scale));
+      if (lane == 0) (wave == 0 ? ap.ks : ap.vs)[row] = scale;
+    }
+    const float* kn = static_cast<const float*>(ap.k_new) + bg * D;
+    for (int d = tid; d < D; d += kBoundsThreads) {
+      const float x = kn[d];
+      uint16_t bmn = f32_to_f16_down(x), bmx = f32_to_f16_up(x);
+      if (!fresh) {
+        bmn = f16_min_bits(kmin[bo + d], bmn);
+        bmx = f16_max_bits(kmax[bo + d], bmx);
+      }
+      kmin[bo + d] = bmn;
+      kmax[bo + d] = bmx;
+    }
+  }
+}
+
+// MODE != kNoAppend: first append one token per sequence at pos0[b] (the
+// first workgroup of each (sequence, KV head) writes it) and score its block
+// with the merged bounds.  The merge is computed from the new key in
+// registers, so it does not matter whether this workgroup reads the side
+// cache before or after the append writes it: min/max with the same key is
+// idempotent, and a fresh block ignores the old values.
+template <int D, int G, int MODE>
 __global__ void __launch_bounds__(kBoundsThreads)
-bounds_kernel(const uint16_t* __restrict__ kmin, const uint16_t* __restrict__ kmax,
+bounds_kernel(uint16_t* __restrict__ kmin, uint16_t* __restrict__ kmax,
               const float* __restrict__ q, const int32_t* __restrict__ seq_len,
               float* __restrict__ score, int32_t Hkv, int32_t max_len, int32_t block,
-              int32_t max_blocks) {
+              int32_t max_blocks, AppendOne ap) {
   static_assert(D == kLanesPerBlock * 8, "one 16-byte load per lane per bound");
   const int32_t g = blockIdx.y, b = blockIdx.z;
+  int32_t jn = -1;
+  bool fresh = false;
+  if constexpr (MODE != kNoAppend) {
+    const int32_t p0 = ap.pos0[b];
+    if (p0 >= 0 && p0 < ap.max_seq) {
+      jn = p0 / block;
+      fresh = (p0 % block) == 0;
+      if (blockIdx.x == 0) append_one<D, MODE>(ap, kmin, kmax, b, g, Hkv, p0, jn, fresh, max_blocks);
+    }
+  }
   const int32_t L = min(max(seq_len[b], 0), max_len);
   const int32_t nb = (L + block - 1) / block;
   const int32_t j = int32_t(blockIdx.x) * kBlocksPerWG + int32_t(threadIdx.x) / kLanesPerBlock;
@@ -52,14 +135,37 @@ bounds_kernel(const uint16_t* __restrict__ kmin, const uint16_t* __restrict__ km
     lo = *reinterpret_cast<const uint4*>(kmin + off);
     hi = *reinterpret_cast<const uint4*>(kmax + off);
   }
-  float mn[8], mx[8];
-  const uint32_t lw[4] = {lo.x, lo.y, lo.z, lo.w};
-  const uint32_t hw[4] = {hi.x, hi.y, hi.z, hi.w};
+  uint16_t lb[8], hb[8];
+  {
+    const uint32_t lw[4] = {lo.x, lo.y, lo.z, lo.w};
+    const uint32_t hw[4] = {hi.x, hi.y, hi.z, hi.w};
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    mn[2 * i] = h2f_lo(lw[i]); mn[2 * i + 1] = h2f_hi(lw[i]);
-    mx[2 * i] = h2f_lo(hw[i]); mx[2 * i + 1] = h2f_hi(hw[i]);
+    for (int i = 0; i < 4; ++i) {
+      lb[2 * i] = uint16_t(lw[i] & 0xFFFFu); lb[2 * i + 1] = uint16_t(lw[i] >> 16);
+      hb[2 * i] = uint16_t(hw[i] & 0xFFFFu); hb[2 * i + 1] = uint16_t(hw[i] >> 16);
+    }
   }
+  if constexpr (MODE != kNoAppend) {
+    if (live && j == jn) {
+      const int64_t src = (int64_t(b) * Hkv + g) * D + c * 8;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        uint16_t nmn, nmx;
+        if constexpr (MODE == kAppendF16) {
+          nmn = nmx = static_cast<const uint16_t*>(ap.k_new)[src + e];
+        } else {
+          const float x = static_cast<const float*>(ap.k_new)[src + e];
+          nmn = f32_to_f16_down(x);
+          nmx = f32_to_f16_up(x);
+        }
+        lb[e] = fresh ? nmn : f16_min_bits(lb[e], nmn);
+        hb[e] = fresh ? nmx : f16_max_bits(hb[e], nmx);
+      }
+    }
+  }
+  float mn[8], mx[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) { mn[e] = h2f(lb[e]); mx[e] = h2f(hb[e]); }
   float best = -INFINITY;
 #pragma unroll
   for (int h = 0; h < G; ++h) {
@@ -76,16 +182,31 @@ bounds_kernel(const uint16_t* __restrict__ kmin, const uint16_t* __restrict__ km
   if (live && c == 0) score[(int64_t(b) * Hkv + g) * max_blocks + j] = best;
 }
 
-template <int G>
+template <int G, int MODE>
 void launch_bounds_g(const skv_cache& c, const float* q, const int32_t* seq_len,
-                     int32_t max_len, float* score, hipStream_t stream) {
+                     int32_t max_len, float* score, const AppendOne& ap, hipStream_t stream) {
   const int32_t max_blocks = (c.max_seq + c.block - 1) / c.block;
   const int32_t nb_max = (max_len + c.block - 1) / c.block;
-  const int32_t tiles = (nb_max + kBlocksPerWG - 1) / kBlocksPerWG;
+  int32_t tiles = (nb_max + kBlocksPerWG - 1) / kBlocksPerWG;
+  if (MODE != kNoAppend && tiles == 0) tiles = 1;           // the append still runs
   if (tiles == 0) return;
   dim3 grid(tiles, c.n_kv_heads, c.batch);
-  bounds_kernel<128, G><<<grid, kBoundsThreads, 0, stream>>>(
-      c.kmin, c.kmax, q, seq_len, score, c.n_kv_heads, max_len, c.block, max_blocks);
+  bounds_kernel<128, G, MODE><<<grid, kBoundsThreads, 0, stream>>>(
+      c.kmin, c.kmax, q, seq_len, score, c.n_kv_heads, max_len, c.block, max_blocks, ap);
+}
+
+template <int MODE>
+hipError_t launch_bounds_m(const skv_cache& c, const float* q, int32_t n_heads,
+                           const int32_t* seq_len, int32_t max_len, float* score,
+                           const AppendOne& ap, hipStream_t stream) {
+  switch (n_heads / c.n_kv_heads) {
+    case 1: launch_bounds_g<1, MODE>(c, q, seq_len, max_len, score, ap, stream); break;
+    case 2: launch_bounds_g<2, MODE>(c, q, seq_len, max_len, score, ap, stream); break;
+    case 4: launch_bounds_g<4, MODE>(c, q, seq_len, max_len, score, ap, stream); break;
+    case 8: launch_bounds_g<8, MODE>(c, q, seq_len, max_len, score, ap, stream); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -93,14 +214,17 @@ void launch_bounds_g(const skv_cache& c, const float* q, const int32_t* seq_len,
 hipError_t launch_bounds(const skv_cache& c, const float* q, int32_t n_heads,
                          const int32_t* seq_len, int32_t max_len, float* score,
                          hipStream_t stream) {
-  switch (n_heads / c.n_kv_heads) {
-    case 1: launch_bounds_g<1>(c, q, seq_len, max_len, score, stream); break;
-    case 2: launch_bounds_g<2>(c, q, seq_len, max_len, score, stream); break;
-    case 4: launch_bounds_g<4>(c, q, seq_len, max_len, score, stream); break;
-    case 8: launch_bounds_g<8>(c, q, seq_len, max_len, score, stream); break;
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
+  return launch_bounds_m<kNoAppend>(c, q, n_heads, seq_len, max_len, score, AppendOne{}, stream);
+}
+
+hipError_t launch_append_bounds(const skv_cache& c, const int32_t* pos0, const void* k_new,
+                                const void* v_new, const float* q, int32_t n_heads,
+                                const int32_t* seq_len, int32_t max_len, float* score,
+                                hipStream_t stream) {
+  AppendOne ap{c.k, c.v, c.k_scale, c.v_scale, k_new, v_new, pos0, c.max_seq};
+  if (c.kv_dtype == SKV_F16)
+    return launch_bounds_m<kAppendF16>(c, q, n_heads, seq_len, max_len, score, ap, stream);
+  return launch_bounds_m<kAppendI8>(c, q, n_heads, seq_len, max_len, score, ap, stream);
 }
 
 }  // namespace skv

@@ -33,6 +33,7 @@
 
 #include "device_common.h"
 #include "launch.h"
+#include "select_core.h"
 
 namespace skv {
 namespace {
@@ -47,6 +48,7 @@ typedef int int2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kMWaves = 4;
 constexpr int kMThreads = kMWaves * kWave;
+static_assert(kMThreads == kSelThreads, "the selection prologue runs on the whole workgroup");
 constexpr int kD = 128;
 constexpr int kRowBytesF16 = kD * 2;   // 256
 constexpr int kRowBytesI8 = kD;        // 128
@@ -114,6 +116,78 @@ __device__ __forceinline__ TileWalk make_walk(const int32_t* sel_idx, const int3
     total = min(max(cnt, 0), max_sel);
   }
   tw.n_units = max(0, min(units_per_split, total - tw.u0));
+  return tw;
+}
+
+// The part's walk when the block selection runs in this workgroup's prologue
+// (the same selection as skv_select_topk, computed redundantly by every part
+// of the row: a workgroup-local job of a few microseconds that replaces a
+// launch and a round trip through memory).  All threads call this.  The
+// part's slice of the ascending list goes to LDS; split 0 also publishes
+// the whole list and its count.
+template <int T, int SELR>
+__device__ __forceinline__ TileWalk fused_walk(const FusedSelect& fs, int32_t max_sel, int64_t bg,
+                                               int32_t b, int32_t L, int32_t L_raw, int32_t block,
+                                               int32_t split, int32_t units_per_split) {
+  __shared__ SelectShared ssh;
+  __shared__ int32_t plist[kWave];
+  const int tid = threadIdx.x;
+  TileWalk tw;
+  tw.block = block;
+  tw.L = L;
+  tw.nb = (L + block - 1) / block;
+  tw.tpb = (block + T - 1) / T;
+  tw.sel = fs.sel_idx;                     // non-null: sparse walk (entries come from jl)
+  tw.u0 = split * units_per_split;
+  // the selection sees the length as skv_select_topk clamps it; blocks past
+  // this kernel's own length are skipped by the walk, as for a given list
+  const int32_t L_sel = min(max(L_raw, 0), fs.max_blocks * block);
+  const int32_t nb = (L_sel + block - 1) / block;
+  const int32_t cs = min(fs.n_sink, nb);                    // candidates [cs, ce)
+  const int32_t ce = max(nb - fs.n_recent, cs);
+  const int32_t n_cand = ce - cs;
+  const int32_t K = min(max(fs.k_sel[b], 0), n_cand);
+  const int32_t n_sel = cs + K + (nb - ce);
+  const int32_t u0 = tw.u0, ups = units_per_split;
+  const bool publish = split == 0;
+  int32_t* out_row = fs.sel_idx + bg * max_sel;
+  // positions whose block follows from the counts alone
+  auto arith = [&](int32_t pos) { return pos < cs || pos >= cs + K || K == n_cand; };
+  auto block_at = [&](int32_t pos) { return pos < cs + K ? pos : ce + (pos - cs - K); };
+  if (tid < ups) {
+    const int32_t pos = u0 + tid;
+    if (pos < n_sel && arith(pos)) plist[tid] = block_at(pos);
+  }
+  if (publish) {
+    for (int32_t p = tid; p < max_sel; p += kMThreads) {
+      if (p >= n_sel) out_row[p] = -1;
+      else if (arith(p)) out_row[p] = block_at(p);
+    }
+    if (tid == 0) fs.sel_cnt[bg] = n_sel;
+  }
+  if (K > 0 && K < n_cand) {
+    SelKeys<SELR> kk;
+    kk.load(fs.score + bg * fs.max_blocks + cs, n_cand);
+    const uint64_t cut = sel_cut(kk, K, ssh);
+    const uint64_t taken = sel_taken_mask(kk, cut);
+    const int R = (n_cand + kSelThreads - 1) / kSelThreads;
+    sel_order_prepare(taken, R, ssh);
+#pragma unroll
+    for (int r = 0; r < SELR; ++r) {
+      if (r < R) {
+        const int32_t pos = cs + sel_order_pos(taken, r, ssh);
+        if ((taken >> r) & 1u) {
+          const int32_t blk = cs + kk.index(r);
+          if (pos >= u0 && pos < u0 + ups) plist[pos - u0] = blk;
+          if (publish && pos < max_sel) out_row[pos] = blk;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  const int lane = tid % kWave;
+  tw.jl = lane < ups ? plist[lane] : -1;
+  tw.n_units = max(0, min(ups, min(n_sel, max_sel) - u0));
   return tw;
 }
 
@@ -212,14 +286,15 @@ __device__ __forceinline__ void finish_mfma(float m_run, float l_run, const floa
 
 // ------------------------------------------------------------------ f16
 // Tile = 16 tokens: K and V tiles are 4 KiB each (4 load instructions).
-template <int G, int P>
+template <int G, int SELR>
 __global__ void __launch_bounds__(kMThreads, 2)
 decode_f16_mfma(const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
                 const float* __restrict__ q, const int32_t* __restrict__ seq_len,
                 const int32_t* __restrict__ sel_idx, const int32_t* __restrict__ sel_cnt,
                 int32_t max_sel, int32_t Hkv, int32_t max_seq, int32_t block, int32_t max_len,
                 int32_t n_split, int32_t units_per_split, float qscale2,
-                float* __restrict__ ws_m, float* __restrict__ ws_l, float* __restrict__ ws_o) {
+                float* __restrict__ ws_m, float* __restrict__ ws_l, float* __restrict__ ws_o,
+                FusedSelect fs) {
   constexpr int T = 16;
   constexpr int kTileBytes = T * kRowBytesF16;              // 4096
   __shared__ __attribute__((aligned(16))) uint8_t smem[kMWaves][2][2 * kTileBytes];
@@ -229,8 +304,6 @@ decode_f16_mfma(const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc
   const int32_t H = Hkv * G;
   const int32_t L = min(max(seq_len[b], 0), max_len);
   const int64_t bg = int64_t(b) * Hkv + g;
-  TileWalk tw = make_walk<T>(sel_idx, sel_cnt, max_sel, bg, L, block, split, units_per_split);
-  tw.init(wave);
 
   // query as the B operand of q.K: column = head lc, k-chunk = lg; f16 hi + lo
   half8_t qhi[4], qlo[4];
@@ -251,6 +324,12 @@ decode_f16_mfma(const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc
       }
     }
   }
+  TileWalk tw;
+  if constexpr (SELR > 0)
+    tw = fused_walk<T, SELR>(fs, max_sel, bg, b, L, seq_len[b], block, split, units_per_split);
+  else
+    tw = make_walk<T>(sel_idx, sel_cnt, max_sel, bg, L, block, split, units_per_split);
+  tw.init(wave);
   float m_run = -INFINITY, l_run = 0.0f;
   float4_t O[8];
 #pragma unroll
@@ -372,7 +451,7 @@ __device__ __forceinline__ half8_t widen_codes(int2_t w) {
   return r;
 }
 
-template <int G>
+template <int G, int SELR>
 __global__ void __launch_bounds__(kMThreads, 2)
 decode_i8_mfma(const int8_t* __restrict__ kc, const int8_t* __restrict__ vc,
                const float* __restrict__ ksc, const float* __restrict__ vsc,
@@ -381,7 +460,7 @@ decode_i8_mfma(const int8_t* __restrict__ kc, const int8_t* __restrict__ vc,
                int32_t max_sel, int32_t Hkv, int32_t max_seq, int32_t block, int32_t max_len,
                int32_t n_split, int32_t units_per_split, float scale2,
                float* __restrict__ ws_m, float* __restrict__ ws_l, float* __restrict__ ws_o,
-               int32_t* __restrict__ dbg) {
+               int32_t* __restrict__ dbg, FusedSelect fs) {
   constexpr int T = 32;
   constexpr int kTileBytes = T * kRowBytesI8;               // 4096
   constexpr int kScaleOff = 2 * kTileBytes;                 // 32 K scales, 32 V scales
@@ -393,8 +472,6 @@ decode_i8_mfma(const int8_t* __restrict__ kc, const int8_t* __restrict__ vc,
   const int32_t H = Hkv * G;
   const int32_t L = min(max(seq_len[b], 0), max_len);
   const int64_t bg = int64_t(b) * Hkv + g;
-  TileWalk tw = make_walk<T>(sel_idx, sel_cnt, max_sel, bg, L, block, split, units_per_split);
-  tw.init(wave);
 
   // Query codes as the B operand of q.K (column = head lc, k-chunk lg): the
   // head's absmax scale over all 128 channels (the 4 lanes of a column hold
@@ -431,6 +508,12 @@ decode_i8_mfma(const int8_t* __restrict__ kc, const int8_t* __restrict__ vc,
     }
     coef = hv ? qs * scale2 : 0.0f;
   }
+  TileWalk tw;
+  if constexpr (SELR > 0)
+    tw = fused_walk<T, SELR>(fs, max_sel, bg, b, L, seq_len[b], block, split, units_per_split);
+  else
+    tw = make_walk<T>(sel_idx, sel_cnt, max_sel, bg, L, block, split, units_per_split);
+  tw.init(wave);
   float m_run = -INFINITY, l_run = 0.0f;
   float4_t O[8];
 #pragma unroll
@@ -571,33 +654,38 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   }
   dim3 grid(S, c.n_kv_heads, B);
   const float scale2 = p.softmax_scale * kLog2e;
+  const bool fused = p.fused;
   if (c.kv_dtype == SKV_F16) {
-#define SKV_LAUNCH_F16(GG)                                                                      \
-  decode_f16_mfma<GG, 2><<<grid, kMThreads, 0, stream>>>(                                      \
+#define SKV_LAUNCH_F16(GG, SR)                                                                  \
+  decode_f16_mfma<GG, SR><<<grid, kMThreads, 0, stream>>>(                                     \
       static_cast<const uint16_t*>(c.k), static_cast<const uint16_t*>(c.v), p.q, p.seq_len,    \
       p.sel_idx, p.sel_cnt, p.max_sel, c.n_kv_heads, c.max_seq, c.block, p.max_len, S, ups,    \
-      scale2, ws_m, ws_l, ws_o)
+      scale2, ws_m, ws_l, ws_o, p.fsel)
+#define SKV_F16_G(GG) if (fused) SKV_LAUNCH_F16(GG, kFusedSelR); else SKV_LAUNCH_F16(GG, 0)
     switch (G) {
-      case 1: SKV_LAUNCH_F16(1); break;
-      case 2: SKV_LAUNCH_F16(2); break;
-      case 4: SKV_LAUNCH_F16(4); break;
-      default: SKV_LAUNCH_F16(8); break;
+      case 1: SKV_F16_G(1); break;
+      case 2: SKV_F16_G(2); break;
+      case 4: SKV_F16_G(4); break;
+      default: SKV_F16_G(8); break;
     }
+#undef SKV_F16_G
 #undef SKV_LAUNCH_F16
     return hipGetLastError();
   }
   if (c.kv_dtype != SKV_I8) return hipErrorInvalidValue;
-#define SKV_LAUNCH_I8(GG)                                                                       \
-  decode_i8_mfma<GG><<<grid, kMThreads, 0, stream>>>(                                          \
+#define SKV_LAUNCH_I8(GG, SR)                                                                   \
+  decode_i8_mfma<GG, SR><<<grid, kMThreads, 0, stream>>>(                                      \
       static_cast<const int8_t*>(c.k), static_cast<const int8_t*>(c.v), c.k_scale, c.v_scale,  \
       p.q, p.seq_len, p.sel_idx, p.sel_cnt, p.max_sel, c.n_kv_heads, c.max_seq, c.block,       \
-      p.max_len, S, ups, scale2, ws_m, ws_l, ws_o, p.dbg_logits)
+      p.max_len, S, ups, scale2, ws_m, ws_l, ws_o, p.dbg_logits, p.fsel)
+#define SKV_I8_G(GG) if (fused) SKV_LAUNCH_I8(GG, kFusedSelR); else SKV_LAUNCH_I8(GG, 0)
   switch (G) {
-    case 1: SKV_LAUNCH_I8(1); break;
-    case 2: SKV_LAUNCH_I8(2); break;
-    case 4: SKV_LAUNCH_I8(4); break;
-    default: SKV_LAUNCH_I8(8); break;
+    case 1: SKV_I8_G(1); break;
+    case 2: SKV_I8_G(2); break;
+    case 4: SKV_I8_G(4); break;
+    default: SKV_I8_G(8); break;
   }
+#undef SKV_I8_G
 #undef SKV_LAUNCH_I8
   return hipGetLastError();
 }

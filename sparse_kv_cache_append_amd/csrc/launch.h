@@ -10,6 +10,21 @@
 
 namespace skv {
 
+// Block selection folded into decode_attn's prologue (see skv_decode_step):
+// the score row, the budget and the outputs of skv_select_topk.
+struct FusedSelect {
+  const float* score;
+  int32_t max_blocks;
+  const int32_t* k_sel;
+  int32_t n_sink;
+  int32_t n_recent;
+  int32_t* sel_idx;
+  int32_t* sel_cnt;
+};
+// Largest candidate row the folded selection handles (keys per thread x 256).
+constexpr int kFusedSelR = 16;
+constexpr int32_t kFusedSelMaxCand = kFusedSelR * 256;
+
 struct DecodeParams {
   const skv_cache* c;
   const float* q;
@@ -23,6 +38,8 @@ struct DecodeParams {
   int32_t n_split;
   float* ws;
   int32_t* dbg_logits;
+  bool fused = false;       // select in the prologue from fsel (sel_idx/sel_cnt unused)
+  FusedSelect fsel{};
 };
 
 hipError_t launch_append(const skv_cache& c, const int32_t* pos0, int32_t n_new,
@@ -31,6 +48,24 @@ hipError_t launch_append(const skv_cache& c, const int32_t* pos0, int32_t n_new,
 hipError_t launch_bounds(const skv_cache& c, const float* q, int32_t n_heads,
                          const int32_t* seq_len, int32_t max_len, float* score,
                          hipStream_t stream);
+
+// One new token per sequence ([batch][1][n_kv_heads][head_dim] of the cache's
+// source dtype), written at pos0[b], folded into the bounds pass.
+struct AppendOne {
+  void* k;
+  void* v;
+  float* ks;
+  float* vs;
+  const void* k_new;
+  const void* v_new;
+  const int32_t* pos0;
+  int32_t max_seq;
+};
+
+hipError_t launch_append_bounds(const skv_cache& c, const int32_t* pos0, const void* k_new,
+                                const void* v_new, const float* q, int32_t n_heads,
+                                const int32_t* seq_len, int32_t max_len, float* score,
+                                hipStream_t stream);
 
 hipError_t launch_select(const float* score, const int32_t* seq_len, int32_t batch,
                          int32_t n_kv_heads, int32_t max_blocks, int32_t block,

@@ -1,0 +1,222 @@
+"""skv_decode_step against the five calls it composes.
+
+The step folds the one-token append into the bounds pass and the block
+selection into the attention kernel's prologue; neither changes any
+arithmetic, so every result must be bit-identical to kv_append ->
+block_bounds -> select_topk -> decode_attn -> combine on an identical cache:
+the output, the appended rows, scales and side-cache bounds, the scores and
+the selected lists.  The fallback paths (selection as its own kernel when a
+part spans more than 64 list entries or a row has more than 4096 blocks; the
+dense step) are held to the same bar.  One output per case is also checked
+against the float64 oracle.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_kv_cache_append_amd as skv
+import workloads
+from gpu_harness import DEV, quantized_host, rel_err
+
+pytestmark = pytest.mark.gpu
+
+
+def _print(*a):
+    print("[step]", *a, flush=True)
+
+
+def _prefilled(w, max_seq=None, whole=False):
+    """Cache holding tokens 0 .. L_b - 2 of every sequence (all L_b with
+    ``whole``); rows past them are copies of the last one, or zeros: they
+    never change a bound that is read, and the step's append rewrites
+    position L_b - 1."""
+    keep = 0 if whole else 1
+    rows = max(w.lens) - keep
+    cache = skv.Cache(w.B, w.Hkv, max_seq or max(w.lens), w.D, w.kv_dtype, w.block,
+                      bounds=True, device=DEV)
+    if rows == 0:
+        return cache
+    dt = np.float16 if w.kv_dtype == "f16" else np.float32
+    k = np.zeros((w.B, rows, w.Hkv, w.D), dt)
+    v = np.zeros((w.B, rows, w.Hkv, w.D), dt)
+    for b, L in enumerate(w.lens):
+        n = L - keep
+        if n > 0:
+            k[b, :n] = np.transpose(w.k[b][:, :n], (1, 0, 2))
+            v[b, :n] = np.transpose(w.v[b][:, :n], (1, 0, 2))
+            k[b, n:] = k[b, n - 1]
+            v[b, n:] = v[b, n - 1]
+    skv.kv_append(cache, torch.zeros(w.B, dtype=torch.int32, device=DEV),
+                  torch.from_numpy(k).to(DEV), torch.from_numpy(v).to(DEV))
+    torch.cuda.synchronize()
+    return cache
+
+
+def _new_token(w):
+    dt = torch.float16 if w.kv_dtype == "f16" else torch.float32
+    k = np.stack([w.k[b][:, L - 1] for b, L in enumerate(w.lens)])[:, None]
+    v = np.stack([w.v[b][:, L - 1] for b, L in enumerate(w.lens)])[:, None]
+    pos = torch.tensor([L - 1 for L in w.lens], dtype=torch.int32, device=DEV)
+    return (pos, torch.from_numpy(np.ascontiguousarray(k)).to(DEV).to(dt),
+            torch.from_numpy(np.ascontiguousarray(v)).to(DEV).to(dt))
+
+
+def _buffers(w, cache, quest, max_sel, S):
+    out = torch.full((w.B, w.H, w.D), float("nan"), device=DEV)
+    ws = torch.empty(skv.workspace_bytes(w.B, w.H, w.D, S), dtype=torch.uint8, device=DEV)
+    if not quest:
+        return out, ws, None, None, None
+    score = torch.full((w.B, w.Hkv, cache.max_blocks), float("nan"), device=DEV)
+    sel = torch.full((w.B, w.Hkv, max_sel), -7, dtype=torch.int32, device=DEV)
+    cnt = torch.full((w.B, w.Hkv), -7, dtype=torch.int32, device=DEV)
+    return out, ws, score, sel, cnt
+
+
+def _cache_tensors(c):
+    return [t for t in (c.k, c.v, c.k_scale, c.v_scale, c.kmin, c.kmax) if t is not None]
+
+
+def _run_case(w, quest, append, S=None, max_seq=None, max_sel=None):
+    base = _prefilled(w, max_seq, whole=not append)
+    ca, cb = base.clone(), base.clone()
+    q = torch.from_numpy(np.ascontiguousarray(w.q)).to(DEV)
+    seq_len = torch.tensor(w.lens, dtype=torch.int32, device=DEV)
+    max_len = max(w.lens)
+    ks = torch.tensor(w.k_sel, dtype=torch.int32, device=DEV) if quest else None
+    if quest:
+        max_sel = max_sel or (max(w.k_sel) + w.n_sink + w.n_recent)
+        S = S or skv.default_split(w.B, w.Hkv, max_sel)
+    else:
+        S = S or skv.default_split(w.B, w.Hkv, -(-max_len // w.block))
+    pos, kn, vn = _new_token(w)
+    out_a, ws_a, sc_a, sel_a, cnt_a = _buffers(w, ca, quest, max_sel, S)
+    out_b, ws_b, sc_b, sel_b, cnt_b = _buffers(w, cb, quest, max_sel, S)
+    # composed calls
+    if append:
+        skv.kv_append(ca, pos, kn, vn)
+    if quest:
+        skv.block_bounds(ca, q, seq_len, max_len, sc_a)
+        skv.select_topk(sc_a, seq_len, w.block, ks, w.n_sink, w.n_recent, sel_a, cnt_a)
+        skv.decode_attn(ca, q, seq_len, max_len, w.softmax_scale, S, ws_a, sel_a, cnt_a)
+    else:
+        skv.decode_attn(ca, q, seq_len, max_len, w.softmax_scale, S, ws_a)
+    skv.combine(ws_a, w.B, w.H, w.D, S, out_a)
+    # one step
+    skv.decode_step(cb, q, seq_len, max_len, w.softmax_scale, S, ws_b, out_b,
+                    pos0=pos if append else None, k_new=kn if append else None,
+                    v_new=vn if append else None, k_sel=ks, n_sink=w.n_sink,
+                    n_recent=w.n_recent, score=sc_b, sel_idx=sel_b, sel_cnt=cnt_b)
+    torch.cuda.synchronize()
+    assert torch.equal(out_a, out_b)
+    for ta, tb in zip(_cache_tensors(ca), _cache_tensors(cb)):
+        assert torch.equal(ta, tb)
+    if quest:
+        assert torch.equal(sel_a, sel_b)
+        assert torch.equal(cnt_a, cnt_b)
+        for b, L in enumerate(w.lens):
+            nb = -(-L // w.block)
+            assert torch.equal(sc_a[b, :, :nb], sc_b[b, :, :nb])
+    return out_b.cpu().numpy(), (sel_b.cpu().numpy(), cnt_b.cpu().numpy()) if quest else None
+
+
+def _oracle_check(w, out, sel):
+    """Sequence 0's output against the float64 definition over the step's
+    own selected blocks (f16 within 1e-3; int8 within 1e-4 of the method)."""
+    G = w.G
+    for g in range(w.Hkv):
+        hs = slice(g * G, (g + 1) * G)
+        toks = None
+        if sel is not None:
+            s, c = sel
+            toks = oracle.selected_tokens(s[0, g, :c[0, g]], w.lens[0], w.block)
+        if w.kv_dtype == "f16":
+            ref = oracle.attend_f16(w.q[0][hs], w.k[0][g:g + 1], w.v[0][g:g + 1],
+                                    w.softmax_scale, tokens=toks)
+            assert rel_err(out[0, hs], ref) < 1e-3
+        else:
+            kc, ksc, vc, vsc = quantized_host(w, 0)
+            sl = slice(g, g + 1)
+            ref = oracle.attend_i8(w.q[0][hs], kc[sl], ksc[sl], vc[sl], vsc[sl],
+                                   w.softmax_scale, tokens=toks)
+            assert rel_err(out[0, hs], ref) < 1e-4
+
+
+STEP_CASES = [
+    # name, workload factory, quest, append, extra
+    ("quest-f16 fresh+mid block", lambda: workloads.clustered(
+        [501, 502], 32, 8, 128, [2049, 3000], "f16", n_dirs=16, k_sel=[8, 20],
+        n_sink=1, n_recent=2), True, True, {}),
+    ("quest-i8 G8", lambda: workloads.clustered(
+        [503], 32, 4, 128, [5000], "i8", n_dirs=32, k_sel=[30], n_sink=1, n_recent=4),
+        True, True, {}),
+    ("quest-f16 G1 block 16", lambda: workloads.clustered(
+        [504], 8, 8, 128, [1500], "f16", n_dirs=8, block=16, k_sel=[20], n_sink=1,
+        n_recent=2), True, True, {}),
+    ("quest-f16 G2 L=1 in batch", lambda: workloads.clustered(
+        [505, 506], 16, 8, 128, [1, 700], "f16", n_dirs=8, k_sel=[3, 3], n_sink=1,
+        n_recent=2), True, True, {}),
+    ("quest-f16 no append", lambda: workloads.clustered(
+        [507], 32, 8, 128, [4096], "f16", n_dirs=16, k_sel=[16], n_sink=1, n_recent=2),
+        True, False, {}),
+    ("quest-f16 long parts (select kernel)", lambda: workloads.clustered(
+        [508], 32, 8, 128, [32768], "f16", n_dirs=64, k_sel=[128], n_sink=1, n_recent=2),
+        True, True, {"S": 2}),
+    ("quest-f16 >4096 blocks (select kernel)", lambda: workloads.clustered(
+        [509], 16, 4, 128, [3000], "f16", n_dirs=8, k_sel=[10], n_sink=1, n_recent=2),
+        True, True, {"max_seq": 64 * 4100}),
+    ("dense-f16 varlen", lambda: workloads.gaussian(
+        510, 3, 16, 4, 128, [100, 64, 2500], "f16"), False, True, {}),
+    ("dense-i8 no append", lambda: workloads.gaussian(
+        511, 1, 32, 8, 128, [1000], "i8"), False, False, {}),
+]
+
+
+@pytest.mark.parametrize("name,make,quest,append,extra", STEP_CASES, ids=[c[0] for c in STEP_CASES])
+def test_decode_step_equals_composed_calls(gpu_lib, name, make, quest, append, extra):
+    _print(name)
+    w = make()
+    out, sel = _run_case(w, quest, append, **extra)
+    _oracle_check(w, out, sel)
+
+
+def test_decode_step_replays_in_a_hip_graph(gpu_lib):
+    """The three launches of a Quest step captured once and replayed several
+    times (with eager work between the replays) give the eager result each
+    time; the step allocates nothing and leaves no memset in the graph."""
+    _print("step graph")
+    w = workloads.clustered([512], 32, 8, 128, [8192], "f16", n_dirs=16, k_sel=[32],
+                            n_sink=1, n_recent=2)
+    base = _prefilled(w)
+    q = torch.from_numpy(np.ascontiguousarray(w.q)).to(DEV)
+    seq_len = torch.tensor(w.lens, dtype=torch.int32, device=DEV)
+    ks = torch.tensor(w.k_sel, dtype=torch.int32, device=DEV)
+    pos, kn, vn = _new_token(w)
+    max_sel = 35
+    S = skv.default_split(1, 8, max_sel)
+    out, ws, sc, sel, cnt = _buffers(w, base, True, max_sel, S)
+
+    def step():
+        skv.decode_step(base, q, seq_len, 8192, w.softmax_scale, S, ws, out, pos0=pos,
+                        k_new=kn, v_new=vn, k_sel=ks, score=sc, sel_idx=sel, sel_cnt=cnt)
+
+    step()
+    torch.cuda.synchronize()
+    ref = out.clone()
+    ref_sel = sel.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for _ in range(4):
+        out.fill_(float("nan"))
+        sel.fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref)
+        assert torch.equal(sel, ref_sel)
