@@ -5,61 +5,103 @@
 // non-empty part gets zeros.
 //
 // The merge is latency-bound (a few KiB per head, read right after the decode
-// kernel wrote it, often from another XCD's L2), so each thread owns one
-// (head, channel) output and issues all of its loads before it uses any of
-// them: kBatch parts' numerators, maxima and masses per memory round trip
-// (one round trip for up to kBatch parts).  No barriers and no LDS.  The sum
-// runs over the parts in index order.
+// kernel wrote it from every XCD), so it is shaped for one memory round trip:
+// one wavefront per head, lane l covering channels 4 (l % 32) .. +3 for the
+// parts of its half (half h = l / 32 takes parts h, h + 2, h + 4, ...), every
+// load of a lane issued before any is used (at most 16 parts per half and
+// batch: 16 float4 numerators plus 8 float4 of maxima and masses, under the
+// wavefront's limit of outstanding loads).  The halves meet through a lane
+// swap across the two 32-lane halves.
 #include "device_common.h"
 #include "launch.h"
 
 namespace skv {
 namespace {
 
-constexpr int kCombThreads = 128;
-constexpr int kBatch = 32;
+constexpr int kHalfBatch = 16;          // parts per half-wave per round trip
 
-__global__ void __launch_bounds__(kCombThreads)
+// Four consecutive floats: one 16-byte load when the launcher has checked the
+// 16-byte alignment of the buffers, else four 4-byte loads.
+template <bool VEC>
+__device__ __forceinline__ float4 load4(const float* p) {
+  if constexpr (VEC) return *reinterpret_cast<const float4*>(p);
+  else return make_float4(p[0], p[1], p[2], p[3]);
+}
+template <bool VEC>
+__device__ __forceinline__ void store4(float* p, float4 v) {
+  if constexpr (VEC) {
+    *reinterpret_cast<float4*>(p) = v;
+  } else {
+    p[0] = v.x; p[1] = v.y; p[2] = v.z; p[3] = v.w;
+  }
+}
+
+template <bool VEC>
+__global__ void __launch_bounds__(kWave)
 combine_kernel(const float* __restrict__ ws_m, const float* __restrict__ ws_l,
                const float* __restrict__ ws_o, int32_t n_split, int32_t D,
                float* __restrict__ out) {
   const int64_t head = blockIdx.x;
-  const int d = blockIdx.y * kCombThreads + threadIdx.x;
-  if (d >= D) return;
+  const int lane = threadIdx.x, half = lane / 32;
+  const int d4 = 4 * (lane % 32) + 128 * blockIdx.y;   // first of this lane's 4 channels
+  const bool ch_ok = d4 < D;
   const float* mp = ws_m + head * n_split;
   const float* lp = ws_l + head * n_split;
-  const float* op = ws_o + head * int64_t(n_split) * D + d;
-  // One batch of parts per memory round trip: all maxima, masses and
-  // numerators of the batch are loaded, then folded into a running max with
-  // the accumulators rescaled when it grows (2^(m - M) is exact at m == M).
-  float M = -INFINITY, num = 0.0f, den = 0.0f;
-  for (int32_t i0 = 0; i0 < n_split; i0 += kBatch) {
-    float mv[kBatch], lv[kBatch], ov[kBatch];
+  const float* op = ws_o + head * int64_t(n_split) * D;
+  float M = -INFINITY, den = 0.0f;
+  float4 num = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  for (int32_t i0 = 0; i0 < n_split; i0 += 2 * kHalfBatch) {
+    float mv[kHalfBatch], lv[kHalfBatch];
+    float4 ov[kHalfBatch];
 #pragma unroll
-    for (int j = 0; j < kBatch; ++j) {
-      const bool in = i0 + j < n_split;
-      mv[j] = in ? mp[i0 + j] : -INFINITY;
-      lv[j] = in ? lp[i0 + j] : 0.0f;
-      ov[j] = in ? op[int64_t(i0 + j) * D] : 0.0f;
+    for (int j = 0; j < kHalfBatch; ++j) {
+      const int32_t i = i0 + 2 * j + half;
+      const bool in = i < n_split;
+      mv[j] = in ? mp[i] : -INFINITY;
+      lv[j] = in ? lp[i] : 0.0f;
+      ov[j] = (in && ch_ok) ? load4<VEC>(op + int64_t(i) * D + d4)
+                            : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     }
+    // running max over both halves (identical in every lane), then rescale
     float bm = M;
 #pragma unroll
-    for (int j = 0; j < kBatch; ++j) bm = fmaxf(bm, mv[j]);
+    for (int j = 0; j < kHalfBatch; ++j) bm = fmaxf(bm, mv[j]);
+    uint32_t hi;
+    const float lo = __uint_as_float(halves_lo(__float_as_uint(bm), hi));
+    bm = fmaxf(lo, __uint_as_float(hi));
     if (bm == -INFINITY) continue;
     if (bm > M) {
       const float c = (M == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(M - bm);
-      num *= c;
+      num.x *= c; num.y *= c; num.z *= c; num.w *= c;
       den *= c;
       M = bm;
     }
 #pragma unroll
-    for (int j = 0; j < kBatch; ++j) {
+    for (int j = 0; j < kHalfBatch; ++j) {
       const float a = (mv[j] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mv[j] - M);
-      num = fmaf(a, ov[j], num);
+      num.x = fmaf(a, ov[j].x, num.x);
+      num.y = fmaf(a, ov[j].y, num.y);
+      num.z = fmaf(a, ov[j].z, num.z);
+      num.w = fmaf(a, ov[j].w, num.w);
       den = fmaf(a, lv[j], den);
     }
   }
-  out[head * D + d] = den > 0.0f ? num / den : 0.0f;
+  // both halves share M: add the lower half's sums to the upper half's
+  uint32_t h;
+  float t;
+  t = __uint_as_float(halves_lo(__float_as_uint(num.x), h)); num.x = t + __uint_as_float(h);
+  t = __uint_as_float(halves_lo(__float_as_uint(num.y), h)); num.y = t + __uint_as_float(h);
+  t = __uint_as_float(halves_lo(__float_as_uint(num.z), h)); num.z = t + __uint_as_float(h);
+  t = __uint_as_float(halves_lo(__float_as_uint(num.w), h)); num.w = t + __uint_as_float(h);
+  t = __uint_as_float(halves_lo(__float_as_uint(den), h)); den = t + __uint_as_float(h);
+  if (half == 0 && ch_ok) {
+    float4 o;
+    o.x = den > 0.0f ? num.x / den : 0.0f;
+    o.y = den > 0.0f ? num.y / den : 0.0f;
+    o.z = den > 0.0f ? num.z / den : 0.0f;
+    o.w = den > 0.0f ? num.w / den : 0.0f;
+    store4<VEC>(out + head * D + d4, o);
+  }
 }
 
 }  // namespace
@@ -69,8 +111,13 @@ hipError_t launch_combine(const float* ws, int32_t batch, int32_t n_heads, int32
   const float* ws_m = ws + ws_m_offset(batch, n_heads, n_split);
   const float* ws_l = ws + ws_l_offset(batch, n_heads, n_split);
   const float* ws_o = ws + ws_o_offset(batch, n_heads, n_split);
-  dim3 grid(batch * n_heads, (head_dim + kCombThreads - 1) / kCombThreads);
-  combine_kernel<<<grid, kCombThreads, 0, stream>>>(ws_m, ws_l, ws_o, n_split, head_dim, out);
+  dim3 grid(batch * n_heads, (head_dim + 127) / 128);
+  const bool vec = (reinterpret_cast<uintptr_t>(ws_o) % 16 == 0) &&
+                   (reinterpret_cast<uintptr_t>(out) % 16 == 0) && head_dim % 4 == 0;
+  if (vec)
+    combine_kernel<true><<<grid, kWave, 0, stream>>>(ws_m, ws_l, ws_o, n_split, head_dim, out);
+  else
+    combine_kernel<false><<<grid, kWave, 0, stream>>>(ws_m, ws_l, ws_o, n_split, head_dim, out);
   return hipGetLastError();
 }
 

@@ -208,11 +208,14 @@ def test_block_sizes_other_than_64(gpu_lib):
 
 
 # ------------------------------------------------------------------ combine
-def test_combine_alone_matches_oracle_merge(gpu_lib):
-    """Partial states made by the oracle, merged by the GPU combine."""
-    _print("combine alone")
-    rng = np.random.default_rng(61)
-    B, H, D, S = 2, 3, 128, 5
+@pytest.mark.parametrize("B,H,S", [(2, 3, 5), (1, 1, 3), (1, 3, 40), (2, 8, 64)])
+def test_combine_alone_matches_oracle_merge(gpu_lib, B, H, S):
+    """Partial states made by the oracle, merged by the GPU combine (parts
+    in more than one batch; a workspace whose numerators are not 16-byte
+    aligned, which takes the 4-byte load path)."""
+    _print("combine alone", B, H, S)
+    rng = np.random.default_rng(61 + S)
+    D = 128
     L = 400
     k = rng.standard_normal((1, L, D)).astype(np.float16)
     v = rng.standard_normal((1, L, D)).astype(np.float16)
