@@ -118,22 +118,28 @@ bounds_kernel(uint16_t* __restrict__ kmin, uint16_t* __restrict__ kmax,
   const int32_t c = threadIdx.x % kLanesPerBlock;  // channels 8c .. 8c+7
   if (int32_t(blockIdx.x) * kBlocksPerWG >= nb) return;   // whole tile past the end
 
-  // Query slice of the G heads of this group.
-  float qv[G][8];
+  // The group's G query rows (G * 512 B) are read once per workgroup into
+  // LDS, one 16-byte load per thread, together with this thread's bounds.
+  __shared__ __attribute__((aligned(16))) float qs[G * D];
   const int32_t H = Hkv * G;
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const float4* qp = reinterpret_cast<const float4*>(q + (int64_t(b) * H + g * G + h) * D + c * 8);
-    const float4 a = qp[0], bq = qp[1];
-    qv[h][0] = a.x; qv[h][1] = a.y; qv[h][2] = a.z; qv[h][3] = a.w;
-    qv[h][4] = bq.x; qv[h][5] = bq.y; qv[h][6] = bq.z; qv[h][7] = bq.w;
-  }
+  const float* qg = q + (int64_t(b) * H + g * G) * D;
+  for (int i = threadIdx.x; i < G * D / 4; i += kBoundsThreads)
+    reinterpret_cast<float4*>(qs)[i] = reinterpret_cast<const float4*>(qg)[i];
   const bool live = j < nb;
   uint4 lo = make_uint4(0, 0, 0, 0), hi = make_uint4(0, 0, 0, 0);
   if (live) {
     const int64_t off = ((int64_t(b) * Hkv + g) * max_blocks + j) * D + c * 8;
     lo = *reinterpret_cast<const uint4*>(kmin + off);
     hi = *reinterpret_cast<const uint4*>(kmax + off);
+  }
+  __syncthreads();
+  float qv[G][8];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const float4 a = reinterpret_cast<const float4*>(qs + h * D + c * 8)[0];
+    const float4 bq = reinterpret_cast<const float4*>(qs + h * D + c * 8)[1];
+    qv[h][0] = a.x; qv[h][1] = a.y; qv[h][2] = a.z; qv[h][3] = a.w;
+    qv[h][4] = bq.x; qv[h][5] = bq.y; qv[h][6] = bq.z; qv[h][7] = bq.w;
   }
   uint16_t lb[8], hb[8];
   {

@@ -132,6 +132,11 @@ __device__ __forceinline__ TileWalk fused_walk(const FusedSelect& fs, int32_t ma
   __shared__ SelectShared ssh;
   __shared__ int32_t plist[kWave];
   const int tid = threadIdx.x;
+  // The candidates start at n_sink whenever there are any, so their scores
+  // are requested before the row's length arrives (up to the row's capacity).
+  const int32_t k_req = fs.k_sel[b];
+  SelKeys<SELR> kk;
+  kk.load(fs.score + bg * fs.max_blocks + fs.n_sink, fs.max_blocks - fs.n_sink);
   TileWalk tw;
   tw.block = block;
   tw.L = L;
@@ -146,7 +151,7 @@ __device__ __forceinline__ TileWalk fused_walk(const FusedSelect& fs, int32_t ma
   const int32_t cs = min(fs.n_sink, nb);                    // candidates [cs, ce)
   const int32_t ce = max(nb - fs.n_recent, cs);
   const int32_t n_cand = ce - cs;
-  const int32_t K = min(max(fs.k_sel[b], 0), n_cand);
+  const int32_t K = min(max(k_req, 0), n_cand);
   const int32_t n_sel = cs + K + (nb - ce);
   const int32_t u0 = tw.u0, ups = units_per_split;
   const bool publish = split == 0;
@@ -165,9 +170,8 @@ __device__ __forceinline__ TileWalk fused_walk(const FusedSelect& fs, int32_t ma
     }
     if (tid == 0) fs.sel_cnt[bg] = n_sel;
   }
-  if (K > 0 && K < n_cand) {
-    SelKeys<SELR> kk;
-    kk.load(fs.score + bg * fs.max_blocks + cs, n_cand);
+  if (K > 0 && K < n_cand) {          // then cs == n_sink
+    kk.set_count(n_cand);
     const uint64_t cut = sel_cut(kk, K, ssh);
     const uint64_t taken = sel_taken_mask(kk, cut);
     const int R = (n_cand + kSelThreads - 1) / kSelThreads;

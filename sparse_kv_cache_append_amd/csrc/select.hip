@@ -30,12 +30,17 @@ select_kernel(const float* __restrict__ score, const int32_t* __restrict__ seq_l
   const int32_t g = blockIdx.x, b = blockIdx.y;
   const int tid = threadIdx.x;
   const int64_t row = int64_t(b) * Hkv + g;
+  // The candidates start at n_sink whenever there are any, so their scores
+  // are requested together with the row's length and budget.
+  const int32_t k_req = k_sel[b];
+  SelKeys<RMAX> kk;
+  kk.load(score + row * max_blocks + n_sink, max_blocks - n_sink);
   const int32_t L = min(max(seq_len[b], 0), max_blocks * block);
   const int32_t nb = (L + block - 1) / block;
   const int32_t cs = min(n_sink, nb);                       // candidates [cs, ce)
   const int32_t ce = max(nb - n_recent, cs);
   const int32_t n_cand = ce - cs;
-  const int32_t K = min(max(k_sel[b], 0), n_cand);
+  const int32_t K = min(max(k_req, 0), n_cand);
   const int32_t n_sel = cs + K + (nb - ce);
   const int32_t n_words = (max_blocks + 31) / 32;
   const bool want_mask = sel_mask != nullptr;
@@ -55,9 +60,8 @@ select_kernel(const float* __restrict__ score, const int32_t* __restrict__ seq_l
 
   if (K == n_cand) {
     for (int32_t j = cs + tid; j < ce; j += kSelThreads) emit(j, j);
-  } else if (K > 0) {
-    SelKeys<RMAX> kk;
-    kk.load(score + row * max_blocks + cs, n_cand);
+  } else if (K > 0) {                 // then cs == n_sink
+    kk.set_count(n_cand);
     const uint64_t cut = sel_cut(kk, K, sh);
     const uint64_t taken = sel_taken_mask(kk, cut);
     const int R = (n_cand + kSelThreads - 1) / kSelThreads;

@@ -17,7 +17,8 @@
 //   * most-significant-digit radix passes (LDS histogram of 256 bins filled
 //     straight from registers, DPP prefix sum over the bins) fixing 8 more
 //     bits of the K-th key each, until at most 64 candidates share its prefix;
-//   * ranking those pairwise (LDS broadcast reads of their order values);
+//   * gathering those into one wavefront and narrowing them with ballots,
+//     one bit of the order value at a time, to the one of the right rank;
 //   * or, if more than 64 keys equal the K-th key exactly, taking its
 //     occurrence of the right rank in index order.
 // Index order of flagged candidates (ascending output positions) comes from
@@ -79,18 +80,24 @@ struct SelKeys {
   __device__ __forceinline__ bool valid(int r) const {
     return int32_t(threadIdx.x) + kSelThreads * r < n;
   }
+  // uniform: chunk r holds at least one candidate (loops skip empty chunks
+  // with a scalar branch instead of running them masked)
+  __device__ __forceinline__ bool used(int r) const { return kSelThreads * r < n; }
   __device__ __forceinline__ int32_t index(int r) const {
     return int32_t(threadIdx.x) + kSelThreads * r;
   }
-  // Every load is issued before any key is formed (one round trip).
-  __device__ __forceinline__ void load(const float* __restrict__ score_row, int32_t n_cand) {
-    n = n_cand;
+  // Every load is issued before any key is formed (one round trip).  n_load
+  // may exceed the final candidate count: set_count() then narrows n (the
+  // loads can start before the row's length is known).
+  __device__ __forceinline__ void load(const float* __restrict__ score_row, int32_t n_load) {
+    n = n_load;
     float v[RMAX];
 #pragma unroll
     for (int r = 0; r < RMAX; ++r) v[r] = valid(r) ? score_row[index(r)] : 0.0f;
 #pragma unroll
-    for (int r = 0; r < RMAX; ++r) k[r] = float_key(v[r]);
+    for (int r = 0; r < RMAX; ++r) k[r] = used(r) ? float_key(v[r]) : 0u;
   }
+  __device__ __forceinline__ void set_count(int32_t n_cand) { n = n_cand; }
 };
 
 // Index order of flagged candidates.  Bit r of `flags` flags candidate
@@ -126,6 +133,7 @@ __device__ __forceinline__ uint64_t sel_cut(const SelKeys<RMAX>& kk, int32_t K, 
   uint32_t a = ~0u, o = 0u;
 #pragma unroll
   for (int r = 0; r < RMAX; ++r) {
+    if (!kk.used(r)) break;
     const bool ok = kk.valid(r);
     a &= ok ? kk.k[r] : ~0u;
     o |= ok ? kk.k[r] : 0u;
@@ -152,6 +160,7 @@ __device__ __forceinline__ uint64_t sel_cut(const SelKeys<RMAX>& kk, int32_t K, 
     __syncthreads();
 #pragma unroll
     for (int r = 0; r < RMAX; ++r) {
+      if (!kk.used(r)) break;
       const uint32_t k = kk.k[r];
       if (kk.valid(r) && (k & pmask) == prefix) atomicAdd(&s.hist[(k >> shift) & dmask], 1u);
     }
@@ -185,21 +194,31 @@ __device__ __forceinline__ uint64_t sel_cut(const SelKeys<RMAX>& kk, int32_t K, 
     __syncthreads();
 #pragma unroll
     for (int r = 0; r < RMAX; ++r) {
+      if (!kk.used(r)) break;
       const uint32_t k = kk.k[r];
       if (kk.valid(r) && (k & pmask) == prefix)
         s.slot[atomicAdd(&s.n_active, 1)] = order_value(k, kk.index(r));
     }
     __syncthreads();
     if (wave == 0) {
+      // the remaining-th largest of the m <= 64 order values, one lane each:
+      // a ballot radix from the highest bit that is not shared, keeping the
+      // lanes that can still hold it (values are distinct, so one remains)
       const int m = active;
       const uint64_t v = lane < m ? s.slot[lane] : 0u;
-      int rank = 0;
-#pragma unroll 8
-      for (int j = 0; j < m; j += 2) {
-        const ulonglong2 p = *reinterpret_cast<const ulonglong2*>(&s.slot[j]);
-        rank += (p.x > v ? 1 : 0) + ((j + 1 < m && p.y > v) ? 1 : 0);
+      uint64_t cand = __ballot(lane < m);
+      int r = remaining;
+      for (int bit = 63 - __popc(pmask); bit >= 0 && __popcll(cand) > 1; --bit) {
+        const uint64_t ones = __ballot(int((v >> bit) & 1u)) & cand;
+        const int n1 = __popcll(ones);
+        if (n1 >= r) {
+          cand = ones;
+        } else {
+          r -= n1;
+          cand &= ~ones;
+        }
       }
-      if (lane < m && rank == remaining - 1) s.cut = v;
+      if (lane == __builtin_ctzll(cand)) s.cut = v;
     }
     __syncthreads();
     return s.cut;
@@ -208,8 +227,10 @@ __device__ __forceinline__ uint64_t sel_cut(const SelKeys<RMAX>& kk, int32_t K, 
   // number `remaining` in index order is the cut
   uint64_t eq = 0u;
 #pragma unroll
-  for (int r = 0; r < RMAX; ++r)
+  for (int r = 0; r < RMAX; ++r) {
+    if (!kk.used(r)) break;
     if (kk.valid(r) && kk.k[r] == prefix) eq |= uint64_t(1) << r;
+  }
   const int R = (n + kSelThreads - 1) / kSelThreads;
   sel_order_prepare(eq, R, s);
 #pragma unroll
@@ -228,8 +249,10 @@ template <int RMAX>
 __device__ __forceinline__ uint64_t sel_taken_mask(const SelKeys<RMAX>& kk, uint64_t cut) {
   uint64_t m = 0u;
 #pragma unroll
-  for (int r = 0; r < RMAX; ++r)
+  for (int r = 0; r < RMAX; ++r) {
+    if (!kk.used(r)) break;
     if (kk.valid(r) && order_value(kk.k[r], kk.index(r)) >= cut) m |= uint64_t(1) << r;
+  }
   return m;
 }
 
