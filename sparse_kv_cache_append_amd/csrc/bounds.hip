@@ -129,8 +129,9 @@ bounds_kernel(uint16_t* __restrict__ kmin, uint16_t* __restrict__ kmax,
   uint4 lo = make_uint4(0, 0, 0, 0), hi = make_uint4(0, 0, 0, 0);
   if (live) {
     const int64_t off = ((int64_t(b) * Hkv + g) * max_blocks + j) * D + c * 8;
-    lo = *reinterpret_cast<const uint4*>(kmin + off);
-    hi = *reinterpret_cast<const uint4*>(kmax + off);
+    // read once per step: streaming (nontemporal) loads
+    lo = __builtin_nontemporal_load(reinterpret_cast<const uint4*>(kmin + off));
+    hi = __builtin_nontemporal_load(reinterpret_cast<const uint4*>(kmax + off));
   }
   __syncthreads();
   float qv[G][8];

