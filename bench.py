@@ -298,7 +298,7 @@ def measure(w, args, quest: bool, dense: bool, detail: bool = False):
     res = {"workload": w.name, "cache_copies": R}
 
     if dense:
-        S_d = args.n_split or skv.default_split(B, Hkv, nb_max)
+        S_d = args.n_split or skv.default_split(B, Hkv, nb_max, kv_dtype=w.kv_dtype)
         ws_d = torch.empty(skv.workspace_bytes(B, H, D, S_d), dtype=torch.uint8, device=dev)
         out_d = torch.empty((B, H, D), dtype=torch.float32, device=dev)
 
@@ -327,7 +327,7 @@ def measure(w, args, quest: bool, dense: bool, detail: bool = False):
         score = torch.empty((B, Hkv, base.max_blocks), dtype=torch.float32, device=dev)
         sel = torch.empty((B, Hkv, max_sel), dtype=torch.int32, device=dev)
         cnt = torch.empty((B, Hkv), dtype=torch.int32, device=dev)
-        S_q = args.n_split or skv.default_split(B, Hkv, max_sel)
+        S_q = args.n_split or skv.default_split(B, Hkv, max_sel, kv_dtype=w.kv_dtype, sparse=True)
         ws_q = torch.empty(skv.workspace_bytes(B, H, D, S_q), dtype=torch.uint8, device=dev)
         out_q = torch.empty((B, H, D), dtype=torch.float32, device=dev)
 
@@ -395,8 +395,9 @@ def main():
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--mode", choices=("both", "quest", "dense"), default="both",
                     help="which step of the 32K workload to time (profiling runs use one)")
-    ap.add_argument("--workloads", default="1,2,4,5",
-                    help="other workloads to time besides the 32K headline ('' = none)")
+    ap.add_argument("--workloads", default="1,2,4,5,3@16384",
+                    help="other workloads to time besides the 32K headline ('' = none; "
+                         "3@L = the 32K Quest generator at context L)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after timing, copy a buffer of this many MiB three times "
                          "(a plain copy of known size that scales HBM byte counters)")
@@ -417,6 +418,12 @@ def main():
     head = measure(w3, args, quest=do_q, dense=do_d, detail=True)
     others = []
     for tok in [t for t in args.workloads.split(",") if t.strip()]:
+        if tok.strip().startswith("3@"):
+            # the 32K generator at another length (Quest vs dense from 16K up)
+            w = workloads.quest32k_at(int(tok.strip()[2:]))
+            others.append(measure(w, args, quest=True, dense=True))
+            del w
+            continue
         cfg = int(tok)
         if cfg == 3:
             continue

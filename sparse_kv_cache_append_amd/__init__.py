@@ -228,9 +228,16 @@ def combine(workspace, batch: int, n_heads: int, head_dim: int, n_split: int, ou
         _stream(stream)))
 
 
-def default_split(batch: int, n_kv_heads: int, n_units: int, target_wgs: int = 256) -> int:
+def default_split(batch: int, n_kv_heads: int, n_units: int, target_wgs: Optional[int] = None,
+                  kv_dtype: str = "f16", sparse: bool = False) -> int:
     """Parts per (sequence, KV head) so the grid has about ``target_wgs``
-    workgroups, at least one block (or selected entry) per part."""
+    workgroups, at least one block (or selected entry) per part.  Default:
+    one workgroup per compute unit, or two for dense decode over an int8
+    cache, whose tiles cost more arithmetic per byte and gain from a second
+    workgroup hiding the first one's loads (sparse decode keeps one: every
+    part of a row also runs the block selection)."""
+    if target_wgs is None:
+        target_wgs = 512 if (kv_dtype == "i8" and not sparse) else 256
     n = max(1, math.ceil(target_wgs / max(1, batch * n_kv_heads)))
     return int(max(1, min(n, n_units, 4096)))
 
@@ -257,7 +264,8 @@ def decode(cache: Cache, q, seq_len, max_len: int, softmax_scale: Optional[float
         select_topk(score, seq_len, cache.block, k_sel, n_sink, n_recent, sel_idx, sel_cnt,
                     stream=stream)
     units = max_sel if k_sel is not None else max(nb_max, 1)
-    S = n_split or default_split(B, cache.n_kv_heads, units)
+    S = n_split or default_split(B, cache.n_kv_heads, units, kv_dtype=cache.kv_dtype,
+                                 sparse=k_sel is not None)
     ws = torch.empty(workspace_bytes(B, H, D, S), dtype=torch.uint8, device=dev)
     out = torch.empty((B, H, D), dtype=torch.float32, device=dev)
     decode_attn(cache, q, seq_len, max_len, scale, S, ws, sel_idx, sel_cnt, stream=stream)

@@ -5,20 +5,20 @@
 // non-empty part gets zeros.
 //
 // The merge is latency-bound (a few KiB per head, read right after the decode
-// kernel wrote it from every XCD), so it is shaped for one memory round trip:
-// one wavefront per head, lane l covering channels 4 (l % 32) .. +3 for the
-// parts of its half (half h = l / 32 takes parts h, h + 2, h + 4, ...), every
-// load of a lane issued before any is used (at most 16 parts per half and
-// batch: 16 float4 numerators plus 8 float4 of maxima and masses, under the
-// wavefront's limit of outstanding loads).  The halves meet through a lane
-// swap across the two 32-lane halves.
+// kernel wrote it from every XCD), so it is shaped for few memory round trips:
+// one wavefront per head, lane l covering channels 4 (l % 32) .. +3, the two
+// 32-lane halves taking the two halves of each batch of 64 parts.  Every load
+// of a batch is issued before any is used: 32 float4 numerators plus the
+// batch's maxima and masses (as float4 where aligned), under the wavefront's
+// limit of outstanding loads.  The halves meet through a lane swap across
+// the two 32-lane halves.
 #include "device_common.h"
 #include "launch.h"
 
 namespace skv {
 namespace {
 
-constexpr int kHalfBatch = 16;          // parts per half-wave per round trip
+constexpr int kHalfBatch = 32;          // parts per half-wave per round trip
 
 // Four consecutive floats: one 16-byte load when the launcher has checked the
 // 16-byte alignment of the buffers, else four 4-byte loads.
@@ -36,7 +36,9 @@ __device__ __forceinline__ void store4(float* p, float4 v) {
   }
 }
 
-template <bool VEC>
+// VEC: numerators and outputs 16-byte aligned; VML: so are the maxima and
+// masses of every head (n_split % 4 == 0 and aligned bases).
+template <bool VEC, bool VML>
 __global__ void __launch_bounds__(kWave)
 combine_kernel(const float* __restrict__ ws_m, const float* __restrict__ ws_l,
                const float* __restrict__ ws_o, int32_t n_split, int32_t D,
@@ -51,16 +53,30 @@ combine_kernel(const float* __restrict__ ws_m, const float* __restrict__ ws_l,
   float M = -INFINITY, den = 0.0f;
   float4 num = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
   for (int32_t i0 = 0; i0 < n_split; i0 += 2 * kHalfBatch) {
+    const int32_t p0 = i0 + kHalfBatch * half;          // this half's first part
     float mv[kHalfBatch], lv[kHalfBatch];
     float4 ov[kHalfBatch];
 #pragma unroll
+    for (int j = 0; j < kHalfBatch; j += 4) {
+      if (VML && p0 + j + 3 < n_split) {
+        const float4 m4 = *reinterpret_cast<const float4*>(mp + p0 + j);
+        const float4 l4 = *reinterpret_cast<const float4*>(lp + p0 + j);
+        mv[j] = m4.x; mv[j + 1] = m4.y; mv[j + 2] = m4.z; mv[j + 3] = m4.w;
+        lv[j] = l4.x; lv[j + 1] = l4.y; lv[j + 2] = l4.z; lv[j + 3] = l4.w;
+      } else {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const bool in = p0 + j + t < n_split;
+          mv[j + t] = in ? mp[p0 + j + t] : -INFINITY;
+          lv[j + t] = in ? lp[p0 + j + t] : 0.0f;
+        }
+      }
+    }
+#pragma unroll
     for (int j = 0; j < kHalfBatch; ++j) {
-      const int32_t i = i0 + 2 * j + half;
-      const bool in = i < n_split;
-      mv[j] = in ? mp[i] : -INFINITY;
-      lv[j] = in ? lp[i] : 0.0f;
-      ov[j] = (in && ch_ok) ? load4<VEC>(op + int64_t(i) * D + d4)
-                            : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      const int32_t i = p0 + j;
+      ov[j] = (i < n_split && ch_ok) ? load4<VEC>(op + int64_t(i) * D + d4)
+                                     : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     }
     // running max over both halves (identical in every lane), then rescale
     float bm = M;
@@ -112,12 +128,16 @@ hipError_t launch_combine(const float* ws, int32_t batch, int32_t n_heads, int32
   const float* ws_l = ws + ws_l_offset(batch, n_heads, n_split);
   const float* ws_o = ws + ws_o_offset(batch, n_heads, n_split);
   dim3 grid(batch * n_heads, (head_dim + 127) / 128);
-  const bool vec = (reinterpret_cast<uintptr_t>(ws_o) % 16 == 0) &&
-                   (reinterpret_cast<uintptr_t>(out) % 16 == 0) && head_dim % 4 == 0;
-  if (vec)
-    combine_kernel<true><<<grid, kWave, 0, stream>>>(ws_m, ws_l, ws_o, n_split, head_dim, out);
-  else
-    combine_kernel<false><<<grid, kWave, 0, stream>>>(ws_m, ws_l, ws_o, n_split, head_dim, out);
+  auto aligned = [](const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; };
+  const bool vec = aligned(ws_o) && aligned(out) && head_dim % 4 == 0;
+  const bool vml = aligned(ws_m) && aligned(ws_l) && n_split % 4 == 0;
+#define SKV_COMBINE(V, M)                                                                     \
+  combine_kernel<V, M><<<grid, kWave, 0, stream>>>(ws_m, ws_l, ws_o, n_split, head_dim, out)
+  if (vec && vml) SKV_COMBINE(true, true);
+  else if (vec) SKV_COMBINE(true, false);
+  else if (vml) SKV_COMBINE(false, true);
+  else SKV_COMBINE(false, false);
+#undef SKV_COMBINE
   return hipGetLastError();
 }
 

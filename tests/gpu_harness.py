@@ -72,7 +72,7 @@ def run_dense(cache, w, n_split=None, dbg=False):
     q, seq_len = device_inputs(w)
     max_len = max(max(w.lens), 0)
     nb = -(-max_len // w.block)
-    S = n_split or skv.default_split(w.B, w.Hkv, max(nb, 1))
+    S = n_split or skv.default_split(w.B, w.Hkv, max(nb, 1), kv_dtype=w.kv_dtype)
     ws = torch.empty(skv.workspace_bytes(w.B, w.H, w.D, S), dtype=torch.uint8, device=DEV)
     out = torch.empty((w.B, w.H, w.D), dtype=torch.float32, device=DEV)
     dl = None
@@ -107,7 +107,7 @@ def run_sparse(cache, w, sel, cnt, n_split=None):
     q, seq_len = device_inputs(w)
     max_len = max(w.lens)
     max_sel = int(sel.shape[2])
-    S = n_split or skv.default_split(w.B, w.Hkv, max_sel)
+    S = n_split or skv.default_split(w.B, w.Hkv, max_sel, kv_dtype=w.kv_dtype, sparse=True)
     ws = torch.empty(skv.workspace_bytes(w.B, w.H, w.D, S), dtype=torch.uint8, device=DEV)
     out = torch.empty((w.B, w.H, w.D), dtype=torch.float32, device=DEV)
     skv.decode_attn(cache, q, seq_len, max_len, w.softmax_scale, S, ws, sel, cnt)

@@ -208,7 +208,7 @@ def test_block_sizes_other_than_64(gpu_lib):
 
 
 # ------------------------------------------------------------------ combine
-@pytest.mark.parametrize("B,H,S", [(2, 3, 5), (1, 1, 3), (1, 3, 40), (2, 8, 64)])
+@pytest.mark.parametrize("B,H,S", [(2, 3, 5), (1, 1, 3), (1, 3, 40), (2, 8, 64), (1, 2, 130), (1, 4, 128)])
 def test_combine_alone_matches_oracle_merge(gpu_lib, B, H, S):
     """Partial states made by the oracle, merged by the GPU combine (parts
     in more than one batch; a workspace whose numerators are not 16-byte

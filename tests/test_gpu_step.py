@@ -86,9 +86,9 @@ def _run_case(w, quest, append, S=None, max_seq=None, max_sel=None):
     ks = torch.tensor(w.k_sel, dtype=torch.int32, device=DEV) if quest else None
     if quest:
         max_sel = max_sel or (max(w.k_sel) + w.n_sink + w.n_recent)
-        S = S or skv.default_split(w.B, w.Hkv, max_sel)
+        S = S or skv.default_split(w.B, w.Hkv, max_sel, kv_dtype=w.kv_dtype, sparse=True)
     else:
-        S = S or skv.default_split(w.B, w.Hkv, -(-max_len // w.block))
+        S = S or skv.default_split(w.B, w.Hkv, -(-max_len // w.block), kv_dtype=w.kv_dtype)
     pos, kn, vn = _new_token(w)
     out_a, ws_a, sc_a, sel_a, cnt_a = _buffers(w, ca, quest, max_sel, S)
     out_b, ws_b, sc_b, sel_b, cnt_b = _buffers(w, cb, quest, max_sel, S)

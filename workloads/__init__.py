@@ -44,7 +44,7 @@ from typing import List, Optional
 
 import numpy as np
 
-__all__ = ["Workload", "gaussian", "clustered", "named", "lengths_config4",
+__all__ = ["Workload", "gaussian", "clustered", "named", "quest32k_at", "lengths_config4",
            "NAMED"]
 
 
@@ -179,3 +179,13 @@ def named(cfg: int) -> Workload:
         return clustered([1005], 32, 4, 128, [262144], "i8", n_dirs=256,
                          name=NAMED[5], k_sel=[512], n_sink=1, n_recent=4)
     raise ValueError(f"unknown workload {cfg}")
+
+
+def quest32k_at(L: int) -> Workload:
+    """The 32K Quest workload's generator (H=32, Hkv=8, 64 directions, block
+    64, sink 1, recent 2, seed 1003) at another context length, with the same
+    25% coverage: K_SEL = floor(NB / 4)."""
+    nb = -(-L // 64)
+    return clustered([1003], 32, 8, 128, [L], "f16", n_dirs=64,
+                     name=f"quest-f16 B1 H32/Hkv8 D128 L{L} K_SEL{nb // 4} sink1 recent2",
+                     k_sel=[nb // 4], n_sink=1, n_recent=2)
