@@ -130,8 +130,11 @@ bounds_kernel(uint16_t* __restrict__ kmin, uint16_t* __restrict__ kmax,
   if (live) {
     const int64_t off = ((int64_t(b) * Hkv + g) * max_blocks + j) * D + c * 8;
     // read once per step: streaming (nontemporal) loads
-    lo = __builtin_nontemporal_load(reinterpret_cast<const uint4*>(kmin + off));
-    hi = __builtin_nontemporal_load(reinterpret_cast<const uint4*>(kmax + off));
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 l4 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kmin + off));
+    const u32x4 h4 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kmax + off));
+    lo = make_uint4(l4.x, l4.y, l4.z, l4.w);
+    hi = make_uint4(h4.x, h4.y, h4.z, h4.w);
   }
   __syncthreads();
   float qv[G][8];

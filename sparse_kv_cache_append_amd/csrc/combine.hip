@@ -7,18 +7,17 @@
 // The merge is latency-bound (a few KiB per head, read right after the decode
 // kernel wrote it from every XCD), so it is shaped for few memory round trips:
 // one wavefront per head, lane l covering channels 4 (l % 32) .. +3, the two
-// 32-lane halves taking the two halves of each batch of 64 parts.  Every load
-// of a batch is issued before any is used: 32 float4 numerators plus the
-// batch's maxima and masses (as float4 where aligned), under the wavefront's
-// limit of outstanding loads.  The halves meet through a lane swap across
-// the two 32-lane halves.
+// 32-lane halves taking the two halves of each batch of 2 HB parts (HB = 16
+// or 32).  Every load of a batch is issued before any is used: HB float4
+// numerators plus the batch's maxima and masses (as float4 where aligned),
+// under the wavefront's limit of outstanding loads.  The halves meet through
+// a lane swap across the two 32-lane halves.
 #include "device_common.h"
 #include "launch.h"
 
 namespace skv {
 namespace {
 
-constexpr int kHalfBatch = 32;          // parts per half-wave per round trip
 
 // Four consecutive floats: one 16-byte load when the launcher has checked the
 // 16-byte alignment of the buffers, else four 4-byte loads.
@@ -37,8 +36,9 @@ __device__ __forceinline__ void store4(float* p, float4 v) {
 }
 
 // VEC: numerators and outputs 16-byte aligned; VML: so are the maxima and
-// masses of every head (n_split % 4 == 0 and aligned bases).
-template <bool VEC, bool VML>
+// masses of every head (n_split % 4 == 0 and aligned bases).  HB: parts per
+// half-wavefront and round trip (16 up to 32 parts, else 32).
+template <bool VEC, bool VML, int HB>
 __global__ void __launch_bounds__(kWave)
 combine_kernel(const float* __restrict__ ws_m, const float* __restrict__ ws_l,
                const float* __restrict__ ws_o, int32_t n_split, int32_t D,
@@ -52,12 +52,12 @@ combine_kernel(const float* __restrict__ ws_m, const float* __restrict__ ws_l,
   const float* op = ws_o + head * int64_t(n_split) * D;
   float M = -INFINITY, den = 0.0f;
   float4 num = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-  for (int32_t i0 = 0; i0 < n_split; i0 += 2 * kHalfBatch) {
-    const int32_t p0 = i0 + kHalfBatch * half;          // this half's first part
-    float mv[kHalfBatch], lv[kHalfBatch];
-    float4 ov[kHalfBatch];
+  for (int32_t i0 = 0; i0 < n_split; i0 += 2 * HB) {
+    const int32_t p0 = i0 + HB * half;          // this half's first part
+    float mv[HB], lv[HB];
+    float4 ov[HB];
 #pragma unroll
-    for (int j = 0; j < kHalfBatch; j += 4) {
+    for (int j = 0; j < HB; j += 4) {
       if (VML && p0 + j + 3 < n_split) {
         const float4 m4 = *reinterpret_cast<const float4*>(mp + p0 + j);
         const float4 l4 = *reinterpret_cast<const float4*>(lp + p0 + j);
@@ -73,7 +73,7 @@ combine_kernel(const float* __restrict__ ws_m, const float* __restrict__ ws_l,
       }
     }
 #pragma unroll
-    for (int j = 0; j < kHalfBatch; ++j) {
+    for (int j = 0; j < HB; ++j) {
       const int32_t i = p0 + j;
       ov[j] = (i < n_split && ch_ok) ? load4<VEC>(op + int64_t(i) * D + d4)
                                      : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
@@ -81,7 +81,7 @@ combine_kernel(const float* __restrict__ ws_m, const float* __restrict__ ws_l,
     // running max over both halves (identical in every lane), then rescale
     float bm = M;
 #pragma unroll
-    for (int j = 0; j < kHalfBatch; ++j) bm = fmaxf(bm, mv[j]);
+    for (int j = 0; j < HB; ++j) bm = fmaxf(bm, mv[j]);
     uint32_t hi;
     const float lo = __uint_as_float(halves_lo(__float_as_uint(bm), hi));
     bm = fmaxf(lo, __uint_as_float(hi));
@@ -93,7 +93,7 @@ combine_kernel(const float* __restrict__ ws_m, const float* __restrict__ ws_l,
       M = bm;
     }
 #pragma unroll
-    for (int j = 0; j < kHalfBatch; ++j) {
+    for (int j = 0; j < HB; ++j) {
       const float a = (mv[j] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mv[j] - M);
       num.x = fmaf(a, ov[j].x, num.x);
       num.y = fmaf(a, ov[j].y, num.y);
@@ -131,12 +131,14 @@ hipError_t launch_combine(const float* ws, int32_t batch, int32_t n_heads, int32
   auto aligned = [](const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; };
   const bool vec = aligned(ws_o) && aligned(out) && head_dim % 4 == 0;
   const bool vml = aligned(ws_m) && aligned(ws_l) && n_split % 4 == 0;
-#define SKV_COMBINE(V, M)                                                                     \
-  combine_kernel<V, M><<<grid, kWave, 0, stream>>>(ws_m, ws_l, ws_o, n_split, head_dim, out)
-  if (vec && vml) SKV_COMBINE(true, true);
-  else if (vec) SKV_COMBINE(true, false);
-  else if (vml) SKV_COMBINE(false, true);
-  else SKV_COMBINE(false, false);
+#define SKV_COMBINE(V, M, HB)                                                                 \
+  combine_kernel<V, M, HB><<<grid, kWave, 0, stream>>>(ws_m, ws_l, ws_o, n_split, head_dim, out)
+#define SKV_COMBINE_HB(V, M) if (n_split <= 32) SKV_COMBINE(V, M, 16); else SKV_COMBINE(V, M, 32)
+  if (vec && vml) SKV_COMBINE_HB(true, true);
+  else if (vec) SKV_COMBINE_HB(true, false);
+  else if (vml) SKV_COMBINE_HB(false, true);
+  else SKV_COMBINE_HB(false, false);
+#undef SKV_COMBINE_HB
 #undef SKV_COMBINE
   return hipGetLastError();
 }

@@ -139,6 +139,7 @@ __device__ __forceinline__ TileWalk fused_walk(const FusedSelect& fs, int32_t ma
   const int32_t k_req = fs.k_sel[b];
   SelKeys<SELR> kk;
   kk.load(fs.score + bg * fs.max_blocks + fs.n_sink, fs.max_blocks - fs.n_sink);
+  sel_init(ssh);
   TileWalk tw;
   tw.block = block;
   tw.L = L;
@@ -436,9 +437,10 @@ decode_f16_mfma(const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc
 // (1152 + c is exact in f16, minus 1152).
 //
 // The V scales are folded into the weights: P' = p * v_scale * 2^-e with
-// 2^e the tile's largest V scale rounded to a power of two, so P' <= 1 keeps
-// full f16 (high + low) precision whatever the scale; the tile's product is
-// then added to the accumulator times 2^e (exact).
+// 2^e the largest V scale seen so far rounded up to a power of two, so
+// P' <= 1 keeps full f16 (high + low) precision whatever the scale's
+// magnitude; the accumulator holds O * 2^-e, is rescaled (exactly, by a power
+// of two) in the rare tile where e grows, and is scaled back at the end.
 __device__ __forceinline__ half8_t widen_codes(int2_t w) {
   typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
   half8_t r;
@@ -552,6 +554,8 @@ decode_i8_mfma(const int8_t* __restrict__ kc, const int8_t* __restrict__ vc,
     f.sc = lane < 32 ? ksb[srow] : vsb[srow];
   };
   auto sw = [](int row, int chunk) { return row * kRowBytesI8 + 16 * (chunk ^ (row & 7)); };
+  constexpr int kExpUnset = -100000;       // no nonzero V scale seen yet
+  int e_run = kExpUnset;
 
   auto process = [&](auto bufc, Frag& fr, bool& have) {
     constexpr int kBuf = decltype(bufc)::value;
@@ -595,15 +599,31 @@ decode_i8_mfma(const int8_t* __restrict__ kc, const int8_t* __restrict__ vc,
       sc[e] = ok ? float(dot) * coef * ks[e] : -INFINITY;
     }
     tile_softmax<G, 2>(sc, m_run, l_run, O);
-    // fold the V scales into the weights, normalized by the tile's largest
+    // fold the V scales into the weights: P' = p * v_scale * 2^-e_run, with
+    // 2^e_run the largest V scale seen so far rounded up to a power of two
+    // (O is kept in units of 2^e_run and rescaled when e_run grows)
     float vmax = 0.0f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) vmax = fmaxf(vmax, vs[e]);
     vmax = rows_max(vmax);
-    const int ex = __builtin_amdgcn_frexp_expf(vmax);
+    if (vmax > 0.0f) {
+      const int ex = __builtin_amdgcn_frexp_expf(vmax);
+      if (e_run == kExpUnset) {
+        e_run = ex;
+      } else if (ex > e_run) {
+        const float c = ldexpf(1.0f, e_run - ex);
+#pragma unroll
+        for (int n = 0; n < 8; ++n) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) O[n][r] *= c;
+        }
+        e_run = ex;
+      }
+    }
+    const int e_use = e_run == kExpUnset ? 0 : e_run;
     float pw[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) pw[e] = sc[e] * ldexpf(vs[e], -ex);
+    for (int e = 0; e < 8; ++e) pw[e] = sc[e] * ldexpf(vs[e], -e_use);
     half8_t phi, plo;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -611,7 +631,6 @@ decode_i8_mfma(const int8_t* __restrict__ kc, const int8_t* __restrict__ vc,
       phi[e] = h;
       plo[e] = (_Float16)(pw[e] - (float)h);
     }
-    const float back = ldexpf(1.0f, ex);
     // P.V: B = V codes of channels 16 n + lc for tokens tok(lg, 0..7)
     const int tr_row = 16 * ((lc / 2) / 4) + 4 * lg + (lc / 2) % 4;
 #pragma unroll
@@ -619,10 +638,8 @@ decode_i8_mfma(const int8_t* __restrict__ kc, const int8_t* __restrict__ vc,
       const int off = sw(tr_row, n) + 8 * (lc & 1);
       const int2_t raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32((SKV_LDS int2_t*)(vt + off));
       const half8_t bv = widen_codes(raw);
-      float4_t t4 = mfma_f16_32(phi, bv, float4_t{0.0f, 0.0f, 0.0f, 0.0f});
-      t4 = mfma_f16_32(plo, bv, t4);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) O[n][r] = fmaf(t4[r], back, O[n][r]);
+      O[n] = mfma_f16_32(phi, bv, O[n]);
+      O[n] = mfma_f16_32(plo, bv, O[n]);
     }
   };
 
@@ -635,6 +652,13 @@ decode_i8_mfma(const int8_t* __restrict__ kc, const int8_t* __restrict__ vc,
     process(std::integral_constant<int, 0>{}, f0, h0);
     if (!h1) break;
     process(std::integral_constant<int, 1>{}, f1, h1);
+  }
+  if (e_run != kExpUnset) {
+#pragma unroll
+    for (int n = 0; n < 8; ++n) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) O[n][r] = ldexpf(O[n][r], e_run);
+    }
   }
   finish_mfma<G>(m_run, l_run, O, reinterpret_cast<float*>(&smem[0][0][0]), ws_m, ws_l, ws_o,
                  int64_t(b) * H + g * G, n_split, split);

@@ -35,6 +35,7 @@ select_kernel(const float* __restrict__ score, const int32_t* __restrict__ seq_l
   const int32_t k_req = k_sel[b];
   SelKeys<RMAX> kk;
   kk.load(score + row * max_blocks + n_sink, max_blocks - n_sink);
+  sel_init(sh);
   const int32_t L = min(max(seq_len[b], 0), max_blocks * block);
   const int32_t nb = (L + block - 1) / block;
   const int32_t cs = min(n_sink, nb);                       // candidates [cs, ce)

@@ -35,7 +35,7 @@ constexpr int kSelWaves = kSelThreads / kWave;
 constexpr int kSelMaxChunks = 64;                 // candidates <= 64 * 256 = 16384
 
 struct __attribute__((aligned(16))) SelectShared {
-  uint32_t hist[256];
+  uint32_t hist[2][256];                          // alternating radix passes
   uint64_t slot[kWave];                           // order values tied on the prefix
   int32_t part[kSelMaxChunks * kSelWaves];        // (chunk, wave) counts -> prefixes
   uint32_t red_and[kSelWaves], red_or[kSelWaves];
@@ -70,6 +70,14 @@ __device__ __forceinline__ int sel_exclusive_scan(int v, int* tmp, int& total) {
   __syncthreads();
   total = tot;
   return off + x - v;
+}
+
+// Clears what the first radix pass and the final gathering count into.  Call
+// it (whole workgroup) before sel_cut, e.g. while the keys are in flight:
+// sel_cut's first barrier orders it before the first use.
+__device__ __forceinline__ void sel_init(SelectShared& s) {
+  s.hist[0][threadIdx.x] = 0u;                    // kSelThreads == 256 bins
+  if (threadIdx.x == 0) s.n_active = 0;
 }
 
 // Keys of candidates threadIdx.x + 256 r, r < RMAX, of a row of n.
@@ -111,20 +119,34 @@ __device__ __forceinline__ int sel_order_prepare(uint64_t flags, int R, SelectSh
     if (lane == 0) s.part[r * kSelWaves + wave] = __popcll(bal);
   }
   __syncthreads();
-  const int v = tid < R * kSelWaves ? s.part[tid] : 0;   // R * 4 <= 256 entries
-  int tot;
-  const int ex = sel_exclusive_scan(v, s.scan_tmp, tot);
-  if (tid < R * kSelWaves) s.part[tid] = ex;
+  // one wavefront scans the R * 4 <= 256 counts, four per lane
+  if (wave == 0) {
+    int c[4], sum = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int j = 4 * lane + e;
+      c[e] = j < R * kSelWaves ? s.part[j] : 0;
+      sum += c[e];
+    }
+    int ex = wave_incl_scan(sum) - sum;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int j = 4 * lane + e;
+      if (j < R * kSelWaves) s.part[j] = ex;
+      ex += c[e];
+    }
+    if (lane == kWave - 1) s.scan_tmp[0] = ex;
+  }
   __syncthreads();
-  return tot;
+  return s.scan_tmp[0];
 }
 __device__ __forceinline__ int sel_order_pos(uint64_t flags, int r, const SelectShared& s) {
   const uint64_t bal = __ballot(int((flags >> r) & 1u));
   return s.part[r * kSelWaves + threadIdx.x / kWave] + lanes_below(bal);
 }
 
-// 0 < K < n.  Returns V* in every thread: candidate i is among the K best iff
-// order_value(key_i, i) >= V*.
+// 0 < K < n, sel_init(s) called before.  Returns V* in every thread:
+// candidate i is among the K best iff order_value(key_i, i) >= V*.
 template <int RMAX>
 __device__ __forceinline__ uint64_t sel_cut(const SelKeys<RMAX>& kk, int32_t K, SelectShared& s) {
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
@@ -151,23 +173,24 @@ __device__ __forceinline__ uint64_t sel_cut(const SelKeys<RMAX>& kk, int32_t K, 
   int remaining = K;
   int active = n;
 
+  int pass = 0;
   while (active > kWave && pmask != ~0u) {
     const int free_bits = __popc(~pmask);
     const int width = free_bits < 8 ? free_bits : 8;
     const int shift = free_bits - width;
     const uint32_t dmask = (1u << width) - 1u;
-    s.hist[tid] = 0u;                      // kSelThreads == 256 bins
-    __syncthreads();
+    uint32_t* hist = s.hist[pass & 1];     // zeroed by sel_init or the previous pass
 #pragma unroll
     for (int r = 0; r < RMAX; ++r) {
       if (!kk.used(r)) break;
       const uint32_t k = kk.k[r];
-      if (kk.valid(r) && (k & pmask) == prefix) atomicAdd(&s.hist[(k >> shift) & dmask], 1u);
+      if (kk.valid(r) && (k & pmask) == prefix) atomicAdd(&hist[(k >> shift) & dmask], 1u);
     }
     __syncthreads();
+    s.hist[(pass + 1) & 1][tid] = 0u;      // for the next pass (read two barriers ago)
     if (wave == 0) {
       // lane l owns digits 255-4l .. 252-4l (descending)
-      const uint4 h4 = *reinterpret_cast<const uint4*>(&s.hist[252 - 4 * lane]);
+      const uint4 h4 = *reinterpret_cast<const uint4*>(&hist[252 - 4 * lane]);
       const int cnt[4] = {int(h4.w), int(h4.z), int(h4.y), int(h4.x)};
       const int sum = cnt[0] + cnt[1] + cnt[2] + cnt[3];
       int above = wave_incl_scan(sum) - sum;
@@ -186,12 +209,12 @@ __device__ __forceinline__ uint64_t sel_cut(const SelKeys<RMAX>& kk, int32_t K, 
     active = s.count;
     prefix |= s.digit << shift;
     pmask |= dmask << shift;
+    ++pass;
   }
 
   if (active <= kWave) {
-    // pairwise ranks of the (at most 64) candidates tied on the prefix
-    if (tid == 0) s.n_active = 0;
-    __syncthreads();
+    // the (at most 64) candidates tied on the prefix, gathered into one
+    // wavefront (s.n_active was zeroed by sel_init)
 #pragma unroll
     for (int r = 0; r < RMAX; ++r) {
       if (!kk.used(r)) break;
