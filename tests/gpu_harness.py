@@ -138,3 +138,70 @@ def quantized_host(w, b):
 
 def softmax_scale(D: int) -> float:
     return 1.0 / math.sqrt(D)
+
+
+def prefilled_cache(w, max_seq=None, whole=False):
+    """Cache holding tokens 0 .. L_b - 2 of every sequence (all L_b with
+    ``whole``), filled by skv.kv_append; rows past them are copies of the last
+    one, or zeros: they never change a bound that is read, and a step's
+    append rewrites position L_b - 1."""
+    keep = 0 if whole else 1
+    rows = max(w.lens) - keep
+    cache = skv.Cache(w.B, w.Hkv, max_seq or max(w.lens), w.D, w.kv_dtype, w.block,
+                      bounds=True, device=DEV)
+    if rows <= 0:
+        return cache
+    dt = np.float16 if w.kv_dtype == "f16" else np.float32
+    k = np.zeros((w.B, rows, w.Hkv, w.D), dt)
+    v = np.zeros((w.B, rows, w.Hkv, w.D), dt)
+    for b, L in enumerate(w.lens):
+        n = L - keep
+        if n > 0:
+            k[b, :n] = np.transpose(w.k[b][:, :n], (1, 0, 2))
+            v[b, :n] = np.transpose(w.v[b][:, :n], (1, 0, 2))
+            k[b, n:] = k[b, n - 1]
+            v[b, n:] = v[b, n - 1]
+    skv.kv_append(cache, torch.zeros(w.B, dtype=torch.int32, device=DEV),
+                  torch.from_numpy(k).to(DEV), torch.from_numpy(v).to(DEV))
+    torch.cuda.synchronize()
+    return cache
+
+
+def new_token(w):
+    """(pos0, k_new, v_new) appending token L_b - 1 of every sequence."""
+    dt = torch.float16 if w.kv_dtype == "f16" else torch.float32
+    k = np.stack([w.k[b][:, L - 1] for b, L in enumerate(w.lens)])[:, None]
+    v = np.stack([w.v[b][:, L - 1] for b, L in enumerate(w.lens)])[:, None]
+    pos = torch.tensor([L - 1 for L in w.lens], dtype=torch.int32, device=DEV)
+    return (pos, torch.from_numpy(np.ascontiguousarray(k)).to(DEV).to(dt),
+            torch.from_numpy(np.ascontiguousarray(v)).to(DEV).to(dt))
+
+
+def run_step(cache, w, quest, append=True, n_split=None):
+    """One skv_decode_step in the launch configuration bench.py times
+    (default_split parts).  Returns out and, for Quest, (score, sel, cnt) on
+    the host."""
+    q, seq_len = device_inputs(w)
+    max_len = max(w.lens)
+    pos, kn, vn = new_token(w)
+    out = torch.empty((w.B, w.H, w.D), dtype=torch.float32, device=DEV)
+    extra = {}
+    if quest:
+        max_sel = max(w.k_sel) + w.n_sink + w.n_recent
+        S = n_split or skv.default_split(w.B, w.Hkv, max_sel, kv_dtype=w.kv_dtype, sparse=True)
+        extra = dict(k_sel=torch.tensor(w.k_sel, dtype=torch.int32, device=DEV),
+                     n_sink=w.n_sink, n_recent=w.n_recent,
+                     score=torch.full((w.B, w.Hkv, cache.max_blocks), float("nan"), device=DEV),
+                     sel_idx=torch.empty((w.B, w.Hkv, max_sel), dtype=torch.int32, device=DEV),
+                     sel_cnt=torch.empty((w.B, w.Hkv), dtype=torch.int32, device=DEV))
+    else:
+        S = n_split or skv.default_split(w.B, w.Hkv, -(-max_len // w.block), kv_dtype=w.kv_dtype)
+    ws = torch.empty(skv.workspace_bytes(w.B, w.H, w.D, S), dtype=torch.uint8, device=DEV)
+    if append:
+        extra.update(pos0=pos, k_new=kn, v_new=vn)
+    skv.decode_step(cache, q, seq_len, max_len, w.softmax_scale, S, ws, out, **extra)
+    torch.cuda.synchronize()
+    if not quest:
+        return out.cpu().numpy(), None
+    return out.cpu().numpy(), (extra["score"].cpu().numpy(), extra["sel_idx"].cpu().numpy(),
+                               extra["sel_cnt"].cpu().numpy())

@@ -17,49 +17,13 @@ import torch
 import oracle
 import sparse_kv_cache_append_amd as skv
 import workloads
-from gpu_harness import DEV, quantized_host, rel_err
+from gpu_harness import DEV, new_token as _new_token, prefilled_cache as _prefilled, quantized_host, rel_err
 
 pytestmark = pytest.mark.gpu
 
 
 def _print(*a):
     print("[step]", *a, flush=True)
-
-
-def _prefilled(w, max_seq=None, whole=False):
-    """Cache holding tokens 0 .. L_b - 2 of every sequence (all L_b with
-    ``whole``); rows past them are copies of the last one, or zeros: they
-    never change a bound that is read, and the step's append rewrites
-    position L_b - 1."""
-    keep = 0 if whole else 1
-    rows = max(w.lens) - keep
-    cache = skv.Cache(w.B, w.Hkv, max_seq or max(w.lens), w.D, w.kv_dtype, w.block,
-                      bounds=True, device=DEV)
-    if rows == 0:
-        return cache
-    dt = np.float16 if w.kv_dtype == "f16" else np.float32
-    k = np.zeros((w.B, rows, w.Hkv, w.D), dt)
-    v = np.zeros((w.B, rows, w.Hkv, w.D), dt)
-    for b, L in enumerate(w.lens):
-        n = L - keep
-        if n > 0:
-            k[b, :n] = np.transpose(w.k[b][:, :n], (1, 0, 2))
-            v[b, :n] = np.transpose(w.v[b][:, :n], (1, 0, 2))
-            k[b, n:] = k[b, n - 1]
-            v[b, n:] = v[b, n - 1]
-    skv.kv_append(cache, torch.zeros(w.B, dtype=torch.int32, device=DEV),
-                  torch.from_numpy(k).to(DEV), torch.from_numpy(v).to(DEV))
-    torch.cuda.synchronize()
-    return cache
-
-
-def _new_token(w):
-    dt = torch.float16 if w.kv_dtype == "f16" else torch.float32
-    k = np.stack([w.k[b][:, L - 1] for b, L in enumerate(w.lens)])[:, None]
-    v = np.stack([w.v[b][:, L - 1] for b, L in enumerate(w.lens)])[:, None]
-    pos = torch.tensor([L - 1 for L in w.lens], dtype=torch.int32, device=DEV)
-    return (pos, torch.from_numpy(np.ascontiguousarray(k)).to(DEV).to(dt),
-            torch.from_numpy(np.ascontiguousarray(v)).to(DEV).to(dt))
 
 
 def _buffers(w, cache, quest, max_sel, S):

@@ -1,5 +1,7 @@
 """The five named decode workloads at full size, in the launch configuration
-bench.py times (skv.default_split parts), against the oracle.
+bench.py times (skv.default_split parts), against the oracle: through the
+five calls, and through skv_decode_step (append of the last token folded into
+the bounds pass, selection into the attention prologue) as bench.py runs it.
 
 Where the float64 oracle over every head would take minutes (the 262,144-token
 int8 cache, the 16-sequence batch) it checks a sample of sequences and heads
@@ -13,8 +15,8 @@ import torch
 
 import oracle
 import workloads
-from gpu_harness import (DEV, build_cache, quantized_host, rel_err, run_dense, run_select,
-                         run_sparse)
+from gpu_harness import (DEV, build_cache, prefilled_cache, quantized_host, rel_err, run_dense,
+                         run_select, run_sparse, run_step)
 
 pytestmark = pytest.mark.gpu
 
@@ -173,3 +175,69 @@ def test_workload5_quest_int8_256k(gpu_lib):
         assert rel_err(dense[0, h:h + 1], meth) < 1e-4
         dots, _, _ = oracle.int8_logit_dots(w.q[0][h:h + 1], kc[sl, ::61])
         assert np.array_equal(dbg[0, h, ::61].astype(np.int64), dots[0])
+
+
+# ------------------------------------------------------------ decode_step
+def _check_quest_step(w, out, score, sel, cnt, seqs, keys_of=None):
+    for b in seqs:
+        keys = None if keys_of is None else keys_of(b)
+        lists, near = check_selection(w, b, score, sel, cnt, keys=keys)
+        _print("seq", b, "near-tie differences", near)
+        for g in range(w.Hkv):
+            toks = oracle.selected_tokens(lists[g], w.lens[b], w.block)
+            hs = slice(g * w.G, (g + 1) * w.G)
+            if w.kv_dtype == "f16":
+                ref = oracle.attend_f16(w.q[b][hs], w.k[b][g:g + 1], w.v[b][g:g + 1],
+                                        w.softmax_scale, tokens=toks)
+                assert rel_err(out[b, hs], ref) < F16_TOL, (b, g)
+            else:
+                kc, ks, vc, vs = quantized_host(w, b)
+                sl = slice(g, g + 1)
+                meth = oracle.attend_i8(w.q[b][hs], kc[sl], ks[sl], vc[sl], vs[sl],
+                                        w.softmax_scale, tokens=toks)
+                assert rel_err(out[b, hs], meth) < 1e-4, (b, g)
+
+
+def test_workload3_decode_step(gpu_lib):
+    """The 32K Quest and dense steps exactly as bench.py times them."""
+    _print("workload 3 decode_step")
+    w = workloads.named(3)
+    base = prefilled_cache(w)
+    c2 = base.clone()
+    out, (score, sel, cnt) = run_step(base, w, quest=True)
+    assert np.all(cnt == 131)
+    _check_quest_step(w, out, score, sel, cnt, [0])
+    dense, _ = run_step(c2, w, quest=False)
+    assert rel_err(dense[0], oracle.attend_f16(w.q[0], w.k[0], w.v[0], w.softmax_scale)) < F16_TOL
+
+
+def test_workload4_decode_step(gpu_lib):
+    _print("workload 4 decode_step")
+    w = workloads.named(4)
+    base = prefilled_cache(w, max_seq=65536)
+    c2 = base.clone()
+    out, (score, sel, cnt) = run_step(base, w, quest=True)
+    _check_quest_step(w, out, score, sel, cnt, SAMPLE4)
+    dense, _ = run_step(c2, w, quest=False)
+    for b in SAMPLE4:
+        ref = oracle.attend_f16(w.q[b], w.k[b], w.v[b], w.softmax_scale)
+        assert rel_err(dense[b], ref) < F16_TOL, b
+
+
+def test_workload5_decode_step(gpu_lib):
+    """The 262K int8 Quest step (fused selection over 4,091 candidates) and a
+    sampled check of the dense int8 step."""
+    _print("workload 5 decode_step")
+    w = workloads.named(5)
+    base = prefilled_cache(w)
+    c2 = base.clone()
+    out, (score, sel, cnt) = run_step(base, w, quest=True)
+    assert np.all(cnt == 517)
+    _check_quest_step(w, out, score, sel, cnt, [0], keys_of=lambda b: w.k[b])
+    dense, _ = run_step(c2, w, quest=False)
+    kc, ks, vc, vs = quantized_host(w, 0)
+    for g in range(w.Hkv):
+        h = g * w.G + ((g + 3) % w.G)
+        sl = slice(g, g + 1)
+        meth = oracle.attend_i8(w.q[0][h:h + 1], kc[sl], ks[sl], vc[sl], vs[sl], w.softmax_scale)
+        assert rel_err(dense[0, h:h + 1], meth) < 1e-4
