@@ -57,6 +57,25 @@ constexpr int kRowBytesI8 = kD;        // 128
 
 __device__ __forceinline__ int swz(int row) { return row & 15; }
 
+// A full tile (4 KiB of K or V rows) as a raw buffer: the resource is built
+// in scalar registers from the tile's first byte, the lane's 16-byte offset
+// is loop-invariant and the row step is the instruction's immediate offset,
+// so a tile's loads need no vector address arithmetic.  Records = the tile's
+// bytes (the range check keeps every access inside it); word 3 is the plain
+// untyped-buffer configuration of the CDNA resource descriptor.  aux = 2 is
+// the nontemporal hint (each K/V byte is read once per step).
+constexpr int kTileRsrcBytes = 4096;
+constexpr int kRsrcWord3 = 0x00020000;
+constexpr int kAuxNontemporal = 2;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint8_t* t) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(t), (short)0, kTileRsrcBytes,
+                                           kRsrcWord3);
+}
+__device__ __forceinline__ int4_t tile_load(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
+  return __builtin_bit_cast(int4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0,
+                                                                         kAuxNontemporal));
+}
+
 __device__ __forceinline__ float4_t mfma_f16_32(half8_t a, half8_t b, float4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
@@ -77,10 +96,13 @@ struct TileWalk {
   }
   __device__ __forceinline__ bool more() const { return unit < n_units; }
   // first row and valid-row count of the current tile, then advance by kMWaves tiles
+  // (the walk state is wave-uniform: it lives in scalar registers)
   template <int T>
   __device__ __forceinline__ void next(int32_t& r0, int32_t& nvalid) {
     int32_t j = u0 + unit;
-    if (sel != nullptr) j = unit < kWave ? __builtin_amdgcn_readlane(jl, unit) : sel[j];
+    if (sel != nullptr)
+      j = unit < kWave ? __builtin_amdgcn_readlane(jl, unit)
+                       : __builtin_amdgcn_readfirstlane(sel[j]);
     if (j < 0 || j >= nb) {
       r0 = 0;
       nvalid = 0;
@@ -200,23 +222,26 @@ __device__ __forceinline__ TileWalk fused_walk(const FusedSelect& fs, int32_t ma
 
 // Softmax bookkeeping of one tile for the 16 MFMA columns (heads): lane l
 // owns head l%16 and rows 4*(l/16) + r of the tile.  s[r] are base-2 logits
-// (-inf for masked rows); returns the weights p[r] and rescales O.
+// (-inf for masked rows); returns the weights p[r] and rescales O (by the
+// running-max correction times o_extra, a caller's exact power of two).
 template <int G, int NT>
 __device__ __forceinline__ void tile_softmax(float (&s)[4 * NT], float& m_run, float& l_run,
-                                             float4_t (&O)[8]) {
+                                             float4_t (&O)[8], float o_extra = 1.0f) {
   const int lane = threadIdx.x % kWave;
   float mx = s[0];
 #pragma unroll
   for (int i = 1; i < 4 * NT; ++i) mx = fmaxf(mx, s[i]);
   mx = rows_max(mx);
   const float m_new = fmaxf(m_run, mx);
+  // exp2(-inf) = 0 covers masked logits and a first live tile (m_run = -inf);
+  // a head with nothing live yet keeps factor 1 and weights exp2(-inf - 0) = 0
   const bool live = m_new != -INFINITY;
-  const float cr = (live && m_run != -INFINITY) ? __builtin_amdgcn_exp2f(m_run - m_new)
-                                                : (live ? 0.0f : 1.0f);
+  const float m_use = live ? m_new : 0.0f;
+  const float cr = live ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
   float ps = 0.0f;
 #pragma unroll
   for (int i = 0; i < 4 * NT; ++i) {
-    s[i] = (s[i] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(s[i] - m_new);
+    s[i] = __builtin_amdgcn_exp2f(s[i] - m_use);
     ps += s[i];
   }
   ps = rows_sum(ps);
@@ -233,6 +258,7 @@ __device__ __forceinline__ void tile_softmax(float (&s)[4 * NT], float& m_run, f
       const float c4 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cr), 4 + r));
       c = upper ? c4 : c;
     }
+    c *= o_extra;
 #pragma unroll
     for (int n = 0; n < 8; ++n) O[n][r] *= c;
   }
@@ -306,7 +332,8 @@ decode_f16_mfma(const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc
   constexpr int kTileBytes = T * kRowBytesF16;              // 4096
   __shared__ __attribute__((aligned(16))) uint8_t smem[kMWaves][2][2 * kTileBytes];
   const int32_t split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lg = lane / 16, lc = lane % 16;
   const int32_t H = Hkv * G;
   const int32_t L = min(max(seq_len[b], 0), max_len);
@@ -346,17 +373,32 @@ decode_f16_mfma(const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc
   const uint8_t* vbase = reinterpret_cast<const uint8_t*>(vc + bg * int64_t(max_seq) * kD);
   const int32_t last = max(L - 1, 0);
   struct Frag { int4_t k[4], v[4]; int32_t nvalid; };
-  // lane loads row 4*i + lane/16 (i = 0..3) of the tile, 16-byte chunk lane%16
+  // lane loads row 4*i + lane/16 (i = 0..3) of the tile, 16-byte chunk lane%16:
+  // byte 1024 i + 16 lane of the tile.  A full tile is addressed from a
+  // uniform base; a partial one clamps its rows to the last valid token, so
+  // the V rows it reads are finite (their weights are zero).
   auto issue = [&](Frag& f) {
     int32_t r0, nv;
     tw.next<T>(r0, nv);
     f.nvalid = nv;
+    if (nv == T) {
+      static_assert(T * kRowBytesF16 == kTileRsrcBytes, "one buffer resource per tile");
+      const uint32_t lo = 16u * uint32_t(lane);
+      const auto kr = tile_rsrc(kbase + int64_t(r0) * kRowBytesF16);
+      const auto vr = tile_rsrc(vbase + int64_t(r0) * kRowBytesF16);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int32_t row = min(r0 + 4 * i + lg, last);
-      const int64_t off = int64_t(row) * kRowBytesF16 + 16 * lc;
-      f.k[i] = __builtin_nontemporal_load(reinterpret_cast<const int4_t*>(kbase + off));
-      f.v[i] = __builtin_nontemporal_load(reinterpret_cast<const int4_t*>(vbase + off));
+      for (int i = 0; i < 4; ++i) {
+        f.k[i] = tile_load(kr, lo + 1024 * i);
+        f.v[i] = tile_load(vr, lo + 1024 * i);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int32_t row = min(r0 + 4 * i + lg, last);
+        const int64_t off = int64_t(row) * kRowBytesF16 + 16 * lc;
+        f.k[i] = __builtin_nontemporal_load(reinterpret_cast<const int4_t*>(kbase + off));
+        f.v[i] = __builtin_nontemporal_load(reinterpret_cast<const int4_t*>(vbase + off));
+      }
     }
   };
 
@@ -389,7 +431,11 @@ decode_f16_mfma(const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc
     }
     float sc[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sc[r] = (4 * lg + r < nvalid) ? acc[r] : -INFINITY;
+    for (int r = 0; r < 4; ++r) sc[r] = acc[r];
+    if (nvalid < T) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sc[r] = (4 * lg + r < nvalid) ? sc[r] : -INFINITY;
+    }
     tile_softmax<G, 1>(sc, m_run, l_run, O);
     half4_t phi, plo;
     split_hi_lo4(sc, phi, plo);
@@ -443,14 +489,19 @@ decode_f16_mfma(const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc
 // of two) in the rare tile where e grows, and is scaled back at the end.
 __device__ __forceinline__ half8_t widen_codes(int2_t w) {
   typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+  // v_perm_b32 picks bytes of {0x64646464, x}: selector 0..3 = bytes of x,
+  // 4 = 0x64.  Each 16-bit half becomes 0x64 : (c + 128) = f16 1024 + c + 128.
+  constexpr uint32_t kLoSel = 0x04010400u;   // (0x64, x1, 0x64, x0)
+  constexpr uint32_t kHiSel = 0x04030402u;   // (0x64, x3, 0x64, x2)
+  const half2_t off = half2_t{(_Float16)1152.0f, (_Float16)1152.0f};
   half8_t r;
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
     const uint32_t x = uint32_t(w[k]) ^ 0x80808080u;         // c + 128 per byte
-    const uint32_t lo = (x & 0xFFu) | ((x & 0xFF00u) << 8) | 0x64006400u;
-    const uint32_t hi = ((x >> 16) & 0xFFu) | ((x >> 8) & 0xFF0000u) | 0x64006400u;
-    const half2_t a = __builtin_bit_cast(half2_t, lo) - half2_t{(_Float16)1152.0f, (_Float16)1152.0f};
-    const half2_t b = __builtin_bit_cast(half2_t, hi) - half2_t{(_Float16)1152.0f, (_Float16)1152.0f};
+    const uint32_t lo = __builtin_amdgcn_perm(0x64646464u, x, kLoSel);
+    const uint32_t hi = __builtin_amdgcn_perm(0x64646464u, x, kHiSel);
+    const half2_t a = __builtin_bit_cast(half2_t, lo) - off;
+    const half2_t b = __builtin_bit_cast(half2_t, hi) - off;
     r[4 * k + 0] = a[0];
     r[4 * k + 1] = a[1];
     r[4 * k + 2] = b[0];
@@ -475,7 +526,8 @@ decode_i8_mfma(const int8_t* __restrict__ kc, const int8_t* __restrict__ vc,
   constexpr int kBufBytes = 2 * kTileBytes + 2 * T * 4;
   __shared__ __attribute__((aligned(16))) uint8_t smem[kMWaves][2][kBufBytes];
   const int32_t split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lg = lane / 16, lc = lane % 16;
   const int32_t H = Hkv * G;
   const int32_t L = min(max(seq_len[b], 0), max_len);
@@ -531,27 +583,43 @@ decode_i8_mfma(const int8_t* __restrict__ kc, const int8_t* __restrict__ vc,
   const uint8_t* vbase = reinterpret_cast<const uint8_t*>(vc + bg * int64_t(max_seq) * kD);
   const float* ksb = ksc + bg * int64_t(max_seq);
   const float* vsb = vsc + bg * int64_t(max_seq);
-  int32_t* dbg_h = (dbg != nullptr && lc < G)
-                       ? dbg + (int64_t(b) * H + g * G + lc) * int64_t(max_len) : nullptr;
+  // optional exact-logit dump (uniform test, so the hot loop only branches once)
+  const bool want_dbg = dbg != nullptr;
+  int32_t* dbg_h = want_dbg ? dbg + (int64_t(b) * H + g * G + min(lc, G - 1)) * int64_t(max_len)
+                            : nullptr;
   const int32_t last = max(L - 1, 0);
+  const float* sbase = (lane < 32 ? ksb : vsb) + lane % 32;
   struct Frag { int4_t k[4], v[4]; float sc; int32_t r0, nvalid; };
   // lane loads row 8 i + lane / 8 (i = 0..3) of the tile, 16-byte chunk
-  // lane % 8; lanes < 32 load the K scale of token lane, the others the V
-  // scale of token lane - 32
+  // lane % 8 (byte 1024 i + 16 lane of the tile); lanes < 32 load the K scale
+  // of token lane, the others the V scale of token lane - 32.  A partial tile
+  // clamps its rows to the last valid token, so the scales it reads are
+  // finite (their weights are zero).  (Plain global loads: on the short
+  // selected-block walks the buffer form of the f16 kernel measured slower.)
   auto issue = [&](Frag& f) {
     int32_t r0, nv;
     tw.next<T>(r0, nv);
     f.r0 = r0;
     f.nvalid = nv;
+    if (nv == T) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int32_t row = min(r0 + 8 * i + lane / 8, last);
-      const int64_t off = int64_t(row) * kRowBytesI8 + 16 * (lane % 8);
-      f.k[i] = __builtin_nontemporal_load(reinterpret_cast<const int4_t*>(kbase + off));
-      f.v[i] = __builtin_nontemporal_load(reinterpret_cast<const int4_t*>(vbase + off));
+      for (int i = 0; i < 4; ++i) {
+        const int32_t row = r0 + 8 * i + lane / 8;
+        const int64_t off = int64_t(row) * kRowBytesI8 + 16 * (lane % 8);
+        f.k[i] = __builtin_nontemporal_load(reinterpret_cast<const int4_t*>(kbase + off));
+        f.v[i] = __builtin_nontemporal_load(reinterpret_cast<const int4_t*>(vbase + off));
+      }
+      f.sc = sbase[r0];
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int32_t row = min(r0 + 8 * i + lane / 8, last);
+        const int64_t off = int64_t(row) * kRowBytesI8 + 16 * (lane % 8);
+        f.k[i] = __builtin_nontemporal_load(reinterpret_cast<const int4_t*>(kbase + off));
+        f.v[i] = __builtin_nontemporal_load(reinterpret_cast<const int4_t*>(vbase + off));
+      }
+      f.sc = sbase[min(r0 + lane % 32, last) - lane % 32];
     }
-    const int32_t srow = min(r0 + lane % 32, last);
-    f.sc = lane < 32 ? ksb[srow] : vsb[srow];
   };
   auto sw = [](int row, int chunk) { return row * kRowBytesI8 + 16 * (chunk ^ (row & 7)); };
   constexpr int kExpUnset = -100000;       // no nonzero V scale seen yet
@@ -568,7 +636,7 @@ decode_i8_mfma(const int8_t* __restrict__ kc, const int8_t* __restrict__ vc,
       *reinterpret_cast<int4_t*>(kt + sw(row, lane % 8)) = fr.k[i];
       *reinterpret_cast<int4_t*>(vt + sw(row, lane % 8)) = fr.v[i];
     }
-    st[lane] = fr.sc;
+    const float scl = fr.sc;
     const int32_t nvalid = fr.nvalid, r0 = fr.r0;
     have = tw.more();
     if (have) issue(fr);
@@ -583,47 +651,52 @@ decode_i8_mfma(const int8_t* __restrict__ kc, const int8_t* __restrict__ vc,
         acc[s] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, qb[kk], acc[s], 0, 0, 0);
       }
     }
+    // V-scale unit (while the matrix cores run): 2^e_run >= every V scale
+    // seen so far; a power of two, so the V scales stored in units of it and
+    // the change of unit of O when it grows are exact
+    const int32_t vbits =
+        __builtin_amdgcn_readfirstlane(__float_as_int(wave_max(lane >= 32 ? scl : 0.0f)));
+    float unit = 1.0f;
+    if (vbits > 0) {
+      const int32_t ex =
+          __builtin_amdgcn_readfirstlane(__builtin_amdgcn_frexp_expf(__int_as_float(vbits)));
+      if (e_run == kExpUnset) {
+        e_run = ex;
+      } else if (ex > e_run) {
+        unit = ldexpf(1.0f, e_run - ex);
+        e_run = ex;
+      }
+    }
+    const int e_use = e_run == kExpUnset ? 0 : e_run;
+    st[lane] = lane >= 32 ? ldexpf(scl, -e_use) : scl;
     const float4 ks0 = *reinterpret_cast<const float4*>(st + 4 * lg);
     const float4 ks1 = *reinterpret_cast<const float4*>(st + 16 + 4 * lg);
     const float4 vs0 = *reinterpret_cast<const float4*>(st + 32 + 4 * lg);
     const float4 vs1 = *reinterpret_cast<const float4*>(st + 48 + 4 * lg);
     const float ks[8] = {ks0.x, ks0.y, ks0.z, ks0.w, ks1.x, ks1.y, ks1.z, ks1.w};
     const float vs[8] = {vs0.x, vs0.y, vs0.z, vs0.w, vs1.x, vs1.y, vs1.z, vs1.w};
-    float sc[8];
+    if (want_dbg) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int t = 16 * (e / 4) + 4 * lg + e % 4;
-      const int32_t dot = acc[e / 4][e % 4];
-      const bool ok = t < nvalid;
-      if (dbg_h != nullptr && ok) dbg_h[r0 + t] = dot;
-      sc[e] = ok ? float(dot) * coef * ks[e] : -INFINITY;
-    }
-    tile_softmax<G, 2>(sc, m_run, l_run, O);
-    // fold the V scales into the weights: P' = p * v_scale * 2^-e_run, with
-    // 2^e_run the largest V scale seen so far rounded up to a power of two
-    // (O is kept in units of 2^e_run and rescaled when e_run grows)
-    float vmax = 0.0f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) vmax = fmaxf(vmax, vs[e]);
-    vmax = rows_max(vmax);
-    if (vmax > 0.0f) {
-      const int ex = __builtin_amdgcn_frexp_expf(vmax);
-      if (e_run == kExpUnset) {
-        e_run = ex;
-      } else if (ex > e_run) {
-        const float c = ldexpf(1.0f, e_run - ex);
-#pragma unroll
-        for (int n = 0; n < 8; ++n) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) O[n][r] *= c;
-        }
-        e_run = ex;
+      for (int e = 0; e < 8; ++e) {
+        const int t = 16 * (e / 4) + 4 * lg + e % 4;
+        if (lc < G && t < nvalid) dbg_h[r0 + t] = acc[e / 4][e % 4];
       }
     }
-    const int e_use = e_run == kExpUnset ? 0 : e_run;
+    float sc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sc[e] = float(acc[e / 4][e % 4]) * coef * ks[e];
+    if (nvalid < T) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        sc[e] = 16 * (e / 4) + 4 * lg + e % 4 < nvalid ? sc[e] : -INFINITY;
+    }
+    // O is kept in units of 2^e_run; the exact change of unit when e_run
+    // grows rides on the softmax rescale of O
+    tile_softmax<G, 2>(sc, m_run, l_run, O, unit);
+    // P' = p * v_scale * 2^-e_run (the stored V scales are in that unit)
     float pw[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) pw[e] = sc[e] * ldexpf(vs[e], -e_use);
+    for (int e = 0; e < 8; ++e) pw[e] = sc[e] * vs[e];
     half8_t phi, plo;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
