@@ -115,8 +115,28 @@ struct TileWalk {
   }
 };
 
+// A given list's count and this part's entries (lane i: entry u0 + i), requested
+// at kernel entry together with the row length and the query, so the first
+// tile loads wait for one round trip only.  Entries past the count are
+// ignored through n_units.
+struct ListSeed {
+  int32_t cnt, jl;
+};
+__device__ __forceinline__ ListSeed list_seed(const int32_t* sel_idx, const int32_t* sel_cnt,
+                                              int32_t max_sel, int64_t bg, int32_t split,
+                                              int32_t units_per_split) {
+  ListSeed ls{0, -1};
+  if (sel_idx != nullptr) {
+    const int lane = threadIdx.x % kWave;
+    const int32_t e = split * units_per_split + lane;
+    ls.cnt = sel_cnt[bg];
+    if (lane < units_per_split && e < max_sel) ls.jl = sel_idx[bg * max_sel + e];
+  }
+  return ls;
+}
+
 template <int T>
-__device__ __forceinline__ TileWalk make_walk(const int32_t* sel_idx, const int32_t* sel_cnt,
+__device__ __forceinline__ TileWalk make_walk(const ListSeed& ls, const int32_t* sel_idx,
                                               int32_t max_sel, int64_t bg, int32_t L,
                                               int32_t block, int32_t split,
                                               int32_t units_per_split) {
@@ -130,14 +150,9 @@ __device__ __forceinline__ TileWalk make_walk(const int32_t* sel_idx, const int3
   tw.jl = -1;
   tw.u0 = split * units_per_split;
   if (sel_idx != nullptr) {
-    // the count and this part's list entries are loaded together (one round
-    // trip); entries past the count are ignored through n_units
     tw.sel = sel_idx + bg * max_sel;
-    const int lane = threadIdx.x % kWave;
-    const int32_t e = tw.u0 + lane;
-    const int32_t cnt = sel_cnt[bg];
-    if (lane < units_per_split && e < max_sel) tw.jl = tw.sel[e];
-    total = min(max(cnt, 0), max_sel);
+    tw.jl = ls.jl;
+    total = min(max(ls.cnt, 0), max_sel);
   }
   tw.n_units = max(0, min(units_per_split, total - tw.u0));
   return tw;
@@ -149,6 +164,8 @@ __device__ __forceinline__ TileWalk make_walk(const int32_t* sel_idx, const int3
 // launch and a round trip through memory).  All threads call this.  The
 // part's slice of the ascending list goes to LDS; split 0 also publishes
 // the whole list and its count.
+// (The scores are requested here, after the query has arrived, rather than
+// at kernel entry: issuing them first measured slower for this kernel.)
 template <int T, int SELR>
 __device__ __forceinline__ TileWalk fused_walk(const FusedSelect& fs, int32_t max_sel, int64_t bg,
                                                int32_t b, int32_t L, int32_t L_raw, int32_t block,
@@ -157,7 +174,7 @@ __device__ __forceinline__ TileWalk fused_walk(const FusedSelect& fs, int32_t ma
   __shared__ int32_t plist[kWave];
   const int tid = threadIdx.x;
   // The candidates start at n_sink whenever there are any, so their scores
-  // are requested before the row's length arrives (up to the row's capacity).
+  // are requested before the row's length is used (up to the row's capacity).
   const int32_t k_req = fs.k_sel[b];
   SelKeys<SELR> kk;
   kk.load(fs.score + bg * fs.max_blocks + fs.n_sink, fs.max_blocks - fs.n_sink);
@@ -336,8 +353,11 @@ decode_f16_mfma(const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lg = lane / 16, lc = lane % 16;
   const int32_t H = Hkv * G;
-  const int32_t L = min(max(seq_len[b], 0), max_len);
   const int64_t bg = int64_t(b) * Hkv + g;
+  // requests issued before anything waits: row length, given list, query
+  const int32_t L_raw = seq_len[b];
+  ListSeed ls{};
+  if constexpr (SELR == 0) ls = list_seed(sel_idx, sel_cnt, max_sel, bg, split, units_per_split);
 
   // query as the B operand of q.K: column = head lc, k-chunk = lg; f16 hi + lo
   half8_t qhi[4], qlo[4];
@@ -358,11 +378,12 @@ decode_f16_mfma(const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc
       }
     }
   }
+  const int32_t L = min(max(L_raw, 0), max_len);
   TileWalk tw;
   if constexpr (SELR > 0)
-    tw = fused_walk<T, SELR>(fs, max_sel, bg, b, L, seq_len[b], block, split, units_per_split);
+    tw = fused_walk<T, SELR>(fs, max_sel, bg, b, L, L_raw, block, split, units_per_split);
   else
-    tw = make_walk<T>(sel_idx, sel_cnt, max_sel, bg, L, block, split, units_per_split);
+    tw = make_walk<T>(ls, sel_idx, max_sel, bg, L, block, split, units_per_split);
   tw.init(wave);
   float m_run = -INFINITY, l_run = 0.0f;
   float4_t O[8];
@@ -530,8 +551,11 @@ decode_i8_mfma(const int8_t* __restrict__ kc, const int8_t* __restrict__ vc,
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lg = lane / 16, lc = lane % 16;
   const int32_t H = Hkv * G;
-  const int32_t L = min(max(seq_len[b], 0), max_len);
   const int64_t bg = int64_t(b) * Hkv + g;
+  // requests issued before anything waits: row length, given list, query
+  const int32_t L_raw = seq_len[b];
+  ListSeed ls{};
+  if constexpr (SELR == 0) ls = list_seed(sel_idx, sel_cnt, max_sel, bg, split, units_per_split);
 
   // Query codes as the B operand of q.K (column = head lc, k-chunk lg): the
   // head's absmax scale over all 128 channels (the 4 lanes of a column hold
@@ -568,11 +592,12 @@ decode_i8_mfma(const int8_t* __restrict__ kc, const int8_t* __restrict__ vc,
     }
     coef = hv ? qs * scale2 : 0.0f;
   }
+  const int32_t L = min(max(L_raw, 0), max_len);
   TileWalk tw;
   if constexpr (SELR > 0)
-    tw = fused_walk<T, SELR>(fs, max_sel, bg, b, L, seq_len[b], block, split, units_per_split);
+    tw = fused_walk<T, SELR>(fs, max_sel, bg, b, L, L_raw, block, split, units_per_split);
   else
-    tw = make_walk<T>(sel_idx, sel_cnt, max_sel, bg, L, block, split, units_per_split);
+    tw = make_walk<T>(ls, sel_idx, max_sel, bg, L, block, split, units_per_split);
   tw.init(wave);
   float m_run = -INFINITY, l_run = 0.0f;
   float4_t O[8];
