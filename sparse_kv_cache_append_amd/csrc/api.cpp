@@ -1,5 +1,6 @@
 // C entry points: argument validation (host only, before anything is
 // enqueued) and dispatch to the kernel launchers.
+#include <algorithm>
 #include <hip/hip_runtime.h>
 
 #include "launch.h"
@@ -201,7 +202,7 @@ skv_status skv_decode_step(const skv_cache* c, const int32_t* pos0, const void* 
     p.sel_cnt = sel_cnt;
     const int32_t ups = (max_sel + n_split - 1) / n_split;
     if (max_blocks <= skv::kFusedSelMaxCand && ups <= 64) {
-      p.fused = true;
+      p.fused_r = skv::fused_sel_chunks(std::max(max_blocks - n_sink, 1));
       p.fsel = skv::FusedSelect{score, max_blocks, k_sel, n_sink, n_recent, sel_idx, sel_cnt};
     } else {
       e = skv::launch_select(score, seq_len, c->batch, c->n_kv_heads, max_blocks, c->block,

@@ -782,14 +782,18 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   }
   dim3 grid(S, c.n_kv_heads, B);
   const float scale2 = p.softmax_scale * kLog2e;
-  const bool fused = p.fused;
+  const int fr = p.fused_r;
   if (c.kv_dtype == SKV_F16) {
 #define SKV_LAUNCH_F16(GG, SR)                                                                  \
   decode_f16_mfma<GG, SR><<<grid, kMThreads, 0, stream>>>(                                     \
       static_cast<const uint16_t*>(c.k), static_cast<const uint16_t*>(c.v), p.q, p.seq_len,    \
       p.sel_idx, p.sel_cnt, p.max_sel, c.n_kv_heads, c.max_seq, c.block, p.max_len, S, ups,    \
       scale2, ws_m, ws_l, ws_o, p.fsel)
-#define SKV_F16_G(GG) if (fused) SKV_LAUNCH_F16(GG, kFusedSelR); else SKV_LAUNCH_F16(GG, 0)
+#define SKV_F16_G(GG)                                  \
+  if (fr == 2) SKV_LAUNCH_F16(GG, 2);                  \
+  else if (fr == 4) SKV_LAUNCH_F16(GG, 4);             \
+  else if (fr > 0) SKV_LAUNCH_F16(GG, kFusedSelR);     \
+  else SKV_LAUNCH_F16(GG, 0)
     switch (G) {
       case 1: SKV_F16_G(1); break;
       case 2: SKV_F16_G(2); break;
@@ -806,7 +810,11 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
       static_cast<const int8_t*>(c.k), static_cast<const int8_t*>(c.v), c.k_scale, c.v_scale,  \
       p.q, p.seq_len, p.sel_idx, p.sel_cnt, p.max_sel, c.n_kv_heads, c.max_seq, c.block,       \
       p.max_len, S, ups, scale2, ws_m, ws_l, ws_o, p.dbg_logits, p.fsel)
-#define SKV_I8_G(GG) if (fused) SKV_LAUNCH_I8(GG, kFusedSelR); else SKV_LAUNCH_I8(GG, 0)
+#define SKV_I8_G(GG)                                   \
+  if (fr == 2) SKV_LAUNCH_I8(GG, 2);                   \
+  else if (fr == 4) SKV_LAUNCH_I8(GG, 4);              \
+  else if (fr > 0) SKV_LAUNCH_I8(GG, kFusedSelR);      \
+  else SKV_LAUNCH_I8(GG, 0)
   switch (G) {
     case 1: SKV_I8_G(1); break;
     case 2: SKV_I8_G(2); break;

@@ -24,6 +24,12 @@ struct FusedSelect {
 // Largest candidate row the folded selection handles (keys per thread x 256).
 constexpr int kFusedSelR = 16;
 constexpr int32_t kFusedSelMaxCand = kFusedSelR * 256;
+// Keys per thread of the folded selection for rows of up to n_load scores:
+// the smallest of 2, 4, 16 that holds them (a shorter unrolled prologue is
+// measurably faster to start: about 1 us per step at 512 blocks).
+inline int fused_sel_chunks(int32_t n_load) {
+  return n_load <= 2 * 256 ? 2 : n_load <= 4 * 256 ? 4 : kFusedSelR;
+}
 
 struct DecodeParams {
   const skv_cache* c;
@@ -38,7 +44,8 @@ struct DecodeParams {
   int32_t n_split;
   float* ws;
   int32_t* dbg_logits;
-  bool fused = false;       // select in the prologue from fsel (sel_idx/sel_cnt unused)
+  int fused_r = 0;          // > 0: select in the prologue from fsel with this many keys
+                            // per thread (sel_idx/sel_cnt then receive the list)
   FusedSelect fsel{};
 };
 

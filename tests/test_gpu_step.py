@@ -5,7 +5,8 @@ selection into the attention kernel's prologue; neither changes any
 arithmetic, so every result must be bit-identical to kv_append ->
 block_bounds -> select_topk -> decode_attn -> combine on an identical cache:
 the output, the appended rows, scales and side-cache bounds, the scores and
-the selected lists.  The fallback paths (selection as its own kernel when a
+the selected lists, for each size class of the folded selection.  The
+fallback paths (selection as its own kernel when a
 part spans more than 64 list entries or a row has more than 4096 blocks; the
 dense step) are held to the same bar.  One output per case is also checked
 against the float64 oracle.
@@ -129,6 +130,14 @@ STEP_CASES = [
     ("quest-f16 >4096 blocks (select kernel)", lambda: workloads.clustered(
         [509], 16, 4, 128, [3000], "f16", n_dirs=8, k_sel=[10], n_sink=1, n_recent=2),
         True, True, {"max_seq": 64 * 4100}),
+    # the folded selection holds 2, 4 or 16 keys per thread by row size:
+    # 513 candidates (the first row past 2 x 256), exactly 512 (no sink)
+    ("quest-f16 513 candidates", lambda: workloads.clustered(
+        [513], 16, 8, 128, [514 * 64 - 10], "f16", n_dirs=32, k_sel=[130], n_sink=1,
+        n_recent=2), True, True, {}),
+    ("quest-i8 512 candidates no sink", lambda: workloads.clustered(
+        [514], 32, 4, 128, [512 * 64], "i8", n_dirs=32, k_sel=[100], n_sink=0,
+        n_recent=4), True, True, {}),
     ("dense-f16 varlen", lambda: workloads.gaussian(
         510, 3, 16, 4, 128, [100, 64, 2500], "f16"), False, True, {}),
     ("dense-i8 no append", lambda: workloads.gaussian(
