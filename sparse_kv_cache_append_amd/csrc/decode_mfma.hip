@@ -162,8 +162,9 @@ __device__ __forceinline__ TileWalk make_walk(const ListSeed& ls, const int32_t*
 // (the same selection as skv_select_topk, computed redundantly by every part
 // of the row: a workgroup-local job of a few microseconds that replaces a
 // launch and a round trip through memory).  All threads call this.  The
-// part's slice of the ascending list goes to LDS; split 0 also publishes
-// the whole list and its count.
+// part's slice [u0, u0 + ups) of the ascending list goes to LDS and to the
+// published list (the n_split slices cover [0, max_sel), ups being
+// ceil(max_sel / n_split)); split 0 also publishes the count.
 // (The scores are requested here, after the query has arrived, rather than
 // at kernel entry: issuing them first measured slower for this kernel.)
 template <int T, int SELR>
@@ -196,36 +197,43 @@ __device__ __forceinline__ TileWalk fused_walk(const FusedSelect& fs, int32_t ma
   const int32_t K = min(max(k_req, 0), n_cand);
   const int32_t n_sel = cs + K + (nb - ce);
   const int32_t u0 = tw.u0, ups = units_per_split;
-  const bool publish = split == 0;
   int32_t* out_row = fs.sel_idx + bg * max_sel;
   // positions whose block follows from the counts alone
   auto arith = [&](int32_t pos) { return pos < cs || pos >= cs + K || K == n_cand; };
   auto block_at = [&](int32_t pos) { return pos < cs + K ? pos : ce + (pos - cs - K); };
   if (tid < ups) {
     const int32_t pos = u0 + tid;
-    if (pos < n_sel && arith(pos)) plist[tid] = block_at(pos);
-  }
-  if (publish) {
-    for (int32_t p = tid; p < max_sel; p += kMThreads) {
-      if (p >= n_sel) out_row[p] = -1;
-      else if (arith(p)) out_row[p] = block_at(p);
+    if (pos < max_sel) {
+      if (pos >= n_sel) {
+        out_row[pos] = -1;
+      } else if (arith(pos)) {
+        const int32_t blk = block_at(pos);
+        plist[tid] = blk;
+        out_row[pos] = blk;
+      }
     }
-    if (tid == 0) fs.sel_cnt[bg] = n_sel;
   }
+  if (split == 0 && tid == 0) fs.sel_cnt[bg] = n_sel;
   if (K > 0 && K < n_cand) {          // then cs == n_sink
     kk.set_count(n_cand);
     const uint64_t cut = sel_cut(kk, K, ssh);
     const uint64_t taken = sel_taken_mask(kk, cut);
     const int R = (n_cand + kSelThreads - 1) / kSelThreads;
-    sel_order_prepare(taken, R, ssh);
+    const SelOrder o = sel_order_prepare(taken, R, ssh);
+    // only the (chunk, wave) groups whose taken candidates reach this part's
+    // slice of positions do any work (a wave-uniform test)
 #pragma unroll
     for (int r = 0; r < SELR; ++r) {
       if (r < R) {
-        const int32_t pos = cs + sel_order_pos(taken, r, ssh);
-        if ((taken >> r) & 1u) {
-          const int32_t blk = cs + kk.index(r);
-          if (pos >= u0 && pos < u0 + ups) plist[pos - u0] = blk;
-          if (publish && pos < max_sel) out_row[pos] = blk;
+        const uint64_t bal = __ballot(int((taken >> r) & 1u));
+        const int32_t first = cs + __builtin_amdgcn_readlane(o.pre, r);
+        if (first < u0 + ups && first + __popcll(bal) > u0 && ((taken >> r) & 1u)) {
+          const int32_t pos = first + lanes_below(bal);
+          if (pos >= u0 && pos < u0 + ups) {
+            const int32_t blk = cs + kk.index(r);
+            plist[pos - u0] = blk;
+            if (pos < max_sel) out_row[pos] = blk;
+          }
         }
       }
     }
@@ -579,14 +587,35 @@ decode_i8_mfma(const int8_t* __restrict__ kc, const int8_t* __restrict__ vc,
     }
     a = rows_max(a);
     const float qs = absmax_scale(a);
+    // codes through the reciprocal; the rare value near a rounding boundary
+    // (flagged per lane) is redone with the exact quotient
+    const float inv = 1.0f / qs;
+    int c[2][16];
+    uint32_t redo = 0u;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        bool ex;
+        c[kk][i] = quant_code_recip(x[kk][i], inv, ex);
+        redo |= uint32_t(ex) << (16 * kk + i);
+      }
+    }
+    if (__builtin_amdgcn_ballot_w64(redo != 0u) != 0u) {
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if ((redo >> (16 * kk + i)) & 1u) c[kk][i] = quant_code(x[kk][i], qs);
+      }
+    }
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
         uint32_t packed = 0u;
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          packed |= (uint32_t(quant_code(x[kk][4 * w + e], qs)) & 0xFFu) << (8 * e);
+        for (int e = 0; e < 4; ++e) packed |= (uint32_t(c[kk][4 * w + e]) & 0xFFu) << (8 * e);
         qb[kk][w] = hv ? int32_t(packed) : 0;
       }
     }

@@ -156,6 +156,20 @@ __device__ __forceinline__ int quant_code(float x, float scale) {
   r = fminf(fmaxf(r, -127.0f), 127.0f);
   return int(r);
 }
+// quant_code(x, scale) through inv = 1 / scale (correctly rounded).  For
+// |x / scale| <= 128, y = x * inv carries two relative roundings of 2^-24, so
+// it lies within 2^-16 of x / scale, and the correctly rounded quotient within
+// 2^-17: the two are less than 2^-15 apart and round to the same integer
+// unless |y| is within 2^-14 of a half-integer.  Such a value (and any
+// non-finite y, e.g. a zero or subnormal scale) sets `exact`: the caller then
+// takes quant_code for it.
+__device__ __forceinline__ int quant_code_recip(float x, float inv, bool& exact) {
+  const float y = x * inv;
+  const float ay = fabsf(y);
+  exact = !(fabsf(ay - floorf(ay) - 0.5f) > 0x1p-14f);
+  const float r = fminf(fmaxf(rintf(y), -127.0f), 127.0f);
+  return int(r);
+}
 
 // ------------------------------------------------------ radix select keys
 // Order-preserving map float32 -> uint32 (larger float -> larger key), with

@@ -66,11 +66,11 @@ select_kernel(const float* __restrict__ score, const int32_t* __restrict__ seq_l
     const uint64_t cut = sel_cut(kk, K, sh);
     const uint64_t taken = sel_taken_mask(kk, cut);
     const int R = (n_cand + kSelThreads - 1) / kSelThreads;
-    sel_order_prepare(taken, R, sh);
+    const SelOrder o = sel_order_prepare(taken, R, sh);
 #pragma unroll
     for (int r = 0; r < RMAX; ++r) {
       if (r < R) {
-        const int pos = sel_order_pos(taken, r, sh);
+        const int pos = sel_order_pos(o, taken, r);
         if ((taken >> r) & 1u) emit(cs + pos, cs + kk.index(r));
       }
     }

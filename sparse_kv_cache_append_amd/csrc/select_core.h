@@ -15,15 +15,17 @@
 //     reduction): the bounds of one row share sign and most exponent bits,
 //     and a histogram of those bits would pile every key into one or two bins;
 //   * most-significant-digit radix passes (LDS histogram of 256 bins filled
-//     straight from registers, DPP prefix sum over the bins) fixing 8 more
-//     bits of the K-th key each, until at most 64 candidates share its prefix;
-//   * gathering those into one wavefront and narrowing them with ballots,
-//     one bit of the order value at a time, to the one of the right rank;
+//     straight from registers, then every wavefront scans the bins itself
+//     with a DPP prefix sum, so a pass costs one barrier) fixing 8 more bits
+//     of the K-th key each, until at most 64 candidates share its prefix;
+//   * gathering those (ballot compaction into per-wavefront rows, no
+//     atomics) and narrowing them in every wavefront with ballots, one bit
+//     of the order value at a time, to the one of the right rank;
 //   * or, if more than 64 keys equal the K-th key exactly, taking its
 //     occurrence of the right rank in index order.
 // Index order of flagged candidates (ascending output positions) comes from
-// per-(chunk, wavefront) ballot counts, one workgroup scan of those counts,
-// and the set ballot bits below each lane.
+// per-(chunk, wavefront) ballot counts, published once and scanned by every
+// wavefront, and the set ballot bits below each lane.
 #pragma once
 
 #include "device_common.h"
@@ -35,14 +37,12 @@ constexpr int kSelWaves = kSelThreads / kWave;
 constexpr int kSelMaxChunks = 64;                 // candidates <= 64 * 256 = 16384
 
 struct __attribute__((aligned(16))) SelectShared {
-  uint32_t hist[2][256];                          // alternating radix passes
-  uint64_t slot[kWave];                           // order values tied on the prefix
-  int32_t part[kSelMaxChunks * kSelWaves];        // (chunk, wave) counts -> prefixes
+  uint32_t hist[3][256];                          // rotating radix-pass histograms
+  uint64_t slot[kSelWaves][kWave];                // per-wave order values tied on the prefix
+  int32_t part[kSelMaxChunks * kSelWaves];        // (chunk, wave) counts, chunk-major
   uint32_t red_and[kSelWaves], red_or[kSelWaves];
-  int scan_tmp[kSelWaves];
-  uint64_t cut;
-  uint32_t digit;
-  int above, count, n_active;
+  int32_t n_gather[kSelWaves];
+  uint64_t cut;                                   // the many-equal-keys case only
 };
 
 __device__ __forceinline__ int lanes_below(uint64_t mask) {
@@ -53,31 +53,11 @@ __device__ __forceinline__ uint64_t order_value(uint32_t key, int32_t i) {
   return (uint64_t(key) << 32) | uint64_t(~uint32_t(i));
 }
 
-// Exclusive scan of one int per thread over the workgroup; also returns the
-// total.
-__device__ __forceinline__ int sel_exclusive_scan(int v, int* tmp, int& total) {
-  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-  const int x = wave_incl_scan(v);
-  if (lane == kWave - 1) tmp[wave] = x;
-  __syncthreads();
-  int off = 0, tot = 0;
-#pragma unroll
-  for (int w = 0; w < kSelWaves; ++w) {
-    const int t = tmp[w];
-    off += (w < wave) ? t : 0;
-    tot += t;
-  }
-  __syncthreads();
-  total = tot;
-  return off + x - v;
-}
-
-// Clears what the first radix pass and the final gathering count into.  Call
-// it (whole workgroup) before sel_cut, e.g. while the keys are in flight:
-// sel_cut's first barrier orders it before the first use.
+// Clears the first radix pass's histogram.  Call it (whole workgroup) before
+// sel_cut, e.g. while the keys are in flight: sel_cut's first barrier orders
+// it before the first use.
 __device__ __forceinline__ void sel_init(SelectShared& s) {
   s.hist[0][threadIdx.x] = 0u;                    // kSelThreads == 256 bins
-  if (threadIdx.x == 0) s.n_active = 0;
 }
 
 // Keys of candidates threadIdx.x + 256 r, r < RMAX, of a row of n.
@@ -109,40 +89,43 @@ struct SelKeys {
 };
 
 // Index order of flagged candidates.  Bit r of `flags` flags candidate
-// threadIdx.x + 256 r.  Afterwards sel_order_pos(flags, r) is a flagged
-// candidate's number of flagged candidates with a smaller index.  Returns the
-// total.  Called by the whole workgroup (R = chunks in use, <= 64).
-__device__ __forceinline__ int sel_order_prepare(uint64_t flags, int R, SelectShared& s) {
-  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+// threadIdx.x + 256 r.  sel_order_prepare publishes the per-(chunk, wave)
+// flag counts (one barrier) and every wavefront scans all of them itself:
+// lane j keeps the number of flagged candidates before (chunk j, this wave).
+// sel_order_pos is then a flagged candidate's number of flagged candidates
+// with a smaller index.  Called by the whole workgroup (R = chunks in use,
+// <= 64).  A later writer of s.part must be separated from these reads by a
+// barrier.
+struct SelOrder {
+  int pre;     // lane j: flagged candidates before (chunk j, this wave)
+  int total;   // all flagged candidates
+};
+__device__ __forceinline__ SelOrder sel_order_prepare(uint64_t flags, int R, SelectShared& s) {
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   for (int r = 0; r < R; ++r) {
     const uint64_t bal = __ballot(int((flags >> r) & 1u));
     if (lane == 0) s.part[r * kSelWaves + wave] = __popcll(bal);
   }
   __syncthreads();
-  // one wavefront scans the R * 4 <= 256 counts, four per lane
-  if (wave == 0) {
-    int c[4], sum = 0;
+  // lane j holds chunk j's four per-wave counts
+  int4 c4 = make_int4(0, 0, 0, 0);
+  if (lane < R) c4 = *reinterpret_cast<const int4*>(&s.part[lane * kSelWaves]);
+  const int c[kSelWaves] = {c4.x, c4.y, c4.z, c4.w};
+  int sum = 0, below = 0;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int j = 4 * lane + e;
-      c[e] = j < R * kSelWaves ? s.part[j] : 0;
-      sum += c[e];
-    }
-    int ex = wave_incl_scan(sum) - sum;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int j = 4 * lane + e;
-      if (j < R * kSelWaves) s.part[j] = ex;
-      ex += c[e];
-    }
-    if (lane == kWave - 1) s.scan_tmp[0] = ex;
+  for (int w = 0; w < kSelWaves; ++w) {
+    sum += c[w];
+    below += w < wave ? c[w] : 0;
   }
-  __syncthreads();
-  return s.scan_tmp[0];
+  const int incl = wave_incl_scan(sum);
+  SelOrder o;
+  o.pre = incl - sum + below;
+  o.total = __builtin_amdgcn_readlane(incl, kWave - 1);
+  return o;
 }
-__device__ __forceinline__ int sel_order_pos(uint64_t flags, int r, const SelectShared& s) {
+__device__ __forceinline__ int sel_order_pos(const SelOrder& o, uint64_t flags, int r) {
   const uint64_t bal = __ballot(int((flags >> r) & 1u));
-  return s.part[r * kSelWaves + threadIdx.x / kWave] + lanes_below(bal);
+  return __builtin_amdgcn_readlane(o.pre, r) + lanes_below(bal);
 }
 
 // 0 < K < n, sel_init(s) called before.  Returns V* in every thread:
@@ -179,72 +162,88 @@ __device__ __forceinline__ uint64_t sel_cut(const SelKeys<RMAX>& kk, int32_t K, 
     const int width = free_bits < 8 ? free_bits : 8;
     const int shift = free_bits - width;
     const uint32_t dmask = (1u << width) - 1u;
-    uint32_t* hist = s.hist[pass & 1];     // zeroed by sel_init or the previous pass
+    uint32_t* hist = s.hist[pass % 3];     // zeroed by sel_init or the previous pass
 #pragma unroll
     for (int r = 0; r < RMAX; ++r) {
       if (!kk.used(r)) break;
       const uint32_t k = kk.k[r];
       if (kk.valid(r) && (k & pmask) == prefix) atomicAdd(&hist[(k >> shift) & dmask], 1u);
     }
+    // the next pass's bins: that buffer was last read two passes ago, before
+    // every wavefront reached the previous barrier
+    s.hist[(pass + 1) % 3][tid] = 0u;
     __syncthreads();
-    s.hist[(pass + 1) & 1][tid] = 0u;      // for the next pass (read two barriers ago)
-    if (wave == 0) {
-      // lane l owns digits 255-4l .. 252-4l (descending)
-      const uint4 h4 = *reinterpret_cast<const uint4*>(&hist[252 - 4 * lane]);
-      const int cnt[4] = {int(h4.w), int(h4.z), int(h4.y), int(h4.x)};
-      const int sum = cnt[0] + cnt[1] + cnt[2] + cnt[3];
-      int above = wave_incl_scan(sum) - sum;
+    // every wavefront finds the digit of the remaining-th largest key; lane l
+    // owns digits 255-4l .. 252-4l (descending), exactly one lane holds it
+    const uint4 h4 = *reinterpret_cast<const uint4*>(&hist[252 - 4 * lane]);
+    const int cnt[4] = {int(h4.w), int(h4.z), int(h4.y), int(h4.x)};
+    const int sum = cnt[0] + cnt[1] + cnt[2] + cnt[3];
+    int above = wave_incl_scan(sum) - sum;
+    int hit = -1, hit_above = 0, hit_count = 0;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        if (above < remaining && remaining <= above + cnt[q]) {
-          s.digit = uint32_t(255 - 4 * lane - q);
-          s.above = above;
-          s.count = cnt[q];
-        }
-        above += cnt[q];
+    for (int q = 0; q < 4; ++q) {
+      if (above < remaining && remaining <= above + cnt[q]) {
+        hit = q;
+        hit_above = above;
+        hit_count = cnt[q];
       }
+      above += cnt[q];
     }
-    __syncthreads();
-    remaining -= s.above;
-    active = s.count;
-    prefix |= s.digit << shift;
+    const int src = __builtin_ctzll(__ballot(hit >= 0));
+    const uint32_t digit = uint32_t(255 - 4 * src - __builtin_amdgcn_readlane(hit, src));
+    remaining -= __builtin_amdgcn_readlane(hit_above, src);
+    active = __builtin_amdgcn_readlane(hit_count, src);
+    prefix |= digit << shift;
     pmask |= dmask << shift;
     ++pass;
   }
 
   if (active <= kWave) {
-    // the (at most 64) candidates tied on the prefix, gathered into one
-    // wavefront (s.n_active was zeroed by sel_init)
+    // the (at most 64) candidates tied on the prefix: each wavefront packs
+    // its own into its slot row (ballot compaction)
+    int n_w = 0;
 #pragma unroll
     for (int r = 0; r < RMAX; ++r) {
       if (!kk.used(r)) break;
       const uint32_t k = kk.k[r];
-      if (kk.valid(r) && (k & pmask) == prefix)
-        s.slot[atomicAdd(&s.n_active, 1)] = order_value(k, kk.index(r));
+      const bool m = kk.valid(r) && (k & pmask) == prefix;
+      const uint64_t bal = __ballot(int(m));
+      if (m) s.slot[wave][n_w + lanes_below(bal)] = order_value(k, kk.index(r));
+      n_w += __popcll(bal);
     }
+    if (lane == 0) s.n_gather[wave] = n_w;
     __syncthreads();
-    if (wave == 0) {
-      // the remaining-th largest of the m <= 64 order values, one lane each:
-      // a ballot radix from the highest bit that is not shared, keeping the
-      // lanes that can still hold it (values are distinct, so one remains)
-      const int m = active;
-      const uint64_t v = lane < m ? s.slot[lane] : 0u;
-      uint64_t cand = __ballot(lane < m);
-      int r = remaining;
-      for (int bit = 63 - __popc(pmask); bit >= 0 && __popcll(cand) > 1; --bit) {
-        const uint64_t ones = __ballot(int((v >> bit) & 1u)) & cand;
-        const int n1 = __popcll(ones);
-        if (n1 >= r) {
-          cand = ones;
-        } else {
-          r -= n1;
-          cand &= ~ones;
-        }
+    // every wavefront: lane l takes the l-th of the concatenated rows, then
+    // the remaining-th largest of the m <= 64 order values by a ballot radix
+    // from the highest bit that is not shared, keeping the lanes that can
+    // still hold it (values are distinct, so one remains)
+    const int m = active;
+    uint64_t v = 0u;
+    {
+      int idx = lane;
+#pragma unroll
+      for (int w = 0; w < kSelWaves; ++w) {
+        const int gw = s.n_gather[w];
+        if (idx >= 0 && idx < gw) v = s.slot[w][idx];
+        idx -= gw;
       }
-      if (lane == __builtin_ctzll(cand)) s.cut = v;
     }
-    __syncthreads();
-    return s.cut;
+    uint64_t cand = __ballot(lane < m);
+    int r = remaining;
+    for (int bit = 63 - __popc(pmask); bit >= 0 && __popcll(cand) > 1; --bit) {
+      const uint64_t ones = __ballot(int((v >> bit) & 1u)) & cand;
+      const int n1 = __popcll(ones);
+      if (n1 >= r) {
+        cand = ones;
+      } else {
+        r -= n1;
+        cand &= ~ones;
+      }
+    }
+    const int win = __builtin_ctzll(cand);
+    const uint32_t hi = __builtin_amdgcn_readlane(uint32_t(v >> 32), win);
+    const uint32_t lo = __builtin_amdgcn_readlane(uint32_t(v), win);
+    return (uint64_t(hi) << 32) | lo;
   }
   // every bit fixed and more than 64 keys equal the K-th key: its occurrence
   // number `remaining` in index order is the cut
@@ -255,15 +254,15 @@ __device__ __forceinline__ uint64_t sel_cut(const SelKeys<RMAX>& kk, int32_t K, 
     if (kk.valid(r) && kk.k[r] == prefix) eq |= uint64_t(1) << r;
   }
   const int R = (n + kSelThreads - 1) / kSelThreads;
-  sel_order_prepare(eq, R, s);
+  const SelOrder ord = sel_order_prepare(eq, R, s);
 #pragma unroll
   for (int r = 0; r < RMAX; ++r) {
     if (r < R) {
-      const int pos = sel_order_pos(eq, r, s);
+      const int pos = sel_order_pos(ord, eq, r);
       if (((eq >> r) & 1u) && pos == remaining - 1) s.cut = order_value(prefix, kk.index(r));
     }
   }
-  __syncthreads();
+  __syncthreads();                          // also ends the reads of s.part
   return s.cut;
 }
 

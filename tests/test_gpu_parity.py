@@ -168,6 +168,45 @@ def test_dense_i8_matches_method_and_contract(gpu_lib, B, H, Hkv, lens):
         assert rel_err(out[b], contract) < contract_bar(meth, contract)
 
 
+def _boundary_query(rng, H, D):
+    """Query rows whose x / scale sit on and next to half-integers: entry 0
+    sets the absmax a (code 127); the others are fl32((k + 1/2) * scale)
+    moved by -2..2 ulps.  Scales that are powers of two make exact ties."""
+    q = np.empty((H, D), np.float32)
+    amax = [127.0 * 2.0 ** -5, 3.7, 0.011, 250.3, 127.0, 1.0e-3, 88.125, 127.0 * 2.0 ** 3]
+    for h in range(H):
+        a = np.float32(amax[h % len(amax)])
+        s = np.float32(a / np.float32(127))
+        q[h, 0] = a
+        k = rng.integers(-126, 126, size=D - 1)
+        x = ((k + 0.5) * np.float64(s)).astype(np.float32)
+        for j, step in enumerate(rng.integers(-2, 3, size=D - 1)):
+            for _ in range(abs(int(step))):
+                x[j] = np.nextafter(x[j], np.float32(np.inf if step > 0 else -np.inf))
+        q[h, 1:] = x
+    return q
+
+
+def test_i8_query_codes_at_rounding_boundaries(gpu_lib):
+    """The kernel quantizes the query through the reciprocal of its scale and
+    redoes a value with the exact quotient when the product lands within 2^-14
+    of a half-integer.  Queries built on those boundaries (ties included) must
+    still give the oracle's codes: the int32 logits are compared exactly."""
+    _print("i8 query rounding boundaries")
+    w = workloads.gaussian(44, 1, 16, 2, 128, [300], "i8")
+    rng = np.random.default_rng(4401)
+    w.q[0] = _boundary_query(rng, 16, 128)
+    s = (np.max(np.abs(w.q[0]), axis=1) / np.float32(127)).astype(np.float32)
+    y = w.q[0] * (np.float32(1) / s)[:, None]
+    near = np.abs(np.abs(y) - np.floor(np.abs(y)) - 0.5) <= 2.0 ** -14
+    assert near.sum() > 100                    # the exact path runs
+    cache = build_cache(w)
+    _, dbg = run_dense(cache, w, dbg=True)
+    kc, _, _, _ = quantized_host(w, 0)
+    dots, _, _ = oracle.int8_logit_dots(w.q[0], kc)
+    assert np.array_equal(dbg[0, :, :300].astype(np.int64), dots)
+
+
 def test_zero_query_gives_mean_of_values(gpu_lib):
     """q = 0: every logit is 0 and the output is mean(V) (cpu-attn card,
     'Method': uniform-logit constructions)."""
