@@ -101,33 +101,24 @@ bounds_kernel(uint16_t* __restrict__ kmin, uint16_t* __restrict__ kmax,
               float* __restrict__ score, int32_t Hkv, int32_t max_len, int32_t block,
               int32_t max_blocks, AppendOne ap) {
   static_assert(D == kLanesPerBlock * 8, "one 16-byte load per lane per bound");
+  static_assert(G * D / 4 <= kBoundsThreads, "one 16-byte query load per thread");
   const int32_t g = blockIdx.y, b = blockIdx.z;
-  int32_t jn = -1;
-  bool fresh = false;
-  if constexpr (MODE != kNoAppend) {
-    const int32_t p0 = ap.pos0[b];
-    if (p0 >= 0 && p0 < ap.max_seq) {
-      jn = p0 / block;
-      fresh = (p0 % block) == 0;
-      if (blockIdx.x == 0) append_one<D, MODE>(ap, kmin, kmax, b, g, Hkv, p0, jn, fresh, max_blocks);
-    }
-  }
-  const int32_t L = min(max(seq_len[b], 0), max_len);
-  const int32_t nb = (L + block - 1) / block;
   const int32_t j = int32_t(blockIdx.x) * kBlocksPerWG + int32_t(threadIdx.x) / kLanesPerBlock;
   const int32_t c = threadIdx.x % kLanesPerBlock;  // channels 8c .. 8c+7
-  if (int32_t(blockIdx.x) * kBlocksPerWG >= nb) return;   // whole tile past the end
-
-  // The group's G query rows (G * 512 B) are read once per workgroup into
-  // LDS, one 16-byte load per thread, together with this thread's bounds.
-  __shared__ __attribute__((aligned(16))) float qs[G * D];
+  // Requests issued before anything waits (one round trip): the row length
+  // (and append position), the group's G query rows (G * 512 B, one 16-byte
+  // load per thread, staged once per workgroup in LDS) and this thread's
+  // bounds, read for every block of the launched tile that exists in the
+  // side cache; only those below the row's length are scored.
+  const int32_t L_raw = seq_len[b];
+  int32_t p0 = -1;
+  if constexpr (MODE != kNoAppend) p0 = ap.pos0[b];
   const int32_t H = Hkv * G;
   const float* qg = q + (int64_t(b) * H + g * G) * D;
-  for (int i = threadIdx.x; i < G * D / 4; i += kBoundsThreads)
-    reinterpret_cast<float4*>(qs)[i] = reinterpret_cast<const float4*>(qg)[i];
-  const bool live = j < nb;
+  float4 qreg = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  if (threadIdx.x < G * D / 4) qreg = reinterpret_cast<const float4*>(qg)[threadIdx.x];
   uint4 lo = make_uint4(0, 0, 0, 0), hi = make_uint4(0, 0, 0, 0);
-  if (live) {
+  if (j < max_blocks) {
     const int64_t off = ((int64_t(b) * Hkv + g) * max_blocks + j) * D + c * 8;
     // read once per step: streaming (nontemporal) loads
     typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -136,6 +127,22 @@ bounds_kernel(uint16_t* __restrict__ kmin, uint16_t* __restrict__ kmax,
     lo = make_uint4(l4.x, l4.y, l4.z, l4.w);
     hi = make_uint4(h4.x, h4.y, h4.z, h4.w);
   }
+  int32_t jn = -1;
+  bool fresh = false;
+  if constexpr (MODE != kNoAppend) {
+    if (p0 >= 0 && p0 < ap.max_seq) {
+      jn = p0 / block;
+      fresh = (p0 % block) == 0;
+      if (blockIdx.x == 0) append_one<D, MODE>(ap, kmin, kmax, b, g, Hkv, p0, jn, fresh, max_blocks);
+    }
+  }
+  const int32_t L = min(max(L_raw, 0), max_len);
+  const int32_t nb = (L + block - 1) / block;
+  if (int32_t(blockIdx.x) * kBlocksPerWG >= nb) return;   // whole tile past the end
+
+  __shared__ __attribute__((aligned(16))) float qs[G * D];
+  if (threadIdx.x < G * D / 4) reinterpret_cast<float4*>(qs)[threadIdx.x] = qreg;
+  const bool live = j < nb;
   __syncthreads();
   float qv[G][8];
 #pragma unroll
