@@ -171,9 +171,12 @@ def test_dense_i8_matches_method_and_contract(gpu_lib, B, H, Hkv, lens):
 def _boundary_query(rng, H, D):
     """Query rows whose x / scale sit on and next to half-integers: entry 0
     sets the absmax a (code 127); the others are fl32((k + 1/2) * scale)
-    moved by -2..2 ulps.  Scales that are powers of two make exact ties."""
+    moved by -2..2 ulps.  Scales that are powers of two make exact ties; an
+    absmax of 1e-37 gives a subnormal scale, and 1e-44 a scale that rounds to
+    0 (all codes 0; the reciprocal is then infinite)."""
     q = np.empty((H, D), np.float32)
-    amax = [127.0 * 2.0 ** -5, 3.7, 0.011, 250.3, 127.0, 1.0e-3, 88.125, 127.0 * 2.0 ** 3]
+    amax = [127.0 * 2.0 ** -5, 3.7, 0.011, 250.3, 127.0, 1.0e-3, 88.125, 127.0 * 2.0 ** 3,
+            1.0e-37, 1.0e-44]
     for h in range(H):
         a = np.float32(amax[h % len(amax)])
         s = np.float32(a / np.float32(127))
@@ -197,8 +200,9 @@ def test_i8_query_codes_at_rounding_boundaries(gpu_lib):
     rng = np.random.default_rng(4401)
     w.q[0] = _boundary_query(rng, 16, 128)
     s = (np.max(np.abs(w.q[0]), axis=1) / np.float32(127)).astype(np.float32)
-    y = w.q[0] * (np.float32(1) / s)[:, None]
-    near = np.abs(np.abs(y) - np.floor(np.abs(y)) - 0.5) <= 2.0 ** -14
+    with np.errstate(divide="ignore", over="ignore", invalid="ignore"):
+        y = w.q[0] * (np.float32(1) / s)[:, None]           # inf / nan for the zero scale
+        near = ~(np.abs(np.abs(y) - np.floor(np.abs(y)) - 0.5) > 2.0 ** -14)
     assert near.sum() > 100                    # the exact path runs
     cache = build_cache(w)
     _, dbg = run_dense(cache, w, dbg=True)

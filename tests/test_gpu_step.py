@@ -138,6 +138,10 @@ STEP_CASES = [
     ("quest-i8 512 candidates no sink", lambda: workloads.clustered(
         [514], 32, 4, 128, [512 * 64], "i8", n_dirs=32, k_sel=[100], n_sink=0,
         n_recent=4), True, True, {}),
+    # 7 parts: the published slices do not divide the list evenly
+    ("quest-f16 7 parts", lambda: workloads.clustered(
+        [515, 516], 32, 8, 128, [6000, 9000], "f16", n_dirs=16, k_sel=[20, 33], n_sink=1,
+        n_recent=2), True, True, {"S": 7}),
     ("dense-f16 varlen", lambda: workloads.gaussian(
         510, 3, 16, 4, 128, [100, 64, 2500], "f16"), False, True, {}),
     ("dense-i8 no append", lambda: workloads.gaussian(
@@ -193,3 +197,20 @@ def test_decode_step_replays_in_a_hip_graph(gpu_lib):
         torch.cuda.synchronize()
         assert torch.equal(out, ref)
         assert torch.equal(sel, ref_sel)
+
+
+def test_decode_step_all_scores_equal(gpu_lib):
+    """q = 0: every block bound is 0, so more than 64 candidates tie on the
+    cut key and the folded selection takes its index-order branch; the lowest
+    candidate indices win (the tie rule), as in skv_select_topk."""
+    _print("step q=0")
+    w = workloads.clustered([517], 32, 8, 128, [20000], "f16", n_dirs=16, k_sel=[70],
+                            n_sink=1, n_recent=2)
+    w.q[:] = 0
+    out, (sel, cnt) = _run_case(w, True, True)
+    nb = -(-20000 // 64)
+    want = list(range(0, 1 + 70)) + [nb - 2, nb - 1]
+    for g in range(w.Hkv):
+        assert cnt[0, g] == len(want)
+        assert list(sel[0, g, :cnt[0, g]]) == want
+    _oracle_check(w, out, (sel, cnt))
