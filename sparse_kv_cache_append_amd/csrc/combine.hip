@@ -5,13 +5,15 @@
 // non-empty part gets zeros.
 //
 // The merge is latency-bound (a few KiB per head, read right after the decode
-// kernel wrote it from every XCD), so it is shaped for few memory round trips:
-// one wavefront per head, lane l covering channels 4 (l % 32) .. +3, the two
-// 32-lane halves taking the two halves of each batch of 2 HB parts (HB = 16
-// or 32).  Every load of a batch is issued before any is used: HB float4
-// numerators plus the batch's maxima and masses (as float4 where aligned),
-// under the wavefront's limit of outstanding loads.  The halves meet through
-// a lane swap across the two 32-lane halves.
+// kernel wrote it from every XCD), so it is shaped for few memory round trips
+// and short per-lane queues: W = min(4, ceil(n_split / 16)) wavefronts per
+// head, wavefront w taking parts 16 w .. 16 w + 15 of every batch of 16 W
+// parts, its two 32-lane halves 8 parts each, lane l covering channels
+// 4 (l % 32) .. +3.  Every load of a batch is issued before any is used
+// (8 float4 numerators plus the maxima and masses).  The halves meet through
+// a lane swap across the two 32-lane halves, the wavefronts through LDS.
+#include <algorithm>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -35,16 +37,21 @@ __device__ __forceinline__ void store4(float* p, float4 v) {
   }
 }
 
+constexpr int kCombineMaxWaves = 4;
+constexpr int kCombineHalf = 8;                         // parts per half-wavefront and batch
+constexpr int kCombineWavePart = 2 * kCombineHalf;      // parts per wavefront and batch
+
 // VEC: numerators and outputs 16-byte aligned; VML: so are the maxima and
-// masses of every head (n_split % 4 == 0 and aligned bases).  HB: parts per
-// half-wavefront and round trip (16 up to 32 parts, else 32).
-template <bool VEC, bool VML, int HB>
-__global__ void __launch_bounds__(kWave)
+// masses of every head (n_split % 4 == 0 and aligned bases).
+template <bool VEC, bool VML>
+__global__ void __launch_bounds__(kCombineMaxWaves * kWave)
 combine_kernel(const float* __restrict__ ws_m, const float* __restrict__ ws_l,
                const float* __restrict__ ws_o, int32_t n_split, int32_t D,
                float* __restrict__ out) {
+  constexpr int HB = kCombineHalf;
   const int64_t head = blockIdx.x;
-  const int lane = threadIdx.x, half = lane / 32;
+  const int lane = threadIdx.x % kWave, half = lane / 32;
+  const int wave = threadIdx.x / kWave, W = blockDim.x / kWave;
   const int d4 = 4 * (lane % 32) + 128 * blockIdx.y;   // first of this lane's 4 channels
   const bool ch_ok = d4 < D;
   const float* mp = ws_m + head * n_split;
@@ -52,7 +59,7 @@ combine_kernel(const float* __restrict__ ws_m, const float* __restrict__ ws_l,
   const float* op = ws_o + head * int64_t(n_split) * D;
   float M = -INFINITY, den = 0.0f;
   float4 num = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-  for (int32_t i0 = 0; i0 < n_split; i0 += 2 * HB) {
+  for (int32_t i0 = kCombineWavePart * wave; i0 < n_split; i0 += kCombineWavePart * W) {
     const int32_t p0 = i0 + HB * half;          // this half's first part
     float mv[HB], lv[HB];
     float4 ov[HB];
@@ -110,6 +117,32 @@ combine_kernel(const float* __restrict__ ws_m, const float* __restrict__ ws_l,
   t = __uint_as_float(halves_lo(__float_as_uint(num.z), h)); num.z = t + __uint_as_float(h);
   t = __uint_as_float(halves_lo(__float_as_uint(num.w), h)); num.w = t + __uint_as_float(h);
   t = __uint_as_float(halves_lo(__float_as_uint(den), h)); den = t + __uint_as_float(h);
+  if (W > 1) {
+    // the wavefronts' states meet in wavefront 0 (a wavefront with no
+    // non-empty part has M = -inf and adds nothing)
+    __shared__ float s_m[kCombineMaxWaves], s_den[kCombineMaxWaves];
+    __shared__ float4 s_num[kCombineMaxWaves][32];
+    if (lane == 0) { s_m[wave] = M; s_den[wave] = den; }
+    if (half == 0) s_num[wave][lane] = num;
+    __syncthreads();
+    if (wave != 0) return;
+    float Mg = -INFINITY;
+    for (int w = 0; w < W; ++w) Mg = fmaxf(Mg, s_m[w]);
+    M = Mg;
+    den = 0.0f;
+    num = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    if (Mg != -INFINITY) {
+      for (int w = 0; w < W; ++w) {
+        const float a = (s_m[w] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(s_m[w] - Mg);
+        const float4 nw = s_num[w][lane % 32];
+        num.x = fmaf(a, nw.x, num.x);
+        num.y = fmaf(a, nw.y, num.y);
+        num.z = fmaf(a, nw.z, num.z);
+        num.w = fmaf(a, nw.w, num.w);
+        den = fmaf(a, s_den[w], den);
+      }
+    }
+  }
   if (half == 0 && ch_ok) {
     float4 o;
     o.x = den > 0.0f ? num.x / den : 0.0f;
@@ -131,14 +164,14 @@ hipError_t launch_combine(const float* ws, int32_t batch, int32_t n_heads, int32
   auto aligned = [](const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; };
   const bool vec = aligned(ws_o) && aligned(out) && head_dim % 4 == 0;
   const bool vml = aligned(ws_m) && aligned(ws_l) && n_split % 4 == 0;
-#define SKV_COMBINE(V, M, HB)                                                                 \
-  combine_kernel<V, M, HB><<<grid, kWave, 0, stream>>>(ws_m, ws_l, ws_o, n_split, head_dim, out)
-#define SKV_COMBINE_HB(V, M) if (n_split <= 32) SKV_COMBINE(V, M, 16); else SKV_COMBINE(V, M, 32)
-  if (vec && vml) SKV_COMBINE_HB(true, true);
-  else if (vec) SKV_COMBINE_HB(true, false);
-  else if (vml) SKV_COMBINE_HB(false, true);
-  else SKV_COMBINE_HB(false, false);
-#undef SKV_COMBINE_HB
+  const int W = std::min(kCombineMaxWaves, std::max(1, (n_split + kCombineWavePart - 1) /
+                                                         kCombineWavePart));
+#define SKV_COMBINE(V, M)                                                                     \
+  combine_kernel<V, M><<<grid, W * kWave, 0, stream>>>(ws_m, ws_l, ws_o, n_split, head_dim, out)
+  if (vec && vml) SKV_COMBINE(true, true);
+  else if (vec) SKV_COMBINE(true, false);
+  else if (vml) SKV_COMBINE(false, true);
+  else SKV_COMBINE(false, false);
 #undef SKV_COMBINE
   return hipGetLastError();
 }
