@@ -6,7 +6,7 @@
 //
 // The merge is latency-bound (a few KiB per head, read right after the decode
 // kernel wrote it from every XCD), so it is shaped for few memory round trips
-// and short per-lane queues: W = min(4, ceil(n_split / 16)) wavefronts per
+// and short per-lane queues: W = min(8, ceil(n_split / 16)) wavefronts per
 // head, wavefront w taking parts 16 w .. 16 w + 15 of every batch of 16 W
 // parts, its two 32-lane halves 8 parts each, lane l covering channels
 // 4 (l % 32) .. +3.  Every load of a batch is issued before any is used
@@ -37,7 +37,7 @@ __device__ __forceinline__ void store4(float* p, float4 v) {
   }
 }
 
-constexpr int kCombineMaxWaves = 4;
+constexpr int kCombineMaxWaves = 8;
 constexpr int kCombineHalf = 8;                         // parts per half-wavefront and batch
 constexpr int kCombineWavePart = 2 * kCombineHalf;      // parts per wavefront and batch
 
