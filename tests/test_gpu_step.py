@@ -214,3 +214,46 @@ def test_decode_step_all_scores_equal(gpu_lib):
         assert cnt[0, g] == len(want)
         assert list(sel[0, g, :cnt[0, g]]) == want
     _oracle_check(w, out, (sel, cnt))
+
+
+def test_int8_decode_step_replays_in_a_hip_graph(gpu_lib):
+    """The int8 Quest step (append folded into bounds, selection folded into
+    the attention prologue with 4 keys per thread) captured once and replayed
+    with eager work between the replays gives the eager result each time."""
+    _print("int8 step graph")
+    w = workloads.clustered([518], 32, 4, 128, [40000], "i8", n_dirs=32, k_sel=[80],
+                            n_sink=1, n_recent=4)
+    base = _prefilled(w)
+    q = torch.from_numpy(np.ascontiguousarray(w.q)).to(DEV)
+    seq_len = torch.tensor(w.lens, dtype=torch.int32, device=DEV)
+    ks = torch.tensor(w.k_sel, dtype=torch.int32, device=DEV)
+    pos, kn, vn = _new_token(w)
+    max_sel = 85
+    S = skv.default_split(1, 4, max_sel, kv_dtype="i8", sparse=True)
+    out, ws, sc, sel, cnt = _buffers(w, base, True, max_sel, S)
+
+    def step():
+        skv.decode_step(base, q, seq_len, 40000, w.softmax_scale, S, ws, out, pos0=pos,
+                        k_new=kn, v_new=vn, k_sel=ks, n_sink=1, n_recent=4, score=sc,
+                        sel_idx=sel, sel_cnt=cnt)
+
+    step()
+    torch.cuda.synchronize()
+    ref, ref_sel = out.clone(), sel.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for _ in range(4):
+        out.fill_(float("nan"))
+        sel.fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref)
+        assert torch.equal(sel, ref_sel)
+    _oracle_check(w, out.cpu().numpy(), (sel.cpu().numpy(), cnt.cpu().numpy()))
