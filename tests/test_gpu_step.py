@@ -257,3 +257,35 @@ def test_int8_decode_step_replays_in_a_hip_graph(gpu_lib):
         assert torch.equal(out, ref)
         assert torch.equal(sel, ref_sel)
     _oracle_check(w, out.cpu().numpy(), (sel.cpu().numpy(), cnt.cpu().numpy()))
+
+
+@pytest.mark.parametrize("k_sel", [100, 300])
+def test_decode_step_tie_classes(gpu_lib, k_sel):
+    """Blocks that repeat 8 contents have 8 distinct bounds per KV head, each
+    shared by about 64 candidates, so the cut falls inside a tie class: the
+    folded selection must give the oracle's rule on the step's own scores
+    (the K best, exact ties to the lower index)."""
+    _print("step tie classes", k_sel)
+    w = workloads.clustered([519], 32, 8, 128, [512 * 64], "f16", n_dirs=8, k_sel=[k_sel],
+                            n_sink=1, n_recent=2)
+    for j in range(8, 512):
+        src = j % 8
+        w.k[0][:, j * 64:(j + 1) * 64] = w.k[0][:, src * 64:(src + 1) * 64]
+    base = _prefilled(w)
+    cb = base.clone()
+    q = torch.from_numpy(np.ascontiguousarray(w.q)).to(DEV)
+    seq_len = torch.tensor(w.lens, dtype=torch.int32, device=DEV)
+    ks = torch.tensor(w.k_sel, dtype=torch.int32, device=DEV)
+    max_sel = k_sel + 3
+    S = skv.default_split(1, 8, max_sel, sparse=True)
+    pos, kn, vn = _new_token(w)
+    out, ws, sc, sel, cnt = _buffers(w, cb, True, max_sel, S)
+    skv.decode_step(cb, q, seq_len, 512 * 64, w.softmax_scale, S, ws, out, pos0=pos, k_new=kn,
+                    v_new=vn, k_sel=ks, n_sink=1, n_recent=2, score=sc, sel_idx=sel, sel_cnt=cnt)
+    torch.cuda.synchronize()
+    score, s_h, c_h = sc.cpu().numpy(), sel.cpu().numpy(), cnt.cpu().numpy()
+    for g in range(8):
+        assert len(np.unique(score[0, g, 1:510])) <= 8
+        own = oracle.select_blocks(score[0, g], 512, k_sel, 1, 2)["sel"]
+        assert np.array_equal(s_h[0, g, :c_h[0, g]], own), g
+    _oracle_check(w, out.cpu().numpy(), (s_h, c_h))
