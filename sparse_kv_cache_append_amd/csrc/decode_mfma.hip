@@ -70,14 +70,23 @@ __device__ __forceinline__ int swz(int row) { return row & 15; }
 constexpr int kTileRsrcBytes = 4096;
 constexpr int kRsrcWord3 = 0x00020000;
 constexpr int kAuxNontemporal = 2;
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint8_t* t) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(t), (short)0, kTileRsrcBytes,
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint8_t* t,
+                                                           int bytes = kTileRsrcBytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(t), (short)0, bytes,
                                            kRsrcWord3);
 }
 __device__ __forceinline__ int4_t tile_load(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
   return __builtin_bit_cast(int4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0,
                                                                          kAuxNontemporal));
 }
+
+// Every refill of a tile fragment issues the same number of loads, also
+// when the walk is over: then through a resource of zero records, which
+// returns zeros and touches no memory.  The hardware load counter completes
+// in order, and a path that issued fewer loads (a conditional refill) makes
+// the compiler's wait at the next join conservative: the wave would then
+// wait for every tile in flight, the one two steps ahead included, at each
+// turn of the loop.
 
 __device__ __forceinline__ float4_t mfma_f16_32(half8_t a, half8_t b, float4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
@@ -98,6 +107,11 @@ struct TileWalk {
     sub = w - unit * tpb;
   }
   __device__ __forceinline__ bool more() const { return unit < n_units; }
+  // tiles left in this wavefront's walk (it takes every kMWaves-th tile)
+  __device__ __forceinline__ int32_t count() const {
+    const int32_t left = (n_units - unit) * tpb - sub;
+    return left > 0 ? (left + kMWaves - 1) / kMWaves : 0;
+  }
   // first row and valid-row count of the current tile, then advance by kMWaves tiles
   // (the walk state is wave-uniform: it lives in scalar registers)
   template <int T>
@@ -111,7 +125,7 @@ struct TileWalk {
       nvalid = 0;
     } else {
       r0 = j * block + sub * T;
-      nvalid = min(min(T, block - sub * T), L - r0);
+      nvalid = __builtin_amdgcn_readfirstlane(min(min(T, block - sub * T), L - r0));
     }
     sub += kMWaves;
     while (sub >= tpb) { sub -= tpb; ++unit; }
@@ -155,7 +169,7 @@ __device__ __forceinline__ TileWalk make_walk(const ListSeed& ls, const int32_t*
   if (sel_idx != nullptr) {
     tw.sel = sel_idx + bg * max_sel;
     tw.jl = ls.jl;
-    total = min(max(ls.cnt, 0), max_sel);
+    total = min(max(__builtin_amdgcn_readfirstlane(ls.cnt), 0), max_sel);
   }
   tw.n_units = max(0, min(units_per_split, total - tw.u0));
   return tw;
@@ -244,7 +258,7 @@ __device__ __forceinline__ TileWalk fused_walk(const FusedSelect& fs, int32_t ma
   __syncthreads();
   const int lane = tid % kWave;
   tw.jl = lane < ups ? plist[lane] : -1;
-  tw.n_units = max(0, min(ups, min(n_sel, max_sel) - u0));
+  tw.n_units = __builtin_amdgcn_readfirstlane(max(0, min(ups, min(n_sel, max_sel) - u0)));
   return tw;
 }
 
@@ -389,7 +403,8 @@ decode_f16_mfma(const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc
       }
     }
   }
-  const int32_t L = min(max(L_raw, 0), max_len);
+  // wave-uniform (scalar): the walk and its branches stay scalar
+  const int32_t L = __builtin_amdgcn_readfirstlane(min(max(L_raw, 0), max_len));
   TileWalk tw;
   if constexpr (SELR > 0)
     tw = fused_walk<T, SELR>(fs, max_sel, bg, b, L, L_raw, block, split, units_per_split);
@@ -403,40 +418,32 @@ decode_f16_mfma(const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc
 
   const uint8_t* kbase = reinterpret_cast<const uint8_t*>(kc + bg * int64_t(max_seq) * kD);
   const uint8_t* vbase = reinterpret_cast<const uint8_t*>(vc + bg * int64_t(max_seq) * kD);
-  const int32_t last = max(L - 1, 0);
   struct Frag { int4_t k[4], v[4]; int32_t nvalid; };
   // lane loads row 4*i + lane/16 (i = 0..3) of the tile, 16-byte chunk lane%16:
-  // byte 1024 i + 16 lane of the tile.  A full tile is addressed from a
-  // uniform base; a partial one clamps its rows to the last valid token, so
-  // the V rows it reads are finite (their weights are zero).
+  // byte 1024 i + 16 lane of the tile, through the tile's buffer resource.
+  // Its record count is the tile's valid bytes, so the rows of a partial
+  // tile past the row's length, and every row once the walk is over, read as
+  // zeros without touching memory: one load sequence for every case, no
+  // branch (the masked weights of those rows are zero).
   auto issue = [&](Frag& f) {
-    int32_t r0, nv;
-    tw.next<T>(r0, nv);
+    int32_t r0 = 0, nv = 0;
+    if (tw.more()) tw.next<T>(r0, nv);
     f.nvalid = nv;
-    if (nv == T) {
-      static_assert(T * kRowBytesF16 == kTileRsrcBytes, "one buffer resource per tile");
-      const uint32_t lo = 16u * uint32_t(lane);
-      const auto kr = tile_rsrc(kbase + int64_t(r0) * kRowBytesF16);
-      const auto vr = tile_rsrc(vbase + int64_t(r0) * kRowBytesF16);
+    static_assert(T * kRowBytesF16 == kTileRsrcBytes, "one buffer resource per tile");
+    const uint32_t lo = 16u * uint32_t(lane);
+    const int bytes = __builtin_amdgcn_readfirstlane(max(nv, 0) * kRowBytesF16);
+    const auto kr = tile_rsrc(kbase + int64_t(r0) * kRowBytesF16, bytes);
+    const auto vr = tile_rsrc(vbase + int64_t(r0) * kRowBytesF16, bytes);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        f.k[i] = tile_load(kr, lo + 1024 * i);
-        f.v[i] = tile_load(vr, lo + 1024 * i);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int32_t row = min(r0 + 4 * i + lg, last);
-        const int64_t off = int64_t(row) * kRowBytesF16 + 16 * lc;
-        f.k[i] = __builtin_nontemporal_load(reinterpret_cast<const int4_t*>(kbase + off));
-        f.v[i] = __builtin_nontemporal_load(reinterpret_cast<const int4_t*>(vbase + off));
-      }
+    for (int i = 0; i < 4; ++i) {
+      f.k[i] = tile_load(kr, lo + 1024 * i);
+      f.v[i] = tile_load(vr, lo + 1024 * i);
     }
   };
 
   // Process one tile held in registers: stage it in LDS buffer `buf`, refill
   // the fragment with the tile two steps ahead, then q.K, softmax and P.V.
-  auto process = [&](auto bufc, Frag& fr, bool& have) {
+  auto process = [&](auto bufc, Frag& fr) {
     constexpr int kBuf = decltype(bufc)::value;
     uint8_t* kt = smem[wave][kBuf];
     uint8_t* vt = kt + kTileBytes;
@@ -448,8 +455,7 @@ decode_f16_mfma(const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc
       *reinterpret_cast<int4_t*>(vt + off) = fr.v[i];
     }
     const int32_t nvalid = fr.nvalid;
-    have = tw.more();
-    if (have) issue(fr);
+    issue(fr);
     // LDS writes above and reads below touch the same array: they stay in
     // program order, and LDS executes one wavefront's accesses in order.
     // q.K: A = K row lc, logical chunk lg + 4kk
@@ -485,16 +491,19 @@ decode_f16_mfma(const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc
     }
   };
 
+  // Pairs of tiles, then an odd last one: the loop has no exit between its
+  // two halves (an exit there gives the compiler a path to the loop head that
+  // skips the second refill, and its waits at the head then drain both
+  // fragments in flight).
   Frag f0, f1;
-  bool h0 = tw.more();
-  if (h0) issue(f0);
-  bool h1 = tw.more();
-  if (h1) issue(f1);
-  while (h0) {
-    process(std::integral_constant<int, 0>{}, f0, h0);
-    if (!h1) break;
-    process(std::integral_constant<int, 1>{}, f1, h1);
+  const int32_t n_mine = tw.count();
+  issue(f0);
+  issue(f1);
+  for (int32_t t = 0; t + 1 < n_mine; t += 2) {
+    process(std::integral_constant<int, 0>{}, f0);
+    process(std::integral_constant<int, 1>{}, f1);
   }
+  if (n_mine & 1) process(std::integral_constant<int, 0>{}, f0);
   finish_mfma<G>(m_run, l_run, O, reinterpret_cast<float*>(&smem[0][0][0]), ws_m, ws_l, ws_o,
                  int64_t(b) * H + g * G, n_split, split);
 }
@@ -624,7 +633,8 @@ decode_i8_mfma(const int8_t* __restrict__ kc, const int8_t* __restrict__ vc,
     }
     coef = hv ? qs * scale2 : 0.0f;
   }
-  const int32_t L = min(max(L_raw, 0), max_len);
+  // wave-uniform (scalar): the walk and its branches stay scalar
+  const int32_t L = __builtin_amdgcn_readfirstlane(min(max(L_raw, 0), max_len));
   TileWalk tw;
   if constexpr (SELR > 0)
     tw = fused_walk<T, SELR>(fs, max_sel, bg, b, L, L_raw, block, split, units_per_split);
@@ -648,41 +658,35 @@ decode_i8_mfma(const int8_t* __restrict__ kc, const int8_t* __restrict__ vc,
   const float* sbase = (lane < 32 ? ksb : vsb) + lane % 32;
   struct Frag { int4_t k[4], v[4]; float sc; int32_t r0, nvalid; };
   // lane loads row 8 i + lane / 8 (i = 0..3) of the tile, 16-byte chunk
-  // lane % 8 (byte 1024 i + 16 lane of the tile); lanes < 32 load the K scale
-  // of token lane, the others the V scale of token lane - 32.  A partial tile
-  // clamps its rows to the last valid token, so the scales it reads are
-  // finite (their weights are zero).  (Plain global loads: on the short
-  // selected-block walks the buffer form of the f16 kernel measured slower.)
+  // lane % 8 (byte 1024 i + 16 lane of the tile), through the tile's buffer
+  // resource whose record count is the valid bytes: rows past the row's
+  // length, and every row once the walk is over, read as zeros without
+  // touching memory.  Lanes < 32 load the K scale of token lane, the others
+  // the V scale of token lane - 32, clamped to the last valid token (finite;
+  // the weights of those rows are zero).  One load sequence for every case,
+  // no branch.
   auto issue = [&](Frag& f) {
-    int32_t r0, nv;
-    tw.next<T>(r0, nv);
+    int32_t r0 = 0, nv = 0;
+    if (tw.more()) tw.next<T>(r0, nv);
     f.r0 = r0;
     f.nvalid = nv;
-    if (nv == T) {
+    static_assert(T * kRowBytesI8 == kTileRsrcBytes, "one buffer resource per tile");
+    const uint32_t lo = 16u * uint32_t(lane);
+    const int bytes = __builtin_amdgcn_readfirstlane(max(nv, 0) * kRowBytesI8);
+    const auto kr = tile_rsrc(kbase + int64_t(r0) * kRowBytesI8, bytes);
+    const auto vr = tile_rsrc(vbase + int64_t(r0) * kRowBytesI8, bytes);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int32_t row = r0 + 8 * i + lane / 8;
-        const int64_t off = int64_t(row) * kRowBytesI8 + 16 * (lane % 8);
-        f.k[i] = __builtin_nontemporal_load(reinterpret_cast<const int4_t*>(kbase + off));
-        f.v[i] = __builtin_nontemporal_load(reinterpret_cast<const int4_t*>(vbase + off));
-      }
-      f.sc = sbase[r0];
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int32_t row = min(r0 + 8 * i + lane / 8, last);
-        const int64_t off = int64_t(row) * kRowBytesI8 + 16 * (lane % 8);
-        f.k[i] = __builtin_nontemporal_load(reinterpret_cast<const int4_t*>(kbase + off));
-        f.v[i] = __builtin_nontemporal_load(reinterpret_cast<const int4_t*>(vbase + off));
-      }
-      f.sc = sbase[min(r0 + lane % 32, last) - lane % 32];
+    for (int i = 0; i < 4; ++i) {
+      f.k[i] = tile_load(kr, lo + 1024 * i);
+      f.v[i] = tile_load(vr, lo + 1024 * i);
     }
+    f.sc = sbase[min(r0 + lane % 32, last) - lane % 32];
   };
   auto sw = [](int row, int chunk) { return row * kRowBytesI8 + 16 * (chunk ^ (row & 7)); };
   constexpr int kExpUnset = -100000;       // no nonzero V scale seen yet
   int e_run = kExpUnset;
 
-  auto process = [&](auto bufc, Frag& fr, bool& have) {
+  auto process = [&](auto bufc, Frag& fr) {
     constexpr int kBuf = decltype(bufc)::value;
     uint8_t* kt = smem[wave][kBuf];
     uint8_t* vt = kt + kTileBytes;
@@ -695,22 +699,11 @@ decode_i8_mfma(const int8_t* __restrict__ kc, const int8_t* __restrict__ vc,
     }
     const float scl = fr.sc;
     const int32_t nvalid = fr.nvalid, r0 = fr.r0;
-    have = tw.more();
-    if (have) issue(fr);
-    // q.K, exact: two 16-token halves, 128 channels as two k = 64 steps
-    int4_t acc[2];
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      acc[s] = int4_t{0, 0, 0, 0};
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const int4_t a = *reinterpret_cast<const int4_t*>(kt + sw(16 * s + lc, lg + 4 * kk));
-        acc[s] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, qb[kk], acc[s], 0, 0, 0);
-      }
-    }
-    // V-scale unit (while the matrix cores run): 2^e_run >= every V scale
-    // seen so far; a power of two, so the V scales stored in units of it and
-    // the change of unit of O when it grows are exact
+    // V-scale unit: 2^e_run >= every V scale seen so far; a power of two, so
+    // the V scales stored in units of it and the change of unit of O when it
+    // grows are exact.  Done before the refill, so the fragment's scale
+    // register is free when the refill's scale lands in it (a copy of a
+    // register still being loaded would make the wave wait for every load).
     const int32_t vbits =
         __builtin_amdgcn_readfirstlane(__float_as_int(wave_max(lane >= 32 ? scl : 0.0f)));
     float unit = 1.0f;
@@ -726,6 +719,18 @@ decode_i8_mfma(const int8_t* __restrict__ kc, const int8_t* __restrict__ vc,
     }
     const int e_use = e_run == kExpUnset ? 0 : e_run;
     st[lane] = lane >= 32 ? ldexpf(scl, -e_use) : scl;
+    issue(fr);
+    // q.K, exact: two 16-token halves, 128 channels as two k = 64 steps
+    int4_t acc[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      acc[s] = int4_t{0, 0, 0, 0};
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const int4_t a = *reinterpret_cast<const int4_t*>(kt + sw(16 * s + lc, lg + 4 * kk));
+        acc[s] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, qb[kk], acc[s], 0, 0, 0);
+      }
+    }
     const float4 ks0 = *reinterpret_cast<const float4*>(st + 4 * lg);
     const float4 ks1 = *reinterpret_cast<const float4*>(st + 16 + 4 * lg);
     const float4 vs0 = *reinterpret_cast<const float4*>(st + 32 + 4 * lg);
@@ -773,16 +778,19 @@ decode_i8_mfma(const int8_t* __restrict__ kc, const int8_t* __restrict__ vc,
     }
   };
 
+  // Pairs of tiles, then an odd last one: the loop has no exit between its
+  // two halves (an exit there gives the compiler a path to the loop head that
+  // skips the second refill, and its waits at the head then drain both
+  // fragments in flight).
   Frag f0, f1;
-  bool h0 = tw.more();
-  if (h0) issue(f0);
-  bool h1 = tw.more();
-  if (h1) issue(f1);
-  while (h0) {
-    process(std::integral_constant<int, 0>{}, f0, h0);
-    if (!h1) break;
-    process(std::integral_constant<int, 1>{}, f1, h1);
+  const int32_t n_mine = tw.count();
+  issue(f0);
+  issue(f1);
+  for (int32_t t = 0; t + 1 < n_mine; t += 2) {
+    process(std::integral_constant<int, 0>{}, f0);
+    process(std::integral_constant<int, 1>{}, f1);
   }
+  if (n_mine & 1) process(std::integral_constant<int, 0>{}, f0);
   if (e_run != kExpUnset) {
 #pragma unroll
     for (int n = 0; n < 8; ++n) {
