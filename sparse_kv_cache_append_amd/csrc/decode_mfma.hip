@@ -264,9 +264,21 @@ __device__ __forceinline__ TileWalk fused_walk(const FusedSelect& fs, int32_t ma
 
 // Softmax bookkeeping of one tile for the 16 MFMA columns (heads): lane l
 // owns head l%16 and rows 4*(l/16) + r of the tile.  s[r] are base-2 logits
-// (-inf for masked rows); returns the weights p[r] and rescales O (by the
-// running-max correction times o_extra, a caller's exact power of two).
-template <int G, int NT>
+// (-inf for masked rows); returns the weights p[r] and rescales O when the
+// reference moves (by the change of reference times o_extra, a caller's exact
+// power of two).
+//
+// With LAZY, the reference m_run is a lazy maximum: it moves to a tile's
+// maximum only when that exceeds it by more than kLazySlack (base 2), so the
+// weights stay below 2^kLazySlack (finite in fp32, and the f16 high + low
+// split of P keeps its relative precision at any magnitude) while the
+// accumulators are rescaled only on the few tiles that move it; O and l stay
+// relative to the same m_run, which is all the merge and the combine need.
+// (The int8 kernel, whose tiles carry more vector work, gains from skipping
+// the rescale: 262K dense 53.6 -> 51.9 us; the f16 kernel does not, and keeps
+// the exact running maximum.)
+constexpr float kLazySlack = 8.0f;
+template <int G, int NT, bool LAZY>
 __device__ __forceinline__ void tile_softmax(float (&s)[4 * NT], float& m_run, float& l_run,
                                              float4_t (&O)[8], float o_extra = 1.0f) {
   const int lane = threadIdx.x % kWave;
@@ -274,12 +286,13 @@ __device__ __forceinline__ void tile_softmax(float (&s)[4 * NT], float& m_run, f
 #pragma unroll
   for (int i = 1; i < 4 * NT; ++i) mx = fmaxf(mx, s[i]);
   mx = rows_max(mx);
-  const float m_new = fmaxf(m_run, mx);
-  // exp2(-inf) = 0 covers masked logits and a first live tile (m_run = -inf);
-  // a head with nothing live yet keeps factor 1 and weights exp2(-inf - 0) = 0
-  const bool live = m_new != -INFINITY;
-  const float m_use = live ? m_new : 0.0f;
-  const float cr = live ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+  // -inf + slack = -inf: the first live tile of a head moves its reference
+  const bool bump = LAZY ? mx > m_run + kLazySlack : mx > m_run;
+  const float m_ref = bump ? mx : m_run;
+  // exp2(-inf) = 0 covers masked logits; a head with nothing live yet keeps
+  // factor 1 and weights exp2(-inf - 0) = 0
+  const bool live = m_ref != -INFINITY;
+  const float m_use = live ? m_ref : 0.0f;
   float ps = 0.0f;
 #pragma unroll
   for (int i = 0; i < 4 * NT; ++i) {
@@ -287,23 +300,30 @@ __device__ __forceinline__ void tile_softmax(float (&s)[4 * NT], float& m_run, f
     ps += s[i];
   }
   ps = rows_sum(ps);
-  l_run = l_run * cr + ps;
-  m_run = m_new;
-  // O rows are heads 4*(lane/16) + r; head h's factor is in lane h (column
-  // h of every row holds it).  Only heads < G matter: rows past them hold
-  // padding and may take any finite factor.
-  const bool upper = G > 4 && lane >= 16;
+  // heads past G are padding
+  const bool moved = !LAZY || __ballot(bump && (lane % 16) < G) != 0;
+  if (moved || o_extra != 1.0f) {
+    const float cr = live ? __builtin_amdgcn_exp2f(m_run - m_ref) : 1.0f;
+    l_run = l_run * cr + ps;
+    // O rows are heads 4*(lane/16) + r; head h's factor is in lane h (column
+    // h of every row holds it).  Only heads < G matter: rows past them hold
+    // padding and may take any finite factor.
+    const bool upper = G > 4 && lane >= 16;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cr), r));
-    if (G > 4) {
-      const float c4 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cr), 4 + r));
-      c = upper ? c4 : c;
+    for (int r = 0; r < 4; ++r) {
+      float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cr), r));
+      if (G > 4) {
+        const float c4 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cr), 4 + r));
+        c = upper ? c4 : c;
+      }
+      c *= o_extra;
+#pragma unroll
+      for (int n = 0; n < 8; ++n) O[n][r] *= c;
     }
-    c *= o_extra;
-#pragma unroll
-    for (int n = 0; n < 8; ++n) O[n][r] *= c;
+  } else {
+    l_run += ps;
   }
+  m_run = m_ref;
 }
 
 __device__ __forceinline__ void split_hi_lo4(const float* p, half4_t& hi, half4_t& lo) {
@@ -474,7 +494,7 @@ decode_f16_mfma(const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc
 #pragma unroll
       for (int r = 0; r < 4; ++r) sc[r] = (4 * lg + r < nvalid) ? sc[r] : -INFINITY;
     }
-    tile_softmax<G, 1>(sc, m_run, l_run, O);
+    tile_softmax<G, 1, false>(sc, m_run, l_run, O);
     half4_t phi, plo;
     split_hi_lo4(sc, phi, plo);
     // P.V: B = V^T rows 4lg..4lg+3 via the transposing read; 16 channels per n
@@ -754,7 +774,7 @@ decode_i8_mfma(const int8_t* __restrict__ kc, const int8_t* __restrict__ vc,
     }
     // O is kept in units of 2^e_run; the exact change of unit when e_run
     // grows rides on the softmax rescale of O
-    tile_softmax<G, 2>(sc, m_run, l_run, O, unit);
+    tile_softmax<G, 2, true>(sc, m_run, l_run, O, unit);
     // P' = p * v_scale * 2^-e_run (the stored V scales are in that unit)
     float pw[8];
 #pragma unroll
