@@ -544,8 +544,9 @@ decode_f16_mfma(const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc
 // (1152 + c is exact in f16, minus 1152).
 //
 // The V scales are folded into the weights: P' = p * v_scale * 2^-e with
-// 2^e the largest V scale seen so far rounded up to a power of two, so
-// P' <= 1 keeps full f16 (high + low) precision whatever the scale's
+// 2^e the largest V scale seen so far rounded up to a power of two, so P'
+// stays below the softmax's weight bound (2^8 with its lazy reference) and
+// the f16 high + low split keeps its precision whatever the scale's
 // magnitude; the accumulator holds O * 2^-e, is rescaled (exactly, by a power
 // of two) in the rare tile where e grows, and is scaled back at the end.
 __device__ __forceinline__ half8_t widen_codes(int2_t w) {
