@@ -598,16 +598,12 @@ decode_i8_mfma(const int8_t* __restrict__ kc, const int8_t* __restrict__ vc,
   ListSeed ls{};
   if constexpr (SELR == 0) ls = list_seed(sel_idx, sel_cnt, max_sel, bg, split, units_per_split);
 
-  // Query codes as the B operand of q.K (column = head lc, k-chunk lg): the
-  // head's absmax scale over all 128 channels (the 4 lanes of a column hold
-  // 32 channels each), then the codes of channels 64 kk + 16 lg + 0..15.
-  int4_t qb[2];
-  float coef;
+  // the query (float32), requested at entry with the row length and list;
+  // its codes are computed once the first tiles are in flight
+  const bool hv = lc < G;
+  float x[2][16];
   {
-    const bool hv = lc < G;
     const float* qp = q + (int64_t(b) * H + g * G + (hv ? lc : 0)) * kD;
-    float x[2][16];
-    float a = 0.0f;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
@@ -615,45 +611,11 @@ decode_i8_mfma(const int8_t* __restrict__ kc, const int8_t* __restrict__ vc,
         const float4 v4 = *reinterpret_cast<const float4*>(qp + 64 * kk + 16 * lg + 4 * i);
         x[kk][4 * i + 0] = v4.x; x[kk][4 * i + 1] = v4.y;
         x[kk][4 * i + 2] = v4.z; x[kk][4 * i + 3] = v4.w;
-        a = fmaxf(a, fmaxf(fmaxf(fabsf(v4.x), fabsf(v4.y)), fmaxf(fabsf(v4.z), fabsf(v4.w))));
       }
     }
-    a = rows_max(a);
-    const float qs = absmax_scale(a);
-    // codes through the reciprocal; the rare value near a rounding boundary
-    // (flagged per lane) is redone with the exact quotient
-    const float inv = 1.0f / qs;
-    int c[2][16];
-    uint32_t redo = 0u;
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        bool ex;
-        c[kk][i] = quant_code_recip(x[kk][i], inv, ex);
-        redo |= uint32_t(ex) << (16 * kk + i);
-      }
-    }
-    if (__builtin_amdgcn_ballot_w64(redo != 0u) != 0u) {
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if ((redo >> (16 * kk + i)) & 1u) c[kk][i] = quant_code(x[kk][i], qs);
-      }
-    }
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        uint32_t packed = 0u;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) packed |= (uint32_t(c[kk][4 * w + e]) & 0xFFu) << (8 * e);
-        qb[kk][w] = hv ? int32_t(packed) : 0;
-      }
-    }
-    coef = hv ? qs * scale2 : 0.0f;
   }
+  int4_t qb[2];
+  float coef;
   // wave-uniform (scalar): the walk and its branches stay scalar
   const int32_t L = __builtin_amdgcn_readfirstlane(min(max(L_raw, 0), max_len));
   TileWalk tw;
@@ -807,6 +769,54 @@ decode_i8_mfma(const int8_t* __restrict__ kc, const int8_t* __restrict__ vc,
   const int32_t n_mine = tw.count();
   issue(f0);
   issue(f1);
+  // Query codes as the B operand of q.K (column = head lc, k-chunk lg): the
+  // head's absmax scale over all 128 channels (the 4 lanes of a column hold
+  // 32 channels each), then the codes of channels 64 kk + 16 lg + 0..15.
+  // (After the first two refills: this is a few hundred vector instructions
+  // that would otherwise delay every wavefront's first tile loads.)
+  {
+    float a = 0.0f;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) a = fmaxf(a, fabsf(x[kk][i]));
+    }
+    a = rows_max(a);
+    const float qs = absmax_scale(a);
+    // codes through the reciprocal; the rare value near a rounding boundary
+    // (flagged per lane) is redone with the exact quotient
+    const float inv = 1.0f / qs;
+    int c[2][16];
+    uint32_t redo = 0u;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        bool ex;
+        c[kk][i] = quant_code_recip(x[kk][i], inv, ex);
+        redo |= uint32_t(ex) << (16 * kk + i);
+      }
+    }
+    if (__builtin_amdgcn_ballot_w64(redo != 0u) != 0u) {
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if ((redo >> (16 * kk + i)) & 1u) c[kk][i] = quant_code(x[kk][i], qs);
+      }
+    }
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        uint32_t packed = 0u;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) packed |= (uint32_t(c[kk][4 * w + e]) & 0xFFu) << (8 * e);
+        qb[kk][w] = hv ? int32_t(packed) : 0;
+      }
+    }
+    coef = hv ? qs * scale2 : 0.0f;
+  }
   for (int32_t t = 0; t + 1 < n_mine; t += 2) {
     process(std::integral_constant<int, 0>{}, f0);
     process(std::integral_constant<int, 1>{}, f1);
