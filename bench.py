@@ -86,11 +86,16 @@ KERNEL_SOURCES = [os.path.join(ROOT, "sparse_kv_cache_append_amd", "csrc", f)
 
 
 def kernel_source_digest() -> str:
-    """sha256 over the sources the decode kernel is compiled from."""
+    """sha256 over the code of the sources the decode kernel is compiled from
+    (comments and whitespace removed, so an edit to a comment keeps it)."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        h.update(open(f, "rb").read())
+        text = open(f, encoding="utf-8").read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        h.update(re.sub(r"\s+", "", text).encode())
     return h.hexdigest()
 
 

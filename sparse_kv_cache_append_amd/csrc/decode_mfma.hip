@@ -17,10 +17,12 @@
 //     lanes j/8, 2+j/8, ..., 14+j/8.
 //
 // Data flow per wavefront and tile (f16: 16 tokens, int8: 32 tokens):
-//   global -> registers: coalesced 16-byte loads, 4 rows per instruction
-//     (f16 full tiles: raw-buffer loads off a per-tile resource, no vector
-//     address arithmetic), two tiles in flight per wavefront (each refilled
-//     as soon as it is staged in LDS); nontemporal, since every K/V byte is
+//   global -> registers: coalesced 16-byte loads, 4 rows per instruction,
+//     raw-buffer loads off a per-tile resource (no vector address
+//     arithmetic; its record count is the tile's valid bytes, so rows past
+//     the length read as zeros and every refill is the same branch-free
+//     load sequence), two tiles in flight per wavefront (each refilled as
+//     soon as it is staged in LDS); nontemporal, since every K/V byte is
 //     read once per step (the streaming hint raises the read rate of this
 //     part by about a tenth);
 //   registers -> LDS: row-major tile with the 16-byte chunks of row r XOR-
@@ -30,8 +32,9 @@
 //     part, two MFMAs, ~22-bit query precision; int8: the absmax codes, an
 //     exact int32 product);
 //   softmax: per-head tile max across the 4 lane groups, running max/mass,
-//     one rescale of the accumulators per tile (masks only on a partial
-//     tile; the tile walk is wave-uniform, in scalar registers);
+//     one rescale of the accumulators per tile (int8: only on the tiles that
+//     move its lazy reference maximum; masks only on a partial tile; the
+//     tile walk is wave-uniform, in scalar registers);
 //   P.V: A = P (f16 high + low parts, straight from the q.K output registers),
 //     B = V^T via the transposing LDS read (int8 codes widened to f16, exact).
 #include <type_traits>
