@@ -168,6 +168,30 @@ def test_dense_i8_matches_method_and_contract(gpu_lib, B, H, Hkv, lens):
         assert rel_err(out[b], contract) < contract_bar(meth, contract)
 
 
+# Lengths that give the 4 wavefronts of a single part 0 .. 5 tiles each (f16
+# tiles are 16 tokens, int8 tiles 32), with full and partial last tiles: the
+# tile loop runs pairs and an odd last tile, and a wavefront whose walk ends
+# still issues its two refills (they read zeros).
+WAVE_TILE_LENS = [1, 15, 16, 17, 40, 63, 64, 65, 100, 127, 128, 129, 200, 257, 320, 333]
+
+
+@pytest.mark.parametrize("kv", ["f16", "i8"])
+def test_tiles_per_wave_from_zero_to_five(gpu_lib, kv):
+    _print("tiles per wave", kv)
+    B = len(WAVE_TILE_LENS)
+    w = workloads.gaussian(61 if kv == "f16" else 62, B, 8, 2, 128, WAVE_TILE_LENS, kv)
+    cache = build_cache(w)
+    out, _ = run_dense(cache, w, n_split=1)
+    for b in range(B):
+        if kv == "f16":
+            ref = oracle.attend_f16(w.q[b], w.k[b], w.v[b], w.softmax_scale)
+            assert rel_err(out[b], ref) < F16_TOL, WAVE_TILE_LENS[b]
+        else:
+            kc, ks, vc, vs = quantized_host(w, b)
+            meth = oracle.attend_i8(w.q[b], kc, ks, vc, vs, w.softmax_scale)
+            assert rel_err(out[b], meth) < I8_TOL_METHOD, WAVE_TILE_LENS[b]
+
+
 def _boundary_query(rng, H, D):
     """Query rows whose x / scale sit on and next to half-integers: entry 0
     sets the absmax a (code 127); the others are fl32((k + 1/2) * scale)
