@@ -99,11 +99,16 @@ __global__ void __launch_bounds__(kBoundsThreads)
 bounds_kernel(uint16_t* __restrict__ kmin, uint16_t* __restrict__ kmax,
               const float* __restrict__ q, const int32_t* __restrict__ seq_len,
               float* __restrict__ score, int32_t Hkv, int32_t max_len, int32_t block,
-              int32_t max_blocks, AppendOne ap) {
+              int32_t max_blocks, int32_t tiles, AppendOne ap) {
   static_assert(D == kLanesPerBlock * 8, "one 16-byte load per lane per bound");
   static_assert(G * D / 4 <= kBoundsThreads, "one 16-byte query load per thread");
-  const int32_t g = blockIdx.y, b = blockIdx.z;
-  const int32_t j = int32_t(blockIdx.x) * kBlocksPerWG + int32_t(threadIdx.x) / kLanesPerBlock;
+  // 1-D grid of tiles x Hkv x batch, row by row (XCD-aware slots: a row's
+  // scores are written on the XCD whose L2 its decode parts read them from)
+  const uint32_t slot = xcd_slot(blockIdx.x, gridDim.x);
+  const int32_t tile = int32_t(slot % uint32_t(tiles));
+  const int32_t g = int32_t((slot / uint32_t(tiles)) % uint32_t(Hkv));
+  const int32_t b = int32_t(slot / uint32_t(tiles) / uint32_t(Hkv));
+  const int32_t j = tile * kBlocksPerWG + int32_t(threadIdx.x) / kLanesPerBlock;
   const int32_t c = threadIdx.x % kLanesPerBlock;  // channels 8c .. 8c+7
   // Requests issued before anything waits (one round trip): the row length
   // (and append position), the group's G query rows (G * 512 B, one 16-byte
@@ -133,12 +138,12 @@ bounds_kernel(uint16_t* __restrict__ kmin, uint16_t* __restrict__ kmax,
     if (p0 >= 0 && p0 < ap.max_seq) {
       jn = p0 / block;
       fresh = (p0 % block) == 0;
-      if (blockIdx.x == 0) append_one<D, MODE>(ap, kmin, kmax, b, g, Hkv, p0, jn, fresh, max_blocks);
+      if (tile == 0) append_one<D, MODE>(ap, kmin, kmax, b, g, Hkv, p0, jn, fresh, max_blocks);
     }
   }
   const int32_t L = min(max(L_raw, 0), max_len);
   const int32_t nb = (L + block - 1) / block;
-  if (int32_t(blockIdx.x) * kBlocksPerWG >= nb) return;   // whole tile past the end
+  if (tile * kBlocksPerWG >= nb) return;   // whole tile past the end
 
   __shared__ __attribute__((aligned(16))) float qs[G * D];
   if (threadIdx.x < G * D / 4) reinterpret_cast<float4*>(qs)[threadIdx.x] = qreg;
@@ -200,16 +205,20 @@ bounds_kernel(uint16_t* __restrict__ kmin, uint16_t* __restrict__ kmax,
 }
 
 template <int G, int MODE>
-void launch_bounds_g(const skv_cache& c, const float* q, const int32_t* seq_len,
-                     int32_t max_len, float* score, const AppendOne& ap, hipStream_t stream) {
+hipError_t launch_bounds_g(const skv_cache& c, const float* q, const int32_t* seq_len,
+                           int32_t max_len, float* score, const AppendOne& ap,
+                           hipStream_t stream) {
   const int32_t max_blocks = (c.max_seq + c.block - 1) / c.block;
   const int32_t nb_max = (max_len + c.block - 1) / c.block;
   int32_t tiles = (nb_max + kBlocksPerWG - 1) / kBlocksPerWG;
   if (MODE != kNoAppend && tiles == 0) tiles = 1;           // the append still runs
-  if (tiles == 0) return;
-  dim3 grid(tiles, c.n_kv_heads, c.batch);
+  if (tiles == 0) return hipSuccess;
+  const int64_t n_wg = int64_t(tiles) * c.n_kv_heads * c.batch;
+  if (n_wg > 0x7fffffff) return hipErrorInvalidValue;
+  const dim3 grid(static_cast<uint32_t>(n_wg));
   bounds_kernel<128, G, MODE><<<grid, kBoundsThreads, 0, stream>>>(
-      c.kmin, c.kmax, q, seq_len, score, c.n_kv_heads, max_len, c.block, max_blocks, ap);
+      c.kmin, c.kmax, q, seq_len, score, c.n_kv_heads, max_len, c.block, max_blocks, tiles, ap);
+  return hipGetLastError();
 }
 
 template <int MODE>
@@ -217,13 +226,12 @@ hipError_t launch_bounds_m(const skv_cache& c, const float* q, int32_t n_heads,
                            const int32_t* seq_len, int32_t max_len, float* score,
                            const AppendOne& ap, hipStream_t stream) {
   switch (n_heads / c.n_kv_heads) {
-    case 1: launch_bounds_g<1, MODE>(c, q, seq_len, max_len, score, ap, stream); break;
-    case 2: launch_bounds_g<2, MODE>(c, q, seq_len, max_len, score, ap, stream); break;
-    case 4: launch_bounds_g<4, MODE>(c, q, seq_len, max_len, score, ap, stream); break;
-    case 8: launch_bounds_g<8, MODE>(c, q, seq_len, max_len, score, ap, stream); break;
+    case 1: return launch_bounds_g<1, MODE>(c, q, seq_len, max_len, score, ap, stream);
+    case 2: return launch_bounds_g<2, MODE>(c, q, seq_len, max_len, score, ap, stream);
+    case 4: return launch_bounds_g<4, MODE>(c, q, seq_len, max_len, score, ap, stream);
+    case 8: return launch_bounds_g<8, MODE>(c, q, seq_len, max_len, score, ap, stream);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 }  // namespace

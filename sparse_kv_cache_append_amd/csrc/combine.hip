@@ -49,7 +49,7 @@ combine_kernel(const float* __restrict__ ws_m, const float* __restrict__ ws_l,
                const float* __restrict__ ws_o, int32_t n_split, int32_t D,
                float* __restrict__ out) {
   constexpr int HB = kCombineHalf;
-  const int64_t head = blockIdx.x;
+  const int64_t head = xcd_slot(blockIdx.x, gridDim.x);   // heads row by row per XCD
   const int lane = threadIdx.x % kWave, half = lane / 32;
   const int wave = threadIdx.x / kWave, W = blockDim.x / kWave;
   const int d4 = 4 * (lane % 32) + 128 * blockIdx.y;   // first of this lane's 4 channels

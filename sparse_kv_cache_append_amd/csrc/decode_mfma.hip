@@ -396,7 +396,11 @@ decode_f16_mfma(const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc
   constexpr int T = 16;
   constexpr int kTileBytes = T * kRowBytesF16;              // 4096
   __shared__ __attribute__((aligned(16))) uint8_t smem[kMWaves][2][2 * kTileBytes];
-  const int32_t split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  // 1-D grid of n_split x Hkv x batch parts, row by row (XCD-aware slots)
+  const uint32_t slot = xcd_slot(blockIdx.x, gridDim.x);
+  const int32_t split = int32_t(slot % uint32_t(n_split));
+  const int32_t g = int32_t((slot / uint32_t(n_split)) % uint32_t(Hkv));
+  const int32_t b = int32_t(slot / uint32_t(n_split) / uint32_t(Hkv));
   const int lane = threadIdx.x % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lg = lane / 16, lc = lane % 16;
@@ -590,7 +594,11 @@ decode_i8_mfma(const int8_t* __restrict__ kc, const int8_t* __restrict__ vc,
   constexpr int kScaleOff = 2 * kTileBytes;                 // 32 K scales, 32 V scales
   constexpr int kBufBytes = 2 * kTileBytes + 2 * T * 4;
   __shared__ __attribute__((aligned(16))) uint8_t smem[kMWaves][2][kBufBytes];
-  const int32_t split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  // 1-D grid of n_split x Hkv x batch parts, row by row (XCD-aware slots)
+  const uint32_t slot = xcd_slot(blockIdx.x, gridDim.x);
+  const int32_t split = int32_t(slot % uint32_t(n_split));
+  const int32_t g = int32_t((slot / uint32_t(n_split)) % uint32_t(Hkv));
+  const int32_t b = int32_t(slot / uint32_t(n_split) / uint32_t(Hkv));
   const int lane = threadIdx.x % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lg = lane / 16, lc = lane % 16;
@@ -854,7 +862,9 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
     const int32_t nb_max = (p.max_len + c.block - 1) / c.block;
     ups = (nb_max + S - 1) / S;
   }
-  dim3 grid(S, c.n_kv_heads, B);
+  const int64_t n_wg = int64_t(S) * c.n_kv_heads * B;
+  if (n_wg > 0x7fffffff) return hipErrorInvalidValue;
+  const dim3 grid(static_cast<uint32_t>(n_wg));
   const float scale2 = p.softmax_scale * kLog2e;
   const int fr = p.fused_r;
   if (c.kv_dtype == SKV_F16) {

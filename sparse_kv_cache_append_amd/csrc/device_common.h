@@ -12,6 +12,22 @@ namespace skv {
 constexpr int kWave = 64;
 constexpr float kLog2e = 1.4426950408889634f;
 
+// ------------------------------------------------------- XCD-aware placement
+// The dispatcher hands the workgroups of a launch to the 8 XCDs in turn by
+// linear id, and each XCD has its own L2.  xcd_slot renumbers a 1-D grid so
+// that every XCD runs one contiguous range of work items ("slots"): a kernel
+// that lays out its work row by row then keeps each row on one XCD (or on
+// consecutive XCDs for rows larger than a range), the same XCD for every
+// kernel of a step that uses this layout, so a consumer kernel finds its
+// producer's lines (scores, partial states) in its own L2.  A bijection of
+// [0, n) for any n; on a part with another XCD count it is just a
+// permutation.
+constexpr uint32_t kXcds = 8;
+__device__ __forceinline__ uint32_t xcd_slot(uint32_t id, uint32_t n) {
+  const uint32_t x = id % kXcds, k = id / kXcds, q = n / kXcds, rem = n % kXcds;
+  return x * q + min(x, rem) + k;
+}
+
 // ---------------------------------------------------------------- DPP lanes
 // DPP control codes (GFX9 encoding).
 constexpr int kDppQuadXor1 = 0xB1;      // quad_perm [1,0,3,2]
