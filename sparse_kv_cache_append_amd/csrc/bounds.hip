@@ -99,15 +99,15 @@ __global__ void __launch_bounds__(kBoundsThreads)
 bounds_kernel(uint16_t* __restrict__ kmin, uint16_t* __restrict__ kmax,
               const float* __restrict__ q, const int32_t* __restrict__ seq_len,
               float* __restrict__ score, int32_t Hkv, int32_t max_len, int32_t block,
-              int32_t max_blocks, int32_t tiles, AppendOne ap) {
+              int32_t max_blocks, int32_t tiles, int32_t n_rows, AppendOne ap) {
   static_assert(D == kLanesPerBlock * 8, "one 16-byte load per lane per bound");
   static_assert(G * D / 4 <= kBoundsThreads, "one 16-byte query load per thread");
   // 1-D grid of tiles x Hkv x batch, row by row (XCD-aware slots: a row's
   // scores are written on the XCD whose L2 its decode parts read them from)
   const uint32_t slot = xcd_slot(blockIdx.x, gridDim.x);
   const int32_t tile = int32_t(slot % uint32_t(tiles));
-  const int32_t g = int32_t((slot / uint32_t(tiles)) % uint32_t(Hkv));
-  const int32_t b = int32_t(slot / uint32_t(tiles) / uint32_t(Hkv));
+  const uint32_t row = xcd_row(slot / uint32_t(tiles), uint32_t(n_rows));
+  const int32_t g = int32_t(row % uint32_t(Hkv)), b = int32_t(row / uint32_t(Hkv));
   const int32_t j = tile * kBlocksPerWG + int32_t(threadIdx.x) / kLanesPerBlock;
   const int32_t c = threadIdx.x % kLanesPerBlock;  // channels 8c .. 8c+7
   // Requests issued before anything waits (one round trip): the row length
@@ -217,7 +217,8 @@ hipError_t launch_bounds_g(const skv_cache& c, const float* q, const int32_t* se
   if (n_wg > 0x7fffffff) return hipErrorInvalidValue;
   const dim3 grid(static_cast<uint32_t>(n_wg));
   bounds_kernel<128, G, MODE><<<grid, kBoundsThreads, 0, stream>>>(
-      c.kmin, c.kmax, q, seq_len, score, c.n_kv_heads, max_len, c.block, max_blocks, tiles, ap);
+      c.kmin, c.kmax, q, seq_len, score, c.n_kv_heads, max_len, c.block, max_blocks, tiles,
+      c.n_kv_heads * c.batch, ap);
   return hipGetLastError();
 }
 

@@ -390,7 +390,7 @@ decode_f16_mfma(const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc
                 const float* __restrict__ q, const int32_t* __restrict__ seq_len,
                 const int32_t* __restrict__ sel_idx, const int32_t* __restrict__ sel_cnt,
                 int32_t max_sel, int32_t Hkv, int32_t max_seq, int32_t block, int32_t max_len,
-                int32_t n_split, int32_t units_per_split, float qscale2,
+                int32_t n_split, int32_t n_rows, int32_t units_per_split, float qscale2,
                 float* __restrict__ ws_m, float* __restrict__ ws_l, float* __restrict__ ws_o,
                 FusedSelect fs) {
   constexpr int T = 16;
@@ -399,8 +399,8 @@ decode_f16_mfma(const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc
   // 1-D grid of n_split x Hkv x batch parts, row by row (XCD-aware slots)
   const uint32_t slot = xcd_slot(blockIdx.x, gridDim.x);
   const int32_t split = int32_t(slot % uint32_t(n_split));
-  const int32_t g = int32_t((slot / uint32_t(n_split)) % uint32_t(Hkv));
-  const int32_t b = int32_t(slot / uint32_t(n_split) / uint32_t(Hkv));
+  const uint32_t row = xcd_row(slot / uint32_t(n_split), uint32_t(n_rows));
+  const int32_t g = int32_t(row % uint32_t(Hkv)), b = int32_t(row / uint32_t(Hkv));
   const int lane = threadIdx.x % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lg = lane / 16, lc = lane % 16;
@@ -586,7 +586,7 @@ decode_i8_mfma(const int8_t* __restrict__ kc, const int8_t* __restrict__ vc,
                const float* __restrict__ q, const int32_t* __restrict__ seq_len,
                const int32_t* __restrict__ sel_idx, const int32_t* __restrict__ sel_cnt,
                int32_t max_sel, int32_t Hkv, int32_t max_seq, int32_t block, int32_t max_len,
-               int32_t n_split, int32_t units_per_split, float scale2,
+               int32_t n_split, int32_t n_rows, int32_t units_per_split, float scale2,
                float* __restrict__ ws_m, float* __restrict__ ws_l, float* __restrict__ ws_o,
                int32_t* __restrict__ dbg, FusedSelect fs) {
   constexpr int T = 32;
@@ -597,8 +597,8 @@ decode_i8_mfma(const int8_t* __restrict__ kc, const int8_t* __restrict__ vc,
   // 1-D grid of n_split x Hkv x batch parts, row by row (XCD-aware slots)
   const uint32_t slot = xcd_slot(blockIdx.x, gridDim.x);
   const int32_t split = int32_t(slot % uint32_t(n_split));
-  const int32_t g = int32_t((slot / uint32_t(n_split)) % uint32_t(Hkv));
-  const int32_t b = int32_t(slot / uint32_t(n_split) / uint32_t(Hkv));
+  const uint32_t row = xcd_row(slot / uint32_t(n_split), uint32_t(n_rows));
+  const int32_t g = int32_t(row % uint32_t(Hkv)), b = int32_t(row / uint32_t(Hkv));
   const int lane = threadIdx.x % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lg = lane / 16, lc = lane % 16;
@@ -864,6 +864,7 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   }
   const int64_t n_wg = int64_t(S) * c.n_kv_heads * B;
   if (n_wg > 0x7fffffff) return hipErrorInvalidValue;
+  const int32_t n_rows = c.n_kv_heads * B;
   const dim3 grid(static_cast<uint32_t>(n_wg));
   const float scale2 = p.softmax_scale * kLog2e;
   const int fr = p.fused_r;
@@ -871,8 +872,8 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
 #define SKV_LAUNCH_F16(GG, SR)                                                                  \
   decode_f16_mfma<GG, SR><<<grid, kMThreads, 0, stream>>>(                                     \
       static_cast<const uint16_t*>(c.k), static_cast<const uint16_t*>(c.v), p.q, p.seq_len,    \
-      p.sel_idx, p.sel_cnt, p.max_sel, c.n_kv_heads, c.max_seq, c.block, p.max_len, S, ups,    \
-      scale2, ws_m, ws_l, ws_o, p.fsel)
+      p.sel_idx, p.sel_cnt, p.max_sel, c.n_kv_heads, c.max_seq, c.block, p.max_len, S,        \
+      n_rows, ups, scale2, ws_m, ws_l, ws_o, p.fsel)
 #define SKV_F16_G(GG)                                  \
   if (fr == 2) SKV_LAUNCH_F16(GG, 2);                  \
   else if (fr == 4) SKV_LAUNCH_F16(GG, 4);             \
@@ -893,7 +894,7 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   decode_i8_mfma<GG, SR><<<grid, kMThreads, 0, stream>>>(                                      \
       static_cast<const int8_t*>(c.k), static_cast<const int8_t*>(c.v), c.k_scale, c.v_scale,  \
       p.q, p.seq_len, p.sel_idx, p.sel_cnt, p.max_sel, c.n_kv_heads, c.max_seq, c.block,       \
-      p.max_len, S, ups, scale2, ws_m, ws_l, ws_o, p.dbg_logits, p.fsel)
+      p.max_len, S, n_rows, ups, scale2, ws_m, ws_l, ws_o, p.dbg_logits, p.fsel)
 #define SKV_I8_G(GG)                                   \
   if (fr == 2) SKV_LAUNCH_I8(GG, 2);                   \
   else if (fr == 4) SKV_LAUNCH_I8(GG, 4);              \

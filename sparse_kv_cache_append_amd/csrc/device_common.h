@@ -27,6 +27,15 @@ __device__ __forceinline__ uint32_t xcd_slot(uint32_t id, uint32_t n) {
   const uint32_t x = id % kXcds, k = id / kXcds, q = n / kXcds, rem = n % kXcds;
   return x * q + min(x, rem) + k;
 }
+// Row of the r-th row-sized range of slots.  With more rows than XCDs (a
+// multiple of their count), XCD x takes rows x, x + 8, x + 16, ... rather than
+// a run of consecutive rows, so every XCD gets the same KV head of every
+// sequence and sequences of different lengths spread evenly over the XCDs.
+__device__ __forceinline__ uint32_t xcd_row(uint32_t r, uint32_t rows) {
+  if (rows <= kXcds || rows % kXcds != 0) return r;
+  const uint32_t per = rows / kXcds;
+  return (r % per) * kXcds + r / per;
+}
 
 // ---------------------------------------------------------------- DPP lanes
 // DPP control codes (GFX9 encoding).
