@@ -20,6 +20,8 @@ Timing protocol:
   (torch.cuda.CUDAGraph over the library's launches), replayed once
   untimed and once timed between synchronizations; the stream-launch time
   of K eager steps is reported too.
+* Warm cache (secondary, headline steps only): the same K-step graph on one
+  copy of the cache, so a step's bytes may stay in the last-level cache.
 * The dominant kernel (decode_attn) is timed alone the same way (K launches
   in one graph), with HIP events on the replay stream; achieved GB/s =
   algorithmic bytes per launch / average launch time.
@@ -258,6 +260,15 @@ def padded_prefill(w, rows):
     return k, v
 
 
+def _warm_us(torch, args, step):
+    """The same step on one cache copy every time (warm: the step's bytes may
+    stay in the last-level cache between steps), µs per step; a secondary
+    figure beside the cold-ring one."""
+    T1 = Timer(torch, 1, args.steps, args.warmup, not args.no_graph)
+    gr, _ = T1.graph(lambda i: step(0))
+    return (gr if gr is not None else T1.stream(lambda i: step(0))) * 1e6
+
+
 def measure(w, args, quest: bool, dense: bool, detail: bool = False):
     """Time the dense and/or Quest decode step of workload w on a cold ring of
     cache copies.  Returns a dict of per-step figures (and, with detail, the
@@ -314,6 +325,7 @@ def measure(w, args, quest: bool, dense: bool, detail: bool = False):
         st = T.stream(dense_step)
         gr, n = T.graph(dense_step)
         us = (gr if gr is not None else st) * 1e6
+        warm = _warm_us(torch, args, dense_step) if detail else None
         dec_us = T.kernel(lambda i: skv.decode_attn(caches[i % R], q, seq_len, Lmax,
                                                     w.softmax_scale, S_d, ws_d))
         db = step_bytes(w.lens, Hkv, H, D, w.kv_dtype, blk, None)
@@ -326,6 +338,8 @@ def measure(w, args, quest: bool, dense: bool, detail: bool = False):
                         "decode_attn_GBps": round(dec_bytes / dec_us / 1e3, 1),
                         "decode_attn_pct_peak": round(100 * dec_bytes / dec_us / 1e3
                                                       / HBM_PEAK_GBPS, 2)}
+        if warm is not None:
+            res["dense"]["warm_us_per_step"] = round(warm, 3)
 
     if k_sel:
         ks = torch.tensor(k_sel, dtype=torch.int32, device=dev)
@@ -353,6 +367,7 @@ def measure(w, args, quest: bool, dense: bool, detail: bool = False):
         st = T.stream(quest_step)
         gr, n = T.graph(quest_step)
         us = (gr if gr is not None else st) * 1e6
+        warm = _warm_us(torch, args, quest_step) if detail else None
         gr_c, _ = T.graph(quest_calls)
         calls_us = (gr_c if gr_c is not None else T.stream(quest_calls)) * 1e6
         quest_step(0)
@@ -376,6 +391,8 @@ def measure(w, args, quest: bool, dense: bool, detail: bool = False):
                         "decode_attn_GBps": round(dec_bytes / dec_us / 1e3, 1),
                         "decode_attn_pct_peak": round(100 * dec_bytes / dec_us / 1e3
                                                       / HBM_PEAK_GBPS, 2)}
+        if warm is not None:
+            res["quest"]["warm_us_per_step"] = round(warm, 3)
         if detail:
             res["_roofline"] = (dec_bytes, dec_us)
         if "dense" in res:
