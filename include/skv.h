@@ -34,6 +34,11 @@
  *   - Supported in this version: head_dim D = 128; GQA group size
  *     G = H / Hkv in {1, 2, 4, 8}; block a multiple of 16.  Other values that
  *     are otherwise valid return SKV_EUNSUPPORTED.
+ *   - Launch sizes: batch and n_kv_heads up to 65,535, and at most
+ *     2^31 - 1 workgroups per launch (n_split x n_kv_heads x batch for
+ *     decode, max_blocks x n_kv_heads x batch for the cache, n_kv_heads x
+ *     batch for select, batch x n_heads for combine); larger sizes return
+ *     SKV_ERANGE.  (A cache that fits in device memory is far inside these.)
  */
 #ifndef SKV_H
 #define SKV_H

@@ -18,6 +18,12 @@ int32_t blocks_of(int32_t n, int32_t block) {
   return int32_t((int64_t(n) + block - 1) / block);
 }
 
+// Launch grids are 1-D over (part or block tile) x KV head x sequence; the
+// append's grid keeps KV heads and sequences in its y and z dimensions.
+constexpr int64_t kMaxGridX = 0x7fffffff;
+constexpr int32_t kMaxGridYZ = 65535;
+bool grid_fits(int64_t a, int64_t b, int64_t c) { return a * b * c <= kMaxGridX; }
+
 skv_status check_cache(const skv_cache* c, bool need_bounds) {
   if (c == nullptr) return SKV_EINVAL;
   if (c->batch < 1 || c->n_kv_heads < 1 || c->max_seq < 1) return SKV_EINVAL;
@@ -31,6 +37,8 @@ skv_status check_cache(const skv_cache* c, bool need_bounds) {
   // element counts must fit comfortably in int64 address arithmetic
   const double elems = double(c->batch) * c->n_kv_heads * double(c->max_seq) * c->head_dim;
   if (elems > 4.0e18) return SKV_ERANGE;
+  if (c->batch > kMaxGridYZ || c->n_kv_heads > kMaxGridYZ) return SKV_ERANGE;
+  if (!grid_fits(blocks_of(c->max_seq, c->block), c->n_kv_heads, c->batch)) return SKV_ERANGE;
   if (c->head_dim != 128) return SKV_EUNSUPPORTED;
   return SKV_OK;
 }
@@ -107,6 +115,7 @@ skv_status skv_select_topk(const float* score, const int32_t* seq_len, int32_t b
     return SKV_EINVAL;
   if (n_sink < 0 || n_recent < 0 || max_sel < 1) return SKV_EINVAL;
   if (max_blocks > kMaxSelectBlocks) return SKV_EUNSUPPORTED;
+  if (!grid_fits(batch, n_kv_heads, 1)) return SKV_ERANGE;
   return device_status(skv::launch_select(score, seq_len, batch, n_kv_heads, max_blocks, block,
                                           k_sel, n_sink, n_recent, max_sel, sel_idx, sel_cnt,
                                           sel_mask, stream));
@@ -126,6 +135,7 @@ skv_status skv_decode_attn(const skv_cache* c, const float* q, int32_t n_heads,
   if ((sel_idx == nullptr) != (sel_cnt == nullptr)) return SKV_EINVAL;
   if (sel_idx != nullptr && max_sel < 1) return SKV_EINVAL;
   if (n_split < 1 || n_split > kMaxSplit) return SKV_EINVAL;
+  if (!grid_fits(n_split, c->n_kv_heads, c->batch)) return SKV_ERANGE;
   if (!(softmax_scale == softmax_scale) || softmax_scale < 0.0f) return SKV_EINVAL;
   if (dbg_logits != nullptr && c->kv_dtype != SKV_I8) return SKV_EINVAL;
   if (max_len < 0 || max_len > c->max_seq) return SKV_ERANGE;
@@ -173,6 +183,8 @@ skv_status skv_decode_step(const skv_cache* c, const int32_t* pos0, const void* 
     if (max_blocks > kMaxSelectBlocks) return SKV_EUNSUPPORTED;
   }
   if (n_split < 1 || n_split > kMaxSplit) return SKV_EINVAL;
+  if (!grid_fits(n_split, c->n_kv_heads, c->batch)) return SKV_ERANGE;
+  if (!grid_fits(c->batch, n_heads, 1)) return SKV_ERANGE;
   if (!(softmax_scale == softmax_scale) || softmax_scale < 0.0f) return SKV_EINVAL;
   if (max_len < 0 || max_len > c->max_seq) return SKV_ERANGE;
   const size_t need = skv_workspace_bytes(c->batch, n_heads, c->head_dim, n_split);
@@ -224,6 +236,7 @@ skv_status skv_combine(const void* workspace, int32_t batch, int32_t n_heads, in
   if (workspace == nullptr || out == nullptr) return SKV_EINVAL;
   if (batch < 1 || n_heads < 1 || !valid_head_dim(head_dim)) return SKV_EINVAL;
   if (n_split < 1 || n_split > kMaxSplit) return SKV_EINVAL;
+  if (!grid_fits(batch, n_heads, 1)) return SKV_ERANGE;
   return device_status(skv::launch_combine(static_cast<const float*>(workspace), batch, n_heads,
                                            head_dim, n_split, out, stream));
 }

@@ -160,7 +160,9 @@ hipError_t launch_combine(const float* ws, int32_t batch, int32_t n_heads, int32
   const float* ws_m = ws + ws_m_offset(batch, n_heads, n_split);
   const float* ws_l = ws + ws_l_offset(batch, n_heads, n_split);
   const float* ws_o = ws + ws_o_offset(batch, n_heads, n_split);
-  dim3 grid(batch * n_heads, (head_dim + 127) / 128);
+  const int64_t heads = int64_t(batch) * n_heads;
+  if (heads > 0x7fffffff) return hipErrorInvalidValue;
+  dim3 grid(static_cast<uint32_t>(heads), (head_dim + 127) / 128);
   auto aligned = [](const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; };
   const bool vec = aligned(ws_o) && aligned(out) && head_dim % 4 == 0;
   const bool vml = aligned(ws_m) && aligned(ws_l) && n_split % 4 == 0;

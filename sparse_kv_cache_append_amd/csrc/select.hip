@@ -27,7 +27,9 @@ select_kernel(const float* __restrict__ score, const int32_t* __restrict__ seq_l
   __shared__ SelectShared sh;
   __shared__ uint32_t maskw[kMaxSelectBlocks / 32];
 
-  const int32_t g = blockIdx.x, b = blockIdx.y;
+  // 1-D grid of Hkv x batch rows in the XCD order of the decode's parts
+  const uint32_t r = xcd_row(xcd_slot(blockIdx.x, gridDim.x), gridDim.x);
+  const int32_t g = int32_t(r % uint32_t(Hkv)), b = int32_t(r / uint32_t(Hkv));
   const int tid = threadIdx.x;
   const int64_t row = int64_t(b) * Hkv + g;
   // The candidates start at n_sink whenever there are any, so their scores
@@ -92,7 +94,9 @@ hipError_t launch_select(const float* score, const int32_t* seq_len, int32_t bat
                          int32_t max_sel, int32_t* sel_idx, int32_t* sel_cnt,
                          uint32_t* sel_mask, hipStream_t stream) {
   if (max_blocks > kMaxSelectBlocks) return hipErrorInvalidValue;
-  dim3 grid(n_kv_heads, batch);
+  const int64_t rows = int64_t(n_kv_heads) * batch;
+  if (rows > 0x7fffffff) return hipErrorInvalidValue;
+  const dim3 grid(static_cast<uint32_t>(rows));
 #define SKV_LAUNCH_SELECT(RM)                                                                 \
   select_kernel<RM><<<grid, kSelThreads, 0, stream>>>(score, seq_len, n_kv_heads, max_blocks, \
                                                       block, k_sel, n_sink, n_recent, max_sel, \

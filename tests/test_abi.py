@@ -143,3 +143,18 @@ def test_binding_fails_loudly_without_the_library(tmp_path):
             mod.load(str(tmp_path / "nope.so"))
     finally:
         mod._lib = saved
+
+
+def test_grid_size_limits(lib):
+    """Launch grids that would not fit the hardware's grid dimensions are
+    rejected on the host with SKV_ERANGE (1-D grids up to 2^31 - 1
+    workgroups; the append keeps KV heads and sequences in y and z)."""
+    big = desc(batch=65536, n_kv_heads=1, max_seq=64)
+    assert lib.skv_decode_attn(ctypes.byref(big), BAD, 1, BAD, 10, None, None, 0, 0.1, 1,
+                               BAD, 1 << 40, None, None) == skv.SKV_ERANGE
+    wide = desc(batch=65535, n_kv_heads=16, max_seq=64)       # 1,048,560 rows x 4,096 parts
+    assert lib.skv_decode_attn(ctypes.byref(wide), BAD, 16, BAD, 10, None, None, 0, 0.1, 4096,
+                               BAD, 1 << 62, None, None) == skv.SKV_ERANGE
+    assert lib.skv_select_topk(BAD, BAD, 70000, 40000, 16, 64, BAD, 1, 2, 8, BAD, BAD, None,
+                               None) == skv.SKV_ERANGE
+    assert lib.skv_combine(BAD, 70000, 40000, 128, 4, BAD, None) == skv.SKV_ERANGE
