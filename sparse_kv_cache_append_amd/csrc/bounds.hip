@@ -88,6 +88,67 @@ __device__ __forceinline__ void append_one(const AppendOne& ap, uint16_t* __rest
   }
 }
 
+// The append without extra round trips: every lane requested its 8 channels
+// (8c .. 8c + 7) of the new token's K and V rows at entry.  The 16 lanes that
+// hold the token's block (in the workgroup of its tile) merge the new key into
+// that block's bounds, which they read at entry (the side cache as it was),
+// and for f16 write the new rows; for int8, every thread of the row's first
+// workgroup quantizes one value (each 16-lane slot holds the whole row: slots
+// 0..7 take channel 8c + slot of K, slots 8..15 channel 8c + slot - 8 of V,
+// with the row's absmax over the slot, one DPP row).  All of this is register work; the stores come at the end of the
+// kernel, after the scoring, so no wait for the position or for a write
+// stands in front of the bounds.
+template <int MODE>
+__device__ __forceinline__ void merge_new_key(bool fresh, const uint4& kx, const float (&kf)[8],
+                                              uint16_t (&lb)[8], uint16_t (&hb)[8]) {
+  uint16_t nmn[8], nmx[8];
+  if constexpr (MODE == kAppendF16) {
+    const uint32_t w[4] = {kx.x, kx.y, kx.z, kx.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      nmn[2 * i] = nmx[2 * i] = uint16_t(w[i] & 0xFFFFu);
+      nmn[2 * i + 1] = nmx[2 * i + 1] = uint16_t(w[i] >> 16);
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      nmn[e] = f32_to_f16_down(kf[e]);
+      nmx[e] = f32_to_f16_up(kf[e]);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    lb[e] = fresh ? nmn[e] : f16_min_bits(lb[e], nmn[e]);
+    hb[e] = fresh ? nmx[e] : f16_max_bits(hb[e], nmx[e]);
+  }
+}
+
+__device__ __forceinline__ int8_t quant_slot_i8(const float (&kf)[8], const float (&vf)[8],
+                                                float& ks, float& vs) {
+  static_assert(kBlocksPerWG == 16 && kLanesPerBlock * 8 == 128, "16 slots of a 128-value row");
+  float ka = 0.0f, va = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    ka = fmaxf(ka, fabsf(kf[e]));
+    va = fmaxf(va, fabsf(vf[e]));
+  }
+  ks = absmax_scale(group16_max(ka));
+  vs = absmax_scale(group16_max(va));
+  const int slot = int(threadIdx.x) / kLanesPerBlock, e = slot % 8;
+  const bool is_v = slot >= 8;
+  float x = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x = e == i ? (is_v ? vf[i] : kf[i]) : x;
+  return int8_t(quant_code(x, is_v ? vs : ks));
+}
+
+__device__ __forceinline__ uint4 pack_bits(const uint16_t (&h)[8]) {
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) w[i] = uint32_t(h[2 * i]) | (uint32_t(h[2 * i + 1]) << 16);
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
 // MODE != kNoAppend: first append one token per sequence at pos0[b] (the
 // first workgroup of each (sequence, KV head) writes it) and score its block
 // with the merged bounds.  The merge is computed from the new key in
@@ -132,31 +193,25 @@ bounds_kernel(uint16_t* __restrict__ kmin, uint16_t* __restrict__ kmax,
     lo = make_uint4(l4.x, l4.y, l4.z, l4.w);
     hi = make_uint4(h4.x, h4.y, h4.z, h4.w);
   }
-  int32_t jn = -1;
-  bool fresh = false;
-  if constexpr (MODE != kNoAppend) {
-    if (p0 >= 0 && p0 < ap.max_seq) {
-      jn = p0 / block;
-      fresh = (p0 % block) == 0;
-      if (tile == 0) append_one<D, MODE>(ap, kmin, kmax, b, g, Hkv, p0, jn, fresh, max_blocks);
+  // With the append: this lane's 8 channels of the new token's K and V rows,
+  // requested here too (they do not depend on the position).
+  const int64_t src = (int64_t(b) * Hkv + g) * D + c * 8;
+  uint4 kx = make_uint4(0, 0, 0, 0), vx = make_uint4(0, 0, 0, 0);
+  float kf[8], vf[8];
+  if constexpr (MODE == kAppendF16) {
+    kx = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(ap.k_new) + src);
+    vx = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(ap.v_new) + src);
+  } else if constexpr (MODE == kAppendI8) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      kf[e] = static_cast<const float*>(ap.k_new)[src + e];
+      vf[e] = static_cast<const float*>(ap.v_new)[src + e];
     }
   }
-  const int32_t L = min(max(L_raw, 0), max_len);
-  const int32_t nb = (L + block - 1) / block;
-  if (tile * kBlocksPerWG >= nb) return;   // whole tile past the end
-
-  __shared__ __attribute__((aligned(16))) float qs[G * D];
-  if (threadIdx.x < G * D / 4) reinterpret_cast<float4*>(qs)[threadIdx.x] = qreg;
-  const bool live = j < nb;
-  __syncthreads();
-  float qv[G][8];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const float4 a = reinterpret_cast<const float4*>(qs + h * D + c * 8)[0];
-    const float4 bq = reinterpret_cast<const float4*>(qs + h * D + c * 8)[1];
-    qv[h][0] = a.x; qv[h][1] = a.y; qv[h][2] = a.z; qv[h][3] = a.w;
-    qv[h][4] = bq.x; qv[h][5] = bq.y; qv[h][6] = bq.z; qv[h][7] = bq.w;
-  }
+  // keep those requests here, with the others (only the 16 owner lanes use
+  // them, and the compiler would otherwise move them into that branch,
+  // behind the wait for the position)
+  if constexpr (MODE != kNoAppend) asm volatile("" ::: "memory");
   uint16_t lb[8], hb[8];
   {
     const uint32_t lw[4] = {lo.x, lo.y, lo.z, lo.w};
@@ -167,41 +222,83 @@ bounds_kernel(uint16_t* __restrict__ kmin, uint16_t* __restrict__ kmax,
       hb[2 * i] = uint16_t(hw[i] & 0xFFFFu); hb[2 * i + 1] = uint16_t(hw[i] >> 16);
     }
   }
+  bool own = false, own_wg = false;
+  int64_t arow = 0, bo = 0;
+  int8_t code = 0;
+  float ks_new = 0.0f, vs_new = 0.0f;
   if constexpr (MODE != kNoAppend) {
-    if (live && j == jn) {
-      const int64_t src = (int64_t(b) * Hkv + g) * D + c * 8;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        uint16_t nmn, nmx;
-        if constexpr (MODE == kAppendF16) {
-          nmn = nmx = static_cast<const uint16_t*>(ap.k_new)[src + e];
-        } else {
-          const float x = static_cast<const float*>(ap.k_new)[src + e];
-          nmn = f32_to_f16_down(x);
-          nmx = f32_to_f16_up(x);
+    if (p0 >= 0 && p0 < ap.max_seq) {
+      const int32_t jn = p0 / block;
+      const bool fresh = (p0 % block) == 0;
+      arow = (int64_t(b) * Hkv + g) * ap.max_seq + p0;
+      bo = ((int64_t(b) * Hkv + g) * max_blocks + jn) * D + c * 8;
+      if (jn / kBlocksPerWG < tiles) {
+        own = j == jn;
+        if (own) merge_new_key<MODE>(fresh, kx, kf, lb, hb);
+        // int8 rows: by the row's first workgroup (dispatched first, so its
+        // extra arithmetic is hidden behind the later tiles)
+        if constexpr (MODE == kAppendI8) {
+          own_wg = tile == 0;
+          if (own_wg) code = quant_slot_i8(kf, vf, ks_new, vs_new);
         }
-        lb[e] = fresh ? nmn : f16_min_bits(lb[e], nmn);
-        hb[e] = fresh ? nmx : f16_max_bits(hb[e], nmx);
+      } else if (tile == 0) {
+        // the token's block lies past the launched tiles: append it here
+        append_one<D, MODE>(ap, kmin, kmax, b, g, Hkv, p0, jn, fresh, max_blocks);
       }
     }
   }
-  float mn[8], mx[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) { mn[e] = h2f(lb[e]); mx[e] = h2f(hb[e]); }
+  const int32_t L = min(max(L_raw, 0), max_len);
+  const int32_t nb = (L + block - 1) / block;
+  const bool live = j < nb;
   float best = -INFINITY;
+  if (tile * kBlocksPerWG < nb) {          // else the whole tile is past the end
+    __shared__ __attribute__((aligned(16))) float qs[G * D];
+    if (threadIdx.x < G * D / 4) reinterpret_cast<float4*>(qs)[threadIdx.x] = qreg;
+    __syncthreads();
+    float qv[G][8];
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    float acc = 0.0f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float x = qv[h][e];
-      const float kb = x > 0.0f ? mx[e] : mn[e];
-      acc += (x != 0.0f) ? x * kb : 0.0f;
+    for (int h = 0; h < G; ++h) {
+      const float4 a = reinterpret_cast<const float4*>(qs + h * D + c * 8)[0];
+      const float4 bq = reinterpret_cast<const float4*>(qs + h * D + c * 8)[1];
+      qv[h][0] = a.x; qv[h][1] = a.y; qv[h][2] = a.z; qv[h][3] = a.w;
+      qv[h][4] = bq.x; qv[h][5] = bq.y; qv[h][6] = bq.z; qv[h][7] = bq.w;
     }
-    acc = group16_sum(acc);
-    best = fmaxf(best, acc);
+    float mn[8], mx[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) { mn[e] = h2f(lb[e]); mx[e] = h2f(hb[e]); }
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float acc = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = qv[h][e];
+        const float kb = x > 0.0f ? mx[e] : mn[e];
+        acc += (x != 0.0f) ? x * kb : 0.0f;
+      }
+      acc = group16_sum(acc);
+      best = fmaxf(best, acc);
+    }
+    if (live && c == 0) score[(int64_t(b) * Hkv + g) * max_blocks + j] = best;
   }
-  if (live && c == 0) score[(int64_t(b) * Hkv + g) * max_blocks + j] = best;
+  // the append's stores
+  if constexpr (MODE != kNoAppend) {
+    if (own) {
+      *reinterpret_cast<uint4*>(kmin + bo) = pack_bits(lb);
+      *reinterpret_cast<uint4*>(kmax + bo) = pack_bits(hb);
+      if constexpr (MODE == kAppendF16) {
+        reinterpret_cast<uint4*>(static_cast<uint16_t*>(ap.k) + arow * D)[c] = kx;
+        reinterpret_cast<uint4*>(static_cast<uint16_t*>(ap.v) + arow * D)[c] = vx;
+      }
+    }
+    if constexpr (MODE == kAppendI8) {
+      if (own_wg) {
+        const int slot = int(threadIdx.x) / kLanesPerBlock;
+        (static_cast<int8_t*>(slot >= 8 ? ap.v : ap.k) + arow * D)[8 * c + slot % 8] = code;
+        if (threadIdx.x == 0) ap.ks[arow] = ks_new;
+        if (threadIdx.x == 8 * kLanesPerBlock) ap.vs[arow] = vs_new;
+      }
+    }
+  }
 }
 
 template <int G, int MODE>

@@ -63,6 +63,14 @@ __device__ __forceinline__ float group16_sum(float x) {
   x += dpp_f<kDppRowMirror>(x);
   return x;
 }
+// Max over aligned groups of 16 lanes (one DPP row); same bits in every lane.
+__device__ __forceinline__ float group16_max(float x) {
+  x = fmaxf(x, dpp_f<kDppQuadXor1>(x));
+  x = fmaxf(x, dpp_f<kDppQuadXor2>(x));
+  x = fmaxf(x, dpp_f<kDppRowHalfMirror>(x));
+  x = fmaxf(x, dpp_f<kDppRowMirror>(x));
+  return x;
+}
 
 
 // ------------------------------------------------------- across the 4 rows
