@@ -31,6 +31,9 @@
  *     below, and each call documents what it does with out-of-range values.
  *   - Layouts are dense, row-major, with the last dimension contiguous.
  *     f16 means IEEE binary16 bit patterns (uint16_t storage).
+ *   - The cache's k, v, kmin, kmax, the queries q and the new rows k_new,
+ *     v_new are 16-byte aligned, the int8 scales 4-byte aligned (SKV_EINVAL
+ *     otherwise); other buffers need their element's natural alignment.
  *   - Supported in this version: head_dim D = 128; GQA group size
  *     G = H / Hkv in {1, 2, 4, 8}; block a multiple of 16.  Other values that
  *     are otherwise valid return SKV_EUNSUPPORTED.
@@ -235,7 +238,8 @@ skv_status skv_combine(const void* workspace, int32_t batch, int32_t n_heads,
                        int32_t head_dim, int32_t n_split, float* out, hipStream_t stream);
 
 /*
- * skv_decode_step — one whole decode step in three kernel launches.
+ * skv_decode_step — one whole decode step in three kernel launches (Quest)
+ * or two (dense).
  * Defines: the composition of the calls above, in the order the pages run
  * them (cpu-attn kernel card, "Usage": append the token, then decode;
  * sparse_attn.md, "S2/S3 engineering design": fill the side cache, select,
@@ -251,7 +255,10 @@ skv_status skv_combine(const void* workspace, int32_t batch, int32_t n_heads,
  *                     workspace, workspace_bytes, NULL)
  *     skv_combine(workspace, batch, n_heads, head_dim, n_split, out)
  * with max_blocks = skv_max_blocks(c).  The append runs inside the bounds
- * pass (Quest), and the selection inside the attention kernel's prologue
+ * pass (Quest) or inside the attention kernel (dense: the part whose blocks
+ * hold pos0[b] writes the token, and the attention takes the token's row
+ * from k_new, v_new, so the cache row's old contents are never read), and
+ * the selection inside the attention kernel's prologue
  * (each part of a row recomputes it) when max_blocks <= 4096 and
  * ceil(max_sel / n_split) <= 64; otherwise they run as their own kernels.
  *   pos0, k_new, v_new, src_dtype : as skv_kv_append with n_new = 1

@@ -208,7 +208,7 @@ def decode_attn(cache: Cache, q, seq_len, max_len: int, softmax_scale: float, n_
 def decode_step(cache: Cache, q, seq_len, max_len: int, softmax_scale: float, n_split: int,
                 workspace, out, pos0=None, k_new=None, v_new=None, k_sel=None, n_sink: int = 1,
                 n_recent: int = 2, score=None, sel_idx=None, sel_cnt=None, stream=None):
-    """One decode step in three launches (skv_decode_step): optional one-token
+    """One decode step in three launches, two when dense (skv_decode_step): optional one-token
     append (k_new, v_new [batch][1][Hkv][D] at pos0), dense or Quest (k_sel)
     attention, combine into ``out``.  Quest needs score [batch][Hkv][max_blocks]
     scratch and sel_idx [batch][Hkv][max_sel] / sel_cnt [batch][Hkv] outputs."""

@@ -24,6 +24,9 @@ constexpr int64_t kMaxGridX = 0x7fffffff;
 constexpr int32_t kMaxGridYZ = 65535;
 bool grid_fits(int64_t a, int64_t b, int64_t c) { return a * b * c <= kMaxGridX; }
 
+// The kernels move cache rows, bounds, queries and new rows in 16-byte vectors.
+bool aligned(const void* p, uintptr_t a = 16) { return reinterpret_cast<uintptr_t>(p) % a == 0; }
+
 skv_status check_cache(const skv_cache* c, bool need_bounds) {
   if (c == nullptr) return SKV_EINVAL;
   if (c->batch < 1 || c->n_kv_heads < 1 || c->max_seq < 1) return SKV_EINVAL;
@@ -34,6 +37,9 @@ skv_status check_cache(const skv_cache* c, bool need_bounds) {
   if (c->kv_dtype == SKV_I8 && (c->k_scale == nullptr || c->v_scale == nullptr)) return SKV_EINVAL;
   if ((c->kmin == nullptr) != (c->kmax == nullptr)) return SKV_EINVAL;
   if (need_bounds && c->kmin == nullptr) return SKV_EINVAL;
+  if (!aligned(c->k) || !aligned(c->v) || !aligned(c->kmin) || !aligned(c->kmax) ||
+      !aligned(c->k_scale, 4) || !aligned(c->v_scale, 4))
+    return SKV_EINVAL;
   // element counts must fit comfortably in int64 address arithmetic
   const double elems = double(c->batch) * c->n_kv_heads * double(c->max_seq) * c->head_dim;
   if (elems > 4.0e18) return SKV_ERANGE;
@@ -84,6 +90,7 @@ skv_status skv_kv_append(const skv_cache* c, const int32_t* pos0, int32_t n_new,
   skv_status st = check_cache(c, false);
   if (st != SKV_OK) return st;
   if (pos0 == nullptr || k_new == nullptr || v_new == nullptr || n_new < 1) return SKV_EINVAL;
+  if (!aligned(k_new) || !aligned(v_new)) return SKV_EINVAL;
   if (n_new > c->max_seq) return SKV_ERANGE;
   const bool ok = (c->kv_dtype == SKV_F16 && src_dtype == SKV_F16) ||
                   (c->kv_dtype == SKV_I8 && src_dtype == SKV_F32);
@@ -96,7 +103,7 @@ skv_status skv_block_bounds(const skv_cache* c, const float* q, int32_t n_heads,
                             hipStream_t stream) {
   skv_status st = check_cache(c, true);
   if (st != SKV_OK) return st;
-  if (q == nullptr || seq_len == nullptr || score == nullptr) return SKV_EINVAL;
+  if (q == nullptr || seq_len == nullptr || score == nullptr || !aligned(q)) return SKV_EINVAL;
   st = check_heads(c, n_heads);
   if (st != SKV_OK) return st;
   if (max_len < 0 || max_len > c->max_seq) return SKV_ERANGE;
@@ -129,7 +136,7 @@ skv_status skv_decode_attn(const skv_cache* c, const float* q, int32_t n_heads,
                            int32_t* dbg_logits, hipStream_t stream) {
   skv_status st = check_cache(c, false);
   if (st != SKV_OK) return st;
-  if (q == nullptr || seq_len == nullptr) return SKV_EINVAL;
+  if (q == nullptr || seq_len == nullptr || !aligned(q)) return SKV_EINVAL;
   st = check_heads(c, n_heads);
   if (st != SKV_OK) return st;
   if ((sel_idx == nullptr) != (sel_cnt == nullptr)) return SKV_EINVAL;
@@ -167,11 +174,12 @@ skv_status skv_decode_step(const skv_cache* c, const int32_t* pos0, const void* 
   const bool quest = k_sel != nullptr;
   skv_status st = check_cache(c, quest);
   if (st != SKV_OK) return st;
-  if (q == nullptr || seq_len == nullptr || out == nullptr) return SKV_EINVAL;
+  if (q == nullptr || seq_len == nullptr || out == nullptr || !aligned(q)) return SKV_EINVAL;
   st = check_heads(c, n_heads);
   if (st != SKV_OK) return st;
   if (k_new != nullptr) {
-    if (pos0 == nullptr || v_new == nullptr) return SKV_EINVAL;
+    if (pos0 == nullptr || v_new == nullptr || !aligned(k_new) || !aligned(v_new))
+      return SKV_EINVAL;
     const bool ok = (c->kv_dtype == SKV_F16 && src_dtype == SKV_F16) ||
                     (c->kv_dtype == SKV_I8 && src_dtype == SKV_F32);
     if (!ok) return (src_dtype == SKV_F16 || src_dtype == SKV_F32) ? SKV_EUNSUPPORTED : SKV_EINVAL;
@@ -222,8 +230,7 @@ skv_status skv_decode_step(const skv_cache* c, const int32_t* pos0, const void* 
       if (e != hipSuccess) return SKV_EDEVICE;
     }
   } else if (k_new != nullptr) {
-    e = skv::launch_append(*c, pos0, 1, k_new, v_new, stream);
-    if (e != hipSuccess) return SKV_EDEVICE;
+    p.app = skv::FoldedAppend{k_new, v_new, pos0};   // written by the attention kernel
   }
   e = skv::launch_decode(p, stream);
   if (e != hipSuccess) return SKV_EDEVICE;

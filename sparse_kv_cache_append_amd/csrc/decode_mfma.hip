@@ -382,9 +382,77 @@ __device__ __forceinline__ void finish_mfma(float m_run, float l_run, const floa
   }
 }
 
+// The one-token append of a dense step (APP kernels).  Every wavefront reads
+// the new K and V rows (this lane: channels 2 lane, 2 lane + 1) and, when one
+// of its tiles holds position pos0[b], writes them over that row of the tile
+// staged in LDS, so the attention sees exactly what the separate append would
+// have stored there (the cache row itself is stale until this step writes it).
+// The part whose blocks hold pos0[b] (its last part when pos0 lies past them)
+// writes the rows, the int8 scales and the block's merged side-cache bounds,
+// as skv_kv_append does for one token: wavefront 0, after its walk.  The old
+// bounds it merges with are requested before the walk through a buffer
+// resource that has records only in that wavefront and only for a block that
+// keeps earlier tokens.
+struct AppendArgs {
+  void* k;
+  void* v;
+  float* ks;
+  float* vs;
+  uint16_t* kmin;          // nullptr: the cache has no side cache
+  uint16_t* kmax;
+  const void* k_new;
+  const void* v_new;
+  const int32_t* pos0;
+  int32_t max_blocks;
+};
+
+// Who writes the appended token of row (b, g), and the block's old bounds
+// (zeros where not needed).
+struct AppendOwner {
+  bool own, fresh;
+  int32_t jp;
+  uint32_t bmn_old, bmx_old;
+};
+__device__ __forceinline__ AppendOwner append_owner(const AppendArgs& app, int32_t p_new,
+                                                    int64_t bg, int32_t max_seq, int32_t block,
+                                                    int32_t split, int32_t n_split,
+                                                    int32_t units_per_split, int wave) {
+  AppendOwner o;
+  const bool p_ok = p_new >= 0 && p_new < max_seq;
+  o.jp = p_ok ? p_new / block : 0;
+  o.fresh = p_ok && o.jp * block == p_new;
+  o.own = p_ok && wave == 0 && split == min(o.jp / units_per_split, n_split - 1);
+  const int bytes = (o.own && app.kmin != nullptr && !o.fresh) ? kD * 2 : 0;
+  const int64_t bo = (bg * app.max_blocks + o.jp) * kD;
+  const auto rmn = __builtin_amdgcn_make_buffer_rsrc(app.kmin + bo, (short)0, bytes, kRsrcWord3);
+  const auto rmx = __builtin_amdgcn_make_buffer_rsrc(app.kmax + bo, (short)0, bytes, kRsrcWord3);
+  const uint32_t lane = threadIdx.x % kWave;
+  o.bmn_old = __builtin_amdgcn_raw_buffer_load_b32(rmn, 4u * lane, 0, 0);
+  o.bmx_old = __builtin_amdgcn_raw_buffer_load_b32(rmx, 4u * lane, 0, 0);
+  return o;
+}
+
+// Store this lane's two channels of the new key's bounds (lo, hi: the rounded
+// min and max per channel), min/max-merged with the old ones unless the block
+// starts at the new token.
+__device__ __forceinline__ void store_new_bounds(const AppendArgs& app, const AppendOwner& o,
+                                                 int64_t bg, const uint16_t (&mn)[2],
+                                                 const uint16_t (&mx)[2]) {
+  uint16_t a[2] = {mn[0], mn[1]}, c[2] = {mx[0], mx[1]};
+  if (!o.fresh) {
+    a[0] = f16_min_bits(uint16_t(o.bmn_old & 0xFFFFu), a[0]);
+    a[1] = f16_min_bits(uint16_t(o.bmn_old >> 16), a[1]);
+    c[0] = f16_max_bits(uint16_t(o.bmx_old & 0xFFFFu), c[0]);
+    c[1] = f16_max_bits(uint16_t(o.bmx_old >> 16), c[1]);
+  }
+  const int64_t bo = (bg * app.max_blocks + o.jp) * (kD / 2) + threadIdx.x % kWave;
+  reinterpret_cast<uint32_t*>(app.kmin)[bo] = uint32_t(a[0]) | (uint32_t(a[1]) << 16);
+  reinterpret_cast<uint32_t*>(app.kmax)[bo] = uint32_t(c[0]) | (uint32_t(c[1]) << 16);
+}
+
 // ------------------------------------------------------------------ f16
 // Tile = 16 tokens: K and V tiles are 4 KiB each (4 load instructions).
-template <int G, int SELR>
+template <int G, int SELR, bool APP>
 __global__ void __launch_bounds__(kMThreads, 2)
 decode_f16_mfma(const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
                 const float* __restrict__ q, const int32_t* __restrict__ seq_len,
@@ -392,7 +460,7 @@ decode_f16_mfma(const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc
                 int32_t max_sel, int32_t Hkv, int32_t max_seq, int32_t block, int32_t max_len,
                 int32_t n_split, int32_t n_rows, int32_t units_per_split, float qscale2,
                 float* __restrict__ ws_m, float* __restrict__ ws_l, float* __restrict__ ws_o,
-                FusedSelect fs) {
+                FusedSelect fs, AppendArgs app) {
   constexpr int T = 16;
   constexpr int kTileBytes = T * kRowBytesF16;              // 4096
   __shared__ __attribute__((aligned(16))) uint8_t smem[kMWaves][2][2 * kTileBytes];
@@ -410,6 +478,14 @@ decode_f16_mfma(const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc
   const int32_t L_raw = seq_len[b];
   ListSeed ls{};
   if constexpr (SELR == 0) ls = list_seed(sel_idx, sel_cnt, max_sel, bg, split, units_per_split);
+  // folded append: the position and this lane's two channels of the new rows
+  int32_t p_new = -1;
+  uint32_t kx = 0u, vx = 0u;
+  if constexpr (APP) {
+    p_new = app.pos0[b];
+    kx = static_cast<const uint32_t*>(app.k_new)[bg * (kD / 2) + lane];
+    vx = static_cast<const uint32_t*>(app.v_new)[bg * (kD / 2) + lane];
+  }
 
   // query as the B operand of q.K: column = head lc, k-chunk = lg; f16 hi + lo
   half8_t qhi[4], qlo[4];
@@ -445,7 +521,7 @@ decode_f16_mfma(const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc
 
   const uint8_t* kbase = reinterpret_cast<const uint8_t*>(kc + bg * int64_t(max_seq) * kD);
   const uint8_t* vbase = reinterpret_cast<const uint8_t*>(vc + bg * int64_t(max_seq) * kD);
-  struct Frag { int4_t k[4], v[4]; int32_t nvalid; };
+  struct Frag { int4_t k[4], v[4]; int32_t r0, nvalid; };
   // lane loads row 4*i + lane/16 (i = 0..3) of the tile, 16-byte chunk lane%16:
   // byte 1024 i + 16 lane of the tile, through the tile's buffer resource.
   // Its record count is the tile's valid bytes, so the rows of a partial
@@ -455,6 +531,7 @@ decode_f16_mfma(const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc
   auto issue = [&](Frag& f) {
     int32_t r0 = 0, nv = 0;
     if (tw.more()) tw.next<T>(r0, nv);
+    f.r0 = r0;
     f.nvalid = nv;
     static_assert(T * kRowBytesF16 == kTileRsrcBytes, "one buffer resource per tile");
     const uint32_t lo = 16u * uint32_t(lane);
@@ -480,6 +557,17 @@ decode_f16_mfma(const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc
       const int off = row * kRowBytesF16 + 16 * (lc ^ swz(row));
       *reinterpret_cast<int4_t*>(kt + off) = fr.k[i];
       *reinterpret_cast<int4_t*>(vt + off) = fr.v[i];
+    }
+    if constexpr (APP) {
+      // the appended token's row, if this tile holds it (a wave-uniform test;
+      // LDS applies the wavefront's writes in order, so these win)
+      // (nvalid is negative for the tile slots past the row's end)
+      const int32_t prel = p_new - fr.r0;
+      if (prel >= 0 && prel < fr.nvalid) {
+        const int off = prel * kRowBytesF16 + 16 * ((lane >> 2) ^ swz(prel)) + 4 * (lane & 3);
+        *reinterpret_cast<uint32_t*>(kt + off) = kx;
+        *reinterpret_cast<uint32_t*>(vt + off) = vx;
+      }
     }
     const int32_t nvalid = fr.nvalid;
     issue(fr);
@@ -526,6 +614,11 @@ decode_f16_mfma(const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc
   const int32_t n_mine = tw.count();
   issue(f0);
   issue(f1);
+  AppendOwner ao{};
+  if constexpr (APP) {
+    p_new = __builtin_amdgcn_readfirstlane(p_new);
+    ao = append_owner(app, p_new, bg, max_seq, block, split, n_split, units_per_split, wave);
+  }
   for (int32_t t = 0; t + 1 < n_mine; t += 2) {
     process(std::integral_constant<int, 0>{}, f0);
     process(std::integral_constant<int, 1>{}, f1);
@@ -533,6 +626,26 @@ decode_f16_mfma(const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc
   if (n_mine & 1) process(std::integral_constant<int, 0>{}, f0);
   finish_mfma<G>(m_run, l_run, O, reinterpret_cast<float*>(&smem[0][0][0]), ws_m, ws_l, ws_o,
                  int64_t(b) * H + g * G, n_split, split);
+  if constexpr (APP) {
+    if (ao.own) {
+      const int64_t row = (bg * max_seq + p_new) * (kD / 2) + lane;
+      static_cast<uint32_t*>(app.k)[row] = kx;
+      static_cast<uint32_t*>(app.v)[row] = vx;
+      if (app.kmin != nullptr) {
+        // one token's bounds are its own key (a NaN channel keeps +inf / -inf,
+        // as the min/max scan of the append kernel leaves it)
+        uint16_t mn[2], mx[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const uint16_t x = uint16_t(kx >> (16 * e));
+          const float xf = h2f(x);
+          mn[e] = xf < INFINITY ? x : uint16_t(0x7C00u);
+          mx[e] = xf > -INFINITY ? x : uint16_t(0xFC00u);
+        }
+        store_new_bounds(app, ao, bg, mn, mx);
+      }
+    }
+  }
 }
 
 // ------------------------------------------------------------------ int8
@@ -579,7 +692,7 @@ __device__ __forceinline__ half8_t widen_codes(int2_t w) {
   return r;
 }
 
-template <int G, int SELR>
+template <int G, int SELR, bool APP>
 __global__ void __launch_bounds__(kMThreads, 2)
 decode_i8_mfma(const int8_t* __restrict__ kc, const int8_t* __restrict__ vc,
                const float* __restrict__ ksc, const float* __restrict__ vsc,
@@ -588,7 +701,7 @@ decode_i8_mfma(const int8_t* __restrict__ kc, const int8_t* __restrict__ vc,
                int32_t max_sel, int32_t Hkv, int32_t max_seq, int32_t block, int32_t max_len,
                int32_t n_split, int32_t n_rows, int32_t units_per_split, float scale2,
                float* __restrict__ ws_m, float* __restrict__ ws_l, float* __restrict__ ws_o,
-               int32_t* __restrict__ dbg, FusedSelect fs) {
+               int32_t* __restrict__ dbg, FusedSelect fs, AppendArgs app) {
   constexpr int T = 32;
   constexpr int kTileBytes = T * kRowBytesI8;               // 4096
   constexpr int kScaleOff = 2 * kTileBytes;                 // 32 K scales, 32 V scales
@@ -608,6 +721,14 @@ decode_i8_mfma(const int8_t* __restrict__ kc, const int8_t* __restrict__ vc,
   const int32_t L_raw = seq_len[b];
   ListSeed ls{};
   if constexpr (SELR == 0) ls = list_seed(sel_idx, sel_cnt, max_sel, bg, split, units_per_split);
+  // folded append: the position and this lane's two channels of the new rows
+  int32_t p_new = -1;
+  float2 kf = {0.0f, 0.0f}, vf = {0.0f, 0.0f};
+  if constexpr (APP) {
+    p_new = app.pos0[b];
+    kf = static_cast<const float2*>(app.k_new)[bg * (kD / 2) + lane];
+    vf = static_cast<const float2*>(app.v_new)[bg * (kD / 2) + lane];
+  }
 
   // the query (float32), requested at entry with the row length and list;
   // its codes are computed once the first tiles are in flight
@@ -679,6 +800,8 @@ decode_i8_mfma(const int8_t* __restrict__ kc, const int8_t* __restrict__ vc,
   auto sw = [](int row, int chunk) { return row * kRowBytesI8 + 16 * (chunk ^ (row & 7)); };
   constexpr int kExpUnset = -100000;       // no nonzero V scale seen yet
   int e_run = kExpUnset;
+  float ks_new = 0.0f, vs_new = 0.0f;      // the appended token's scales and codes
+  uint32_t kcode = 0u, vcode = 0u;
 
   auto process = [&](auto bufc, Frag& fr) {
     constexpr int kBuf = decltype(bufc)::value;
@@ -691,8 +814,19 @@ decode_i8_mfma(const int8_t* __restrict__ kc, const int8_t* __restrict__ vc,
       *reinterpret_cast<int4_t*>(kt + sw(row, lane % 8)) = fr.k[i];
       *reinterpret_cast<int4_t*>(vt + sw(row, lane % 8)) = fr.v[i];
     }
-    const float scl = fr.sc;
+    float scl = fr.sc;
     const int32_t nvalid = fr.nvalid, r0 = fr.r0;
+    if constexpr (APP) {
+      // the appended token's codes and scales, if this tile holds it (the
+      // scale also where a lane's clamped token is that token)
+      const int32_t prel = p_new - r0;
+      if (prel >= 0 && prel < nvalid) {          // nvalid < 0 past the row's end
+        const int off = sw(prel, lane >> 3) + 2 * (lane & 7);
+        *reinterpret_cast<uint16_t*>(kt + off) = uint16_t(kcode);
+        *reinterpret_cast<uint16_t*>(vt + off) = uint16_t(vcode);
+      }
+      scl = min(r0 + lane % 32, last) == p_new ? (lane < 32 ? ks_new : vs_new) : scl;
+    }
     // V-scale unit: 2^e_run >= every V scale seen so far; a power of two, so
     // the V scales stored in units of it and the change of unit of O when it
     // grows are exact.  Done before the refill, so the fragment's scale
@@ -780,6 +914,20 @@ decode_i8_mfma(const int8_t* __restrict__ kc, const int8_t* __restrict__ vc,
   const int32_t n_mine = tw.count();
   issue(f0);
   issue(f1);
+  AppendOwner ao{};
+  if constexpr (APP) {
+    p_new = __builtin_amdgcn_readfirstlane(p_new);
+    ao = append_owner(app, p_new, bg, max_seq, block, split, n_split, units_per_split, wave);
+    // the new rows quantized as the append kernel does (same reduction order)
+    auto quant2 = [](float2 x, float& scale) {
+      const float a = wave_max(fmaxf(fmaxf(0.0f, fabsf(x.x)), fabsf(x.y)));
+      scale = absmax_scale(a);
+      return (uint32_t(quant_code(x.x, scale)) & 0xFFu) |
+             ((uint32_t(quant_code(x.y, scale)) & 0xFFu) << 8);
+    };
+    kcode = quant2(kf, ks_new);
+    vcode = quant2(vf, vs_new);
+  }
   // Query codes as the B operand of q.K (column = head lc, k-chunk lg): the
   // head's absmax scale over all 128 channels (the 4 lanes of a column hold
   // 32 channels each), then the codes of channels 64 kk + 16 lg + 0..15.
@@ -842,6 +990,25 @@ decode_i8_mfma(const int8_t* __restrict__ kc, const int8_t* __restrict__ vc,
   }
   finish_mfma<G>(m_run, l_run, O, reinterpret_cast<float*>(&smem[0][0][0]), ws_m, ws_l, ws_o,
                  int64_t(b) * H + g * G, n_split, split);
+  if constexpr (APP) {
+    if (ao.own) {
+      const int64_t row = bg * max_seq + p_new;
+      reinterpret_cast<uint16_t*>(static_cast<int8_t*>(app.k) + row * kD)[lane] = uint16_t(kcode);
+      reinterpret_cast<uint16_t*>(static_cast<int8_t*>(app.v) + row * kD)[lane] = uint16_t(vcode);
+      if (lane == 0) {
+        app.ks[row] = ks_new;
+        app.vs[row] = vs_new;
+      }
+      if (app.kmin != nullptr) {
+        // bounds from the float32 key, rounded outward to f16
+        const uint16_t mn[2] = {f32_to_f16_down(fminf(INFINITY, kf.x)),
+                                f32_to_f16_down(fminf(INFINITY, kf.y))};
+        const uint16_t mx[2] = {f32_to_f16_up(fmaxf(-INFINITY, kf.x)),
+                                f32_to_f16_up(fmaxf(-INFINITY, kf.y))};
+        store_new_bounds(app, ao, bg, mn, mx);
+      }
+    }
+  }
 }
 
 }  // namespace
@@ -868,17 +1035,26 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   const dim3 grid(static_cast<uint32_t>(n_wg));
   const float scale2 = p.softmax_scale * kLog2e;
   const int fr = p.fused_r;
+  const bool app = p.app.k_new != nullptr;
+  AppendArgs aa{};
+  if (app) {
+    if (p.sel_idx != nullptr || fr > 0 || p.app.v_new == nullptr || p.app.pos0 == nullptr)
+      return hipErrorInvalidValue;
+    aa = AppendArgs{c.k, c.v, c.k_scale, c.v_scale, c.kmin, c.kmax, p.app.k_new, p.app.v_new,
+                    p.app.pos0, (c.max_seq + c.block - 1) / c.block};
+  }
   if (c.kv_dtype == SKV_F16) {
-#define SKV_LAUNCH_F16(GG, SR)                                                                  \
-  decode_f16_mfma<GG, SR><<<grid, kMThreads, 0, stream>>>(                                     \
+#define SKV_LAUNCH_F16(GG, SR, AP)                                                              \
+  decode_f16_mfma<GG, SR, AP><<<grid, kMThreads, 0, stream>>>(                                 \
       static_cast<const uint16_t*>(c.k), static_cast<const uint16_t*>(c.v), p.q, p.seq_len,    \
       p.sel_idx, p.sel_cnt, p.max_sel, c.n_kv_heads, c.max_seq, c.block, p.max_len, S,        \
-      n_rows, ups, scale2, ws_m, ws_l, ws_o, p.fsel)
+      n_rows, ups, scale2, ws_m, ws_l, ws_o, p.fsel, aa)
 #define SKV_F16_G(GG)                                  \
-  if (fr == 2) SKV_LAUNCH_F16(GG, 2);                  \
-  else if (fr == 4) SKV_LAUNCH_F16(GG, 4);             \
-  else if (fr > 0) SKV_LAUNCH_F16(GG, kFusedSelR);     \
-  else SKV_LAUNCH_F16(GG, 0)
+  if (app) SKV_LAUNCH_F16(GG, 0, true);                \
+  else if (fr == 2) SKV_LAUNCH_F16(GG, 2, false);      \
+  else if (fr == 4) SKV_LAUNCH_F16(GG, 4, false);      \
+  else if (fr > 0) SKV_LAUNCH_F16(GG, kFusedSelR, false); \
+  else SKV_LAUNCH_F16(GG, 0, false)
     switch (G) {
       case 1: SKV_F16_G(1); break;
       case 2: SKV_F16_G(2); break;
@@ -890,16 +1066,17 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
     return hipGetLastError();
   }
   if (c.kv_dtype != SKV_I8) return hipErrorInvalidValue;
-#define SKV_LAUNCH_I8(GG, SR)                                                                   \
-  decode_i8_mfma<GG, SR><<<grid, kMThreads, 0, stream>>>(                                      \
+#define SKV_LAUNCH_I8(GG, SR, AP)                                                               \
+  decode_i8_mfma<GG, SR, AP><<<grid, kMThreads, 0, stream>>>(                                  \
       static_cast<const int8_t*>(c.k), static_cast<const int8_t*>(c.v), c.k_scale, c.v_scale,  \
       p.q, p.seq_len, p.sel_idx, p.sel_cnt, p.max_sel, c.n_kv_heads, c.max_seq, c.block,       \
-      p.max_len, S, n_rows, ups, scale2, ws_m, ws_l, ws_o, p.dbg_logits, p.fsel)
+      p.max_len, S, n_rows, ups, scale2, ws_m, ws_l, ws_o, p.dbg_logits, p.fsel, aa)
 #define SKV_I8_G(GG)                                   \
-  if (fr == 2) SKV_LAUNCH_I8(GG, 2);                   \
-  else if (fr == 4) SKV_LAUNCH_I8(GG, 4);              \
-  else if (fr > 0) SKV_LAUNCH_I8(GG, kFusedSelR);      \
-  else SKV_LAUNCH_I8(GG, 0)
+  if (app) SKV_LAUNCH_I8(GG, 0, true);                 \
+  else if (fr == 2) SKV_LAUNCH_I8(GG, 2, false);       \
+  else if (fr == 4) SKV_LAUNCH_I8(GG, 4, false);       \
+  else if (fr > 0) SKV_LAUNCH_I8(GG, kFusedSelR, false); \
+  else SKV_LAUNCH_I8(GG, 0, false)
   switch (G) {
     case 1: SKV_I8_G(1); break;
     case 2: SKV_I8_G(2); break;

@@ -31,6 +31,15 @@ inline int fused_sel_chunks(int32_t n_load) {
   return n_load <= 2 * 256 ? 2 : n_load <= 4 * 256 ? 4 : kFusedSelR;
 }
 
+// The one-token append of a dense decode step, folded into decode_attn (see
+// skv_decode_step): rows [batch][1][n_kv_heads][128] of the cache's source
+// dtype (f16 for an f16 cache, float32 for an int8 cache) written at pos0[b].
+struct FoldedAppend {
+  const void* k_new = nullptr;   // nullptr: no append
+  const void* v_new = nullptr;
+  const int32_t* pos0 = nullptr;
+};
+
 struct DecodeParams {
   const skv_cache* c;
   const float* q;
@@ -47,6 +56,7 @@ struct DecodeParams {
   int fused_r = 0;          // > 0: select in the prologue from fsel with this many keys
                             // per thread (sel_idx/sel_cnt then receive the list)
   FusedSelect fsel{};
+  FoldedAppend app{};       // dense walks only (sel_idx == nullptr, fused_r == 0)
 };
 
 hipError_t launch_append(const skv_cache& c, const int32_t* pos0, int32_t n_new,

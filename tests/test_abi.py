@@ -58,6 +58,9 @@ BAD = 0x10  # never dereferenced: every call below fails validation first
     (dict(kv_dtype=skv.SKV_I8), skv.SKV_EINVAL),  # int8 without scales
     (dict(kmax=None), skv.SKV_EINVAL),            # half a side cache
     (dict(max_seq=0), skv.SKV_EINVAL),
+    (dict(k=0x1008), skv.SKV_EINVAL),             # rows move in 16-byte vectors
+    (dict(kmin=0x3004, kmax=0x4004), skv.SKV_EINVAL),
+    (dict(kv_dtype=skv.SKV_I8, k_scale=0x5002, v_scale=0x6000), skv.SKV_EINVAL),
 ])
 def test_cache_descriptor_validation(lib, kw, expect):
     d = desc(**kw)
@@ -75,6 +78,7 @@ def test_decode_argument_validation(lib):
     assert call(H=30) == skv.SKV_EINVAL               # H % Hkv != 0
     assert call(H=128) == skv.SKV_EUNSUPPORTED        # G = 16 not built
     assert call(q=None) == skv.SKV_EINVAL
+    assert call(q=BAD + 4) == skv.SKV_EINVAL          # q not 16-byte aligned
     assert call(sl=None) == skv.SKV_EINVAL
     assert call(si=BAD) == skv.SKV_EINVAL             # sel_idx without sel_cnt
     assert call(si=BAD, sc=BAD, ms=0) == skv.SKV_EINVAL
@@ -97,6 +101,7 @@ def test_append_validation(lib):
     assert f(d, pos=None) == skv.SKV_EINVAL
     assert f(d, n=0) == skv.SKV_EINVAL
     assert f(d, k=None) == skv.SKV_EINVAL
+    assert f(d, v=BAD + 8) == skv.SKV_EINVAL               # new rows 16-byte aligned
     assert f(d, n=1025) == skv.SKV_ERANGE
     assert f(d, src=skv.SKV_F32) == skv.SKV_EUNSUPPORTED   # f16 cache takes f16 rows
     assert f(d, src=99) == skv.SKV_EINVAL

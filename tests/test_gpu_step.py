@@ -5,7 +5,9 @@ selection into the attention kernel's prologue; neither changes any
 arithmetic, so every result must be bit-identical to kv_append ->
 block_bounds -> select_topk -> decode_attn -> combine on an identical cache:
 the output, the appended rows, scales and side-cache bounds, the scores and
-the selected lists, for each size class of the folded selection.  The
+the selected lists, for each size class of the folded selection.  The dense
+step folds the append into the attention kernel instead; its cases start
+from poisoned rows at the append positions.  The
 fallback paths (selection as its own kernel when a
 part spans more than 64 list entries or a row has more than 4096 blocks; the
 dense step) are held to the same bar.  One output per case is also checked
@@ -42,11 +44,30 @@ def _cache_tensors(c):
     return [t for t in (c.k, c.v, c.k_scale, c.v_scale, c.kmin, c.kmax) if t is not None]
 
 
-def _run_case(w, quest, append, S=None, max_seq=None, max_sel=None):
+def _poison_rows(cache, pos):
+    """Fill the rows the step's append will write with values no correct
+    result can depend on (NaN halves; int8 code -128 and NaN scales)."""
+    for b, p in enumerate(pos.tolist()):
+        if cache.kv_dtype == "f16":
+            cache.k[b, :, p] = float("nan")
+            cache.v[b, :, p] = float("nan")
+        else:
+            cache.k[b, :, p] = -128
+            cache.v[b, :, p] = -128
+            cache.k_scale[b, :, p] = float("nan")
+            cache.v_scale[b, :, p] = float("nan")
+
+
+def _run_case(w, quest, append, S=None, max_seq=None, max_sel=None, poison=False, lag=0):
+    """``poison``: the append positions hold NaN / out-of-range data before the
+    step; ``lag``: seq_len excludes the last ``lag`` tokens (with lag 1 the new
+    token lies past every walk)."""
     base = _prefilled(w, max_seq, whole=not append)
+    if poison:
+        _poison_rows(base, _new_token(w)[0])
     ca, cb = base.clone(), base.clone()
     q = torch.from_numpy(np.ascontiguousarray(w.q)).to(DEV)
-    seq_len = torch.tensor(w.lens, dtype=torch.int32, device=DEV)
+    seq_len = torch.tensor([L - lag for L in w.lens], dtype=torch.int32, device=DEV)
     max_len = max(w.lens)
     ks = torch.tensor(w.k_sel, dtype=torch.int32, device=DEV) if quest else None
     if quest:
@@ -144,6 +165,22 @@ STEP_CASES = [
         n_recent=2), True, True, {"S": 7}),
     ("dense-f16 varlen", lambda: workloads.gaussian(
         510, 3, 16, 4, 128, [100, 64, 2500], "f16"), False, True, {}),
+    # the dense step writes the new token from the attention kernel: its rows
+    # start out poisoned; positions at a block's first token (fresh bounds),
+    # mid block, position 0, a part count that does not divide the blocks
+    ("dense-f16 append poisoned rows", lambda: workloads.gaussian(
+        518, 3, 32, 8, 128, [65, 1, 4097], "f16"), False, True, {"poison": True}),
+    ("dense-i8 append poisoned rows G8", lambda: workloads.gaussian(
+        519, 2, 32, 4, 128, [3000, 129], "i8"), False, True, {"poison": True}),
+    ("dense-i8 append 7 parts", lambda: workloads.gaussian(
+        520, 2, 16, 8, 128, [2050, 700], "i8"), False, True, {"poison": True, "S": 7}),
+    ("dense-f16 append 40 parts G1", lambda: workloads.gaussian(
+        521, 1, 8, 8, 128, [999], "f16"), False, True, {"poison": True, "S": 40}),
+    # seq_len without the new token: the append still lands, no walk reads it
+    ("dense-f16 append past the length", lambda: workloads.gaussian(
+        522, 2, 32, 8, 128, [2, 300], "f16"), False, True, {"lag": 1}),
+    ("dense-i8 append past the length", lambda: workloads.gaussian(
+        523, 2, 32, 8, 128, [1, 129], "i8"), False, True, {"lag": 1}),
     ("dense-i8 no append", lambda: workloads.gaussian(
         511, 1, 32, 8, 128, [1000], "i8"), False, False, {}),
 ]
@@ -154,7 +191,8 @@ def test_decode_step_equals_composed_calls(gpu_lib, name, make, quest, append, e
     _print(name)
     w = make()
     out, sel = _run_case(w, quest, append, **extra)
-    _oracle_check(w, out, sel)
+    if not extra.get("lag"):
+        _oracle_check(w, out, sel)
 
 
 def test_decode_step_replays_in_a_hip_graph(gpu_lib):
