@@ -7,8 +7,9 @@ split-K merge (combine), issued as one skv_decode_step (three launches:
 append folded into the bounds pass, selection into the attention
 prologue); the same five calls issued one by one are timed too.  The headline workload is the 32K-context GQA
 decode (B=1, H=32, Hkv=8, D=128, f16 KV, block 64, K_SEL=128 + sink + 2
-recent); the same cache is also timed with dense decode (append +
-decode_attn + combine) for the sparse/dense ratio.  The other named
+recent); the same cache is also timed with the dense step (two launches:
+the append folded into decode_attn, then combine) for the sparse/dense
+ratio.  The other named
 workloads (512-token dense f16, 8K int8, the 16-sequence 16K-64K batch,
 262K int8 Quest) are timed the same way and reported under "workloads".
 
@@ -481,7 +482,7 @@ def main():
                    "step": ("decode_step: kv_append + block_bounds + select_topk + "
                             "decode_attn(selected blocks) + combine in 3 launches")
                            if hq is not None else
-                           "decode_step: kv_append + decode_attn(dense) + combine",
+                           "decode_step: kv_append + decode_attn(dense) + combine in 2 launches",
                    "cache_copies": head["cache_copies"],
                    "launch": "hipgraph" if not args.no_graph else "stream",
                    "n_split": top["n_split"]},
