@@ -297,6 +297,88 @@ def test_int8_decode_step_replays_in_a_hip_graph(gpu_lib):
     _oracle_check(w, out.cpu().numpy(), (sel.cpu().numpy(), cnt.cpu().numpy()))
 
 
+@pytest.mark.parametrize("kv", ["f16", "i8"])
+def test_dense_decode_step_replays_in_a_hip_graph(gpu_lib, kv):
+    """The dense step (append folded into the attention kernel, then combine)
+    captured once and replayed; before each replay the append positions are
+    poisoned again by eager work, so every replay must take the new token
+    from k_new / v_new and write it back, as the eager step did."""
+    _print("dense step graph", kv)
+    w = workloads.gaussian(524, 2, 32, 8, 128, [5000, 4097], kv)
+    base = _prefilled(w)
+    q = torch.from_numpy(np.ascontiguousarray(w.q)).to(DEV)
+    seq_len = torch.tensor(w.lens, dtype=torch.int32, device=DEV)
+    pos, kn, vn = _new_token(w)
+    S = skv.default_split(2, 8, -(-5000 // 64), kv_dtype=kv)
+    out, ws, _, _, _ = _buffers(w, base, False, 0, S)
+
+    def step():
+        skv.decode_step(base, q, seq_len, 5000, w.softmax_scale, S, ws, out, pos0=pos,
+                        k_new=kn, v_new=vn)
+
+    _poison_rows(base, pos)
+    step()
+    torch.cuda.synchronize()
+    ref = out.clone()
+    ref_cache = [t.clone() for t in _cache_tensors(base)]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for _ in range(4):
+        out.fill_(float("nan"))
+        _poison_rows(base, pos)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref)
+        for a, b in zip(ref_cache, _cache_tensors(base)):
+            assert torch.equal(a, b)
+    _oracle_check(w, out.cpu().numpy(), None)
+
+
+@pytest.mark.parametrize("kv", ["f16", "i8"])
+def test_dense_decode_step_without_side_cache(gpu_lib, kv):
+    """A cache built without Quest bounds: the dense step's folded append
+    writes the rows (and int8 scales) only, bit-identical to kv_append +
+    decode_attn + combine."""
+    _print("dense step, no side cache", kv)
+    w = workloads.gaussian(525, 2, 16, 4, 128, [3001, 64], kv)
+    pos, kn, vn = _new_token(w)
+    dt = np.float16 if kv == "f16" else np.float32
+    rows = max(w.lens) - 1
+    k = np.zeros((w.B, rows, w.Hkv, w.D), dt)
+    v = np.zeros((w.B, rows, w.Hkv, w.D), dt)
+    for b, L in enumerate(w.lens):
+        k[b, :L - 1] = np.transpose(w.k[b][:, :L - 1], (1, 0, 2))
+        v[b, :L - 1] = np.transpose(w.v[b][:, :L - 1], (1, 0, 2))
+    base = skv.Cache(w.B, w.Hkv, max(w.lens), w.D, kv, w.block, bounds=False, device=DEV)
+    skv.kv_append(base, torch.zeros(w.B, dtype=torch.int32, device=DEV),
+                  torch.from_numpy(k).to(DEV), torch.from_numpy(v).to(DEV))
+    _poison_rows(base, pos)
+    ca, cb = base.clone(), base.clone()
+    q = torch.from_numpy(np.ascontiguousarray(w.q)).to(DEV)
+    seq_len = torch.tensor(w.lens, dtype=torch.int32, device=DEV)
+    S = skv.default_split(w.B, w.Hkv, -(-max(w.lens) // w.block), kv_dtype=kv)
+    out_a, ws_a, _, _, _ = _buffers(w, ca, False, 0, S)
+    out_b, ws_b, _, _, _ = _buffers(w, cb, False, 0, S)
+    skv.kv_append(ca, pos, kn, vn)
+    skv.decode_attn(ca, q, seq_len, max(w.lens), w.softmax_scale, S, ws_a)
+    skv.combine(ws_a, w.B, w.H, w.D, S, out_a)
+    skv.decode_step(cb, q, seq_len, max(w.lens), w.softmax_scale, S, ws_b, out_b, pos0=pos,
+                    k_new=kn, v_new=vn)
+    torch.cuda.synchronize()
+    assert cb.kmin is None
+    assert torch.equal(out_a, out_b)
+    for ta, tb in zip(_cache_tensors(ca), _cache_tensors(cb)):
+        assert torch.equal(ta, tb)
+    _oracle_check(w, out_b.cpu().numpy(), None)
+
+
 @pytest.mark.parametrize("k_sel", [100, 300])
 def test_decode_step_tie_classes(gpu_lib, k_sel):
     """Blocks that repeat 8 contents have 8 distinct bounds per KV head, each
