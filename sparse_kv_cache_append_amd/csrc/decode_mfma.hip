@@ -239,7 +239,7 @@ __device__ __forceinline__ TileWalk fused_walk(const FusedSelect& fs, int32_t ma
     const uint64_t cut = sel_cut(kk, K, ssh);
     const uint64_t taken = sel_taken_mask(kk, cut);
     const int R = (n_cand + kSelThreads - 1) / kSelThreads;
-    const SelOrder o = sel_order_prepare(taken, R, ssh);
+    const SelOrder o = sel_order_prepare<SELR>(taken, R, ssh);
     // only the (chunk, wave) groups whose taken candidates reach this part's
     // slice of positions do any work (a wave-uniform test)
 #pragma unroll

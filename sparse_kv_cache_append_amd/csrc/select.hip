@@ -68,7 +68,7 @@ select_kernel(const float* __restrict__ score, const int32_t* __restrict__ seq_l
     const uint64_t cut = sel_cut(kk, K, sh);
     const uint64_t taken = sel_taken_mask(kk, cut);
     const int R = (n_cand + kSelThreads - 1) / kSelThreads;
-    const SelOrder o = sel_order_prepare(taken, R, sh);
+    const SelOrder o = sel_order_prepare<RMAX>(taken, R, sh);
 #pragma unroll
     for (int r = 0; r < RMAX; ++r) {
       if (r < R) {
