@@ -192,7 +192,7 @@ __device__ __forceinline__ TileWalk fused_walk(const FusedSelect& fs, int32_t ma
                                                int32_t b, int32_t L, int32_t L_raw, int32_t block,
                                                int32_t split, int32_t units_per_split) {
   __shared__ SelectShared ssh;
-  __shared__ int32_t plist[kWave];
+  __shared__ int32_t plist[kWave + kSelThreads];   // the slice, then one spare entry per thread
   const int tid = threadIdx.x;
   // The candidates start at n_sink whenever there are any, so their scores
   // are requested before the row's length is used (up to the row's capacity).
@@ -240,25 +240,25 @@ __device__ __forceinline__ TileWalk fused_walk(const FusedSelect& fs, int32_t ma
     const uint64_t taken = sel_taken_mask(kk, cut);
     const int R = (n_cand + kSelThreads - 1) / kSelThreads;
     const SelOrder o = sel_order_prepare<SELR>(taken, R, ssh);
-    // only the (chunk, wave) groups whose taken candidates reach this part's
-    // slice of positions do any work (a wave-uniform test)
+    // the taken candidates whose positions fall in this part's slice go to
+    // plist; every thread writes once per chunk, the others to a spare entry
+    // of their own, so the chunks carry no branch and overlap (chunks past R
+    // have no taken bit)
 #pragma unroll
     for (int r = 0; r < SELR; ++r) {
-      if (r < R) {
-        const uint64_t bal = __ballot(int((taken >> r) & 1u));
-        const int32_t first = cs + __builtin_amdgcn_readlane(o.pre, r);
-        if (first < u0 + ups && first + __popcll(bal) > u0 && ((taken >> r) & 1u)) {
-          const int32_t pos = first + lanes_below(bal);
-          if (pos >= u0 && pos < u0 + ups) {
-            const int32_t blk = cs + kk.index(r);
-            plist[pos - u0] = blk;
-            if (pos < max_sel) out_row[pos] = blk;
-          }
-        }
-      }
+      const bool t = (taken >> r) & 1u;
+      const uint64_t bal = __ballot(int(t));
+      const int32_t pos = cs + __builtin_amdgcn_readlane(o.pre, r) + lanes_below(bal);
+      const bool hit = t && pos >= u0 && pos < u0 + ups;
+      plist[hit ? pos - u0 : kWave + tid] = cs + kk.index(r);
     }
   }
   __syncthreads();
+  // the selected (not arithmetic) entries of the slice, published
+  if (tid < ups && K > 0 && K < n_cand) {
+    const int32_t pos = u0 + tid;
+    if (pos >= cs && pos < cs + K && pos < max_sel) out_row[pos] = plist[tid];
+  }
   const int lane = tid % kWave;
   tw.jl = lane < ups ? plist[lane] : -1;
   tw.n_units = __builtin_amdgcn_readfirstlane(max(0, min(ups, min(n_sel, max_sel) - u0)));
