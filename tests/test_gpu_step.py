@@ -379,6 +379,35 @@ def test_dense_decode_step_without_side_cache(gpu_lib, kv):
     _oracle_check(w, out_b.cpu().numpy(), None)
 
 
+@pytest.mark.parametrize("kv", ["f16", "i8"])
+def test_dense_decode_step_out_of_range_positions(gpu_lib, kv):
+    """Append positions the append kernel skips (negative, or at or past the
+    cache capacity) are skipped by the dense step's folded append too: the
+    cache is untouched for those sequences and everything stays
+    bit-identical to kv_append + decode_attn + combine."""
+    _print("dense step, out-of-range positions", kv)
+    w = workloads.gaussian(526, 3, 32, 8, 128, [700, 1000, 1500], kv)
+    base = _prefilled(w, max_seq=1500)
+    _, kn, vn = _new_token(w)
+    pos = torch.tensor([-1, 1500, 1499], dtype=torch.int32, device=DEV)
+    ca, cb = base.clone(), base.clone()
+    q = torch.from_numpy(np.ascontiguousarray(w.q)).to(DEV)
+    seq_len = torch.tensor(w.lens, dtype=torch.int32, device=DEV)
+    S = skv.default_split(w.B, w.Hkv, -(-1500 // w.block), kv_dtype=kv)
+    out_a, ws_a, _, _, _ = _buffers(w, ca, False, 0, S)
+    out_b, ws_b, _, _, _ = _buffers(w, cb, False, 0, S)
+    skv.kv_append(ca, pos, kn, vn)
+    skv.decode_attn(ca, q, seq_len, 1500, w.softmax_scale, S, ws_a)
+    skv.combine(ws_a, w.B, w.H, w.D, S, out_a)
+    skv.decode_step(cb, q, seq_len, 1500, w.softmax_scale, S, ws_b, out_b, pos0=pos,
+                    k_new=kn, v_new=vn)
+    torch.cuda.synchronize()
+    assert torch.equal(out_a, out_b)
+    for ta, tb, t0 in zip(_cache_tensors(ca), _cache_tensors(cb), _cache_tensors(base)):
+        assert torch.equal(ta, tb)
+        assert torch.equal(tb[:2], t0[:2])      # sequences 0 and 1 were not written
+
+
 @pytest.mark.parametrize("k_sel", [100, 300])
 def test_decode_step_tie_classes(gpu_lib, k_sel):
     """Blocks that repeat 8 contents have 8 distinct bounds per KV head, each
