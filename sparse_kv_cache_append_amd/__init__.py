@@ -233,11 +233,18 @@ def default_split(batch: int, n_kv_heads: int, n_units: int, target_wgs: Optiona
     """Parts per (sequence, KV head) so the grid has about ``target_wgs``
     workgroups, at least one block (or selected entry) per part.  Default:
     one workgroup per compute unit, or two for dense decode over an int8
-    cache, whose tiles cost more arithmetic per byte and gain from a second
-    workgroup hiding the first one's loads (sparse decode keeps one: every
-    part of a row also runs the block selection)."""
+    cache while every part still gets at least 4 blocks: its tiles cost more
+    arithmetic per byte and gain from a second workgroup hiding the first
+    one's loads (262K context, 4 KV heads: 128 parts of 32 blocks), but short
+    parts are dominated by their fixed cost (8K context, 8 KV heads: the step
+    takes 12.1 us with 64 parts of 2 blocks, 11.5 us with 32 parts of 4).
+    Sparse decode keeps one: every part of a row also runs the block
+    selection."""
     if target_wgs is None:
-        target_wgs = 512 if (kv_dtype == "i8" and not sparse) else 256
+        target_wgs = 256
+        two = math.ceil(512 / max(1, batch * n_kv_heads))
+        if kv_dtype == "i8" and not sparse and n_units >= 4 * two:
+            target_wgs = 512
     n = max(1, math.ceil(target_wgs / max(1, batch * n_kv_heads)))
     return int(max(1, min(n, n_units, 4096)))
 
