@@ -163,3 +163,21 @@ def test_grid_size_limits(lib):
     assert lib.skv_select_topk(BAD, BAD, 70000, 40000, 16, 64, BAD, 1, 2, 8, BAD, BAD, None,
                                None) == skv.SKV_ERANGE
     assert lib.skv_combine(BAD, 70000, 40000, 128, 4, BAD, None) == skv.SKV_ERANGE
+
+
+def test_default_split_rule():
+    """Host-side split choice: about one workgroup per compute unit, at least
+    one unit per part; dense int8 doubles that only while every part keeps at
+    least 4 blocks; Quest parts run over the selected list."""
+    ds = skv.default_split
+    assert ds(1, 8, 512) == 32                              # 32K f16: 256 workgroups
+    assert ds(1, 8, 8) == 8                                 # 512 tokens: one block per part
+    assert ds(16, 8, 1024) == 2                             # 16 sequences x 8 KV heads
+    assert ds(1, 4, 4096, kv_dtype="i8") == 128             # 262K int8: 512 workgroups
+    assert ds(1, 8, 128, kv_dtype="i8") == 32               # 8K int8: 4-block parts kept
+    assert ds(1, 8, 255, kv_dtype="i8") == 32               # 64 parts would hold < 4 blocks
+    assert ds(1, 8, 256, kv_dtype="i8") == 64
+    assert ds(1, 4, 517, kv_dtype="i8", sparse=True) == 64  # Quest: one workgroup per CU
+    assert ds(1, 8, 131, sparse=True) == 32
+    assert ds(1, 1, 10 ** 6) == 256 and ds(1, 1, 10 ** 9, target_wgs=10 ** 6) == 4096
+    assert ds(4096, 16, 1000) == 1
