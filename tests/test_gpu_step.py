@@ -174,6 +174,10 @@ STEP_CASES = [
         519, 2, 32, 4, 128, [3000, 129], "i8"), False, True, {"poison": True}),
     ("dense-i8 append 7 parts", lambda: workloads.gaussian(
         520, 2, 16, 8, 128, [2050, 700], "i8"), False, True, {"poison": True, "S": 7}),
+    ("dense-f16 append block 16", lambda: workloads.gaussian(
+        527, 2, 32, 8, 128, [1601, 999], "f16", block=16), False, True, {"poison": True}),
+    ("dense-i8 append block 128 G2", lambda: workloads.gaussian(
+        528, 2, 16, 8, 128, [1025, 2000], "i8", block=128), False, True, {"poison": True}),
     ("dense-f16 append 40 parts G1", lambda: workloads.gaussian(
         521, 1, 8, 8, 128, [999], "f16"), False, True, {"poison": True, "S": 40}),
     # seq_len without the new token: the append still lands, no walk reads it
