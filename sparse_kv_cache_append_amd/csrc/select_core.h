@@ -242,15 +242,19 @@ __device__ __forceinline__ uint64_t sel_cut(const SelKeys<RMAX>& kk, int32_t K, 
     }
     uint64_t cand = __ballot(lane < m);
     int r = remaining;
-    for (int bit = 63 - __popc(pmask); bit >= 0 && __popcll(cand) > 1; --bit) {
-      const uint64_t ones = __ballot(int((v >> bit) & 1u)) & cand;
+    // Two bits per trip and one uniqueness test per trip (each bit is a
+    // chain of dependent scalar instructions, ~150 cycles): a step after the
+    // candidate is alone keeps it (r is then 1), and bit -1 has no ones.
+    auto step = [&](int bit) {
+      const uint64_t ones = bit >= 0 ? __ballot(int((v >> bit) & 1u)) & cand : uint64_t(0);
       const int n1 = __popcll(ones);
-      if (n1 >= r) {
-        cand = ones;
-      } else {
-        r -= n1;
-        cand &= ~ones;
-      }
+      const bool take = n1 >= r;
+      r = take ? r : r - n1;
+      cand = take ? ones : cand ^ ones;      // ones is a subset of cand
+    };
+    for (int bit = 63 - __popc(pmask); bit >= 0 && (cand & (cand - 1u)) != 0u; bit -= 2) {
+      step(bit);
+      step(bit - 1);
     }
     const int win = __builtin_ctzll(cand);
     const uint32_t hi = __builtin_amdgcn_readlane(uint32_t(v >> 32), win);
