@@ -387,8 +387,8 @@ __device__ __forceinline__ void finish_mfma(float m_run, float l_run, const floa
 // of its tiles holds position pos0[b], writes them over that row of the tile
 // staged in LDS, so the attention sees exactly what the separate append would
 // have stored there (the cache row itself is stale until this step writes it).
-// The part whose blocks hold pos0[b] (its last part when pos0 lies past them)
-// writes the rows, the int8 scales and the block's merged side-cache bounds,
+// The part whose blocks hold pos0[b] (the row's last part when pos0 lies past
+// every part's blocks) writes the rows, the int8 scales and the block's merged side-cache bounds,
 // as skv_kv_append does for one token: wavefront 0, after its walk.  The old
 // bounds it merges with are requested before the walk through a buffer
 // resource that has records only in that wavefront and only for a block that
@@ -422,8 +422,9 @@ __device__ __forceinline__ AppendOwner append_owner(const AppendArgs& app, int32
   o.jp = p_ok ? p_new / block : 0;
   o.fresh = p_ok && o.jp * block == p_new;
   o.own = p_ok && wave == 0 && split == min(o.jp / units_per_split, n_split - 1);
-  const int bytes = (o.own && app.kmin != nullptr && !o.fresh) ? kD * 2 : 0;
-  const int64_t bo = (bg * app.max_blocks + o.jp) * kD;
+  const bool side = app.kmin != nullptr;
+  const int bytes = (o.own && side && !o.fresh) ? kD * 2 : 0;
+  const int64_t bo = side ? (bg * app.max_blocks + o.jp) * kD : 0;   // no offset on a null base
   const auto rmn = __builtin_amdgcn_make_buffer_rsrc(app.kmin + bo, (short)0, bytes, kRsrcWord3);
   const auto rmx = __builtin_amdgcn_make_buffer_rsrc(app.kmax + bo, (short)0, bytes, kRsrcWord3);
   const uint32_t lane = threadIdx.x % kWave;
