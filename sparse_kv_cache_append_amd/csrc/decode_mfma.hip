@@ -185,8 +185,8 @@ __device__ __forceinline__ TileWalk make_walk(const ListSeed& ls, const int32_t*
 // part's slice [u0, u0 + ups) of the ascending list goes to LDS and to the
 // published list (the n_split slices cover [0, max_sel), ups being
 // ceil(max_sel / n_split)); split 0 also publishes the count.
-// (The scores are requested here, after the query has arrived, rather than
-// at kernel entry: issuing them first measured slower for this kernel.)
+// (The scores are requested here, after the query has arrived; requesting
+// them at kernel entry instead measured no faster.)
 template <int T, int SELR>
 __device__ __forceinline__ TileWalk fused_walk(const FusedSelect& fs, int32_t max_sel, int64_t bg,
                                                int32_t b, int32_t L, int32_t L_raw, int32_t block,
