@@ -44,6 +44,10 @@ def block_bounds(keys: np.ndarray, L: int, block: int):
     keys [Hkv][L][D], float16 (f16 cache: exact) or float32 (int8 cache:
     kmin rounded toward -inf, kmax toward +inf into float16).
     Returns (kmin, kmax) float16 [Hkv][NB][D], NB = ceil(L / block).
+
+    A NaN key value is left out of its channel's min and max (reading taken;
+    the page does not say): a channel whose keys in the block are all NaN
+    gets kmin = +inf, kmax = -inf, so it can only lower the block's bound.
     """
     Hkv, _, D = keys.shape
     nb = -(-L // block)
@@ -51,8 +55,9 @@ def block_bounds(keys: np.ndarray, L: int, block: int):
     kmax = np.empty((Hkv, nb, D), dtype=keys.dtype)
     for j in range(nb):
         blk = keys[:, j * block:min((j + 1) * block, L), :]
-        kmin[:, j] = blk.min(axis=1)
-        kmax[:, j] = blk.max(axis=1)
+        nan = np.isnan(blk)
+        kmin[:, j] = np.where(nan, np.inf, blk).min(axis=1)
+        kmax[:, j] = np.where(nan, -np.inf, blk).max(axis=1)
     if keys.dtype == np.float16:
         return kmin, kmax
     return f16_round_down(kmin), f16_round_up(kmax)

@@ -190,3 +190,29 @@ def test_zero_query_channel_contributes_zero_even_against_infinite_bounds():
     kmax = np.array([[[np.inf, 2.0]]], np.float16)
     q = np.array([[0.0, 3.0]], np.float32)
     assert oracle.upper_bounds(q, kmin, kmax)[0, 0] == 6.0
+
+
+def test_nan_keys_are_left_out_of_the_envelope():
+    """Reading taken for NaN keys: they do not enter a channel's min/max.  The
+    pin is a plain Python min/max over the non-NaN values of each channel
+    (+inf / -inf when none is left)."""
+    rng = np.random.default_rng(7)
+    for dt in (np.float16, np.float32):
+        k = rng.standard_normal((2, 70, 16)).astype(dt)
+        k[0, 3, 5] = np.nan                  # one NaN in a block
+        k[1, 64:70, 2] = np.nan              # a whole (partial) block's channel
+        kmin, kmax = oracle.block_bounds(k, 70, 64)
+        for g in range(2):
+            for j in range(2):
+                for d in range(16):
+                    vals = [float(x) for x in k[g, j * 64:min(70, (j + 1) * 64), d]
+                            if not np.isnan(x)]
+                    lo = min(vals) if vals else np.inf
+                    hi = max(vals) if vals else -np.inf
+                    if dt == np.float16:
+                        assert float(kmin[g, j, d]) == lo and float(kmax[g, j, d]) == hi
+                    else:
+                        assert float(kmin[g, j, d]) <= lo and float(kmax[g, j, d]) >= hi
+                        if vals:
+                            assert float(kmin[g, j, d]) > lo - 2e-3 * (abs(lo) + 1)
+        assert kmin[1, 1, 2] == np.inf and kmax[1, 1, 2] == -np.inf
