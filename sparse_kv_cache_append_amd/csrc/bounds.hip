@@ -46,7 +46,8 @@ __device__ __forceinline__ void append_one(const AppendOne& ap, uint16_t* __rest
     const uint16_t* kn = static_cast<const uint16_t*>(ap.k_new) + bg * D;
     for (int d = tid; d < D; d += kBoundsThreads) {
       const uint16_t x = kn[d];
-      uint16_t bmn = x, bmx = x;
+      const bool nan = (x & 0x7FFFu) > 0x7C00u;      // skipped, as by the append kernel
+      uint16_t bmn = nan ? uint16_t(0x7C00u) : x, bmx = nan ? uint16_t(0xFC00u) : x;
       if (!fresh) {
         bmn = f16_min_bits(kmin[bo + d], bmn);
         bmx = f16_max_bits(kmax[bo + d], bmx);
@@ -77,7 +78,7 @@ __device__ __forceinline__ void append_one(const AppendOne& ap, uint16_t* __rest
     const float* kn = static_cast<const float*>(ap.k_new) + bg * D;
     for (int d = tid; d < D; d += kBoundsThreads) {
       const float x = kn[d];
-      uint16_t bmn = f32_to_f16_down(x), bmx = f32_to_f16_up(x);
+      uint16_t bmn = f32_to_f16_down(fminf(INFINITY, x)), bmx = f32_to_f16_up(fmaxf(-INFINITY, x));
       if (!fresh) {
         bmn = f16_min_bits(kmin[bo + d], bmn);
         bmx = f16_max_bits(kmax[bo + d], bmx);
@@ -102,18 +103,25 @@ template <int MODE>
 __device__ __forceinline__ void merge_new_key(bool fresh, const uint4& kx, const float (&kf)[8],
                                               uint16_t (&lb)[8], uint16_t (&hb)[8]) {
   uint16_t nmn[8], nmx[8];
+  // a NaN channel leaves the bounds as they were (+inf / -inf in a fresh
+  // block), the rule of the append kernel's min/max scan
   if constexpr (MODE == kAppendF16) {
     const uint32_t w[4] = {kx.x, kx.y, kx.z, kx.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      nmn[2 * i] = nmx[2 * i] = uint16_t(w[i] & 0xFFFFu);
-      nmn[2 * i + 1] = nmx[2 * i + 1] = uint16_t(w[i] >> 16);
+#pragma unroll
+      for (int hlf = 0; hlf < 2; ++hlf) {
+        const uint16_t x = uint16_t(hlf ? (w[i] >> 16) : (w[i] & 0xFFFFu));
+        const bool nan = (x & 0x7FFFu) > 0x7C00u;
+        nmn[2 * i + hlf] = nan ? uint16_t(0x7C00u) : x;
+        nmx[2 * i + hlf] = nan ? uint16_t(0xFC00u) : x;
+      }
     }
   } else {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      nmn[e] = f32_to_f16_down(kf[e]);
-      nmx[e] = f32_to_f16_up(kf[e]);
+      nmn[e] = f32_to_f16_down(fminf(INFINITY, kf[e]));
+      nmx[e] = f32_to_f16_up(fmaxf(-INFINITY, kf[e]));
     }
   }
 #pragma unroll

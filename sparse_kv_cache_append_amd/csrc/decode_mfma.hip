@@ -329,12 +329,22 @@ __device__ __forceinline__ void tile_softmax(float (&s)[4 * NT], float& m_run, f
   m_run = m_ref;
 }
 
+// The weights enter P.V as an f16 high part plus an f16 low part, both taken
+// from the weight times 2^kPwShift (exact).  The f16 kernel's weights are at
+// most 1 (exact running maximum), so the scaled weights stay below 2^15 and
+// every weight down to 2^-18 of the running maximum keeps its full ~22-bit
+// precision, weights down to 2^-29 at least 11 bits; without the shift a long
+// flat tail of weights below 2^-14 would reach P.V with only a few
+// (subnormal) bits while its full mass counts in the normalizer.  O is
+// scaled back (exactly) before the partial state is written.
+constexpr int kPwShiftF16 = 15;
 __device__ __forceinline__ void split_hi_lo4(const float* p, half4_t& hi, half4_t& lo) {
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
-    const _Float16 h = (_Float16)p[s];
+    const float x = p[s] * float(1 << kPwShiftF16);
+    const _Float16 h = (_Float16)x;
     hi[s] = h;
-    lo[s] = (_Float16)(p[s] - (float)h);
+    lo[s] = (_Float16)(x - (float)h);
   }
 }
 
@@ -625,6 +635,11 @@ decode_f16_mfma(const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc
     process(std::integral_constant<int, 1>{}, f1);
   }
   if (n_mine & 1) process(std::integral_constant<int, 0>{}, f0);
+#pragma unroll
+  for (int n = 0; n < 8; ++n) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) O[n][r] *= 1.0f / float(1 << kPwShiftF16);
+  }
   finish_mfma<G>(m_run, l_run, O, reinterpret_cast<float*>(&smem[0][0][0]), ws_m, ws_l, ws_o,
                  int64_t(b) * H + g * G, n_split, split);
   if constexpr (APP) {
@@ -664,12 +679,15 @@ decode_f16_mfma(const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc
 // 16 n + j of tokens tok(lg, 0..7).  The codes are widened to f16 exactly
 // (1152 + c is exact in f16, minus 1152).
 //
-// The V scales are folded into the weights: P' = p * v_scale * 2^-e with
+// The V scales are folded into the weights: P' = p * v_scale * 2^(7 - e) with
 // 2^e the largest V scale seen so far rounded up to a power of two, so P'
-// stays below the softmax's weight bound (2^8 with its lazy reference) and
-// the f16 high + low split keeps its precision whatever the scale's
-// magnitude; the accumulator holds O * 2^-e, is rescaled (exactly, by a power
-// of two) in the rare tile where e grows, and is scaled back at the end.
+// stays below 2^15 (the softmax's weight bound is 2^8 with its lazy
+// reference) and the f16 high + low split keeps its precision whatever the
+// scale's magnitude, with 7 bits of headroom for small weights (a weight 2^-10
+// of the largest still gets about 18 bits); the accumulator holds
+// O * 2^(7 - e), is rescaled (exactly, by a power of two) in the rare tile
+// where e grows, and is scaled back at the end.
+constexpr int kPwShiftI8 = 7;
 __device__ __forceinline__ half8_t widen_codes(int2_t w) {
   typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
   // v_perm_b32 picks bytes of {0x64646464, x}: selector 0..3 = bytes of x,
@@ -847,7 +865,7 @@ decode_i8_mfma(const int8_t* __restrict__ kc, const int8_t* __restrict__ vc,
       }
     }
     const int e_use = e_run == kExpUnset ? 0 : e_run;
-    st[lane] = lane >= 32 ? ldexpf(scl, -e_use) : scl;
+    st[lane] = lane >= 32 ? ldexpf(scl, kPwShiftI8 - e_use) : scl;
     issue(fr);
     // q.K, exact: two 16-token halves, 128 channels as two k = 64 steps
     int4_t acc[2];
@@ -881,10 +899,10 @@ decode_i8_mfma(const int8_t* __restrict__ kc, const int8_t* __restrict__ vc,
       for (int e = 0; e < 8; ++e)
         sc[e] = 16 * (e / 4) + 4 * lg + e % 4 < nvalid ? sc[e] : -INFINITY;
     }
-    // O is kept in units of 2^e_run; the exact change of unit when e_run
+    // O is kept in units of 2^(e_run - 7); the exact change of unit when e_run
     // grows rides on the softmax rescale of O
     tile_softmax<G, 2, true>(sc, m_run, l_run, O, unit);
-    // P' = p * v_scale * 2^-e_run (the stored V scales are in that unit)
+    // P' = p * v_scale * 2^(7 - e_run) (the stored V scales are in that unit)
     float pw[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) pw[e] = sc[e] * vs[e];
@@ -986,7 +1004,7 @@ decode_i8_mfma(const int8_t* __restrict__ kc, const int8_t* __restrict__ vc,
 #pragma unroll
     for (int n = 0; n < 8; ++n) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) O[n][r] = ldexpf(O[n][r], e_run);
+      for (int r = 0; r < 4; ++r) O[n][r] = ldexpf(O[n][r], e_run - kPwShiftI8);
     }
   }
   finish_mfma<G>(m_run, l_run, O, reinterpret_cast<float*>(&smem[0][0][0]), ws_m, ws_l, ws_o,
@@ -1023,6 +1041,9 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   float* ws_m = p.ws + ws_m_offset(B, H, S);
   float* ws_l = p.ws + ws_l_offset(B, H, S);
   float* ws_o = p.ws + ws_o_offset(B, H, S);
+  // units (blocks, or entries of the selected list) per part; at least one,
+  // also for an empty cache (max_len == 0), since the folded append divides
+  // the new token's block index by it to find the part that writes the token
   int32_t ups;
   if (p.sel_idx != nullptr) {
     ups = (p.max_sel + S - 1) / S;
@@ -1030,6 +1051,7 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
     const int32_t nb_max = (p.max_len + c.block - 1) / c.block;
     ups = (nb_max + S - 1) / S;
   }
+  ups = ups < 1 ? 1 : ups;
   const int64_t n_wg = int64_t(S) * c.n_kv_heads * B;
   if (n_wg > 0x7fffffff) return hipErrorInvalidValue;
   const int32_t n_rows = c.n_kv_heads * B;

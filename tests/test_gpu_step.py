@@ -20,7 +20,8 @@ import torch
 import oracle
 import sparse_kv_cache_append_amd as skv
 import workloads
-from gpu_harness import DEV, new_token as _new_token, prefilled_cache as _prefilled, quantized_host, rel_err
+from gpu_harness import (DEV, assert_close, new_token as _new_token, prefilled_cache as _prefilled,
+                         quantized_host, rel_err)
 
 pytestmark = pytest.mark.gpu
 
@@ -58,17 +59,19 @@ def _poison_rows(cache, pos):
             cache.v_scale[b, :, p] = float("nan")
 
 
-def _run_case(w, quest, append, S=None, max_seq=None, max_sel=None, poison=False, lag=0):
+def _run_case(w, quest, append, S=None, max_seq=None, max_sel=None, poison=False, lag=0,
+              tight=False, no_oracle=False):
     """``poison``: the append positions hold NaN / out-of-range data before the
     step; ``lag``: seq_len excludes the last ``lag`` tokens (with lag 1 the new
-    token lies past every walk)."""
+    token lies past every walk); ``tight``: max_len is the largest seq_len
+    (0 for an empty cache) instead of the largest L_b."""
     base = _prefilled(w, max_seq, whole=not append)
     if poison:
         _poison_rows(base, _new_token(w)[0])
     ca, cb = base.clone(), base.clone()
     q = torch.from_numpy(np.ascontiguousarray(w.q)).to(DEV)
     seq_len = torch.tensor([L - lag for L in w.lens], dtype=torch.int32, device=DEV)
-    max_len = max(w.lens)
+    max_len = max(w.lens) - (lag if tight else 0)
     ks = torch.tensor(w.k_sel, dtype=torch.int32, device=DEV) if quest else None
     if quest:
         max_sel = max_sel or (max(w.k_sel) + w.n_sink + w.n_recent)
@@ -96,14 +99,25 @@ def _run_case(w, quest, append, S=None, max_seq=None, max_sel=None, poison=False
     torch.cuda.synchronize()
     assert torch.equal(out_a, out_b)
     for ta, tb in zip(_cache_tensors(ca), _cache_tensors(cb)):
-        assert torch.equal(ta, tb)
+        assert torch.equal(ta.view(torch.uint8), tb.view(torch.uint8))     # bits (NaN rows too)
     if quest:
         assert torch.equal(sel_a, sel_b)
         assert torch.equal(cnt_a, cnt_b)
         for b, L in enumerate(w.lens):
             nb = -(-L // w.block)
-            assert torch.equal(sc_a[b, :, :nb], sc_b[b, :, :nb])
+            a_, b_ = sc_a[b, :, :nb], sc_b[b, :, :nb]
+            bad = (a_.view(torch.int32) != b_.view(torch.int32)).nonzero().tolist()
+            assert not bad, ("scores differ", b, bad[:8],
+                             [(float(a_[i, j]), float(b_[i, j])) for i, j in bad[:8]])
     return out_b.cpu().numpy(), (sel_b.cpu().numpy(), cnt_b.cpu().numpy()) if quest else None
+
+
+def _with_nan_key(w):
+    """Channels 3 and 77 of the last (appended) key are NaN in every KV head."""
+    for b, L in enumerate(w.lens):
+        w.k[b][:, L - 1, 3] = np.nan
+        w.k[b][:, L - 1, 77] = np.nan
+    return w
 
 
 def _oracle_check(w, out, sel):
@@ -119,13 +133,13 @@ def _oracle_check(w, out, sel):
         if w.kv_dtype == "f16":
             ref = oracle.attend_f16(w.q[0][hs], w.k[0][g:g + 1], w.v[0][g:g + 1],
                                     w.softmax_scale, tokens=toks)
-            assert rel_err(out[0, hs], ref) < 1e-3
+            assert_close(out[0, hs], ref, 1e-3)
         else:
             kc, ksc, vc, vsc = quantized_host(w, 0)
             sl = slice(g, g + 1)
             ref = oracle.attend_i8(w.q[0][hs], kc[sl], ksc[sl], vc[sl], vsc[sl],
                                    w.softmax_scale, tokens=toks)
-            assert rel_err(out[0, hs], ref) < 1e-4
+            assert_close(out[0, hs], ref, 1e-4)
 
 
 STEP_CASES = [
@@ -187,6 +201,22 @@ STEP_CASES = [
         523, 2, 32, 8, 128, [1, 129], "i8"), False, True, {"lag": 1}),
     ("dense-i8 no append", lambda: workloads.gaussian(
         511, 1, 32, 8, 128, [1000], "i8"), False, False, {}),
+    # the first token of an empty cache: seq_len 0, max_len 0, position 0 (the
+    # part that writes the row is found with at least one block per part)
+    ("dense-f16 first token of an empty cache", lambda: workloads.gaussian(
+        529, 2, 32, 8, 128, [1, 1], "f16"), False, True, {"lag": 1, "tight": True}),
+    ("dense-i8 first token of an empty cache", lambda: workloads.gaussian(
+        530, 1, 32, 4, 128, [1], "i8"), False, True, {"lag": 1, "tight": True}),
+    # a NaN channel in the appended key: every path leaves that channel out of
+    # the block's min/max (the new token itself is not attended: lag 1)
+    ("quest-f16 NaN channel in the new key", lambda: _with_nan_key(workloads.clustered(
+        [531, 532], 32, 8, 128, [3000, 4097], "f16", n_dirs=16, k_sel=[10, 12],
+        n_sink=1, n_recent=2)), True, True, {"lag": 1}),
+    ("quest-i8 NaN channel in the new key", lambda: _with_nan_key(workloads.clustered(
+        [533], 32, 4, 128, [5001], "i8", n_dirs=16, k_sel=[20], n_sink=1, n_recent=4)),
+        True, True, {"lag": 1}),
+    ("dense-f16 NaN channel in the new key", lambda: _with_nan_key(workloads.gaussian(
+        534, 2, 32, 8, 128, [700, 1025], "f16")), False, True, {"lag": 1}),
 ]
 
 
@@ -442,3 +472,31 @@ def test_decode_step_tie_classes(gpu_lib, k_sel):
         own = oracle.select_blocks(score[0, g], 512, k_sel, 1, 2)["sel"]
         assert np.array_equal(s_h[0, g, :c_h[0, g]], own), g
     _oracle_check(w, out.cpu().numpy(), (s_h, c_h))
+
+
+@pytest.mark.parametrize("kv_dtype,L,S", [("f16", 32768, 32), ("i8", 20000, 24), ("f16", 3000, 1)])
+def test_decode_attn_select_equals_select_then_decode(gpu_lib, kv_dtype, L, S):
+    """skv_decode_attn_select (selection folded into the attention prologue;
+    with S = 1 a part spans more than 64 entries and the selection runs as
+    its own kernel) writes the same list and partial states as select_topk +
+    decode_attn, bit for bit."""
+    _print("decode_attn_select", kv_dtype, L, S)
+    w = workloads.clustered([540], 32, 8, 128, [L], kv_dtype, n_dirs=32,
+                            k_sel=[(-(-L // 64)) // 4], n_sink=1, n_recent=2)
+    cache = _prefilled(w, whole=True)
+    q = torch.from_numpy(np.ascontiguousarray(w.q)).to(DEV)
+    seq_len = torch.tensor(w.lens, dtype=torch.int32, device=DEV)
+    ks = torch.tensor(w.k_sel, dtype=torch.int32, device=DEV)
+    max_sel = w.k_sel[0] + 3
+    _, ws_a, score, sel_a, cnt_a = _buffers(w, cache, True, max_sel, S)
+    _, ws_b, _, sel_b, cnt_b = _buffers(w, cache, True, max_sel, S)
+    ws_a.zero_()
+    ws_b.fill_(255)
+    skv.block_bounds(cache, q, seq_len, L, score)
+    skv.select_topk(score, seq_len, w.block, ks, w.n_sink, w.n_recent, sel_a, cnt_a)
+    skv.decode_attn(cache, q, seq_len, L, w.softmax_scale, S, ws_a, sel_a, cnt_a)
+    skv.decode_attn_select(cache, q, seq_len, L, w.softmax_scale, S, ws_b, score, ks, w.n_sink,
+                           w.n_recent, sel_b, cnt_b)
+    torch.cuda.synchronize()
+    assert torch.equal(sel_a, sel_b) and torch.equal(cnt_a, cnt_b)
+    assert torch.equal(ws_a, ws_b)
