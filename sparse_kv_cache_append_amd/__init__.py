@@ -24,7 +24,7 @@ import os
 from typing import Optional
 
 __all__ = ["load", "Cache", "SkvError", "kv_append", "block_bounds", "select_topk",
-           "decode_attn", "decode_step", "combine", "workspace_bytes", "status_str", "decode",
+           "decode_attn", "decode_attn_select", "decode_step", "combine", "workspace_bytes", "status_str", "decode",
            "SKV_F16", "SKV_F32", "SKV_I8", "LIB_PATH", "EXPORTS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libskv.so")
@@ -33,8 +33,8 @@ SKV_OK, SKV_EINVAL, SKV_ERANGE, SKV_EWORKSPACE, SKV_EUNSUPPORTED, SKV_EDEVICE = 
 SKV_F16, SKV_F32, SKV_I8 = 1, 2, 3
 
 EXPORTS = ("skv_max_blocks", "skv_kv_append", "skv_block_bounds", "skv_select_topk",
-           "skv_decode_attn", "skv_decode_step", "skv_combine", "skv_workspace_bytes",
-           "skv_status_str")
+           "skv_decode_attn", "skv_decode_attn_select", "skv_decode_step", "skv_combine",
+           "skv_workspace_bytes", "skv_status_str")
 
 
 class SkvCacheDesc(ctypes.Structure):
@@ -48,8 +48,9 @@ class SkvCacheDesc(ctypes.Structure):
 
 
 class SkvError(RuntimeError):
-    def __init__(self, call: str, status: int):
-        super().__init__(f"{call} failed: {status_str(status)} ({status})")
+    def __init__(self, call: str, status: int, detail: str = ""):
+        msg = f"{call} failed: {status_str(status)} ({status})"
+        super().__init__(msg + (f": {detail}" if detail else ""))
         self.status = status
 
 
@@ -73,6 +74,8 @@ def load(path: str = LIB_PATH):
         "skv_block_bounds": (I32, [desc, P, I32, P, I32, P, P]),
         "skv_select_topk": (I32, [P, P, I32, I32, I32, I32, P, I32, I32, I32, P, P, P, P]),
         "skv_decode_attn": (I32, [desc, P, I32, P, I32, P, P, I32, ctypes.c_float, I32, P, SZ, P, P]),
+        "skv_decode_attn_select": (I32, [desc, P, I32, P, I32, P, P, I32, I32, I32, P, P,
+                                         ctypes.c_float, I32, P, SZ, P]),
         "skv_decode_step": (I32, [desc, P, P, P, I32, P, I32, P, I32, P, I32, I32, I32, P, P, P,
                                    ctypes.c_float, I32, P, SZ, P, P]),
         "skv_combine": (I32, [P, I32, I32, I32, I32, P, P]),
@@ -87,8 +90,16 @@ def load(path: str = LIB_PATH):
     return lib
 
 
+_STATUS_NAMES = {SKV_OK: "SKV_OK", SKV_EINVAL: "SKV_EINVAL", SKV_ERANGE: "SKV_ERANGE",
+                 SKV_EWORKSPACE: "SKV_EWORKSPACE", SKV_EUNSUPPORTED: "SKV_EUNSUPPORTED",
+                 SKV_EDEVICE: "SKV_EDEVICE"}
+
+
 def status_str(status: int) -> str:
-    return load().skv_status_str(int(status)).decode()
+    try:
+        return load().skv_status_str(int(status)).decode()
+    except RuntimeError:          # library missing: name the code only
+        return _STATUS_NAMES.get(int(status), "unknown skv_status")
 
 
 def workspace_bytes(batch: int, n_heads: int, head_dim: int, n_split: int) -> int:
@@ -109,6 +120,55 @@ def _ptr(t) -> Optional[int]:
     if not t.is_contiguous():
         raise ValueError("tensor must be contiguous")
     return t.data_ptr()
+
+
+def _dtype_code(t) -> int:
+    """skv_dtype of a tensor's element type (0, which the C side rejects, for
+    any other type)."""
+    import torch
+    return {torch.float16: SKV_F16, torch.float32: SKV_F32, torch.int8: SKV_I8}.get(t.dtype, 0)
+
+
+def _need(call: str, ok: bool, what: str):
+    """Reject a malformed argument before anything is enqueued (SKV_EINVAL)."""
+    if not ok:
+        raise SkvError(call, SKV_EINVAL, what)
+
+
+def _is(t, dtype, shape) -> bool:
+    """t has element type dtype and the given shape (None entries: any size)."""
+    if t is None or t.dtype != dtype or t.dim() != len(shape):
+        return False
+    return all(s is None or int(d) == s for d, s in zip(t.shape, shape))
+
+
+def _check_rows(call: str, cache, k_new, v_new, n_new: Optional[int] = None):
+    """New rows: [batch][n_new][Hkv][D], k_new and v_new alike, float16 for an
+    f16 cache and float32 for an int8 cache (the C call checks the pair)."""
+    import torch
+    _need(call, k_new is not None and v_new is not None, "k_new and v_new are required")
+    _need(call, k_new.dim() == 4 and tuple(k_new.shape) == tuple(v_new.shape)
+          and k_new.dtype == v_new.dtype, "k_new and v_new must have one shape and dtype")
+    _need(call, _is(k_new, k_new.dtype, (cache.batch, n_new, cache.n_kv_heads, cache.head_dim)),
+          "k_new must be [batch][n_new][n_kv_heads][head_dim]")
+    _need(call, k_new.dtype in (torch.float16, torch.float32), "k_new must be float16 or float32")
+
+
+def _check_q(call: str, cache, q, seq_len):
+    import torch
+    _need(call, q is not None and _is(q, torch.float32, (cache.batch, None, cache.head_dim)),
+          "q must be float32 [batch][n_heads][head_dim]")
+    _need(call, _is(seq_len, torch.int32, (cache.batch,)), "seq_len must be int32 [batch]")
+
+
+def _check_sel(call: str, batch: int, n_kv: int, sel_idx, sel_cnt):
+    import torch
+    _need(call, (sel_idx is None) == (sel_cnt is None), "sel_idx and sel_cnt go together")
+    if sel_idx is not None:
+        _need(call, _is(sel_idx, torch.int32, (batch, n_kv, None)),
+              "sel_idx must be int32 [batch][n_kv_heads][max_sel]")
+        _need(call, _is(sel_cnt, torch.int32, (batch, n_kv)),
+              "sel_cnt must be int32 [batch][n_kv_heads]")
 
 
 def _stream(stream) -> Optional[int]:
@@ -170,14 +230,23 @@ class Cache:
 def kv_append(cache: Cache, pos0, k_new, v_new, stream=None):
     """Append n_new tokens per sequence: k_new, v_new [batch][n_new][Hkv][D]
     (float16 for an f16 cache, float32 for an int8 cache); pos0 int32 [batch]."""
+    import torch
+    call = "skv_kv_append"
+    _check_rows(call, cache, k_new, v_new)
+    _need(call, _is(pos0, torch.int32, (cache.batch,)), "pos0 must be int32 [batch]")
     n_new = int(k_new.shape[1])
-    _check("skv_kv_append", load().skv_kv_append(
+    _check(call, load().skv_kv_append(
         ctypes.byref(cache.desc), _ptr(pos0), n_new, _ptr(k_new), _ptr(v_new),
-        cache.src_dtype(), _stream(stream)))
+        _dtype_code(k_new), _stream(stream)))
 
 
 def block_bounds(cache: Cache, q, seq_len, max_len: int, score, stream=None):
     """score [batch][Hkv][max_blocks] <- group-max Quest bound of every block."""
+    import torch
+    _check_q("skv_block_bounds", cache, q, seq_len)
+    _need("skv_block_bounds", _is(score, torch.float32,
+                                  (cache.batch, cache.n_kv_heads, cache.max_blocks)),
+          "score must be float32 [batch][n_kv_heads][max_blocks]")
     _check("skv_block_bounds", load().skv_block_bounds(
         ctypes.byref(cache.desc), _ptr(q), int(q.shape[1]), _ptr(seq_len), int(max_len),
         _ptr(score), _stream(stream)))
@@ -186,7 +255,19 @@ def block_bounds(cache: Cache, q, seq_len, max_len: int, score, stream=None):
 def select_topk(score, seq_len, block: int, k_sel, n_sink: int, n_recent: int,
                 sel_idx, sel_cnt, sel_mask=None, stream=None):
     """Fixed top-K + sink + recent; sel_idx [batch][Hkv][max_sel] int32 ascending."""
+    import torch
+    call = "skv_select_topk"
+    _need(call, _is(score, torch.float32, (None, None, None)),
+          "score must be float32 [batch][n_kv_heads][max_blocks]")
     B, Hkv, max_blocks = (int(x) for x in score.shape)
+    _need(call, _is(seq_len, torch.int32, (B,)), "seq_len must be int32 [batch]")
+    _need(call, _is(k_sel, torch.int32, (B,)), "k_sel must be int32 [batch]")
+    _need(call, sel_idx is not None, "sel_idx and sel_cnt are required")
+    _check_sel(call, B, Hkv, sel_idx, sel_cnt)
+    if sel_mask is not None:
+        _need(call, sel_mask.dtype in (torch.int32, getattr(torch, "uint32", torch.int32))
+              and _is(sel_mask, sel_mask.dtype, (B, Hkv, -(-max_blocks // 32))),
+              "sel_mask must be 32-bit [batch][n_kv_heads][ceil(max_blocks/32)]")
     _check("skv_select_topk", load().skv_select_topk(
         _ptr(score), _ptr(seq_len), B, Hkv, max_blocks, int(block), _ptr(k_sel), int(n_sink),
         int(n_recent), int(sel_idx.shape[2]), _ptr(sel_idx), _ptr(sel_cnt), _ptr(sel_mask),
@@ -197,12 +278,41 @@ def decode_attn(cache: Cache, q, seq_len, max_len: int, softmax_scale: float, n_
                 workspace, sel_idx=None, sel_cnt=None, dbg_logits=None, stream=None):
     """Split-K partial states into ``workspace`` (uint8/float tensor of at least
     workspace_bytes(...) bytes)."""
+    import torch
+    call = "skv_decode_attn"
+    _check_q(call, cache, q, seq_len)
+    _check_sel(call, cache.batch, cache.n_kv_heads, sel_idx, sel_cnt)
+    if dbg_logits is not None:
+        _need(call, _is(dbg_logits, torch.int32, (cache.batch, int(q.shape[1]), None))
+              and int(dbg_logits.shape[2]) >= int(max_len),
+              "dbg_logits must be int32 [batch][n_heads][>= max_len]")
     max_sel = int(sel_idx.shape[2]) if sel_idx is not None else 0
-    _check("skv_decode_attn", load().skv_decode_attn(
+    _check(call, load().skv_decode_attn(
         ctypes.byref(cache.desc), _ptr(q), int(q.shape[1]), _ptr(seq_len), int(max_len),
         _ptr(sel_idx), _ptr(sel_cnt), max_sel, float(softmax_scale), int(n_split),
         _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(dbg_logits),
         _stream(stream)))
+
+
+def decode_attn_select(cache: Cache, q, seq_len, max_len: int, softmax_scale: float,
+                       n_split: int, workspace, score, k_sel, n_sink: int, n_recent: int,
+                       sel_idx, sel_cnt, stream=None):
+    """select_topk + decode_attn in one launch (the selection in the attention
+    kernel's prologue): sel_idx/sel_cnt receive the list, ``workspace`` the
+    split-K partial states."""
+    import torch
+    call = "skv_decode_attn_select"
+    _check_q(call, cache, q, seq_len)
+    _need(call, _is(k_sel, torch.int32, (cache.batch,)), "k_sel must be int32 [batch]")
+    _need(call, _is(score, torch.float32, (cache.batch, cache.n_kv_heads, cache.max_blocks)),
+          "score must be float32 [batch][n_kv_heads][max_blocks]")
+    _need(call, sel_idx is not None, "sel_idx and sel_cnt are required")
+    _check_sel(call, cache.batch, cache.n_kv_heads, sel_idx, sel_cnt)
+    _check(call, load().skv_decode_attn_select(
+        ctypes.byref(cache.desc), _ptr(q), int(q.shape[1]), _ptr(seq_len), int(max_len),
+        _ptr(score), _ptr(k_sel), int(n_sink), int(n_recent), int(sel_idx.shape[2]),
+        _ptr(sel_idx), _ptr(sel_cnt), float(softmax_scale), int(n_split), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 def decode_step(cache: Cache, q, seq_len, max_len: int, softmax_scale: float, n_split: int,
@@ -212,9 +322,24 @@ def decode_step(cache: Cache, q, seq_len, max_len: int, softmax_scale: float, n_
     append (k_new, v_new [batch][1][Hkv][D] at pos0), dense or Quest (k_sel)
     attention, combine into ``out``.  Quest needs score [batch][Hkv][max_blocks]
     scratch and sel_idx [batch][Hkv][max_sel] / sel_cnt [batch][Hkv] outputs."""
+    import torch
+    call = "skv_decode_step"
+    _check_q(call, cache, q, seq_len)
+    _need(call, _is(out, torch.float32, tuple(q.shape)), "out must be float32 like q")
+    src = 0
+    if k_new is not None:
+        _check_rows(call, cache, k_new, v_new, 1)
+        _need(call, _is(pos0, torch.int32, (cache.batch,)), "pos0 must be int32 [batch]")
+        src = _dtype_code(k_new)
+    if k_sel is not None:
+        _need(call, _is(k_sel, torch.int32, (cache.batch,)), "k_sel must be int32 [batch]")
+        _need(call, _is(score, torch.float32, (cache.batch, cache.n_kv_heads, cache.max_blocks)),
+              "score must be float32 [batch][n_kv_heads][max_blocks]")
+        _need(call, sel_idx is not None, "sel_idx and sel_cnt are required for Quest")
+        _check_sel(call, cache.batch, cache.n_kv_heads, sel_idx, sel_cnt)
     max_sel = int(sel_idx.shape[2]) if sel_idx is not None else 0
-    _check("skv_decode_step", load().skv_decode_step(
-        ctypes.byref(cache.desc), _ptr(pos0), _ptr(k_new), _ptr(v_new), cache.src_dtype(),
+    _check(call, load().skv_decode_step(
+        ctypes.byref(cache.desc), _ptr(pos0), _ptr(k_new), _ptr(v_new), src,
         _ptr(q), int(q.shape[1]), _ptr(seq_len), int(max_len), _ptr(k_sel), int(n_sink),
         int(n_recent), max_sel, _ptr(score), _ptr(sel_idx), _ptr(sel_cnt),
         float(softmax_scale), int(n_split), _ptr(workspace),
@@ -223,6 +348,9 @@ def decode_step(cache: Cache, q, seq_len, max_len: int, softmax_scale: float, n_
 
 def combine(workspace, batch: int, n_heads: int, head_dim: int, n_split: int, out, stream=None):
     """out [batch][n_heads][head_dim] float32 from the split-K partials."""
+    import torch
+    _need("skv_combine", _is(out, torch.float32, (batch, n_heads, head_dim)),
+          "out must be float32 [batch][n_heads][head_dim]")
     _check("skv_combine", load().skv_combine(
         _ptr(workspace), int(batch), int(n_heads), int(head_dim), int(n_split), _ptr(out),
         _stream(stream)))

@@ -181,3 +181,106 @@ def test_default_split_rule():
     assert ds(1, 8, 131, sparse=True) == 32
     assert ds(1, 1, 10 ** 6) == 256 and ds(1, 1, 10 ** 9, target_wgs=10 ** 6) == 4096
     assert ds(4096, 16, 1000) == 1
+
+
+# ------------------------------------------------- binding argument checks
+class _FakeCache:
+    """The attributes the binding reads from a Cache (no device memory: every
+    call below must be rejected before a pointer is taken)."""
+    def __init__(self, kv_dtype="f16", batch=2, n_kv_heads=4, head_dim=128, max_blocks=8):
+        self.kv_dtype, self.batch, self.n_kv_heads = kv_dtype, batch, n_kv_heads
+        self.head_dim, self.max_blocks, self.block = head_dim, max_blocks, 64
+        self.desc = desc(batch=batch, n_kv_heads=n_kv_heads)
+
+
+def _t(shape, dtype):
+    import torch
+    return torch.zeros(shape, dtype=dtype)
+
+
+def _rejected(fn):
+    with pytest.raises(skv.SkvError) as e:
+        fn()
+    assert e.value.status == skv.SKV_EINVAL
+
+
+def _reaches_pointers(fn):
+    """Validation passed: the binding got as far as taking device pointers
+    of these CPU tensors."""
+    with pytest.raises(ValueError, match="GPU"):
+        fn()
+
+
+def test_binding_checks_append_rows(lib):
+    import torch
+    c = _FakeCache("i8")
+    pos = _t((2,), torch.int32)
+    good = _t((2, 3, 4, 128), torch.float32)
+    _reaches_pointers(lambda: skv.kv_append(c, pos, good, good.clone()))
+    # the source dtype passed to C is the rows' own (a float16 row for an int8
+    # cache is then rejected by the C side, not read as float32)
+    _rejected(lambda: skv.kv_append(c, pos, good, _t((2, 3, 4, 128), torch.float16)))
+    _rejected(lambda: skv.kv_append(c, pos, _t((2, 3, 4, 128), torch.float64),
+                                    _t((2, 3, 4, 128), torch.float64)))
+    _rejected(lambda: skv.kv_append(c, pos, _t((2, 3, 4, 64), torch.float32),
+                                    _t((2, 3, 4, 64), torch.float32)))
+    _rejected(lambda: skv.kv_append(c, pos, _t((1, 3, 4, 128), torch.float32),
+                                    _t((1, 3, 4, 128), torch.float32)))
+    _rejected(lambda: skv.kv_append(c, _t((2,), torch.int64), good, good.clone()))
+    _rejected(lambda: skv.kv_append(c, _t((3,), torch.int32), good, good.clone()))
+
+
+def test_binding_checks_query_lengths_and_lists(lib):
+    import torch
+    c = _FakeCache()
+    q = _t((2, 8, 128), torch.float32)
+    sl = _t((2,), torch.int32)
+    ws = _t((1024,), torch.uint8)
+    _reaches_pointers(lambda: skv.decode_attn(c, q, sl, 64, 0.1, 2, ws))
+    _rejected(lambda: skv.decode_attn(c, q.half(), sl, 64, 0.1, 2, ws))
+    _rejected(lambda: skv.decode_attn(c, q, sl.long(), 64, 0.1, 2, ws))
+    _rejected(lambda: skv.decode_attn(c, _t((3, 8, 128), torch.float32), sl, 64, 0.1, 2, ws))
+    si, sc = _t((2, 4, 5), torch.int32), _t((2, 4), torch.int32)
+    _reaches_pointers(lambda: skv.decode_attn(c, q, sl, 64, 0.1, 2, ws, si, sc))
+    _rejected(lambda: skv.decode_attn(c, q, sl, 64, 0.1, 2, ws, si.long(), sc))
+    _rejected(lambda: skv.decode_attn(c, q, sl, 64, 0.1, 2, ws, si, None))
+    _rejected(lambda: skv.decode_attn(c, q, sl, 64, 0.1, 2, ws,
+                                      dbg_logits=_t((2, 8, 32), torch.int32)))
+    score = _t((2, 4, 8), torch.float32)
+    _reaches_pointers(lambda: skv.block_bounds(c, q, sl, 64, score))
+    _rejected(lambda: skv.block_bounds(c, q, sl, 64, _t((2, 4, 7), torch.float32)))
+    ks = _t((2,), torch.int32)
+    _reaches_pointers(lambda: skv.select_topk(score, sl, 64, ks, 1, 2, si, sc))
+    _rejected(lambda: skv.select_topk(score, sl, 64, ks.long(), 1, 2, si, sc))
+    _rejected(lambda: skv.select_topk(score.double(), sl, 64, ks, 1, 2, si, sc))
+    out = _t((2, 8, 128), torch.float32)
+    _reaches_pointers(lambda: skv.combine(ws, 2, 8, 128, 2, out))
+    _rejected(lambda: skv.combine(ws, 2, 8, 128, 2, out.half()))
+
+
+def test_binding_checks_decode_step(lib):
+    import torch
+    c = _FakeCache("f16")
+    q = _t((2, 8, 128), torch.float32)
+    sl = _t((2,), torch.int32)
+    ws = _t((1024,), torch.uint8)
+    out = _t((2, 8, 128), torch.float32)
+    rows = _t((2, 1, 4, 128), torch.float16)
+    pos = _t((2,), torch.int32)
+    _reaches_pointers(lambda: skv.decode_step(c, q, sl, 64, 0.1, 2, ws, out, pos0=pos,
+                                              k_new=rows, v_new=rows.clone()))
+    # two tokens where the step appends one
+    two = _t((2, 2, 4, 128), torch.float16)
+    _rejected(lambda: skv.decode_step(c, q, sl, 64, 0.1, 2, ws, out, pos0=pos, k_new=two,
+                                      v_new=two.clone()))
+    _rejected(lambda: skv.decode_step(c, q, sl, 64, 0.1, 2, ws, out, pos0=pos.long(),
+                                      k_new=rows, v_new=rows.clone()))
+    _rejected(lambda: skv.decode_step(c, q, sl, 64, 0.1, 2, ws, out.half()))
+    score = _t((2, 4, 8), torch.float32)
+    si, sc = _t((2, 4, 5), torch.int32), _t((2, 4), torch.int32)
+    ks = _t((2,), torch.int32)
+    _reaches_pointers(lambda: skv.decode_step(c, q, sl, 64, 0.1, 2, ws, out, k_sel=ks,
+                                              score=score, sel_idx=si, sel_cnt=sc))
+    _rejected(lambda: skv.decode_step(c, q, sl, 64, 0.1, 2, ws, out, k_sel=ks, score=score))
+    _rejected(lambda: skv.decode_step(c, q, sl, 64, 0.1, 2, ws, out, k_sel=ks.long(),
+                                      score=score, sel_idx=si, sel_cnt=sc))
