@@ -21,6 +21,40 @@ def rel_err(got, ref) -> float:
     return float(np.linalg.norm(got - ref) / (den if den > 0 else 1.0))
 
 
+def close_report(got, ref, tol: float) -> str:
+    """Element-wise parity of one output against its reference, '' when it
+    holds.  got, ref: [..., D] (a sequence's [H][D] output, a KV group's
+    [G][D] slice, or one head's [D]).  Three bars, each at ``tol``:
+      * Frobenius-relative over the whole array;
+      * per head (every row of the last axis): Frobenius-relative;
+      * per head: max |got - ref| <= tol * max |ref| (no single element of a
+        head may be off by more than tol of that head's largest value)."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    if not np.all(np.isfinite(got)):
+        return "non-finite output"
+    g2 = got.reshape(-1, got.shape[-1])
+    r2 = ref.reshape(-1, ref.shape[-1])
+    msgs = []
+    whole = rel_err(got, ref)
+    if not whole < tol:
+        msgs.append(f"whole {whole:.3g}")
+    for h in range(r2.shape[0]):
+        den = np.linalg.norm(r2[h])
+        fro = np.linalg.norm(g2[h] - r2[h]) / (den if den > 0 else 1.0)
+        mx = np.max(np.abs(r2[h]))
+        el = np.max(np.abs(g2[h] - r2[h])) / (mx if mx > 0 else 1.0)
+        if not (fro < tol and el <= tol):
+            msgs.append(f"head {h}: frobenius {fro:.3g}, max element {el:.3g}")
+    return "; ".join(msgs[:6])
+
+
+def assert_close(got, ref, tol: float, *ctx):
+    """Assert close_report(got, ref, tol) is clean; ctx names the case."""
+    rep = close_report(got, ref, tol)
+    assert rep == "", (ctx, tol, rep)
+
+
 def padded_rows(w, b_rows: int):
     """[B][b_rows][Hkv][D] source tensors for a one-call prefill of every
     sequence; sequence b is padded past L_b with copies of its last row, which

@@ -19,7 +19,7 @@ import torch
 
 import oracle
 import workloads
-from gpu_harness import (DEV, build_cache, device_inputs, quantized_host, rel_err, run_dense,
+from gpu_harness import (DEV, assert_close, build_cache, device_inputs, quantized_host, rel_err, run_dense,
                          run_select, run_sparse, sel_tensor_from_lists)
 
 import sparse_kv_cache_append_amd as skv
@@ -148,7 +148,7 @@ def test_dense_f16_matches_definition(gpu_lib, B, H, Hkv, lens, n_split):
     out, _ = run_dense(cache, w, n_split)
     for b in range(B):
         ref = oracle.attend_f16(w.q[b], w.k[b], w.v[b], w.softmax_scale)
-        assert rel_err(out[b], ref) < F16_TOL
+        assert_close(out[b], ref, F16_TOL)
 
 
 @pytest.mark.parametrize("B,H,Hkv,lens", [(1, 32, 8, [8192]), (2, 8, 2, [130, 777]),
@@ -164,7 +164,7 @@ def test_dense_i8_matches_method_and_contract(gpu_lib, B, H, Hkv, lens):
         assert np.array_equal(dbg[b, :, :lens[b]].astype(np.int64), dots)
         meth = oracle.attend_i8(w.q[b], kc, ks, vc, vs, w.softmax_scale)
         contract = oracle.attend_i8_dequant(w.q[b], kc, ks, vc, vs, w.softmax_scale)
-        assert rel_err(out[b], meth) < I8_TOL_METHOD
+        assert_close(out[b], meth, I8_TOL_METHOD)
         assert rel_err(out[b], contract) < contract_bar(meth, contract)
 
 
@@ -185,11 +185,11 @@ def test_tiles_per_wave_from_zero_to_five(gpu_lib, kv):
     for b in range(B):
         if kv == "f16":
             ref = oracle.attend_f16(w.q[b], w.k[b], w.v[b], w.softmax_scale)
-            assert rel_err(out[b], ref) < F16_TOL, WAVE_TILE_LENS[b]
+            assert_close(out[b], ref, F16_TOL, WAVE_TILE_LENS[b])
         else:
             kc, ks, vc, vs = quantized_host(w, b)
             meth = oracle.attend_i8(w.q[b], kc, ks, vc, vs, w.softmax_scale)
-            assert rel_err(out[b], meth) < I8_TOL_METHOD, WAVE_TILE_LENS[b]
+            assert_close(out[b], meth, I8_TOL_METHOD, WAVE_TILE_LENS[b])
 
 
 def _boundary_query(rng, H, D):
@@ -250,7 +250,7 @@ def test_zero_query_gives_mean_of_values(gpu_lib):
             _, _, vc, vs = quantized_host(w, 0)
             ref = (vc.astype(np.float64) * vs.astype(np.float64)[..., None]).mean(axis=1)
         for h in range(8):
-            assert rel_err(out[0, h], ref[h // 4]) < 1e-6
+            assert_close(out[0, h], ref[h // 4], 1e-6)
 
 
 def test_empty_and_single_token_sequences(gpu_lib):
@@ -261,7 +261,7 @@ def test_empty_and_single_token_sequences(gpu_lib):
     assert np.all(out[0] == 0)
     for h in range(8):
         np.testing.assert_array_equal(out[1, h], w.v[1][h // 4, 0].astype(np.float32))
-    assert rel_err(out[2], oracle.attend_f16(w.q[2], w.k[2], w.v[2], w.softmax_scale)) < F16_TOL
+    assert_close(out[2], oracle.attend_f16(w.q[2], w.k[2], w.v[2], w.softmax_scale), F16_TOL)
 
 
 def test_block_sizes_other_than_64(gpu_lib):
@@ -271,7 +271,7 @@ def test_block_sizes_other_than_64(gpu_lib):
         cache = build_cache(w)
         out, _ = run_dense(cache, w)
         for b in range(2):
-            assert rel_err(out[b], oracle.attend_f16(w.q[b], w.k[b], w.v[b], w.softmax_scale)) < F16_TOL
+            assert_close(out[b], oracle.attend_f16(w.q[b], w.k[b], w.v[b], w.softmax_scale), F16_TOL)
 
 
 # ------------------------------------------------------------------ combine
@@ -302,7 +302,7 @@ def test_combine_alone_matches_oracle_merge(gpu_lib, B, H, S):
     out = torch.empty((B, H, D), dtype=torch.float32, device=DEV)
     skv.combine(wst, B, H, D, S, out)
     torch.cuda.synchronize()
-    assert rel_err(out.cpu().numpy(), refs) < 1e-6
+    assert_close(out.cpu().numpy(), refs, 1e-6)
 
 
 # ------------------------------------------------------------------ quest
@@ -374,7 +374,7 @@ def test_sparse_attention_over_oracle_selection(gpu_lib, seeds, H, Hkv, lens, kv
                 if kv == "f16":
                     ref = oracle.attend_f16(w.q[b][hs], w.k[b][g:g + 1], w.v[b][g:g + 1],
                                             w.softmax_scale, tokens=toks)
-                    assert rel_err(out[b, hs], ref) < F16_TOL
+                    assert_close(out[b, hs], ref, F16_TOL)
                 else:
                     kc, ks, vc, vs = quantized_host(w, b)
                     sl = slice(g, g + 1)
@@ -382,7 +382,7 @@ def test_sparse_attention_over_oracle_selection(gpu_lib, seeds, H, Hkv, lens, kv
                                             w.softmax_scale, tokens=toks)
                     con = oracle.attend_i8_dequant(w.q[b][hs], kc[sl], ks[sl], vc[sl], vs[sl],
                                                    w.softmax_scale, tokens=toks)
-                    assert rel_err(out[b, hs], meth) < I8_TOL_METHOD
+                    assert_close(out[b, hs], meth, I8_TOL_METHOD)
                     assert rel_err(out[b, hs], con) < contract_bar(meth, con)
 
 
@@ -500,8 +500,8 @@ def test_invalid_selected_indices_are_skipped(gpu_lib):
         toks = oracle.selected_tokens(np.array(good[g]), 700, 64)
         ref = oracle.attend_f16(w.q[0][4 * g:4 * g + 4], w.k[0][g:g + 1], w.v[0][g:g + 1],
                                 w.softmax_scale, tokens=toks)
-        assert rel_err(a[0, 4 * g:4 * g + 4], ref) < F16_TOL
-        assert rel_err(b[0, 4 * g:4 * g + 4], ref) < F16_TOL
+        assert_close(a[0, 4 * g:4 * g + 4], ref, F16_TOL)
+        assert_close(b[0, 4 * g:4 * g + 4], ref, F16_TOL)
 
 
 def test_runs_are_bit_identical(gpu_lib):
@@ -525,7 +525,7 @@ def test_decode_helper_chains_the_calls(gpu_lib):
     cache = build_cache(w)
     q, seq_len = device_inputs(w)
     out = skv.decode(cache, q, seq_len, 3000).cpu().numpy()
-    assert rel_err(out[0], oracle.attend_f16(w.q[0], w.k[0], w.v[0], w.softmax_scale)) < F16_TOL
+    assert_close(out[0], oracle.attend_f16(w.q[0], w.k[0], w.v[0], w.softmax_scale), F16_TOL)
     ks = torch.tensor([12], dtype=torch.int32, device=DEV)
     outq = skv.decode(cache, q, seq_len, 3000, k_sel=ks).cpu().numpy()
     # the list the helper used (the same deterministic calls): equal to the
@@ -541,7 +541,7 @@ def test_decode_helper_chains_the_calls(gpu_lib):
         toks = oracle.selected_tokens(got, 3000, 64)
         ref = oracle.attend_f16(w.q[0][4 * g:4 * g + 4], w.k[0][g:g + 1], w.v[0][g:g + 1],
                                 w.softmax_scale, tokens=toks)
-        assert rel_err(outq[0, 4 * g:4 * g + 4], ref) < F16_TOL
+        assert_close(outq[0, 4 * g:4 * g + 4], ref, F16_TOL)
 
 
 # ------------------------------------------------------------------ HIP graphs
