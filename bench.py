@@ -19,13 +19,19 @@ Timing protocol:
   consecutive steps touch more than twice the 256 MB last-level cache.
 * W warmup steps, then exactly K steps captured in one HIP graph
   (torch.cuda.CUDAGraph over the library's launches), replayed once
-  untimed and once timed between synchronizations; the stream-launch time
-  of K eager steps is reported too.
+  untimed, then 5 times, each replay bracketed by HIP events on the replay
+  stream; the median replay / K is the time per step.  The stream-launch
+  time of K eager steps is reported too.
 * Warm cache (secondary, headline steps only): the same K-step graph on one
   copy of the cache, so a step's bytes may stay in the last-level cache.
-* The dominant kernel (decode_attn) is timed alone the same way (K launches
-  in one graph), with HIP events on the replay stream; achieved GB/s =
-  algorithmic bytes per launch / average launch time.
+* The dominant kernel is timed alone the same way (K launches in one
+  graph, median of 5 event-timed replays): for the Quest step its own
+  attention kernel, decode_attn_select (selection in the prologue), and
+  decode_attn over the given list beside it; achieved GB/s = algorithmic
+  bytes per launch / average launch time.
+* The CPU baseline: the float64 oracle's step of every timed workload on
+  a bounded sample of its (sequence, KV head) units, on one core and on a
+  pool of up to 16 cores, scaled to one step, run before the GPU is used.
 
 Prints ONE JSON line (one GPU).
 """
@@ -121,54 +127,153 @@ def recorded_traffic(kernel: str):
 
 
 # ------------------------------------------------------------- cpu baseline
-def cpu_baseline(w, budget_s: float = 12.0):
-    """The oracle's Quest step (append the token, bounds, selection, sparse
-    attention) on the host cores, single-threaded, repeated for ~budget_s."""
-    import oracle
-    try:
-        from threadpoolctl import threadpool_limits
-        limiter = threadpool_limits(limits=1)
-    except Exception:  # pragma: no cover - threadpoolctl is in the image
-        limiter = None
-    L = w.lens[0]
-    keys, vals, q = w.k[0], w.v[0], w.q[0]
+CPU_POOL_MAX = 16          # the GPU machine's CPU share for one GPU
 
-    def step():
-        # append: the new token's row joins its block's bounds (from scratch is
-        # the same bytes, by exactness of min/max)
-        kmin, kmax = oracle.block_bounds(keys, L, w.block)
-        sc = oracle.group_scores(oracle.upper_bounds(q, kmin, kmax), w.Hkv)
-        out = np.zeros((w.H, w.D))
-        for g in range(w.Hkv):
-            r = oracle.select_blocks(sc[g], w.n_blocks(0), w.k_sel[0], w.n_sink, w.n_recent)
-            toks = oracle.selected_tokens(r["sel"], L, w.block)
-            hs = slice(g * w.G, (g + 1) * w.G)
-            out[hs] = oracle.attend_f16(q[hs], keys[g:g + 1], vals[g:g + 1], w.softmax_scale,
-                                        tokens=toks)
-        return out
 
-    n = 0
-    t0 = time.perf_counter()
-    while True:
-        step()
-        n += 1
-        if time.perf_counter() - t0 > budget_s or n >= 50:
-            break
-    dt = (time.perf_counter() - t0) / n
-    if limiter is not None:
-        limiter.unregister() if hasattr(limiter, "unregister") else None
-    cpu = "unknown"
+def _cpu_model() -> str:
     try:
         for line in open("/proc/cpuinfo"):
             if line.startswith("model name"):
-                cpu = line.split(":", 1)[1].strip()
-                break
+                return line.split(":", 1)[1].strip()
     except OSError:
         pass
-    return {"value": dt * 1e6, "unit": "us/step", "cores": 1, "kind": "oracle",
-            "sample": f"{n} full Quest steps of the same workload (float64 NumPy oracle: "
-                      f"bounds with exact sums, selection, attention over the selected "
-                      f"blocks), one thread, on {cpu}"}
+    return "unknown"
+
+
+def _one_thread():
+    """Limit the BLAS pools of this process to one thread."""
+    try:
+        from threadpoolctl import threadpool_limits
+        return threadpool_limits(limits=1)
+    except Exception:  # pragma: no cover - threadpoolctl is in the image
+        return None
+
+
+class OracleStep:
+    """The oracle's decode step of one workload, split into its independent
+    (sequence, KV head) units: dense attention of the unit's G query heads,
+    or the Quest pipeline of the unit (the appended token's block bounds,
+    the upper bounds of every block for the G heads, their max, the top-K
+    selection, attention over the selected blocks).  The cache state (the
+    side cache before the step, the int8 codes and scales) is prepared
+    outside the timed region: it is the cache the step finds in memory."""
+
+    def __init__(self, w, quest: bool):
+        import oracle
+        self.w, self.quest, self.oracle = w, quest, oracle
+        self.units = [(b, g) for b in range(w.B) for g in range(w.Hkv)]
+        self.kmin, self.kmax, self.codes = {}, {}, {}
+        for b in range(w.B):
+            L = w.lens[b]
+            if quest:
+                # the side cache as it stands before the step (tokens < L - 1)
+                mn, mx = oracle.block_bounds(w.k[b][:, :L - 1], L - 1, w.block) if L > 1 else (
+                    None, None)
+                self.kmin[b], self.kmax[b] = mn, mx
+            if w.kv_dtype == "i8":
+                kc, ks = oracle.quantize_rows(w.k[b])
+                vc, vs = oracle.quantize_rows(w.v[b])
+                self.codes[b] = (kc, ks, vc, vs)
+
+    def unit(self, bg):
+        o, w = self.oracle, self.w
+        b, g = bg
+        L = w.lens[b]
+        hs = slice(g * w.G, (g + 1) * w.G)
+        q = w.q[b][hs]
+        toks = None
+        if self.quest:
+            # append: the new token's block, min/max-merged (from scratch over
+            # the block is the same bytes, min and max being exact)
+            j = (L - 1) // w.block
+            bmn, bmx = o.block_bounds(w.k[b][g:g + 1, j * w.block:L], L - j * w.block, w.block)
+            if self.kmin[b] is None:
+                mn, mx = bmn, bmx
+            else:
+                # the token's block replaces the old one, or starts a new one
+                mn = np.concatenate([self.kmin[b][g:g + 1, :j], bmn], axis=1)
+                mx = np.concatenate([self.kmax[b][g:g + 1, :j], bmx], axis=1)
+            sc = o.group_scores(o.upper_bounds(q, mn, mx), 1)[0]
+            r = o.select_blocks(sc, w.n_blocks(b), w.k_sel[b], w.n_sink, w.n_recent)
+            toks = o.selected_tokens(r["sel"], L, w.block)
+        if w.kv_dtype == "f16":
+            return o.attend_f16(q, w.k[b][g:g + 1], w.v[b][g:g + 1], w.softmax_scale, tokens=toks)
+        kc, ks, vc, vs = self.codes[b]
+        sl = slice(g, g + 1)
+        return o.attend_i8(q, kc[sl], ks[sl], vc[sl], vs[sl], w.softmax_scale, tokens=toks)
+
+
+_POOL_STEP = None
+
+
+_POOL_LIMIT = None
+
+
+def _pool_init():
+    global _POOL_LIMIT
+    _POOL_LIMIT = _one_thread()
+
+
+def _pool_noop(i):
+    return i
+
+
+def _pool_unit(i):
+    t0 = time.perf_counter()
+    _POOL_STEP.unit(_POOL_STEP.units[i])
+    return time.perf_counter() - t0
+
+
+def cpu_baseline(w, quest: bool, budget_s: float = 4.0):
+    """The oracle's step of workload w on the host cores, on a bounded sample
+    of its (sequence, KV head) units, scaled to one whole step:
+    * one core: units run one after another on one thread, until budget_s
+      has passed (at least one unit); us/step = mean unit time x units;
+    * all cores: a pool of min(cores, units) forked workers (one thread
+      each) runs one unit per worker at once (best of up to 3 rounds);
+      us/step = wall time x ceil(units / workers).
+    Runs before the GPU is touched (the pool forks this process)."""
+    import multiprocessing as mp
+    global _POOL_STEP
+    st = OracleStep(w, quest)
+    n = len(st.units)
+    lim = _one_thread()
+    times = []
+    t_all = time.perf_counter()
+    for i in range(n):
+        t0 = time.perf_counter()
+        st.unit(st.units[i])
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() - t_all > budget_s:
+            break
+    if lim is not None and hasattr(lim, "unregister"):
+        lim.unregister()
+    one = sum(times) / len(times) * n
+    cores = max(1, min(len(os.sched_getaffinity(0)), CPU_POOL_MAX))
+    workers = min(cores, n)
+    _POOL_STEP = st
+    ctx = mp.get_context("fork")
+    with ctx.Pool(workers, initializer=_pool_init) as pool:
+        pool.map(_pool_noop, range(4 * workers), chunksize=1)     # workers up
+        wall = float("inf")
+        t_end = time.perf_counter() + budget_s
+        for rep in range(3):                                      # best of up to 3
+            t0 = time.perf_counter()
+            pool.map(_pool_unit, range(workers), chunksize=1)
+            wall = min(wall, time.perf_counter() - t0)
+            if time.perf_counter() > t_end:
+                break
+    _POOL_STEP = None
+    allc = wall * math.ceil(n / workers)
+    what = ("Quest step (append's block bounds, upper bounds, group max, top-K, attention "
+            "over the selected blocks)" if quest else "dense attention")
+    return {"workload": w.name, "step": "quest" if quest else "dense", "units": n,
+            "one_core": {"value": round(one * 1e6, 1), "unit": "us/step", "cores": 1,
+                         "sample": f"{len(times)} of {n} (sequence, KV head) units, scaled"},
+            "all_cores": {"value": round(allc * 1e6, 1), "unit": "us/step", "cores": workers,
+                          "sample": f"{workers} units at once on {workers} workers, scaled "
+                                    f"x{math.ceil(n / workers)}"},
+            "what": f"float64 NumPy oracle, {what}"}
 
 
 # ------------------------------------------------------------- GPU bench
@@ -176,10 +281,14 @@ class Timer:
     """Graph- and stream-timed replays of a step function f(i) over a ring of
     R cache copies (step i reads copy i % R)."""
 
+    REPS = 5
+
     def __init__(self, torch, R, steps, warmup, use_graph):
         self.torch, self.R, self.K, self.W, self.use_graph = torch, R, steps, warmup, use_graph
 
     def stream(self, fn):
+        """Host wall time per step of K eager steps (launch-bound when a step's
+        GPU time is below the host's launch time)."""
         torch = self.torch
         for i in range(self.W):
             fn(i)
@@ -190,59 +299,72 @@ class Timer:
         torch.cuda.synchronize()
         return (time.perf_counter() - t0) / self.K
 
+    def _replays(self, g, st):
+        """Median over REPS timed replays of graph g on stream st, HIP events
+        recorded on st around each replay; seconds per replay."""
+        torch = self.torch
+        ts = []
+        with torch.cuda.stream(st):
+            g.replay()                                   # untimed
+            for _ in range(self.REPS):
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(st)
+                g.replay()
+                e1.record(st)
+                st.synchronize()
+                ts.append(e0.elapsed_time(e1) * 1e-3)
+        return float(np.median(ts))
+
     def graph(self, fn):
-        """Wall time per step of exactly K steps captured in one HIP graph
-        (step i reads copy i % R), replayed once untimed, then once timed.
-        Returns (None, K) when graphs are off."""
+        """Device time per step of exactly K steps captured in one HIP graph
+        (step i reads copy i % R): median of REPS replays, each bracketed by
+        HIP events on the replay stream.  Returns (None, K) when graphs are
+        off."""
         if not self.use_graph:
             return None, self.K
         torch, R, K = self.torch, self.R, self.K
-        for i in range(max(self.W, R)):
-            fn(i)
-        torch.cuda.synchronize()
+        st = torch.cuda.Stream()
+        with torch.cuda.stream(st):
+            for i in range(max(self.W, R)):
+                fn(i)
+        st.synchronize()
         g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
+        with torch.cuda.graph(g, stream=st):
             for i in range(K):
                 fn(i)
-        g.replay()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        g.replay()
-        torch.cuda.synchronize()
-        dt = (time.perf_counter() - t0) / K
+        dt = self._replays(g, st) / K
         del g
         return dt, K
 
     def kernel(self, fn):
-        """Average duration of one launch of fn, HIP events on the launch
-        stream around K launches (graph-replayed when graphs are on)."""
+        """Average duration of one launch of fn (K launches in one graph,
+        median of REPS replays, HIP events on the launch stream)."""
         torch, R, K = self.torch, self.R, self.K
         st = torch.cuda.Stream()
         with torch.cuda.stream(st):
             for i in range(R):
                 fn(i)
         st.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         if not self.use_graph:
-            with torch.cuda.stream(st):
-                e0.record(st)
-                for i in range(K):
-                    fn(i)
-                e1.record(st)
-            st.synchronize()
-            return e0.elapsed_time(e1) * 1e3 / K
+            ts = []
+            for _ in range(self.REPS):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                with torch.cuda.stream(st):
+                    e0.record(st)
+                    for i in range(K):
+                        fn(i)
+                    e1.record(st)
+                st.synchronize()
+                ts.append(e0.elapsed_time(e1) * 1e3 / K)
+            return float(np.median(ts))
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=st):
             for i in range(K):
                 fn(i)
-        with torch.cuda.stream(st):
-            g.replay()
-            e0.record(st)
-            g.replay()
-            e1.record(st)
-        st.synchronize()
+        dt = self._replays(g, st) * 1e6 / K
         del g
-        return e0.elapsed_time(e1) * 1e3 / K
+        return dt
 
 
 def padded_prefill(w, rows):
@@ -379,6 +501,11 @@ def measure(w, args, quest: bool, dense: bool, detail: bool = False):
         dec_bytes = qb["kv"] + B * H * D * 4
         dec_us = T.kernel(lambda i: skv.decode_attn(caches[i % R], q, seq_len, Lmax,
                                                     w.softmax_scale, S_q, ws_q, sel, cnt))
+        # the step's own attention kernel: the selection folded into its
+        # prologue (the scores are the step's, identical for every copy)
+        sel_us = T.kernel(lambda i: skv.decode_attn_select(
+            caches[i % R], q, seq_len, Lmax, w.softmax_scale, S_q, ws_q, score, ks, w.n_sink,
+            w.n_recent, sel, cnt))
         n_att = sum(len(x) for x in attended.values())
         n_all = sum(-(-L // blk) for L in w.lens) * Hkv
         res["quest"] = {"us_per_step": round(us, 3), "stream_us_per_step": round(st * 1e6, 3),
@@ -391,11 +518,14 @@ def measure(w, args, quest: bool, dense: bool, detail: bool = False):
                         "decode_attn_us": round(dec_us, 3),
                         "decode_attn_GBps": round(dec_bytes / dec_us / 1e3, 1),
                         "decode_attn_pct_peak": round(100 * dec_bytes / dec_us / 1e3
-                                                      / HBM_PEAK_GBPS, 2)}
+                                                      / HBM_PEAK_GBPS, 2),
+                        "decode_attn_select_us": round(sel_us, 3),
+                        "decode_attn_select_pct_peak": round(100 * dec_bytes / sel_us / 1e3
+                                                             / HBM_PEAK_GBPS, 2)}
         if warm is not None:
             res["quest"]["warm_us_per_step"] = round(warm, 3)
         if detail:
-            res["_roofline"] = (dec_bytes, dec_us)
+            res["_roofline"] = (dec_bytes, sel_us, dec_us)
         if "dense" in res:
             res["quest_over_dense"] = round(res["quest"]["us_per_step"]
                                             / res["dense"]["us_per_step"], 4)
@@ -430,35 +560,50 @@ def main():
               "multi-GPU mode in this build", file=sys.stderr)
         sys.exit(2)
 
+    import workloads
+
+    # the workloads, drawn once (host arrays) for the CPU baseline and the GPU
+    jobs = [(workloads.named(3), args.mode in ("both", "quest"),
+             args.mode in ("both", "dense"), True)]
+    for tok in [t.strip() for t in args.workloads.split(",") if t.strip()]:
+        if tok.startswith("3@"):
+            # the 32K generator at another length (Quest vs dense from 16K up)
+            jobs.append((workloads.quest32k_at(int(tok[2:])), True, True, False))
+        elif int(tok) != 3:
+            w = workloads.named(int(tok))
+            jobs.append((w, bool(w.k_sel), True, False))
+
+    # the oracle on the host cores, before anything touches the GPU (its
+    # all-cores leg forks this process)
+    cpu_rows = []
+    if not args.no_cpu:
+        for w, quest, dense, _ in jobs:
+            if quest:
+                cpu_rows.append(cpu_baseline(w, quest=True))
+            if dense:
+                cpu_rows.append(cpu_baseline(w, quest=False))
+
     import torch
     import sparse_kv_cache_append_amd as skv
-    import workloads
 
     skv.load()
     torch.cuda.set_device(0)
-    w3 = workloads.named(3)
-    do_q, do_d = args.mode in ("both", "quest"), args.mode in ("both", "dense")
-    head = measure(w3, args, quest=do_q, dense=do_d, detail=True)
+    w3 = jobs[0][0]
+    head = None
     others = []
-    for tok in [t for t in args.workloads.split(",") if t.strip()]:
-        if tok.strip().startswith("3@"):
-            # the 32K generator at another length (Quest vs dense from 16K up)
-            w = workloads.quest32k_at(int(tok.strip()[2:]))
-            others.append(measure(w, args, quest=True, dense=True))
-            del w
-            continue
-        cfg = int(tok)
-        if cfg == 3:
-            continue
-        w = workloads.named(cfg)
-        others.append(measure(w, args, quest=bool(w.k_sel), dense=True))
-        del w
+    for w, quest, dense, detail in jobs:
+        r = measure(w, args, quest=quest, dense=dense, detail=detail)
+        if detail:
+            head = r
+        else:
+            others.append(r)
 
     hq, hd = head.get("quest"), head.get("dense")
     top = hq if hq is not None else hd
     if hq is not None:
-        rk = "decode_f16_mfma (decode_attn over the selected blocks)"
-        rb, rus = head["_roofline"]
+        rk = ("decode_f16_mfma, selection in the prologue (decode_attn_select over the "
+              "selected blocks: the Quest step's attention kernel)")
+        rb, rus, _ = head["_roofline"]
     else:
         rk = "decode_f16_mfma (decode_attn, dense)"
         rus = hd["decode_attn_us"]
@@ -505,8 +650,16 @@ def main():
             b2.copy_(a)
         torch.cuda.synchronize()
         res["copy_probe_bytes"] = {"read": a.numel() * 4, "written": a.numel() * 4}
-    if not args.no_cpu:
-        res["cpu_baseline"] = cpu_baseline(w3)
+    if cpu_rows:
+        top_cpu = cpu_rows[0]
+        res["cpu_baseline"] = {
+            "value": top_cpu["all_cores"]["value"], "unit": "us/step",
+            "cores": top_cpu["all_cores"]["cores"], "kind": "oracle",
+            "sample": f"{top_cpu['workload']} {top_cpu['step']} step: "
+                      f"{top_cpu['all_cores']['sample']}; {top_cpu['what']}",
+            "cpu_model": _cpu_model(),
+            "single_core": top_cpu["one_core"],
+            "per_config": cpu_rows}
     print(json.dumps(res), flush=True)
 
 

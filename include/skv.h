@@ -225,6 +225,36 @@ skv_status skv_decode_attn(const skv_cache* c, const float* q, int32_t n_heads,
                            int32_t* dbg_logits, hipStream_t stream);
 
 /*
+ * skv_decode_attn_select — skv_select_topk followed by skv_decode_attn over
+ * the selected list, with the selection folded into the attention kernel's
+ * prologue: one launch instead of two, and no round trip of the list through
+ * memory before the first K/V load.  Defines: sparse_attn.md, "Open
+ * questions" (computing the selector as its own small operator or folding it
+ * into the attention launch) and "Method" (the selection and the kernel
+ * skip).  Every part of a (sequence, KV head) recomputes the row's selection
+ * (bit-identical to skv_select_topk's) and walks its share of the list.
+ * The results -- the workspace's partial states, sel_idx, sel_cnt -- are
+ * bit-identical to
+ *     skv_select_topk(score, seq_len, batch, n_kv_heads, max_blocks, block,
+ *                     k_sel, n_sink, n_recent, max_sel, sel_idx, sel_cnt, NULL)
+ *     skv_decode_attn(c, q, n_heads, seq_len, max_len, sel_idx, sel_cnt,
+ *                     max_sel, softmax_scale, n_split, workspace,
+ *                     workspace_bytes, NULL)
+ * with max_blocks = skv_max_blocks(c).  The fold applies when max_blocks <=
+ * 4096 and ceil(max_sel / n_split) <= 64; otherwise the two kernels run one
+ * after the other (same results).
+ *   Arguments as in skv_select_topk (score, k_sel, n_sink, n_recent,
+ *   max_sel, sel_idx, sel_cnt) and skv_decode_attn (the rest).
+ * Errors: those of the two calls, checked before any launch.
+ */
+skv_status skv_decode_attn_select(const skv_cache* c, const float* q, int32_t n_heads,
+                                  const int32_t* seq_len, int32_t max_len, const float* score,
+                                  const int32_t* k_sel, int32_t n_sink, int32_t n_recent,
+                                  int32_t max_sel, int32_t* sel_idx, int32_t* sel_cnt,
+                                  float softmax_scale, int32_t n_split, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream);
+
+/*
  * skv_combine — merge the split-K partial states into the output.
  * Defines: M = max_i m_i; out = sum_i 2^(m_i - M) o_i / sum_i 2^(m_i - M) l_i
  * over the non-empty parts (the numerator/mass form of a split softmax).  A

@@ -74,8 +74,9 @@ def int8_logit_dots(q: np.ndarray, k_codes: np.ndarray):
     Hkv = k_codes.shape[0]
     G = H // Hkv
     dots = np.empty((H, k_codes.shape[1]), dtype=np.int64)
-    for h in range(H):
-        dots[h] = k_codes[h // G].astype(np.int64) @ q_codes[h].astype(np.int64)
+    for g in range(Hkv):
+        hs = slice(g * G, (g + 1) * G)
+        dots[hs] = (k_codes[g].astype(np.int64) @ q_codes[hs].astype(np.int64).T).T
     return dots, q_codes, q_scale
 
 
@@ -87,21 +88,21 @@ def attend_i8(q, k_codes, k_scale, v_codes, v_scale, scale, tokens=None):
     q [H][D] f32; codes [Hkv][L][D] int8; scales [Hkv][L] f32.  Returns [H][D]
     float64.
     """
-    dots, _, q_scale = int8_logit_dots(q, k_codes)
     H, D = q.shape
     Hkv = k_codes.shape[0]
     G = H // Hkv
+    idx = np.arange(k_codes.shape[1]) if tokens is None else np.asarray(tokens)
     out = np.zeros((H, D), dtype=np.float64)
-    for h in range(H):
-        g = h // G
-        idx = np.arange(k_codes.shape[1]) if tokens is None else np.asarray(tokens)
-        if idx.size == 0:
-            continue
-        logit = (dots[h, idx].astype(np.float64) * np.float64(q_scale[h])
-                 * k_scale[g, idx].astype(np.float64) * np.float64(scale))
-        p = _softmax_weights(logit)
+    if idx.size == 0:
+        return out
+    dots, _, q_scale = int8_logit_dots(q, k_codes[:, idx])
+    for g in range(Hkv):
         vd = v_codes[g, idx].astype(np.float64) * v_scale[g, idx].astype(np.float64)[:, None]
-        out[h] = p @ vd
+        ksg = k_scale[g, idx].astype(np.float64)
+        for h in range(g * G, (g + 1) * G):
+            logit = (dots[h].astype(np.float64) * np.float64(q_scale[h]) * ksg
+                     * np.float64(scale))
+            out[h] = _softmax_weights(logit) @ vd
     return out
 
 

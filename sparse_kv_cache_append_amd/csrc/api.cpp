@@ -238,6 +238,54 @@ skv_status skv_decode_step(const skv_cache* c, const int32_t* pos0, const void* 
                                            n_heads, c->head_dim, n_split, out, stream));
 }
 
+skv_status skv_decode_attn_select(const skv_cache* c, const float* q, int32_t n_heads,
+                                  const int32_t* seq_len, int32_t max_len, const float* score,
+                                  const int32_t* k_sel, int32_t n_sink, int32_t n_recent,
+                                  int32_t max_sel, int32_t* sel_idx, int32_t* sel_cnt,
+                                  float softmax_scale, int32_t n_split, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream) {
+  skv_status st = check_cache(c, false);
+  if (st != SKV_OK) return st;
+  if (q == nullptr || seq_len == nullptr || !aligned(q)) return SKV_EINVAL;
+  st = check_heads(c, n_heads);
+  if (st != SKV_OK) return st;
+  if (score == nullptr || k_sel == nullptr || sel_idx == nullptr || sel_cnt == nullptr)
+    return SKV_EINVAL;
+  if (n_sink < 0 || n_recent < 0 || max_sel < 1) return SKV_EINVAL;
+  const int32_t max_blocks = blocks_of(c->max_seq, c->block);
+  if (max_blocks > kMaxSelectBlocks) return SKV_EUNSUPPORTED;
+  if (n_split < 1 || n_split > kMaxSplit) return SKV_EINVAL;
+  if (!grid_fits(n_split, c->n_kv_heads, c->batch)) return SKV_ERANGE;
+  if (!(softmax_scale == softmax_scale) || softmax_scale < 0.0f) return SKV_EINVAL;
+  if (max_len < 0 || max_len > c->max_seq) return SKV_ERANGE;
+  const size_t need = skv_workspace_bytes(c->batch, n_heads, c->head_dim, n_split);
+  if (workspace == nullptr || workspace_bytes < need) return SKV_EWORKSPACE;
+  skv::DecodeParams p;
+  p.c = c;
+  p.q = q;
+  p.n_heads = n_heads;
+  p.seq_len = seq_len;
+  p.max_len = max_len;
+  p.sel_idx = sel_idx;
+  p.sel_cnt = sel_cnt;
+  p.max_sel = max_sel;
+  p.softmax_scale = softmax_scale;
+  p.n_split = n_split;
+  p.ws = static_cast<float*>(workspace);
+  p.dbg_logits = nullptr;
+  const int32_t ups = (max_sel + n_split - 1) / n_split;
+  if (max_blocks <= skv::kFusedSelMaxCand && ups <= 64) {
+    p.fused_r = skv::fused_sel_chunks(std::max(max_blocks - n_sink, 1));
+    p.fsel = skv::FusedSelect{score, max_blocks, k_sel, n_sink, n_recent, sel_idx, sel_cnt};
+  } else {
+    const hipError_t e = skv::launch_select(score, seq_len, c->batch, c->n_kv_heads, max_blocks,
+                                            c->block, k_sel, n_sink, n_recent, max_sel, sel_idx,
+                                            sel_cnt, nullptr, stream);
+    if (e != hipSuccess) return SKV_EDEVICE;
+  }
+  return device_status(skv::launch_decode(p, stream));
+}
+
 skv_status skv_combine(const void* workspace, int32_t batch, int32_t n_heads, int32_t head_dim,
                        int32_t n_split, float* out, hipStream_t stream) {
   if (workspace == nullptr || out == nullptr) return SKV_EINVAL;
