@@ -314,6 +314,38 @@ skv_status skv_decode_step(const skv_cache* c, const int32_t* pos0, const void* 
                            float softmax_scale, int32_t n_split, void* workspace,
                            size_t workspace_bytes, float* out, hipStream_t stream);
 
+/*
+ * skv_decode_step_static — skv_decode_step without caller scratch buffers.
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the score
+ * row and the split-K workspace come from a fixed array inside the library,
+ * skv_static_scratch_bytes() bytes (16 MiB) per GPU, held by each GPU the
+ * library runs on from the first call there until the process ends.  The
+ * call allocates nothing; the caller still passes every input and output.
+ *   Arguments and results are those of skv_decode_step (same kernels, same
+ *   bits), without score, workspace and workspace_bytes.
+ *   Capacity: 4 * batch * n_heads * n_split * (head_dim + 2) bytes of
+ *   workspace, plus (Quest only) 4 * batch * n_kv_heads * max_blocks bytes of
+ *   scores rounded up to 256, must fit in the array; larger calls return
+ *   SKV_ERANGE before anything is enqueued.
+ *   Concurrency: every call on one GPU uses the same array, so calls that may
+ *   overlap on one GPU (different streams without ordering between them)
+ *   race; calls ordered on one stream are safe.  Nothing in the array needs
+ *   clearing between calls: each call writes what it reads.
+ * Errors: those of skv_decode_step, SKV_ERANGE for a call beyond the array,
+ * SKV_EDEVICE if the array's device address cannot be obtained.
+ */
+skv_status skv_decode_step_static(const skv_cache* c, const int32_t* pos0, const void* k_new,
+                                  const void* v_new, int32_t src_dtype, const float* q,
+                                  int32_t n_heads, const int32_t* seq_len, int32_t max_len,
+                                  const int32_t* k_sel, int32_t n_sink, int32_t n_recent,
+                                  int32_t max_sel, int32_t* sel_idx, int32_t* sel_cnt,
+                                  float softmax_scale, int32_t n_split, float* out,
+                                  hipStream_t stream);
+
+/* Size in bytes of skv_decode_step_static's per-GPU scratch array. */
+size_t skv_static_scratch_bytes(void);
+
 /* Bytes of workspace skv_decode_attn needs: 4 * batch * n_heads * n_split *
  * (head_dim + 2); 0 for invalid arguments. */
 size_t skv_workspace_bytes(int32_t batch, int32_t n_heads, int32_t head_dim, int32_t n_split);

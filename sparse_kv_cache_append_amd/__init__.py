@@ -24,7 +24,7 @@ import os
 from typing import Optional
 
 __all__ = ["load", "Cache", "SkvError", "kv_append", "block_bounds", "select_topk",
-           "decode_attn", "decode_attn_select", "decode_step", "combine", "workspace_bytes", "status_str", "decode",
+           "decode_attn", "decode_attn_select", "decode_step", "decode_step_static", "combine", "workspace_bytes", "status_str", "decode",
            "SKV_F16", "SKV_F32", "SKV_I8", "LIB_PATH", "EXPORTS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libskv.so")
@@ -33,7 +33,8 @@ SKV_OK, SKV_EINVAL, SKV_ERANGE, SKV_EWORKSPACE, SKV_EUNSUPPORTED, SKV_EDEVICE = 
 SKV_F16, SKV_F32, SKV_I8 = 1, 2, 3
 
 EXPORTS = ("skv_max_blocks", "skv_kv_append", "skv_block_bounds", "skv_select_topk",
-           "skv_decode_attn", "skv_decode_attn_select", "skv_decode_step", "skv_combine",
+           "skv_decode_attn", "skv_decode_attn_select", "skv_decode_step",
+           "skv_decode_step_static", "skv_static_scratch_bytes", "skv_combine",
            "skv_workspace_bytes", "skv_status_str")
 
 
@@ -78,6 +79,9 @@ def load(path: str = LIB_PATH):
                                          ctypes.c_float, I32, P, SZ, P]),
         "skv_decode_step": (I32, [desc, P, P, P, I32, P, I32, P, I32, P, I32, I32, I32, P, P, P,
                                    ctypes.c_float, I32, P, SZ, P, P]),
+        "skv_decode_step_static": (I32, [desc, P, P, P, I32, P, I32, P, I32, P, I32, I32, I32,
+                                         P, P, ctypes.c_float, I32, P, P]),
+        "skv_static_scratch_bytes": (SZ, []),
         "skv_combine": (I32, [P, I32, I32, I32, I32, P, P]),
         "skv_workspace_bytes": (SZ, [I32, I32, I32, I32]),
         "skv_status_str": (ctypes.c_char_p, [I32]),
@@ -344,6 +348,38 @@ def decode_step(cache: Cache, q, seq_len, max_len: int, softmax_scale: float, n_
         int(n_recent), max_sel, _ptr(score), _ptr(sel_idx), _ptr(sel_cnt),
         float(softmax_scale), int(n_split), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _ptr(out), _stream(stream)))
+
+
+def decode_step_static(cache: Cache, q, seq_len, max_len: int, softmax_scale: float,
+                       n_split: int, out, pos0=None, k_new=None, v_new=None, k_sel=None,
+                       n_sink: int = 1, n_recent: int = 2, sel_idx=None, sel_cnt=None,
+                       stream=None):
+    """decode_step with its scratch (scores, split-K partials) in the library's
+    fixed per-GPU array (skv_decode_step_static): allocates nothing.  Calls that
+    overlap on one GPU race on that array."""
+    import torch
+    call = "skv_decode_step_static"
+    _check_q(call, cache, q, seq_len)
+    _need(call, _is(out, torch.float32, tuple(q.shape)), "out must be float32 like q")
+    src = 0
+    if k_new is not None:
+        _check_rows(call, cache, k_new, v_new, 1)
+        _need(call, _is(pos0, torch.int32, (cache.batch,)), "pos0 must be int32 [batch]")
+        src = _dtype_code(k_new)
+    if k_sel is not None:
+        _need(call, _is(k_sel, torch.int32, (cache.batch,)), "k_sel must be int32 [batch]")
+        _need(call, sel_idx is not None, "sel_idx and sel_cnt are required for Quest")
+        _check_sel(call, cache.batch, cache.n_kv_heads, sel_idx, sel_cnt)
+    max_sel = int(sel_idx.shape[2]) if sel_idx is not None else 0
+    _check(call, load().skv_decode_step_static(
+        ctypes.byref(cache.desc), _ptr(pos0), _ptr(k_new), _ptr(v_new), src,
+        _ptr(q), int(q.shape[1]), _ptr(seq_len), int(max_len), _ptr(k_sel), int(n_sink),
+        int(n_recent), max_sel, _ptr(sel_idx), _ptr(sel_cnt), float(softmax_scale),
+        int(n_split), _ptr(out), _stream(stream)))
+
+
+def static_scratch_bytes() -> int:
+    return int(load().skv_static_scratch_bytes())
 
 
 def combine(workspace, batch: int, n_heads: int, head_dim: int, n_split: int, out, stream=None):
