@@ -26,6 +26,8 @@ Modules
                exact int32 logit dots, split-K combine
 ``quest``      per-block kmin/kmax side cache, channel-wise upper bound,
                fixed top-K + sink + recent selection
+``sparse_v``   skipping the value rows of negligible softmax weight (static tau
+               or the adaptive eps rule)
 
 Parity pins: every function is checked by the ``-m "not gpu"`` tests in
 ``tests/test_oracle_*.py`` against brute force, closed forms, invariants or
@@ -33,9 +35,10 @@ page-printed numbers.  Two choices have no such pin and are marked "parity
 unpinned" where they are made: the near-tie report width (1e-5 relative) and
 the reading that forced blocks are excluded from the top-K candidates.
 """
-from . import quant, attention, quest  # noqa: F401
+from . import quant, attention, quest, sparse_v  # noqa: F401
 from .quant import quantize_rows, f16_round_down, f16_round_up  # noqa: F401
 from .attention import (attend_f16, attend_i8, attend_i8_dequant,  # noqa: F401
                         int8_logit_dots, combine_partials, softmax_partials)
 from .quest import (block_bounds, upper_bounds, group_scores, select_blocks,  # noqa: F401
                     selected_tokens)
+from .sparse_v import attend_f16_sparse_v, attend_i8_sparse_v  # noqa: F401
