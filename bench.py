@@ -91,7 +91,8 @@ def step_bytes(lens, Hkv, H, D, kv_dtype, block, attended_blocks=None):
 # ------------------------------------------------------------- HBM traffic
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic_quest32k.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "sparse_kv_cache_append_amd", "csrc", f)
-                  for f in ("decode_mfma.hip", "device_common.h", "launch.h", "select_core.h")]
+                  for f in ("decode_mfma.hip", "decode_core.h", "device_common.h", "launch.h",
+                            "select_core.h")]
 
 
 def kernel_source_digest() -> str:
@@ -526,6 +527,10 @@ def measure(w, args, quest: bool, dense: bool, detail: bool = False):
             res["quest"]["warm_us_per_step"] = round(warm, 3)
         if detail:
             res["_roofline"] = (dec_bytes, sel_us, dec_us)
+        if args.sparse_v_tau > 0:
+            res["quest_sparse_v"] = measure_sparse_v(
+                T, skv, torch, w, caches, R, q, seq_len, Lmax, new_k, new_v, pos_last, ks, score,
+                sel, cnt, attended, args.sparse_v_tau, calls_us)
         if "dense" in res:
             res["quest_over_dense"] = round(res["quest"]["us_per_step"]
                                             / res["dense"]["us_per_step"], 4)
@@ -533,6 +538,70 @@ def measure(w, args, quest: bool, dense: bool, detail: bool = False):
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     return res
+
+
+def measure_sparse_v(T, skv, torch, w, caches, R, q, seq_len, Lmax, new_k, new_v, pos_last, ks,
+                     score, sel, cnt, attended, tau, calls_us):
+    """The Quest step with sparse-V inside the selected blocks (static tau):
+    kv_append, block_bounds, select_topk, decode_attn_sparse_v (its q.K pass
+    and its value pass over the kept rows), combine.  Bytes: the side cache,
+    the K rows of the selected blocks, the V rows some head of the group
+    keeps (read once for the group), q and the output; the logits the two
+    passes exchange are implementation traffic, reported beside them."""
+    B, H, Hkv, D, blk = w.B, w.H, w.Hkv, w.D, w.block
+    S = skv.default_split(B, Hkv, int(sel.shape[2]), kv_dtype=w.kv_dtype, sparse=True)
+    dev = q.device
+    ws = torch.empty(skv.sparse_v_workspace_bytes(B, H, Hkv, D, S, Lmax), dtype=torch.uint8,
+                     device=dev)
+    out = torch.empty((B, H, D), dtype=torch.float32, device=dev)
+    keep = torch.zeros((B, H, -(-Lmax // 32)), dtype=torch.int32, device=dev)
+    skv.decode_attn_sparse_v(caches[0], q, seq_len, Lmax, w.softmax_scale, S, ws, tau=tau,
+                             sel_idx=sel, sel_cnt=cnt, keep_mask=keep)
+    torch.cuda.synchronize()
+    kw = keep.cpu().numpy().view(np.uint32)
+    row_k = 2 * D if w.kv_dtype == "f16" else D + 4          # a K (or V) row and its scale
+    k_bytes = v_bytes = 0
+    kept_pairs = att_pairs = 0
+    for b, L in enumerate(w.lens):
+        for g in range(Hkv):
+            toks = np.concatenate([np.arange(j * blk, min((j + 1) * blk, L))
+                                   for j in attended[(b, g)]])
+            bits = np.zeros(toks.size, bool)
+            for h in range(g * w.G, (g + 1) * w.G):
+                hb = (kw[b, h][toks // 32] >> (toks % 32).astype(np.uint32)) & 1
+                kept_pairs += int(hb.sum())
+                bits |= hb.astype(bool)
+            att_pairs += w.G * toks.size
+            k_bytes += toks.size * row_k
+            v_bytes += int(bits.sum()) * row_k
+    bounds = sum(-(-L // blk) for L in w.lens) * Hkv * side_cache_bytes_per_block(D)
+    total = bounds + k_bytes + v_bytes + 2 * B * H * D * 4
+    logit_bytes = 2 * 4 * sum(len(v) for v in attended.values()) * blk * w.G
+
+    def sv_calls(i):
+        c = caches[i % R]
+        skv.kv_append(c, pos_last, new_k, new_v)
+        skv.block_bounds(c, q, seq_len, Lmax, score)
+        skv.select_topk(score, seq_len, blk, ks, w.n_sink, w.n_recent, sel, cnt)
+        skv.decode_attn_sparse_v(c, q, seq_len, Lmax, w.softmax_scale, S, ws, tau=tau,
+                                 sel_idx=sel, sel_cnt=cnt)
+        skv.combine(ws, B, H, D, S, out)
+
+    gr, _ = T.graph(sv_calls)
+    us = (gr if gr is not None else T.stream(sv_calls)) * 1e6
+    pair_us = T.kernel(lambda i: skv.decode_attn_sparse_v(
+        caches[i % R], q, seq_len, Lmax, w.softmax_scale, S, ws, tau=tau, sel_idx=sel,
+        sel_cnt=cnt))
+    att_bytes = k_bytes + v_bytes + B * H * D * 4
+    return {"tau": tau, "us_per_step": round(us, 3),
+            "vs_five_calls_without": round(us / calls_us, 4),
+            "bytes_per_step": total, "k_bytes": k_bytes, "v_bytes_kept": v_bytes,
+            "kept_head_token_frac": round(kept_pairs / max(att_pairs, 1), 5),
+            "v_rows_read_frac": round(v_bytes / max(k_bytes, 1), 5),
+            "logit_bytes_exchanged": logit_bytes,
+            "sparse_v_pair_us": round(pair_us, 3),
+            "sparse_v_pair_pct_peak": round(100 * att_bytes / pair_us / 1e3 / HBM_PEAK_GBPS, 2),
+            "n_split": S}
 
 
 def main():
@@ -551,6 +620,9 @@ def main():
     ap.add_argument("--workloads", default="1,2,4,5,3@16384",
                     help="other workloads to time besides the 32K headline ('' = none; "
                          "3@L = the 32K Quest generator at context L)")
+    ap.add_argument("--sparse-v-tau", type=float, default=1e-3,
+                    help="also time the Quest steps with sparse-V at this static threshold "
+                         "(0 = off)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after timing, copy a buffer of this many MiB three times "
                          "(a plain copy of known size that scales HBM byte counters)")
@@ -636,6 +708,7 @@ def main():
         "quest": hq,
         "dense": hd,
         "quest_over_dense_time": head.get("quest_over_dense"),
+        "quest_sparse_v": head.get("quest_sparse_v"),
         "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4),
                      "traffic": recorded_traffic(rk), "kernel": rk,

@@ -255,6 +255,51 @@ skv_status skv_decode_attn_select(const skv_cache* c, const float* q, int32_t n_
                                   size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * skv_decode_attn_sparse_v — skv_decode_attn that leaves out the value rows
+ * of negligible softmax weight.  Defines: sparse_attn.md, "Compose (three
+ * sparsity levers, three pipeline stages)" item 3 (inside the attended
+ * blocks, skip the value work of positions whose post-softmax weight is
+ * negligible), "Stacking with sparse-V" (a static threshold tau) and
+ * "Adaptive tau (the eps mode)" (eps times the softmax denominator over the
+ * number of positions, so the dropped mass stays below eps; eps = 0 falls
+ * back to tau).  For each query head, with p_t the normalized softmax weight
+ * of attended token t over all n attended tokens of its (sequence, KV head):
+ * token t's value row is used iff p_t >= theta, theta = eps / n if eps > 0
+ * else tau; the normalizer still counts every token, so
+ *     out = sum over used t of p_t v_t.
+ * tau = eps = 0 uses every row (the dense or Quest result).  The weights and
+ * the decision are float32 (a token within about 1e-5 relative of theta may
+ * fall either way).  Value rows no head of the group uses are not read.
+ * Two launches (the q.K pass, then the value pass over the kept rows); the
+ * workspace then holds the standard partial states at its start, so
+ *     skv_combine(workspace, batch, n_heads, head_dim, n_split, out)
+ * produces the output.
+ *   Arguments as skv_decode_attn, and:
+ *   tau, eps   : thresholds, finite and >= 0 (SKV_EINVAL otherwise).
+ *   workspace  : at least skv_sparse_v_workspace_bytes(batch, n_heads,
+ *                n_kv_heads, head_dim, n_split, max_len) bytes, 16-byte
+ *                aligned.  Layout: the skv_decode_attn partial states, then
+ *                per part the q.K pass's logit maximum, denominator and
+ *                token count, then each query head's base-2 logits.
+ *   keep_mask  : optional (NULL = none) device uint32
+ *                [batch][n_heads][ceil(max_len / 32)]: bit t % 32 of word
+ *                t / 32 is set iff token t's value row was used for the
+ *                head; words of tokens that are not attended are not written
+ *                (zero the buffer first).
+ * Errors: those of skv_decode_attn.
+ */
+skv_status skv_decode_attn_sparse_v(const skv_cache* c, const float* q, int32_t n_heads,
+                                    const int32_t* seq_len, int32_t max_len,
+                                    const int32_t* sel_idx, const int32_t* sel_cnt,
+                                    int32_t max_sel, float softmax_scale, float tau, float eps,
+                                    int32_t n_split, void* workspace, size_t workspace_bytes,
+                                    uint32_t* keep_mask, hipStream_t stream);
+
+/* Bytes of workspace skv_decode_attn_sparse_v needs; 0 for invalid arguments. */
+size_t skv_sparse_v_workspace_bytes(int32_t batch, int32_t n_heads, int32_t n_kv_heads,
+                                    int32_t head_dim, int32_t n_split, int32_t max_len);
+
+/*
  * skv_combine — merge the split-K partial states into the output.
  * Defines: M = max_i m_i; out = sum_i 2^(m_i - M) o_i / sum_i 2^(m_i - M) l_i
  * over the non-empty parts (the numerator/mass form of a split softmax).  A

@@ -24,7 +24,8 @@ import os
 from typing import Optional
 
 __all__ = ["load", "Cache", "SkvError", "kv_append", "block_bounds", "select_topk",
-           "decode_attn", "decode_attn_select", "decode_step", "decode_step_static", "combine", "workspace_bytes", "status_str", "decode",
+           "decode_attn", "decode_attn_select", "decode_attn_sparse_v", "sparse_v_workspace_bytes",
+           "decode_step", "decode_step_static", "combine", "workspace_bytes", "status_str", "decode",
            "SKV_F16", "SKV_F32", "SKV_I8", "LIB_PATH", "EXPORTS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libskv.so")
@@ -34,7 +35,8 @@ SKV_F16, SKV_F32, SKV_I8 = 1, 2, 3
 
 EXPORTS = ("skv_max_blocks", "skv_kv_append", "skv_block_bounds", "skv_select_topk",
            "skv_decode_attn", "skv_decode_attn_select", "skv_decode_step",
-           "skv_decode_step_static", "skv_static_scratch_bytes", "skv_combine",
+           "skv_decode_step_static", "skv_static_scratch_bytes", "skv_decode_attn_sparse_v",
+           "skv_sparse_v_workspace_bytes", "skv_combine",
            "skv_workspace_bytes", "skv_status_str")
 
 
@@ -82,6 +84,9 @@ def load(path: str = LIB_PATH):
         "skv_decode_step_static": (I32, [desc, P, P, P, I32, P, I32, P, I32, P, I32, I32, I32,
                                          P, P, ctypes.c_float, I32, P, P]),
         "skv_static_scratch_bytes": (SZ, []),
+        "skv_decode_attn_sparse_v": (I32, [desc, P, I32, P, I32, P, P, I32, ctypes.c_float,
+                                           ctypes.c_float, ctypes.c_float, I32, P, SZ, P, P]),
+        "skv_sparse_v_workspace_bytes": (SZ, [I32, I32, I32, I32, I32, I32]),
         "skv_combine": (I32, [P, I32, I32, I32, I32, P, P]),
         "skv_workspace_bytes": (SZ, [I32, I32, I32, I32]),
         "skv_status_str": (ctypes.c_char_p, [I32]),
@@ -348,6 +353,37 @@ def decode_step(cache: Cache, q, seq_len, max_len: int, softmax_scale: float, n_
         int(n_recent), max_sel, _ptr(score), _ptr(sel_idx), _ptr(sel_cnt),
         float(softmax_scale), int(n_split), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _ptr(out), _stream(stream)))
+
+
+def sparse_v_workspace_bytes(batch: int, n_heads: int, n_kv_heads: int, head_dim: int,
+                             n_split: int, max_len: int) -> int:
+    return int(load().skv_sparse_v_workspace_bytes(batch, n_heads, n_kv_heads, head_dim,
+                                                   n_split, max_len))
+
+
+def decode_attn_sparse_v(cache: Cache, q, seq_len, max_len: int, softmax_scale: float,
+                         n_split: int, workspace, tau: float = 0.0, eps: float = 0.0,
+                         sel_idx=None, sel_cnt=None, keep_mask=None, stream=None):
+    """Split-K partial states with sparse-V (value rows of normalized weight
+    below tau, or below eps / n, left out) into ``workspace`` (at least
+    sparse_v_workspace_bytes(...) bytes); combine() then gives the output.
+    keep_mask: optional zeroed int32 [batch][n_heads][ceil(max_len/32)]
+    receiving the kept-row bits."""
+    import torch
+    call = "skv_decode_attn_sparse_v"
+    _check_q(call, cache, q, seq_len)
+    _check_sel(call, cache.batch, cache.n_kv_heads, sel_idx, sel_cnt)
+    if keep_mask is not None:
+        _need(call, _is(keep_mask, keep_mask.dtype, (cache.batch, int(q.shape[1]),
+                                                     -(-int(max_len) // 32)))
+              and keep_mask.element_size() == 4, "keep_mask must be 32-bit "
+              "[batch][n_heads][ceil(max_len/32)]")
+    max_sel = int(sel_idx.shape[2]) if sel_idx is not None else 0
+    _check(call, load().skv_decode_attn_sparse_v(
+        ctypes.byref(cache.desc), _ptr(q), int(q.shape[1]), _ptr(seq_len), int(max_len),
+        _ptr(sel_idx), _ptr(sel_cnt), max_sel, float(softmax_scale), float(tau), float(eps),
+        int(n_split), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _ptr(keep_mask), _stream(stream)))
 
 
 def decode_step_static(cache: Cache, q, seq_len, max_len: int, softmax_scale: float,

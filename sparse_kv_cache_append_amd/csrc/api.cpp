@@ -286,6 +286,56 @@ skv_status skv_decode_attn_select(const skv_cache* c, const float* q, int32_t n_
   return device_status(skv::launch_decode(p, stream));
 }
 
+size_t skv_sparse_v_workspace_bytes(int32_t batch, int32_t n_heads, int32_t n_kv_heads,
+                                    int32_t head_dim, int32_t n_split, int32_t max_len) {
+  if (batch < 1 || n_heads < 1 || n_kv_heads < 1 || !valid_head_dim(head_dim) || n_split < 1 ||
+      n_split > kMaxSplit || max_len < 0)
+    return 0;
+  return sizeof(float) *
+         skv::sparse_v_workspace_floats(batch, n_heads, n_kv_heads, head_dim, n_split, max_len);
+}
+
+skv_status skv_decode_attn_sparse_v(const skv_cache* c, const float* q, int32_t n_heads,
+                                    const int32_t* seq_len, int32_t max_len,
+                                    const int32_t* sel_idx, const int32_t* sel_cnt,
+                                    int32_t max_sel, float softmax_scale, float tau, float eps,
+                                    int32_t n_split, void* workspace, size_t workspace_bytes,
+                                    uint32_t* keep_mask, hipStream_t stream) {
+  skv_status st = check_cache(c, false);
+  if (st != SKV_OK) return st;
+  if (q == nullptr || seq_len == nullptr || !aligned(q)) return SKV_EINVAL;
+  st = check_heads(c, n_heads);
+  if (st != SKV_OK) return st;
+  if ((sel_idx == nullptr) != (sel_cnt == nullptr)) return SKV_EINVAL;
+  if (sel_idx != nullptr && max_sel < 1) return SKV_EINVAL;
+  if (n_split < 1 || n_split > kMaxSplit) return SKV_EINVAL;
+  if (!grid_fits(n_split, c->n_kv_heads, c->batch)) return SKV_ERANGE;
+  if (!(softmax_scale == softmax_scale) || softmax_scale < 0.0f) return SKV_EINVAL;
+  // thresholds: finite and >= 0 (NaN fails both comparisons)
+  if (!(tau >= 0.0f && tau <= 3.4e38f) || !(eps >= 0.0f && eps <= 3.4e38f)) return SKV_EINVAL;
+  if (max_len < 0 || max_len > c->max_seq) return SKV_ERANGE;
+  const size_t need = skv_sparse_v_workspace_bytes(c->batch, n_heads, c->n_kv_heads,
+                                                   c->head_dim, n_split, max_len);
+  if (workspace == nullptr || workspace_bytes < need) return SKV_EWORKSPACE;
+  if (!aligned(workspace)) return SKV_EINVAL;
+  skv::SparseVParams p;
+  p.c = c;
+  p.q = q;
+  p.n_heads = n_heads;
+  p.seq_len = seq_len;
+  p.max_len = max_len;
+  p.sel_idx = sel_idx;
+  p.sel_cnt = sel_cnt;
+  p.max_sel = max_sel;
+  p.softmax_scale = softmax_scale;
+  p.tau = tau;
+  p.eps = eps;
+  p.n_split = n_split;
+  p.ws = static_cast<float*>(workspace);
+  p.keep = keep_mask;
+  return device_status(skv::launch_sparse_v(p, stream));
+}
+
 skv_status skv_combine(const void* workspace, int32_t batch, int32_t n_heads, int32_t head_dim,
                        int32_t n_split, float* out, hipStream_t stream) {
   if (workspace == nullptr || out == nullptr) return SKV_EINVAL;

@@ -1,0 +1,225 @@
+// Shared pieces of the attention kernels (decode_mfma.hip, sparse_v.hip):
+// vector types, the 16-byte tile loads through per-tile buffer resources, the
+// MFMA wrappers, the wave-uniform tile walk over a part's blocks (or its
+// share of a selected list) and the exact int8 -> f16 widening of V codes.
+// Included by the .hip sources only; everything here has internal linkage.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "device_common.h"
+
+namespace skv {
+namespace {
+
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef int int4_t __attribute__((ext_vector_type(4)));
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef int int2_t __attribute__((ext_vector_type(2)));
+#define SKV_LDS __attribute__((address_space(3)))
+
+constexpr int kMWaves = 4;
+constexpr int kMThreads = kMWaves * kWave;
+constexpr int kD = 128;
+constexpr int kRowBytesF16 = kD * 2;   // 256
+constexpr int kRowBytesI8 = kD;        // 128
+
+__device__ __forceinline__ int swz(int row) { return row & 15; }
+
+// A full tile (4 KiB of K or V rows) as a raw buffer: the resource is built
+// in scalar registers from the tile's first byte, the lane's 16-byte offset
+// is loop-invariant and the row step is the instruction's immediate offset,
+// so a tile's loads need no vector address arithmetic.  Records = the tile's
+// bytes (the range check keeps every access inside it); word 3 is the plain
+// untyped-buffer configuration of the CDNA resource descriptor.  aux = 2 is
+// the nontemporal hint (each K/V byte is read once per step).
+constexpr int kTileRsrcBytes = 4096;
+constexpr int kRsrcWord3 = 0x00020000;
+constexpr int kAuxNontemporal = 2;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint8_t* t,
+                                                           int bytes = kTileRsrcBytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(t), (short)0, bytes,
+                                           kRsrcWord3);
+}
+__device__ __forceinline__ int4_t tile_load(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
+  return __builtin_bit_cast(int4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0,
+                                                                         kAuxNontemporal));
+}
+
+// Every refill of a tile fragment issues the same number of loads, also
+// when the walk is over: then through a resource of zero records, which
+// returns zeros and touches no memory.  The hardware load counter completes
+// in order, and a path that issued fewer loads (a conditional refill) makes
+// the compiler's wait at the next join conservative: the wave would then
+// wait for every tile in flight, the one two steps ahead included, at each
+// turn of the loop.
+
+__device__ __forceinline__ float4_t mfma_f16_32(half8_t a, half8_t b, float4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ float4_t mfma_f16_16(half4_t a, half4_t b, float4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+}
+
+// Tile walk of one wavefront: tiles w, w + kMWaves, ... of the part's
+// sequence of T-row tiles (each block holds block / T tiles).
+struct TileWalk {
+  const int32_t* sel;
+  int32_t jl, u0, n_units, tpb, block, L, nb;
+  int32_t unit, sub;
+
+  __device__ __forceinline__ void init(int w) {
+    unit = w / tpb;
+    sub = w - unit * tpb;
+  }
+  __device__ __forceinline__ bool more() const { return unit < n_units; }
+  // tiles left in this wavefront's walk (it takes every kMWaves-th tile)
+  __device__ __forceinline__ int32_t count() const {
+    const int32_t left = (n_units - unit) * tpb - sub;
+    return left > 0 ? (left + kMWaves - 1) / kMWaves : 0;
+  }
+  // first row and valid-row count of the current tile, then advance by kMWaves tiles
+  // (the walk state is wave-uniform: it lives in scalar registers)
+  template <int T>
+  __device__ __forceinline__ void next(int32_t& r0, int32_t& nvalid) {
+    int32_t j = u0 + unit;
+    if (sel != nullptr)
+      j = unit < kWave ? __builtin_amdgcn_readlane(jl, unit)
+                       : __builtin_amdgcn_readfirstlane(sel[j]);
+    if (j < 0 || j >= nb) {
+      r0 = 0;
+      nvalid = 0;
+    } else {
+      r0 = j * block + sub * T;
+      nvalid = __builtin_amdgcn_readfirstlane(min(min(T, block - sub * T), L - r0));
+    }
+    sub += kMWaves;
+    while (sub >= tpb) { sub -= tpb; ++unit; }
+  }
+};
+
+// A given list's count and this part's entries (lane i: entry u0 + i), requested
+// at kernel entry together with the row length and the query, so the first
+// tile loads wait for one round trip only.  Entries past the count are
+// ignored through n_units.
+struct ListSeed {
+  int32_t cnt, jl;
+};
+__device__ __forceinline__ ListSeed list_seed(const int32_t* sel_idx, const int32_t* sel_cnt,
+                                              int32_t max_sel, int64_t bg, int32_t split,
+                                              int32_t units_per_split) {
+  ListSeed ls{0, -1};
+  if (sel_idx != nullptr) {
+    const int lane = threadIdx.x % kWave;
+    const int32_t e = split * units_per_split + lane;
+    ls.cnt = sel_cnt[bg];
+    if (lane < units_per_split && e < max_sel) ls.jl = sel_idx[bg * max_sel + e];
+  }
+  return ls;
+}
+
+template <int T>
+__device__ __forceinline__ TileWalk make_walk(const ListSeed& ls, const int32_t* sel_idx,
+                                              int32_t max_sel, int64_t bg, int32_t L,
+                                              int32_t block, int32_t split,
+                                              int32_t units_per_split) {
+  TileWalk tw;
+  tw.block = block;
+  tw.L = L;
+  tw.nb = (L + block - 1) / block;
+  tw.tpb = (block + T - 1) / T;
+  int32_t total = tw.nb;
+  tw.sel = nullptr;
+  tw.jl = -1;
+  tw.u0 = split * units_per_split;
+  if (sel_idx != nullptr) {
+    tw.sel = sel_idx + bg * max_sel;
+    tw.jl = ls.jl;
+    total = min(max(__builtin_amdgcn_readfirstlane(ls.cnt), 0), max_sel);
+  }
+  tw.n_units = max(0, min(units_per_split, total - tw.u0));
+  return tw;
+}
+
+// The int8 kernels' query as the B operand of the integer q.K product
+// (column = head lc, k-chunk lg): x holds this lane's channels
+// 64 kk + 16 lg + 0..15 of its head (zeros past the group); the head's absmax
+// scale over all 128 channels (the 4 lanes of a column hold 32 channels each)
+// and the codes, which equal the correctly rounded rint(x / scale) of the
+// append quantizer bit for bit: taken through the reciprocal, with the rare
+// value near a rounding boundary (flagged per lane) redone with the exact
+// quotient.  coef = scale * softmax scale * log2 e (0 past the group).
+__device__ __forceinline__ void i8_query_operand(const float (&x)[2][16], bool hv, float scale2,
+                                                 int4_t (&qb)[2], float& coef) {
+  float a = 0.0f;
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) a = fmaxf(a, fabsf(x[kk][i]));
+  }
+  a = rows_max(a);
+  const float qs = absmax_scale(a);
+  // codes through the reciprocal; the rare value near a rounding boundary
+  // (flagged per lane) is redone with the exact quotient
+  const float inv = 1.0f / qs;
+  int c[2][16];
+  uint32_t redo = 0u;
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      bool ex;
+      c[kk][i] = quant_code_recip(x[kk][i], inv, ex);
+      redo |= uint32_t(ex) << (16 * kk + i);
+    }
+  }
+  if (__builtin_amdgcn_ballot_w64(redo != 0u) != 0u) {
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if ((redo >> (16 * kk + i)) & 1u) c[kk][i] = quant_code(x[kk][i], qs);
+    }
+  }
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      uint32_t packed = 0u;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) packed |= (uint32_t(c[kk][4 * w + e]) & 0xFFu) << (8 * e);
+      qb[kk][w] = hv ? int32_t(packed) : 0;
+    }
+  }
+  coef = hv ? qs * scale2 : 0.0f;
+}
+
+// int8 V codes widened to f16 exactly: 1152 + c is exact in f16, minus 1152.
+__device__ __forceinline__ half8_t widen_codes(int2_t w) {
+  typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+  // v_perm_b32 picks bytes of {0x64646464, x}: selector 0..3 = bytes of x,
+  // 4 = 0x64.  Each 16-bit half becomes 0x64 : (c + 128) = f16 1024 + c + 128.
+  constexpr uint32_t kLoSel = 0x04010400u;   // (0x64, x1, 0x64, x0)
+  constexpr uint32_t kHiSel = 0x04030402u;   // (0x64, x3, 0x64, x2)
+  const half2_t off = half2_t{(_Float16)1152.0f, (_Float16)1152.0f};
+  half8_t r;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const uint32_t x = uint32_t(w[k]) ^ 0x80808080u;         // c + 128 per byte
+    const uint32_t lo = __builtin_amdgcn_perm(0x64646464u, x, kLoSel);
+    const uint32_t hi = __builtin_amdgcn_perm(0x64646464u, x, kHiSel);
+    const half2_t a = __builtin_bit_cast(half2_t, lo) - off;
+    const half2_t b = __builtin_bit_cast(half2_t, hi) - off;
+    r[4 * k + 0] = a[0];
+    r[4 * k + 1] = a[1];
+    r[4 * k + 2] = b[0];
+    r[4 * k + 3] = b[1];
+  }
+  return r;
+}
+
+}  // namespace
+}  // namespace skv

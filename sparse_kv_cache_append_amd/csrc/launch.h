@@ -92,6 +92,35 @@ hipError_t launch_select(const float* score, const int32_t* seq_len, int32_t bat
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
 
+// Sparse-V decode attention (sparse_v.hip): the q.K pass and the value pass
+// over the kept rows, writing the standard partial states for skv_combine.
+struct SparseVParams {
+  const skv_cache* c;
+  const float* q;
+  int32_t n_heads;
+  const int32_t* seq_len;
+  int32_t max_len;
+  const int32_t* sel_idx;  // nullptr = dense
+  const int32_t* sel_cnt;
+  int32_t max_sel;
+  float softmax_scale;
+  float tau, eps;
+  int32_t n_split;
+  float* ws;               // layout: sparse_v_workspace_floats
+  uint32_t* keep;          // optional keep-bit output
+};
+// Floats of the sparse-V workspace: the standard partial states, then per
+// part the pass-A maximum and denominator ([B][H][S] each) and token count
+// ([B][Hkv][S] int32), then the logits [B][H][max_len rounded up to 32] and
+// 32 floats of padding.
+inline size_t sparse_v_workspace_floats(int32_t B, int32_t H, int32_t Hkv, int32_t D, int32_t S,
+                                        int32_t max_len) {
+  const size_t bhs = size_t(B) * H * S;
+  const size_t lstride = (size_t(max_len) + 31) / 32 * 32;
+  return bhs * (size_t(D) + 2) + 2 * bhs + size_t(B) * Hkv * S + size_t(B) * H * lstride + 32;
+}
+hipError_t launch_sparse_v(const SparseVParams& p, hipStream_t stream);
+
 hipError_t launch_combine(const float* ws, int32_t batch, int32_t n_heads, int32_t head_dim,
                           int32_t n_split, float* out, hipStream_t stream);
 
