@@ -138,3 +138,34 @@ def selected_tokens(sel: np.ndarray, L: int, block: int) -> np.ndarray:
     if len(sel) == 0:
         return np.zeros(0, dtype=np.int64)
     return np.concatenate([np.arange(j * block, min((j + 1) * block, L)) for j in sel])
+
+
+# ------------------------------------------------------- per-query-head sets
+# sparse_attn.md, "S2/S3 engineering design" item 2 and "Open questions":
+# the GQA group can be reduced to one block set per KV head (the max rule
+# above) or each query head can keep its own set ("per-Q-head mask
+# divergence", which the group max avoids).  The per-head variant: head h
+# ranks blocks by its own bound UB[h] and takes its own top-K plus the same
+# forced blocks; it attends to exactly its own blocks.  Its KV head's blocks
+# are read once for the group: the union of the G sets, each block tagged
+# with the heads that chose it.
+
+def select_blocks_per_head(ub: np.ndarray, n_blocks: int, k_sel: int, n_sink: int = 1,
+                           n_recent: int = 2):
+    """ub [G][>= n_blocks]: the bounds of one KV head's G query heads.
+    Returns one select_blocks result per head (same rule, own scores)."""
+    return [select_blocks(ub[i], n_blocks, k_sel, n_sink, n_recent) for i in range(ub.shape[0])]
+
+
+def union_with_heads(sets):
+    """sets: G ascending block arrays (one per query head of a KV head).
+    Returns (union ascending int64 [U], mask int64 [U]) with bit i of
+    mask[u] set iff head i's set holds union[u]."""
+    allb = sorted(set().union(*[set(np.asarray(s).tolist()) for s in sets])) if sets else []
+    union = np.array(allb, dtype=np.int64)
+    mask = np.zeros(union.size, dtype=np.int64)
+    pos = {b: u for u, b in enumerate(allb)}
+    for i, s in enumerate(sets):
+        for b in np.asarray(s).tolist():
+            mask[pos[b]] |= 1 << i
+    return union, mask
