@@ -527,6 +527,9 @@ def measure(w, args, quest: bool, dense: bool, detail: bool = False):
             res["quest"]["warm_us_per_step"] = round(warm, 3)
         if detail:
             res["_roofline"] = (dec_bytes, sel_us, dec_us)
+        if not args.no_per_head:
+            res["quest_per_head"] = measure_per_head(T, skv, torch, w, caches, R, q, seq_len, Lmax,
+                                                     new_k, new_v, pos_last, ks, res["quest"])
         if args.sparse_v_tau > 0:
             res["quest_sparse_v"] = measure_sparse_v(
                 T, skv, torch, w, caches, R, q, seq_len, Lmax, new_k, new_v, pos_last, ks, score,
@@ -538,6 +541,59 @@ def measure(w, args, quest: bool, dense: bool, detail: bool = False):
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     return res
+
+
+def measure_per_head(T, skv, torch, w, caches, R, q, seq_len, Lmax, new_k, new_v, pos_last, ks,
+                     group_res):
+    """The Quest step with one block set per query head: kv_append,
+    block_bounds_heads, select_topk over the H per-head rows, select_union,
+    decode_attn_heads (each head over its own blocks, the union read once
+    for the group), combine.  Bytes: the side cache, the KV rows of the
+    union's blocks, q and the output."""
+    B, H, Hkv, D, blk = w.B, w.H, w.Hkv, w.D, w.block
+    dev = q.device
+    max_sel = max(w.k_sel) + w.n_sink + w.n_recent
+    max_blocks = caches[0].max_blocks
+    max_union = min(max_blocks, w.G * max_sel)
+    sc = torch.empty((B, H, max_blocks), dtype=torch.float32, device=dev)
+    sel = torch.empty((B, H, max_sel), dtype=torch.int32, device=dev)
+    cnt = torch.empty((B, H), dtype=torch.int32, device=dev)
+    uni = torch.empty((B, Hkv, max_union), dtype=torch.int32, device=dev)
+    ucnt = torch.empty((B, Hkv), dtype=torch.int32, device=dev)
+    um = torch.empty((B, Hkv, max_union), dtype=torch.int32, device=dev)
+    S = skv.default_split(B, Hkv, max_union, kv_dtype=w.kv_dtype, sparse=True)
+    ws = torch.empty(skv.workspace_bytes(B, H, D, S), dtype=torch.uint8, device=dev)
+    out = torch.empty((B, H, D), dtype=torch.float32, device=dev)
+
+    def step(i):
+        c = caches[i % R]
+        skv.kv_append(c, pos_last, new_k, new_v)
+        skv.block_bounds_heads(c, q, seq_len, Lmax, sc)
+        skv.select_topk(sc, seq_len, blk, ks, w.n_sink, w.n_recent, sel, cnt)
+        skv.select_union(sel, cnt, Hkv, max_blocks, uni, ucnt, um)
+        skv.decode_attn_heads(c, q, seq_len, Lmax, w.softmax_scale, S, ws, uni, ucnt, um)
+        skv.combine(ws, B, H, D, S, out)
+
+    step(0)
+    torch.cuda.synchronize()
+    u_h, c_h = uni.cpu().numpy(), ucnt.cpu().numpy()
+    attended = {(b, g): u_h[b, g, :c_h[b, g]].tolist() for b in range(B) for g in range(Hkv)}
+    qb = step_bytes(w.lens, Hkv, H, D, w.kv_dtype, blk, attended)
+    gr, _ = T.graph(step)
+    us = (gr if gr is not None else T.stream(step)) * 1e6
+    dec_bytes = qb["kv"] + B * H * D * 4
+    dec_us = T.kernel(lambda i: skv.decode_attn_heads(caches[i % R], q, seq_len, Lmax,
+                                                      w.softmax_scale, S, ws, uni, ucnt, um))
+    n_all = sum(-(-L // blk) for L in w.lens) * Hkv
+    return {"us_per_step": round(us, 3),
+            "vs_group_five_calls": round(us / group_res["five_calls_us_per_step"], 4),
+            "bytes_per_step": qb["total"], "kv_bytes": qb["kv"],
+            "union_blocks_frac": round(sum(len(x) for x in attended.values()) / n_all, 4),
+            "GBps": round(qb["total"] / us / 1e3, 1),
+            "pct_hbm_peak": round(100 * qb["total"] / us / 1e3 / HBM_PEAK_GBPS, 2),
+            "decode_attn_heads_us": round(dec_us, 3),
+            "decode_attn_heads_pct_peak": round(100 * dec_bytes / dec_us / 1e3 / HBM_PEAK_GBPS, 2),
+            "n_split": S}
 
 
 def measure_sparse_v(T, skv, torch, w, caches, R, q, seq_len, Lmax, new_k, new_v, pos_last, ks,
@@ -620,6 +676,8 @@ def main():
     ap.add_argument("--workloads", default="1,2,4,5,3@16384",
                     help="other workloads to time besides the 32K headline ('' = none; "
                          "3@L = the 32K Quest generator at context L)")
+    ap.add_argument("--no-per-head", action="store_true",
+                    help="skip the Quest steps with one block set per query head")
     ap.add_argument("--sparse-v-tau", type=float, default=1e-3,
                     help="also time the Quest steps with sparse-V at this static threshold "
                          "(0 = off)")
@@ -709,6 +767,7 @@ def main():
         "dense": hd,
         "quest_over_dense_time": head.get("quest_over_dense"),
         "quest_sparse_v": head.get("quest_sparse_v"),
+        "quest_per_head": head.get("quest_per_head"),
         "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4),
                      "traffic": recorded_traffic(rk), "kernel": rk,

@@ -255,6 +255,71 @@ skv_status skv_decode_attn_select(const skv_cache* c, const float* q, int32_t n_
                                   size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Per-query-head selection.  sparse_attn.md, "S2/S3 engineering design"
+ * item 2 and "Open questions": the group max above gives one block set per KV
+ * head; the alternative keeps one set per query head.  Three calls:
+ *   skv_block_bounds_heads  each query head's own bound per block;
+ *   skv_select_topk         unchanged, called with n_kv_heads = n_heads (one
+ *                           row per query head: score [batch][n_heads][...],
+ *                           sel_idx [batch][n_heads][max_sel]);
+ *   skv_select_union        per KV head, the union of its G heads' lists
+ *                           with the heads that chose each block;
+ *   skv_decode_attn_heads   attention over the union, each query head over
+ *                           its own blocks only; skv_combine as usual.
+ * The union's blocks are read once for the whole group.
+ */
+
+/*
+ * skv_block_bounds_heads — skv_block_bounds without the group max:
+ * score[b][h][j] = sum_d max(q_hd * kmin_gjd, q_hd * kmax_gjd), g = h / G.
+ *   score : device float32 [batch][n_heads][max_blocks]; entries of blocks
+ *           >= ceil(L_b / block) are not written.
+ * Other arguments and errors as skv_block_bounds.
+ */
+skv_status skv_block_bounds_heads(const skv_cache* c, const float* q, int32_t n_heads,
+                                  const int32_t* seq_len, int32_t max_len, float* score,
+                                  hipStream_t stream);
+
+/*
+ * skv_select_union — for each (sequence, KV head), the ascending union of
+ * the per-query-head lists of its G = n_heads / n_kv_heads heads.
+ *   sel_idx, sel_cnt : from skv_select_topk over per-head rows
+ *                      ([batch][n_heads][max_sel], [batch][n_heads]); at most
+ *                      min(sel_cnt, max_sel) entries per head are read,
+ *                      entries outside [0, max_blocks) are ignored.
+ *   uni_idx  : device int32 [batch][n_kv_heads][max_union], ascending, padded
+ *              with -1; at most max_union entries are written.
+ *   uni_cnt  : device int32 [batch][n_kv_heads], the union's full size
+ *              (larger than max_union signals a truncated list; it is at
+ *              most min(NB, G * max_sel)).
+ *   uni_mask : device uint32 [batch][n_kv_heads][max_union]: bit i set iff
+ *              query head g * G + i chose the entry's block (0 on padding).
+ * Errors: SKV_EINVAL (NULL, sizes < 1, n_heads % n_kv_heads),
+ * SKV_EUNSUPPORTED (G not in {1, 2, 4, 8}, max_blocks > 16384), SKV_ERANGE,
+ * SKV_EDEVICE.
+ */
+skv_status skv_select_union(const int32_t* sel_idx, const int32_t* sel_cnt, int32_t batch,
+                            int32_t n_heads, int32_t n_kv_heads, int32_t max_sel,
+                            int32_t max_blocks, int32_t max_union, int32_t* uni_idx,
+                            int32_t* uni_cnt, uint32_t* uni_mask, hipStream_t stream);
+
+/*
+ * skv_decode_attn_heads — skv_decode_attn over a KV head's union list where
+ * query head g * G + i attends only the blocks whose uni_mask bit i is set
+ * (its own selected set): for every query head, the softmax over exactly its
+ * own blocks' tokens (last block clipped at L_b).  Partial states as
+ * skv_decode_attn (a part where a head has no block: m = -inf, l = 0, o = 0).
+ *   uni_idx, uni_cnt, uni_mask, max_union : from skv_select_union.
+ * Other arguments, workspace and errors as skv_decode_attn.
+ */
+skv_status skv_decode_attn_heads(const skv_cache* c, const float* q, int32_t n_heads,
+                                 const int32_t* seq_len, int32_t max_len,
+                                 const int32_t* uni_idx, const int32_t* uni_cnt,
+                                 const uint32_t* uni_mask, int32_t max_union,
+                                 float softmax_scale, int32_t n_split, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream);
+
+/*
  * skv_decode_attn_sparse_v — skv_decode_attn that leaves out the value rows
  * of negligible softmax weight.  Defines: sparse_attn.md, "Compose (three
  * sparsity levers, three pipeline stages)" item 3 (inside the attended

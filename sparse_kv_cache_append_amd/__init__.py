@@ -25,6 +25,7 @@ from typing import Optional
 
 __all__ = ["load", "Cache", "SkvError", "kv_append", "block_bounds", "select_topk",
            "decode_attn", "decode_attn_select", "decode_attn_sparse_v", "sparse_v_workspace_bytes",
+           "block_bounds_heads", "select_union", "decode_attn_heads",
            "decode_step", "decode_step_static", "combine", "workspace_bytes", "status_str", "decode",
            "SKV_F16", "SKV_F32", "SKV_I8", "LIB_PATH", "EXPORTS"]
 
@@ -36,7 +37,8 @@ SKV_F16, SKV_F32, SKV_I8 = 1, 2, 3
 EXPORTS = ("skv_max_blocks", "skv_kv_append", "skv_block_bounds", "skv_select_topk",
            "skv_decode_attn", "skv_decode_attn_select", "skv_decode_step",
            "skv_decode_step_static", "skv_static_scratch_bytes", "skv_decode_attn_sparse_v",
-           "skv_sparse_v_workspace_bytes", "skv_combine",
+           "skv_sparse_v_workspace_bytes", "skv_block_bounds_heads", "skv_select_union",
+           "skv_decode_attn_heads", "skv_combine",
            "skv_workspace_bytes", "skv_status_str")
 
 
@@ -87,6 +89,10 @@ def load(path: str = LIB_PATH):
         "skv_decode_attn_sparse_v": (I32, [desc, P, I32, P, I32, P, P, I32, ctypes.c_float,
                                            ctypes.c_float, ctypes.c_float, I32, P, SZ, P, P]),
         "skv_sparse_v_workspace_bytes": (SZ, [I32, I32, I32, I32, I32, I32]),
+        "skv_block_bounds_heads": (I32, [desc, P, I32, P, I32, P, P]),
+        "skv_select_union": (I32, [P, P, I32, I32, I32, I32, I32, I32, P, P, P, P]),
+        "skv_decode_attn_heads": (I32, [desc, P, I32, P, I32, P, P, P, I32, ctypes.c_float, I32,
+                                        P, SZ, P]),
         "skv_combine": (I32, [P, I32, I32, I32, I32, P, P]),
         "skv_workspace_bytes": (SZ, [I32, I32, I32, I32]),
         "skv_status_str": (ctypes.c_char_p, [I32]),
@@ -353,6 +359,54 @@ def decode_step(cache: Cache, q, seq_len, max_len: int, softmax_scale: float, n_
         int(n_recent), max_sel, _ptr(score), _ptr(sel_idx), _ptr(sel_cnt),
         float(softmax_scale), int(n_split), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _ptr(out), _stream(stream)))
+
+
+def block_bounds_heads(cache: Cache, q, seq_len, max_len: int, score, stream=None):
+    """score [batch][H][max_blocks] <- each query head's own Quest bound."""
+    import torch
+    call = "skv_block_bounds_heads"
+    _check_q(call, cache, q, seq_len)
+    _need(call, _is(score, torch.float32, (cache.batch, int(q.shape[1]), cache.max_blocks)),
+          "score must be float32 [batch][n_heads][max_blocks]")
+    _check(call, load().skv_block_bounds_heads(
+        ctypes.byref(cache.desc), _ptr(q), int(q.shape[1]), _ptr(seq_len), int(max_len),
+        _ptr(score), _stream(stream)))
+
+
+def select_union(sel_idx, sel_cnt, n_kv_heads: int, max_blocks: int, uni_idx, uni_cnt,
+                 uni_mask, stream=None):
+    """Per KV head, the ascending union of its query heads' lists
+    (sel_idx [batch][H][max_sel]) with a head bit mask per block."""
+    import torch
+    call = "skv_select_union"
+    _need(call, _is(sel_idx, torch.int32, (None, None, None)), "sel_idx must be int32 3-D")
+    B, H, max_sel = (int(x) for x in sel_idx.shape)
+    _need(call, _is(sel_cnt, torch.int32, (B, H)), "sel_cnt must be int32 [batch][n_heads]")
+    _need(call, _is(uni_idx, torch.int32, (B, n_kv_heads, None)),
+          "uni_idx must be int32 [batch][n_kv_heads][max_union]")
+    max_union = int(uni_idx.shape[2])
+    _need(call, _is(uni_cnt, torch.int32, (B, n_kv_heads)), "uni_cnt must be int32 [batch][Hkv]")
+    _need(call, _is(uni_mask, uni_mask.dtype, (B, n_kv_heads, max_union))
+          and uni_mask.element_size() == 4, "uni_mask must be 32-bit like uni_idx")
+    _check(call, load().skv_select_union(
+        _ptr(sel_idx), _ptr(sel_cnt), B, H, int(n_kv_heads), max_sel, int(max_blocks), max_union,
+        _ptr(uni_idx), _ptr(uni_cnt), _ptr(uni_mask), _stream(stream)))
+
+
+def decode_attn_heads(cache: Cache, q, seq_len, max_len: int, softmax_scale: float,
+                      n_split: int, workspace, uni_idx, uni_cnt, uni_mask, stream=None):
+    """Split-K partial states with each query head over its own blocks (the
+    union list with head masks from select_union)."""
+    call = "skv_decode_attn_heads"
+    _check_q(call, cache, q, seq_len)
+    _check_sel(call, cache.batch, cache.n_kv_heads, uni_idx, uni_cnt)
+    _need(call, uni_mask is not None and tuple(uni_mask.shape) == tuple(uni_idx.shape)
+          and uni_mask.element_size() == 4, "uni_mask must be 32-bit like uni_idx")
+    _check(call, load().skv_decode_attn_heads(
+        ctypes.byref(cache.desc), _ptr(q), int(q.shape[1]), _ptr(seq_len), int(max_len),
+        _ptr(uni_idx), _ptr(uni_cnt), _ptr(uni_mask), int(uni_idx.shape[2]),
+        float(softmax_scale), int(n_split), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 def sparse_v_workspace_bytes(batch: int, n_heads: int, n_kv_heads: int, head_dim: int,

@@ -286,6 +286,71 @@ skv_status skv_decode_attn_select(const skv_cache* c, const float* q, int32_t n_
   return device_status(skv::launch_decode(p, stream));
 }
 
+skv_status skv_block_bounds_heads(const skv_cache* c, const float* q, int32_t n_heads,
+                                  const int32_t* seq_len, int32_t max_len, float* score,
+                                  hipStream_t stream) {
+  skv_status st = check_cache(c, true);
+  if (st != SKV_OK) return st;
+  if (q == nullptr || seq_len == nullptr || score == nullptr || !aligned(q)) return SKV_EINVAL;
+  st = check_heads(c, n_heads);
+  if (st != SKV_OK) return st;
+  if (max_len < 0 || max_len > c->max_seq) return SKV_ERANGE;
+  return device_status(skv::launch_bounds_heads(*c, q, n_heads, seq_len, max_len, score, stream));
+}
+
+skv_status skv_select_union(const int32_t* sel_idx, const int32_t* sel_cnt, int32_t batch,
+                            int32_t n_heads, int32_t n_kv_heads, int32_t max_sel,
+                            int32_t max_blocks, int32_t max_union, int32_t* uni_idx,
+                            int32_t* uni_cnt, uint32_t* uni_mask, hipStream_t stream) {
+  if (sel_idx == nullptr || sel_cnt == nullptr || uni_idx == nullptr || uni_cnt == nullptr ||
+      uni_mask == nullptr)
+    return SKV_EINVAL;
+  if (batch < 1 || n_kv_heads < 1 || n_heads < 1 || n_heads % n_kv_heads != 0) return SKV_EINVAL;
+  if (max_sel < 1 || max_blocks < 1 || max_union < 1) return SKV_EINVAL;
+  if (!supported_group(n_heads / n_kv_heads)) return SKV_EUNSUPPORTED;
+  if (max_blocks > kMaxSelectBlocks) return SKV_EUNSUPPORTED;
+  if (!grid_fits(batch, n_kv_heads, 1)) return SKV_ERANGE;
+  return device_status(skv::launch_union(sel_idx, sel_cnt, batch, n_kv_heads,
+                                         n_heads / n_kv_heads, max_sel, max_blocks, max_union,
+                                         uni_idx, uni_cnt, uni_mask, stream));
+}
+
+skv_status skv_decode_attn_heads(const skv_cache* c, const float* q, int32_t n_heads,
+                                 const int32_t* seq_len, int32_t max_len,
+                                 const int32_t* uni_idx, const int32_t* uni_cnt,
+                                 const uint32_t* uni_mask, int32_t max_union,
+                                 float softmax_scale, int32_t n_split, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream) {
+  skv_status st = check_cache(c, false);
+  if (st != SKV_OK) return st;
+  if (q == nullptr || seq_len == nullptr || !aligned(q)) return SKV_EINVAL;
+  if (uni_idx == nullptr || uni_cnt == nullptr || uni_mask == nullptr || max_union < 1)
+    return SKV_EINVAL;
+  st = check_heads(c, n_heads);
+  if (st != SKV_OK) return st;
+  if (n_split < 1 || n_split > kMaxSplit) return SKV_EINVAL;
+  if (!grid_fits(n_split, c->n_kv_heads, c->batch)) return SKV_ERANGE;
+  if (!(softmax_scale == softmax_scale) || softmax_scale < 0.0f) return SKV_EINVAL;
+  if (max_len < 0 || max_len > c->max_seq) return SKV_ERANGE;
+  const size_t need = skv_workspace_bytes(c->batch, n_heads, c->head_dim, n_split);
+  if (workspace == nullptr || workspace_bytes < need) return SKV_EWORKSPACE;
+  skv::DecodeParams p;
+  p.c = c;
+  p.q = q;
+  p.n_heads = n_heads;
+  p.seq_len = seq_len;
+  p.max_len = max_len;
+  p.sel_idx = uni_idx;
+  p.sel_cnt = uni_cnt;
+  p.max_sel = max_union;
+  p.softmax_scale = softmax_scale;
+  p.n_split = n_split;
+  p.ws = static_cast<float*>(workspace);
+  p.dbg_logits = nullptr;
+  p.sel_hmask = uni_mask;
+  return device_status(skv::launch_decode(p, stream));
+}
+
 size_t skv_sparse_v_workspace_bytes(int32_t batch, int32_t n_heads, int32_t n_kv_heads,
                                     int32_t head_dim, int32_t n_split, int32_t max_len) {
   if (batch < 1 || n_heads < 1 || n_kv_heads < 1 || !valid_head_dim(head_dim) || n_split < 1 ||

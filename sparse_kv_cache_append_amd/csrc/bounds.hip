@@ -163,7 +163,9 @@ __device__ __forceinline__ uint4 pack_bits(const uint16_t (&h)[8]) {
 // registers, so it does not matter whether this workgroup reads the side
 // cache before or after the append writes it: min/max with the same key is
 // idempotent, and a fresh block ignores the old values.
-template <int D, int G, int MODE>
+// PH: per-query-head bounds (score [batch][n_heads][max_blocks], no group
+// max): each query head ranks the blocks by its own bound.
+template <int D, int G, int MODE, bool PH = false>
 __global__ void __launch_bounds__(kBoundsThreads)
 bounds_kernel(uint16_t* __restrict__ kmin, uint16_t* __restrict__ kmax,
               const float* __restrict__ q, const int32_t* __restrict__ seq_len,
@@ -285,8 +287,11 @@ bounds_kernel(uint16_t* __restrict__ kmin, uint16_t* __restrict__ kmax,
       }
       acc = group16_sum(acc);
       best = fmaxf(best, acc);
+      if constexpr (PH) {
+        if (live && c == 0) score[(int64_t(b) * H + g * G + h) * max_blocks + j] = acc;
+      }
     }
-    if (live && c == 0) score[(int64_t(b) * Hkv + g) * max_blocks + j] = best;
+    if (!PH && live && c == 0) score[(int64_t(b) * Hkv + g) * max_blocks + j] = best;
   }
   // the append's stores
   if constexpr (MODE != kNoAppend) {
@@ -309,7 +314,7 @@ bounds_kernel(uint16_t* __restrict__ kmin, uint16_t* __restrict__ kmax,
   }
 }
 
-template <int G, int MODE>
+template <int G, int MODE, bool PH = false>
 hipError_t launch_bounds_g(const skv_cache& c, const float* q, const int32_t* seq_len,
                            int32_t max_len, float* score, const AppendOne& ap,
                            hipStream_t stream) {
@@ -321,7 +326,7 @@ hipError_t launch_bounds_g(const skv_cache& c, const float* q, const int32_t* se
   const int64_t n_wg = int64_t(tiles) * c.n_kv_heads * c.batch;
   if (n_wg > 0x7fffffff) return hipErrorInvalidValue;
   const dim3 grid(static_cast<uint32_t>(n_wg));
-  bounds_kernel<128, G, MODE><<<grid, kBoundsThreads, 0, stream>>>(
+  bounds_kernel<128, G, MODE, PH><<<grid, kBoundsThreads, 0, stream>>>(
       c.kmin, c.kmax, q, seq_len, score, c.n_kv_heads, max_len, c.block, max_blocks, tiles,
       c.n_kv_heads * c.batch, ap);
   return hipGetLastError();
@@ -346,6 +351,19 @@ hipError_t launch_bounds(const skv_cache& c, const float* q, int32_t n_heads,
                          const int32_t* seq_len, int32_t max_len, float* score,
                          hipStream_t stream) {
   return launch_bounds_m<kNoAppend>(c, q, n_heads, seq_len, max_len, score, AppendOne{}, stream);
+}
+
+hipError_t launch_bounds_heads(const skv_cache& c, const float* q, int32_t n_heads,
+                               const int32_t* seq_len, int32_t max_len, float* score,
+                               hipStream_t stream) {
+  const AppendOne ap{};
+  switch (n_heads / c.n_kv_heads) {
+    case 1: return launch_bounds_g<1, kNoAppend, true>(c, q, seq_len, max_len, score, ap, stream);
+    case 2: return launch_bounds_g<2, kNoAppend, true>(c, q, seq_len, max_len, score, ap, stream);
+    case 4: return launch_bounds_g<4, kNoAppend, true>(c, q, seq_len, max_len, score, ap, stream);
+    case 8: return launch_bounds_g<8, kNoAppend, true>(c, q, seq_len, max_len, score, ap, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_append_bounds(const skv_cache& c, const int32_t* pos0, const void* k_new,

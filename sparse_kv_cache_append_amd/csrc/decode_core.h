@@ -70,6 +70,10 @@ struct TileWalk {
   const int32_t* sel;
   int32_t jl, u0, n_units, tpb, block, L, nb;
   int32_t unit, sub;
+  // per-query-head lists: the row's head mask per list entry (bit i: query
+  // head i of the group chose the entry's block), lane i holding entry u0 + i
+  const uint32_t* hsel = nullptr;
+  uint32_t hl = ~0u;
 
   __device__ __forceinline__ void init(int w) {
     unit = w / tpb;
@@ -83,9 +87,13 @@ struct TileWalk {
   }
   // first row and valid-row count of the current tile, then advance by kMWaves tiles
   // (the walk state is wave-uniform: it lives in scalar registers)
-  template <int T>
-  __device__ __forceinline__ void next(int32_t& r0, int32_t& nvalid) {
+  // (HM: also the head mask of the tile's list entry)
+  template <int T, bool HM = false>
+  __device__ __forceinline__ void next(int32_t& r0, int32_t& nvalid, uint32_t* hm = nullptr) {
     int32_t j = u0 + unit;
+    if constexpr (HM)
+      *hm = unit < kWave ? uint32_t(__builtin_amdgcn_readlane(int32_t(hl), unit))
+                         : uint32_t(__builtin_amdgcn_readfirstlane(int32_t(hsel[j])));
     if (sel != nullptr)
       j = unit < kWave ? __builtin_amdgcn_readlane(jl, unit)
                        : __builtin_amdgcn_readfirstlane(sel[j]);
@@ -107,16 +115,21 @@ struct TileWalk {
 // ignored through n_units.
 struct ListSeed {
   int32_t cnt, jl;
+  uint32_t hl;
 };
 __device__ __forceinline__ ListSeed list_seed(const int32_t* sel_idx, const int32_t* sel_cnt,
                                               int32_t max_sel, int64_t bg, int32_t split,
-                                              int32_t units_per_split) {
-  ListSeed ls{0, -1};
+                                              int32_t units_per_split,
+                                              const uint32_t* sel_hmask = nullptr) {
+  ListSeed ls{0, -1, ~0u};
   if (sel_idx != nullptr) {
     const int lane = threadIdx.x % kWave;
     const int32_t e = split * units_per_split + lane;
     ls.cnt = sel_cnt[bg];
-    if (lane < units_per_split && e < max_sel) ls.jl = sel_idx[bg * max_sel + e];
+    if (lane < units_per_split && e < max_sel) {
+      ls.jl = sel_idx[bg * max_sel + e];
+      if (sel_hmask != nullptr) ls.hl = sel_hmask[bg * max_sel + e];
+    }
   }
   return ls;
 }
@@ -135,6 +148,7 @@ __device__ __forceinline__ TileWalk make_walk(const ListSeed& ls, const int32_t*
   tw.sel = nullptr;
   tw.jl = -1;
   tw.u0 = split * units_per_split;
+  tw.hl = ls.hl;
   if (sel_idx != nullptr) {
     tw.sel = sel_idx + bg * max_sel;
     tw.jl = ls.jl;

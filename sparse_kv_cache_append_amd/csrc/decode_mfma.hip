@@ -334,7 +334,7 @@ __device__ __forceinline__ void store_new_bounds(const AppendArgs& app, const Ap
 
 // ------------------------------------------------------------------ f16
 // Tile = 16 tokens: K and V tiles are 4 KiB each (4 load instructions).
-template <int G, int SELR, bool APP>
+template <int G, int SELR, bool APP, bool HM = false>
 __global__ void __launch_bounds__(kMThreads, 2)
 decode_f16_mfma(const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
                 const float* __restrict__ q, const int32_t* __restrict__ seq_len,
@@ -342,7 +342,7 @@ decode_f16_mfma(const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc
                 int32_t max_sel, int32_t Hkv, int32_t max_seq, int32_t block, int32_t max_len,
                 int32_t n_split, int32_t n_rows, int32_t units_per_split, float qscale2,
                 float* __restrict__ ws_m, float* __restrict__ ws_l, float* __restrict__ ws_o,
-                FusedSelect fs, AppendArgs app) {
+                FusedSelect fs, AppendArgs app, const uint32_t* __restrict__ sel_hmask) {
   constexpr int T = 16;
   constexpr int kTileBytes = T * kRowBytesF16;              // 4096
   __shared__ __attribute__((aligned(16))) uint8_t smem[kMWaves][2][2 * kTileBytes];
@@ -359,7 +359,8 @@ decode_f16_mfma(const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc
   // requests issued before anything waits: row length, given list, query
   const int32_t L_raw = seq_len[b];
   ListSeed ls{};
-  if constexpr (SELR == 0) ls = list_seed(sel_idx, sel_cnt, max_sel, bg, split, units_per_split);
+  if constexpr (SELR == 0)
+    ls = list_seed(sel_idx, sel_cnt, max_sel, bg, split, units_per_split, HM ? sel_hmask : nullptr);
   // folded append: the position and this lane's two channels of the new rows
   int32_t p_new = -1;
   uint32_t kx = 0u, vx = 0u;
@@ -395,6 +396,7 @@ decode_f16_mfma(const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc
     tw = fused_walk<T, SELR>(fs, max_sel, bg, b, L, L_raw, block, split, units_per_split);
   else
     tw = make_walk<T>(ls, sel_idx, max_sel, bg, L, block, split, units_per_split);
+  if constexpr (HM) tw.hsel = sel_hmask + bg * max_sel;
   tw.init(wave);
   float m_run = -INFINITY, l_run = 0.0f;
   float4_t O[8];
@@ -403,7 +405,7 @@ decode_f16_mfma(const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc
 
   const uint8_t* kbase = reinterpret_cast<const uint8_t*>(kc + bg * int64_t(max_seq) * kD);
   const uint8_t* vbase = reinterpret_cast<const uint8_t*>(vc + bg * int64_t(max_seq) * kD);
-  struct Frag { int4_t k[4], v[4]; int32_t r0, nvalid; };
+  struct Frag { int4_t k[4], v[4]; int32_t r0, nvalid; uint32_t hm; };
   // lane loads row 4*i + lane/16 (i = 0..3) of the tile, 16-byte chunk lane%16:
   // byte 1024 i + 16 lane of the tile, through the tile's buffer resource.
   // Its record count is the tile's valid bytes, so the rows of a partial
@@ -412,9 +414,11 @@ decode_f16_mfma(const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc
   // branch (the masked weights of those rows are zero).
   auto issue = [&](Frag& f) {
     int32_t r0 = 0, nv = 0;
-    if (tw.more()) tw.next<T>(r0, nv);
+    uint32_t hm = ~0u;
+    if (tw.more()) tw.next<T, HM>(r0, nv, &hm);
     f.r0 = r0;
     f.nvalid = nv;
+    f.hm = hm;
     static_assert(T * kRowBytesF16 == kTileRsrcBytes, "one buffer resource per tile");
     const uint32_t lo = 16u * uint32_t(lane);
     const int bytes = __builtin_amdgcn_readfirstlane(max(nv, 0) * kRowBytesF16);
@@ -452,6 +456,7 @@ decode_f16_mfma(const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc
       }
     }
     const int32_t nvalid = fr.nvalid;
+    const uint32_t hm = fr.hm;
     issue(fr);
     // LDS writes above and reads below touch the same array: they stay in
     // program order, and LDS executes one wavefront's accesses in order.
@@ -470,6 +475,12 @@ decode_f16_mfma(const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc
     if (nvalid < T) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) sc[r] = (4 * lg + r < nvalid) ? sc[r] : -INFINITY;
+    }
+    if constexpr (HM) {
+      // the heads that did not choose this block leave it out
+      const bool off = ((hm >> lc) & 1u) == 0u;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sc[r] = off ? -INFINITY : sc[r];
     }
     tile_softmax<G, 1, false>(sc, m_run, l_run, O);
     half4_t phi, plo;
@@ -559,7 +570,7 @@ decode_f16_mfma(const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc
 // O * 2^(7 - e), is rescaled (exactly, by a power of two) in the rare tile
 // where e grows, and is scaled back at the end.
 constexpr int kPwShiftI8 = 7;
-template <int G, int SELR, bool APP>
+template <int G, int SELR, bool APP, bool HM = false>
 __global__ void __launch_bounds__(kMThreads, 2)
 decode_i8_mfma(const int8_t* __restrict__ kc, const int8_t* __restrict__ vc,
                const float* __restrict__ ksc, const float* __restrict__ vsc,
@@ -568,7 +579,8 @@ decode_i8_mfma(const int8_t* __restrict__ kc, const int8_t* __restrict__ vc,
                int32_t max_sel, int32_t Hkv, int32_t max_seq, int32_t block, int32_t max_len,
                int32_t n_split, int32_t n_rows, int32_t units_per_split, float scale2,
                float* __restrict__ ws_m, float* __restrict__ ws_l, float* __restrict__ ws_o,
-               int32_t* __restrict__ dbg, FusedSelect fs, AppendArgs app) {
+               int32_t* __restrict__ dbg, FusedSelect fs, AppendArgs app,
+               const uint32_t* __restrict__ sel_hmask) {
   constexpr int T = 32;
   constexpr int kTileBytes = T * kRowBytesI8;               // 4096
   constexpr int kScaleOff = 2 * kTileBytes;                 // 32 K scales, 32 V scales
@@ -587,7 +599,8 @@ decode_i8_mfma(const int8_t* __restrict__ kc, const int8_t* __restrict__ vc,
   // requests issued before anything waits: row length, given list, query
   const int32_t L_raw = seq_len[b];
   ListSeed ls{};
-  if constexpr (SELR == 0) ls = list_seed(sel_idx, sel_cnt, max_sel, bg, split, units_per_split);
+  if constexpr (SELR == 0)
+    ls = list_seed(sel_idx, sel_cnt, max_sel, bg, split, units_per_split, HM ? sel_hmask : nullptr);
   // folded append: the position and this lane's two channels of the new rows
   int32_t p_new = -1;
   float2 kf = {0.0f, 0.0f}, vf = {0.0f, 0.0f};
@@ -622,6 +635,7 @@ decode_i8_mfma(const int8_t* __restrict__ kc, const int8_t* __restrict__ vc,
     tw = fused_walk<T, SELR>(fs, max_sel, bg, b, L, L_raw, block, split, units_per_split);
   else
     tw = make_walk<T>(ls, sel_idx, max_sel, bg, L, block, split, units_per_split);
+  if constexpr (HM) tw.hsel = sel_hmask + bg * max_sel;
   tw.init(wave);
   float m_run = -INFINITY, l_run = 0.0f;
   float4_t O[8];
@@ -638,7 +652,7 @@ decode_i8_mfma(const int8_t* __restrict__ kc, const int8_t* __restrict__ vc,
                             : nullptr;
   const int32_t last = max(L - 1, 0);
   const float* sbase = (lane < 32 ? ksb : vsb) + lane % 32;
-  struct Frag { int4_t k[4], v[4]; float sc; int32_t r0, nvalid; };
+  struct Frag { int4_t k[4], v[4]; float sc; int32_t r0, nvalid; uint32_t hm; };
   // lane loads row 8 i + lane / 8 (i = 0..3) of the tile, 16-byte chunk
   // lane % 8 (byte 1024 i + 16 lane of the tile), through the tile's buffer
   // resource whose record count is the valid bytes: rows past the row's
@@ -649,9 +663,11 @@ decode_i8_mfma(const int8_t* __restrict__ kc, const int8_t* __restrict__ vc,
   // no branch.
   auto issue = [&](Frag& f) {
     int32_t r0 = 0, nv = 0;
-    if (tw.more()) tw.next<T>(r0, nv);
+    uint32_t hm = ~0u;
+    if (tw.more()) tw.next<T, HM>(r0, nv, &hm);
     f.r0 = r0;
     f.nvalid = nv;
+    f.hm = hm;
     static_assert(T * kRowBytesI8 == kTileRsrcBytes, "one buffer resource per tile");
     const uint32_t lo = 16u * uint32_t(lane);
     const int bytes = __builtin_amdgcn_readfirstlane(max(nv, 0) * kRowBytesI8);
@@ -683,6 +699,7 @@ decode_i8_mfma(const int8_t* __restrict__ kc, const int8_t* __restrict__ vc,
     }
     float scl = fr.sc;
     const int32_t nvalid = fr.nvalid, r0 = fr.r0;
+    const uint32_t hm = fr.hm;
     if constexpr (APP) {
       // the appended token's codes and scales, if this tile holds it (the
       // scale also where a lane's clamped token is that token)
@@ -746,6 +763,12 @@ decode_i8_mfma(const int8_t* __restrict__ kc, const int8_t* __restrict__ vc,
 #pragma unroll
       for (int e = 0; e < 8; ++e)
         sc[e] = 16 * (e / 4) + 4 * lg + e % 4 < nvalid ? sc[e] : -INFINITY;
+    }
+    if constexpr (HM) {
+      // the heads that did not choose this block leave it out
+      const bool off = ((hm >> lc) & 1u) == 0u;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sc[e] = off ? -INFINITY : sc[e];
     }
     // O is kept in units of 2^(e_run - 7); the exact change of unit when e_run
     // grows rides on the softmax rescale of O
@@ -865,6 +888,8 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   const float scale2 = p.softmax_scale * kLog2e;
   const int fr = p.fused_r;
   const bool app = p.app.k_new != nullptr;
+  const bool hmk = p.sel_hmask != nullptr;
+  if (hmk && (p.sel_idx == nullptr || fr > 0 || app)) return hipErrorInvalidValue;
   AppendArgs aa{};
   if (app) {
     if (p.sel_idx != nullptr || fr > 0 || p.app.v_new == nullptr || p.app.pos0 == nullptr)
@@ -873,17 +898,18 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
                     p.app.pos0, (c.max_seq + c.block - 1) / c.block};
   }
   if (c.kv_dtype == SKV_F16) {
-#define SKV_LAUNCH_F16(GG, SR, AP)                                                              \
-  decode_f16_mfma<GG, SR, AP><<<grid, kMThreads, 0, stream>>>(                                 \
+#define SKV_LAUNCH_F16(GG, SR, AP, HMK)                                                         \
+  decode_f16_mfma<GG, SR, AP, HMK><<<grid, kMThreads, 0, stream>>>(                            \
       static_cast<const uint16_t*>(c.k), static_cast<const uint16_t*>(c.v), p.q, p.seq_len,    \
       p.sel_idx, p.sel_cnt, p.max_sel, c.n_kv_heads, c.max_seq, c.block, p.max_len, S,        \
-      n_rows, ups, scale2, ws_m, ws_l, ws_o, p.fsel, aa)
+      n_rows, ups, scale2, ws_m, ws_l, ws_o, p.fsel, aa, p.sel_hmask)
 #define SKV_F16_G(GG)                                  \
-  if (app) SKV_LAUNCH_F16(GG, 0, true);                \
-  else if (fr == 2) SKV_LAUNCH_F16(GG, 2, false);      \
-  else if (fr == 4) SKV_LAUNCH_F16(GG, 4, false);      \
-  else if (fr > 0) SKV_LAUNCH_F16(GG, kFusedSelR, false); \
-  else SKV_LAUNCH_F16(GG, 0, false)
+  if (app) SKV_LAUNCH_F16(GG, 0, true, false);         \
+  else if (hmk) SKV_LAUNCH_F16(GG, 0, false, true);    \
+  else if (fr == 2) SKV_LAUNCH_F16(GG, 2, false, false); \
+  else if (fr == 4) SKV_LAUNCH_F16(GG, 4, false, false); \
+  else if (fr > 0) SKV_LAUNCH_F16(GG, kFusedSelR, false, false); \
+  else SKV_LAUNCH_F16(GG, 0, false, false)
     switch (G) {
       case 1: SKV_F16_G(1); break;
       case 2: SKV_F16_G(2); break;
@@ -895,17 +921,19 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
     return hipGetLastError();
   }
   if (c.kv_dtype != SKV_I8) return hipErrorInvalidValue;
-#define SKV_LAUNCH_I8(GG, SR, AP)                                                               \
-  decode_i8_mfma<GG, SR, AP><<<grid, kMThreads, 0, stream>>>(                                  \
+#define SKV_LAUNCH_I8(GG, SR, AP, HMK)                                                          \
+  decode_i8_mfma<GG, SR, AP, HMK><<<grid, kMThreads, 0, stream>>>(                             \
       static_cast<const int8_t*>(c.k), static_cast<const int8_t*>(c.v), c.k_scale, c.v_scale,  \
       p.q, p.seq_len, p.sel_idx, p.sel_cnt, p.max_sel, c.n_kv_heads, c.max_seq, c.block,       \
-      p.max_len, S, n_rows, ups, scale2, ws_m, ws_l, ws_o, p.dbg_logits, p.fsel, aa)
+      p.max_len, S, n_rows, ups, scale2, ws_m, ws_l, ws_o, p.dbg_logits, p.fsel, aa,          \
+      p.sel_hmask)
 #define SKV_I8_G(GG)                                   \
-  if (app) SKV_LAUNCH_I8(GG, 0, true);                 \
-  else if (fr == 2) SKV_LAUNCH_I8(GG, 2, false);       \
-  else if (fr == 4) SKV_LAUNCH_I8(GG, 4, false);       \
-  else if (fr > 0) SKV_LAUNCH_I8(GG, kFusedSelR, false); \
-  else SKV_LAUNCH_I8(GG, 0, false)
+  if (app) SKV_LAUNCH_I8(GG, 0, true, false);          \
+  else if (hmk) SKV_LAUNCH_I8(GG, 0, false, true);     \
+  else if (fr == 2) SKV_LAUNCH_I8(GG, 2, false, false); \
+  else if (fr == 4) SKV_LAUNCH_I8(GG, 4, false, false); \
+  else if (fr > 0) SKV_LAUNCH_I8(GG, kFusedSelR, false, false); \
+  else SKV_LAUNCH_I8(GG, 0, false, false)
   switch (G) {
     case 1: SKV_I8_G(1); break;
     case 2: SKV_I8_G(2); break;

@@ -57,6 +57,7 @@ struct DecodeParams {
                             // per thread (sel_idx/sel_cnt then receive the list)
   FusedSelect fsel{};
   FoldedAppend app{};       // dense walks only (sel_idx == nullptr, fused_r == 0)
+  const uint32_t* sel_hmask = nullptr;   // per-query-head lists: head mask per entry
 };
 
 hipError_t launch_append(const skv_cache& c, const int32_t* pos0, int32_t n_new,
@@ -83,6 +84,17 @@ hipError_t launch_append_bounds(const skv_cache& c, const int32_t* pos0, const v
                                 const void* v_new, const float* q, int32_t n_heads,
                                 const int32_t* seq_len, int32_t max_len, float* score,
                                 hipStream_t stream);
+
+// Per-query-head bounds: score [batch][n_heads][max_blocks], no group max.
+hipError_t launch_bounds_heads(const skv_cache& c, const float* q, int32_t n_heads,
+                               const int32_t* seq_len, int32_t max_len, float* score,
+                               hipStream_t stream);
+
+// Union of a KV head's per-query-head lists with a head mask per block.
+hipError_t launch_union(const int32_t* sel_idx, const int32_t* sel_cnt, int32_t batch,
+                        int32_t n_kv_heads, int32_t group, int32_t max_sel, int32_t max_blocks,
+                        int32_t max_union, int32_t* uni_idx, int32_t* uni_cnt,
+                        uint32_t* uni_mask, hipStream_t stream);
 
 hipError_t launch_select(const float* score, const int32_t* seq_len, int32_t batch,
                          int32_t n_kv_heads, int32_t max_blocks, int32_t block,

@@ -86,6 +86,66 @@ select_kernel(const float* __restrict__ score, const int32_t* __restrict__ seq_l
   }
 }
 
+// The union of a KV head's per-query-head lists (ascending), each block with
+// the bits of the heads (within the group) that chose it.  One workgroup per
+// (sequence, KV head): the heads' entries set their bit in a byte per block
+// (LDS, four blocks per word), then the marked blocks are compacted in
+// ascending order with a workgroup prefix sum.
+__global__ void __launch_bounds__(kSelThreads)
+union_kernel(const int32_t* __restrict__ sel_idx, const int32_t* __restrict__ sel_cnt,
+             int32_t Hkv, int32_t G, int32_t max_sel, int32_t max_blocks, int32_t max_union,
+             int32_t* __restrict__ uni_idx, int32_t* __restrict__ uni_cnt,
+             uint32_t* __restrict__ uni_mask) {
+  __shared__ uint32_t hw[kMaxSelectBlocks / 4];
+  __shared__ int32_t wsum[kSelThreads / kWave];
+  const int32_t row = int32_t(blockIdx.x);
+  const int32_t b = row / Hkv, g = row % Hkv;
+  const int32_t H = Hkv * G;
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int32_t n_words = (max_blocks + 3) / 4;
+  for (int32_t w = tid; w < n_words; w += kSelThreads) hw[w] = 0u;
+  __syncthreads();
+  for (int32_t i = 0; i < G; ++i) {
+    const int64_t hrow = int64_t(b) * H + g * G + i;
+    const int32_t cnt = min(max(sel_cnt[hrow], 0), max_sel);
+    for (int32_t e = tid; e < cnt; e += kSelThreads) {
+      const int32_t j = sel_idx[hrow * max_sel + e];
+      if (j >= 0 && j < max_blocks) atomicOr(&hw[j >> 2], (1u << i) << (8 * (j & 3)));
+    }
+  }
+  __syncthreads();
+  // thread t owns blocks [t * per, (t + 1) * per)
+  const int32_t per = (max_blocks + kSelThreads - 1) / kSelThreads;
+  const int32_t j0 = tid * per, j1 = min(j0 + per, max_blocks);
+  int32_t c = 0;
+  for (int32_t j = j0; j < j1; ++j) c += ((hw[j >> 2] >> (8 * (j & 3))) & 0xFFu) != 0u;
+  const int32_t incl = wave_incl_scan(c);
+  if (lane == kWave - 1) wsum[wave] = incl;
+  __syncthreads();
+  int32_t base = 0, total = 0;
+  for (int w = 0; w < kSelThreads / kWave; ++w) {
+    base += w < wave ? wsum[w] : 0;
+    total += wsum[w];
+  }
+  int32_t pos = base + incl - c;
+  const int64_t out = int64_t(row) * max_union;
+  for (int32_t j = j0; j < j1; ++j) {
+    const uint32_t m = (hw[j >> 2] >> (8 * (j & 3))) & 0xFFu;
+    if (m != 0u) {
+      if (pos < max_union) {
+        uni_idx[out + pos] = j;
+        uni_mask[out + pos] = m;
+      }
+      ++pos;
+    }
+  }
+  for (int32_t p = total + tid; p < max_union; p += kSelThreads) {
+    uni_idx[out + p] = -1;
+    uni_mask[out + p] = 0u;
+  }
+  if (tid == 0) uni_cnt[row] = total;
+}
+
 }  // namespace
 
 hipError_t launch_select(const float* score, const int32_t* seq_len, int32_t batch,
@@ -105,6 +165,19 @@ hipError_t launch_select(const float* score, const int32_t* seq_len, int32_t bat
   else if (max_blocks <= 16 * kSelThreads) SKV_LAUNCH_SELECT(16);
   else SKV_LAUNCH_SELECT(64);
 #undef SKV_LAUNCH_SELECT
+  return hipGetLastError();
+}
+
+hipError_t launch_union(const int32_t* sel_idx, const int32_t* sel_cnt, int32_t batch,
+                        int32_t n_kv_heads, int32_t group, int32_t max_sel, int32_t max_blocks,
+                        int32_t max_union, int32_t* uni_idx, int32_t* uni_cnt,
+                        uint32_t* uni_mask, hipStream_t stream) {
+  if (max_blocks > kMaxSelectBlocks || group < 1 || group > 8) return hipErrorInvalidValue;
+  const int64_t rows = int64_t(batch) * n_kv_heads;
+  if (rows > 0x7fffffff) return hipErrorInvalidValue;
+  union_kernel<<<dim3(uint32_t(rows)), kSelThreads, 0, stream>>>(
+      sel_idx, sel_cnt, n_kv_heads, group, max_sel, max_blocks, max_union, uni_idx, uni_cnt,
+      uni_mask);
   return hipGetLastError();
 }
 

@@ -1,0 +1,166 @@
+"""Per-query-head block selection on the GPU (skv_block_bounds_heads,
+skv_select_topk over per-head rows, skv_select_union,
+skv_decode_attn_heads) against the oracle (oracle/quest.py:
+select_blocks_per_head, union_with_heads): per-head bounds within float32
+rounding of the exact-sum bounds and bit-equal to the group path's values,
+selections bit-exact on the GPU's own scores and equal to the float64 ones up
+to reported near-ties, the union and its head masks bit-exact, each head's
+output element-wise against attention over its own blocks."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_kv_cache_append_amd as skv
+import workloads
+from gpu_harness import DEV, assert_close, build_cache, device_inputs, quantized_host
+from oracle import quest
+
+pytestmark = pytest.mark.gpu
+
+
+def _print(*a):
+    print("[per-head]", *a, flush=True)
+
+
+def run_per_head(cache, w, S=None):
+    q, seq_len = device_inputs(w)
+    max_len = max(w.lens)
+    H, Hkv, B = w.H, w.Hkv, w.B
+    max_sel = max(w.k_sel) + w.n_sink + w.n_recent
+    score_h = torch.full((B, H, cache.max_blocks), float("nan"), device=DEV)
+    score_g = torch.full((B, Hkv, cache.max_blocks), float("nan"), device=DEV)
+    sel = torch.full((B, H, max_sel), -7, dtype=torch.int32, device=DEV)
+    cnt = torch.full((B, H), -7, dtype=torch.int32, device=DEV)
+    max_union = min(cache.max_blocks, w.G * max_sel)
+    uni = torch.full((B, Hkv, max_union), -7, dtype=torch.int32, device=DEV)
+    ucnt = torch.full((B, Hkv), -7, dtype=torch.int32, device=DEV)
+    umask = torch.full((B, Hkv, max_union), 7, dtype=torch.int32, device=DEV)
+    ks = torch.tensor(w.k_sel, dtype=torch.int32, device=DEV)
+    skv.block_bounds_heads(cache, q, seq_len, max_len, score_h)
+    skv.block_bounds(cache, q, seq_len, max_len, score_g)
+    skv.select_topk(score_h, seq_len, w.block, ks, w.n_sink, w.n_recent, sel, cnt)
+    skv.select_union(sel, cnt, Hkv, cache.max_blocks, uni, ucnt, umask)
+    S = S or skv.default_split(B, Hkv, max_union, kv_dtype=w.kv_dtype, sparse=True)
+    ws = torch.empty(skv.workspace_bytes(B, H, w.D, S), dtype=torch.uint8, device=DEV)
+    out = torch.empty((B, H, w.D), dtype=torch.float32, device=DEV)
+    skv.decode_attn_heads(cache, q, seq_len, max_len, w.softmax_scale, S, ws, uni, ucnt, umask)
+    skv.combine(ws, B, H, w.D, S, out)
+    torch.cuda.synchronize()
+    return dict(score_h=score_h.cpu().numpy(), score_g=score_g.cpu().numpy(),
+                sel=sel.cpu().numpy(), cnt=cnt.cpu().numpy(), uni=uni.cpu().numpy(),
+                ucnt=ucnt.cpu().numpy(), umask=umask.cpu().numpy().view(np.uint32),
+                out=out.cpu().numpy(), max_union=max_union)
+
+
+def check(w, r, seqs=None, keys_of=None):
+    tol = 1e-3 if w.kv_dtype == "f16" else 1e-4
+    near_total = 0
+    for b in (range(w.B) if seqs is None else seqs):
+        nb = w.n_blocks(b)
+        keys = w.k[b] if keys_of is None else keys_of(b)
+        kmin, kmax = oracle.block_bounds(keys, w.lens[b], w.block)
+        ub = oracle.upper_bounds(w.q[b], kmin, kmax)                    # [H][NB]
+        sh = r["score_h"][b, :, :nb]
+        np.testing.assert_allclose(sh, ub, rtol=2e-6, atol=1e-4)
+        # the group path's score is the max of these very values
+        gmax = sh.reshape(w.Hkv, w.G, nb).max(axis=1)
+        assert np.array_equal(gmax.view(np.uint32), r["score_g"][b, :, :nb].view(np.uint32))
+        if w.kv_dtype == "i8":
+            kc, ks, vc, vs = quantized_host(w, b)
+        for g in range(w.Hkv):
+            sets = []
+            for i in range(w.G):
+                h = g * w.G + i
+                got = r["sel"][b, h, :r["cnt"][b, h]]
+                own = oracle.select_blocks(sh[h], nb, w.k_sel[b], w.n_sink, w.n_recent)
+                assert np.array_equal(got, own["sel"]), (b, h)
+                ref = oracle.select_blocks(ub[h], nb, w.k_sel[b], w.n_sink, w.n_recent)
+                diff = set(got.tolist()) ^ set(ref["sel"].tolist())
+                assert diff <= set(ref["near"].tolist()), (b, h, diff)
+                near_total += len(diff)
+                sets.append(got)
+            u, m = quest.union_with_heads(sets)
+            assert r["ucnt"][b, g] == u.size
+            n = min(u.size, r["max_union"])
+            assert np.array_equal(r["uni"][b, g, :n], u[:n])
+            assert np.array_equal(r["umask"][b, g, :n].astype(np.int64), m[:n])
+            assert np.all(r["uni"][b, g, n:] == -1) and np.all(r["umask"][b, g, n:] == 0)
+            for i in range(w.G):
+                h = g * w.G + i
+                toks = oracle.selected_tokens(sets[i], w.lens[b], w.block)
+                if w.kv_dtype == "f16":
+                    ref = oracle.attend_f16(w.q[b][h:h + 1], w.k[b][g:g + 1], w.v[b][g:g + 1],
+                                            w.softmax_scale, tokens=toks)
+                else:
+                    sl = slice(g, g + 1)
+                    ref = oracle.attend_i8(w.q[b][h:h + 1], kc[sl], ks[sl], vc[sl], vs[sl],
+                                           w.softmax_scale, tokens=toks)
+                assert_close(r["out"][b, h], ref[0], tol, b, h)
+    return near_total
+
+
+CASES = [
+    # seeds, H, Hkv, lens, kv, n_dirs, k_sel, n_sink, n_recent, block
+    ([801, 802], 32, 8, [5000, 777], "f16", 16, [20, 4], 1, 2, 64),
+    ([803], 8, 8, [3001], "f16", 8, [9], 1, 2, 64),
+    ([804], 16, 8, [4100], "i8", 16, [12], 1, 4, 64),
+    ([805, 806, 807], 32, 4, [2000, 1, 6500], "i8", 32, [7, 0, 30], 1, 2, 64),
+    ([808], 16, 8, [2500], "f16", 8, [30], 0, 1, 16),
+]
+
+
+@pytest.mark.parametrize("seeds,H,Hkv,lens,kv,nd,ksel,ns,nr,blk", CASES)
+def test_per_head_selection(gpu_lib, seeds, H, Hkv, lens, kv, nd, ksel, ns, nr, blk):
+    _print(H, Hkv, lens, kv, ksel)
+    w = workloads.clustered(seeds, H, Hkv, 128, lens, kv, n_dirs=nd, k_sel=ksel, n_sink=ns,
+                            n_recent=nr, block=blk)
+    cache = build_cache(w)
+    r = run_per_head(cache, w)
+    near = check(w, r, keys_of=(lambda b: w.k[b]))
+    _print("near-tie differences", near)
+
+
+def test_per_head_union_truncated(gpu_lib):
+    """A union longer than max_union: the count reports the full size, the
+    list holds its first max_union blocks."""
+    w = workloads.clustered([809], 32, 8, 128, [8000], "f16", n_dirs=32, k_sel=[20], n_sink=1,
+                            n_recent=2)
+    cache = build_cache(w)
+    q, seq_len = device_inputs(w)
+    sc = torch.empty((1, 32, cache.max_blocks), device=DEV)
+    sel = torch.empty((1, 32, 23), dtype=torch.int32, device=DEV)
+    cnt = torch.empty((1, 32), dtype=torch.int32, device=DEV)
+    skv.block_bounds_heads(cache, q, seq_len, 8000, sc)
+    skv.select_topk(sc, seq_len, 64, torch.tensor([20], dtype=torch.int32, device=DEV), 1, 2,
+                    sel, cnt)
+    uni = torch.empty((1, 8, 10), dtype=torch.int32, device=DEV)
+    ucnt = torch.empty((1, 8), dtype=torch.int32, device=DEV)
+    um = torch.empty((1, 8, 10), dtype=torch.int32, device=DEV)
+    skv.select_union(sel, cnt, 8, cache.max_blocks, uni, ucnt, um)
+    torch.cuda.synchronize()
+    s_h, c_h = sel.cpu().numpy(), cnt.cpu().numpy()
+    for g in range(8):
+        u, m = quest.union_with_heads([s_h[0, h, :c_h[0, h]] for h in range(4 * g, 4 * g + 4)])
+        assert ucnt[0, g].item() == u.size > 10
+        assert uni[0, g].cpu().numpy().tolist() == u[:10].tolist()
+        assert um[0, g].cpu().numpy().astype(np.int64).tolist() == m[:10].tolist()
+
+
+def test_per_head_32k_workload(gpu_lib):
+    """The 32K workload with per-head sets, in the bench's launch shape."""
+    w = workloads.named(3)
+    cache = build_cache(w)
+    r = run_per_head(cache, w)
+    near = check(w, r)
+    _print("32K near-tie differences", near, "union blocks per KV head",
+           r["ucnt"][0].tolist())
+
+
+def test_per_head_262k_int8_workload(gpu_lib):
+    w = workloads.named(5)
+    cache = build_cache(w)
+    r = run_per_head(cache, w)
+    near = check(w, r, keys_of=(lambda b: w.k[b]))
+    _print("262K near-tie differences", near, "union blocks per KV head",
+           r["ucnt"][0].tolist())
