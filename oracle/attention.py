@@ -23,7 +23,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .quant import quantize_rows
+from .quant import dequantize_groups, quantize_rows
 
 
 def _softmax_weights(s: np.ndarray) -> np.ndarray:
@@ -150,3 +150,13 @@ def combine_partials(m: np.ndarray, l: np.ndarray, a: np.ndarray, base: float = 
     M = np.max(m[live])
     w = np.power(base, m[live] - M)
     return (w @ np.asarray(a, np.float64)[live]) / np.sum(w * np.asarray(l, np.float64)[live])
+
+
+def attend_grouped(q, k_codes, k_scales, v_codes, v_scales, scale, tokens=None):
+    """Attention over a group-wise quantized cache (q8_0 / q4_0): the
+    definition applied to the dequantized values scale * code (exact in
+    float64), the query unquantized.  codes [Hkv][L][D] int8, scales
+    [Hkv][L][D / 32] float16.  Returns [H][D] float64."""
+    kd = dequantize_groups(k_codes, k_scales)
+    vd = dequantize_groups(v_codes, v_scales)
+    return attend_f16(q, kd, vd, scale, tokens)
