@@ -58,8 +58,14 @@ LLC_BYTES = 256 * 2 ** 20
 # ------------------------------------------------------------- accounting
 def kv_bytes_per_token(kv_dtype: str, D: int) -> int:
     """Algorithmic bytes of one attended (token, KV head): K and V rows, plus
-    the two float32 scales for int8."""
-    return 4 * D if kv_dtype == "f16" else 2 * D + 8
+    the two float32 scales for int8, or the f16 scale of every 32-channel
+    group of both rows for q8_0 (int8 codes) and q4_0 (4-bit codes)."""
+    if kv_dtype == "f16":
+        return 4 * D
+    if kv_dtype == "i8":
+        return 2 * D + 8
+    codes = D if kv_dtype == "q8_0" else D // 2
+    return 2 * (codes + 2 * (D // 32))
 
 
 def side_cache_bytes_per_block(D: int) -> int:
@@ -175,6 +181,11 @@ class OracleStep:
                 kc, ks = oracle.quantize_rows(w.k[b])
                 vc, vs = oracle.quantize_rows(w.v[b])
                 self.codes[b] = (kc, ks, vc, vs)
+            elif w.kv_dtype in ("q8_0", "q4_0"):
+                qmax = oracle.QMAX_Q8 if w.kv_dtype == "q8_0" else oracle.QMAX_Q4
+                kc, ks = oracle.quantize_groups(w.k[b], qmax)
+                vc, vs = oracle.quantize_groups(w.v[b], qmax)
+                self.codes[b] = (kc, ks, vc, vs)
 
     def unit(self, bg):
         o, w = self.oracle, self.w
@@ -201,7 +212,9 @@ class OracleStep:
             return o.attend_f16(q, w.k[b][g:g + 1], w.v[b][g:g + 1], w.softmax_scale, tokens=toks)
         kc, ks, vc, vs = self.codes[b]
         sl = slice(g, g + 1)
-        return o.attend_i8(q, kc[sl], ks[sl], vc[sl], vs[sl], w.softmax_scale, tokens=toks)
+        if w.kv_dtype == "i8":
+            return o.attend_i8(q, kc[sl], ks[sl], vc[sl], vs[sl], w.softmax_scale, tokens=toks)
+        return o.attend_grouped(q, kc[sl], ks[sl], vc[sl], vs[sl], w.softmax_scale, tokens=toks)
 
 
 _POOL_STEP = None
@@ -527,10 +540,11 @@ def measure(w, args, quest: bool, dense: bool, detail: bool = False):
             res["quest"]["warm_us_per_step"] = round(warm, 3)
         if detail:
             res["_roofline"] = (dec_bytes, sel_us, dec_us)
-        if not args.no_per_head:
+        grouped = w.kv_dtype in ("q8_0", "q4_0")      # per-head and sparse-V: f16 and int8
+        if not args.no_per_head and not grouped:
             res["quest_per_head"] = measure_per_head(T, skv, torch, w, caches, R, q, seq_len, Lmax,
                                                      new_k, new_v, pos_last, ks, res["quest"])
-        if args.sparse_v_tau > 0:
+        if args.sparse_v_tau > 0 and not grouped:
             res["quest_sparse_v"] = measure_sparse_v(
                 T, skv, torch, w, caches, R, q, seq_len, Lmax, new_k, new_v, pos_last, ks, score,
                 sel, cnt, attended, args.sparse_v_tau, calls_us)
@@ -673,9 +687,10 @@ def main():
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--mode", choices=("both", "quest", "dense"), default="both",
                     help="which step of the 32K workload to time (profiling runs use one)")
-    ap.add_argument("--workloads", default="1,2,4,5,3@16384",
+    ap.add_argument("--workloads", default="1,2,4,5,3@16384,3q8,3q4",
                     help="other workloads to time besides the 32K headline ('' = none; "
-                         "3@L = the 32K Quest generator at context L)")
+                         "3@L = the 32K Quest generator at context L; 3q8 / 3q4 = over a "
+                         "q8_0 / q4_0 cache)")
     ap.add_argument("--no-per-head", action="store_true",
                     help="skip the Quest steps with one block set per query head")
     ap.add_argument("--sparse-v-tau", type=float, default=1e-3,
@@ -699,6 +714,10 @@ def main():
         if tok.startswith("3@"):
             # the 32K generator at another length (Quest vs dense from 16K up)
             jobs.append((workloads.quest32k_at(int(tok[2:])), True, True, False))
+        elif tok.startswith("3q"):
+            # the 32K generator over a group-wise quantized cache (3q8, 3q4)
+            jobs.append((workloads.quest32k_quant("q8_0" if tok == "3q8" else "q4_0"), True,
+                         True, False))
         elif int(tok) != 3:
             w = workloads.named(int(tok))
             jobs.append((w, bool(w.k_sel), True, False))

@@ -67,7 +67,9 @@ typedef enum skv_status {
 typedef enum skv_dtype {
   SKV_F16 = 1,
   SKV_F32 = 2,
-  SKV_I8 = 3
+  SKV_I8 = 3,
+  SKV_Q8_0 = 4,   /* group-wise: 32-channel groups, int8 codes, an f16 scale each */
+  SKV_Q4_0 = 5    /* group-wise: 32-channel groups, 4-bit codes, an f16 scale each */
 } skv_dtype;
 
 /*
@@ -83,6 +85,21 @@ typedef enum skv_dtype {
  *               before quantization (sparse_attn.md, "Method" and
  *               "All-KV-types composition").  Both NULL = no side cache
  *               (dense only; appends then skip the bounds update).
+ * Group-wise quantized caches (SKV_Q8_0, SKV_Q4_0; sparse_attn.md, "All-KV-
+ * types composition": quantized blocks of 32 values with the side cache
+ * filled before quantization):
+ *   k, v      : [batch][n_kv_heads][max_seq][row] bytes, row = head_dim
+ *               (q8_0: int8 codes -127..127) or head_dim / 2 (q4_0: channel
+ *               2i in the low nibble of byte i, 2i + 1 in the high nibble,
+ *               each code + 8, codes -7..7);
+ *   k_scale,
+ *   v_scale   : f16 bit patterns (uint16_t storage behind the float*
+ *               pointers) [batch][n_kv_heads][max_seq][head_dim / 32], the
+ *               scale of each group of 32 consecutive channels.
+ *   Per group: a = max |x|, scale = f16(a / QMAX) (QMAX 127 or 7), code =
+ *   clamp(rint(x / scale), -QMAX, QMAX) against the stored scale (a scale of
+ *   0, or beyond f16's range, gives codes 0); a value is scale * code, and
+ *   attention runs on those values with the float32 query.
  * Token t of sequence b lives at position t (0-based) of its row.
  */
 typedef struct skv_cache {
@@ -121,8 +138,9 @@ int32_t skv_max_blocks(const skv_cache* c);
  *   k_new,
  *   v_new  : device [batch][n_new][n_kv_heads][head_dim] of src_dtype:
  *            SKV_F16 for an f16 cache (copied bit for bit), SKV_F32 for an
- *            int8 cache (quantized; side-cache bounds are the float32 min
- *            rounded toward -inf and max rounded toward +inf into f16).
+ *            int8, q8_0 or q4_0 cache (quantized; side-cache bounds are the
+ *            float32 min rounded toward -inf and max rounded toward +inf into
+ *            f16).
  * Errors: SKV_EINVAL (NULL, n_new < 1), SKV_ERANGE (n_new > max_seq),
  * SKV_EUNSUPPORTED (other dtype pairs), SKV_EDEVICE.
  */

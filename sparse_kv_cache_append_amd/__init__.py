@@ -27,12 +27,13 @@ __all__ = ["load", "Cache", "SkvError", "kv_append", "block_bounds", "select_top
            "decode_attn", "decode_attn_select", "decode_attn_sparse_v", "sparse_v_workspace_bytes",
            "block_bounds_heads", "select_union", "decode_attn_heads",
            "decode_step", "decode_step_static", "combine", "workspace_bytes", "status_str", "decode",
-           "SKV_F16", "SKV_F32", "SKV_I8", "LIB_PATH", "EXPORTS"]
+           "SKV_F16", "SKV_F32", "SKV_I8", "SKV_Q8_0", "SKV_Q4_0", "LIB_PATH", "EXPORTS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libskv.so")
 
 SKV_OK, SKV_EINVAL, SKV_ERANGE, SKV_EWORKSPACE, SKV_EUNSUPPORTED, SKV_EDEVICE = 0, -1, -2, -3, -4, -5
-SKV_F16, SKV_F32, SKV_I8 = 1, 2, 3
+SKV_F16, SKV_F32, SKV_I8, SKV_Q8_0, SKV_Q4_0 = 1, 2, 3, 4, 5
+_KV_CODES = {"f16": SKV_F16, "i8": SKV_I8, "q8_0": SKV_Q8_0, "q4_0": SKV_Q4_0}
 
 EXPORTS = ("skv_max_blocks", "skv_kv_append", "skv_block_bounds", "skv_select_topk",
            "skv_decode_attn", "skv_decode_attn_select", "skv_decode_step",
@@ -195,34 +196,47 @@ def _stream(stream) -> Optional[int]:
 class Cache:
     """KV cache tensors plus the C descriptor.
 
-    k, v: [batch][n_kv_heads][max_seq][head_dim] (float16 or int8);
-    k_scale, v_scale: [batch][n_kv_heads][max_seq] float32 (int8 only);
+    kv_dtype "f16": k, v [batch][n_kv_heads][max_seq][head_dim] float16.
+    kv_dtype "i8": k, v int8 codes, same shape; k_scale, v_scale
+    [batch][n_kv_heads][max_seq] float32.
+    kv_dtype "q8_0" / "q4_0" (groups of 32 channels): k, v uint8
+    [batch][n_kv_heads][max_seq][head_dim] (q8_0 int8 codes) or [...][head_dim
+    / 2] (q4_0 nibbles); k_scale, v_scale float16 [batch][n_kv_heads][max_seq]
+    [head_dim / 32].
     kmin, kmax: [batch][n_kv_heads][max_blocks][head_dim] float16 (Quest side
     cache, allocated when ``bounds``)."""
 
     def __init__(self, batch: int, n_kv_heads: int, max_seq: int, head_dim: int = 128,
                  kv_dtype: str = "f16", block: int = 64, bounds: bool = True, device="cuda"):
         import torch
-        if kv_dtype not in ("f16", "i8"):
-            raise ValueError("kv_dtype must be 'f16' or 'i8'")
+        if kv_dtype not in _KV_CODES:
+            raise ValueError("kv_dtype must be 'f16', 'i8', 'q8_0' or 'q4_0'")
         self.batch, self.n_kv_heads, self.max_seq = batch, n_kv_heads, max_seq
         self.head_dim, self.block, self.kv_dtype = head_dim, block, kv_dtype
         self.max_blocks = -(-max_seq // block)
         shape = (batch, n_kv_heads, max_seq, head_dim)
-        dt = torch.float16 if kv_dtype == "f16" else torch.int8
-        self.k = torch.zeros(shape, dtype=dt, device=device)
-        self.v = torch.zeros(shape, dtype=dt, device=device)
+        if kv_dtype in ("q8_0", "q4_0"):
+            row = head_dim if kv_dtype == "q8_0" else head_dim // 2
+            self.k = torch.zeros(shape[:3] + (row,), dtype=torch.uint8, device=device)
+            self.v = torch.zeros(shape[:3] + (row,), dtype=torch.uint8, device=device)
+        else:
+            dt = torch.float16 if kv_dtype == "f16" else torch.int8
+            self.k = torch.zeros(shape, dtype=dt, device=device)
+            self.v = torch.zeros(shape, dtype=dt, device=device)
         self.k_scale = self.v_scale = None
         if kv_dtype == "i8":
             self.k_scale = torch.zeros(shape[:3], dtype=torch.float32, device=device)
             self.v_scale = torch.zeros(shape[:3], dtype=torch.float32, device=device)
+        elif kv_dtype in ("q8_0", "q4_0"):
+            gshape = shape[:3] + (head_dim // 32,)
+            self.k_scale = torch.zeros(gshape, dtype=torch.float16, device=device)
+            self.v_scale = torch.zeros(gshape, dtype=torch.float16, device=device)
         self.kmin = self.kmax = None
         if bounds:
             bshape = (batch, n_kv_heads, self.max_blocks, head_dim)
             self.kmin = torch.zeros(bshape, dtype=torch.float16, device=device)
             self.kmax = torch.zeros(bshape, dtype=torch.float16, device=device)
-        self.desc = SkvCacheDesc(batch, n_kv_heads, head_dim, max_seq, block,
-                                 SKV_F16 if kv_dtype == "f16" else SKV_I8,
+        self.desc = SkvCacheDesc(batch, n_kv_heads, head_dim, max_seq, block, _KV_CODES[kv_dtype],
                                  _ptr(self.k), _ptr(self.v), _ptr(self.k_scale),
                                  _ptr(self.v_scale), _ptr(self.kmin), _ptr(self.kmax))
 

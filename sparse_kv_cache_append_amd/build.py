@@ -23,7 +23,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libskv.so")
 
 SOURCES = ["api.cpp", "append.hip", "bounds.hip", "select.hip", "decode_mfma.hip",
-           "combine.hip", "static_step.hip", "sparse_v.hip"]
+           "combine.hip", "static_step.hip", "sparse_v.hip",
+           "decode_grouped.hip"]
 ARCH = "gfx950"
 
 

@@ -32,9 +32,10 @@ skv_status check_cache(const skv_cache* c, bool need_bounds) {
   if (c->batch < 1 || c->n_kv_heads < 1 || c->max_seq < 1) return SKV_EINVAL;
   if (!valid_head_dim(c->head_dim)) return SKV_EINVAL;
   if (c->block < 16 || c->block % 16 != 0) return SKV_EINVAL;
-  if (c->kv_dtype != SKV_F16 && c->kv_dtype != SKV_I8) return SKV_EINVAL;
+  if (c->kv_dtype != SKV_F16 && c->kv_dtype != SKV_I8 && !skv::is_grouped(c->kv_dtype))
+    return SKV_EINVAL;
   if (c->k == nullptr || c->v == nullptr) return SKV_EINVAL;
-  if (c->kv_dtype == SKV_I8 && (c->k_scale == nullptr || c->v_scale == nullptr)) return SKV_EINVAL;
+  if (c->kv_dtype != SKV_F16 && (c->k_scale == nullptr || c->v_scale == nullptr)) return SKV_EINVAL;
   if ((c->kmin == nullptr) != (c->kmax == nullptr)) return SKV_EINVAL;
   if (need_bounds && c->kmin == nullptr) return SKV_EINVAL;
   if (!aligned(c->k) || !aligned(c->v) || !aligned(c->kmin) || !aligned(c->kmax) ||
@@ -56,6 +57,26 @@ skv_status check_heads(const skv_cache* c, int32_t n_heads) {
 }
 
 skv_status device_status(hipError_t e) { return e == hipSuccess ? SKV_OK : SKV_EDEVICE; }
+
+// The new rows' dtype for a cache: f16 rows for an f16 cache, float32 rows
+// for every quantized cache.
+skv_status check_src(const skv_cache* c, int32_t src_dtype) {
+  const bool ok = (c->kv_dtype == SKV_F16 && src_dtype == SKV_F16) ||
+                  (c->kv_dtype != SKV_F16 && src_dtype == SKV_F32);
+  if (ok) return SKV_OK;
+  return (src_dtype == SKV_F16 || src_dtype == SKV_F32) ? SKV_EUNSUPPORTED : SKV_EINVAL;
+}
+
+hipError_t append_any(const skv_cache& c, const int32_t* pos0, int32_t n_new, const void* k_new,
+                      const void* v_new, hipStream_t stream) {
+  return skv::is_grouped(c.kv_dtype) ? skv::launch_append_grouped(c, pos0, n_new, k_new, v_new, stream)
+                                     : skv::launch_append(c, pos0, n_new, k_new, v_new, stream);
+}
+
+hipError_t decode_any(const skv::DecodeParams& p, hipStream_t stream) {
+  return skv::is_grouped(p.c->kv_dtype) ? skv::launch_decode_grouped(p, stream)
+                                        : skv::launch_decode(p, stream);
+}
 
 }  // namespace
 
@@ -92,10 +113,9 @@ skv_status skv_kv_append(const skv_cache* c, const int32_t* pos0, int32_t n_new,
   if (pos0 == nullptr || k_new == nullptr || v_new == nullptr || n_new < 1) return SKV_EINVAL;
   if (!aligned(k_new) || !aligned(v_new)) return SKV_EINVAL;
   if (n_new > c->max_seq) return SKV_ERANGE;
-  const bool ok = (c->kv_dtype == SKV_F16 && src_dtype == SKV_F16) ||
-                  (c->kv_dtype == SKV_I8 && src_dtype == SKV_F32);
-  if (!ok) return (src_dtype == SKV_F16 || src_dtype == SKV_F32) ? SKV_EUNSUPPORTED : SKV_EINVAL;
-  return device_status(skv::launch_append(*c, pos0, n_new, k_new, v_new, stream));
+  st = check_src(c, src_dtype);
+  if (st != SKV_OK) return st;
+  return device_status(append_any(*c, pos0, n_new, k_new, v_new, stream));
 }
 
 skv_status skv_block_bounds(const skv_cache* c, const float* q, int32_t n_heads,
@@ -161,7 +181,7 @@ skv_status skv_decode_attn(const skv_cache* c, const float* q, int32_t n_heads,
   p.n_split = n_split;
   p.ws = static_cast<float*>(workspace);
   p.dbg_logits = dbg_logits;
-  return device_status(skv::launch_decode(p, stream));
+  return device_status(decode_any(p, stream));
 }
 
 skv_status skv_decode_step(const skv_cache* c, const int32_t* pos0, const void* k_new,
@@ -180,9 +200,8 @@ skv_status skv_decode_step(const skv_cache* c, const int32_t* pos0, const void* 
   if (k_new != nullptr) {
     if (pos0 == nullptr || v_new == nullptr || !aligned(k_new) || !aligned(v_new))
       return SKV_EINVAL;
-    const bool ok = (c->kv_dtype == SKV_F16 && src_dtype == SKV_F16) ||
-                    (c->kv_dtype == SKV_I8 && src_dtype == SKV_F32);
-    if (!ok) return (src_dtype == SKV_F16 || src_dtype == SKV_F32) ? SKV_EUNSUPPORTED : SKV_EINVAL;
+    st = check_src(c, src_dtype);
+    if (st != SKV_OK) return st;
   }
   const int32_t max_blocks = blocks_of(c->max_seq, c->block);
   if (quest) {
@@ -212,8 +231,14 @@ skv_status skv_decode_step(const skv_cache* c, const int32_t* pos0, const void* 
   p.ws = static_cast<float*>(workspace);
   p.dbg_logits = nullptr;
   hipError_t e = hipSuccess;
+  const bool grouped = skv::is_grouped(c->kv_dtype);
+  if (grouped && k_new != nullptr) {
+    // group-wise caches: the append runs as its own kernel
+    e = skv::launch_append_grouped(*c, pos0, 1, k_new, v_new, stream);
+    if (e != hipSuccess) return SKV_EDEVICE;
+  }
   if (quest) {
-    e = k_new != nullptr
+    e = k_new != nullptr && !grouped
             ? skv::launch_append_bounds(*c, pos0, k_new, v_new, q, n_heads, seq_len, max_len,
                                         score, stream)
             : skv::launch_bounds(*c, q, n_heads, seq_len, max_len, score, stream);
@@ -221,7 +246,7 @@ skv_status skv_decode_step(const skv_cache* c, const int32_t* pos0, const void* 
     p.sel_idx = sel_idx;
     p.sel_cnt = sel_cnt;
     const int32_t ups = (max_sel + n_split - 1) / n_split;
-    if (max_blocks <= skv::kFusedSelMaxCand && ups <= 64) {
+    if (!grouped && max_blocks <= skv::kFusedSelMaxCand && ups <= 64) {
       p.fused_r = skv::fused_sel_chunks(std::max(max_blocks - n_sink, 1));
       p.fsel = skv::FusedSelect{score, max_blocks, k_sel, n_sink, n_recent, sel_idx, sel_cnt};
     } else {
@@ -229,10 +254,10 @@ skv_status skv_decode_step(const skv_cache* c, const int32_t* pos0, const void* 
                              k_sel, n_sink, n_recent, max_sel, sel_idx, sel_cnt, nullptr, stream);
       if (e != hipSuccess) return SKV_EDEVICE;
     }
-  } else if (k_new != nullptr) {
+  } else if (k_new != nullptr && !grouped) {
     p.app = skv::FoldedAppend{k_new, v_new, pos0};   // written by the attention kernel
   }
-  e = skv::launch_decode(p, stream);
+  e = decode_any(p, stream);
   if (e != hipSuccess) return SKV_EDEVICE;
   return device_status(skv::launch_combine(static_cast<const float*>(workspace), c->batch,
                                            n_heads, c->head_dim, n_split, out, stream));
@@ -274,7 +299,7 @@ skv_status skv_decode_attn_select(const skv_cache* c, const float* q, int32_t n_
   p.ws = static_cast<float*>(workspace);
   p.dbg_logits = nullptr;
   const int32_t ups = (max_sel + n_split - 1) / n_split;
-  if (max_blocks <= skv::kFusedSelMaxCand && ups <= 64) {
+  if (!skv::is_grouped(c->kv_dtype) && max_blocks <= skv::kFusedSelMaxCand && ups <= 64) {
     p.fused_r = skv::fused_sel_chunks(std::max(max_blocks - n_sink, 1));
     p.fsel = skv::FusedSelect{score, max_blocks, k_sel, n_sink, n_recent, sel_idx, sel_cnt};
   } else {
@@ -283,7 +308,7 @@ skv_status skv_decode_attn_select(const skv_cache* c, const float* q, int32_t n_
                                             sel_cnt, nullptr, stream);
     if (e != hipSuccess) return SKV_EDEVICE;
   }
-  return device_status(skv::launch_decode(p, stream));
+  return device_status(decode_any(p, stream));
 }
 
 skv_status skv_block_bounds_heads(const skv_cache* c, const float* q, int32_t n_heads,
@@ -328,6 +353,7 @@ skv_status skv_decode_attn_heads(const skv_cache* c, const float* q, int32_t n_h
     return SKV_EINVAL;
   st = check_heads(c, n_heads);
   if (st != SKV_OK) return st;
+  if (skv::is_grouped(c->kv_dtype)) return SKV_EUNSUPPORTED;
   if (n_split < 1 || n_split > kMaxSplit) return SKV_EINVAL;
   if (!grid_fits(n_split, c->n_kv_heads, c->batch)) return SKV_ERANGE;
   if (!(softmax_scale == softmax_scale) || softmax_scale < 0.0f) return SKV_EINVAL;
@@ -383,6 +409,7 @@ skv_status skv_decode_attn_sparse_v(const skv_cache* c, const float* q, int32_t 
                                                    c->head_dim, n_split, max_len);
   if (workspace == nullptr || workspace_bytes < need) return SKV_EWORKSPACE;
   if (!aligned(workspace)) return SKV_EINVAL;
+  if (skv::is_grouped(c->kv_dtype)) return SKV_EUNSUPPORTED;
   skv::SparseVParams p;
   p.c = c;
   p.q = q;

@@ -1,0 +1,441 @@
+// Group-wise quantized caches (q8_0, q4_0): append and decode attention.
+//
+// opencoti-llamafile sparse_attn.md, "All-KV-types composition": the side
+// cache of the block selector is filled from the keys before quantization, so
+// the Quest bound composes with quantized caches; "The decode win lives on
+// quantized KV": a dense pass must dequantize every block, the block skip
+// skips that work too.  The formats hold groups of 32 channels (the page's
+// quant block size, blck = 32) with one scale each; the cpu-attn card
+// ("Requirements and limits") contrasts its per-token scale with such
+// group-wise scaling within a row.
+//
+// Layout: codes [batch][n_kv_heads][max_seq][row] with row = 128 bytes
+// (q8_0, int8 codes -127..127) or 64 bytes (q4_0: channel 2i in the low
+// nibble of byte i, channel 2i + 1 in the high nibble, each code + 8 with
+// codes -7..7); scales [batch][n_kv_heads][max_seq][4] f16, one per group of
+// 32 channels.  Per group: a = max |x|, s = f16(a / QMAX) (QMAX 127 or 7),
+// code = clamp(rint(x / s), -QMAX, QMAX) against the stored scale, so a value
+// is exactly s * code (s == 0 or not finite: codes 0).
+//
+// Decode (decode_grp_mfma) follows the int8 kernel's structure -- 32-token
+// tiles, two in flight per wavefront, LDS staging with XOR-swizzled 16-byte
+// chunks, MFMA for both contractions -- with:
+//   q.K: the codes widened to f16 exactly (the int8 kernel's byte trick) as
+//     the A operand, the query as f16 high + low parts (~22-bit precision) as
+//     B; one v_mfma_f32_16x16x32_f16 pair per 32-channel group, so each
+//     group's partial dot leaves the matrix core on its own and is weighted
+//     by that (token, group)'s scale in float32 (4 FMAs per token and head);
+//   P.V: the transposed V codes widened to f16 as B, and as A the weight
+//     times the (token, group) V scale in a running power-of-two unit, split
+//     into f16 high + low parts per group (each 16-channel MFMA block lies in
+//     one group);
+//   q4_0 tiles arrive as nibbles (half the bytes) and are widened to int8
+//     codes in registers before the LDS stage, so both formats share the
+//     LDS layout and the arithmetic.
+#include <type_traits>
+
+#include "decode_core.h"
+#include "device_common.h"
+#include "launch.h"
+
+namespace skv {
+namespace {
+
+constexpr int kGroup = 32;
+constexpr int kGroups = kD / kGroup;        // 4
+
+template <bool Q4>
+struct GrpFmt {
+  static constexpr int kQmax = Q4 ? 7 : 127;
+  static constexpr int kRowBytes = Q4 ? kD / 2 : kD;      // codes per (token, KV head)
+};
+
+// The group-wise quantizer for one value given its group's absmax (the
+// append's arithmetic): stored f16 scale and code.
+__device__ __forceinline__ uint16_t grp_scale_bits(float a, int qmax) {
+  return __half_as_ushort(__float2half_rn(a / float(qmax)));
+}
+__device__ __forceinline__ int grp_code(float x, float s, int qmax) {
+  if (!(s > 0.0f && s < INFINITY)) return 0;
+  float r = rintf(x / s);
+  r = fminf(fmaxf(r, -float(qmax)), float(qmax));
+  return int(r);
+}
+
+// ------------------------------------------------------------------ append
+// One workgroup per (sequence, KV head, block touched by the append); one
+// wavefront per new row: lane l holds channels 2l, 2l + 1, a group is 16 lanes
+// (one DPP row, whose max gives the group's absmax).  Bounds as for the int8
+// cache: the float32 keys' min / max rounded outward to f16.
+constexpr int kAppendThreads = 256;
+
+template <bool Q4>
+__global__ void __launch_bounds__(kAppendThreads)
+append_grp_kernel(uint8_t* __restrict__ kc, uint8_t* __restrict__ vc,
+                  uint16_t* __restrict__ ksc, uint16_t* __restrict__ vsc,
+                  uint16_t* __restrict__ kmin, uint16_t* __restrict__ kmax,
+                  const float* __restrict__ kn, const float* __restrict__ vn,
+                  const int32_t* __restrict__ pos0, int32_t n_new, int32_t Hkv,
+                  int32_t max_seq, int32_t block, int32_t max_blocks) {
+  using F = GrpFmt<Q4>;
+  const int32_t g = blockIdx.y, b = blockIdx.z;
+  const int32_t p0 = pos0[b];
+  if (p0 < 0) return;
+  const int32_t j = p0 / block + int32_t(blockIdx.x);
+  const int64_t lo64 = max(int64_t(p0), int64_t(j) * block);
+  const int64_t hi64 = min(min(int64_t(p0) + n_new, int64_t(j + 1) * block), int64_t(max_seq));
+  if (lo64 >= hi64) return;
+  const int32_t t0 = int32_t(lo64), t1 = int32_t(hi64);
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  for (int32_t t = t0 + wave; t < t1; t += kAppendThreads / kWave) {
+    const int64_t src = ((int64_t(b) * n_new + (t - p0)) * Hkv + g) * kD;
+    const int64_t row = (int64_t(b) * Hkv + g) * max_seq + t;
+#pragma unroll
+    for (int which = 0; which < 2; ++which) {
+      const float2 x = reinterpret_cast<const float2*>((which == 0 ? kn : vn) + src)[lane];
+      const float a = group16_max(fmaxf(fmaxf(0.0f, fabsf(x.x)), fabsf(x.y)));
+      const uint16_t sb = grp_scale_bits(a, F::kQmax);
+      const float s = h2f(sb);
+      const int c0 = grp_code(x.x, s, F::kQmax), c1 = grp_code(x.y, s, F::kQmax);
+      uint8_t* dst = (which == 0 ? kc : vc) + row * F::kRowBytes;
+      if constexpr (Q4) {
+        dst[lane] = uint8_t((c0 + 8) | ((c1 + 8) << 4));
+      } else {
+        reinterpret_cast<uint16_t*>(dst)[lane] = uint16_t((c0 & 0xFF) | ((c1 & 0xFF) << 8));
+      }
+      if (lane % 16 == 0) (which == 0 ? ksc : vsc)[row * kGroups + lane / 16] = sb;
+    }
+  }
+  if (kmin == nullptr) return;
+  const bool fresh = int64_t(j) * block >= p0;
+  for (int32_t d = threadIdx.x; d < kD; d += kAppendThreads) {
+    float mn = INFINITY, mx = -INFINITY;
+    for (int32_t t = t0; t < t1; ++t) {
+      const float x = kn[((int64_t(b) * n_new + (t - p0)) * Hkv + g) * kD + d];
+      mn = fminf(mn, x);
+      mx = fmaxf(mx, x);
+    }
+    uint16_t bmn = f32_to_f16_down(mn), bmx = f32_to_f16_up(mx);
+    const int64_t o = ((int64_t(b) * Hkv + g) * max_blocks + j) * kD + d;
+    if (!fresh) {
+      bmn = f16_min_bits(kmin[o], bmn);
+      bmx = f16_max_bits(kmax[o], bmx);
+    }
+    kmin[o] = bmn;
+    kmax[o] = bmx;
+  }
+}
+
+// ------------------------------------------------------------------ decode
+// 32 nibble codes (16 bytes: byte i = channels 2i, 2i + 1, each code + 8) to
+// 32 int8 codes in channel order.
+__device__ __forceinline__ void unpack_q4(const int4_t& w, int4_t& c0, int4_t& c1) {
+  uint32_t o[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t x = uint32_t(w[i]);
+    const uint32_t lo = x & 0x0F0F0F0Fu, hi = (x >> 4) & 0x0F0F0F0Fu;
+    // (lo0, hi0, lo1, hi1) and (lo2, hi2, lo3, hi3); then n - 8 per byte as
+    // (n + 120) ^ 128 (no carry: n + 120 < 256)
+    const uint32_t a = __builtin_amdgcn_perm(hi, lo, 0x05010400u);
+    const uint32_t b = __builtin_amdgcn_perm(hi, lo, 0x07030602u);
+    o[2 * i] = (a + 0x78787878u) ^ 0x80808080u;
+    o[2 * i + 1] = (b + 0x78787878u) ^ 0x80808080u;
+  }
+  c0 = int4_t{int(o[0]), int(o[1]), int(o[2]), int(o[3])};
+  c1 = int4_t{int(o[4]), int(o[5]), int(o[6]), int(o[7])};
+}
+
+constexpr int kPwShiftGrp = 7;
+
+template <int G, bool Q4>
+__global__ void __launch_bounds__(kMThreads, 2)
+decode_grp_mfma(const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
+                const uint16_t* __restrict__ ksc, const uint16_t* __restrict__ vsc,
+                const float* __restrict__ q, const int32_t* __restrict__ seq_len,
+                const int32_t* __restrict__ sel_idx, const int32_t* __restrict__ sel_cnt,
+                int32_t max_sel, int32_t Hkv, int32_t max_seq, int32_t block, int32_t max_len,
+                int32_t n_split, int32_t n_rows, int32_t units_per_split, float qscale2,
+                float* __restrict__ ws_m, float* __restrict__ ws_l, float* __restrict__ ws_o) {
+  using F = GrpFmt<Q4>;
+  constexpr int T = 32;
+  constexpr int kCodeBytes = T * kRowBytesI8;               // 4096 (int8 codes in LDS)
+  constexpr int kScaleOff = 2 * kCodeBytes;                 // K, V scales as float [T][4]
+  constexpr int kBufBytes = 2 * kCodeBytes + 2 * T * kGroups * 4;
+  constexpr int kTileBytes = T * F::kRowBytes;              // HBM bytes of a code tile
+  constexpr int kLoads = Q4 ? 2 : 4;                        // 16-byte code loads per lane
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kMWaves][2][kBufBytes];
+  const uint32_t slot = xcd_slot(blockIdx.x, gridDim.x);
+  const int32_t split = int32_t(slot % uint32_t(n_split));
+  const uint32_t row = xcd_row(slot / uint32_t(n_split), uint32_t(n_rows));
+  const int32_t g = int32_t(row % uint32_t(Hkv)), b = int32_t(row / uint32_t(Hkv));
+  const int lane = threadIdx.x % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int lg = lane / 16, lc = lane % 16;
+  const int32_t H = Hkv * G;
+  const int64_t bg = int64_t(b) * Hkv + g;
+  const int32_t L_raw = seq_len[b];
+  const ListSeed ls = list_seed(sel_idx, sel_cnt, max_sel, bg, split, units_per_split);
+  // query as the B operand of the per-group q.K: column = head lc, k-chunk lg
+  // of group kk = channels 32 kk + 8 lg .. + 7; f16 high + low parts
+  half8_t qhi[kGroups], qlo[kGroups];
+  {
+    const bool hv = lc < G;
+    const float* qp = q + (int64_t(b) * H + g * G + (hv ? lc : 0)) * kD;
+#pragma unroll
+    for (int kk = 0; kk < kGroups; ++kk) {
+      const float4 a = *reinterpret_cast<const float4*>(qp + 32 * kk + 8 * lg);
+      const float4 c = *reinterpret_cast<const float4*>(qp + 32 * kk + 8 * lg + 4);
+      const float x[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const float v = hv ? x[s] * qscale2 : 0.0f;
+        const _Float16 h = (_Float16)v;
+        qhi[kk][s] = h;
+        qlo[kk][s] = (_Float16)(v - (float)h);
+      }
+    }
+  }
+  const int32_t L = __builtin_amdgcn_readfirstlane(min(max(L_raw, 0), max_len));
+  TileWalk tw = make_walk<T>(ls, sel_idx, max_sel, bg, L, block, split, units_per_split);
+  tw.init(wave);
+  float m_run = -INFINITY, l_run = 0.0f;
+  float4_t O[8];
+#pragma unroll
+  for (int n = 0; n < 8; ++n) O[n] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  const uint8_t* kbase = kc + bg * int64_t(max_seq) * F::kRowBytes;
+  const uint8_t* vbase = vc + bg * int64_t(max_seq) * F::kRowBytes;
+  const uint8_t* ksb = reinterpret_cast<const uint8_t*>(ksc + bg * int64_t(max_seq) * kGroups);
+  const uint8_t* vsb = reinterpret_cast<const uint8_t*>(vsc + bg * int64_t(max_seq) * kGroups);
+  // Lane loads, per code tile: q8_0 row 8 i + lane / 8, 16-byte chunk lane % 8
+  // (i = 0..3); q4_0 row 16 i + lane / 4, chunk lane % 4 of the 64-byte row
+  // (i = 0..1).  Scales: 4 bytes per lane = the two f16 scales of groups
+  // 2 (lane % 2), + 1 of token lane / 2.  Buffer resources with the tile's
+  // valid bytes: rows past the length read as zeros.
+  struct Frag { int4_t k[kLoads], v[kLoads]; uint32_t ks, vs; int32_t r0, nvalid; };
+  auto issue = [&](Frag& f) {
+    int32_t r0 = 0, nv = 0;
+    if (tw.more()) tw.next<T>(r0, nv);
+    f.r0 = r0;
+    f.nvalid = nv;
+    const uint32_t lo = 16u * uint32_t(lane);
+    const int bytes = __builtin_amdgcn_readfirstlane(max(nv, 0) * F::kRowBytes);
+    const auto kr = tile_rsrc(kbase + int64_t(r0) * F::kRowBytes, bytes);
+    const auto vr = tile_rsrc(vbase + int64_t(r0) * F::kRowBytes, bytes);
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      f.k[i] = tile_load(kr, lo + 1024 * i);
+      f.v[i] = tile_load(vr, lo + 1024 * i);
+    }
+    const int sbytes = __builtin_amdgcn_readfirstlane(max(nv, 0) * kGroups * 2);
+    const auto ksr = tile_rsrc(ksb + int64_t(r0) * kGroups * 2, sbytes);
+    const auto vsr = tile_rsrc(vsb + int64_t(r0) * kGroups * 2, sbytes);
+    f.ks = __builtin_amdgcn_raw_buffer_load_b32(ksr, 4u * uint32_t(lane), 0, kAuxNontemporal);
+    f.vs = __builtin_amdgcn_raw_buffer_load_b32(vsr, 4u * uint32_t(lane), 0, kAuxNontemporal);
+  };
+  static_assert(kTileBytes <= kTileRsrcBytes, "one buffer resource per tile");
+  auto sw = [](int rw, int chunk) { return rw * kRowBytesI8 + 16 * (chunk ^ (rw & 7)); };
+  constexpr int kExpUnset = -100000;
+  int e_run = kExpUnset;
+
+  auto process = [&](auto bufc, Frag& fr) {
+    constexpr int kBuf = decltype(bufc)::value;
+    uint8_t* kt = smem[wave][kBuf];
+    uint8_t* vt = kt + kCodeBytes;
+    float* stk = reinterpret_cast<float*>(kt + kScaleOff);          // [T][4]
+    float* stv = stk + T * kGroups;
+    if constexpr (Q4) {
+#pragma unroll
+      for (int i = 0; i < kLoads; ++i) {
+        const int rw = 16 * i + lane / 4, ch = 2 * (lane % 4);
+        int4_t a0, a1;
+        unpack_q4(fr.k[i], a0, a1);
+        *reinterpret_cast<int4_t*>(kt + sw(rw, ch)) = a0;
+        *reinterpret_cast<int4_t*>(kt + sw(rw, ch + 1)) = a1;
+        unpack_q4(fr.v[i], a0, a1);
+        *reinterpret_cast<int4_t*>(vt + sw(rw, ch)) = a0;
+        *reinterpret_cast<int4_t*>(vt + sw(rw, ch + 1)) = a1;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kLoads; ++i) {
+        const int rw = 8 * i + lane / 8;
+        *reinterpret_cast<int4_t*>(kt + sw(rw, lane % 8)) = fr.k[i];
+        *reinterpret_cast<int4_t*>(vt + sw(rw, lane % 8)) = fr.v[i];
+      }
+    }
+    // scales: f16 pairs to float; V scales in the running power-of-two unit
+    // 2^e_run >= every V scale so far, times 2^kPwShiftGrp
+    const float k0 = h2f_lo(fr.ks), k1 = h2f_hi(fr.ks);
+    const float v0 = h2f_lo(fr.vs), v1 = h2f_hi(fr.vs);
+    const int32_t vbits =
+        __builtin_amdgcn_readfirstlane(__float_as_int(wave_max(fmaxf(v0, v1))));
+    float unit = 1.0f;
+    if (vbits > 0 && vbits < 0x7F800000) {
+      const int32_t ex =
+          __builtin_amdgcn_readfirstlane(__builtin_amdgcn_frexp_expf(__int_as_float(vbits)));
+      if (e_run == kExpUnset) {
+        e_run = ex;
+      } else if (ex > e_run) {
+        unit = ldexpf(1.0f, e_run - ex);
+        e_run = ex;
+      }
+    }
+    const int e_use = e_run == kExpUnset ? 0 : e_run;
+    reinterpret_cast<float2*>(stk)[lane] = make_float2(k0, k1);
+    reinterpret_cast<float2*>(stv)[lane] =
+        make_float2(ldexpf(v0, kPwShiftGrp - e_use), ldexpf(v1, kPwShiftGrp - e_use));
+    const int32_t nvalid = fr.nvalid;
+    issue(fr);
+    // q.K per group: two 16-token halves, one MFMA pair per 32-channel group
+    float sc[8];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      float4_t acc[kGroups];
+#pragma unroll
+      for (int kk = 0; kk < kGroups; ++kk) {
+        const int rw = 16 * s + lc;
+        const int2_t raw = *reinterpret_cast<const int2_t*>(kt + sw(rw, 2 * kk + lg / 2) +
+                                                            8 * (lg & 1));
+        const half8_t a = widen_codes(raw);
+        acc[kk] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        acc[kk] = mfma_f16_32(a, qhi[kk], acc[kk]);
+        acc[kk] = mfma_f16_32(a, qlo[kk], acc[kk]);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float4 kss = *reinterpret_cast<const float4*>(stk + (16 * s + 4 * lg + r) * kGroups);
+        sc[4 * s + r] = acc[0][r] * kss.x + acc[1][r] * kss.y + acc[2][r] * kss.z +
+                        acc[3][r] * kss.w;
+      }
+    }
+    if (nvalid < T) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        sc[e] = 16 * (e / 4) + 4 * lg + e % 4 < nvalid ? sc[e] : -INFINITY;
+    }
+    tile_softmax<G, 2, true>(sc, m_run, l_run, O, unit);
+    // P.V: per 16-channel block n (group n / 2), A = weight x V scale of
+    // (token tok(lg, e), group), f16 high + low; B = V codes of channels
+    // 16 n + lc for tokens tok(lg, 0..7) (the int8 kernel's transposing read)
+    float4 vsr[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      vsr[e] = *reinterpret_cast<const float4*>(stv + (16 * (e / 4) + 4 * lg + e % 4) * kGroups);
+    const int tr_row = 16 * ((lc / 2) / 4) + 4 * lg + (lc / 2) % 4;
+#pragma unroll
+    for (int grp = 0; grp < kGroups; ++grp) {
+      half8_t phi, plo;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float vsg = grp == 0 ? vsr[e].x : grp == 1 ? vsr[e].y : grp == 2 ? vsr[e].z
+                                                                                 : vsr[e].w;
+        const float pw = sc[e] * vsg;
+        const _Float16 h = (_Float16)pw;
+        phi[e] = h;
+        plo[e] = (_Float16)(pw - (float)h);
+      }
+#pragma unroll
+      for (int nn = 0; nn < 2; ++nn) {
+        const int n = 2 * grp + nn;
+        const int off = sw(tr_row, n) + 8 * (lc & 1);
+        const int2_t raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32((SKV_LDS int2_t*)(vt + off));
+        const half8_t bv = widen_codes(raw);
+        O[n] = mfma_f16_32(phi, bv, O[n]);
+        O[n] = mfma_f16_32(plo, bv, O[n]);
+      }
+    }
+  };
+
+  Frag f0, f1;
+  const int32_t n_mine = tw.count();
+  issue(f0);
+  issue(f1);
+  for (int32_t t = 0; t + 1 < n_mine; t += 2) {
+    process(std::integral_constant<int, 0>{}, f0);
+    process(std::integral_constant<int, 1>{}, f1);
+  }
+  if (n_mine & 1) process(std::integral_constant<int, 0>{}, f0);
+  if (e_run != kExpUnset) {
+#pragma unroll
+    for (int n = 0; n < 8; ++n) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) O[n][r] = ldexpf(O[n][r], e_run - kPwShiftGrp);
+    }
+  }
+  finish_mfma<G>(m_run, l_run, O, reinterpret_cast<float*>(&smem[0][0][0]), ws_m, ws_l, ws_o,
+                 int64_t(b) * H + g * G, n_split, split);
+}
+
+}  // namespace
+
+hipError_t launch_append_grouped(const skv_cache& c, const int32_t* pos0, int32_t n_new,
+                                 const void* k_new, const void* v_new, hipStream_t stream) {
+  const int32_t max_blocks = (c.max_seq + c.block - 1) / c.block;
+  const int32_t n_aff = (n_new + c.block - 2) / c.block + 1;
+  const dim3 grid(n_aff, c.n_kv_heads, c.batch);
+  uint16_t* ks = reinterpret_cast<uint16_t*>(c.k_scale);
+  uint16_t* vs = reinterpret_cast<uint16_t*>(c.v_scale);
+  if (c.kv_dtype == SKV_Q4_0) {
+    append_grp_kernel<true><<<grid, kAppendThreads, 0, stream>>>(
+        static_cast<uint8_t*>(c.k), static_cast<uint8_t*>(c.v), ks, vs, c.kmin, c.kmax,
+        static_cast<const float*>(k_new), static_cast<const float*>(v_new), pos0, n_new,
+        c.n_kv_heads, c.max_seq, c.block, max_blocks);
+  } else {
+    append_grp_kernel<false><<<grid, kAppendThreads, 0, stream>>>(
+        static_cast<uint8_t*>(c.k), static_cast<uint8_t*>(c.v), ks, vs, c.kmin, c.kmax,
+        static_cast<const float*>(k_new), static_cast<const float*>(v_new), pos0, n_new,
+        c.n_kv_heads, c.max_seq, c.block, max_blocks);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_grouped(const DecodeParams& p, hipStream_t stream) {
+  const skv_cache& c = *p.c;
+  const int32_t B = c.batch, H = p.n_heads, S = p.n_split;
+  const int G = H / c.n_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return hipErrorInvalidValue;
+  if (p.fused_r > 0 || p.app.k_new != nullptr || p.sel_hmask != nullptr ||
+      p.dbg_logits != nullptr)
+    return hipErrorInvalidValue;
+  float* ws_m = p.ws + ws_m_offset(B, H, S);
+  float* ws_l = p.ws + ws_l_offset(B, H, S);
+  float* ws_o = p.ws + ws_o_offset(B, H, S);
+  int32_t ups;
+  if (p.sel_idx != nullptr) {
+    ups = (p.max_sel + S - 1) / S;
+  } else {
+    const int32_t nb_max = (p.max_len + c.block - 1) / c.block;
+    ups = (nb_max + S - 1) / S;
+  }
+  ups = ups < 1 ? 1 : ups;
+  const int64_t n_wg = int64_t(S) * c.n_kv_heads * B;
+  if (n_wg > 0x7fffffff) return hipErrorInvalidValue;
+  const dim3 grid(static_cast<uint32_t>(n_wg));
+  const int32_t n_rows = c.n_kv_heads * B;
+  const float scale2 = p.softmax_scale * kLog2e;
+  const uint8_t* kc = static_cast<const uint8_t*>(c.k);
+  const uint8_t* vc = static_cast<const uint8_t*>(c.v);
+  const uint16_t* ks = reinterpret_cast<const uint16_t*>(c.k_scale);
+  const uint16_t* vs = reinterpret_cast<const uint16_t*>(c.v_scale);
+#define SKV_GRP(GG, Q)                                                                          \
+  decode_grp_mfma<GG, Q><<<grid, kMThreads, 0, stream>>>(kc, vc, ks, vs, p.q, p.seq_len,       \
+                                                        p.sel_idx, p.sel_cnt, p.max_sel,        \
+                                                        c.n_kv_heads, c.max_seq, c.block,       \
+                                                        p.max_len, S, n_rows, ups, scale2,      \
+                                                        ws_m, ws_l, ws_o)
+#define SKV_GRP_G(GG)                          \
+  if (c.kv_dtype == SKV_Q4_0) SKV_GRP(GG, true); \
+  else SKV_GRP(GG, false)
+  switch (G) {
+    case 1: SKV_GRP_G(1); break;
+    case 2: SKV_GRP_G(2); break;
+    case 4: SKV_GRP_G(4); break;
+    default: SKV_GRP_G(8); break;
+  }
+#undef SKV_GRP_G
+#undef SKV_GRP
+  return hipGetLastError();
+}
+
+}  // namespace skv

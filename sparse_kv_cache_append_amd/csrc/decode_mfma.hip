@@ -136,70 +136,6 @@ __device__ __forceinline__ TileWalk fused_walk(const FusedSelect& fs, int32_t ma
   return tw;
 }
 
-// Softmax bookkeeping of one tile for the 16 MFMA columns (heads): lane l
-// owns head l%16 and rows 4*(l/16) + r of the tile.  s[r] are base-2 logits
-// (-inf for masked rows); returns the weights p[r] and rescales O when the
-// reference moves (by the change of reference times o_extra, a caller's exact
-// power of two).
-//
-// With LAZY, the reference m_run is a lazy maximum: it moves to a tile's
-// maximum only when that exceeds it by more than kLazySlack (base 2), so the
-// weights stay below 2^kLazySlack (finite in fp32, and the f16 high + low
-// split of P keeps its relative precision at any magnitude) while the
-// accumulators are rescaled only on the few tiles that move it; O and l stay
-// relative to the same m_run, which is all the merge and the combine need.
-// (The int8 kernel, whose tiles carry more vector work, gains from skipping
-// the rescale: 262K dense 53.6 -> 51.9 us; the f16 kernel does not, and keeps
-// the exact running maximum.)
-constexpr float kLazySlack = 8.0f;
-template <int G, int NT, bool LAZY>
-__device__ __forceinline__ void tile_softmax(float (&s)[4 * NT], float& m_run, float& l_run,
-                                             float4_t (&O)[8], float o_extra = 1.0f) {
-  const int lane = threadIdx.x % kWave;
-  float mx = s[0];
-#pragma unroll
-  for (int i = 1; i < 4 * NT; ++i) mx = fmaxf(mx, s[i]);
-  mx = rows_max(mx);
-  // -inf + slack = -inf: the first live tile of a head moves its reference
-  const bool bump = LAZY ? mx > m_run + kLazySlack : mx > m_run;
-  const float m_ref = bump ? mx : m_run;
-  // exp2(-inf) = 0 covers masked logits; a head with nothing live yet keeps
-  // factor 1 and weights exp2(-inf - 0) = 0
-  const bool live = m_ref != -INFINITY;
-  const float m_use = live ? m_ref : 0.0f;
-  float ps = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 4 * NT; ++i) {
-    s[i] = __builtin_amdgcn_exp2f(s[i] - m_use);
-    ps += s[i];
-  }
-  ps = rows_sum(ps);
-  // heads past G are padding
-  const bool moved = !LAZY || __ballot(bump && (lane % 16) < G) != 0;
-  if (moved || o_extra != 1.0f) {
-    const float cr = live ? __builtin_amdgcn_exp2f(m_run - m_ref) : 1.0f;
-    l_run = l_run * cr + ps;
-    // O rows are heads 4*(lane/16) + r; head h's factor is in lane h (column
-    // h of every row holds it).  Only heads < G matter: rows past them hold
-    // padding and may take any finite factor.
-    const bool upper = G > 4 && lane >= 16;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cr), r));
-      if (G > 4) {
-        const float c4 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cr), 4 + r));
-        c = upper ? c4 : c;
-      }
-      c *= o_extra;
-#pragma unroll
-      for (int n = 0; n < 8; ++n) O[n][r] *= c;
-    }
-  } else {
-    l_run += ps;
-  }
-  m_run = m_ref;
-}
-
 // The weights enter P.V as an f16 high part plus an f16 low part, both taken
 // from the weight times 2^kPwShift (exact).  The f16 kernel's weights are at
 // most 1 (exact running maximum), so the scaled weights stay below 2^15 and
@@ -216,50 +152,6 @@ __device__ __forceinline__ void split_hi_lo4(const float* p, half4_t& hi, half4_
     const _Float16 h = (_Float16)x;
     hi[s] = h;
     lo[s] = (_Float16)(x - (float)h);
-  }
-}
-
-// Merge the 4 wavefronts' states (heads < G) through LDS and write the
-// part's partial softmax state.
-template <int G>
-__device__ __forceinline__ void finish_mfma(float m_run, float l_run, const float4_t (&O)[8],
-                                            float* lds, float* __restrict__ ws_m,
-                                            float* __restrict__ ws_l, float* __restrict__ ws_o,
-                                            int64_t head0, int32_t n_split, int32_t split) {
-  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-  float* lo = lds;                          // [waves][G][D]
-  float* lm = lds + kMWaves * G * kD;       // [waves][G]
-  float* ll = lm + kMWaves * G;
-  __syncthreads();                          // tile buffers are reused
-  const int g4 = 4 * (lane / 16);
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int h = g4 + r;
-    if (h < G) {
-#pragma unroll
-      for (int n = 0; n < 8; ++n) lo[(wave * G + h) * kD + 16 * n + lane % 16] = O[n][r];
-    }
-  }
-  if (lane < G) { lm[wave * G + lane] = m_run; ll[wave * G + lane] = l_run; }
-  __syncthreads();
-  for (int idx = threadIdx.x; idx < G * kD; idx += kMThreads) {
-    const int h = idx / kD, d = idx % kD;
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kMWaves; ++w) M = fmaxf(M, lm[w * G + h]);
-    float so = 0.0f, sl = 0.0f;
-    if (M != -INFINITY) {
-#pragma unroll
-      for (int w = 0; w < kMWaves; ++w) {
-        const float mw = lm[w * G + h];
-        const float a = (mw == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mw - M);
-        so += a * lo[(w * G + h) * kD + d];
-        sl += a * ll[w * G + h];
-      }
-    }
-    const int64_t ps = (head0 + h) * n_split + split;
-    ws_o[ps * kD + d] = so;
-    if (d == 0) { ws_m[ps] = M; ws_l[ps] = sl; }
   }
 }
 

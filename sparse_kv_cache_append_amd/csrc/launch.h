@@ -133,6 +133,13 @@ inline size_t sparse_v_workspace_floats(int32_t B, int32_t H, int32_t Hkv, int32
 }
 hipError_t launch_sparse_v(const SparseVParams& p, hipStream_t stream);
 
+// Group-wise quantized caches (q8_0, q4_0): append and decode attention
+// (decode_grouped.hip; dense walks and given lists).
+hipError_t launch_append_grouped(const skv_cache& c, const int32_t* pos0, int32_t n_new,
+                                 const void* k_new, const void* v_new, hipStream_t stream);
+hipError_t launch_decode_grouped(const DecodeParams& p, hipStream_t stream);
+inline bool is_grouped(int32_t kv_dtype) { return kv_dtype == SKV_Q8_0 || kv_dtype == SKV_Q4_0; }
+
 hipError_t launch_combine(const float* ws, int32_t batch, int32_t n_heads, int32_t head_dim,
                           int32_t n_split, float* out, hipStream_t stream);
 

@@ -80,3 +80,14 @@ def test_partial_last_block_is_clipped():
     assert r["bounds"] == 2 * 512
     r = bench.step_bytes([100], 1, 1, 128, "f16", 64, {(0, 0): [1]})
     assert r["kv"] == 36 * 512
+
+
+def test_grouped_cache_bytes():
+    """q8_0 / q4_0 (sparse_attn.md, "All-KV-types composition": blocks of 32
+    values): per (token, KV head) the K and V rows hold D codes of 8 or 4 bits
+    and an f16 scale per 32 channels -- 2 x (128 + 8) and 2 x (64 + 8) bytes at
+    D = 128, i.e. 34 and 18 bytes per 32 values."""
+    assert bench.kv_bytes_per_token("q8_0", 128) == 272
+    assert bench.kv_bytes_per_token("q4_0", 128) == 144
+    assert bench.kv_bytes_per_token("q8_0", 128) / 2 / 4 == 34
+    assert bench.kv_bytes_per_token("q4_0", 128) / 2 / 4 == 18

@@ -47,11 +47,17 @@ def _cache_tensors(c):
 
 def _poison_rows(cache, pos):
     """Fill the rows the step's append will write with values no correct
-    result can depend on (NaN halves; int8 code -128 and NaN scales)."""
+    result can depend on (NaN halves; int8 code -128 and NaN scales; q8_0 /
+    q4_0 bytes 0x80 and NaN group scales)."""
     for b, p in enumerate(pos.tolist()):
         if cache.kv_dtype == "f16":
             cache.k[b, :, p] = float("nan")
             cache.v[b, :, p] = float("nan")
+        elif cache.kv_dtype in ("q8_0", "q4_0"):
+            cache.k[b, :, p] = 0x80
+            cache.v[b, :, p] = 0x80
+            cache.k_scale[b, :, p] = float("nan")
+            cache.v_scale[b, :, p] = float("nan")
         else:
             cache.k[b, :, p] = -128
             cache.v[b, :, p] = -128
@@ -134,6 +140,13 @@ def _oracle_check(w, out, sel):
             ref = oracle.attend_f16(w.q[0][hs], w.k[0][g:g + 1], w.v[0][g:g + 1],
                                     w.softmax_scale, tokens=toks)
             assert_close(out[0, hs], ref, 1e-3)
+        elif w.kv_dtype in ("q8_0", "q4_0"):
+            qmax = oracle.QMAX_Q8 if w.kv_dtype == "q8_0" else oracle.QMAX_Q4
+            kc, ksc = oracle.quantize_groups(w.k[0][g:g + 1], qmax)
+            vc, vsc = oracle.quantize_groups(w.v[0][g:g + 1], qmax)
+            ref = oracle.attend_grouped(w.q[0][hs], kc, ksc, vc, vsc, w.softmax_scale,
+                                        tokens=toks)
+            assert_close(out[0, hs], ref, 1e-3)
         else:
             kc, ksc, vc, vsc = quantized_host(w, 0)
             sl = slice(g, g + 1)
@@ -215,6 +228,18 @@ STEP_CASES = [
     ("quest-i8 NaN channel in the new key", lambda: _with_nan_key(workloads.clustered(
         [533], 32, 4, 128, [5001], "i8", n_dirs=16, k_sel=[20], n_sink=1, n_recent=4)),
         True, True, {"lag": 1}),
+    # group-wise quantized caches: append, bounds, select and attention as
+    # the step's own kernels
+    ("quest-q8_0", lambda: workloads.clustered(
+        [541, 542], 32, 8, 128, [3000, 4097], "q8_0", n_dirs=16, k_sel=[10, 12], n_sink=1,
+        n_recent=2), True, True, {}),
+    ("quest-q4_0 G8", lambda: workloads.clustered(
+        [543], 32, 4, 128, [5001], "q4_0", n_dirs=16, k_sel=[20], n_sink=1, n_recent=4),
+        True, True, {}),
+    ("dense-q8_0 append poisoned rows", lambda: workloads.gaussian(
+        544, 2, 32, 8, 128, [65, 2000], "q8_0"), False, True, {"poison": True}),
+    ("dense-q4_0 append 5 parts G2", lambda: workloads.gaussian(
+        545, 2, 16, 8, 128, [1025, 300], "q4_0"), False, True, {"poison": True, "S": 5}),
     ("dense-f16 NaN channel in the new key", lambda: _with_nan_key(workloads.gaussian(
         534, 2, 32, 8, 128, [700, 1025], "f16")), False, True, {"lag": 1}),
 ]

@@ -44,8 +44,8 @@ from typing import List, Optional
 
 import numpy as np
 
-__all__ = ["Workload", "gaussian", "clustered", "named", "quest32k_at", "lengths_config4",
-           "NAMED"]
+__all__ = ["Workload", "gaussian", "clustered", "named", "quest32k_at", "quest32k_quant",
+           "lengths_config4", "NAMED"]
 
 
 @dataclasses.dataclass
@@ -53,7 +53,7 @@ class Workload:
     """One batch of decode-step inputs.
 
     ``k[b]``/``v[b]`` are ``[Hkv][L_b][D]``: float16 for an f16 cache, float32
-    (pre-quantization) for an int8 cache.  ``q`` is ``[B][H][D]`` float32.
+    (pre-quantization) for an int8, q8_0 or q4_0 cache.  ``q`` is ``[B][H][D]`` float32.
     ``k_sel`` is the per-sequence top-K budget (None = dense only).
     """
     name: str
@@ -62,7 +62,7 @@ class Workload:
     Hkv: int
     D: int
     lens: List[int]
-    kv_dtype: str            # "f16" or "i8"
+    kv_dtype: str            # "f16", "i8", "q8_0" or "q4_0"
     k: List[np.ndarray]
     v: List[np.ndarray]
     q: np.ndarray
@@ -179,6 +179,15 @@ def named(cfg: int) -> Workload:
         return clustered([1005], 32, 4, 128, [262144], "i8", n_dirs=256,
                          name=NAMED[5], k_sel=[512], n_sink=1, n_recent=4)
     raise ValueError(f"unknown workload {cfg}")
+
+
+def quest32k_quant(kv_dtype: str) -> Workload:
+    """The 32K Quest workload's generator (H=32, Hkv=8, 64 directions, block
+    64, K_SEL=128, sink 1, recent 2, seed 1003) drawn for a group-wise
+    quantized cache ("q8_0" or "q4_0"): the float32 rows that get appended."""
+    return clustered([1003], 32, 8, 128, [32768], kv_dtype, n_dirs=64,
+                     name=f"quest-{kv_dtype} B1 H32/Hkv8 D128 L32768 K_SEL128 sink1 recent2",
+                     k_sel=[128], n_sink=1, n_recent=2)
 
 
 def quest32k_at(L: int) -> Workload:
