@@ -544,6 +544,9 @@ def measure(w, args, quest: bool, dense: bool, detail: bool = False):
         if not args.no_per_head and not grouped:
             res["quest_per_head"] = measure_per_head(T, skv, torch, w, caches, R, q, seq_len, Lmax,
                                                      new_k, new_v, pos_last, ks, res["quest"])
+        if not args.no_scan4 and w.kv_dtype == "f16":
+            res["scan4"] = measure_scan4(T, skv, torch, w, caches, R, q, seq_len, Lmax,
+                                         args.scan4_delta)
         if args.sparse_v_tau > 0 and not grouped:
             res["quest_sparse_v"] = measure_sparse_v(
                 T, skv, torch, w, caches, R, q, seq_len, Lmax, new_k, new_v, pos_last, ks, score,
@@ -608,6 +611,39 @@ def measure_per_head(T, skv, torch, w, caches, R, q, seq_len, Lmax, new_k, new_v
             "decode_attn_heads_us": round(dec_us, 3),
             "decode_attn_heads_pct_peak": round(100 * dec_bytes / dec_us / 1e3 / HBM_PEAK_GBPS, 2),
             "n_split": S}
+
+
+def measure_scan4(T, skv, torch, w, caches, R, q, seq_len, Lmax, delta):
+    """The GQA-shared 4-bit scan: skv_scan4_candidates over every token
+    (index built beforehand, as an append would keep it).  Bytes: the 4-bit
+    codes (D / 2 per (token, KV head), read once for the G heads) and the
+    per-block lo / step / err (3 x D x 4 B per (block, KV head)); the UB
+    values the two passes exchange are implementation traffic."""
+    B, H, Hkv, D, blk = w.B, w.H, w.Hkv, w.D, w.block
+    dev = q.device
+    idx = [skv.Scan4Index(c, device=dev) for c in caches]
+    zero = torch.zeros(B, dtype=torch.int32, device=dev)
+    for c, ix in zip(caches, idx):
+        skv.scan4_build(c, ix, zero, seq_len, Lmax)
+    S = skv.default_split(B, Hkv, -(-Lmax // blk))
+    ws = torch.empty(skv.scan4_workspace_bytes(B, H, S, Lmax), dtype=torch.uint8, device=dev)
+    cand = torch.empty((B, H, -(-Lmax // 32)), dtype=torch.int32, device=dev)
+    cnt = torch.empty((B, H), dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+    us = T.kernel(lambda i: skv.scan4_candidates(caches[i % R], idx[i % R], q, seq_len, Lmax,
+                                                 delta, S, ws, cand, cnt))
+    build_us = T.kernel(lambda i: skv.scan4_build(caches[i % R], idx[i % R], zero, seq_len,
+                                                  Lmax))
+    toks = sum(w.lens) * Hkv
+    nblk = sum(-(-L // blk) for L in w.lens) * Hkv
+    byts = toks * (D // 2) + nblk * 3 * D * 4 + B * H * D * 4
+    n_c = int(cnt.sum().item())
+    del idx
+    return {"delta": delta, "us": round(us, 3), "bytes": byts,
+            "pct_hbm_peak": round(100 * byts / us / 1e3 / HBM_PEAK_GBPS, 2),
+            "per_head_scan_bytes": toks * w.G * (D // 2) + nblk * 3 * D * 4 + B * H * D * 4,
+            "candidates_frac": round(n_c / (sum(w.lens) * H), 5),
+            "build_all_us": round(build_us, 3), "n_split": S}
 
 
 def measure_sparse_v(T, skv, torch, w, caches, R, q, seq_len, Lmax, new_k, new_v, pos_last, ks,
@@ -693,6 +729,10 @@ def main():
                          "q8_0 / q4_0 cache)")
     ap.add_argument("--no-per-head", action="store_true",
                     help="skip the Quest steps with one block set per query head")
+    ap.add_argument("--no-scan4", action="store_true",
+                    help="skip the GQA-shared 4-bit scan timing")
+    ap.add_argument("--scan4-delta", type=float, default=8.0,
+                    help="candidate margin of the 4-bit scan, in q.k units")
     ap.add_argument("--sparse-v-tau", type=float, default=1e-3,
                     help="also time the Quest steps with sparse-V at this static threshold "
                          "(0 = off)")
@@ -787,6 +827,7 @@ def main():
         "quest_over_dense_time": head.get("quest_over_dense"),
         "quest_sparse_v": head.get("quest_sparse_v"),
         "quest_per_head": head.get("quest_per_head"),
+        "scan4": head.get("scan4"),
         "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4),
                      "traffic": recorded_traffic(rk), "kernel": rk,

@@ -338,6 +338,67 @@ skv_status skv_decode_attn_heads(const skv_cache* c, const float* q, int32_t n_h
                                  size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * The 4-bit key index and its GQA-shared scan (Certified Sparse Attention via
+ * Perturbed Retrieval: the abstract -- a 4-bit scan with deterministic
+ * bounds, shared across the GQA group, generates the candidates exactly and
+ * reads every key; the appendix layout table -- 4-bit codes of 64 B per token
+ * at D = 128, per-block per-channel float32 lo and step).  A token-level
+ * candidate generator; the certificate, perturbation and sampling layers of
+ * that method are not part of this library.  f16 caches, block <= 256.
+ *
+ * Index, per block of `block` tokens and channel d: lo = min k, step =
+ * fl32(fl32(max k - lo) / 15), code = clamp(rint(fl32(fl32(k - lo) / step)),
+ * 0, 15) (0 if step == 0), err = max over the block of |fl32(k - fl32(lo +
+ * fl32(step * code)))| (single float32 operations), so the reconstruction is
+ * within err of every key.  Bounds for query head h and token t (block b):
+ * s~ = sum_d q_d (lo_bd + step_bd code_td), r = sum_d |q_d| err_bd,
+ * LB = s~ - r <= q . k_t <= UB = s~ + r.
+ */
+
+/*
+ * skv_scan4_build — (re)build the index of blocks floor(pos0[b] / block) ..
+ * ceil(L_b / block) - 1 from the cache's keys (call after an append with its
+ * pos0, or with pos0 = 0 for the whole row).  pos0[b] < 0 skips sequence b.
+ *   codes4 : device uint8 [batch][n_kv_heads][max_seq][head_dim / 2]: channel
+ *            2i in the low nibble of byte i, 2i + 1 in the high nibble.
+ *   lo, step, err : device float32 [batch][n_kv_heads][max_blocks][head_dim].
+ * Errors: SKV_EINVAL, SKV_ERANGE (max_len), SKV_EUNSUPPORTED (not f16, block
+ * > 256), SKV_EDEVICE.
+ */
+skv_status skv_scan4_build(const skv_cache* c, const int32_t* pos0, const int32_t* seq_len,
+                           int32_t max_len, uint8_t* codes4, float* lo, float* step, float* err,
+                           hipStream_t stream);
+
+/* Bytes of workspace skv_scan4_candidates needs: 4 * batch * n_heads *
+ * (max_len + n_split); 0 for invalid arguments. */
+size_t skv_scan4_workspace_bytes(int32_t batch, int32_t n_heads, int32_t n_split,
+                                 int32_t max_len);
+
+/*
+ * skv_scan4_candidates — one scan of the index per (sequence, KV head) for
+ * its G query heads: for every head, the tokens whose exact q . k could lie
+ * within delta of the largest, C_h = {t < L_b : UB_t >= max_u LB_u - delta}
+ * (float32; a token within about 1e-5 relative of the threshold may fall
+ * either way).  C_h contains every token with q . k_t >= max_u q . k_u -
+ * delta.  delta is in q . k units (no softmax scale); finite, >= 0.
+ *   workspace : at least skv_scan4_workspace_bytes(batch, n_heads, n_split,
+ *               max_len) bytes, 16-byte aligned; afterwards it holds UB as
+ *               float32 [batch][n_heads][max_len] (tokens < L_b), then the
+ *               parts' largest LB [batch][n_heads][n_split].
+ *   cand      : device uint32 [batch][n_heads][ceil(max_len / 32)]: bit t % 32
+ *               of word t / 32 set iff token t is a candidate (every word
+ *               written).
+ *   cand_cnt  : device int32 [batch][n_heads]: |C_h|.
+ * Errors: SKV_EINVAL, SKV_ERANGE, SKV_EWORKSPACE, SKV_EUNSUPPORTED, SKV_EDEVICE.
+ */
+skv_status skv_scan4_candidates(const skv_cache* c, const uint8_t* codes4, const float* lo,
+                                const float* step, const float* err, const float* q,
+                                int32_t n_heads, const int32_t* seq_len, int32_t max_len,
+                                float delta, int32_t n_split, void* workspace,
+                                size_t workspace_bytes, uint32_t* cand, int32_t* cand_cnt,
+                                hipStream_t stream);
+
+/*
  * skv_decode_attn_sparse_v — skv_decode_attn that leaves out the value rows
  * of negligible softmax weight.  Defines: sparse_attn.md, "Compose (three
  * sparsity levers, three pipeline stages)" item 3 (inside the attended

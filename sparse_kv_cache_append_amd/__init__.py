@@ -25,7 +25,8 @@ from typing import Optional
 
 __all__ = ["load", "Cache", "SkvError", "kv_append", "block_bounds", "select_topk",
            "decode_attn", "decode_attn_select", "decode_attn_sparse_v", "sparse_v_workspace_bytes",
-           "block_bounds_heads", "select_union", "decode_attn_heads",
+           "block_bounds_heads", "select_union", "decode_attn_heads", "Scan4Index",
+           "scan4_build", "scan4_candidates", "scan4_workspace_bytes",
            "decode_step", "decode_step_static", "combine", "workspace_bytes", "status_str", "decode",
            "SKV_F16", "SKV_F32", "SKV_I8", "SKV_Q8_0", "SKV_Q4_0", "LIB_PATH", "EXPORTS"]
 
@@ -39,7 +40,8 @@ EXPORTS = ("skv_max_blocks", "skv_kv_append", "skv_block_bounds", "skv_select_to
            "skv_decode_attn", "skv_decode_attn_select", "skv_decode_step",
            "skv_decode_step_static", "skv_static_scratch_bytes", "skv_decode_attn_sparse_v",
            "skv_sparse_v_workspace_bytes", "skv_block_bounds_heads", "skv_select_union",
-           "skv_decode_attn_heads", "skv_combine",
+           "skv_decode_attn_heads", "skv_scan4_build", "skv_scan4_workspace_bytes",
+           "skv_scan4_candidates", "skv_combine",
            "skv_workspace_bytes", "skv_status_str")
 
 
@@ -91,6 +93,10 @@ def load(path: str = LIB_PATH):
                                            ctypes.c_float, ctypes.c_float, I32, P, SZ, P, P]),
         "skv_sparse_v_workspace_bytes": (SZ, [I32, I32, I32, I32, I32, I32]),
         "skv_block_bounds_heads": (I32, [desc, P, I32, P, I32, P, P]),
+        "skv_scan4_build": (I32, [desc, P, P, I32, P, P, P, P, P]),
+        "skv_scan4_workspace_bytes": (SZ, [I32, I32, I32, I32]),
+        "skv_scan4_candidates": (I32, [desc, P, P, P, P, P, I32, P, I32, ctypes.c_float, I32, P,
+                                       SZ, P, P, P]),
         "skv_select_union": (I32, [P, P, I32, I32, I32, I32, I32, I32, P, P, P, P]),
         "skv_decode_attn_heads": (I32, [desc, P, I32, P, I32, P, P, P, I32, ctypes.c_float, I32,
                                         P, SZ, P]),
@@ -421,6 +427,57 @@ def decode_attn_heads(cache: Cache, q, seq_len, max_len: int, softmax_scale: flo
         _ptr(uni_idx), _ptr(uni_cnt), _ptr(uni_mask), int(uni_idx.shape[2]),
         float(softmax_scale), int(n_split), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+class Scan4Index:
+    """The 4-bit key index of an f16 cache: codes4 uint8
+    [batch][n_kv_heads][max_seq][head_dim / 2], lo / step / err float32
+    [batch][n_kv_heads][max_blocks][head_dim]."""
+
+    def __init__(self, cache: Cache, device="cuda"):
+        import torch
+        B, Hkv, D = cache.batch, cache.n_kv_heads, cache.head_dim
+        self.codes4 = torch.zeros((B, Hkv, cache.max_seq, D // 2), dtype=torch.uint8,
+                                  device=device)
+        shape = (B, Hkv, cache.max_blocks, D)
+        self.lo = torch.zeros(shape, dtype=torch.float32, device=device)
+        self.step = torch.zeros(shape, dtype=torch.float32, device=device)
+        self.err = torch.zeros(shape, dtype=torch.float32, device=device)
+
+
+def scan4_build(cache: Cache, index: Scan4Index, pos0, seq_len, max_len: int, stream=None):
+    """(Re)build the index blocks from the one holding pos0[b] to the end of
+    sequence b."""
+    import torch
+    call = "skv_scan4_build"
+    _need(call, _is(pos0, torch.int32, (cache.batch,)), "pos0 must be int32 [batch]")
+    _need(call, _is(seq_len, torch.int32, (cache.batch,)), "seq_len must be int32 [batch]")
+    _check(call, load().skv_scan4_build(
+        ctypes.byref(cache.desc), _ptr(pos0), _ptr(seq_len), int(max_len), _ptr(index.codes4),
+        _ptr(index.lo), _ptr(index.step), _ptr(index.err), _stream(stream)))
+
+
+def scan4_workspace_bytes(batch: int, n_heads: int, n_split: int, max_len: int) -> int:
+    return int(load().skv_scan4_workspace_bytes(batch, n_heads, n_split, max_len))
+
+
+def scan4_candidates(cache: Cache, index: Scan4Index, q, seq_len, max_len: int, delta: float,
+                     n_split: int, workspace, cand, cand_cnt, stream=None):
+    """Per query head, the tokens whose exact q.k could be within delta of the
+    largest (cand: 32-bit [batch][H][ceil(max_len/32)], cand_cnt: int32
+    [batch][H]); workspace then holds UB [batch][H][max_len] first."""
+    import torch
+    call = "skv_scan4_candidates"
+    _check_q(call, cache, q, seq_len)
+    H = int(q.shape[1])
+    _need(call, _is(cand, cand.dtype, (cache.batch, H, -(-int(max_len) // 32)))
+          and cand.element_size() == 4, "cand must be 32-bit [batch][H][ceil(max_len/32)]")
+    _need(call, _is(cand_cnt, torch.int32, (cache.batch, H)), "cand_cnt must be int32 [batch][H]")
+    _check(call, load().skv_scan4_candidates(
+        ctypes.byref(cache.desc), _ptr(index.codes4), _ptr(index.lo), _ptr(index.step),
+        _ptr(index.err), _ptr(q), H, _ptr(seq_len), int(max_len), float(delta), int(n_split),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(cand),
+        _ptr(cand_cnt), _stream(stream)))
 
 
 def sparse_v_workspace_bytes(batch: int, n_heads: int, n_kv_heads: int, head_dim: int,

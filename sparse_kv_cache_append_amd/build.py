@@ -24,7 +24,7 @@ LIB = os.path.join(PKG, "libskv.so")
 
 SOURCES = ["api.cpp", "append.hip", "bounds.hip", "select.hip", "decode_mfma.hip",
            "combine.hip", "static_step.hip", "sparse_v.hip",
-           "decode_grouped.hip"]
+           "decode_grouped.hip", "scan4.hip"]
 ARCH = "gfx950"
 
 

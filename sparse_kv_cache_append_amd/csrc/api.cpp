@@ -377,6 +377,67 @@ skv_status skv_decode_attn_heads(const skv_cache* c, const float* q, int32_t n_h
   return device_status(skv::launch_decode(p, stream));
 }
 
+skv_status skv_scan4_build(const skv_cache* c, const int32_t* pos0, const int32_t* seq_len,
+                           int32_t max_len, uint8_t* codes4, float* lo, float* step, float* err,
+                           hipStream_t stream) {
+  skv_status st = check_cache(c, false);
+  if (st != SKV_OK) return st;
+  if (pos0 == nullptr || seq_len == nullptr || codes4 == nullptr || lo == nullptr ||
+      step == nullptr || err == nullptr)
+    return SKV_EINVAL;
+  if (c->kv_dtype != SKV_F16 || c->block > 256) return SKV_EUNSUPPORTED;
+  if (!aligned(lo) || !aligned(step) || !aligned(err)) return SKV_EINVAL;
+  if (max_len < 0 || max_len > c->max_seq) return SKV_ERANGE;
+  return device_status(skv::launch_scan4_build(*c, pos0, seq_len, max_len, codes4, lo, step, err,
+                                               stream));
+}
+
+size_t skv_scan4_workspace_bytes(int32_t batch, int32_t n_heads, int32_t n_split,
+                                 int32_t max_len) {
+  if (batch < 1 || n_heads < 1 || n_split < 1 || n_split > kMaxSplit || max_len < 0) return 0;
+  return sizeof(float) * (size_t(batch) * n_heads * (size_t(max_len) + size_t(n_split)));
+}
+
+skv_status skv_scan4_candidates(const skv_cache* c, const uint8_t* codes4, const float* lo,
+                                const float* step, const float* err, const float* q,
+                                int32_t n_heads, const int32_t* seq_len, int32_t max_len,
+                                float delta, int32_t n_split, void* workspace,
+                                size_t workspace_bytes, uint32_t* cand, int32_t* cand_cnt,
+                                hipStream_t stream) {
+  skv_status st = check_cache(c, false);
+  if (st != SKV_OK) return st;
+  if (codes4 == nullptr || lo == nullptr || step == nullptr || err == nullptr || q == nullptr ||
+      seq_len == nullptr || cand == nullptr || cand_cnt == nullptr || !aligned(q))
+    return SKV_EINVAL;
+  if (!aligned(codes4) || !aligned(lo) || !aligned(step) || !aligned(err)) return SKV_EINVAL;
+  st = check_heads(c, n_heads);
+  if (st != SKV_OK) return st;
+  if (c->kv_dtype != SKV_F16 || c->block > 256) return SKV_EUNSUPPORTED;
+  if (!(delta >= 0.0f && delta <= 3.4e38f)) return SKV_EINVAL;
+  if (n_split < 1 || n_split > kMaxSplit) return SKV_EINVAL;
+  if (!grid_fits(n_split, c->n_kv_heads, c->batch)) return SKV_ERANGE;
+  if (max_len < 0 || max_len > c->max_seq) return SKV_ERANGE;
+  const size_t need = skv_scan4_workspace_bytes(c->batch, n_heads, n_split, max_len);
+  if (workspace == nullptr || workspace_bytes < need || !aligned(workspace))
+    return SKV_EWORKSPACE;
+  skv::Scan4Params p;
+  p.c = c;
+  p.codes4 = codes4;
+  p.lo = lo;
+  p.step = step;
+  p.err = err;
+  p.q = q;
+  p.n_heads = n_heads;
+  p.seq_len = seq_len;
+  p.max_len = max_len;
+  p.delta = delta;
+  p.n_split = n_split;
+  p.ws = static_cast<float*>(workspace);
+  p.cand = cand;
+  p.cand_cnt = cand_cnt;
+  return device_status(skv::launch_scan4(p, stream));
+}
+
 size_t skv_sparse_v_workspace_bytes(int32_t batch, int32_t n_heads, int32_t n_kv_heads,
                                     int32_t head_dim, int32_t n_split, int32_t max_len) {
   if (batch < 1 || n_heads < 1 || n_kv_heads < 1 || !valid_head_dim(head_dim) || n_split < 1 ||

@@ -140,6 +140,28 @@ hipError_t launch_append_grouped(const skv_cache& c, const int32_t* pos0, int32_
 hipError_t launch_decode_grouped(const DecodeParams& p, hipStream_t stream);
 inline bool is_grouped(int32_t kv_dtype) { return kv_dtype == SKV_Q8_0 || kv_dtype == SKV_Q4_0; }
 
+// The 4-bit key index and its GQA-shared scan (scan4.hip).
+struct Scan4Params {
+  const skv_cache* c;
+  const uint8_t* codes4;
+  const float* lo;
+  const float* step;
+  const float* err;
+  const float* q;
+  int32_t n_heads;
+  const int32_t* seq_len;
+  int32_t max_len;
+  float delta;
+  int32_t n_split;
+  float* ws;               // UB [B][H][max_len], then the parts' LB maxima [B][H][S]
+  uint32_t* cand;
+  int32_t* cand_cnt;
+};
+hipError_t launch_scan4_build(const skv_cache& c, const int32_t* pos0, const int32_t* seq_len,
+                              int32_t max_len, uint8_t* codes4, float* lo, float* step,
+                              float* err, hipStream_t stream);
+hipError_t launch_scan4(const Scan4Params& p, hipStream_t stream);
+
 hipError_t launch_combine(const float* ws, int32_t batch, int32_t n_heads, int32_t head_dim,
                           int32_t n_split, float* out, hipStream_t stream);
 

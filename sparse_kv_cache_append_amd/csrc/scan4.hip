@@ -1,0 +1,386 @@
+// A 4-bit key index and its GQA-shared scan with deterministic score bounds:
+// a token-level candidate generator ("Certified Sparse Attention via
+// Perturbed Retrieval": the abstract -- a 4-bit scan with deterministic
+// bounds, shared across a GQA group, generates the candidates exactly but
+// reads every key; the appendix layout table -- 4-bit codes, 64 B per token
+// at D = 128, per-block per-channel fp32 lo / step; the ablation table --
+// scanning per query head instead reads 2.7-4.0x the bytes).
+//
+// Index (per block of `block` tokens, per channel d; f16 cache keys):
+//   lo = min k, step = fl32(fl32(max k - lo) / 15), code = clamp(rint(
+//   fl32(fl32(k - lo) / step)), 0, 15) (0 if step == 0), recon = fl32(lo +
+//   fl32(step * code)), err = max |fl32(k - recon)|, each one IEEE float32
+//   operation (no fused multiply-add), so |k - recon| <= err.
+// Bounds of token t in block b for query head h:
+//   s~ = sum_d q_d recon_td = a_h + sum_d (q_d step_d) code_td,
+//   a_h = sum_d q_d lo_d, r_h = sum_d |q_d| err_d,
+//   LB = s~ - r_h <= q.k_t <= UB = s~ + r_h.
+// Candidates of head h for a margin delta: UB_t >= max_u LB_u - delta.
+//
+// Kernels: scan4_build (one workgroup per (block, KV head, sequence));
+// scan4_bounds (pass 1: split-K parts as the decode kernels, the codes of a
+// KV head read once for its G query heads: q.K~ on the matrix cores with the
+// codes widened to f16 as A and (q * step) as f16 high + low parts as B, one
+// MFMA pair per 32 channels; writes UB per (head, token) and each part's
+// largest LB per head); scan4_select (pass 2: the threshold from the parts'
+// LB maxima, a ballot per 64 tokens into the candidate bitmask, the count).
+#include <type_traits>
+
+#include "decode_core.h"
+#include "device_common.h"
+#include "launch.h"
+
+namespace skv {
+namespace {
+
+constexpr int kLevels = 15;
+constexpr int kScanBlockMax = 256;
+constexpr int kRow4 = kD / 2;              // 64 bytes of nibbles per (token, KV head)
+
+// ------------------------------------------------------------------- build
+// The block's keys (up to 64 tokens at a time) are staged in LDS with
+// 16-byte loads, all in flight at once, then thread d < 128 reduces channel d.
+constexpr int kBuildChunk = 64;
+__global__ void __launch_bounds__(256)
+scan4_build(const uint16_t* __restrict__ kc, const int32_t* __restrict__ pos0,
+            const int32_t* __restrict__ seq_len, int32_t Hkv, int32_t max_seq, int32_t max_len,
+            int32_t block, int32_t max_blocks, uint8_t* __restrict__ codes4,
+            float* __restrict__ lo_out, float* __restrict__ step_out,
+            float* __restrict__ err_out) {
+  __shared__ uint8_t cs[kScanBlockMax][kD];
+  __shared__ __attribute__((aligned(16))) uint16_t ks[kBuildChunk][kD];
+  const int32_t g = blockIdx.y, b = blockIdx.z;
+  const int32_t L = min(max(seq_len[b], 0), max_len);
+  const int32_t p0 = pos0[b];
+  const int32_t j = int32_t(blockIdx.x);
+  const int32_t nb = (L + block - 1) / block;
+  if (p0 < 0 || j < p0 / block || j >= nb) return;
+  const int32_t t0 = j * block, t1 = min(t0 + block, L);
+  const int64_t bg = int64_t(b) * Hkv + g;
+  const int d = threadIdx.x;
+  const uint4* krow = reinterpret_cast<const uint4*>(kc + (bg * max_seq) * kD);
+  // one chunk of rows into LDS: 16 bytes per thread per instruction
+  auto stage = [&](int32_t c0, int32_t n) {
+    __syncthreads();
+    for (int32_t e = threadIdx.x; e < n * (kD / 8); e += 256)
+      reinterpret_cast<uint4*>(&ks[0][0])[e] = krow[int64_t(c0) * (kD / 8) + e];
+    __syncthreads();
+  };
+  float mn = INFINITY, mx = -INFINITY;
+  for (int32_t c0 = t0; c0 < t1; c0 += kBuildChunk) {
+    const int32_t n = min(kBuildChunk, t1 - c0);
+    stage(c0, n);
+    if (d < kD) {
+      for (int32_t t = 0; t < n; ++t) {
+        const float x = h2f(ks[t][d]);
+        mn = fminf(mn, x);
+        mx = fmaxf(mx, x);
+      }
+    }
+  }
+  float lo = mn, st = 0.0f, err = 0.0f;
+  if (d < kD) st = __fdiv_rn(__fsub_rn(mx, mn), float(kLevels));
+  for (int32_t c0 = t0; c0 < t1; c0 += kBuildChunk) {
+    const int32_t n = min(kBuildChunk, t1 - c0);
+    if (block > kBuildChunk) stage(c0, n);           // else the chunk is still staged
+    if (d >= kD) continue;
+    for (int32_t t = c0; t < c0 + n; ++t) {
+      const float x = h2f(ks[t - c0][d]);
+      float c = 0.0f;
+      if (st > 0.0f) c = fminf(fmaxf(rintf(__fdiv_rn(__fsub_rn(x, lo), st)), 0.0f), float(kLevels));
+      // the product rounds on its own (the empty asm keeps the compiler from
+      // fusing it with the sum into one multiply-add)
+      float prod = st * c;
+      asm volatile("" : "+v"(prod));
+      const float rec = lo + prod;
+      err = fmaxf(err, fabsf(__fsub_rn(x, rec)));
+      cs[t - t0][d] = uint8_t(c);
+    }
+  }
+  if (d < kD) {
+    const int64_t o = (bg * max_blocks + j) * kD + d;
+    lo_out[o] = lo;
+    step_out[o] = st;
+    err_out[o] = err;
+  }
+  __syncthreads();
+  // pack: byte i of a token's row = channel 2i (low nibble), 2i + 1 (high)
+  const int32_t n = (t1 - t0) * kRow4;
+  uint8_t* dst = codes4 + (bg * max_seq + t0) * kRow4;
+  for (int32_t e = threadIdx.x; e < n; e += 256) {
+    const int32_t t = e / kRow4, i = e % kRow4;
+    dst[e] = uint8_t(cs[t][2 * i] | (cs[t][2 * i + 1] << 4));
+  }
+}
+
+// ------------------------------------------------------------ pass 1: bounds
+// 8 nibbles (4 bytes: channels 2i, 2i + 1 per byte) to 8 byte codes 0..15 in
+// channel order.
+__device__ __forceinline__ int2_t nibbles_to_bytes(uint32_t x) {
+  const uint32_t lo = x & 0x0F0F0F0Fu, hi = (x >> 4) & 0x0F0F0F0Fu;
+  return int2_t{int(__builtin_amdgcn_perm(hi, lo, 0x05010400u)),
+                int(__builtin_amdgcn_perm(hi, lo, 0x07030602u))};
+}
+
+template <int G>
+__global__ void __launch_bounds__(kMThreads, 2)
+scan4_bounds(const uint8_t* __restrict__ codes4, const float* __restrict__ lo_in,
+             const float* __restrict__ step_in, const float* __restrict__ err_in,
+             const float* __restrict__ q, const int32_t* __restrict__ seq_len, int32_t Hkv,
+             int32_t max_seq, int32_t block, int32_t max_blocks, int32_t max_len,
+             int32_t n_split, int32_t n_rows, int32_t ups, float* __restrict__ ub_out,
+             float* __restrict__ lbmax, int32_t* __restrict__ cand_cnt) {
+  constexpr int T = 32;
+  constexpr int kTileBytes = T * kRow4;                      // 2048
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kMWaves][2][kTileBytes];
+  __shared__ float red[kMWaves][16];
+  const uint32_t slot = xcd_slot(blockIdx.x, gridDim.x);
+  const int32_t split = int32_t(slot % uint32_t(n_split));
+  const uint32_t row = xcd_row(slot / uint32_t(n_split), uint32_t(n_rows));
+  const int32_t g = int32_t(row % uint32_t(Hkv)), b = int32_t(row / uint32_t(Hkv));
+  const int lane = threadIdx.x % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int lg = lane / 16, lc = lane % 16;
+  const int32_t H = Hkv * G;
+  const int64_t bg = int64_t(b) * Hkv + g;
+  const bool hv = lc < G;
+  if (split == 0 && threadIdx.x < G) cand_cnt[int64_t(b) * H + g * G + threadIdx.x] = 0;
+  const int32_t L_raw = seq_len[b];
+  // this lane's query channels 32 kk + 8 lg + s (head lc)
+  float qv[4][8];
+  {
+    const float* qp = q + (int64_t(b) * H + g * G + (hv ? lc : 0)) * kD;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const float4 a = *reinterpret_cast<const float4*>(qp + 32 * kk + 8 * lg);
+      const float4 c = *reinterpret_cast<const float4*>(qp + 32 * kk + 8 * lg + 4);
+      const float x[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
+#pragma unroll
+      for (int s = 0; s < 8; ++s) qv[kk][s] = hv ? x[s] : 0.0f;
+    }
+  }
+  const int32_t L = __builtin_amdgcn_readfirstlane(min(max(L_raw, 0), max_len));
+  const ListSeed ls{};
+  TileWalk tw = make_walk<T>(ls, nullptr, 0, bg, L, block, split, ups);
+  tw.init(wave);
+  const uint8_t* cbase = codes4 + bg * int64_t(max_seq) * kRow4;
+  float* urow = ub_out + (int64_t(b) * H + g * G + (hv ? lc : 0)) * int64_t(max_len);
+  float lb_run = -INFINITY;
+  // per-block operands, recomputed when a tile starts another block
+  int32_t cur_blk = -1;
+  half8_t whi[4], wlo[4];
+  float a_h = 0.0f, r_h = 0.0f;
+  int w_exp = 0;
+  // B = q * step per (head, channel), scaled by a power of two per head so
+  // that its largest value lies in [2^13, 2^14): the f16 low parts stay in
+  // the normal range (the MFMA result is scaled back exactly)
+  auto block_params = [&](int32_t jb) {
+    const int64_t o = (bg * max_blocks + jb) * kD;
+    float pa = 0.0f, pr = 0.0f;
+    float wv[4][8];
+    float mw = 0.0f;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int ch = 32 * kk + 8 * lg;
+      const float4 s0 = *reinterpret_cast<const float4*>(step_in + o + ch);
+      const float4 s1 = *reinterpret_cast<const float4*>(step_in + o + ch + 4);
+      const float4 l0 = *reinterpret_cast<const float4*>(lo_in + o + ch);
+      const float4 l1 = *reinterpret_cast<const float4*>(lo_in + o + ch + 4);
+      const float4 e0 = *reinterpret_cast<const float4*>(err_in + o + ch);
+      const float4 e1 = *reinterpret_cast<const float4*>(err_in + o + ch + 4);
+      const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+      const float lv[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
+      const float ev[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        wv[kk][s] = qv[kk][s] * sv[s];
+        mw = fmaxf(mw, fabsf(wv[kk][s]));
+        pa += qv[kk][s] * lv[s];
+        pr += fabsf(qv[kk][s]) * ev[s];
+      }
+    }
+    mw = rows_max(mw);
+    w_exp = mw > 0.0f ? 14 - __builtin_amdgcn_frexp_expf(mw) : 0;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const float w = ldexpf(wv[kk][s], w_exp);
+        const _Float16 h = (_Float16)w;
+        whi[kk][s] = h;
+        wlo[kk][s] = (_Float16)(w - (float)h);
+      }
+    }
+    a_h = rows_sum(pa);
+    r_h = rows_sum(pr);
+  };
+  struct Frag { int4_t c[2]; int32_t r0, nvalid; };
+  auto issue = [&](Frag& f) {
+    int32_t r0 = 0, nv = 0;
+    if (tw.more()) tw.next<T>(r0, nv);
+    f.r0 = r0;
+    f.nvalid = nv;
+    const int bytes = __builtin_amdgcn_readfirstlane(max(nv, 0) * kRow4);
+    const auto cr = tile_rsrc(cbase + int64_t(r0) * kRow4, bytes);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) f.c[i] = tile_load(cr, 16u * uint32_t(lane) + 1024 * i);
+  };
+  auto process = [&](auto bufc, Frag& fr) {
+    constexpr int kBuf = decltype(bufc)::value;
+    uint8_t* ct = smem[wave][kBuf];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) *reinterpret_cast<int4_t*>(ct + 16 * lane + 1024 * i) = fr.c[i];
+    const int32_t nvalid = fr.nvalid, r0 = fr.r0;
+    // the block's operands first: their loads then queue ahead of the
+    // refill's, so waiting for them leaves the refill in flight
+    const int32_t jb = r0 / block;
+    if (nvalid > 0 && jb != cur_blk) {       // wave-uniform
+      block_params(jb);
+      cur_blk = jb;
+    }
+    issue(fr);
+    if (nvalid <= 0) return;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        // token 16 s + lc, channels 32 kk + 8 lg .. + 7: 4 bytes of nibbles
+        const uint32_t x =
+            *reinterpret_cast<const uint32_t*>(ct + (16 * s + lc) * kRow4 + 16 * kk + 4 * lg);
+        const half8_t a = widen_codes(nibbles_to_bytes(x));
+        acc = mfma_f16_32(a, whi[kk], acc);
+        acc = mfma_f16_32(a, wlo[kk], acc);
+      }
+      float ub[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const bool ok = 16 * s + 4 * lg + r < nvalid;
+        const float st = ldexpf(acc[r], -w_exp) + a_h;
+        ub[r] = st + r_h;
+        lb_run = ok ? fmaxf(lb_run, st - r_h) : lb_run;
+      }
+      if (hv) {
+        const int32_t t = r0 + 16 * s + 4 * lg;
+        if (16 * s + 4 * lg + 3 < nvalid) {
+          *reinterpret_cast<float4*>(urow + t) = make_float4(ub[0], ub[1], ub[2], ub[3]);
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (16 * s + 4 * lg + r < nvalid) urow[t + r] = ub[r];
+        }
+      }
+    }
+  };
+  Frag f0, f1;
+  const int32_t n_mine = tw.count();
+  issue(f0);
+  issue(f1);
+  for (int32_t t = 0; t + 1 < n_mine; t += 2) {
+    process(std::integral_constant<int, 0>{}, f0);
+    process(std::integral_constant<int, 1>{}, f1);
+  }
+  if (n_mine & 1) process(std::integral_constant<int, 0>{}, f0);
+  // the part's largest LB per head: over the 4 lane groups, then the waves
+  lb_run = rows_max(lb_run);
+  if (lane < 16) red[wave][lane] = lb_run;
+  __syncthreads();
+  if (threadIdx.x < G) {
+    float m = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kMWaves; ++w) m = fmaxf(m, red[w][threadIdx.x]);
+    lbmax[(int64_t(b) * H + g * G + threadIdx.x) * n_split + split] = m;
+  }
+}
+
+// ------------------------------------------------------- pass 2: candidates
+// One workgroup per (4096-token chunk, query head, sequence): the threshold
+// max LB - delta from the parts' maxima, one ballot per 64 tokens, one count
+// added per workgroup.
+constexpr int kSelectChunk = 4096;
+__global__ void __launch_bounds__(256)
+scan4_select(const float* __restrict__ ub, const float* __restrict__ lbmax,
+             const int32_t* __restrict__ seq_len, int32_t H, int32_t max_len, int32_t n_split,
+             float delta, int32_t words, uint32_t* __restrict__ cand,
+             int32_t* __restrict__ cand_cnt) {
+  __shared__ float thr;
+  __shared__ int32_t wc[4];
+  const int32_t h = blockIdx.y, b = blockIdx.z;
+  const int64_t bh = int64_t(b) * H + h;
+  const int32_t L = min(max(seq_len[b], 0), max_len);
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  if (wave == 0) {
+    float m = -INFINITY;
+    for (int32_t i = lane; i < n_split; i += kWave) m = fmaxf(m, lbmax[bh * n_split + i]);
+    m = wave_max(m);
+    if (lane == 0) thr = m - delta;
+  }
+  __syncthreads();
+  const float th = thr;
+  int32_t n = 0;
+  const int32_t c0 = int32_t(blockIdx.x) * kSelectChunk;
+  for (int32_t t0 = c0 + 64 * wave; t0 < min(c0 + kSelectChunk, max_len); t0 += 256) {
+    const int32_t t = t0 + lane;
+    const bool c = t < L && ub[bh * max_len + t] >= th;
+    const uint64_t bal = __ballot(int(c));
+    const int32_t w0 = t0 / 32;
+    if (lane == 0 && w0 < words) cand[bh * words + w0] = uint32_t(bal & 0xFFFFFFFFu);
+    if (lane == 0 && w0 + 1 < words) cand[bh * words + w0 + 1] = uint32_t(bal >> 32);
+    n += int32_t(__popcll(bal));
+  }
+  if (lane == 0) wc[wave] = n;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int32_t tot = wc[0] + wc[1] + wc[2] + wc[3];
+    if (tot != 0) atomicAdd(&cand_cnt[bh], tot);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_scan4_build(const skv_cache& c, const int32_t* pos0, const int32_t* seq_len,
+                              int32_t max_len, uint8_t* codes4, float* lo, float* step,
+                              float* err, hipStream_t stream) {
+  if (c.kv_dtype != SKV_F16 || c.block > kScanBlockMax) return hipErrorInvalidValue;
+  const int32_t max_blocks = (c.max_seq + c.block - 1) / c.block;
+  const int32_t nb = (max_len + c.block - 1) / c.block;
+  if (nb == 0) return hipSuccess;
+  scan4_build<<<dim3(nb, c.n_kv_heads, c.batch), 256, 0, stream>>>(
+      static_cast<const uint16_t*>(c.k), pos0, seq_len, c.n_kv_heads, c.max_seq, max_len,
+      c.block, max_blocks, codes4, lo, step, err);
+  return hipGetLastError();
+}
+
+hipError_t launch_scan4(const Scan4Params& p, hipStream_t stream) {
+  const skv_cache& c = *p.c;
+  const int32_t B = c.batch, H = p.n_heads, S = p.n_split, Hkv = c.n_kv_heads;
+  const int G = H / Hkv;
+  const int32_t max_blocks = (c.max_seq + c.block - 1) / c.block;
+  const int32_t nb_max = (p.max_len + c.block - 1) / c.block;
+  int32_t ups = (nb_max + S - 1) / S;
+  ups = ups < 1 ? 1 : ups;
+  const int64_t n_wg = int64_t(S) * Hkv * B;
+  if (n_wg > 0x7fffffff) return hipErrorInvalidValue;
+  float* ub = p.ws;
+  float* lbm = p.ws + size_t(B) * H * p.max_len;
+#define SKV_SCAN(GG)                                                                            \
+  scan4_bounds<GG><<<dim3(uint32_t(n_wg)), kMThreads, 0, stream>>>(                            \
+      p.codes4, p.lo, p.step, p.err, p.q, p.seq_len, Hkv, c.max_seq, c.block, max_blocks,     \
+      p.max_len, S, Hkv * B, ups, ub, lbm, p.cand_cnt)
+  switch (G) {
+    case 1: SKV_SCAN(1); break;
+    case 2: SKV_SCAN(2); break;
+    case 4: SKV_SCAN(4); break;
+    case 8: SKV_SCAN(8); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef SKV_SCAN
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.max_len == 0) return e;
+  const int32_t words = (p.max_len + 31) / 32;
+  scan4_select<<<dim3((p.max_len + kSelectChunk - 1) / kSelectChunk, H, B), 256, 0, stream>>>(
+      ub, lbm, p.seq_len, H, p.max_len, S, p.delta, words, p.cand, p.cand_cnt);
+  return hipGetLastError();
+}
+
+}  // namespace skv

@@ -24,7 +24,7 @@ def lib():
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(skv_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(skv_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_every_declared_function_is_exported(lib):

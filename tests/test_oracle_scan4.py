@@ -105,3 +105,14 @@ def test_exact_index_gives_exact_candidates():
     assert np.array_equal(lb, ub)
     exact = k[0].astype(np.float64) @ q[0].astype(np.float64)
     np.testing.assert_allclose(ub[0], exact, rtol=1e-12, atol=1e-12)
+
+
+def test_float64_bounds_agree_with_the_exact_sums():
+    k = keys(11, L=130)
+    rng = np.random.default_rng(12)
+    q = rng.standard_normal((4, 32)).astype(np.float32)
+    idx = scan4.build_index(k, 130, 64)
+    lb, ub = scan4.scan_bounds(q, *idx, 64)
+    lb2, ub2 = scan4.scan_bounds_f64(q, *idx, 64)
+    np.testing.assert_allclose(lb2, lb, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(ub2, ub, rtol=1e-12, atol=1e-12)
