@@ -104,6 +104,7 @@ def _run_case(w, quest, append, S=None, max_seq=None, max_sel=None, poison=False
                     n_recent=w.n_recent, score=sc_b, sel_idx=sel_b, sel_cnt=cnt_b)
     torch.cuda.synchronize()
     assert torch.equal(out_a, out_b)
+    assert torch.equal(ws_a, ws_b)      # the same partial states, bit for bit
     for ta, tb in zip(_cache_tensors(ca), _cache_tensors(cb)):
         assert torch.equal(ta.view(torch.uint8), tb.view(torch.uint8))     # bits (NaN rows too)
     if quest:
@@ -240,6 +241,19 @@ STEP_CASES = [
         544, 2, 32, 8, 128, [65, 2000], "q8_0"), False, True, {"poison": True}),
     ("dense-q4_0 append 5 parts G2", lambda: workloads.gaussian(
         545, 2, 16, 8, 128, [1025, 300], "q4_0"), False, True, {"poison": True, "S": 5}),
+    # part counts whose merge takes 1, 2, 3 and 4 wavefronts per head
+    ("quest-f16 8 parts", lambda: workloads.clustered(
+        [546, 547], 32, 8, 128, [3000, 4097], "f16", n_dirs=16, k_sel=[10, 12], n_sink=1,
+        n_recent=2), True, True, {"S": 8}),
+    ("quest-i8 32 parts G8", lambda: workloads.clustered(
+        [548], 32, 4, 128, [9001], "i8", n_dirs=16, k_sel=[60], n_sink=1, n_recent=4),
+        True, True, {"S": 32}),
+    ("quest-f16 64 parts", lambda: workloads.clustered(
+        [549, 550], 32, 8, 128, [20000, 1500], "f16", n_dirs=16, k_sel=[100, 10], n_sink=1,
+        n_recent=2), True, True, {"S": 64}),
+    ("quest-i8 40 parts", lambda: workloads.clustered(
+        [551], 16, 8, 128, [12000], "i8", n_dirs=16, k_sel=[80], n_sink=1, n_recent=2),
+        True, True, {"S": 40}),
     ("dense-f16 NaN channel in the new key", lambda: _with_nan_key(workloads.gaussian(
         534, 2, 32, 8, 128, [700, 1025], "f16")), False, True, {"lag": 1}),
 ]
