@@ -457,8 +457,8 @@ skv_status skv_combine(const void* workspace, int32_t batch, int32_t n_heads,
                        int32_t head_dim, int32_t n_split, float* out, hipStream_t stream);
 
 /*
- * skv_decode_step — one whole decode step in two kernel launches (Quest
- * and dense alike, in the common case).
+ * skv_decode_step — one whole decode step in three kernel launches (Quest)
+ * or two (dense).
  * Defines: the composition of the calls above, in the order the pages run
  * them (cpu-attn kernel card, "Usage": append the token, then decode;
  * sparse_attn.md, "S2/S3 engineering design": fill the side cache, select,
@@ -480,15 +480,6 @@ skv_status skv_combine(const void* workspace, int32_t batch, int32_t n_heads,
  * the selection inside the attention kernel's prologue
  * (each part of a row recomputes it) when max_blocks <= 4096 and
  * ceil(max_sel / n_split) <= 64; otherwise they run as their own kernels.
- * In the Quest step the combine is folded into the attention kernel when
- * head_dim == 128, n_split is a multiple of 4 and at most 64, max_len > 0
- * and workspace and out are 16-byte aligned: the bounds pass zeroes one
- * counter per (sequence, KV head) in the workspace's counter region, every
- * part of that row adds one to it after storing its partial state, and the
- * part that arrives last merges the row's heads with the combine kernel's
- * arithmetic (out and the partial states in the workspace are the same as
- * without the fold) and sets the counter back to zero.  Calls that overlap
- * on one workspace race.
  *   pos0, k_new, v_new, src_dtype : as skv_kv_append with n_new = 1
  *            (k_new, v_new: [batch][1][n_kv_heads][head_dim]); k_new == NULL
  *            skips the append (pos0, v_new, src_dtype ignored).
@@ -544,11 +535,8 @@ skv_status skv_decode_step_static(const skv_cache* c, const int32_t* pos0, const
 /* Size in bytes of skv_decode_step_static's per-GPU scratch array. */
 size_t skv_static_scratch_bytes(void);
 
-/* Bytes of workspace skv_decode_attn and skv_decode_step need: the partial
- * states, 4 * batch * n_heads * n_split * (head_dim + 2) bytes rounded up to a
- * multiple of 16, then 4 * batch * n_heads bytes (rounded up likewise) of
- * int32 arrival counters that skv_decode_step's folded merge uses; 0 for
- * invalid arguments. */
+/* Bytes of workspace skv_decode_attn needs: 4 * batch * n_heads * n_split *
+ * (head_dim + 2); 0 for invalid arguments. */
 size_t skv_workspace_bytes(int32_t batch, int32_t n_heads, int32_t head_dim, int32_t n_split);
 
 /* Static, human-readable name of a status code. */

@@ -87,17 +87,10 @@ int32_t skv_max_blocks(const skv_cache* c) {
   return blocks_of(c->max_seq, c->block);
 }
 
-static size_t round16(size_t n) { return (n + 15) & ~size_t(15); }
-
 size_t skv_workspace_bytes(int32_t batch, int32_t n_heads, int32_t head_dim, int32_t n_split) {
   if (batch < 1 || n_heads < 1 || !valid_head_dim(head_dim) || n_split < 1 || n_split > kMaxSplit)
     return 0;
-  // partial states, then (from a 16-byte boundary) one int32 arrival counter
-  // per (sequence, head) for the step's folded merge
-  const size_t states =
-      sizeof(float) * size_t(batch) * size_t(n_heads) * size_t(n_split) * size_t(head_dim + 2);
-  const size_t counters = sizeof(int32_t) * size_t(batch) * size_t(n_heads);
-  return round16(states) + round16(counters);
+  return sizeof(float) * size_t(batch) * size_t(n_heads) * size_t(n_split) * size_t(head_dim + 2);
 }
 
 const char* skv_status_str(int32_t s) {
@@ -244,23 +237,11 @@ skv_status skv_decode_step(const skv_cache* c, const int32_t* pos0, const void* 
     e = skv::launch_append_grouped(*c, pos0, 1, k_new, v_new, stream);
     if (e != hipSuccess) return SKV_EDEVICE;
   }
-  // The Quest step folds the split-K merge into the attention kernel (the
-  // last part of each (sequence, KV head) to finish merges its heads): the
-  // bounds pass zeroes the arrival counters, so no extra launch clears them.
-  // Only where the fold's merge covers a head with at most 4 wavefronts and
-  // its vector loads are aligned; otherwise the combine kernel runs.
-  const bool fold = quest && !grouped && max_len > 0 && skv::fold_fits(n_split, c->head_dim) &&
-                    aligned(workspace) && aligned(out);
-  int32_t* cnt = fold ? reinterpret_cast<int32_t*>(
-                            static_cast<unsigned char*>(workspace) +
-                            round16(sizeof(float) * skv::ws_cnt_offset(c->batch, n_heads, n_split,
-                                                                       c->head_dim)))
-                      : nullptr;
   if (quest) {
     e = k_new != nullptr && !grouped
             ? skv::launch_append_bounds(*c, pos0, k_new, v_new, q, n_heads, seq_len, max_len,
-                                        score, stream, cnt)
-            : skv::launch_bounds(*c, q, n_heads, seq_len, max_len, score, stream, cnt);
+                                        score, stream)
+            : skv::launch_bounds(*c, q, n_heads, seq_len, max_len, score, stream);
     if (e != hipSuccess) return SKV_EDEVICE;
     p.sel_idx = sel_idx;
     p.sel_cnt = sel_cnt;
@@ -276,10 +257,8 @@ skv_status skv_decode_step(const skv_cache* c, const int32_t* pos0, const void* 
   } else if (k_new != nullptr && !grouped) {
     p.app = skv::FoldedAppend{k_new, v_new, pos0};   // written by the attention kernel
   }
-  if (fold) p.fold = skv::FoldCombine{out, cnt};
   e = decode_any(p, stream);
   if (e != hipSuccess) return SKV_EDEVICE;
-  if (fold) return SKV_OK;
   return device_status(skv::launch_combine(static_cast<const float*>(workspace), c->batch,
                                            n_heads, c->head_dim, n_split, out, stream));
 }

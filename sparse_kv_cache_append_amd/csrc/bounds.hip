@@ -170,8 +170,7 @@ __global__ void __launch_bounds__(kBoundsThreads)
 bounds_kernel(uint16_t* __restrict__ kmin, uint16_t* __restrict__ kmax,
               const float* __restrict__ q, const int32_t* __restrict__ seq_len,
               float* __restrict__ score, int32_t Hkv, int32_t max_len, int32_t block,
-              int32_t max_blocks, int32_t tiles, int32_t n_rows, AppendOne ap,
-              int32_t* __restrict__ zero_cnt) {
+              int32_t max_blocks, int32_t tiles, int32_t n_rows, AppendOne ap) {
   static_assert(D == kLanesPerBlock * 8, "one 16-byte load per lane per bound");
   static_assert(G * D / 4 <= kBoundsThreads, "one 16-byte query load per thread");
   // 1-D grid of tiles x Hkv x batch, row by row (XCD-aware slots: a row's
@@ -180,9 +179,6 @@ bounds_kernel(uint16_t* __restrict__ kmin, uint16_t* __restrict__ kmax,
   const int32_t tile = int32_t(slot % uint32_t(tiles));
   const uint32_t row = xcd_row(slot / uint32_t(tiles), uint32_t(n_rows));
   const int32_t g = int32_t(row % uint32_t(Hkv)), b = int32_t(row / uint32_t(Hkv));
-  // a decode step's arrival counters (one per row), zeroed for the attention
-  // kernel that follows in the same stream
-  if (zero_cnt != nullptr && tile == 0 && threadIdx.x == 0) zero_cnt[row] = 0;
   const int32_t j = tile * kBlocksPerWG + int32_t(threadIdx.x) / kLanesPerBlock;
   const int32_t c = threadIdx.x % kLanesPerBlock;  // channels 8c .. 8c+7
   // Requests issued before anything waits (one round trip): the row length
@@ -321,7 +317,7 @@ bounds_kernel(uint16_t* __restrict__ kmin, uint16_t* __restrict__ kmax,
 template <int G, int MODE, bool PH = false>
 hipError_t launch_bounds_g(const skv_cache& c, const float* q, const int32_t* seq_len,
                            int32_t max_len, float* score, const AppendOne& ap,
-                           hipStream_t stream, int32_t* zero_cnt = nullptr) {
+                           hipStream_t stream) {
   const int32_t max_blocks = (c.max_seq + c.block - 1) / c.block;
   const int32_t nb_max = (max_len + c.block - 1) / c.block;
   int32_t tiles = (nb_max + kBlocksPerWG - 1) / kBlocksPerWG;
@@ -332,19 +328,19 @@ hipError_t launch_bounds_g(const skv_cache& c, const float* q, const int32_t* se
   const dim3 grid(static_cast<uint32_t>(n_wg));
   bounds_kernel<128, G, MODE, PH><<<grid, kBoundsThreads, 0, stream>>>(
       c.kmin, c.kmax, q, seq_len, score, c.n_kv_heads, max_len, c.block, max_blocks, tiles,
-      c.n_kv_heads * c.batch, ap, zero_cnt);
+      c.n_kv_heads * c.batch, ap);
   return hipGetLastError();
 }
 
 template <int MODE>
 hipError_t launch_bounds_m(const skv_cache& c, const float* q, int32_t n_heads,
                            const int32_t* seq_len, int32_t max_len, float* score,
-                           const AppendOne& ap, hipStream_t stream, int32_t* zero_cnt) {
+                           const AppendOne& ap, hipStream_t stream) {
   switch (n_heads / c.n_kv_heads) {
-    case 1: return launch_bounds_g<1, MODE>(c, q, seq_len, max_len, score, ap, stream, zero_cnt);
-    case 2: return launch_bounds_g<2, MODE>(c, q, seq_len, max_len, score, ap, stream, zero_cnt);
-    case 4: return launch_bounds_g<4, MODE>(c, q, seq_len, max_len, score, ap, stream, zero_cnt);
-    case 8: return launch_bounds_g<8, MODE>(c, q, seq_len, max_len, score, ap, stream, zero_cnt);
+    case 1: return launch_bounds_g<1, MODE>(c, q, seq_len, max_len, score, ap, stream);
+    case 2: return launch_bounds_g<2, MODE>(c, q, seq_len, max_len, score, ap, stream);
+    case 4: return launch_bounds_g<4, MODE>(c, q, seq_len, max_len, score, ap, stream);
+    case 8: return launch_bounds_g<8, MODE>(c, q, seq_len, max_len, score, ap, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -353,9 +349,8 @@ hipError_t launch_bounds_m(const skv_cache& c, const float* q, int32_t n_heads,
 
 hipError_t launch_bounds(const skv_cache& c, const float* q, int32_t n_heads,
                          const int32_t* seq_len, int32_t max_len, float* score,
-                         hipStream_t stream, int32_t* zero_cnt) {
-  return launch_bounds_m<kNoAppend>(c, q, n_heads, seq_len, max_len, score, AppendOne{}, stream,
-                                    zero_cnt);
+                         hipStream_t stream) {
+  return launch_bounds_m<kNoAppend>(c, q, n_heads, seq_len, max_len, score, AppendOne{}, stream);
 }
 
 hipError_t launch_bounds_heads(const skv_cache& c, const float* q, int32_t n_heads,
@@ -374,12 +369,11 @@ hipError_t launch_bounds_heads(const skv_cache& c, const float* q, int32_t n_hea
 hipError_t launch_append_bounds(const skv_cache& c, const int32_t* pos0, const void* k_new,
                                 const void* v_new, const float* q, int32_t n_heads,
                                 const int32_t* seq_len, int32_t max_len, float* score,
-                                hipStream_t stream, int32_t* zero_cnt) {
+                                hipStream_t stream) {
   AppendOne ap{c.k, c.v, c.k_scale, c.v_scale, k_new, v_new, pos0, c.max_seq};
   if (c.kv_dtype == SKV_F16)
-    return launch_bounds_m<kAppendF16>(c, q, n_heads, seq_len, max_len, score, ap, stream,
-                                       zero_cnt);
-  return launch_bounds_m<kAppendI8>(c, q, n_heads, seq_len, max_len, score, ap, stream, zero_cnt);
+    return launch_bounds_m<kAppendF16>(c, q, n_heads, seq_len, max_len, score, ap, stream);
+  return launch_bounds_m<kAppendI8>(c, q, n_heads, seq_len, max_len, score, ap, stream);
 }
 
 }  // namespace skv

@@ -39,7 +39,6 @@
 //     B = V^T via the transposing LDS read (int8 codes widened to f16, exact).
 #include <type_traits>
 
-#include "combine_core.h"
 #include "decode_core.h"
 #include "device_common.h"
 #include "launch.h"
@@ -156,45 +155,6 @@ __device__ __forceinline__ void split_hi_lo4(const float* p, half4_t& hi, half4_
   }
 }
 
-// The split-K merge folded into the attention kernel (see FoldCombine): every
-// part makes its partial states visible device-wide and counts itself on its
-// row's counter; the part that brings the count to n_split merges the row's
-// G heads with combine_head (the combine kernel's arithmetic, so the output
-// is bit-identical), W = combine_waves(n_split) wavefronts per head, 4 / W
-// heads at a time, and resets the counter.  No part ever waits for another.
-template <int G>
-__device__ __forceinline__ void fold_merge(const FoldCombine& fc, const float* ws_m,
-                                           const float* ws_l, const float* ws_o,
-                                           int32_t n_split, int64_t head0, int64_t row) {
-  __shared__ int32_t last;
-  __shared__ float s_m[kMWaves], s_den[kMWaves];
-  __shared__ float4 s_num[kMWaves * 32];
-  // the barrier orders the workgroup's partial-state stores before thread
-  // 0's device-scope release (one per workgroup: a device-scope release
-  // writes the XCD's L2 back, a cost paid once, not once per wavefront); only
-  // the last part pays the acquire
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const bool is_last = __hip_atomic_fetch_add(&fc.cnt[row], 1, __ATOMIC_RELEASE,
-                                                __HIP_MEMORY_SCOPE_AGENT) == n_split - 1;
-    if (is_last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    last = is_last;
-  }
-  __syncthreads();
-  if (!last) return;                      // uniform over the workgroup
-  const int W = combine_waves(n_split);   // 1, 2 or 4 (the host folds only then)
-  const int per = kMWaves / W;            // heads per round
-  const int wave = threadIdx.x / kWave;
-  const int slot = wave / W, win = wave % W;
-  for (int h0 = 0; h0 < G; h0 += per) {
-    const int h = h0 + slot;
-    combine_head<true, true>(ws_m, ws_l, ws_o, n_split, kD, fc.out, head0 + h, 0, win, W,
-                             h < G, s_m + slot * W, s_den + slot * W, s_num + slot * W * 32);
-    __syncthreads();                      // the LDS slots are reused next round
-  }
-  if (threadIdx.x == 0) fc.cnt[row] = 0;
-}
-
 // The one-token append of a dense step (APP kernels).  Every wavefront reads
 // the new K and V rows (this lane: channels 2 lane, 2 lane + 1) and, when one
 // of its tiles holds position pos0[b], writes them over that row of the tile
@@ -274,8 +234,7 @@ decode_f16_mfma(const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc
                 int32_t max_sel, int32_t Hkv, int32_t max_seq, int32_t block, int32_t max_len,
                 int32_t n_split, int32_t n_rows, int32_t units_per_split, float qscale2,
                 float* __restrict__ ws_m, float* __restrict__ ws_l, float* __restrict__ ws_o,
-                FusedSelect fs, AppendArgs app, const uint32_t* __restrict__ sel_hmask,
-                FoldCombine fc) {
+                FusedSelect fs, AppendArgs app, const uint32_t* __restrict__ sel_hmask) {
   constexpr int T = 16;
   constexpr int kTileBytes = T * kRowBytesF16;              // 4096
   __shared__ __attribute__((aligned(16))) uint8_t smem[kMWaves][2][2 * kTileBytes];
@@ -457,7 +416,6 @@ decode_f16_mfma(const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc
   }
   finish_mfma<G>(m_run, l_run, O, reinterpret_cast<float*>(&smem[0][0][0]), ws_m, ws_l, ws_o,
                  int64_t(b) * H + g * G, n_split, split);
-  if (fc.out != nullptr) fold_merge<G>(fc, ws_m, ws_l, ws_o, n_split, int64_t(b) * H + g * G, bg);
   if constexpr (APP) {
     if (ao.own) {
       const int64_t row = (bg * max_seq + p_new) * (kD / 2) + lane;
@@ -514,7 +472,7 @@ decode_i8_mfma(const int8_t* __restrict__ kc, const int8_t* __restrict__ vc,
                int32_t n_split, int32_t n_rows, int32_t units_per_split, float scale2,
                float* __restrict__ ws_m, float* __restrict__ ws_l, float* __restrict__ ws_o,
                int32_t* __restrict__ dbg, FusedSelect fs, AppendArgs app,
-               const uint32_t* __restrict__ sel_hmask, FoldCombine fc) {
+               const uint32_t* __restrict__ sel_hmask) {
   constexpr int T = 32;
   constexpr int kTileBytes = T * kRowBytesI8;               // 4096
   constexpr int kScaleOff = 2 * kTileBytes;                 // 32 K scales, 32 V scales
@@ -772,7 +730,6 @@ decode_i8_mfma(const int8_t* __restrict__ kc, const int8_t* __restrict__ vc,
   }
   finish_mfma<G>(m_run, l_run, O, reinterpret_cast<float*>(&smem[0][0][0]), ws_m, ws_l, ws_o,
                  int64_t(b) * H + g * G, n_split, split);
-  if (fc.out != nullptr) fold_merge<G>(fc, ws_m, ws_l, ws_o, n_split, int64_t(b) * H + g * G, bg);
   if constexpr (APP) {
     if (ao.own) {
       const int64_t row = bg * max_seq + p_new;
@@ -795,13 +752,6 @@ decode_i8_mfma(const int8_t* __restrict__ kc, const int8_t* __restrict__ vc,
 }
 
 }  // namespace
-
-bool fold_fits(int32_t n_split, int32_t head_dim) {
-  // W wavefronts per head must tile the workgroup's kMWaves; the m / l loads
-  // of the merge are 16-byte vectors (n_split % 4 == 0)
-  const int W = combine_waves(n_split);
-  return head_dim == kD && W <= kMWaves && kMWaves % W == 0 && n_split % 4 == 0;
-}
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   const skv_cache& c = *p.c;
@@ -831,8 +781,6 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   const int fr = p.fused_r;
   const bool app = p.app.k_new != nullptr;
   const bool hmk = p.sel_hmask != nullptr;
-  if (p.fold.out != nullptr && (!fold_fits(S, p.c->head_dim) || p.fold.cnt == nullptr))
-    return hipErrorInvalidValue;
   if (hmk && (p.sel_idx == nullptr || fr > 0 || app)) return hipErrorInvalidValue;
   AppendArgs aa{};
   if (app) {
@@ -846,7 +794,7 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   decode_f16_mfma<GG, SR, AP, HMK><<<grid, kMThreads, 0, stream>>>(                            \
       static_cast<const uint16_t*>(c.k), static_cast<const uint16_t*>(c.v), p.q, p.seq_len,    \
       p.sel_idx, p.sel_cnt, p.max_sel, c.n_kv_heads, c.max_seq, c.block, p.max_len, S,        \
-      n_rows, ups, scale2, ws_m, ws_l, ws_o, p.fsel, aa, p.sel_hmask, p.fold)
+      n_rows, ups, scale2, ws_m, ws_l, ws_o, p.fsel, aa, p.sel_hmask)
 #define SKV_F16_G(GG)                                  \
   if (app) SKV_LAUNCH_F16(GG, 0, true, false);         \
   else if (hmk) SKV_LAUNCH_F16(GG, 0, false, true);    \
@@ -870,7 +818,7 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
       static_cast<const int8_t*>(c.k), static_cast<const int8_t*>(c.v), c.k_scale, c.v_scale,  \
       p.q, p.seq_len, p.sel_idx, p.sel_cnt, p.max_sel, c.n_kv_heads, c.max_seq, c.block,       \
       p.max_len, S, n_rows, ups, scale2, ws_m, ws_l, ws_o, p.dbg_logits, p.fsel, aa,          \
-      p.sel_hmask, p.fold)
+      p.sel_hmask)
 #define SKV_I8_G(GG)                                   \
   if (app) SKV_LAUNCH_I8(GG, 0, true, false);          \
   else if (hmk) SKV_LAUNCH_I8(GG, 0, false, true);     \

@@ -40,15 +40,6 @@ struct FoldedAppend {
   const int32_t* pos0 = nullptr;
 };
 
-// The split-K merge folded into the attention kernel (a Quest decode step):
-// each part counts its arrival on its row's counter (zeroed by the bounds
-// pass of the same step) and the last part of a row merges the row's
-// partial states into out, with combine_head's arithmetic.
-struct FoldCombine {
-  float* out = nullptr;     // nullptr: no fold (skv_combine runs separately)
-  int32_t* cnt = nullptr;   // [batch][n_kv_heads]
-};
-
 struct DecodeParams {
   const skv_cache* c;
   const float* q;
@@ -67,17 +58,14 @@ struct DecodeParams {
   FusedSelect fsel{};
   FoldedAppend app{};       // dense walks only (sel_idx == nullptr, fused_r == 0)
   const uint32_t* sel_hmask = nullptr;   // per-query-head lists: head mask per entry
-  FoldCombine fold{};
 };
 
 hipError_t launch_append(const skv_cache& c, const int32_t* pos0, int32_t n_new,
                          const void* k_new, const void* v_new, hipStream_t stream);
 
-// zero_cnt (optional): a decode step's arrival counters, one per (sequence,
-// KV head) row, set to 0 for the attention kernel that follows.
 hipError_t launch_bounds(const skv_cache& c, const float* q, int32_t n_heads,
                          const int32_t* seq_len, int32_t max_len, float* score,
-                         hipStream_t stream, int32_t* zero_cnt = nullptr);
+                         hipStream_t stream);
 
 // One new token per sequence ([batch][1][n_kv_heads][head_dim] of the cache's
 // source dtype), written at pos0[b], folded into the bounds pass.
@@ -95,7 +83,7 @@ struct AppendOne {
 hipError_t launch_append_bounds(const skv_cache& c, const int32_t* pos0, const void* k_new,
                                 const void* v_new, const float* q, int32_t n_heads,
                                 const int32_t* seq_len, int32_t max_len, float* score,
-                                hipStream_t stream, int32_t* zero_cnt = nullptr);
+                                hipStream_t stream);
 
 // Per-query-head bounds: score [batch][n_heads][max_blocks], no group max.
 hipError_t launch_bounds_heads(const skv_cache& c, const float* q, int32_t n_heads,
@@ -174,10 +162,6 @@ hipError_t launch_scan4_build(const skv_cache& c, const int32_t* pos0, const int
                               float* err, hipStream_t stream);
 hipError_t launch_scan4(const Scan4Params& p, hipStream_t stream);
 
-// Whether the attention kernels can fold the split-K merge for n_split parts
-// of head_dim channels (FoldCombine).
-bool fold_fits(int32_t n_split, int32_t head_dim);
-
 hipError_t launch_combine(const float* ws, int32_t batch, int32_t n_heads, int32_t head_dim,
                           int32_t n_split, float* out, hipStream_t stream);
 
@@ -185,10 +169,6 @@ hipError_t launch_combine(const float* ws, int32_t batch, int32_t n_heads, int32
 inline size_t ws_m_offset(int32_t, int32_t, int32_t) { return 0; }
 inline size_t ws_l_offset(int32_t B, int32_t H, int32_t S) { return size_t(B) * H * S; }
 inline size_t ws_o_offset(int32_t B, int32_t H, int32_t S) { return 2 * size_t(B) * H * S; }
-// then the decode step's arrival counters (int32 per (sequence, KV head) row)
-inline size_t ws_cnt_offset(int32_t B, int32_t H, int32_t S, int32_t D) {
-  return size_t(B) * H * S * (size_t(D) + 2);
-}
 
 
 }  // namespace skv

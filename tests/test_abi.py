@@ -132,10 +132,7 @@ def test_combine_validation_and_sizes(lib):
     assert lib.skv_combine(None, 1, 32, 128, 4, BAD, None) == skv.SKV_EINVAL
     assert lib.skv_combine(BAD, 1, 32, 100, 4, BAD, None) == skv.SKV_EINVAL
     assert lib.skv_combine(BAD, 1, 32, 128, 0, BAD, None) == skv.SKV_EINVAL
-    # partial states, then one int32 counter per (sequence, head), each region
-    # padded to 16 bytes
-    assert skv.workspace_bytes(2, 32, 128, 64) == 4 * 2 * 32 * 64 * 130 + 4 * 2 * 32
-    assert skv.workspace_bytes(1, 1, 16, 1) == 80 + 16
+    assert skv.workspace_bytes(2, 32, 128, 64) == 4 * 2 * 32 * 64 * 130
     assert skv.workspace_bytes(0, 32, 128, 64) == 0
     assert lib.skv_max_blocks(ctypes.byref(desc(max_seq=1000, block=64))) == 16
     assert skv.status_str(-3).startswith("SKV_EWORKSPACE")
