@@ -73,6 +73,15 @@ def side_cache_bytes_per_block(D: int) -> int:
     return 2 * 2 * D
 
 
+def scan4_index_bytes(lens, Hkv: int, D: int, block: int, reads_per_token: int = 1) -> int:
+    """Bytes one scan of the 4-bit index reads: D / 2 bytes of codes per
+    (token, KV head) (read reads_per_token times: 1 for the GQA-shared scan, G
+    when every query head scans on its own) and lo, step, err (3 x D float32)
+    per (block, KV head)."""
+    toks = sum(lens) * Hkv
+    nblk = sum(-(-L // block) for L in lens) * Hkv
+    return toks * (D // 2) * reads_per_token + nblk * 3 * D * 4
+
 def step_bytes(lens, Hkv, H, D, kv_dtype, block, attended_blocks=None):
     """Algorithmic bytes of one decode step.
 
@@ -634,14 +643,13 @@ def measure_scan4(T, skv, torch, w, caches, R, q, seq_len, Lmax, delta):
                                                  delta, S, ws, cand, cnt))
     build_us = T.kernel(lambda i: skv.scan4_build(caches[i % R], idx[i % R], zero, seq_len,
                                                   Lmax))
-    toks = sum(w.lens) * Hkv
-    nblk = sum(-(-L // blk) for L in w.lens) * Hkv
-    byts = toks * (D // 2) + nblk * 3 * D * 4 + B * H * D * 4
+    byts = scan4_index_bytes(w.lens, Hkv, D, blk) + B * H * D * 4
+    per_head = scan4_index_bytes(w.lens, Hkv, D, blk, reads_per_token=w.G) + B * H * D * 4
     n_c = int(cnt.sum().item())
     del idx
     return {"delta": delta, "us": round(us, 3), "bytes": byts,
             "pct_hbm_peak": round(100 * byts / us / 1e3 / HBM_PEAK_GBPS, 2),
-            "per_head_scan_bytes": toks * w.G * (D // 2) + nblk * 3 * D * 4 + B * H * D * 4,
+            "per_head_scan_bytes": per_head,
             "candidates_frac": round(n_c / (sum(w.lens) * H), 5),
             "build_all_us": round(build_us, 3), "n_split": S}
 

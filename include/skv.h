@@ -446,7 +446,10 @@ size_t skv_sparse_v_workspace_bytes(int32_t batch, int32_t n_heads, int32_t n_kv
 /*
  * skv_combine — merge the split-K partial states into the output.
  * Defines: M = max_i m_i; out = sum_i 2^(m_i - M) o_i / sum_i 2^(m_i - M) l_i
- * over the non-empty parts (the numerator/mass form of a split softmax).  A
+ * over the non-empty parts: the output as a sum of partial numerators over a
+ * sum of partial masses, each part's pair scaled to the common maximum
+ * (SCSA: Self-Calibrating Subquadratic Attention, "Mechanism", per-query
+ * step 4, forms its output the same way from an exact and a tail part).  A
  * query head whose parts are all empty (L_b == 0) gets zeros.
  *   workspace : as written by skv_decode_attn with the same batch, n_heads,
  *               head_dim, n_split.

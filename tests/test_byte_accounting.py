@@ -91,3 +91,21 @@ def test_grouped_cache_bytes():
     assert bench.kv_bytes_per_token("q4_0", 128) == 144
     assert bench.kv_bytes_per_token("q8_0", 128) / 2 / 4 == 34
     assert bench.kv_bytes_per_token("q4_0", 128) / 2 / 4 == 18
+
+
+def test_scan4_index_bytes_match_the_layout_table():
+    """The 4-bit scan reads 64 B of codes per token and, per block, three
+    float32 values per channel; at the table's 128-token blocks those are 12 B
+    per token (Certified Sparse Attention via Perturbed Retrieval, appendix
+    layout table, rows "4-bit codes" and "Block scales").  The GQA-shared scan
+    reads the codes once per KV head, a per-head scan G times."""
+    p = PAGES["scan4_index_bytes"]
+    D, blk = p["head_dim"], p["block_tokens_implied"]
+    one_token = bench.scan4_index_bytes([blk], 1, D, blk) / blk
+    assert one_token == p["codes_bytes_per_token"] + p["block_scales_bytes_per_token"]
+    codes_only = bench.scan4_index_bytes([blk], 1, D, blk) - 3 * D * 4
+    assert codes_only == p["codes_bytes_per_token"] * blk
+    # 32K f16 workload: 32,768 tokens x 8 KV heads, 64-token blocks
+    assert bench.scan4_index_bytes([32768], 8, 128, 64) == 32768 * 8 * 64 + 512 * 8 * 1536
+    assert bench.scan4_index_bytes([32768], 8, 128, 64, reads_per_token=4) == \
+        4 * 32768 * 8 * 64 + 512 * 8 * 1536
