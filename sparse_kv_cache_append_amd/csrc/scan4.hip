@@ -122,7 +122,16 @@ __device__ __forceinline__ int2_t nibbles_to_bytes(uint32_t x) {
                 int(__builtin_amdgcn_perm(hi, lo, 0x07030602u))};
 }
 
-template <int G>
+// T-token tiles (T = 64 when the block is a multiple of 64, else 32), two in
+// flight per wavefront.  The codes go straight from memory into the MFMA
+// operand registers: lane (lg, lc) loads the 16 bytes of token 16 s + lc
+// that hold channels 32 lg .. 32 lg + 31, and MFMA kk takes channels
+// 32 lg + 8 kk .. + 7 as its K index 8 lg .. 8 lg + 7 (the query side uses
+// the same assignment, so the dot is over all 128 channels).  Each tile's
+// refill also requests its block's lo, step and err rows (8 bytes of each per
+// lane, 1.5 KiB per tile), staged through LDS, so no tile waits on a separate
+// round trip for its block's operands.
+template <int G, int T>
 __global__ void __launch_bounds__(kMThreads, 2)
 scan4_bounds(const uint8_t* __restrict__ codes4, const float* __restrict__ lo_in,
              const float* __restrict__ step_in, const float* __restrict__ err_in,
@@ -130,9 +139,8 @@ scan4_bounds(const uint8_t* __restrict__ codes4, const float* __restrict__ lo_in
              int32_t max_seq, int32_t block, int32_t max_blocks, int32_t max_len,
              int32_t n_split, int32_t n_rows, int32_t ups, float* __restrict__ ub_out,
              float* __restrict__ lbmax, int32_t* __restrict__ cand_cnt) {
-  constexpr int T = 32;
-  constexpr int kTileBytes = T * kRow4;                      // 2048
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kMWaves][2][kTileBytes];
+  constexpr int kSubs = T / 16;                              // 16-token MFMA row blocks
+  __shared__ __attribute__((aligned(16))) float sprm[kMWaves][2][3][kD];   // lo, step, err
   __shared__ float red[kMWaves][16];
   const uint32_t slot = xcd_slot(blockIdx.x, gridDim.x);
   const int32_t split = int32_t(slot % uint32_t(n_split));
@@ -146,14 +154,14 @@ scan4_bounds(const uint8_t* __restrict__ codes4, const float* __restrict__ lo_in
   const bool hv = lc < G;
   if (split == 0 && threadIdx.x < G) cand_cnt[int64_t(b) * H + g * G + threadIdx.x] = 0;
   const int32_t L_raw = seq_len[b];
-  // this lane's query channels 32 kk + 8 lg + s (head lc)
+  // this lane's query channels 32 lg + 8 kk + s (head lc)
   float qv[4][8];
   {
     const float* qp = q + (int64_t(b) * H + g * G + (hv ? lc : 0)) * kD;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      const float4 a = *reinterpret_cast<const float4*>(qp + 32 * kk + 8 * lg);
-      const float4 c = *reinterpret_cast<const float4*>(qp + 32 * kk + 8 * lg + 4);
+      const float4 a = *reinterpret_cast<const float4*>(qp + 32 * lg + 8 * kk);
+      const float4 c = *reinterpret_cast<const float4*>(qp + 32 * lg + 8 * kk + 4);
       const float x[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
 #pragma unroll
       for (int s = 0; s < 8; ++s) qv[kk][s] = hv ? x[s] : 0.0f;
@@ -164,30 +172,67 @@ scan4_bounds(const uint8_t* __restrict__ codes4, const float* __restrict__ lo_in
   TileWalk tw = make_walk<T>(ls, nullptr, 0, bg, L, block, split, ups);
   tw.init(wave);
   const uint8_t* cbase = codes4 + bg * int64_t(max_seq) * kRow4;
+  const uint8_t* lbase = reinterpret_cast<const uint8_t*>(lo_in + bg * int64_t(max_blocks) * kD);
+  const uint8_t* sbase = reinterpret_cast<const uint8_t*>(step_in + bg * int64_t(max_blocks) * kD);
+  const uint8_t* ebase = reinterpret_cast<const uint8_t*>(err_in + bg * int64_t(max_blocks) * kD);
   float* urow = ub_out + (int64_t(b) * H + g * G + (hv ? lc : 0)) * int64_t(max_len);
   float lb_run = -INFINITY;
-  // per-block operands, recomputed when a tile starts another block
-  int32_t cur_blk = -1;
-  half8_t whi[4], wlo[4];
-  float a_h = 0.0f, r_h = 0.0f;
-  int w_exp = 0;
-  // B = q * step per (head, channel), scaled by a power of two per head so
-  // that its largest value lies in [2^13, 2^14): the f16 low parts stay in
-  // the normal range (the MFMA result is scaled back exactly)
-  auto block_params = [&](int32_t jb) {
-    const int64_t o = (bg * max_blocks + jb) * kD;
-    float pa = 0.0f, pr = 0.0f;
+  struct Frag {
+    int4_t c[kSubs];         // token 16 s + lc, channels 32 lg .. 32 lg + 31
+    int2_t p[3];             // channels 2 lane, 2 lane + 1 of lo, step, err
+    int32_t r0, nvalid;
+  };
+  // Every refill issues the same loads, through resources of zero records
+  // once the walk is over (they return zeros and touch no memory).
+  auto issue = [&](Frag& f) {
+    int32_t r0 = 0, nv = 0;
+    if (tw.more()) tw.next<T>(r0, nv);
+    f.r0 = r0;
+    f.nvalid = nv;
+    const int bytes = __builtin_amdgcn_readfirstlane(max(nv, 0) * kRow4);
+    const auto cr = tile_rsrc(cbase + int64_t(r0) * kRow4, bytes);
+#pragma unroll
+    for (int i = 0; i < kSubs; ++i)
+      f.c[i] = tile_load(cr, uint32_t(1024 * i + kRow4 * lc + 16 * lg));
+    const int pbytes = __builtin_amdgcn_readfirstlane(nv > 0 ? kD * 4 : 0);
+    const int64_t po = int64_t(r0 / block) * kD * 4;
+    const uint8_t* bases[3] = {lbase, sbase, ebase};
+#pragma unroll
+    for (int a = 0; a < 3; ++a) {
+      const auto pr = tile_rsrc(bases[a] + po, pbytes);
+      f.p[a] = __builtin_bit_cast(int2_t, __builtin_amdgcn_raw_buffer_load_b64(
+                                              pr, 8u * uint32_t(lane), 0, 0));
+    }
+  };
+  auto process = [&](auto bufc, Frag& fr) {
+    constexpr int kBuf = decltype(bufc)::value;
+    float(*pm)[kD] = sprm[wave][kBuf];
+#pragma unroll
+    for (int a = 0; a < 3; ++a) *reinterpret_cast<int2_t*>(&pm[a][2 * lane]) = fr.p[a];
+    int4_t cv[kSubs];
+#pragma unroll
+    for (int i = 0; i < kSubs; ++i) cv[i] = fr.c[i];
+    const int32_t nvalid = fr.nvalid, r0 = fr.r0;
+    issue(fr);
+    if (nvalid <= 0) return;               // wave-uniform
+    // the LDS stores above precede these reads (one wavefront, in order)
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    // the block's operands: B = q * step per (head, channel), scaled by a
+    // power of two per head so that its largest value lies in [2^13, 2^14)
+    // (the f16 low parts stay normal; the MFMA result is scaled back
+    // exactly); a_h = sum q lo, r_h = sum |q| err
+    half8_t whi[4], wlo[4];
+    float pa = 0.0f, pr = 0.0f, mw = 0.0f;
     float wv[4][8];
-    float mw = 0.0f;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      const int ch = 32 * kk + 8 * lg;
-      const float4 s0 = *reinterpret_cast<const float4*>(step_in + o + ch);
-      const float4 s1 = *reinterpret_cast<const float4*>(step_in + o + ch + 4);
-      const float4 l0 = *reinterpret_cast<const float4*>(lo_in + o + ch);
-      const float4 l1 = *reinterpret_cast<const float4*>(lo_in + o + ch + 4);
-      const float4 e0 = *reinterpret_cast<const float4*>(err_in + o + ch);
-      const float4 e1 = *reinterpret_cast<const float4*>(err_in + o + ch + 4);
+      const int ch = 32 * lg + 8 * kk;
+      const float4 s0 = *reinterpret_cast<const float4*>(&pm[1][ch]);
+      const float4 s1 = *reinterpret_cast<const float4*>(&pm[1][ch + 4]);
+      const float4 l0 = *reinterpret_cast<const float4*>(&pm[0][ch]);
+      const float4 l1 = *reinterpret_cast<const float4*>(&pm[0][ch + 4]);
+      const float4 e0 = *reinterpret_cast<const float4*>(&pm[2][ch]);
+      const float4 e1 = *reinterpret_cast<const float4*>(&pm[2][ch + 4]);
       const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
       const float lv[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
       const float ev[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
@@ -200,7 +245,7 @@ scan4_bounds(const uint8_t* __restrict__ codes4, const float* __restrict__ lo_in
       }
     }
     mw = rows_max(mw);
-    w_exp = mw > 0.0f ? 14 - __builtin_amdgcn_frexp_expf(mw) : 0;
+    const int w_exp = mw > 0.0f ? 14 - __builtin_amdgcn_frexp_expf(mw) : 0;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
@@ -211,44 +256,15 @@ scan4_bounds(const uint8_t* __restrict__ codes4, const float* __restrict__ lo_in
         wlo[kk][s] = (_Float16)(w - (float)h);
       }
     }
-    a_h = rows_sum(pa);
-    r_h = rows_sum(pr);
-  };
-  struct Frag { int4_t c[2]; int32_t r0, nvalid; };
-  auto issue = [&](Frag& f) {
-    int32_t r0 = 0, nv = 0;
-    if (tw.more()) tw.next<T>(r0, nv);
-    f.r0 = r0;
-    f.nvalid = nv;
-    const int bytes = __builtin_amdgcn_readfirstlane(max(nv, 0) * kRow4);
-    const auto cr = tile_rsrc(cbase + int64_t(r0) * kRow4, bytes);
+    const float a_h = rows_sum(pa);
+    const float r_h = rows_sum(pr);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) f.c[i] = tile_load(cr, 16u * uint32_t(lane) + 1024 * i);
-  };
-  auto process = [&](auto bufc, Frag& fr) {
-    constexpr int kBuf = decltype(bufc)::value;
-    uint8_t* ct = smem[wave][kBuf];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) *reinterpret_cast<int4_t*>(ct + 16 * lane + 1024 * i) = fr.c[i];
-    const int32_t nvalid = fr.nvalid, r0 = fr.r0;
-    // the block's operands first: their loads then queue ahead of the
-    // refill's, so waiting for them leaves the refill in flight
-    const int32_t jb = r0 / block;
-    if (nvalid > 0 && jb != cur_blk) {       // wave-uniform
-      block_params(jb);
-      cur_blk = jb;
-    }
-    issue(fr);
-    if (nvalid <= 0) return;
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
+    for (int s = 0; s < kSubs; ++s) {
       float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        // token 16 s + lc, channels 32 kk + 8 lg .. + 7: 4 bytes of nibbles
-        const uint32_t x =
-            *reinterpret_cast<const uint32_t*>(ct + (16 * s + lc) * kRow4 + 16 * kk + 4 * lg);
-        const half8_t a = widen_codes(nibbles_to_bytes(x));
+        // token 16 s + lc, channels 32 lg + 8 kk .. + 7: 4 bytes of nibbles
+        const half8_t a = widen_codes(nibbles_to_bytes(uint32_t(cv[s][kk])));
         acc = mfma_f16_32(a, whi[kk], acc);
         acc = mfma_f16_32(a, wlo[kk], acc);
       }
@@ -298,6 +314,7 @@ scan4_bounds(const uint8_t* __restrict__ codes4, const float* __restrict__ lo_in
 // max LB - delta from the parts' maxima, one ballot per 64 tokens, one count
 // added per workgroup.
 constexpr int kSelectChunk = 4096;
+constexpr int kSelectPer = kSelectChunk / 256;     // tokens per thread and chunk
 __global__ void __launch_bounds__(256)
 scan4_select(const float* __restrict__ ub, const float* __restrict__ lbmax,
              const int32_t* __restrict__ seq_len, int32_t H, int32_t max_len, int32_t n_split,
@@ -309,6 +326,15 @@ scan4_select(const float* __restrict__ ub, const float* __restrict__ lbmax,
   const int64_t bh = int64_t(b) * H + h;
   const int32_t L = min(max(seq_len[b], 0), max_len);
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int32_t c0 = int32_t(blockIdx.x) * kSelectChunk;
+  // every UB value of this thread is requested before the threshold is
+  // known (one round trip for both)
+  float u[kSelectPer];
+#pragma unroll
+  for (int i = 0; i < kSelectPer; ++i) {
+    const int32_t t = c0 + 256 * i + 64 * wave + lane;
+    u[i] = t < L ? ub[bh * max_len + t] : 0.0f;
+  }
   if (wave == 0) {
     float m = -INFINITY;
     for (int32_t i = lane; i < n_split; i += kWave) m = fmaxf(m, lbmax[bh * n_split + i]);
@@ -318,14 +344,16 @@ scan4_select(const float* __restrict__ ub, const float* __restrict__ lbmax,
   __syncthreads();
   const float th = thr;
   int32_t n = 0;
-  const int32_t c0 = int32_t(blockIdx.x) * kSelectChunk;
-  for (int32_t t0 = c0 + 64 * wave; t0 < min(c0 + kSelectChunk, max_len); t0 += 256) {
-    const int32_t t = t0 + lane;
-    const bool c = t < L && ub[bh * max_len + t] >= th;
+#pragma unroll
+  for (int i = 0; i < kSelectPer; ++i) {
+    const int32_t t0 = c0 + 256 * i + 64 * wave;
+    const bool c = t0 + lane < L && u[i] >= th;
     const uint64_t bal = __ballot(int(c));
     const int32_t w0 = t0 / 32;
-    if (lane == 0 && w0 < words) cand[bh * words + w0] = uint32_t(bal & 0xFFFFFFFFu);
-    if (lane == 0 && w0 + 1 < words) cand[bh * words + w0 + 1] = uint32_t(bal >> 32);
+    if (t0 < max_len) {
+      if (lane == 0 && w0 < words) cand[bh * words + w0] = uint32_t(bal & 0xFFFFFFFFu);
+      if (lane == 0 && w0 + 1 < words) cand[bh * words + w0 + 1] = uint32_t(bal >> 32);
+    }
     n += int32_t(__popcll(bal));
   }
   if (lane == 0) wc[wave] = n;
@@ -363,17 +391,20 @@ hipError_t launch_scan4(const Scan4Params& p, hipStream_t stream) {
   if (n_wg > 0x7fffffff) return hipErrorInvalidValue;
   float* ub = p.ws;
   float* lbm = p.ws + size_t(B) * H * p.max_len;
-#define SKV_SCAN(GG)                                                                            \
-  scan4_bounds<GG><<<dim3(uint32_t(n_wg)), kMThreads, 0, stream>>>(                            \
+#define SKV_SCAN(GG, TT)                                                                        \
+  scan4_bounds<GG, TT><<<dim3(uint32_t(n_wg)), kMThreads, 0, stream>>>(                        \
       p.codes4, p.lo, p.step, p.err, p.q, p.seq_len, Hkv, c.max_seq, c.block, max_blocks,     \
       p.max_len, S, Hkv * B, ups, ub, lbm, p.cand_cnt)
+#define SKV_SCAN_T(GG)                                                                          \
+  if (c.block % 64 == 0) SKV_SCAN(GG, 64); else SKV_SCAN(GG, 32);
   switch (G) {
-    case 1: SKV_SCAN(1); break;
-    case 2: SKV_SCAN(2); break;
-    case 4: SKV_SCAN(4); break;
-    case 8: SKV_SCAN(8); break;
+    case 1: SKV_SCAN_T(1); break;
+    case 2: SKV_SCAN_T(2); break;
+    case 4: SKV_SCAN_T(4); break;
+    case 8: SKV_SCAN_T(8); break;
     default: return hipErrorInvalidValue;
   }
+#undef SKV_SCAN_T
 #undef SKV_SCAN
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.max_len == 0) return e;
