@@ -31,6 +31,8 @@ Modules
                or the adaptive eps rule)
 ``scan4``      the 4-bit key index, its deterministic score bounds and the
                candidate tokens they give
+``multi_token`` a chunk of T query tokens per sequence, each attending
+               causally (dense, or through its own Quest block set)
 
 Parity pins: every function is checked by the ``-m "not gpu"`` tests in
 ``tests/test_oracle_*.py`` against brute force, closed forms, invariants or
@@ -38,7 +40,7 @@ page-printed numbers.  Two choices have no such pin and are marked "parity
 unpinned" where they are made: the near-tie report width (1e-5 relative) and
 the reading that forced blocks are excluded from the top-K candidates.
 """
-from . import quant, attention, quest, sparse_v, scan4  # noqa: F401
+from . import quant, attention, quest, sparse_v, scan4, multi_token  # noqa: F401
 from .quant import (quantize_rows, f16_round_down, f16_round_up,  # noqa: F401
                     quantize_groups, dequantize_groups, QMAX_Q8, QMAX_Q4)
 from .attention import (attend_f16, attend_i8, attend_i8_dequant, attend_grouped,  # noqa: F401
