@@ -338,6 +338,93 @@ skv_status skv_decode_attn_heads(const skv_cache* c, const float* q, int32_t n_h
                                  size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Query-token chunks (sparse_attn.md, "S2/S3 engineering design" item 2 and
+ * "Open questions": the selector serves the decode path first; a selector
+ * for the prefill path, where one call carries many query tokens, is a later
+ * stage whose rule the page leaves open).  A chunk is the last T = n_tokens
+ * positions of each sequence, already appended: with L_b = seq_len[b] (the
+ * chunk included), token t sits at position L_b - T + t and attends to the
+ * positions [0, L_bt), L_bt = L_b - T + 1 + t (a token with L_bt <= 0
+ * attends to nothing and gets zeros).  Each token is a decode query of its
+ * own: dense over its prefix, or Quest with its own bound (group max over its
+ * G heads), its own top-K with the sink and recent blocks counted over its
+ * own ceil(L_bt / block) blocks, and attention over its own blocks clipped at
+ * L_bt.  The bounds are the side cache's after the chunk's append (a block
+ * may hold positions past L_bt: the bound then covers a superset of the keys
+ * the token sees and stays sound).  A KV head's K/V are read once for the
+ * chunk: its T x G query rows are the columns of one MFMA operand.
+ * A chunk step:
+ *     skv_block_bounds_multi -> skv_select_topk_multi -> skv_select_union_tokens
+ *     -> skv_decode_attn_multi -> skv_combine(ws, batch, T * n_heads, ...)
+ * (dense: skv_decode_attn_multi with NULL lists, then skv_combine).
+ * q is float32 [batch][T][n_heads][head_dim]; T in {1, 2, 4, 8} with
+ * T * G <= 16; head_dim 128.
+ */
+
+/*
+ * skv_block_bounds_multi — skv_block_bounds for each token of a chunk, the
+ * side cache read once for the chunk.
+ *   score : device float32 [batch][n_kv_heads][T][max_blocks]: token t's
+ *           group-max bound; blocks >= ceil(L_b / block) are not written.
+ * Errors: as skv_block_bounds; SKV_EUNSUPPORTED for T or T * G outside the
+ * supported set.
+ */
+skv_status skv_block_bounds_multi(const skv_cache* c, const float* q, int32_t n_tokens,
+                                  int32_t n_heads, const int32_t* seq_len, int32_t max_len,
+                                  float* score, hipStream_t stream);
+
+/*
+ * skv_select_topk_multi — skv_select_topk for each (sequence, KV head,
+ * token) row of skv_block_bounds_multi's score, token t's row taking
+ * L_bt = seq_len[b] - T + 1 + t positions (its own blocks, sink and recent
+ * window) and the sequence's budget k_sel[b].
+ *   sel_idx : device int32 [batch][n_kv_heads][T][max_sel], ascending, -1 pad.
+ *   sel_cnt : device int32 [batch][n_kv_heads][T].
+ * Errors: as skv_select_topk; SKV_EUNSUPPORTED for T not in {1, 2, 4, 8}.
+ */
+skv_status skv_select_topk_multi(const float* score, const int32_t* seq_len, int32_t batch,
+                                 int32_t n_tokens, int32_t n_kv_heads, int32_t max_blocks,
+                                 int32_t block, const int32_t* k_sel, int32_t n_sink,
+                                 int32_t n_recent, int32_t max_sel, int32_t* sel_idx,
+                                 int32_t* sel_cnt, hipStream_t stream);
+
+/*
+ * skv_select_union_tokens — for each (sequence, KV head), the ascending union
+ * of its T tokens' lists; an entry's mask has bits [t G, (t + 1) G) set iff
+ * token t chose the block (G = group, the query heads per KV head: one bit per
+ * MFMA column of skv_decode_attn_multi).
+ *   sel_idx, sel_cnt : from skv_select_topk_multi.
+ *   uni_idx, uni_cnt, uni_mask, max_union : as skv_select_union.
+ * Errors: SKV_EINVAL (NULL, sizes < 1), SKV_EUNSUPPORTED (T or G outside the
+ * supported sets, T * G > 16, max_blocks > 16384), SKV_ERANGE, SKV_EDEVICE.
+ */
+skv_status skv_select_union_tokens(const int32_t* sel_idx, const int32_t* sel_cnt,
+                                   int32_t batch, int32_t n_tokens, int32_t n_kv_heads,
+                                   int32_t group, int32_t max_sel, int32_t max_blocks,
+                                   int32_t max_union, int32_t* uni_idx, int32_t* uni_cnt,
+                                   uint32_t* uni_mask, hipStream_t stream);
+
+/*
+ * skv_decode_attn_multi — split-K partial attention of a chunk: token t of
+ * sequence b, query head h over its positions [0, L_bt), either all of them
+ * (uni_idx, uni_cnt, uni_mask all NULL) or those of the union's blocks whose
+ * mask has bit t G + (h % G) (its own selected set, from
+ * skv_select_union_tokens).  Partial states as skv_decode_attn with
+ * T * n_heads query rows per sequence, row t * n_heads + h: the workspace is
+ * skv_workspace_bytes(batch, T * n_heads, head_dim, n_split) bytes, and
+ * skv_combine(workspace, batch, T * n_heads, head_dim, n_split, out) gives
+ * out float32 [batch][T][n_heads][head_dim].
+ * Errors: as skv_decode_attn; SKV_EUNSUPPORTED for T or T * G outside the
+ * supported set, or a q8_0 / q4_0 cache.
+ */
+skv_status skv_decode_attn_multi(const skv_cache* c, const float* q, int32_t n_tokens,
+                                 int32_t n_heads, const int32_t* seq_len, int32_t max_len,
+                                 const int32_t* uni_idx, const int32_t* uni_cnt,
+                                 const uint32_t* uni_mask, int32_t max_union,
+                                 float softmax_scale, int32_t n_split, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream);
+
+/*
  * The 4-bit key index and its GQA-shared scan (Certified Sparse Attention via
  * Perturbed Retrieval: the abstract -- a 4-bit scan with deterministic
  * bounds, shared across the GQA group, generates the candidates exactly and

@@ -25,7 +25,8 @@ from typing import Optional
 
 __all__ = ["load", "Cache", "SkvError", "kv_append", "block_bounds", "select_topk",
            "decode_attn", "decode_attn_select", "decode_attn_sparse_v", "sparse_v_workspace_bytes",
-           "block_bounds_heads", "select_union", "decode_attn_heads", "Scan4Index",
+           "block_bounds_heads", "select_union", "decode_attn_heads", "block_bounds_multi",
+           "select_topk_multi", "select_union_tokens", "decode_attn_multi", "Scan4Index",
            "scan4_build", "scan4_candidates", "scan4_workspace_bytes",
            "decode_step", "decode_step_static", "combine", "workspace_bytes", "status_str", "decode",
            "SKV_F16", "SKV_F32", "SKV_I8", "SKV_Q8_0", "SKV_Q4_0", "LIB_PATH", "EXPORTS"]
@@ -40,7 +41,9 @@ EXPORTS = ("skv_max_blocks", "skv_kv_append", "skv_block_bounds", "skv_select_to
            "skv_decode_attn", "skv_decode_attn_select", "skv_decode_step",
            "skv_decode_step_static", "skv_static_scratch_bytes", "skv_decode_attn_sparse_v",
            "skv_sparse_v_workspace_bytes", "skv_block_bounds_heads", "skv_select_union",
-           "skv_decode_attn_heads", "skv_scan4_build", "skv_scan4_workspace_bytes",
+           "skv_decode_attn_heads", "skv_block_bounds_multi", "skv_select_topk_multi",
+           "skv_select_union_tokens", "skv_decode_attn_multi", "skv_scan4_build",
+           "skv_scan4_workspace_bytes",
            "skv_scan4_candidates", "skv_combine",
            "skv_workspace_bytes", "skv_status_str")
 
@@ -100,6 +103,12 @@ def load(path: str = LIB_PATH):
         "skv_select_union": (I32, [P, P, I32, I32, I32, I32, I32, I32, P, P, P, P]),
         "skv_decode_attn_heads": (I32, [desc, P, I32, P, I32, P, P, P, I32, ctypes.c_float, I32,
                                         P, SZ, P]),
+        "skv_block_bounds_multi": (I32, [desc, P, I32, I32, P, I32, P, P]),
+        "skv_select_topk_multi": (I32, [P, P, I32, I32, I32, I32, I32, P, I32, I32, I32, P, P,
+                                        P]),
+        "skv_select_union_tokens": (I32, [P, P, I32, I32, I32, I32, I32, I32, I32, P, P, P, P]),
+        "skv_decode_attn_multi": (I32, [desc, P, I32, I32, P, I32, P, P, P, I32, ctypes.c_float,
+                                        I32, P, SZ, P]),
         "skv_combine": (I32, [P, I32, I32, I32, I32, P, P]),
         "skv_workspace_bytes": (SZ, [I32, I32, I32, I32]),
         "skv_status_str": (ctypes.c_char_p, [I32]),
@@ -425,6 +434,90 @@ def decode_attn_heads(cache: Cache, q, seq_len, max_len: int, softmax_scale: flo
     _check(call, load().skv_decode_attn_heads(
         ctypes.byref(cache.desc), _ptr(q), int(q.shape[1]), _ptr(seq_len), int(max_len),
         _ptr(uni_idx), _ptr(uni_cnt), _ptr(uni_mask), int(uni_idx.shape[2]),
+        float(softmax_scale), int(n_split), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+# ----------------------------------------------------------- token chunks
+def _check_qt(call: str, cache, q, seq_len):
+    """q float32 [batch][T][n_heads][head_dim], seq_len int32 [batch]."""
+    import torch
+    _need(call, q is not None and _is(q, torch.float32, (cache.batch, None, None, cache.head_dim)),
+          "q must be float32 [batch][n_tokens][n_heads][head_dim]")
+    _need(call, _is(seq_len, torch.int32, (cache.batch,)), "seq_len must be int32 [batch]")
+    return int(q.shape[1]), int(q.shape[2])
+
+
+def block_bounds_multi(cache: Cache, q, seq_len, max_len: int, score, stream=None):
+    """score [batch][Hkv][T][max_blocks] <- each chunk token's group-max bound."""
+    import torch
+    call = "skv_block_bounds_multi"
+    T, H = _check_qt(call, cache, q, seq_len)
+    _need(call, _is(score, torch.float32, (cache.batch, cache.n_kv_heads, T, cache.max_blocks)),
+          "score must be float32 [batch][n_kv_heads][n_tokens][max_blocks]")
+    _check(call, load().skv_block_bounds_multi(
+        ctypes.byref(cache.desc), _ptr(q), T, H, _ptr(seq_len), int(max_len), _ptr(score),
+        _stream(stream)))
+
+
+def select_topk_multi(score, seq_len, block: int, k_sel, n_sink: int, n_recent: int,
+                      sel_idx, sel_cnt, stream=None):
+    """Each chunk token's top-K (score [batch][Hkv][T][max_blocks]) into
+    sel_idx [batch][Hkv][T][max_sel], sel_cnt [batch][Hkv][T]."""
+    import torch
+    call = "skv_select_topk_multi"
+    _need(call, _is(score, torch.float32, (None, None, None, None)), "score must be float32 4-D")
+    B, Hkv, T, max_blocks = (int(x) for x in score.shape)
+    _need(call, _is(seq_len, torch.int32, (B,)) and _is(k_sel, torch.int32, (B,)),
+          "seq_len and k_sel must be int32 [batch]")
+    _need(call, _is(sel_idx, torch.int32, (B, Hkv, T, None)),
+          "sel_idx must be int32 [batch][n_kv_heads][n_tokens][max_sel]")
+    _need(call, _is(sel_cnt, torch.int32, (B, Hkv, T)),
+          "sel_cnt must be int32 [batch][n_kv_heads][n_tokens]")
+    _check(call, load().skv_select_topk_multi(
+        _ptr(score), _ptr(seq_len), B, T, Hkv, max_blocks, int(block), _ptr(k_sel), int(n_sink),
+        int(n_recent), int(sel_idx.shape[3]), _ptr(sel_idx), _ptr(sel_cnt), _stream(stream)))
+
+
+def select_union_tokens(sel_idx, sel_cnt, group: int, max_blocks: int, uni_idx, uni_cnt,
+                        uni_mask, stream=None):
+    """Per KV head, the ascending union of its chunk tokens' lists, token t's
+    blocks tagged with bits [t * group, (t + 1) * group)."""
+    import torch
+    call = "skv_select_union_tokens"
+    _need(call, _is(sel_idx, torch.int32, (None, None, None, None)), "sel_idx must be int32 4-D")
+    B, Hkv, T, max_sel = (int(x) for x in sel_idx.shape)
+    _need(call, _is(sel_cnt, torch.int32, (B, Hkv, T)),
+          "sel_cnt must be int32 [batch][n_kv_heads][n_tokens]")
+    _need(call, _is(uni_idx, torch.int32, (B, Hkv, None)),
+          "uni_idx must be int32 [batch][n_kv_heads][max_union]")
+    max_union = int(uni_idx.shape[2])
+    _need(call, _is(uni_cnt, torch.int32, (B, Hkv)), "uni_cnt must be int32 [batch][Hkv]")
+    _need(call, _is(uni_mask, uni_mask.dtype, (B, Hkv, max_union))
+          and uni_mask.element_size() == 4, "uni_mask must be 32-bit like uni_idx")
+    _check(call, load().skv_select_union_tokens(
+        _ptr(sel_idx), _ptr(sel_cnt), B, T, Hkv, int(group), max_sel, int(max_blocks),
+        max_union, _ptr(uni_idx), _ptr(uni_cnt), _ptr(uni_mask), _stream(stream)))
+
+
+def decode_attn_multi(cache: Cache, q, seq_len, max_len: int, softmax_scale: float,
+                      n_split: int, workspace, uni_idx=None, uni_cnt=None, uni_mask=None,
+                      stream=None):
+    """Split-K partial states of a chunk of query tokens (q [batch][T][H][D]),
+    each token causal over its prefix, densely (no lists) or over its own
+    blocks (the union list with token masks from select_union_tokens).
+    combine(workspace, batch, T * H, D, n_split, out) then gives
+    out [batch][T][H][D]."""
+    call = "skv_decode_attn_multi"
+    T, H = _check_qt(call, cache, q, seq_len)
+    _check_sel(call, cache.batch, cache.n_kv_heads, uni_idx, uni_cnt)
+    _need(call, (uni_mask is None) == (uni_idx is None), "uni_mask goes with uni_idx")
+    if uni_mask is not None:
+        _need(call, tuple(uni_mask.shape) == tuple(uni_idx.shape)
+              and uni_mask.element_size() == 4, "uni_mask must be 32-bit like uni_idx")
+    _check(call, load().skv_decode_attn_multi(
+        ctypes.byref(cache.desc), _ptr(q), T, H, _ptr(seq_len), int(max_len), _ptr(uni_idx),
+        _ptr(uni_cnt), _ptr(uni_mask), int(uni_idx.shape[2]) if uni_idx is not None else 0,
         float(softmax_scale), int(n_split), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))
 

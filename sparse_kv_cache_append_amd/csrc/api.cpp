@@ -13,6 +13,7 @@ constexpr int32_t kMaxSelectBlocks = 16384;
 
 bool valid_head_dim(int32_t d) { return d >= 16 && d <= 1024 && d % 16 == 0; }
 bool supported_group(int32_t g) { return g == 1 || g == 2 || g == 4 || g == 8; }
+bool supported_tokens(int32_t n) { return n == 1 || n == 2 || n == 4 || n == 8; }
 
 int32_t blocks_of(int32_t n, int32_t block) {
   return int32_t((int64_t(n) + block - 1) / block);
@@ -374,6 +375,103 @@ skv_status skv_decode_attn_heads(const skv_cache* c, const float* q, int32_t n_h
   p.ws = static_cast<float*>(workspace);
   p.dbg_logits = nullptr;
   p.sel_hmask = uni_mask;
+  return device_status(skv::launch_decode(p, stream));
+}
+
+// ------------------------------------------------------- query-token chunks
+skv_status skv_block_bounds_multi(const skv_cache* c, const float* q, int32_t n_tokens,
+                                  int32_t n_heads, const int32_t* seq_len, int32_t max_len,
+                                  float* score, hipStream_t stream) {
+  skv_status st = check_cache(c, true);
+  if (st != SKV_OK) return st;
+  if (q == nullptr || seq_len == nullptr || score == nullptr || !aligned(q)) return SKV_EINVAL;
+  st = check_heads(c, n_heads);
+  if (st != SKV_OK) return st;
+  if (n_tokens < 1) return SKV_EINVAL;
+  if (!supported_tokens(n_tokens) || (n_heads / c->n_kv_heads) * n_tokens > 16)
+    return SKV_EUNSUPPORTED;
+  if (max_len < 0 || max_len > c->max_seq) return SKV_ERANGE;
+  return device_status(
+      skv::launch_bounds_multi(*c, q, n_tokens, n_heads, seq_len, max_len, score, stream));
+}
+
+skv_status skv_select_topk_multi(const float* score, const int32_t* seq_len, int32_t batch,
+                                 int32_t n_tokens, int32_t n_kv_heads, int32_t max_blocks,
+                                 int32_t block, const int32_t* k_sel, int32_t n_sink,
+                                 int32_t n_recent, int32_t max_sel, int32_t* sel_idx,
+                                 int32_t* sel_cnt, hipStream_t stream) {
+  if (score == nullptr || seq_len == nullptr || k_sel == nullptr || sel_idx == nullptr ||
+      sel_cnt == nullptr)
+    return SKV_EINVAL;
+  if (batch < 1 || n_kv_heads < 1 || n_tokens < 1 || max_blocks < 1 || block < 1) return SKV_EINVAL;
+  if (n_sink < 0 || n_recent < 0 || max_sel < 1) return SKV_EINVAL;
+  if (!supported_tokens(n_tokens)) return SKV_EUNSUPPORTED;
+  if (max_blocks > kMaxSelectBlocks) return SKV_EUNSUPPORTED;
+  if (int64_t(max_blocks) * block > 0x7fffffff) return SKV_ERANGE;
+  if (!grid_fits(batch, n_kv_heads, n_tokens)) return SKV_ERANGE;
+  return device_status(skv::launch_select(score, seq_len, batch, n_kv_heads * n_tokens,
+                                          max_blocks, block, k_sel, n_sink, n_recent, max_sel,
+                                          sel_idx, sel_cnt, nullptr, stream, n_tokens));
+}
+
+skv_status skv_select_union_tokens(const int32_t* sel_idx, const int32_t* sel_cnt,
+                                   int32_t batch, int32_t n_tokens, int32_t n_kv_heads,
+                                   int32_t group, int32_t max_sel, int32_t max_blocks,
+                                   int32_t max_union, int32_t* uni_idx, int32_t* uni_cnt,
+                                   uint32_t* uni_mask, hipStream_t stream) {
+  if (sel_idx == nullptr || sel_cnt == nullptr || uni_idx == nullptr || uni_cnt == nullptr ||
+      uni_mask == nullptr)
+    return SKV_EINVAL;
+  if (batch < 1 || n_kv_heads < 1 || n_tokens < 1 || group < 1) return SKV_EINVAL;
+  if (max_sel < 1 || max_blocks < 1 || max_union < 1) return SKV_EINVAL;
+  if (!supported_tokens(n_tokens) || !supported_group(group) || n_tokens * group > 16)
+    return SKV_EUNSUPPORTED;
+  if (max_blocks > kMaxSelectBlocks) return SKV_EUNSUPPORTED;
+  if (!grid_fits(batch, n_kv_heads, 1)) return SKV_ERANGE;
+  return device_status(skv::launch_union(sel_idx, sel_cnt, batch, n_kv_heads, n_tokens, max_sel,
+                                         max_blocks, max_union, uni_idx, uni_cnt, uni_mask,
+                                         stream, group));
+}
+
+skv_status skv_decode_attn_multi(const skv_cache* c, const float* q, int32_t n_tokens,
+                                 int32_t n_heads, const int32_t* seq_len, int32_t max_len,
+                                 const int32_t* uni_idx, const int32_t* uni_cnt,
+                                 const uint32_t* uni_mask, int32_t max_union,
+                                 float softmax_scale, int32_t n_split, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream) {
+  skv_status st = check_cache(c, false);
+  if (st != SKV_OK) return st;
+  if (q == nullptr || seq_len == nullptr || !aligned(q)) return SKV_EINVAL;
+  const bool list = uni_idx != nullptr;
+  if (list != (uni_cnt != nullptr) || list != (uni_mask != nullptr)) return SKV_EINVAL;
+  if (list && max_union < 1) return SKV_EINVAL;
+  st = check_heads(c, n_heads);
+  if (st != SKV_OK) return st;
+  if (n_tokens < 1) return SKV_EINVAL;
+  if (!supported_tokens(n_tokens) || (n_heads / c->n_kv_heads) * n_tokens > 16)
+    return SKV_EUNSUPPORTED;
+  if (skv::is_grouped(c->kv_dtype)) return SKV_EUNSUPPORTED;
+  if (n_split < 1 || n_split > kMaxSplit) return SKV_EINVAL;
+  if (!grid_fits(n_split, c->n_kv_heads, c->batch)) return SKV_ERANGE;
+  if (!(softmax_scale == softmax_scale) || softmax_scale < 0.0f) return SKV_EINVAL;
+  if (max_len < 0 || max_len > c->max_seq) return SKV_ERANGE;
+  const size_t need = skv_workspace_bytes(c->batch, n_tokens * n_heads, c->head_dim, n_split);
+  if (workspace == nullptr || workspace_bytes < need) return SKV_EWORKSPACE;
+  skv::DecodeParams p;
+  p.c = c;
+  p.q = q;
+  p.n_heads = n_heads;
+  p.seq_len = seq_len;
+  p.max_len = max_len;
+  p.sel_idx = uni_idx;
+  p.sel_cnt = uni_cnt;
+  p.max_sel = list ? max_union : 0;
+  p.softmax_scale = softmax_scale;
+  p.n_split = n_split;
+  p.ws = static_cast<float*>(workspace);
+  p.dbg_logits = nullptr;
+  p.sel_hmask = uni_mask;
+  p.n_tok = n_tokens;
   return device_status(skv::launch_decode(p, stream));
 }
 

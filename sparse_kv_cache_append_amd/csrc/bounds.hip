@@ -165,14 +165,20 @@ __device__ __forceinline__ uint4 pack_bits(const uint16_t (&h)[8]) {
 // idempotent, and a fresh block ignores the old values.
 // PH: per-query-head bounds (score [batch][n_heads][max_blocks], no group
 // max): each query head ranks the blocks by its own bound.
-template <int D, int G, int MODE, bool PH = false>
+// NT > 1: a chunk of NT query tokens per sequence (q [batch][NT][H][D]); the
+// side cache is read once for the NT x G query rows, and each token gets its
+// own group max (score [batch][Hkv][NT][max_blocks]).
+template <int D, int G, int MODE, bool PH = false, int NT = 1>
 __global__ void __launch_bounds__(kBoundsThreads)
 bounds_kernel(uint16_t* __restrict__ kmin, uint16_t* __restrict__ kmax,
               const float* __restrict__ q, const int32_t* __restrict__ seq_len,
               float* __restrict__ score, int32_t Hkv, int32_t max_len, int32_t block,
               int32_t max_blocks, int32_t tiles, int32_t n_rows, AppendOne ap) {
   static_assert(D == kLanesPerBlock * 8, "one 16-byte load per lane per bound");
-  static_assert(G * D / 4 <= kBoundsThreads, "one 16-byte query load per thread");
+  static_assert(NT == 1 || (MODE == kNoAppend && !PH), "token chunks: plain bounds only");
+  constexpr int kQ4 = NT * G * D / 4;                          // 16-byte query loads
+  constexpr int kQPer = (kQ4 + kBoundsThreads - 1) / kBoundsThreads;
+  static_assert(kQPer <= 2, "at most 16 query rows");
   // 1-D grid of tiles x Hkv x batch, row by row (XCD-aware slots: a row's
   // scores are written on the XCD whose L2 its decode parts read them from)
   const uint32_t slot = xcd_slot(blockIdx.x, gridDim.x);
@@ -190,9 +196,17 @@ bounds_kernel(uint16_t* __restrict__ kmin, uint16_t* __restrict__ kmax,
   int32_t p0 = -1;
   if constexpr (MODE != kNoAppend) p0 = ap.pos0[b];
   const int32_t H = Hkv * G;
-  const float* qg = q + (int64_t(b) * H + g * G) * D;
-  float4 qreg = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-  if (threadIdx.x < G * D / 4) qreg = reinterpret_cast<const float4*>(qg)[threadIdx.x];
+  // query row rr = token rr / G, head rr % G: q row (b NT + t) H + g G + h
+  float4 qreg[kQPer];
+#pragma unroll
+  for (int i = 0; i < kQPer; ++i) {
+    const int e = int(threadIdx.x) + kBoundsThreads * i;
+    const int rr = e / (D / 4);
+    qreg[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    if (e < kQ4)
+      qreg[i] = reinterpret_cast<const float4*>(
+          q + ((int64_t(b) * NT + rr / G) * H + g * G + rr % G) * D)[e % (D / 4)];
+  }
   uint4 lo = make_uint4(0, 0, 0, 0), hi = make_uint4(0, 0, 0, 0);
   if (j < max_blocks) {
     const int64_t off = ((int64_t(b) * Hkv + g) * max_blocks + j) * D + c * 8;
@@ -262,36 +276,49 @@ bounds_kernel(uint16_t* __restrict__ kmin, uint16_t* __restrict__ kmax,
   const bool live = j < nb;
   float best = -INFINITY;
   if (tile * kBlocksPerWG < nb) {          // else the whole tile is past the end
-    __shared__ __attribute__((aligned(16))) float qs[G * D];
-    if (threadIdx.x < G * D / 4) reinterpret_cast<float4*>(qs)[threadIdx.x] = qreg;
-    __syncthreads();
-    float qv[G][8];
+    __shared__ __attribute__((aligned(16))) float qs[NT * G * D];
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float4 a = reinterpret_cast<const float4*>(qs + h * D + c * 8)[0];
-      const float4 bq = reinterpret_cast<const float4*>(qs + h * D + c * 8)[1];
-      qv[h][0] = a.x; qv[h][1] = a.y; qv[h][2] = a.z; qv[h][3] = a.w;
-      qv[h][4] = bq.x; qv[h][5] = bq.y; qv[h][6] = bq.z; qv[h][7] = bq.w;
+    for (int i = 0; i < kQPer; ++i) {
+      const int e = int(threadIdx.x) + kBoundsThreads * i;
+      if (e < kQ4) reinterpret_cast<float4*>(qs)[e] = qreg[i];
     }
+    __syncthreads();
     float mn[8], mx[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) { mn[e] = h2f(lb[e]); mx[e] = h2f(hb[e]); }
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float acc = 0.0f;
+    for (int t = 0; t < NT; ++t) {
+      float qv[G][8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float x = qv[h][e];
-        const float kb = x > 0.0f ? mx[e] : mn[e];
-        acc += (x != 0.0f) ? x * kb : 0.0f;
+      for (int h = 0; h < G; ++h) {
+        const float* qr = qs + (t * G + h) * D + c * 8;
+        const float4 a = reinterpret_cast<const float4*>(qr)[0];
+        const float4 bq = reinterpret_cast<const float4*>(qr)[1];
+        qv[h][0] = a.x; qv[h][1] = a.y; qv[h][2] = a.z; qv[h][3] = a.w;
+        qv[h][4] = bq.x; qv[h][5] = bq.y; qv[h][6] = bq.z; qv[h][7] = bq.w;
       }
-      acc = group16_sum(acc);
-      best = fmaxf(best, acc);
-      if constexpr (PH) {
-        if (live && c == 0) score[(int64_t(b) * H + g * G + h) * max_blocks + j] = acc;
+      float tbest = -INFINITY;
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float acc = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float x = qv[h][e];
+          const float kb = x > 0.0f ? mx[e] : mn[e];
+          acc += (x != 0.0f) ? x * kb : 0.0f;
+        }
+        acc = group16_sum(acc);
+        tbest = fmaxf(tbest, acc);
+        if constexpr (PH) {
+          if (live && c == 0) score[(int64_t(b) * H + g * G + h) * max_blocks + j] = acc;
+        }
       }
+      if constexpr (NT > 1) {
+        if (live && c == 0) score[((int64_t(b) * Hkv + g) * NT + t) * max_blocks + j] = tbest;
+      }
+      best = tbest;
     }
-    if (!PH && live && c == 0) score[(int64_t(b) * Hkv + g) * max_blocks + j] = best;
+    if (NT == 1 && !PH && live && c == 0) score[(int64_t(b) * Hkv + g) * max_blocks + j] = best;
   }
   // the append's stores
   if constexpr (MODE != kNoAppend) {
@@ -314,7 +341,7 @@ bounds_kernel(uint16_t* __restrict__ kmin, uint16_t* __restrict__ kmax,
   }
 }
 
-template <int G, int MODE, bool PH = false>
+template <int G, int MODE, bool PH = false, int NT = 1>
 hipError_t launch_bounds_g(const skv_cache& c, const float* q, const int32_t* seq_len,
                            int32_t max_len, float* score, const AppendOne& ap,
                            hipStream_t stream) {
@@ -326,7 +353,7 @@ hipError_t launch_bounds_g(const skv_cache& c, const float* q, const int32_t* se
   const int64_t n_wg = int64_t(tiles) * c.n_kv_heads * c.batch;
   if (n_wg > 0x7fffffff) return hipErrorInvalidValue;
   const dim3 grid(static_cast<uint32_t>(n_wg));
-  bounds_kernel<128, G, MODE, PH><<<grid, kBoundsThreads, 0, stream>>>(
+  bounds_kernel<128, G, MODE, PH, NT><<<grid, kBoundsThreads, 0, stream>>>(
       c.kmin, c.kmax, q, seq_len, score, c.n_kv_heads, max_len, c.block, max_blocks, tiles,
       c.n_kv_heads * c.batch, ap);
   return hipGetLastError();
@@ -351,6 +378,23 @@ hipError_t launch_bounds(const skv_cache& c, const float* q, int32_t n_heads,
                          const int32_t* seq_len, int32_t max_len, float* score,
                          hipStream_t stream) {
   return launch_bounds_m<kNoAppend>(c, q, n_heads, seq_len, max_len, score, AppendOne{}, stream);
+}
+
+hipError_t launch_bounds_multi(const skv_cache& c, const float* q, int32_t n_tok,
+                               int32_t n_heads, const int32_t* seq_len, int32_t max_len,
+                               float* score, hipStream_t stream) {
+  const AppendOne ap{};
+  const int G = n_heads / c.n_kv_heads;
+#define SKV_BMT(GG, NN)                                                                        \
+  if (G == GG && n_tok == NN)                                                                  \
+    return launch_bounds_g<GG, kNoAppend, false, NN>(c, q, seq_len, max_len, score, ap, stream)
+  SKV_BMT(1, 1); SKV_BMT(2, 1); SKV_BMT(4, 1); SKV_BMT(8, 1);
+  SKV_BMT(1, 2); SKV_BMT(1, 4); SKV_BMT(1, 8);
+  SKV_BMT(2, 2); SKV_BMT(2, 4); SKV_BMT(2, 8);
+  SKV_BMT(4, 2); SKV_BMT(4, 4);
+  SKV_BMT(8, 2);
+#undef SKV_BMT
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_bounds_heads(const skv_cache& c, const float* q, int32_t n_heads,

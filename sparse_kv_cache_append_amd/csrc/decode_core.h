@@ -158,6 +158,23 @@ __device__ __forceinline__ TileWalk make_walk(const ListSeed& ls, const int32_t*
   return tw;
 }
 
+// The query rows behind the G MFMA columns of KV head g of sequence b: a
+// chunk of ntok query tokens times gh = G / ntok heads, column i = token
+// i / gh, head i % gh of the group.  q and the partial states are laid out
+// [batch][ntok][Hkv * gh] rows; ntok = 1 gives the decode layout, row
+// b * H + g * G + i.
+struct QRows {
+  int32_t ntok, gsh, H;    // tokens, log2 of the heads per token, heads per token
+  __device__ __forceinline__ int64_t row(int32_t b, int32_t g, int i) const {
+    return (int64_t(b) * ntok + (i >> gsh)) * H + (int64_t(g) << gsh) + (i & ((1 << gsh) - 1));
+  }
+};
+template <int G>
+__device__ __forceinline__ QRows make_qrows(int32_t ntok, int32_t Hkv) {
+  const int32_t gh = G / ntok;
+  return QRows{ntok, __builtin_ctz(uint32_t(gh)), Hkv * gh};
+}
+
 // Softmax bookkeeping of one tile for the 16 MFMA columns (heads): lane l
 // owns head l%16 and rows 4*(l/16) + r of the tile.  s[r] are base-2 logits
 // (-inf for masked rows); returns the weights p[r] and rescales O when the
@@ -203,14 +220,21 @@ __device__ __forceinline__ void tile_softmax(float (&s)[4 * NT], float& m_run, f
     l_run = l_run * cr + ps;
     // O rows are heads 4*(lane/16) + r; head h's factor is in lane h (column
     // h of every row holds it).  Only heads < G matter: rows past them hold
-    // padding and may take any finite factor.
-    const bool upper = G > 4 && lane >= 16;
+    // padding and may take any finite factor.  (G <= 16.)
+    const int quad = lane / 16;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cr), r));
       if (G > 4) {
         const float c4 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cr), 4 + r));
-        c = upper ? c4 : c;
+        if (G > 8) {
+          const float c8 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cr), 8 + r));
+          const float c12 =
+              __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cr), 12 + r));
+          c = quad == 0 ? c : (quad == 1 ? c4 : (quad == 2 ? c8 : c12));
+        } else {
+          c = quad > 0 ? c4 : c;
+        }
       }
       c *= o_extra;
 #pragma unroll
@@ -228,7 +252,8 @@ template <int G>
 __device__ __forceinline__ void finish_mfma(float m_run, float l_run, const float4_t (&O)[8],
                                             float* lds, float* __restrict__ ws_m,
                                             float* __restrict__ ws_l, float* __restrict__ ws_o,
-                                            int64_t head0, int32_t n_split, int32_t split) {
+                                            const QRows& qr, int32_t b, int32_t g,
+                                            int32_t n_split, int32_t split) {
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   float* lo = lds;                          // [waves][G][D]
   float* lm = lds + kMWaves * G * kD;       // [waves][G]
@@ -260,7 +285,7 @@ __device__ __forceinline__ void finish_mfma(float m_run, float l_run, const floa
         sl += a * ll[w * G + h];
       }
     }
-    const int64_t ps = (head0 + h) * n_split + split;
+    const int64_t ps = qr.row(b, g, h) * n_split + split;
     ws_o[ps * kD + d] = so;
     if (d == 0) { ws_m[ps] = M; ws_l[ps] = sl; }
   }

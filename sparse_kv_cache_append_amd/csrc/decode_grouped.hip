@@ -364,7 +364,7 @@ decode_grp_mfma(const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
     }
   }
   finish_mfma<G>(m_run, l_run, O, reinterpret_cast<float*>(&smem[0][0][0]), ws_m, ws_l, ws_o,
-                 int64_t(b) * H + g * G, n_split, split);
+                 make_qrows<G>(1, Hkv), b, g, n_split, split);
 }
 
 }  // namespace

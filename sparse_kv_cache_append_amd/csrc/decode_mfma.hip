@@ -234,7 +234,8 @@ decode_f16_mfma(const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc
                 int32_t max_sel, int32_t Hkv, int32_t max_seq, int32_t block, int32_t max_len,
                 int32_t n_split, int32_t n_rows, int32_t units_per_split, float qscale2,
                 float* __restrict__ ws_m, float* __restrict__ ws_l, float* __restrict__ ws_o,
-                FusedSelect fs, AppendArgs app, const uint32_t* __restrict__ sel_hmask) {
+                FusedSelect fs, AppendArgs app, const uint32_t* __restrict__ sel_hmask,
+                int32_t ntok) {
   constexpr int T = 16;
   constexpr int kTileBytes = T * kRowBytesF16;              // 4096
   __shared__ __attribute__((aligned(16))) uint8_t smem[kMWaves][2][2 * kTileBytes];
@@ -246,7 +247,7 @@ decode_f16_mfma(const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc
   const int lane = threadIdx.x % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lg = lane / 16, lc = lane % 16;
-  const int32_t H = Hkv * G;
+  const QRows qr = make_qrows<G>(ntok, Hkv);
   const int64_t bg = int64_t(b) * Hkv + g;
   // requests issued before anything waits: row length, given list, query
   const int32_t L_raw = seq_len[b];
@@ -266,7 +267,7 @@ decode_f16_mfma(const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc
   half8_t qhi[4], qlo[4];
   {
     const bool hv = lc < G;
-    const float* qp = q + (int64_t(b) * H + g * G + (hv ? lc : 0)) * kD;
+    const float* qp = q + qr.row(b, g, hv ? lc : 0) * kD;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       const float4 a = *reinterpret_cast<const float4*>(qp + 32 * kk + 8 * lg);
@@ -347,7 +348,7 @@ decode_f16_mfma(const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc
         *reinterpret_cast<uint32_t*>(vt + off) = vx;
       }
     }
-    const int32_t nvalid = fr.nvalid;
+    const int32_t nvalid = fr.nvalid, r0 = fr.r0;
     const uint32_t hm = fr.hm;
     issue(fr);
     // LDS writes above and reads below touch the same array: they stay in
@@ -364,9 +365,13 @@ decode_f16_mfma(const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc
     float sc[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) sc[r] = acc[r];
-    if (nvalid < T) {
+    if (nvalid < T || r0 + T > L - ntok + 1) {     // wave-uniform
+      // rows past the row's length; with a chunk of query tokens, column lc
+      // is token lc >> gsh, which sees the positions below
+      // L - (ntok - 1 - token) only
+      const int32_t lim = min(nvalid, L - (ntok - 1 - (lc >> qr.gsh)) - r0);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sc[r] = (4 * lg + r < nvalid) ? sc[r] : -INFINITY;
+      for (int r = 0; r < 4; ++r) sc[r] = (4 * lg + r < lim) ? sc[r] : -INFINITY;
     }
     if constexpr (HM) {
       // the heads that did not choose this block leave it out
@@ -415,7 +420,7 @@ decode_f16_mfma(const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc
     for (int r = 0; r < 4; ++r) O[n][r] *= 1.0f / float(1 << kPwShiftF16);
   }
   finish_mfma<G>(m_run, l_run, O, reinterpret_cast<float*>(&smem[0][0][0]), ws_m, ws_l, ws_o,
-                 int64_t(b) * H + g * G, n_split, split);
+                 qr, b, g, n_split, split);
   if constexpr (APP) {
     if (ao.own) {
       const int64_t row = (bg * max_seq + p_new) * (kD / 2) + lane;
@@ -472,7 +477,7 @@ decode_i8_mfma(const int8_t* __restrict__ kc, const int8_t* __restrict__ vc,
                int32_t n_split, int32_t n_rows, int32_t units_per_split, float scale2,
                float* __restrict__ ws_m, float* __restrict__ ws_l, float* __restrict__ ws_o,
                int32_t* __restrict__ dbg, FusedSelect fs, AppendArgs app,
-               const uint32_t* __restrict__ sel_hmask) {
+               const uint32_t* __restrict__ sel_hmask, int32_t ntok) {
   constexpr int T = 32;
   constexpr int kTileBytes = T * kRowBytesI8;               // 4096
   constexpr int kScaleOff = 2 * kTileBytes;                 // 32 K scales, 32 V scales
@@ -486,7 +491,7 @@ decode_i8_mfma(const int8_t* __restrict__ kc, const int8_t* __restrict__ vc,
   const int lane = threadIdx.x % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lg = lane / 16, lc = lane % 16;
-  const int32_t H = Hkv * G;
+  const QRows qr = make_qrows<G>(ntok, Hkv);
   const int64_t bg = int64_t(b) * Hkv + g;
   // requests issued before anything waits: row length, given list, query
   const int32_t L_raw = seq_len[b];
@@ -507,7 +512,7 @@ decode_i8_mfma(const int8_t* __restrict__ kc, const int8_t* __restrict__ vc,
   const bool hv = lc < G;
   float x[2][16];
   {
-    const float* qp = q + (int64_t(b) * H + g * G + (hv ? lc : 0)) * kD;
+    const float* qp = q + qr.row(b, g, hv ? lc : 0) * kD;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
@@ -540,8 +545,7 @@ decode_i8_mfma(const int8_t* __restrict__ kc, const int8_t* __restrict__ vc,
   const float* vsb = vsc + bg * int64_t(max_seq);
   // optional exact-logit dump (uniform test, so the hot loop only branches once)
   const bool want_dbg = dbg != nullptr;
-  int32_t* dbg_h = want_dbg ? dbg + (int64_t(b) * H + g * G + min(lc, G - 1)) * int64_t(max_len)
-                            : nullptr;
+  int32_t* dbg_h = want_dbg ? dbg + qr.row(b, g, min(lc, G - 1)) * int64_t(max_len) : nullptr;
   const int32_t last = max(L - 1, 0);
   const float* sbase = (lane < 32 ? ksb : vsb) + lane % 32;
   struct Frag { int4_t k[4], v[4]; float sc; int32_t r0, nvalid; uint32_t hm; };
@@ -651,10 +655,13 @@ decode_i8_mfma(const int8_t* __restrict__ kc, const int8_t* __restrict__ vc,
     float sc[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) sc[e] = float(acc[e / 4][e % 4]) * coef * ks[e];
-    if (nvalid < T) {
+    if (nvalid < T || r0 + T > L - ntok + 1) {     // wave-uniform
+      // rows past the row's length, and a chunk token's causal limit (as in
+      // the f16 kernel)
+      const int32_t lim = min(nvalid, L - (ntok - 1 - (lc >> qr.gsh)) - r0);
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        sc[e] = 16 * (e / 4) + 4 * lg + e % 4 < nvalid ? sc[e] : -INFINITY;
+        sc[e] = 16 * (e / 4) + 4 * lg + e % 4 < lim ? sc[e] : -INFINITY;
     }
     if constexpr (HM) {
       // the heads that did not choose this block leave it out
@@ -729,7 +736,7 @@ decode_i8_mfma(const int8_t* __restrict__ kc, const int8_t* __restrict__ vc,
     }
   }
   finish_mfma<G>(m_run, l_run, O, reinterpret_cast<float*>(&smem[0][0][0]), ws_m, ws_l, ws_o,
-                 int64_t(b) * H + g * G, n_split, split);
+                 qr, b, g, n_split, split);
   if constexpr (APP) {
     if (ao.own) {
       const int64_t row = bg * max_seq + p_new;
@@ -757,11 +764,16 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   const skv_cache& c = *p.c;
   if (c.block % 16 != 0) return hipErrorInvalidValue;
   const int32_t B = c.batch, H = p.n_heads, S = p.n_split;
-  const int G = H / c.n_kv_heads;
-  if (G != 1 && G != 2 && G != 4 && G != 8) return hipErrorInvalidValue;
-  float* ws_m = p.ws + ws_m_offset(B, H, S);
-  float* ws_l = p.ws + ws_l_offset(B, H, S);
-  float* ws_o = p.ws + ws_o_offset(B, H, S);
+  // MFMA columns per KV head: n_tok query tokens x the group's heads
+  const int32_t nt = p.n_tok;
+  if (nt != 1 && nt != 2 && nt != 4 && nt != 8) return hipErrorInvalidValue;
+  const int G = (H / c.n_kv_heads) * nt;
+  if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16) return hipErrorInvalidValue;
+  if (nt > 1 && (p.fused_r > 0 || p.app.k_new != nullptr)) return hipErrorInvalidValue;
+  const int32_t Hq = H * nt;                  // partial-state rows per sequence
+  float* ws_m = p.ws + ws_m_offset(B, Hq, S);
+  float* ws_l = p.ws + ws_l_offset(B, Hq, S);
+  float* ws_o = p.ws + ws_o_offset(B, Hq, S);
   // units (blocks, or entries of the selected list) per part; at least one,
   // also for an empty cache (max_len == 0), since the folded append divides
   // the new token's block index by it to find the part that writes the token
@@ -794,7 +806,7 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   decode_f16_mfma<GG, SR, AP, HMK><<<grid, kMThreads, 0, stream>>>(                            \
       static_cast<const uint16_t*>(c.k), static_cast<const uint16_t*>(c.v), p.q, p.seq_len,    \
       p.sel_idx, p.sel_cnt, p.max_sel, c.n_kv_heads, c.max_seq, c.block, p.max_len, S,        \
-      n_rows, ups, scale2, ws_m, ws_l, ws_o, p.fsel, aa, p.sel_hmask)
+      n_rows, ups, scale2, ws_m, ws_l, ws_o, p.fsel, aa, p.sel_hmask, nt)
 #define SKV_F16_G(GG)                                  \
   if (app) SKV_LAUNCH_F16(GG, 0, true, false);         \
   else if (hmk) SKV_LAUNCH_F16(GG, 0, false, true);    \
@@ -806,7 +818,11 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
       case 1: SKV_F16_G(1); break;
       case 2: SKV_F16_G(2); break;
       case 4: SKV_F16_G(4); break;
-      default: SKV_F16_G(8); break;
+      case 8: SKV_F16_G(8); break;
+      default:                // 16 columns: query-token chunks only (no fused variants)
+        if (hmk) SKV_LAUNCH_F16(16, 0, false, true);
+        else SKV_LAUNCH_F16(16, 0, false, false);
+        break;
     }
 #undef SKV_F16_G
 #undef SKV_LAUNCH_F16
@@ -818,7 +834,7 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
       static_cast<const int8_t*>(c.k), static_cast<const int8_t*>(c.v), c.k_scale, c.v_scale,  \
       p.q, p.seq_len, p.sel_idx, p.sel_cnt, p.max_sel, c.n_kv_heads, c.max_seq, c.block,       \
       p.max_len, S, n_rows, ups, scale2, ws_m, ws_l, ws_o, p.dbg_logits, p.fsel, aa,          \
-      p.sel_hmask)
+      p.sel_hmask, nt)
 #define SKV_I8_G(GG)                                   \
   if (app) SKV_LAUNCH_I8(GG, 0, true, false);          \
   else if (hmk) SKV_LAUNCH_I8(GG, 0, false, true);     \
@@ -830,7 +846,11 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
     case 1: SKV_I8_G(1); break;
     case 2: SKV_I8_G(2); break;
     case 4: SKV_I8_G(4); break;
-    default: SKV_I8_G(8); break;
+    case 8: SKV_I8_G(8); break;
+    default:
+      if (hmk) SKV_LAUNCH_I8(16, 0, false, true);
+      else SKV_LAUNCH_I8(16, 0, false, false);
+      break;
   }
 #undef SKV_I8_G
 #undef SKV_LAUNCH_I8

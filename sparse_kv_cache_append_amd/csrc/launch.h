@@ -58,6 +58,7 @@ struct DecodeParams {
   FusedSelect fsel{};
   FoldedAppend app{};       // dense walks only (sel_idx == nullptr, fused_r == 0)
   const uint32_t* sel_hmask = nullptr;   // per-query-head lists: head mask per entry
+  int32_t n_tok = 1;        // query tokens per sequence (q [batch][n_tok][n_heads][D])
 };
 
 hipError_t launch_append(const skv_cache& c, const int32_t* pos0, int32_t n_new,
@@ -90,17 +91,29 @@ hipError_t launch_bounds_heads(const skv_cache& c, const float* q, int32_t n_hea
                                const int32_t* seq_len, int32_t max_len, float* score,
                                hipStream_t stream);
 
-// Union of a KV head's per-query-head lists with a head mask per block.
+// Bounds of a chunk of n_tok query tokens per sequence (q [batch][n_tok]
+// [n_heads][D]): score [batch][n_kv_heads][n_tok][max_blocks], each token's
+// group max.
+hipError_t launch_bounds_multi(const skv_cache& c, const float* q, int32_t n_tok,
+                               int32_t n_heads, const int32_t* seq_len, int32_t max_len,
+                               float* score, hipStream_t stream);
+
+// Union of `group` consecutive lists per (sequence, KV head) (rows
+// (b n_kv_heads + g) group + i of sel_idx), list i's blocks tagged with bits
+// [i bits_per_list, (i + 1) bits_per_list) of the mask.
 hipError_t launch_union(const int32_t* sel_idx, const int32_t* sel_cnt, int32_t batch,
                         int32_t n_kv_heads, int32_t group, int32_t max_sel, int32_t max_blocks,
                         int32_t max_union, int32_t* uni_idx, int32_t* uni_cnt,
-                        uint32_t* uni_mask, hipStream_t stream);
+                        uint32_t* uni_mask, hipStream_t stream, int32_t bits_per_list = 1);
 
+// n_tok > 1: the rows are (KV head, token) pairs of a query-token chunk
+// (n_kv_heads counts the pairs), token t seeing seq_len - (n_tok - 1 - t)
+// positions.
 hipError_t launch_select(const float* score, const int32_t* seq_len, int32_t batch,
                          int32_t n_kv_heads, int32_t max_blocks, int32_t block,
                          const int32_t* k_sel, int32_t n_sink, int32_t n_recent,
                          int32_t max_sel, int32_t* sel_idx, int32_t* sel_cnt,
-                         uint32_t* sel_mask, hipStream_t stream);
+                         uint32_t* sel_mask, hipStream_t stream, int32_t n_tok = 1);
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
 

@@ -23,7 +23,7 @@ __global__ void __launch_bounds__(kSelThreads)
 select_kernel(const float* __restrict__ score, const int32_t* __restrict__ seq_len,
               int32_t Hkv, int32_t max_blocks, int32_t block, const int32_t* __restrict__ k_sel,
               int32_t n_sink, int32_t n_recent, int32_t max_sel, int32_t* __restrict__ sel_idx,
-              int32_t* __restrict__ sel_cnt, uint32_t* __restrict__ sel_mask) {
+              int32_t* __restrict__ sel_cnt, uint32_t* __restrict__ sel_mask, int32_t n_tok) {
   __shared__ SelectShared sh;
   __shared__ uint32_t maskw[kMaxSelectBlocks / 32];
 
@@ -38,7 +38,11 @@ select_kernel(const float* __restrict__ score, const int32_t* __restrict__ seq_l
   SelKeys<RMAX> kk;
   kk.load(score + row * max_blocks + n_sink, max_blocks - n_sink);
   sel_init(sh);
-  const int32_t L = min(max(seq_len[b], 0), max_blocks * block);
+  // a chunk of n_tok query tokens: rows are (KV head, token) pairs (Hkv counts
+  // them), and token t of the chunk sees the first seq_len - (n_tok - 1 - t)
+  // positions
+  const int32_t back = n_tok - 1 - g % n_tok;
+  const int32_t L = min(max(seq_len[b] - back, 0), max_blocks * block);
   const int32_t nb = (L + block - 1) / block;
   const int32_t cs = min(n_sink, nb);                       // candidates [cs, ce)
   const int32_t ce = max(nb - n_recent, cs);
@@ -95,7 +99,7 @@ __global__ void __launch_bounds__(kSelThreads)
 union_kernel(const int32_t* __restrict__ sel_idx, const int32_t* __restrict__ sel_cnt,
              int32_t Hkv, int32_t G, int32_t max_sel, int32_t max_blocks, int32_t max_union,
              int32_t* __restrict__ uni_idx, int32_t* __restrict__ uni_cnt,
-             uint32_t* __restrict__ uni_mask) {
+             uint32_t* __restrict__ uni_mask, int32_t bpr) {
   __shared__ uint32_t hw[kMaxSelectBlocks / 4];
   __shared__ int32_t wsum[kSelThreads / kWave];
   const int32_t row = int32_t(blockIdx.x);
@@ -133,8 +137,15 @@ union_kernel(const int32_t* __restrict__ sel_idx, const int32_t* __restrict__ se
     const uint32_t m = (hw[j >> 2] >> (8 * (j & 3))) & 0xFFu;
     if (m != 0u) {
       if (pos < max_union) {
+        // list i's bit becomes bits [i bpr, (i + 1) bpr) of the mask
+        uint32_t mm = m;
+        if (bpr > 1) {
+          mm = 0u;
+          for (int i = 0; i < G; ++i)
+            if ((m >> i) & 1u) mm |= ((1u << bpr) - 1u) << (i * bpr);
+        }
         uni_idx[out + pos] = j;
-        uni_mask[out + pos] = m;
+        uni_mask[out + pos] = mm;
       }
       ++pos;
     }
@@ -152,7 +163,8 @@ hipError_t launch_select(const float* score, const int32_t* seq_len, int32_t bat
                          int32_t n_kv_heads, int32_t max_blocks, int32_t block,
                          const int32_t* k_sel, int32_t n_sink, int32_t n_recent,
                          int32_t max_sel, int32_t* sel_idx, int32_t* sel_cnt,
-                         uint32_t* sel_mask, hipStream_t stream) {
+                         uint32_t* sel_mask, hipStream_t stream, int32_t n_tok) {
+  if (n_tok < 1 || n_kv_heads % n_tok != 0) return hipErrorInvalidValue;
   if (max_blocks > kMaxSelectBlocks) return hipErrorInvalidValue;
   const int64_t rows = int64_t(n_kv_heads) * batch;
   if (rows > 0x7fffffff) return hipErrorInvalidValue;
@@ -160,7 +172,7 @@ hipError_t launch_select(const float* score, const int32_t* seq_len, int32_t bat
 #define SKV_LAUNCH_SELECT(RM)                                                                 \
   select_kernel<RM><<<grid, kSelThreads, 0, stream>>>(score, seq_len, n_kv_heads, max_blocks, \
                                                       block, k_sel, n_sink, n_recent, max_sel, \
-                                                      sel_idx, sel_cnt, sel_mask)
+                                                      sel_idx, sel_cnt, sel_mask, n_tok)
   if (max_blocks <= 4 * kSelThreads) SKV_LAUNCH_SELECT(4);
   else if (max_blocks <= 16 * kSelThreads) SKV_LAUNCH_SELECT(16);
   else SKV_LAUNCH_SELECT(64);
@@ -171,13 +183,14 @@ hipError_t launch_select(const float* score, const int32_t* seq_len, int32_t bat
 hipError_t launch_union(const int32_t* sel_idx, const int32_t* sel_cnt, int32_t batch,
                         int32_t n_kv_heads, int32_t group, int32_t max_sel, int32_t max_blocks,
                         int32_t max_union, int32_t* uni_idx, int32_t* uni_cnt,
-                        uint32_t* uni_mask, hipStream_t stream) {
+                        uint32_t* uni_mask, hipStream_t stream, int32_t bits_per_list) {
   if (max_blocks > kMaxSelectBlocks || group < 1 || group > 8) return hipErrorInvalidValue;
+  if (bits_per_list < 1 || group * bits_per_list > 32) return hipErrorInvalidValue;
   const int64_t rows = int64_t(batch) * n_kv_heads;
   if (rows > 0x7fffffff) return hipErrorInvalidValue;
   union_kernel<<<dim3(uint32_t(rows)), kSelThreads, 0, stream>>>(
       sel_idx, sel_cnt, n_kv_heads, group, max_sel, max_blocks, max_union, uni_idx, uni_cnt,
-      uni_mask);
+      uni_mask, bits_per_list);
   return hipGetLastError();
 }
 

@@ -284,3 +284,41 @@ def test_binding_checks_decode_step(lib):
     _rejected(lambda: skv.decode_step(c, q, sl, 64, 0.1, 2, ws, out, k_sel=ks, score=score))
     _rejected(lambda: skv.decode_step(c, q, sl, 64, 0.1, 2, ws, out, k_sel=ks.long(),
                                       score=score, sel_idx=si, sel_cnt=sc))
+
+
+def test_token_chunk_validation(lib):
+    """Query-token chunks: T in {1, 2, 4, 8}, T x G <= 16, lists all-or-none,
+    the workspace sized for T x n_heads rows; every failure before a launch."""
+    d = desc()                                      # G = 32 / 8 = 4
+    q, sl, score = 0x5000, 0x6000, 0x7000
+    bb = lib.skv_block_bounds_multi
+    assert bb(ctypes.byref(d), q, 3, 32, sl, 1024, score, None) == skv.SKV_EUNSUPPORTED
+    assert bb(ctypes.byref(d), q, 8, 32, sl, 1024, score, None) == skv.SKV_EUNSUPPORTED  # 32 cols
+    assert bb(ctypes.byref(d), q, 0, 32, sl, 1024, score, None) == skv.SKV_EINVAL
+    assert bb(ctypes.byref(d), q, 4, 32, sl, 2048, score, None) == skv.SKV_ERANGE
+    assert bb(ctypes.byref(d), None, 4, 32, sl, 1024, score, None) == skv.SKV_EINVAL
+    st = lib.skv_select_topk_multi
+    assert st(score, sl, 1, 3, 8, 16, 64, 0x8000, 1, 2, 8, 0x9000, 0xA000, None) == \
+        skv.SKV_EUNSUPPORTED
+    assert st(score, sl, 1, 0, 8, 16, 64, 0x8000, 1, 2, 8, 0x9000, 0xA000, None) == skv.SKV_EINVAL
+    assert st(score, sl, 1, 4, 8, 16, 64, None, 1, 2, 8, 0x9000, 0xA000, None) == skv.SKV_EINVAL
+    un = lib.skv_select_union_tokens
+    assert un(0x9000, 0xA000, 1, 4, 8, 3, 8, 16, 32, 0xB000, 0xC000, 0xD000, None) == \
+        skv.SKV_EUNSUPPORTED                        # group 3
+    assert un(0x9000, 0xA000, 1, 8, 8, 4, 8, 16, 32, 0xB000, 0xC000, 0xD000, None) == \
+        skv.SKV_EUNSUPPORTED                        # 32 bits
+    assert un(0x9000, 0xA000, 1, 4, 8, 4, 8, 16, 32, 0xB000, 0xC000, None, None) == skv.SKV_EINVAL
+    da = lib.skv_decode_attn_multi
+    need = skv.workspace_bytes(1, 4 * 32, 128, 4)
+    assert need == skv.workspace_bytes(1, 32, 128, 4) * 4
+    assert da(ctypes.byref(d), q, 4, 32, sl, 1024, None, None, None, 0, 0.1, 4, 0xE000,
+              need - 1, None) == skv.SKV_EWORKSPACE
+    assert da(ctypes.byref(d), q, 8, 32, sl, 1024, None, None, None, 0, 0.1, 4, 0xE000,
+              need * 2, None) == skv.SKV_EUNSUPPORTED
+    assert da(ctypes.byref(d), q, 4, 32, sl, 1024, 0x9000, None, None, 8, 0.1, 4, 0xE000,
+              need, None) == skv.SKV_EINVAL       # half a list
+    assert da(ctypes.byref(d), q, 4, 32, sl, 1024, None, None, None, 0, -1.0, 4, 0xE000,
+              need, None) == skv.SKV_EINVAL
+    g = desc(kv_dtype=skv.SKV_Q8_0, k_scale=0xF000, v_scale=0xF100)
+    assert da(ctypes.byref(g), q, 2, 32, sl, 1024, None, None, None, 0, 0.1, 4, 0xE000,
+              need, None) == skv.SKV_EUNSUPPORTED

@@ -45,7 +45,7 @@ from typing import List, Optional
 import numpy as np
 
 __all__ = ["Workload", "gaussian", "clustered", "named", "quest32k_at", "quest32k_quant",
-           "lengths_config4", "NAMED"]
+           "lengths_config4", "chunk_queries", "NAMED"]
 
 
 @dataclasses.dataclass
@@ -198,3 +198,17 @@ def quest32k_at(L: int) -> Workload:
     return clustered([1003], 32, 8, 128, [L], "f16", n_dirs=64,
                      name=f"quest-f16 B1 H32/Hkv8 D128 L{L} K_SEL{nb // 4} sink1 recent2",
                      k_sel=[nb // 4], n_sink=1, n_recent=2)
+
+
+def chunk_queries(w: Workload, T: int, seed: int, noise: float = 1.5) -> np.ndarray:
+    """Queries of a chunk of T tokens per sequence, [B][T][H][D] float32:
+    token 0 is the workload's own query, token t > 0 that query plus
+    ``noise`` * N(0, 1) (drawn in token order), so the chunk's tokens lean on
+    the same key directions but rank the blocks differently."""
+    rng = np.random.default_rng(seed)
+    out = np.empty((w.B, T, w.H, w.D), dtype=np.float32)
+    out[:, 0] = w.q
+    for t in range(1, T):
+        out[:, t] = w.q + np.float32(noise) * rng.standard_normal((w.B, w.H, w.D),
+                                                                 dtype=np.float32)
+    return out
