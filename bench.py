@@ -556,6 +556,10 @@ def measure(w, args, quest: bool, dense: bool, detail: bool = False):
         if not args.no_scan4 and w.kv_dtype == "f16":
             res["scan4"] = measure_scan4(T, skv, torch, w, caches, R, q, seq_len, Lmax,
                                          args.scan4_delta)
+        n_chunk = min(args.chunk_tokens, 16 // w.G)
+        if n_chunk > 1 and not grouped:
+            res["chunk"] = measure_chunk(T, skv, torch, w, caches, R, seq_len, Lmax, n_chunk,
+                                         res.get("dense"), res["quest"])
         if args.sparse_v_tau > 0 and not grouped:
             res["quest_sparse_v"] = measure_sparse_v(
                 T, skv, torch, w, caches, R, q, seq_len, Lmax, new_k, new_v, pos_last, ks, score,
@@ -566,6 +570,85 @@ def measure(w, args, quest: bool, dense: bool, detail: bool = False):
     del caches
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
+    return res
+
+
+def measure_chunk(T, skv, torch, w, caches, R, seq_len, Lmax, n_tok, dense_res, quest_res):
+    """A chunk of n_tok query tokens per sequence (the last n_tok positions;
+    queries from workloads.chunk_queries): the chunk's append (kv_append of
+    n_tok rows), then dense (decode_attn_multi + combine) or Quest
+    (block_bounds_multi, select_topk_multi, select_union_tokens,
+    decode_attn_multi over each token's own blocks, combine).  Compared with
+    n_tok single-token steps of the same workload.  Bytes: the side cache
+    (Quest), the KV rows of every block some token attends (read once for the
+    chunk), n_tok queries and outputs."""
+    import workloads
+    B, H, Hkv, D, blk = w.B, w.H, w.Hkv, w.D, w.block
+    dev = seq_len.device
+    qc = torch.from_numpy(workloads.chunk_queries(w, n_tok, 7000 + n_tok)).to(dev)
+    rng = np.random.default_rng(7100)
+    dt = torch.float16 if w.kv_dtype == "f16" else torch.float32
+    nk = torch.from_numpy(rng.standard_normal((B, n_tok, Hkv, D), dtype=np.float32)).to(dev, dt)
+    nv = torch.from_numpy(rng.standard_normal((B, n_tok, Hkv, D), dtype=np.float32)).to(dev, dt)
+    pos = (seq_len - n_tok).clamp(min=0).to(torch.int32)
+    max_blocks = caches[0].max_blocks
+    max_sel = max(w.k_sel) + w.n_sink + w.n_recent
+    max_union = min(max_blocks, n_tok * max_sel)
+    sc = torch.empty((B, Hkv, n_tok, max_blocks), dtype=torch.float32, device=dev)
+    sel = torch.empty((B, Hkv, n_tok, max_sel), dtype=torch.int32, device=dev)
+    cnt = torch.empty((B, Hkv, n_tok), dtype=torch.int32, device=dev)
+    uni = torch.empty((B, Hkv, max_union), dtype=torch.int32, device=dev)
+    ucnt = torch.empty((B, Hkv), dtype=torch.int32, device=dev)
+    um = torch.empty((B, Hkv, max_union), dtype=torch.int32, device=dev)
+    ks = torch.tensor(w.k_sel, dtype=torch.int32, device=dev)
+    nb = -(-Lmax // blk)
+    S_d = skv.default_split(B, Hkv, nb, kv_dtype=w.kv_dtype)
+    S_q = skv.default_split(B, Hkv, max_union, kv_dtype=w.kv_dtype, sparse=True)
+    ws_d = torch.empty(skv.workspace_bytes(B, n_tok * H, D, S_d), dtype=torch.uint8, device=dev)
+    ws_q = torch.empty(skv.workspace_bytes(B, n_tok * H, D, S_q), dtype=torch.uint8, device=dev)
+    out = torch.empty((B, n_tok * H, D), dtype=torch.float32, device=dev)
+
+    def dense_step(i):
+        c = caches[i % R]
+        skv.kv_append(c, pos, nk, nv)
+        skv.decode_attn_multi(c, qc, seq_len, Lmax, w.softmax_scale, S_d, ws_d)
+        skv.combine(ws_d, B, n_tok * H, D, S_d, out)
+
+    def quest_step(i):
+        c = caches[i % R]
+        skv.kv_append(c, pos, nk, nv)
+        skv.block_bounds_multi(c, qc, seq_len, Lmax, sc)
+        skv.select_topk_multi(sc, seq_len, blk, ks, w.n_sink, w.n_recent, sel, cnt)
+        skv.select_union_tokens(sel, cnt, w.G, max_blocks, uni, ucnt, um)
+        skv.decode_attn_multi(c, qc, seq_len, Lmax, w.softmax_scale, S_q, ws_q, uni, ucnt, um)
+        skv.combine(ws_q, B, n_tok * H, D, S_q, out)
+
+    quest_step(0)
+    torch.cuda.synchronize()
+    u_h, c_h = uni.cpu().numpy(), ucnt.cpu().numpy()
+    attended = {(b, g): u_h[b, g, :c_h[b, g]].tolist() for b in range(B) for g in range(Hkv)}
+    qio = (n_tok - 1) * B * H * D * 4 * 2                     # the extra queries and outputs
+    qb = step_bytes(w.lens, Hkv, H, D, w.kv_dtype, blk, attended)
+    db = step_bytes(w.lens, Hkv, H, D, w.kv_dtype, blk, None)
+    res = {"n_tokens": n_tok, "columns_per_kv_head": n_tok * w.G}
+    gr, _ = T.graph(quest_step)
+    us = (gr if gr is not None else T.stream(quest_step)) * 1e6
+    n_all = sum(-(-L // blk) for L in w.lens) * Hkv
+    res["quest"] = {"us_per_step": round(us, 3),
+                    "vs_single_token_steps": round(us / (n_tok * quest_res["us_per_step"]), 4),
+                    "bytes_per_step": qb["total"] + qio,
+                    "union_blocks_frac": round(sum(len(x) for x in attended.values()) / n_all, 4),
+                    "pct_hbm_peak": round(100 * (qb["total"] + qio) / us / 1e3 / HBM_PEAK_GBPS, 2),
+                    "n_split": S_q}
+    if dense_res is not None:
+        gr, _ = T.graph(dense_step)
+        us = (gr if gr is not None else T.stream(dense_step)) * 1e6
+        res["dense"] = {"us_per_step": round(us, 3),
+                        "vs_single_token_steps": round(us / (n_tok * dense_res["us_per_step"]), 4),
+                        "bytes_per_step": db["total"] + qio,
+                        "pct_hbm_peak": round(100 * (db["total"] + qio) / us / 1e3
+                                              / HBM_PEAK_GBPS, 2),
+                        "n_split": S_d}
     return res
 
 
@@ -735,6 +818,8 @@ def main():
                     help="other workloads to time besides the 32K headline ('' = none; "
                          "3@L = the 32K Quest generator at context L; 3q8 / 3q4 = over a "
                          "q8_0 / q4_0 cache)")
+    ap.add_argument("--chunk-tokens", type=int, default=4,
+                    help="query tokens per chunk for the multi-token measurement (0 = off)")
     ap.add_argument("--no-per-head", action="store_true",
                     help="skip the Quest steps with one block set per query head")
     ap.add_argument("--no-scan4", action="store_true",
@@ -836,6 +921,7 @@ def main():
         "quest_sparse_v": head.get("quest_sparse_v"),
         "quest_per_head": head.get("quest_per_head"),
         "scan4": head.get("scan4"),
+        "chunk": head.get("chunk"),
         "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4),
                      "traffic": recorded_traffic(rk), "kernel": rk,
