@@ -14,6 +14,7 @@
 //
 // A decode step may fold its one-token append into this pass
 // (launch_append_bounds), which saves a launch and a dependent round trip.
+#include "decode_core.h"
 #include "device_common.h"
 #include "launch.h"
 
@@ -157,7 +158,95 @@ __device__ __forceinline__ uint4 pack_bits(const uint16_t (&h)[8]) {
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
-// MODE != kNoAppend: first append one token per sequence at pos0[b] (the
+// The bounds of one 16-block tile for R = NT * G query rows on the matrix
+// cores, by one wavefront.  UB = q+ . kmax + q- . kmin with q+ = max(q, 0),
+// q- = min(q, 0), channel by channel the vector path's product (the bound of
+// a channel with q == 0 is 0 either way, the bounds here being finite): A =
+// the blocks' kmin / kmax rows (f16, exact), B = q+ and q- of the query rows
+// as f16 high + low parts, each row first scaled by a power of two that puts
+// its largest |q| in [2^13, 2^14) (exact; undone on the result), so the low
+// parts keep their precision.  Lane (lg, lc): A = block lc, B = query row
+// lc, channels 32 kk + 8 lg .. + 7; result = blocks 4 lg + r, query row lc,
+// then the max over each token's G rows (lanes of one 16-lane row).
+template <int D, int G, int NT, bool PH>
+__device__ __forceinline__ void score_mfma(const float* qs, const uint16_t (*sb)[kBlocksPerWG][D],
+                                           float* __restrict__ score, int32_t b, int32_t g,
+                                           int32_t Hkv, int32_t tile, int32_t nb,
+                                           int32_t max_blocks) {
+  static_assert(D == 128, "four 32-channel MFMA steps");
+  constexpr int R = NT * G;
+  const int lane = threadIdx.x % kWave, lg = lane / 16, lc = lane % 16;
+  const bool cv = lc < R;
+  const float* qrow = qs + (cv ? lc : 0) * D;
+  float qv[4][8];
+  float mq = 0.0f;
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    const float4 a = *reinterpret_cast<const float4*>(qrow + 32 * kk + 8 * lg);
+    const float4 c4 = *reinterpret_cast<const float4*>(qrow + 32 * kk + 8 * lg + 4);
+    const float x[8] = {a.x, a.y, a.z, a.w, c4.x, c4.y, c4.z, c4.w};
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      qv[kk][s] = cv ? x[s] : 0.0f;
+      mq = fmaxf(mq, fabsf(qv[kk][s]));
+    }
+  }
+  mq = rows_max(mq);                        // the row's 128 channels (4 lane groups)
+  const int qe = mq > 0.0f ? 14 - __builtin_amdgcn_frexp_expf(mq) : 0;
+  float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    half8_t ph, pl, nh, nl;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const float x = ldexpf(qv[kk][s], qe);
+      const float xp = fmaxf(x, 0.0f), xn = fminf(x, 0.0f);
+      const _Float16 hp = (_Float16)xp, hn = (_Float16)xn;
+      ph[s] = hp;
+      pl[s] = (_Float16)(xp - (float)hp);
+      nh[s] = hn;
+      nl[s] = (_Float16)(xn - (float)hn);
+    }
+    const int chunk = 4 * kk + lg;
+    const half8_t amin = *reinterpret_cast<const half8_t*>(&sb[0][lc][8 * (chunk ^ lc)]);
+    const half8_t amax = *reinterpret_cast<const half8_t*>(&sb[1][lc][8 * (chunk ^ lc)]);
+    acc = mfma_f16_32(amax, ph, acc);
+    acc = mfma_f16_32(amax, pl, acc);
+    acc = mfma_f16_32(amin, nh, acc);
+    acc = mfma_f16_32(amin, nl, acc);
+  }
+  float v[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) v[r] = ldexpf(acc[r], -qe);
+  if constexpr (PH) {
+    // per query head (NT == 1): every row's own bound
+    if (cv) {
+      const int64_t srow = (int64_t(b) * Hkv + g) * G + lc;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int32_t j = tile * kBlocksPerWG + 4 * lg + r;
+        if (j < nb) score[srow * max_blocks + j] = v[r];
+      }
+    }
+    return;
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+#pragma unroll
+    for (int o = 1; o < G; o <<= 1) v[r] = fmaxf(v[r], __shfl_xor(v[r], o));
+  }
+  if (cv && lc % G == 0) {
+    const int t = lc / G;
+    const int64_t srow = NT == 1 ? int64_t(b) * Hkv + g : (int64_t(b) * Hkv + g) * NT + t;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int32_t j = tile * kBlocksPerWG + 4 * lg + r;
+      if (j < nb) score[srow * max_blocks + j] = v[r];
+    }
+  }
+}
+
+// MODE != kNoAppend: first append one token per sequence at pos0[b] (the// MODE != kNoAppend: first append one token per sequence at pos0[b] (the
 // first workgroup of each (sequence, KV head) writes it) and score its block
 // with the merged bounds.  The merge is computed from the new key in
 // registers, so it does not matter whether this workgroup reads the side
@@ -275,6 +364,13 @@ bounds_kernel(uint16_t* __restrict__ kmin, uint16_t* __restrict__ kmax,
   const int32_t nb = (L + block - 1) / block;
   const bool live = j < nb;
   float best = -INFINITY;
+  // With 8 or more query rows per block the scoring runs on the matrix
+  // cores (score_mfma; the per-head bounds too, so the group score stays the
+  // max of the per-head values bit for bit); a workgroup whose live bounds
+  // hold an infinity (an int8 cache with keys past the f16 range, or an
+  // all-NaN channel) keeps the vector path, whose q == 0 rule the MFMA form
+  // would turn into NaN.
+  constexpr bool kMfma = NT * G >= 8;
   if (tile * kBlocksPerWG < nb) {          // else the whole tile is past the end
     __shared__ __attribute__((aligned(16))) float qs[NT * G * D];
 #pragma unroll
@@ -282,7 +378,25 @@ bounds_kernel(uint16_t* __restrict__ kmin, uint16_t* __restrict__ kmax,
       const int e = int(threadIdx.x) + kBoundsThreads * i;
       if (e < kQ4) reinterpret_cast<float4*>(qs)[e] = qreg[i];
     }
-    __syncthreads();
+    if constexpr (kMfma) {
+      // the tile's bounds, 16-byte chunks XOR-swizzled by block (the MFMA
+      // reads 16 blocks at one chunk)
+      __shared__ __attribute__((aligned(16))) uint16_t sb[2][kBlocksPerWG][D];
+      const int jj = int(threadIdx.x) / kLanesPerBlock;
+      *reinterpret_cast<uint4*>(&sb[0][jj][8 * (c ^ jj)]) = pack_bits(lb);
+      *reinterpret_cast<uint4*>(&sb[1][jj][8 * (c ^ jj)]) = pack_bits(hb);
+      bool inf = false;
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        inf |= (lb[e] & 0x7FFFu) == 0x7C00u || (hb[e] & 0x7FFFu) == 0x7C00u;
+      if (!__syncthreads_or(live && inf)) {
+        if (threadIdx.x < kWave)
+          score_mfma<D, G, NT, PH>(qs, sb, score, b, g, Hkv, tile, nb, max_blocks);
+        goto scored;
+      }
+    } else {
+      __syncthreads();
+    }
     float mn[8], mx[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) { mn[e] = h2f(lb[e]); mx[e] = h2f(hb[e]); }
@@ -320,6 +434,7 @@ bounds_kernel(uint16_t* __restrict__ kmin, uint16_t* __restrict__ kmax,
     }
     if (NT == 1 && !PH && live && c == 0) score[(int64_t(b) * Hkv + g) * max_blocks + j] = best;
   }
+scored:
   // the append's stores
   if constexpr (MODE != kNoAppend) {
     if (own) {
