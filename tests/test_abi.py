@@ -178,6 +178,9 @@ def test_default_split_rule():
     assert ds(1, 8, 255, kv_dtype="i8") == 32               # 64 parts would hold < 4 blocks
     assert ds(1, 8, 256, kv_dtype="i8") == 64
     assert ds(1, 4, 517, kv_dtype="i8", sparse=True) == 64  # Quest: one workgroup per CU
+    assert ds(1, 8, 512, kv_dtype="q4_0") == 64             # 32K q4_0 dense: two per CU
+    assert ds(1, 8, 512, kv_dtype="q8_0") == 32             # q8_0 keeps one
+    assert ds(1, 8, 131, kv_dtype="q4_0", sparse=True) == 32
     assert ds(1, 8, 131, sparse=True) == 32
     assert ds(1, 1, 10 ** 6) == 256 and ds(1, 1, 10 ** 9, target_wgs=10 ** 6) == 4096
     assert ds(4096, 16, 1000) == 1
