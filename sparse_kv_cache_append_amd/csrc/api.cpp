@@ -247,7 +247,7 @@ skv_status skv_decode_step(const skv_cache* c, const int32_t* pos0, const void* 
     p.sel_idx = sel_idx;
     p.sel_cnt = sel_cnt;
     const int32_t ups = (max_sel + n_split - 1) / n_split;
-    if (!grouped && max_blocks <= skv::kFusedSelMaxCand && ups <= 64) {
+    if (max_blocks <= skv::kFusedSelMaxCand && ups <= 64) {
       p.fused_r = skv::fused_sel_chunks(std::max(max_blocks - n_sink, 1));
       p.fsel = skv::FusedSelect{score, max_blocks, k_sel, n_sink, n_recent, sel_idx, sel_cnt};
     } else {
@@ -300,7 +300,7 @@ skv_status skv_decode_attn_select(const skv_cache* c, const float* q, int32_t n_
   p.ws = static_cast<float*>(workspace);
   p.dbg_logits = nullptr;
   const int32_t ups = (max_sel + n_split - 1) / n_split;
-  if (!skv::is_grouped(c->kv_dtype) && max_blocks <= skv::kFusedSelMaxCand && ups <= 64) {
+  if (max_blocks <= skv::kFusedSelMaxCand && ups <= 64) {
     p.fused_r = skv::fused_sel_chunks(std::max(max_blocks - n_sink, 1));
     p.fsel = skv::FusedSelect{score, max_blocks, k_sel, n_sink, n_recent, sel_idx, sel_cnt};
   } else {

@@ -36,6 +36,7 @@
 
 #include "decode_core.h"
 #include "device_common.h"
+#include "fused_walk.h"
 #include "launch.h"
 
 namespace skv {
@@ -148,7 +149,9 @@ __device__ __forceinline__ void unpack_q4(const int4_t& w, int4_t& c0, int4_t& c
 
 constexpr int kPwShiftGrp = 7;
 
-template <int G, bool Q4>
+// SELR > 0: the block selection runs in the prologue (fused_walk), as in the
+// f16 and int8 attention kernels.
+template <int G, bool Q4, int SELR = 0>
 __global__ void __launch_bounds__(kMThreads, 2)
 decode_grp_mfma(const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
                 const uint16_t* __restrict__ ksc, const uint16_t* __restrict__ vsc,
@@ -156,7 +159,8 @@ decode_grp_mfma(const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
                 const int32_t* __restrict__ sel_idx, const int32_t* __restrict__ sel_cnt,
                 int32_t max_sel, int32_t Hkv, int32_t max_seq, int32_t block, int32_t max_len,
                 int32_t n_split, int32_t n_rows, int32_t units_per_split, float qscale2,
-                float* __restrict__ ws_m, float* __restrict__ ws_l, float* __restrict__ ws_o) {
+                float* __restrict__ ws_m, float* __restrict__ ws_l, float* __restrict__ ws_o,
+                FusedSelect fs) {
   using F = GrpFmt<Q4>;
   constexpr int T = 32;
   constexpr int kCodeBytes = T * kRowBytesI8;               // 4096 (int8 codes in LDS)
@@ -175,7 +179,9 @@ decode_grp_mfma(const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
   const int32_t H = Hkv * G;
   const int64_t bg = int64_t(b) * Hkv + g;
   const int32_t L_raw = seq_len[b];
-  const ListSeed ls = list_seed(sel_idx, sel_cnt, max_sel, bg, split, units_per_split);
+  ListSeed ls{};
+  if constexpr (SELR == 0)
+    ls = list_seed(sel_idx, sel_cnt, max_sel, bg, split, units_per_split);
   // query as the B operand of the per-group q.K: column = head lc, k-chunk lg
   // of group kk = channels 32 kk + 8 lg .. + 7; f16 high + low parts
   half8_t qhi[kGroups], qlo[kGroups];
@@ -197,7 +203,11 @@ decode_grp_mfma(const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
     }
   }
   const int32_t L = __builtin_amdgcn_readfirstlane(min(max(L_raw, 0), max_len));
-  TileWalk tw = make_walk<T>(ls, sel_idx, max_sel, bg, L, block, split, units_per_split);
+  TileWalk tw;
+  if constexpr (SELR > 0)
+    tw = fused_walk<T, SELR>(fs, max_sel, bg, b, L, L_raw, block, split, units_per_split);
+  else
+    tw = make_walk<T>(ls, sel_idx, max_sel, bg, L, block, split, units_per_split);
   tw.init(wave);
   float m_run = -INFINITY, l_run = 0.0f;
   float4_t O[8];
@@ -395,8 +405,8 @@ hipError_t launch_decode_grouped(const DecodeParams& p, hipStream_t stream) {
   const int32_t B = c.batch, H = p.n_heads, S = p.n_split;
   const int G = H / c.n_kv_heads;
   if (G != 1 && G != 2 && G != 4 && G != 8) return hipErrorInvalidValue;
-  if (p.fused_r > 0 || p.app.k_new != nullptr || p.sel_hmask != nullptr ||
-      p.dbg_logits != nullptr)
+  if (p.app.k_new != nullptr || p.sel_hmask != nullptr || p.dbg_logits != nullptr ||
+      p.n_tok != 1)
     return hipErrorInvalidValue;
   float* ws_m = p.ws + ws_m_offset(B, H, S);
   float* ws_l = p.ws + ws_l_offset(B, H, S);
@@ -418,15 +428,21 @@ hipError_t launch_decode_grouped(const DecodeParams& p, hipStream_t stream) {
   const uint8_t* vc = static_cast<const uint8_t*>(c.v);
   const uint16_t* ks = reinterpret_cast<const uint16_t*>(c.k_scale);
   const uint16_t* vs = reinterpret_cast<const uint16_t*>(c.v_scale);
-#define SKV_GRP(GG, Q)                                                                          \
-  decode_grp_mfma<GG, Q><<<grid, kMThreads, 0, stream>>>(kc, vc, ks, vs, p.q, p.seq_len,       \
-                                                        p.sel_idx, p.sel_cnt, p.max_sel,        \
-                                                        c.n_kv_heads, c.max_seq, c.block,       \
-                                                        p.max_len, S, n_rows, ups, scale2,      \
-                                                        ws_m, ws_l, ws_o)
-#define SKV_GRP_G(GG)                          \
-  if (c.kv_dtype == SKV_Q4_0) SKV_GRP(GG, true); \
-  else SKV_GRP(GG, false)
+  const int fr = p.fused_r;
+#define SKV_GRP(GG, Q, SR)                                                                      \
+  decode_grp_mfma<GG, Q, SR><<<grid, kMThreads, 0, stream>>>(kc, vc, ks, vs, p.q, p.seq_len,   \
+                                                            p.sel_idx, p.sel_cnt, p.max_sel,    \
+                                                            c.n_kv_heads, c.max_seq, c.block,   \
+                                                            p.max_len, S, n_rows, ups, scale2,  \
+                                                            ws_m, ws_l, ws_o, p.fsel)
+#define SKV_GRP_Q(GG, Q)                           \
+  if (fr == 2) SKV_GRP(GG, Q, 2);                  \
+  else if (fr == 4) SKV_GRP(GG, Q, 4);             \
+  else if (fr > 0) SKV_GRP(GG, Q, kFusedSelR);     \
+  else SKV_GRP(GG, Q, 0)
+#define SKV_GRP_G(GG)                                \
+  if (c.kv_dtype == SKV_Q4_0) { SKV_GRP_Q(GG, true); } \
+  else { SKV_GRP_Q(GG, false); }
   switch (G) {
     case 1: SKV_GRP_G(1); break;
     case 2: SKV_GRP_G(2); break;
@@ -434,6 +450,7 @@ hipError_t launch_decode_grouped(const DecodeParams& p, hipStream_t stream) {
     default: SKV_GRP_G(8); break;
   }
 #undef SKV_GRP_G
+#undef SKV_GRP_Q
 #undef SKV_GRP
   return hipGetLastError();
 }

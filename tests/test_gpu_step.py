@@ -513,7 +513,8 @@ def test_decode_step_tie_classes(gpu_lib, k_sel):
     _oracle_check(w, out.cpu().numpy(), (s_h, c_h))
 
 
-@pytest.mark.parametrize("kv_dtype,L,S", [("f16", 32768, 32), ("i8", 20000, 24), ("f16", 3000, 1)])
+@pytest.mark.parametrize("kv_dtype,L,S", [("f16", 32768, 32), ("i8", 20000, 24), ("f16", 3000, 1),
+                                          ("q8_0", 9000, 16), ("q4_0", 32768, 32)])
 def test_decode_attn_select_equals_select_then_decode(gpu_lib, kv_dtype, L, S):
     """skv_decode_attn_select (selection folded into the attention prologue;
     with S = 1 a part spans more than 64 entries and the selection runs as
