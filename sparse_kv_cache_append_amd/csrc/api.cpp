@@ -233,13 +233,14 @@ skv_status skv_decode_step(const skv_cache* c, const int32_t* pos0, const void* 
   p.dbg_logits = nullptr;
   hipError_t e = hipSuccess;
   const bool grouped = skv::is_grouped(c->kv_dtype);
-  if (grouped && k_new != nullptr) {
-    // group-wise caches: the append runs as its own kernel
+  if (grouped && k_new != nullptr && !quest) {
+    // dense steps over group-wise caches: the append runs as its own kernel
+    // (the Quest step folds it into the bounds pass, as for every cache)
     e = skv::launch_append_grouped(*c, pos0, 1, k_new, v_new, stream);
     if (e != hipSuccess) return SKV_EDEVICE;
   }
   if (quest) {
-    e = k_new != nullptr && !grouped
+    e = k_new != nullptr
             ? skv::launch_append_bounds(*c, pos0, k_new, v_new, q, n_heads, seq_len, max_len,
                                         score, stream)
             : skv::launch_bounds(*c, q, n_heads, seq_len, max_len, score, stream);

@@ -25,7 +25,29 @@ constexpr int kBoundsThreads = 256;
 constexpr int kLanesPerBlock = 16;
 constexpr int kBlocksPerWG = kBoundsThreads / kLanesPerBlock;  // 16
 
-enum AppendMode { kNoAppend = 0, kAppendF16 = 1, kAppendI8 = 2 };
+enum AppendMode { kNoAppend = 0, kAppendF16 = 1, kAppendI8 = 2, kAppendQ8 = 3, kAppendQ4 = 4 };
+
+// Group-wise caches (q8_0 / q4_0): 32-channel groups with an f16 scale each,
+// the append kernel's arithmetic (decode_grouped.hip): s = f16(absmax / QMAX),
+// code = clamp(rint(x / s), -QMAX, QMAX) against the stored scale (0 when s is
+// 0 or not finite); q4_0 stores code + 8, channels 2i / 2i + 1 in the low /
+// high nibble of byte i.
+constexpr int kGrpChannels = 32;
+template <int MODE>
+struct GrpMode {
+  static constexpr bool kQ4 = MODE == kAppendQ4;
+  static constexpr int kQmax = kQ4 ? 7 : 127;
+  static constexpr int kRowBytes = kQ4 ? 64 : 128;
+};
+__device__ __forceinline__ uint16_t grp_scale_bits_b(float a, int qmax) {
+  return __half_as_ushort(__float2half_rn(a / float(qmax)));
+}
+__device__ __forceinline__ int grp_code_b(float x, float s, int qmax) {
+  if (!(s > 0.0f && s < INFINITY)) return 0;
+  float r = rintf(x / s);
+  r = fminf(fmaxf(r, -float(qmax)), float(qmax));
+  return int(r);
+}
 
 // Write the new token of (sequence b, KV head g) at position p0 -- the
 // one-token case of skv_kv_append, same arithmetic -- and its block's bounds.
@@ -49,6 +71,39 @@ __device__ __forceinline__ void append_one(const AppendOne& ap, uint16_t* __rest
       const uint16_t x = kn[d];
       const bool nan = (x & 0x7FFFu) > 0x7C00u;      // skipped, as by the append kernel
       uint16_t bmn = nan ? uint16_t(0x7C00u) : x, bmx = nan ? uint16_t(0xFC00u) : x;
+      if (!fresh) {
+        bmn = f16_min_bits(kmin[bo + d], bmn);
+        bmx = f16_max_bits(kmax[bo + d], bmx);
+      }
+      kmin[bo + d] = bmn;
+      kmax[bo + d] = bmx;
+    }
+  } else if constexpr (MODE == kAppendQ8 || MODE == kAppendQ4) {
+    // one wavefront per row (K, V): lane l holds channels 2l, 2l + 1, a
+    // group is one 16-lane row (the append kernel's layout and order)
+    using F = GrpMode<MODE>;
+    const int lane = tid % kWave, wave = tid / kWave;
+    if (wave < 2) {
+      const float2 x =
+          reinterpret_cast<const float2*>(static_cast<const float*>(wave == 0 ? ap.k_new : ap.v_new) +
+                                          bg * D)[lane];
+      const float a = group16_max(fmaxf(fmaxf(0.0f, fabsf(x.x)), fabsf(x.y)));
+      const uint16_t sb = grp_scale_bits_b(a, F::kQmax);
+      const float sc = h2f(sb);
+      const int c0 = grp_code_b(x.x, sc, F::kQmax), c1 = grp_code_b(x.y, sc, F::kQmax);
+      uint8_t* dst = static_cast<uint8_t*>(wave == 0 ? ap.k : ap.v) + row * F::kRowBytes;
+      if constexpr (F::kQ4) {
+        dst[lane] = uint8_t((c0 + 8) | ((c1 + 8) << 4));
+      } else {
+        reinterpret_cast<uint16_t*>(dst)[lane] = uint16_t((c0 & 0xFF) | ((c1 & 0xFF) << 8));
+      }
+      if (lane % 16 == 0)
+        reinterpret_cast<uint16_t*>(wave == 0 ? ap.ks : ap.vs)[row * (D / kGrpChannels) + lane / 16] = sb;
+    }
+    const float* kn = static_cast<const float*>(ap.k_new) + bg * D;
+    for (int d = tid; d < D; d += kBoundsThreads) {
+      const float x = kn[d];
+      uint16_t bmn = f32_to_f16_down(fminf(INFINITY, x)), bmx = f32_to_f16_up(fmaxf(-INFINITY, x));
       if (!fresh) {
         bmn = f16_min_bits(kmin[bo + d], bmn);
         bmx = f16_max_bits(kmax[bo + d], bmx);
@@ -149,6 +204,45 @@ __device__ __forceinline__ int8_t quant_slot_i8(const float (&kf)[8], const floa
 #pragma unroll
   for (int i = 0; i < 8; ++i) x = e == i ? (is_v ? vf[i] : kf[i]) : x;
   return int8_t(quant_code(x, is_v ? vs : ks));
+}
+
+// Group-wise codes of the new row in the row's first workgroup: slot 0 (the
+// first 16 lanes) quantizes K, slot 1 V, lane c its channels 8c .. 8c + 7; a
+// group is 4 lanes (xor-shuffles 1, 2 give its absmax).  Returns the lane's
+// codes packed as stored (q8_0: 8 bytes, q4_0: 4 bytes) and its group's
+// scale bits.
+template <int MODE>
+__device__ __forceinline__ uint2 quant_slot_grp(const float (&kf)[8], const float (&vf)[8],
+                                                uint16_t& sbits) {
+  using F = GrpMode<MODE>;
+  const bool is_v = int(threadIdx.x) / kLanesPerBlock == 1;
+  float x[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] = is_v ? vf[e] : kf[e];
+  // the append kernel's absmax: fmaxf over 0 and |x|, so a NaN value is left out
+  float a = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 8; e += 2) a = fmaxf(fmaxf(a, fabsf(x[e])), fabsf(x[e + 1]));
+  a = fmaxf(a, __shfl_xor(a, 1));
+  a = fmaxf(a, __shfl_xor(a, 2));
+  sbits = grp_scale_bits_b(a, F::kQmax);
+  const float sc = h2f(sbits);
+  int c[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) c[e] = grp_code_b(x[e], sc, F::kQmax);
+  uint2 out = make_uint2(0u, 0u);
+  if constexpr (F::kQ4) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      out.x |= uint32_t((c[2 * i] + 8) | ((c[2 * i + 1] + 8) << 4)) << (8 * i);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      out.x |= uint32_t(c[i] & 0xFF) << (8 * i);
+      out.y |= uint32_t(c[4 + i] & 0xFF) << (8 * i);
+    }
+  }
+  return out;
 }
 
 __device__ __forceinline__ uint4 pack_bits(const uint16_t (&h)[8]) {
@@ -314,7 +408,7 @@ bounds_kernel(uint16_t* __restrict__ kmin, uint16_t* __restrict__ kmax,
   if constexpr (MODE == kAppendF16) {
     kx = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(ap.k_new) + src);
     vx = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(ap.v_new) + src);
-  } else if constexpr (MODE == kAppendI8) {
+  } else if constexpr (MODE != kNoAppend) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       kf[e] = static_cast<const float*>(ap.k_new)[src + e];
@@ -339,6 +433,8 @@ bounds_kernel(uint16_t* __restrict__ kmin, uint16_t* __restrict__ kmax,
   int64_t arow = 0, bo = 0;
   int8_t code = 0;
   float ks_new = 0.0f, vs_new = 0.0f;
+  uint2 gcodes = make_uint2(0u, 0u);
+  uint16_t gscale = 0;
   if constexpr (MODE != kNoAppend) {
     if (p0 >= 0 && p0 < ap.max_seq) {
       const int32_t jn = p0 / block;
@@ -353,6 +449,9 @@ bounds_kernel(uint16_t* __restrict__ kmin, uint16_t* __restrict__ kmax,
         if constexpr (MODE == kAppendI8) {
           own_wg = tile == 0;
           if (own_wg) code = quant_slot_i8(kf, vf, ks_new, vs_new);
+        } else if constexpr (MODE == kAppendQ8 || MODE == kAppendQ4) {
+          own_wg = tile == 0 && int(threadIdx.x) < 2 * kLanesPerBlock;
+          if (own_wg) gcodes = quant_slot_grp<MODE>(kf, vf, gscale);
         }
       } else if (tile == 0) {
         // the token's block lies past the launched tiles: append it here
@@ -452,6 +551,17 @@ scored:
         if (threadIdx.x == 0) ap.ks[arow] = ks_new;
         if (threadIdx.x == 8 * kLanesPerBlock) ap.vs[arow] = vs_new;
       }
+    } else if constexpr (MODE == kAppendQ8 || MODE == kAppendQ4) {
+      if (own_wg) {
+        using F = GrpMode<MODE>;
+        const bool is_v = int(threadIdx.x) / kLanesPerBlock == 1;
+        uint8_t* dst = static_cast<uint8_t*>(is_v ? ap.v : ap.k) + arow * F::kRowBytes;
+        if constexpr (F::kQ4) reinterpret_cast<uint32_t*>(dst)[c] = gcodes.x;
+        else reinterpret_cast<uint2*>(dst)[c] = gcodes;
+        if (c % 4 == 0)
+          reinterpret_cast<uint16_t*>(is_v ? ap.vs : ap.ks)[arow * (D / kGrpChannels) + c / 4] =
+              gscale;
+      }
     }
   }
 }
@@ -530,9 +640,18 @@ hipError_t launch_append_bounds(const skv_cache& c, const int32_t* pos0, const v
                                 const int32_t* seq_len, int32_t max_len, float* score,
                                 hipStream_t stream) {
   AppendOne ap{c.k, c.v, c.k_scale, c.v_scale, k_new, v_new, pos0, c.max_seq};
-  if (c.kv_dtype == SKV_F16)
-    return launch_bounds_m<kAppendF16>(c, q, n_heads, seq_len, max_len, score, ap, stream);
-  return launch_bounds_m<kAppendI8>(c, q, n_heads, seq_len, max_len, score, ap, stream);
+  switch (c.kv_dtype) {
+    case SKV_F16:
+      return launch_bounds_m<kAppendF16>(c, q, n_heads, seq_len, max_len, score, ap, stream);
+    case SKV_I8:
+      return launch_bounds_m<kAppendI8>(c, q, n_heads, seq_len, max_len, score, ap, stream);
+    case SKV_Q8_0:
+      return launch_bounds_m<kAppendQ8>(c, q, n_heads, seq_len, max_len, score, ap, stream);
+    case SKV_Q4_0:
+      return launch_bounds_m<kAppendQ4>(c, q, n_heads, seq_len, max_len, score, ap, stream);
+    default:
+      return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace skv

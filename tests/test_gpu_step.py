@@ -237,6 +237,21 @@ STEP_CASES = [
     ("quest-q4_0 G8", lambda: workloads.clustered(
         [543], 32, 4, 128, [5001], "q4_0", n_dirs=16, k_sel=[20], n_sink=1, n_recent=4),
         True, True, {}),
+    # the group-wise append folded into the Quest step's bounds pass: a NaN
+    # channel, poisoned rows, and a token past the launched tiles (the row's
+    # first workgroup then appends it whole)
+    ("quest-q8_0 NaN channel in the new key", lambda: _with_nan_key(workloads.clustered(
+        [552, 553], 32, 8, 128, [3001, 4100], "q8_0", n_dirs=16, k_sel=[10, 12], n_sink=1,
+        n_recent=2)), True, True, {"lag": 1}),
+    ("quest-q4_0 poisoned rows", lambda: workloads.clustered(
+        [554], 16, 8, 128, [2049], "q4_0", n_dirs=16, k_sel=[9], n_sink=1, n_recent=2),
+        True, True, {"poison": True}),
+    ("quest-q4_0 token past the launched tiles", lambda: workloads.clustered(
+        [555], 32, 4, 128, [64 * 16 + 1], "q4_0", n_dirs=16, k_sel=[5], n_sink=1, n_recent=2),
+        True, True, {"lag": 1, "tight": True}),
+    ("quest-q8_0 first token of an empty cache", lambda: workloads.clustered(
+        [556], 32, 8, 128, [1], "q8_0", n_dirs=4, k_sel=[1], n_sink=1, n_recent=1),
+        True, True, {"lag": 1, "tight": True}),
     ("dense-q8_0 append poisoned rows", lambda: workloads.gaussian(
         544, 2, 32, 8, 128, [65, 2000], "q8_0"), False, True, {"poison": True}),
     ("dense-q4_0 append 5 parts G2", lambda: workloads.gaussian(
