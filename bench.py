@@ -717,7 +717,7 @@ def measure_scan4(T, skv, torch, w, caches, R, q, seq_len, Lmax, delta):
     zero = torch.zeros(B, dtype=torch.int32, device=dev)
     for c, ix in zip(caches, idx):
         skv.scan4_build(c, ix, zero, seq_len, Lmax)
-    S = skv.default_split(B, Hkv, -(-Lmax // blk))
+    S = skv.scan4_default_split(B, Hkv, -(-Lmax // blk))
     ws = torch.empty(skv.scan4_workspace_bytes(B, H, S, Lmax), dtype=torch.uint8, device=dev)
     cand = torch.empty((B, H, -(-Lmax // 32)), dtype=torch.int32, device=dev)
     cnt = torch.empty((B, H), dtype=torch.int32, device=dev)

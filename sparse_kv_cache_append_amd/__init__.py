@@ -27,7 +27,7 @@ __all__ = ["load", "Cache", "SkvError", "kv_append", "block_bounds", "select_top
            "decode_attn", "decode_attn_select", "decode_attn_sparse_v", "sparse_v_workspace_bytes",
            "block_bounds_heads", "select_union", "decode_attn_heads", "block_bounds_multi",
            "select_topk_multi", "select_union_tokens", "decode_attn_multi", "Scan4Index",
-           "scan4_build", "scan4_candidates", "scan4_workspace_bytes",
+           "scan4_build", "scan4_candidates", "scan4_workspace_bytes", "scan4_default_split",
            "decode_step", "decode_step_static", "combine", "workspace_bytes", "status_str", "decode",
            "SKV_F16", "SKV_F32", "SKV_I8", "SKV_Q8_0", "SKV_Q4_0", "LIB_PATH", "EXPORTS"]
 
@@ -667,6 +667,17 @@ def default_split(batch: int, n_kv_heads: int, n_units: int, target_wgs: Optiona
             target_wgs = 512
     n = max(1, math.ceil(target_wgs / max(1, batch * n_kv_heads)))
     return int(max(1, min(n, n_units, 4096)))
+
+
+def scan4_default_split(batch: int, n_kv_heads: int, n_blocks: int) -> int:
+    """Parts per (sequence, KV head) for scan4_candidates: two workgroups per
+    compute unit while every part keeps at least 4 blocks.  A scan tile
+    carries the bound arithmetic of all G heads of its KV head, so a second
+    workgroup per compute unit hides the first one's loads (32K context, 8
+    KV heads, warm cache: 16.0 us at 64 parts against 17.6 us at 32)."""
+    two = math.ceil(512 / max(1, batch * n_kv_heads))
+    target = 512 if n_blocks >= 4 * two else 256
+    return default_split(batch, n_kv_heads, n_blocks, target_wgs=target)
 
 
 def decode(cache: Cache, q, seq_len, max_len: int, softmax_scale: Optional[float] = None,

@@ -114,13 +114,23 @@ scan4_build(const uint16_t* __restrict__ kc, const int32_t* __restrict__ pos0,
 }
 
 // ------------------------------------------------------------ pass 1: bounds
-// 8 nibbles (4 bytes: channels 2i, 2i + 1 per byte) to 8 byte codes 0..15 in
-// channel order.
-__device__ __forceinline__ int2_t nibbles_to_bytes(uint32_t x) {
-  const uint32_t lo = x & 0x0F0F0F0Fu, hi = (x >> 4) & 0x0F0F0F0Fu;
-  return int2_t{int(__builtin_amdgcn_perm(hi, lo, 0x05010400u)),
-                int(__builtin_amdgcn_perm(hi, lo, 0x07030602u))};
+// 8 nibbles (4 bytes: channels 2i, 2i + 1 per byte) to 8 exact f16 codes
+// 0..15 in the order c0 c2 c4 c6 c1 c3 c5 c7: v_perm_b32 puts each nibble
+// under a 0x64 high byte (f16 1024 + c), one packed subtraction per pair
+// removes the 1024.  kNibPos maps channel s of the 8 to its position.
+__device__ __forceinline__ half8_t nibbles_to_half8(uint32_t x) {
+  typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+  const uint32_t ev = x & 0x0F0F0F0Fu, od = (x >> 4) & 0x0F0F0F0Fu;
+  constexpr uint32_t kSel01 = 0x04010400u;   // (0x64, x1, 0x64, x0)
+  constexpr uint32_t kSel23 = 0x04030402u;   // (0x64, x3, 0x64, x2)
+  const half2_t off = half2_t{(_Float16)1024.0f, (_Float16)1024.0f};
+  const half2_t p0 = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0x64646464u, ev, kSel01)) - off;
+  const half2_t p1 = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0x64646464u, ev, kSel23)) - off;
+  const half2_t p2 = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0x64646464u, od, kSel01)) - off;
+  const half2_t p3 = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0x64646464u, od, kSel23)) - off;
+  return half8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
+__device__ __forceinline__ constexpr int nib_pos(int s) { return (s & 1) ? 4 + (s >> 1) : (s >> 1); }
 
 // T-token tiles (T = 64 when the block is a multiple of 64, else 32), two in
 // flight per wavefront.  The codes go straight from memory into the MFMA
@@ -141,6 +151,11 @@ scan4_bounds(const uint8_t* __restrict__ codes4, const float* __restrict__ lo_in
              float* __restrict__ lbmax, int32_t* __restrict__ cand_cnt) {
   constexpr int kSubs = T / 16;                              // 16-token MFMA row blocks
   __shared__ __attribute__((aligned(16))) float sprm[kMWaves][2][3][kD];   // lo, step, err
+  // the B operands of the tile's block (f16 high, low) for MFMA lane
+  // (lg, lc < G) at entry lg G + lc, and the per-head scalars, written and
+  // read by one wavefront
+  __shared__ __attribute__((aligned(16))) uint32_t sbw[kMWaves][2][4][4 * G][4];
+  __shared__ float shd[kMWaves][3][16];
   __shared__ float red[kMWaves][16];
   const uint32_t slot = xcd_slot(blockIdx.x, gridDim.x);
   const int32_t split = int32_t(slot % uint32_t(n_split));
@@ -154,17 +169,21 @@ scan4_bounds(const uint8_t* __restrict__ codes4, const float* __restrict__ lo_in
   const bool hv = lc < G;
   if (split == 0 && threadIdx.x < G) cand_cnt[int64_t(b) * H + g * G + threadIdx.x] = 0;
   const int32_t L_raw = seq_len[b];
-  // this lane's query channels 32 lg + 8 kk + s (head lc)
-  float qv[4][8];
+  // The per-block operands are computed spread over the wavefront: lane l
+  // takes head ph = l / LPH of the group and channels pc .. pc + CPL - 1
+  // (LPH = 64 / G lanes per head, CPL = 2 G channels each), instead of every
+  // lane computing its own 32 channels for its MFMA column (of which only G
+  // of 16 are heads).
+  constexpr int LPH = kWave / G, CPL = kD / LPH;
+  const int ph = lane / LPH, pc = (lane % LPH) * CPL;
+  float qd[CPL];
   {
-    const float* qp = q + (int64_t(b) * H + g * G + (hv ? lc : 0)) * kD;
+    const float* qp = q + (int64_t(b) * H + g * G + ph) * kD + pc;
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const float4 a = *reinterpret_cast<const float4*>(qp + 32 * lg + 8 * kk);
-      const float4 c = *reinterpret_cast<const float4*>(qp + 32 * lg + 8 * kk + 4);
-      const float x[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
-#pragma unroll
-      for (int s = 0; s < 8; ++s) qv[kk][s] = hv ? x[s] : 0.0f;
+    for (int e = 0; e < CPL; e += 2) {
+      const float2 v2 = *reinterpret_cast<const float2*>(qp + e);
+      qd[e] = v2.x;
+      qd[e + 1] = v2.y;
     }
   }
   const int32_t L = __builtin_amdgcn_readfirstlane(min(max(L_raw, 0), max_len));
@@ -221,60 +240,108 @@ scan4_bounds(const uint8_t* __restrict__ codes4, const float* __restrict__ lo_in
     // power of two per head so that its largest value lies in [2^13, 2^14)
     // (the f16 low parts stay normal; the MFMA result is scaled back
     // exactly); a_h = sum q lo, r_h = sum |q| err
-    half8_t whi[4], wlo[4];
     float pa = 0.0f, pr = 0.0f, mw = 0.0f;
-    float wv[4][8];
+    float wv[CPL];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const int ch = 32 * lg + 8 * kk;
-      const float4 s0 = *reinterpret_cast<const float4*>(&pm[1][ch]);
-      const float4 s1 = *reinterpret_cast<const float4*>(&pm[1][ch + 4]);
-      const float4 l0 = *reinterpret_cast<const float4*>(&pm[0][ch]);
-      const float4 l1 = *reinterpret_cast<const float4*>(&pm[0][ch + 4]);
-      const float4 e0 = *reinterpret_cast<const float4*>(&pm[2][ch]);
-      const float4 e1 = *reinterpret_cast<const float4*>(&pm[2][ch + 4]);
-      const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
-      const float lv[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
-      const float ev[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
+    for (int e = 0; e < CPL; e += 2) {
+      const float2 s2 = *reinterpret_cast<const float2*>(&pm[1][pc + e]);
+      const float2 l2 = *reinterpret_cast<const float2*>(&pm[0][pc + e]);
+      const float2 e2 = *reinterpret_cast<const float2*>(&pm[2][pc + e]);
+      const float sv[2] = {s2.x, s2.y}, lv[2] = {l2.x, l2.y}, ev[2] = {e2.x, e2.y};
 #pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        wv[kk][s] = qv[kk][s] * sv[s];
-        mw = fmaxf(mw, fabsf(wv[kk][s]));
-        pa += qv[kk][s] * lv[s];
-        pr += fabsf(qv[kk][s]) * ev[s];
+      for (int i = 0; i < 2; ++i) {
+        wv[e + i] = qd[e + i] * sv[i];
+        mw = fmaxf(mw, fabsf(wv[e + i]));
+        pa += qd[e + i] * lv[i];
+        pr += fabsf(qd[e + i]) * ev[i];
       }
     }
-    mw = rows_max(mw);
-    const int w_exp = mw > 0.0f ? 14 - __builtin_amdgcn_frexp_expf(mw) : 0;
+    // the head's LPH lanes
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
+    for (int o = 1; o < LPH; o <<= 1) {
+      mw = fmaxf(mw, __shfl_xor(mw, o));
+      pa += __shfl_xor(pa, o);
+      pr += __shfl_xor(pr, o);
+    }
+    {
+      const int we = mw > 0.0f ? 14 - __builtin_amdgcn_frexp_expf(mw) : 0;
+      // channel c lies in MFMA step (c / 8) % 4 at lane entry G (c / 32) +
+      // head, position nib_pos(c % 8) of the 8 f16 (the A side's order):
+      // channels c, c + 2 (c % 4 < 2) share one 32-bit word
+      auto split = [&](float x, uint16_t& h, uint16_t& l) {
+        const float w = ldexpf(x, we);
+        const _Float16 hh = (_Float16)w;
+        h = __builtin_bit_cast(uint16_t, hh);
+        l = __builtin_bit_cast(uint16_t, (_Float16)(w - (float)hh));
+      };
+      if constexpr (CPL >= 4) {
 #pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const float w = ldexpf(wv[kk][s], w_exp);
-        const _Float16 h = (_Float16)w;
-        whi[kk][s] = h;
-        wlo[kk][s] = (_Float16)(w - (float)h);
+        for (int e = 0; e < CPL; ++e) {
+          if ((e & 3) >= 2) continue;
+          const int c = pc + e;
+          uint16_t h0, l0, h1, l1;
+          split(wv[e], h0, l0);
+          split(wv[e + 2], h1, l1);
+          const int kk = (c >> 3) & 3, col = G * (c >> 5) + ph, wd = nib_pos(c & 7) >> 1;
+          sbw[wave][0][kk][col][wd] = uint32_t(h0) | (uint32_t(h1) << 16);
+          sbw[wave][1][kk][col][wd] = uint32_t(l0) | (uint32_t(l1) << 16);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) {
+          const int c = pc + e;
+          uint16_t h0, l0;
+          split(wv[e], h0, l0);
+          const int kk = (c >> 3) & 3, col = G * (c >> 5) + ph, pos = nib_pos(c & 7);
+          reinterpret_cast<uint16_t*>(&sbw[wave][0][kk][col][0])[pos] = h0;
+          reinterpret_cast<uint16_t*>(&sbw[wave][1][kk][col][0])[pos] = l0;
+        }
+      }
+      if (lane % LPH == 0) {
+        shd[wave][0][ph] = pa;
+        shd[wave][1][ph] = pr;
+        shd[wave][2][ph] = __int_as_float(we);
       }
     }
-    const float a_h = rows_sum(pa);
-    const float r_h = rows_sum(pr);
+    // the stores above precede these reads (one wavefront, in order)
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    half8_t whi[4], wlo[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      whi[kk] = hv ? *reinterpret_cast<const half8_t*>(&sbw[wave][0][kk][G * lg + (hv ? lc : 0)][0]) : half8_t{};
+      wlo[kk] = hv ? *reinterpret_cast<const half8_t*>(&sbw[wave][1][kk][G * lg + (hv ? lc : 0)][0]) : half8_t{};
+    }
+    const float a_h = hv ? shd[wave][0][lc] : 0.0f;
+    const float r_h = hv ? shd[wave][1][lc] : 0.0f;
+    const int w_exp = hv ? __float_as_int(shd[wave][2][lc]) : 0;
+    const float w_scale = ldexpf(1.0f, -w_exp);
+    const bool full = nvalid == T;         // wave-uniform
+    float st_max = -INFINITY;
 #pragma unroll
     for (int s = 0; s < kSubs; ++s) {
       float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         // token 16 s + lc, channels 32 lg + 8 kk .. + 7: 4 bytes of nibbles
-        const half8_t a = widen_codes(nibbles_to_bytes(uint32_t(cv[s][kk])));
+        const half8_t a = nibbles_to_half8(uint32_t(cv[s][kk]));
         acc = mfma_f16_32(a, whi[kk], acc);
         acc = mfma_f16_32(a, wlo[kk], acc);
       }
-      float ub[4];
+      // st = acc 2^-w_exp + a_h in one rounding (the scaling is exact); the
+      // tile's LB is its largest st less r_h (subtracting r_h is monotone)
+      float st[4], ub[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const bool ok = 16 * s + 4 * lg + r < nvalid;
-        const float st = ldexpf(acc[r], -w_exp) + a_h;
-        ub[r] = st + r_h;
-        lb_run = ok ? fmaxf(lb_run, st - r_h) : lb_run;
+        st[r] = __builtin_fmaf(acc[r], w_scale, a_h);
+        ub[r] = st[r] + r_h;
+      }
+      if (full) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) st_max = fmaxf(st_max, st[r]);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          st_max = 16 * s + 4 * lg + r < nvalid ? fmaxf(st_max, st[r]) : st_max;
       }
       if (hv) {
         const int32_t t = r0 + 16 * s + 4 * lg;
@@ -287,6 +354,7 @@ scan4_bounds(const uint8_t* __restrict__ codes4, const float* __restrict__ lo_in
         }
       }
     }
+    lb_run = fmaxf(lb_run, st_max - r_h);
   };
   Frag f0, f1;
   const int32_t n_mine = tw.count();

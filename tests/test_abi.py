@@ -184,6 +184,10 @@ def test_default_split_rule():
     assert ds(1, 8, 131, sparse=True) == 32
     assert ds(1, 1, 10 ** 6) == 256 and ds(1, 1, 10 ** 9, target_wgs=10 ** 6) == 4096
     assert ds(4096, 16, 1000) == 1
+    sc = skv.scan4_default_split
+    assert sc(1, 8, 512) == 64                              # 32K scan: two per CU
+    assert sc(1, 8, 255) == 32 and sc(1, 8, 256) == 64      # 4-block parts kept
+    assert sc(1, 8, 8) == 8 and sc(16, 8, 1024) == 4
 
 
 # ------------------------------------------------- binding argument checks

@@ -50,7 +50,7 @@ def check_index(idx, w, b):
 def run_scan(cache, idx, w, delta, S=None):
     q, seq_len = device_inputs(w)
     max_len = max(w.lens)
-    S = S or skv.default_split(w.B, w.Hkv, max(-(-max_len // w.block), 1))
+    S = S or skv.scan4_default_split(w.B, w.Hkv, max(-(-max_len // w.block), 1))
     ws = torch.empty(skv.scan4_workspace_bytes(w.B, w.H, S, max_len), dtype=torch.uint8,
                      device=DEV)
     cand = torch.full((w.B, w.H, max(-(-max_len // 32), 1)), -1, dtype=torch.int32, device=DEV)
@@ -95,7 +95,8 @@ def check_scan(w, b, index, ub_gpu, cand, cnt, delta):
 
 
 @pytest.mark.parametrize("H,Hkv,lens,block", [(32, 8, [3000, 777], 64), (8, 8, [1500], 16),
-                                              (16, 8, [4100], 128), (32, 4, [2049, 1], 64)])
+                                              (16, 8, [4100], 128), (32, 4, [2049, 1], 64),
+                                              (16, 4, [2500], 96), (8, 4, [5000, 300], 256)])
 def test_index_and_candidates(gpu_lib, H, Hkv, lens, block):
     w = workloads.clustered([950 + b for b in range(len(lens))], H, Hkv, 128, lens, "f16",
                             n_dirs=8, amp=4.0, block=block)
