@@ -550,17 +550,18 @@ def measure(w, args, quest: bool, dense: bool, detail: bool = False):
         if detail:
             res["_roofline"] = (dec_bytes, sel_us, dec_us)
         grouped = w.kv_dtype in ("q8_0", "q4_0")      # per-head and sparse-V: f16 and int8
-        if not args.no_per_head and not grouped:
+        other_dim = w.D != 128       # the NEXT rows' calls are built for head dim 128
+        if not args.no_per_head and not grouped and not other_dim:
             res["quest_per_head"] = measure_per_head(T, skv, torch, w, caches, R, q, seq_len, Lmax,
                                                      new_k, new_v, pos_last, ks, res["quest"])
-        if not args.no_scan4 and w.kv_dtype == "f16":
+        if not args.no_scan4 and w.kv_dtype == "f16" and not other_dim:
             res["scan4"] = measure_scan4(T, skv, torch, w, caches, R, q, seq_len, Lmax,
                                          args.scan4_delta)
         n_chunk = min(args.chunk_tokens, 16 // w.G)
-        if n_chunk > 1 and not grouped:
+        if n_chunk > 1 and not grouped and not other_dim:
             res["chunk"] = measure_chunk(T, skv, torch, w, caches, R, seq_len, Lmax, n_chunk,
                                          res.get("dense"), res["quest"])
-        if args.sparse_v_tau > 0 and not grouped:
+        if args.sparse_v_tau > 0 and not grouped and not other_dim:
             res["quest_sparse_v"] = measure_sparse_v(
                 T, skv, torch, w, caches, R, q, seq_len, Lmax, new_k, new_v, pos_last, ks, score,
                 sel, cnt, attended, args.sparse_v_tau, calls_us)
@@ -814,10 +815,10 @@ def main():
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--mode", choices=("both", "quest", "dense"), default="both",
                     help="which step of the 32K workload to time (profiling runs use one)")
-    ap.add_argument("--workloads", default="1,2,4,5,3@16384,3q8,3q4",
+    ap.add_argument("--workloads", default="1,2,4,5,3@16384,3q8,3q4,3d64,3d256",
                     help="other workloads to time besides the 32K headline ('' = none; "
                          "3@L = the 32K Quest generator at context L; 3q8 / 3q4 = over a "
-                         "q8_0 / q4_0 cache)")
+                         "q8_0 / q4_0 cache; 3d64 / 3d256 = at head dim 64 / 256)")
     ap.add_argument("--chunk-tokens", type=int, default=4,
                     help="query tokens per chunk for the multi-token measurement (0 = off)")
     ap.add_argument("--no-per-head", action="store_true",
@@ -847,6 +848,9 @@ def main():
         if tok.startswith("3@"):
             # the 32K generator at another length (Quest vs dense from 16K up)
             jobs.append((workloads.quest32k_at(int(tok[2:])), True, True, False))
+        elif tok.startswith("3d"):
+            # the 32K generator at another head dim (3d64, 3d256)
+            jobs.append((workloads.quest32k_dim(int(tok[2:])), True, True, False))
         elif tok.startswith("3q"):
             # the 32K generator over a group-wise quantized cache (3q8, 3q4)
             jobs.append((workloads.quest32k_quant("q8_0" if tok == "3q8" else "q4_0"), True,

@@ -22,7 +22,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libskv.so")
 
-SOURCES = ["api.cpp", "append.hip", "bounds.hip", "select.hip", "decode_mfma.hip",
+SOURCES = ["api.cpp", "append.hip", "bounds.hip", "select.hip", "decode_mfma.hip", "decode_dims.hip",
            "combine.hip", "static_step.hip", "sparse_v.hip",
            "decode_grouped.hip", "scan4.hip"]
 ARCH = "gfx950"

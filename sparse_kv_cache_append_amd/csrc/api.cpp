@@ -12,6 +12,10 @@ constexpr int32_t kMaxSplit = 4096;
 constexpr int32_t kMaxSelectBlocks = 16384;
 
 bool valid_head_dim(int32_t d) { return d >= 16 && d <= 1024 && d % 16 == 0; }
+// Head dims built: 128 for every call; 64 and 256 for the f16 and int8
+// caches' append, bounds, attention and step calls (CORE below).
+constexpr int32_t kFullDim = 128;
+bool core_head_dim(int32_t d) { return d == 64 || d == kFullDim || d == 256; }
 bool supported_group(int32_t g) { return g == 1 || g == 2 || g == 4 || g == 8; }
 bool supported_tokens(int32_t n) { return n == 1 || n == 2 || n == 4 || n == 8; }
 
@@ -28,7 +32,8 @@ bool grid_fits(int64_t a, int64_t b, int64_t c) { return a * b * c <= kMaxGridX;
 // The kernels move cache rows, bounds, queries and new rows in 16-byte vectors.
 bool aligned(const void* p, uintptr_t a = 16) { return reinterpret_cast<uintptr_t>(p) % a == 0; }
 
-skv_status check_cache(const skv_cache* c, bool need_bounds) {
+enum DimUse { kDim128Only = 0, kDimCore = 1 };
+skv_status check_cache(const skv_cache* c, bool need_bounds, DimUse dims = kDim128Only) {
   if (c == nullptr) return SKV_EINVAL;
   if (c->batch < 1 || c->n_kv_heads < 1 || c->max_seq < 1) return SKV_EINVAL;
   if (!valid_head_dim(c->head_dim)) return SKV_EINVAL;
@@ -47,7 +52,9 @@ skv_status check_cache(const skv_cache* c, bool need_bounds) {
   if (elems > 4.0e18) return SKV_ERANGE;
   if (c->batch > kMaxGridYZ || c->n_kv_heads > kMaxGridYZ) return SKV_ERANGE;
   if (!grid_fits(blocks_of(c->max_seq, c->block), c->n_kv_heads, c->batch)) return SKV_ERANGE;
-  if (c->head_dim != 128) return SKV_EUNSUPPORTED;
+  if (c->head_dim != kFullDim &&
+      (dims != kDimCore || !core_head_dim(c->head_dim) || skv::is_grouped(c->kv_dtype)))
+    return SKV_EUNSUPPORTED;
   return SKV_OK;
 }
 
@@ -109,7 +116,7 @@ const char* skv_status_str(int32_t s) {
 skv_status skv_kv_append(const skv_cache* c, const int32_t* pos0, int32_t n_new,
                          const void* k_new, const void* v_new, int32_t src_dtype,
                          hipStream_t stream) {
-  skv_status st = check_cache(c, false);
+  skv_status st = check_cache(c, false, kDimCore);
   if (st != SKV_OK) return st;
   if (pos0 == nullptr || k_new == nullptr || v_new == nullptr || n_new < 1) return SKV_EINVAL;
   if (!aligned(k_new) || !aligned(v_new)) return SKV_EINVAL;
@@ -122,7 +129,7 @@ skv_status skv_kv_append(const skv_cache* c, const int32_t* pos0, int32_t n_new,
 skv_status skv_block_bounds(const skv_cache* c, const float* q, int32_t n_heads,
                             const int32_t* seq_len, int32_t max_len, float* score,
                             hipStream_t stream) {
-  skv_status st = check_cache(c, true);
+  skv_status st = check_cache(c, true, kDimCore);
   if (st != SKV_OK) return st;
   if (q == nullptr || seq_len == nullptr || score == nullptr || !aligned(q)) return SKV_EINVAL;
   st = check_heads(c, n_heads);
@@ -155,7 +162,7 @@ skv_status skv_decode_attn(const skv_cache* c, const float* q, int32_t n_heads,
                            float softmax_scale, int32_t n_split,
                            void* workspace, size_t workspace_bytes,
                            int32_t* dbg_logits, hipStream_t stream) {
-  skv_status st = check_cache(c, false);
+  skv_status st = check_cache(c, false, kDimCore);
   if (st != SKV_OK) return st;
   if (q == nullptr || seq_len == nullptr || !aligned(q)) return SKV_EINVAL;
   st = check_heads(c, n_heads);
@@ -193,7 +200,7 @@ skv_status skv_decode_step(const skv_cache* c, const int32_t* pos0, const void* 
                            float softmax_scale, int32_t n_split, void* workspace,
                            size_t workspace_bytes, float* out, hipStream_t stream) {
   const bool quest = k_sel != nullptr;
-  skv_status st = check_cache(c, quest);
+  skv_status st = check_cache(c, quest, kDimCore);
   if (st != SKV_OK) return st;
   if (q == nullptr || seq_len == nullptr || out == nullptr || !aligned(q)) return SKV_EINVAL;
   st = check_heads(c, n_heads);
@@ -233,14 +240,17 @@ skv_status skv_decode_step(const skv_cache* c, const int32_t* pos0, const void* 
   p.dbg_logits = nullptr;
   hipError_t e = hipSuccess;
   const bool grouped = skv::is_grouped(c->kv_dtype);
-  if (grouped && k_new != nullptr && !quest) {
-    // dense steps over group-wise caches: the append runs as its own kernel
-    // (the Quest step folds it into the bounds pass, as for every cache)
-    e = skv::launch_append_grouped(*c, pos0, 1, k_new, v_new, stream);
+  // the folded appends move head dim 128 rows
+  const bool fold = c->head_dim == kFullDim;
+  if (k_new != nullptr && ((grouped && !quest) || !fold)) {
+    // dense steps over group-wise caches, and every step at another head dim:
+    // the append runs as its own kernel (else the Quest step folds it into
+    // the bounds pass, the dense step into the attention kernel)
+    e = append_any(*c, pos0, 1, k_new, v_new, stream);
     if (e != hipSuccess) return SKV_EDEVICE;
   }
   if (quest) {
-    e = k_new != nullptr
+    e = k_new != nullptr && fold
             ? skv::launch_append_bounds(*c, pos0, k_new, v_new, q, n_heads, seq_len, max_len,
                                         score, stream)
             : skv::launch_bounds(*c, q, n_heads, seq_len, max_len, score, stream);
@@ -256,7 +266,7 @@ skv_status skv_decode_step(const skv_cache* c, const int32_t* pos0, const void* 
                              k_sel, n_sink, n_recent, max_sel, sel_idx, sel_cnt, nullptr, stream);
       if (e != hipSuccess) return SKV_EDEVICE;
     }
-  } else if (k_new != nullptr && !grouped) {
+  } else if (k_new != nullptr && !grouped && fold) {
     p.app = skv::FoldedAppend{k_new, v_new, pos0};   // written by the attention kernel
   }
   e = decode_any(p, stream);
@@ -271,7 +281,7 @@ skv_status skv_decode_attn_select(const skv_cache* c, const float* q, int32_t n_
                                   int32_t max_sel, int32_t* sel_idx, int32_t* sel_cnt,
                                   float softmax_scale, int32_t n_split, void* workspace,
                                   size_t workspace_bytes, hipStream_t stream) {
-  skv_status st = check_cache(c, false);
+  skv_status st = check_cache(c, false, kDimCore);
   if (st != SKV_OK) return st;
   if (q == nullptr || seq_len == nullptr || !aligned(q)) return SKV_EINVAL;
   st = check_heads(c, n_heads);

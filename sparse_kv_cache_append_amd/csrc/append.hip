@@ -142,25 +142,36 @@ append_i8_kernel(int8_t* __restrict__ kc, int8_t* __restrict__ vc,
   }
 }
 
-}  // namespace
-
-hipError_t launch_append(const skv_cache& c, const int32_t* pos0, int32_t n_new,
-                         const void* k_new, const void* v_new, hipStream_t stream) {
+template <int D>
+hipError_t launch_append_d(const skv_cache& c, const int32_t* pos0, int32_t n_new,
+                           const void* k_new, const void* v_new, hipStream_t stream) {
   const int32_t max_blocks = (c.max_seq + c.block - 1) / c.block;
   const int32_t n_aff = (n_new + c.block - 2) / c.block + 1;
   dim3 grid(n_aff, c.n_kv_heads, c.batch);
   if (c.kv_dtype == SKV_F16) {
-    append_f16_kernel<128><<<grid, kAppendThreads, 0, stream>>>(
+    append_f16_kernel<D><<<grid, kAppendThreads, 0, stream>>>(
         static_cast<uint16_t*>(c.k), static_cast<uint16_t*>(c.v), c.kmin, c.kmax,
         static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new), pos0, n_new,
         c.n_kv_heads, c.max_seq, c.block, max_blocks);
   } else {
-    append_i8_kernel<128><<<grid, kAppendThreads, 0, stream>>>(
+    append_i8_kernel<D><<<grid, kAppendThreads, 0, stream>>>(
         static_cast<int8_t*>(c.k), static_cast<int8_t*>(c.v), c.k_scale, c.v_scale, c.kmin,
         c.kmax, static_cast<const float*>(k_new), static_cast<const float*>(v_new), pos0, n_new,
         c.n_kv_heads, c.max_seq, c.block, max_blocks);
   }
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_append(const skv_cache& c, const int32_t* pos0, int32_t n_new,
+                         const void* k_new, const void* v_new, hipStream_t stream) {
+  switch (c.head_dim) {
+    case 64: return launch_append_d<64>(c, pos0, n_new, k_new, v_new, stream);
+    case 128: return launch_append_d<128>(c, pos0, n_new, k_new, v_new, stream);
+    case 256: return launch_append_d<256>(c, pos0, n_new, k_new, v_new, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace skv

@@ -9,8 +9,10 @@
 //
 // The pass reads the whole side cache (512 B per block and KV head at
 // D = 128), so it is spread over as many workgroups as there are 16-block
-// tiles: 16 lanes per block, each lane holding 8 channels (one 16-byte load of
-// kmin and one of kmax), a 16-lane DPP sum per head, then the group max.
+// tiles: 16 lanes per block, each lane holding D / 16 channels (at D = 128
+// one 16-byte load of kmin and one of kmax), a 16-lane DPP sum per head, then
+// the group max.  Head dims 64 and 256 take the plain pass (no folded append,
+// per-head scores or token chunks, vector scoring).
 //
 // A decode step may fold its one-token append into this pass
 // (launch_append_bounds), which saves a launch and a dependent round trip.
@@ -357,8 +359,11 @@ bounds_kernel(uint16_t* __restrict__ kmin, uint16_t* __restrict__ kmax,
               const float* __restrict__ q, const int32_t* __restrict__ seq_len,
               float* __restrict__ score, int32_t Hkv, int32_t max_len, int32_t block,
               int32_t max_blocks, int32_t tiles, int32_t n_rows, AppendOne ap) {
-  static_assert(D == kLanesPerBlock * 8, "one 16-byte load per lane per bound");
+  static_assert(D == 64 || D == 128 || D == 256, "head dims 64, 128, 256");
+  static_assert(D == 128 || (MODE == kNoAppend && !PH && NT == 1),
+                "head dims other than 128: plain bounds only");
   static_assert(NT == 1 || (MODE == kNoAppend && !PH), "token chunks: plain bounds only");
+  constexpr int CPL = D / kLanesPerBlock;                      // channels per lane
   constexpr int kQ4 = NT * G * D / 4;                          // 16-byte query loads
   constexpr int kQPer = (kQ4 + kBoundsThreads - 1) / kBoundsThreads;
   static_assert(kQPer <= 2, "at most 16 query rows");
@@ -369,7 +374,7 @@ bounds_kernel(uint16_t* __restrict__ kmin, uint16_t* __restrict__ kmax,
   const uint32_t row = xcd_row(slot / uint32_t(tiles), uint32_t(n_rows));
   const int32_t g = int32_t(row % uint32_t(Hkv)), b = int32_t(row / uint32_t(Hkv));
   const int32_t j = tile * kBlocksPerWG + int32_t(threadIdx.x) / kLanesPerBlock;
-  const int32_t c = threadIdx.x % kLanesPerBlock;  // channels 8c .. 8c+7
+  const int32_t c = threadIdx.x % kLanesPerBlock;  // channels CPL c .. CPL c + CPL - 1
   // Requests issued before anything waits (one round trip): the row length
   // (and append position), the group's G query rows (G * 512 B, one 16-byte
   // load per thread, staged once per workgroup in LDS) and this thread's
@@ -390,15 +395,45 @@ bounds_kernel(uint16_t* __restrict__ kmin, uint16_t* __restrict__ kmax,
       qreg[i] = reinterpret_cast<const float4*>(
           q + ((int64_t(b) * NT + rr / G) * H + g * G + rr % G) * D)[e % (D / 4)];
   }
-  uint4 lo = make_uint4(0, 0, 0, 0), hi = make_uint4(0, 0, 0, 0);
-  if (j < max_blocks) {
-    const int64_t off = ((int64_t(b) * Hkv + g) * max_blocks + j) * D + c * 8;
-    // read once per step: streaming (nontemporal) loads
-    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-    const u32x4 l4 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kmin + off));
-    const u32x4 h4 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kmax + off));
-    lo = make_uint4(l4.x, l4.y, l4.z, l4.w);
-    hi = make_uint4(h4.x, h4.y, h4.z, h4.w);
+  // this lane's CPL bounds of each kind as CPL / 2 words (read once per
+  // step: streaming loads, 16 bytes each, 8 bytes at D = 64)
+  constexpr int kW = CPL / 2;
+  uint32_t lw[kW], hw[kW];
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  if constexpr (D == 128) {
+    uint4 lo = make_uint4(0, 0, 0, 0), hi = make_uint4(0, 0, 0, 0);
+    if (j < max_blocks) {
+      const int64_t off = ((int64_t(b) * Hkv + g) * max_blocks + j) * D + c * 8;
+      const u32x4 l4 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kmin + off));
+      const u32x4 h4 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kmax + off));
+      lo = make_uint4(l4.x, l4.y, l4.z, l4.w);
+      hi = make_uint4(h4.x, h4.y, h4.z, h4.w);
+    }
+    lw[0] = lo.x; lw[1] = lo.y; lw[2] = lo.z; lw[3] = lo.w;
+    hw[0] = hi.x; hw[1] = hi.y; hw[2] = hi.z; hw[3] = hi.w;
+  } else {
+    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+    const int64_t off = ((int64_t(b) * Hkv + g) * max_blocks + j) * D + c * CPL;
+    const bool in = j < max_blocks;
+    if constexpr (kW >= 4) {
+#pragma unroll
+      for (int i = 0; i < kW / 4; ++i) {
+        u32x4 l4 = {0u, 0u, 0u, 0u}, h4 = {0u, 0u, 0u, 0u};
+        if (in) {
+          l4 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kmin + off) + i);
+          h4 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kmax + off) + i);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { lw[4 * i + e] = l4[e]; hw[4 * i + e] = h4[e]; }
+      }
+    } else {
+      u32x2 l2 = {0u, 0u}, h2 = {0u, 0u};
+      if (in) {
+        l2 = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(kmin + off));
+        h2 = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(kmax + off));
+      }
+      lw[0] = l2[0]; lw[1] = l2[1]; hw[0] = h2[0]; hw[1] = h2[1];
+    }
   }
   // With the append: this lane's 8 channels of the new token's K and V rows,
   // requested here too (they do not depend on the position).
@@ -419,12 +454,10 @@ bounds_kernel(uint16_t* __restrict__ kmin, uint16_t* __restrict__ kmax,
   // them, and the compiler would otherwise move them into that branch,
   // behind the wait for the position)
   if constexpr (MODE != kNoAppend) asm volatile("" ::: "memory");
-  uint16_t lb[8], hb[8];
+  uint16_t lb[CPL], hb[CPL];
   {
-    const uint32_t lw[4] = {lo.x, lo.y, lo.z, lo.w};
-    const uint32_t hw[4] = {hi.x, hi.y, hi.z, hi.w};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < kW; ++i) {
       lb[2 * i] = uint16_t(lw[i] & 0xFFFFu); lb[2 * i + 1] = uint16_t(lw[i] >> 16);
       hb[2 * i] = uint16_t(hw[i] & 0xFFFFu); hb[2 * i + 1] = uint16_t(hw[i] >> 16);
     }
@@ -469,7 +502,7 @@ bounds_kernel(uint16_t* __restrict__ kmin, uint16_t* __restrict__ kmax,
   // hold an infinity (an int8 cache with keys past the f16 range, or an
   // all-NaN channel) keeps the vector path, whose q == 0 rule the MFMA form
   // would turn into NaN.
-  constexpr bool kMfma = NT * G >= 8;
+  constexpr bool kMfma = NT * G >= 8 && D == 128;
   if (tile * kBlocksPerWG < nb) {          // else the whole tile is past the end
     __shared__ __attribute__((aligned(16))) float qs[NT * G * D];
 #pragma unroll
@@ -496,26 +529,27 @@ bounds_kernel(uint16_t* __restrict__ kmin, uint16_t* __restrict__ kmax,
     } else {
       __syncthreads();
     }
-    float mn[8], mx[8];
+    float mn[CPL], mx[CPL];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) { mn[e] = h2f(lb[e]); mx[e] = h2f(hb[e]); }
+    for (int e = 0; e < CPL; ++e) { mn[e] = h2f(lb[e]); mx[e] = h2f(hb[e]); }
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      float qv[G][8];
+      float qv[G][CPL];
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        const float* qr = qs + (t * G + h) * D + c * 8;
-        const float4 a = reinterpret_cast<const float4*>(qr)[0];
-        const float4 bq = reinterpret_cast<const float4*>(qr)[1];
-        qv[h][0] = a.x; qv[h][1] = a.y; qv[h][2] = a.z; qv[h][3] = a.w;
-        qv[h][4] = bq.x; qv[h][5] = bq.y; qv[h][6] = bq.z; qv[h][7] = bq.w;
+        const float* qr = qs + (t * G + h) * D + c * CPL;
+#pragma unroll
+        for (int i = 0; i < CPL / 4; ++i) {
+          const float4 a = reinterpret_cast<const float4*>(qr)[i];
+          qv[h][4 * i] = a.x; qv[h][4 * i + 1] = a.y; qv[h][4 * i + 2] = a.z; qv[h][4 * i + 3] = a.w;
+        }
       }
       float tbest = -INFINITY;
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         float acc = 0.0f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
+        for (int e = 0; e < CPL; ++e) {
           const float x = qv[h][e];
           const float kb = x > 0.0f ? mx[e] : mn[e];
           acc += (x != 0.0f) ? x * kb : 0.0f;
@@ -566,7 +600,7 @@ scored:
   }
 }
 
-template <int G, int MODE, bool PH = false, int NT = 1>
+template <int G, int MODE, bool PH = false, int NT = 1, int D = 128>
 hipError_t launch_bounds_g(const skv_cache& c, const float* q, const int32_t* seq_len,
                            int32_t max_len, float* score, const AppendOne& ap,
                            hipStream_t stream) {
@@ -578,21 +612,21 @@ hipError_t launch_bounds_g(const skv_cache& c, const float* q, const int32_t* se
   const int64_t n_wg = int64_t(tiles) * c.n_kv_heads * c.batch;
   if (n_wg > 0x7fffffff) return hipErrorInvalidValue;
   const dim3 grid(static_cast<uint32_t>(n_wg));
-  bounds_kernel<128, G, MODE, PH, NT><<<grid, kBoundsThreads, 0, stream>>>(
+  bounds_kernel<D, G, MODE, PH, NT><<<grid, kBoundsThreads, 0, stream>>>(
       c.kmin, c.kmax, q, seq_len, score, c.n_kv_heads, max_len, c.block, max_blocks, tiles,
       c.n_kv_heads * c.batch, ap);
   return hipGetLastError();
 }
 
-template <int MODE>
+template <int MODE, int D = 128>
 hipError_t launch_bounds_m(const skv_cache& c, const float* q, int32_t n_heads,
                            const int32_t* seq_len, int32_t max_len, float* score,
                            const AppendOne& ap, hipStream_t stream) {
   switch (n_heads / c.n_kv_heads) {
-    case 1: return launch_bounds_g<1, MODE>(c, q, seq_len, max_len, score, ap, stream);
-    case 2: return launch_bounds_g<2, MODE>(c, q, seq_len, max_len, score, ap, stream);
-    case 4: return launch_bounds_g<4, MODE>(c, q, seq_len, max_len, score, ap, stream);
-    case 8: return launch_bounds_g<8, MODE>(c, q, seq_len, max_len, score, ap, stream);
+    case 1: return launch_bounds_g<1, MODE, false, 1, D>(c, q, seq_len, max_len, score, ap, stream);
+    case 2: return launch_bounds_g<2, MODE, false, 1, D>(c, q, seq_len, max_len, score, ap, stream);
+    case 4: return launch_bounds_g<4, MODE, false, 1, D>(c, q, seq_len, max_len, score, ap, stream);
+    case 8: return launch_bounds_g<8, MODE, false, 1, D>(c, q, seq_len, max_len, score, ap, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -602,12 +636,20 @@ hipError_t launch_bounds_m(const skv_cache& c, const float* q, int32_t n_heads,
 hipError_t launch_bounds(const skv_cache& c, const float* q, int32_t n_heads,
                          const int32_t* seq_len, int32_t max_len, float* score,
                          hipStream_t stream) {
-  return launch_bounds_m<kNoAppend>(c, q, n_heads, seq_len, max_len, score, AppendOne{}, stream);
+  const AppendOne ap{};
+  switch (c.head_dim) {
+    case 64: return launch_bounds_m<kNoAppend, 64>(c, q, n_heads, seq_len, max_len, score, ap, stream);
+    case 128: return launch_bounds_m<kNoAppend>(c, q, n_heads, seq_len, max_len, score, ap, stream);
+    case 256:
+      return launch_bounds_m<kNoAppend, 256>(c, q, n_heads, seq_len, max_len, score, ap, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_bounds_multi(const skv_cache& c, const float* q, int32_t n_tok,
                                int32_t n_heads, const int32_t* seq_len, int32_t max_len,
                                float* score, hipStream_t stream) {
+  if (c.head_dim != 128) return hipErrorInvalidValue;
   const AppendOne ap{};
   const int G = n_heads / c.n_kv_heads;
 #define SKV_BMT(GG, NN)                                                                        \
@@ -625,6 +667,7 @@ hipError_t launch_bounds_multi(const skv_cache& c, const float* q, int32_t n_tok
 hipError_t launch_bounds_heads(const skv_cache& c, const float* q, int32_t n_heads,
                                const int32_t* seq_len, int32_t max_len, float* score,
                                hipStream_t stream) {
+  if (c.head_dim != 128) return hipErrorInvalidValue;
   const AppendOne ap{};
   switch (n_heads / c.n_kv_heads) {
     case 1: return launch_bounds_g<1, kNoAppend, true>(c, q, seq_len, max_len, score, ap, stream);
@@ -639,6 +682,7 @@ hipError_t launch_append_bounds(const skv_cache& c, const int32_t* pos0, const v
                                 const void* v_new, const float* q, int32_t n_heads,
                                 const int32_t* seq_len, int32_t max_len, float* score,
                                 hipStream_t stream) {
+  if (c.head_dim != 128) return hipErrorInvalidValue;
   AppendOne ap{c.k, c.v, c.k_scale, c.v_scale, k_new, v_new, pos0, c.max_seq};
   switch (c.kv_dtype) {
     case SKV_F16:

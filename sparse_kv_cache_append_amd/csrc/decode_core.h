@@ -8,6 +8,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "device_common.h"
 
 namespace skv {
@@ -23,7 +25,7 @@ typedef int int2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kMWaves = 4;
 constexpr int kMThreads = kMWaves * kWave;
-constexpr int kD = 128;
+constexpr int kD = 128;                // the head dimension every feature supports
 constexpr int kRowBytesF16 = kD * 2;   // 256
 constexpr int kRowBytesI8 = kD;        // 128
 
@@ -176,7 +178,8 @@ __device__ __forceinline__ QRows make_qrows(int32_t ntok, int32_t Hkv) {
 }
 
 // Softmax bookkeeping of one tile for the 16 MFMA columns (heads): lane l
-// owns head l%16 and rows 4*(l/16) + r of the tile.  s[r] are base-2 logits
+// owns head l%16 and rows 4*(l/16) + r of the tile; O holds N 16-channel
+// blocks of the accumulators (N = D / 16).  s[r] are base-2 logits
 // (-inf for masked rows); returns the weights p[r] and rescales O when the
 // reference moves (by the change of reference times o_extra, a caller's exact
 // power of two).
@@ -191,9 +194,9 @@ __device__ __forceinline__ QRows make_qrows(int32_t ntok, int32_t Hkv) {
 // the rescale: 262K dense 53.6 -> 51.9 us; the f16 kernel does not, and keeps
 // the exact running maximum.)
 constexpr float kLazySlack = 8.0f;
-template <int G, int NT, bool LAZY>
+template <int G, int NT, bool LAZY, int N>
 __device__ __forceinline__ void tile_softmax(float (&s)[4 * NT], float& m_run, float& l_run,
-                                             float4_t (&O)[8], float o_extra = 1.0f) {
+                                             float4_t (&O)[N], float o_extra = 1.0f) {
   const int lane = threadIdx.x % kWave;
   float mx = s[0];
 #pragma unroll
@@ -238,7 +241,7 @@ __device__ __forceinline__ void tile_softmax(float (&s)[4 * NT], float& m_run, f
       }
       c *= o_extra;
 #pragma unroll
-      for (int n = 0; n < 8; ++n) O[n][r] *= c;
+      for (int n = 0; n < N; ++n) O[n][r] *= c;
     }
   } else {
     l_run += ps;
@@ -248,15 +251,16 @@ __device__ __forceinline__ void tile_softmax(float (&s)[4 * NT], float& m_run, f
 
 // Merge the 4 wavefronts' states (heads < G) through LDS and write the
 // part's partial softmax state.
-template <int G>
-__device__ __forceinline__ void finish_mfma(float m_run, float l_run, const float4_t (&O)[8],
+template <int G, int N>
+__device__ __forceinline__ void finish_mfma(float m_run, float l_run, const float4_t (&O)[N],
                                             float* lds, float* __restrict__ ws_m,
                                             float* __restrict__ ws_l, float* __restrict__ ws_o,
                                             const QRows& qr, int32_t b, int32_t g,
                                             int32_t n_split, int32_t split) {
+  constexpr int D = 16 * N;
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   float* lo = lds;                          // [waves][G][D]
-  float* lm = lds + kMWaves * G * kD;       // [waves][G]
+  float* lm = lds + kMWaves * G * D;        // [waves][G]
   float* ll = lm + kMWaves * G;
   __syncthreads();                          // tile buffers are reused
   const int g4 = 4 * (lane / 16);
@@ -265,13 +269,13 @@ __device__ __forceinline__ void finish_mfma(float m_run, float l_run, const floa
     const int h = g4 + r;
     if (h < G) {
 #pragma unroll
-      for (int n = 0; n < 8; ++n) lo[(wave * G + h) * kD + 16 * n + lane % 16] = O[n][r];
+      for (int n = 0; n < N; ++n) lo[(wave * G + h) * D + 16 * n + lane % 16] = O[n][r];
     }
   }
   if (lane < G) { lm[wave * G + lane] = m_run; ll[wave * G + lane] = l_run; }
   __syncthreads();
-  for (int idx = threadIdx.x; idx < G * kD; idx += kMThreads) {
-    const int h = idx / kD, d = idx % kD;
+  for (int idx = threadIdx.x; idx < G * D; idx += kMThreads) {
+    const int h = idx / D, d = idx % D;
     float M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < kMWaves; ++w) M = fmaxf(M, lm[w * G + h]);
@@ -281,29 +285,33 @@ __device__ __forceinline__ void finish_mfma(float m_run, float l_run, const floa
       for (int w = 0; w < kMWaves; ++w) {
         const float mw = lm[w * G + h];
         const float a = (mw == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mw - M);
-        so += a * lo[(w * G + h) * kD + d];
+        so += a * lo[(w * G + h) * D + d];
         sl += a * ll[w * G + h];
       }
     }
     const int64_t ps = qr.row(b, g, h) * n_split + split;
-    ws_o[ps * kD + d] = so;
+    ws_o[ps * D + d] = so;
     if (d == 0) { ws_m[ps] = M; ws_l[ps] = sl; }
   }
 }
 
 // The int8 kernels' query as the B operand of the integer q.K product
 // (column = head lc, k-chunk lg): x holds this lane's channels
-// 64 kk + 16 lg + 0..15 of its head (zeros past the group); the head's absmax
-// scale over all 128 channels (the 4 lanes of a column hold 32 channels each)
+// 64 kk + 16 lg + 0..15 of its head, kk < KK = D / 64 (zeros past the group);
+// the head's absmax scale over all D channels (the 4 lanes of a column hold
+// D / 4 channels each)
 // and the codes, which equal the correctly rounded rint(x / scale) of the
 // append quantizer bit for bit: taken through the reciprocal, with the rare
 // value near a rounding boundary (flagged per lane) redone with the exact
 // quotient.  coef = scale * softmax scale * log2 e (0 past the group).
-__device__ __forceinline__ void i8_query_operand(const float (&x)[2][16], bool hv, float scale2,
-                                                 int4_t (&qb)[2], float& coef) {
+template <int KK>
+__device__ __forceinline__ void i8_query_operand(const float (&x)[KK][16], bool hv, float scale2,
+                                                 int4_t (&qb)[KK], float& coef) {
+  // one bit of the redo mask per value
+  typedef typename std::conditional<(KK > 2), uint64_t, uint32_t>::type Mask;
   float a = 0.0f;
 #pragma unroll
-  for (int kk = 0; kk < 2; ++kk) {
+  for (int kk = 0; kk < KK; ++kk) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) a = fmaxf(a, fabsf(x[kk][i]));
   }
@@ -312,27 +320,27 @@ __device__ __forceinline__ void i8_query_operand(const float (&x)[2][16], bool h
   // codes through the reciprocal; the rare value near a rounding boundary
   // (flagged per lane) is redone with the exact quotient
   const float inv = 1.0f / qs;
-  int c[2][16];
-  uint32_t redo = 0u;
+  int c[KK][16];
+  Mask redo = 0u;
 #pragma unroll
-  for (int kk = 0; kk < 2; ++kk) {
+  for (int kk = 0; kk < KK; ++kk) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       bool ex;
       c[kk][i] = quant_code_recip(x[kk][i], inv, ex);
-      redo |= uint32_t(ex) << (16 * kk + i);
+      redo |= Mask(ex) << (16 * kk + i);
     }
   }
   if (__builtin_amdgcn_ballot_w64(redo != 0u) != 0u) {
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
+    for (int kk = 0; kk < KK; ++kk) {
 #pragma unroll
       for (int i = 0; i < 16; ++i)
         if ((redo >> (16 * kk + i)) & 1u) c[kk][i] = quant_code(x[kk][i], qs);
     }
   }
 #pragma unroll
-  for (int kk = 0; kk < 2; ++kk) {
+  for (int kk = 0; kk < KK; ++kk) {
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       uint32_t packed = 0u;

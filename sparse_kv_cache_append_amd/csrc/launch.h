@@ -116,6 +116,8 @@ hipError_t launch_select(const float* score, const int32_t* seq_len, int32_t bat
                          uint32_t* sel_mask, hipStream_t stream, int32_t n_tok = 1);
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
+// head dims 64 and 256 (called by launch_decode)
+hipError_t launch_decode_dims(const DecodeParams& p, hipStream_t stream);
 
 // Sparse-V decode attention (sparse_v.hip): the q.K pass and the value pass
 // over the kept rows, writing the standard partial states for skv_combine.

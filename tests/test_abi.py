@@ -50,7 +50,10 @@ BAD = 0x10  # never dereferenced: every call below fails validation first
     (dict(n_kv_heads=0), skv.SKV_EINVAL),
     (dict(head_dim=100), skv.SKV_EINVAL),         # not a multiple of 16
     (dict(head_dim=2048), skv.SKV_EINVAL),        # above 1024
-    (dict(head_dim=64), skv.SKV_EUNSUPPORTED),    # valid, not built
+    (dict(head_dim=96), skv.SKV_EUNSUPPORTED),    # valid, not built
+    (dict(head_dim=512), skv.SKV_EUNSUPPORTED),
+    (dict(head_dim=64, kv_dtype=skv.SKV_Q8_0, k_scale=0x5000, v_scale=0x6000),
+     skv.SKV_EUNSUPPORTED),                       # group-wise caches: head dim 128 only
     (dict(block=40), skv.SKV_EINVAL),
     (dict(block=0), skv.SKV_EINVAL),
     (dict(kv_dtype=7), skv.SKV_EINVAL),
@@ -67,6 +70,38 @@ def test_cache_descriptor_validation(lib, kw, expect):
     st = lib.skv_decode_attn(ctypes.byref(d), BAD, 32, BAD, 10, None, None, 0, 0.1, 4,
                              BAD, 1 << 30, None, None)
     assert st == expect
+
+
+@pytest.mark.parametrize("dim", [64, 256])
+def test_head_dims_64_256_core_calls_only(lib, dim):
+    """Head dims 64 and 256 pass the descriptor check of the core calls (the
+    calls below then stop at a later check, before any launch) and are
+    refused by the calls built for head dim 128 only."""
+    d = desc(head_dim=dim)
+    q = 0x7000
+    # decode_attn: accepted, then the workspace is too small
+    assert lib.skv_decode_attn(ctypes.byref(d), q, 32, BAD, 10, None, None, 0, 0.1, 4,
+                               BAD, 16, None, None) == skv.SKV_EWORKSPACE
+    # decode_attn_select and decode_step: the same
+    assert lib.skv_decode_attn_select(ctypes.byref(d), q, 32, BAD, 10, BAD, BAD, 1, 2, 8,
+                                      BAD, BAD, 0.1, 4, BAD, 16, None) == skv.SKV_EWORKSPACE
+    assert lib.skv_decode_step(ctypes.byref(d), None, None, None, skv.SKV_F16, q, 32, BAD, 10,
+                               None, 1, 2, 8, None, None, None, 0.1, 4, BAD, 16, BAD,
+                               None) == skv.SKV_EWORKSPACE
+    # block_bounds and kv_append: accepted, then a range check fails
+    assert lib.skv_block_bounds(ctypes.byref(d), q, 32, BAD, 5000, BAD, None) == skv.SKV_ERANGE
+    assert lib.skv_kv_append(ctypes.byref(d), BAD, 5000, q, q, skv.SKV_F16, None) == \
+        skv.SKV_ERANGE
+    # head dim 128 only: per-head bounds and attention, sparse-V, chunks, the scan
+    assert lib.skv_block_bounds_heads(ctypes.byref(d), q, 32, BAD, 10, BAD, None) == \
+        skv.SKV_EUNSUPPORTED
+    assert lib.skv_block_bounds_multi(ctypes.byref(d), q, 2, 32, BAD, 10, BAD, None) == \
+        skv.SKV_EUNSUPPORTED
+    assert lib.skv_decode_attn_sparse_v(ctypes.byref(d), q, 32, BAD, 10, None, None, 0, 0.1,
+                                        1e-3, 0.0, 4, BAD, 1 << 30, BAD, None) == \
+        skv.SKV_EUNSUPPORTED
+    assert lib.skv_scan4_build(ctypes.byref(d), BAD, BAD, 10, BAD, BAD, BAD, BAD, None) == \
+        skv.SKV_EUNSUPPORTED
 
 
 def test_decode_argument_validation(lib):

@@ -1,0 +1,243 @@
+"""Head dims 64 and 256: the f16 and int8 caches' append, bounds, selection,
+attention and step calls against the oracle (cpu-attn kernel card,
+"Requirements and limits": the head dimension is any multiple of 16 up to
+1024; these two and 128 are built).
+
+Sizes span several tiles per wavefront, several parts and a ragged tail (the
+f16 tile is 16 tokens, the int8 tile 32; a tile's 16-byte loads cover 8, 4 or
+2 rows per instruction at D = 64, 128, 256).  Bars as at D = 128: appended
+rows, codes, scales and bounds exact; int8 logit dots exact; selected sets
+exact on the kernel's own scores; f16 outputs within 1e-3 and int8 outputs
+within 1e-4 of the method (per head and per element); the step bit-identical
+to the calls it composes.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_harness import (DEV, assert_close, build_cache, padded_rows, quantized_host, rel_err,
+                         run_dense, run_select, run_sparse)
+from test_gpu_step import _oracle_check, _run_case
+
+import sparse_kv_cache_append_amd as skv
+
+pytestmark = pytest.mark.gpu
+
+DIMS = [64, 256]
+F16_TOL = 1e-3
+I8_TOL = 1e-4
+
+
+def _print(*a):
+    print("[head dims]", *a, flush=True)
+
+
+@pytest.mark.parametrize("D", DIMS)
+@pytest.mark.parametrize("kv", ["f16", "i8"])
+def test_append_exact(gpu_lib, D, kv):
+    """Chunked appends (a block that straddles each chunk edge) against the
+    oracle's rows, codes, scales and block bounds."""
+    _print("append", D, kv)
+    L = 300
+    w = workloads.clustered([801, 802], 8, 2, D, [L, L], kv, n_dirs=8)
+    cache = skv.Cache(2, 2, 320, D, kv, 64, device=DEV)
+    k, v = padded_rows(w, L)
+    kt, vt = torch.from_numpy(k).to(DEV), torch.from_numpy(v).to(DEV)
+    p0 = 0
+    for n in [37, 27, 64, 1, 99, 72]:
+        pos0 = torch.full((2,), p0, dtype=torch.int32, device=DEV)
+        skv.kv_append(cache, pos0, kt[:, p0:p0 + n].contiguous(), vt[:, p0:p0 + n].contiguous())
+        p0 += n
+    torch.cuda.synchronize()
+    for b in range(2):
+        if kv == "f16":
+            assert np.array_equal(cache.k.cpu().numpy()[b, :, :L].view(np.uint16),
+                                  w.k[b].view(np.uint16))
+            assert np.array_equal(cache.v.cpu().numpy()[b, :, :L].view(np.uint16),
+                                  w.v[b].view(np.uint16))
+        else:
+            kc, ks, vc, vs = quantized_host(w, b)
+            assert np.array_equal(cache.k.cpu().numpy()[b, :, :L], kc)
+            assert np.array_equal(cache.v.cpu().numpy()[b, :, :L], vc)
+            assert np.array_equal(cache.k_scale.cpu().numpy()[b, :, :L].view(np.uint32),
+                                  ks.view(np.uint32))
+            assert np.array_equal(cache.v_scale.cpu().numpy()[b, :, :L].view(np.uint32),
+                                  vs.view(np.uint32))
+        kmin, kmax = oracle.block_bounds(w.k[b], L, 64)
+        assert np.array_equal(cache.kmin.cpu().numpy()[b, :, :5], kmin)
+        assert np.array_equal(cache.kmax.cpu().numpy()[b, :, :5], kmax)
+
+
+DENSE = [
+    # (B, H, Hkv, lens, n_split)
+    (2, 8, 2, [130, 777], None),
+    (1, 32, 8, [2049], 7),
+    (3, 16, 16, [1, 333, 64], None),
+    (1, 8, 1, [1000], 3),
+    (2, 16, 8, [17, 1500], 1),
+]
+
+
+@pytest.mark.parametrize("D", DIMS)
+@pytest.mark.parametrize("kv", ["f16", "i8"])
+@pytest.mark.parametrize("B,H,Hkv,lens,S", DENSE)
+def test_dense(gpu_lib, D, kv, B, H, Hkv, lens, S):
+    _print("dense", D, kv, B, H, Hkv, lens, S)
+    w = workloads.gaussian(811 + D + sum(lens), B, H, Hkv, D, lens, kv)
+    cache = build_cache(w)
+    out, dbg = run_dense(cache, w, S, dbg=kv == "i8")
+    for b in range(B):
+        if kv == "f16":
+            ref = oracle.attend_f16(w.q[b], w.k[b], w.v[b], w.softmax_scale)
+            assert_close(out[b], ref, F16_TOL, b)
+        else:
+            kc, ks, vc, vs = quantized_host(w, b)
+            dots, _, _ = oracle.int8_logit_dots(w.q[b], kc)
+            assert np.array_equal(dbg[b, :, :lens[b]].astype(np.int64), dots), b
+            meth = oracle.attend_i8(w.q[b], kc, ks, vc, vs, w.softmax_scale)
+            assert_close(out[b], meth, I8_TOL, b)
+
+
+def test_zero_query_gives_mean_of_values(gpu_lib):
+    _print("q = 0")
+    for D in DIMS:
+        for kv in ("f16", "i8"):
+            w = workloads.gaussian(820 + D, 1, 8, 2, D, [700], kv)
+            w.q[:] = 0
+            cache = build_cache(w)
+            out, _ = run_dense(cache, w)
+            if kv == "f16":
+                ref = w.v[0].astype(np.float64).mean(axis=1)
+            else:
+                _, _, vc, vs = quantized_host(w, 0)
+                ref = (vc.astype(np.float64) * vs.astype(np.float64)[..., None]).mean(axis=1)
+            for h in range(8):
+                assert_close(out[0, h], ref[h // 4], 1e-6, D, kv, h)
+
+
+QUEST = [
+    # (seeds, H, Hkv, lens, kv, k_sel, n_sink, n_recent)
+    ([831, 832], 32, 8, [3000, 4097], "f16", [10, 12], 1, 2),
+    ([833], 32, 4, [5001], "i8", [20], 1, 4),
+    ([834, 835], 16, 8, [65, 2000], "f16", [0, 7], 2, 1),
+    ([836], 8, 8, [1500], "i8", [6], 1, 2),
+]
+
+
+@pytest.mark.parametrize("D", DIMS)
+@pytest.mark.parametrize("seeds,H,Hkv,lens,kv,k_sel,ns,nr", QUEST)
+def test_quest_bounds_selection_attention(gpu_lib, D, seeds, H, Hkv, lens, kv, k_sel, ns, nr):
+    _print("quest", D, lens, kv, k_sel)
+    w = workloads.clustered(seeds, H, Hkv, D, lens, kv, n_dirs=16, k_sel=k_sel, n_sink=ns,
+                            n_recent=nr)
+    cache = build_cache(w)
+    score, sel, cnt, _ = run_select(cache, w)
+    sel_h, cnt_h = sel.cpu().numpy(), cnt.cpu().numpy()
+    G = H // Hkv
+    out = run_sparse(cache, w, sel, cnt)
+    for b in range(w.B):
+        nb = w.n_blocks(b)
+        kmin, kmax = oracle.block_bounds(w.k[b], w.lens[b], w.block)
+        ref = oracle.group_scores(oracle.upper_bounds(w.q[b], kmin, kmax), Hkv)
+        np.testing.assert_allclose(score[b, :, :nb], ref, rtol=2e-6, atol=1e-4)
+        for g in range(Hkv):
+            own = oracle.select_blocks(score[b, g], nb, k_sel[b], ns, nr)["sel"]
+            got = sel_h[b, g, :cnt_h[b, g]]
+            assert np.array_equal(got, own), (b, g)
+            toks = oracle.selected_tokens(got, w.lens[b], w.block)
+            hs = slice(g * G, (g + 1) * G)
+            if kv == "f16":
+                r = oracle.attend_f16(w.q[b][hs], w.k[b][g:g + 1], w.v[b][g:g + 1],
+                                      w.softmax_scale, tokens=toks)
+                assert_close(out[b, hs], r, F16_TOL, b, g)
+            else:
+                kc, ks, vc, vs = quantized_host(w, b)
+                sl = slice(g, g + 1)
+                r = oracle.attend_i8(w.q[b][hs], kc[sl], ks[sl], vc[sl], vs[sl],
+                                     w.softmax_scale, tokens=toks)
+                assert_close(out[b, hs], r, I8_TOL, b, g)
+
+
+STEP = [
+    # name, factory(D), quest, append, extra
+    ("quest-f16", lambda D: workloads.clustered(
+        [841, 842], 32, 8, D, [2049, 3000], "f16", n_dirs=16, k_sel=[8, 20], n_sink=1,
+        n_recent=2), True, True, {}),
+    ("quest-i8 G8", lambda D: workloads.clustered(
+        [843], 32, 4, D, [5000], "i8", n_dirs=16, k_sel=[30], n_sink=1, n_recent=4),
+        True, True, {}),
+    ("quest-f16 selection as its own kernel", lambda D: workloads.clustered(
+        [844], 16, 8, D, [9000], "f16", n_dirs=16, k_sel=[60], n_sink=1, n_recent=2),
+        True, True, {"S": 1}),
+    ("dense-f16 append poisoned rows", lambda D: workloads.gaussian(
+        845, 2, 32, 8, D, [65, 2000], "f16"), False, True, {"poison": True}),
+    ("dense-i8 append poisoned rows G2", lambda D: workloads.gaussian(
+        846, 2, 16, 8, D, [1025, 300], "i8"), False, True, {"poison": True, "S": 5}),
+    ("dense-i8 first token of an empty cache", lambda D: workloads.gaussian(
+        847, 1, 32, 4, D, [1], "i8"), False, True, {"lag": 1, "tight": True}),
+]
+
+
+@pytest.mark.parametrize("D", DIMS)
+@pytest.mark.parametrize("name,make,quest,append,extra", STEP, ids=[c[0] for c in STEP])
+def test_decode_step_equals_composed_calls(gpu_lib, D, name, make, quest, append, extra):
+    """At these head dims the step runs the append as its own kernel (the
+    folded appends move head dim 128 rows); still bit-identical to the five
+    calls."""
+    _print("step", D, name)
+    w = make(D)
+    out, sel = _run_case(w, quest, append, **extra)
+    if not extra.get("lag"):
+        _oracle_check(w, out, sel)
+
+
+@pytest.mark.parametrize("D", DIMS)
+@pytest.mark.parametrize("kv", ["f16", "i8"])
+def test_decode_attn_select_equals_select_then_decode(gpu_lib, D, kv):
+    _print("decode_attn_select", D, kv)
+    L = 9000
+    w = workloads.clustered([850], 32, 8, D, [L], kv, n_dirs=32, k_sel=[(-(-L // 64)) // 4],
+                            n_sink=1, n_recent=2)
+    cache = build_cache(w)
+    q = torch.from_numpy(np.ascontiguousarray(w.q)).to(DEV)
+    seq_len = torch.tensor(w.lens, dtype=torch.int32, device=DEV)
+    ks = torch.tensor(w.k_sel, dtype=torch.int32, device=DEV)
+    max_sel = w.k_sel[0] + 3
+    S = 16
+    ws_a = torch.zeros(skv.workspace_bytes(1, 32, D, S), dtype=torch.uint8, device=DEV)
+    ws_b = torch.full_like(ws_a, 255)
+    score = torch.full((1, 8, cache.max_blocks), float("nan"), device=DEV)
+    sel_a = torch.full((1, 8, max_sel), -7, dtype=torch.int32, device=DEV)
+    sel_b = sel_a.clone()
+    cnt_a = torch.full((1, 8), -7, dtype=torch.int32, device=DEV)
+    cnt_b = cnt_a.clone()
+    skv.block_bounds(cache, q, seq_len, L, score)
+    skv.select_topk(score, seq_len, w.block, ks, w.n_sink, w.n_recent, sel_a, cnt_a)
+    skv.decode_attn(cache, q, seq_len, L, w.softmax_scale, S, ws_a, sel_a, cnt_a)
+    skv.decode_attn_select(cache, q, seq_len, L, w.softmax_scale, S, ws_b, score, ks, w.n_sink,
+                           w.n_recent, sel_b, cnt_b)
+    torch.cuda.synchronize()
+    assert torch.equal(sel_a, sel_b) and torch.equal(cnt_a, cnt_b)
+    assert torch.equal(ws_a, ws_b)
+
+
+def test_other_head_dims_are_refused(gpu_lib):
+    """Head dim 96 (a multiple of 16, not built) and the calls built for 128
+    only raise SKV_EUNSUPPORTED before any launch."""
+    _print("refused")
+    c96 = skv.Cache(1, 2, 128, 96, "f16", 64, device=DEV)
+    q = torch.zeros((1, 8, 96), dtype=torch.float32, device=DEV)
+    sl = torch.tensor([10], dtype=torch.int32, device=DEV)
+    score = torch.empty((1, 2, c96.max_blocks), dtype=torch.float32, device=DEV)
+    with pytest.raises(skv.SkvError) as e:
+        skv.block_bounds(c96, q, sl, 10, score)
+    assert e.value.status == skv.SKV_EUNSUPPORTED
+    c64 = skv.Cache(1, 2, 128, 64, "f16", 64, device=DEV)
+    q = torch.zeros((1, 8, 64), dtype=torch.float32, device=DEV)
+    score = torch.empty((1, 8, c64.max_blocks), dtype=torch.float32, device=DEV)
+    with pytest.raises(skv.SkvError) as e:
+        skv.block_bounds_heads(c64, q, sl, 10, score)
+    assert e.value.status == skv.SKV_EUNSUPPORTED
+    torch.cuda.synchronize()

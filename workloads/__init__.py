@@ -200,6 +200,14 @@ def quest32k_at(L: int) -> Workload:
                      k_sel=[nb // 4], n_sink=1, n_recent=2)
 
 
+def quest32k_dim(D: int) -> Workload:
+    """The 32K Quest workload's generator (H=32, Hkv=8, 64 directions, block
+    64, K_SEL=128, sink 1, recent 2, seed 1003, f16) at head dim D."""
+    return clustered([1003], 32, 8, D, [32768], "f16", n_dirs=64,
+                     name=f"quest-f16 B1 H32/Hkv8 D{D} L32768 K_SEL128 sink1 recent2",
+                     k_sel=[128], n_sink=1, n_recent=2)
+
+
 def chunk_queries(w: Workload, T: int, seed: int, noise: float = 1.5) -> np.ndarray:
     """Queries of a chunk of T tokens per sequence, [B][T][H][D] float32:
     token 0 is the workload's own query, token t > 0 that query plus
