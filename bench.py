@@ -106,8 +106,8 @@ def step_bytes(lens, Hkv, H, D, kv_dtype, block, attended_blocks=None):
 # ------------------------------------------------------------- HBM traffic
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic_quest32k.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "sparse_kv_cache_append_amd", "csrc", f)
-                  for f in ("decode_mfma.hip", "decode_core.h", "device_common.h", "launch.h",
-                            "select_core.h")]
+                  for f in ("decode_kernels.h", "decode_mfma.hip", "decode_core.h",
+                            "device_common.h", "launch.h", "select_core.h", "fused_walk.h")]
 
 
 def kernel_source_digest() -> str:

@@ -1,4 +1,5 @@
-// Shared pieces of the attention kernels (decode_mfma.hip, sparse_v.hip):
+// Shared pieces of the attention kernels (decode_kernels.h, sparse_v.hip,
+// decode_grouped.hip):
 // vector types, the 16-byte tile loads through per-tile buffer resources, the
 // MFMA wrappers, the wave-uniform tile walk over a part's blocks (or its
 // share of a selected list) and the exact int8 -> f16 widening of V codes.

@@ -1,4 +1,4 @@
-// The block selection in the prologue of an attention kernel (decode_mfma.hip
+// The block selection in the prologue of an attention kernel (decode_kernels.h
 // and decode_grouped.hip): every part of a (sequence, KV head) row computes
 // the row's top-K with the select kernel's own code (select_core.h) and walks
 // its slice of the ascending list.  Included by the .hip sources only;
