@@ -29,9 +29,10 @@
 //     times the (token, group) V scale in a running power-of-two unit, split
 //     into f16 high + low parts per group (each 16-channel MFMA block lies in
 //     one group);
-//   q4_0 tiles arrive as nibbles (half the bytes) and are widened to int8
-//     codes in registers before the LDS stage, so both formats share the
-//     LDS layout and the arithmetic.
+//   q4_0 tiles arrive as nibbles (half the bytes) and are spread to one
+//     byte each (code + 8) in registers before the LDS stage, so both formats
+//     share the LDS layout and the transposing reads; the bias comes off in
+//     the exact widening to f16.
 #include <type_traits>
 
 #include "decode_core.h"
@@ -129,22 +130,48 @@ append_grp_kernel(uint8_t* __restrict__ kc, uint8_t* __restrict__ vc,
 
 // ------------------------------------------------------------------ decode
 // 32 nibble codes (16 bytes: byte i = channels 2i, 2i + 1, each code + 8) to
-// 32 int8 codes in channel order.
+// 32 bytes in channel order, still biased (code + 8, 0..15): the bias comes
+// off in the widening to f16 (widen_q4), in the same packed subtraction.
 __device__ __forceinline__ void unpack_q4(const int4_t& w, int4_t& c0, int4_t& c1) {
   uint32_t o[8];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const uint32_t x = uint32_t(w[i]);
     const uint32_t lo = x & 0x0F0F0F0Fu, hi = (x >> 4) & 0x0F0F0F0Fu;
-    // (lo0, hi0, lo1, hi1) and (lo2, hi2, lo3, hi3); then n - 8 per byte as
-    // (n + 120) ^ 128 (no carry: n + 120 < 256)
-    const uint32_t a = __builtin_amdgcn_perm(hi, lo, 0x05010400u);
-    const uint32_t b = __builtin_amdgcn_perm(hi, lo, 0x07030602u);
-    o[2 * i] = (a + 0x78787878u) ^ 0x80808080u;
-    o[2 * i + 1] = (b + 0x78787878u) ^ 0x80808080u;
+    // (lo0, hi0, lo1, hi1) and (lo2, hi2, lo3, hi3)
+    o[2 * i] = __builtin_amdgcn_perm(hi, lo, 0x05010400u);
+    o[2 * i + 1] = __builtin_amdgcn_perm(hi, lo, 0x07030602u);
   }
   c0 = int4_t{int(o[0]), int(o[1]), int(o[2]), int(o[3])};
   c1 = int4_t{int(o[4]), int(o[5]), int(o[6]), int(o[7])};
+}
+
+// 8 biased q4_0 bytes n = code + 8 to the f16 codes, exactly: each byte goes
+// under a 0x64 high byte (f16 1024 + n), minus 1032.
+__device__ __forceinline__ half8_t widen_q4(int2_t w) {
+  typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+  constexpr uint32_t kLoSel = 0x04010400u;   // (0x64, x1, 0x64, x0)
+  constexpr uint32_t kHiSel = 0x04030402u;   // (0x64, x3, 0x64, x2)
+  const half2_t off = half2_t{(_Float16)1032.0f, (_Float16)1032.0f};
+  half8_t r;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const uint32_t x = uint32_t(w[k]);
+    const half2_t a = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0x64646464u, x, kLoSel)) - off;
+    const half2_t b = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0x64646464u, x, kHiSel)) - off;
+    r[4 * k + 0] = a[0];
+    r[4 * k + 1] = a[1];
+    r[4 * k + 2] = b[0];
+    r[4 * k + 3] = b[1];
+  }
+  return r;
+}
+
+// The LDS codes of a tile as f16: q4_0 biased bytes or q8_0 int8 codes.
+template <bool Q4>
+__device__ __forceinline__ half8_t widen_grp(int2_t w) {
+  if constexpr (Q4) return widen_q4(w);
+  else return widen_codes(w);
 }
 
 constexpr int kPwShiftGrp = 7;
@@ -307,7 +334,7 @@ decode_grp_mfma(const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
         const int rw = 16 * s + lc;
         const int2_t raw = *reinterpret_cast<const int2_t*>(kt + sw(rw, 2 * kk + lg / 2) +
                                                             8 * (lg & 1));
-        const half8_t a = widen_codes(raw);
+        const half8_t a = widen_grp<Q4>(raw);
         acc[kk] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
         acc[kk] = mfma_f16_32(a, qhi[kk], acc[kk]);
         acc[kk] = mfma_f16_32(a, qlo[kk], acc[kk]);
@@ -350,7 +377,7 @@ decode_grp_mfma(const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
         const int n = 2 * grp + nn;
         const int off = sw(tr_row, n) + 8 * (lc & 1);
         const int2_t raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32((SKV_LDS int2_t*)(vt + off));
-        const half8_t bv = widen_codes(raw);
+        const half8_t bv = widen_grp<Q4>(raw);
         O[n] = mfma_f16_32(phi, bv, O[n]);
         O[n] = mfma_f16_32(plo, bv, O[n]);
       }
