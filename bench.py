@@ -59,12 +59,13 @@ LLC_BYTES = 256 * 2 ** 20
 def kv_bytes_per_token(kv_dtype: str, D: int) -> int:
     """Algorithmic bytes of one attended (token, KV head): K and V rows, plus
     the two float32 scales for int8, or the f16 scale of every 32-channel
-    group of both rows for q8_0 (int8 codes) and q4_0 (4-bit codes)."""
+    group of both rows for q8_0 (int8 codes), q4_0 (4-bit codes) and q5_0
+    (5-bit codes: a nibble plane plus a plane of fifth bits)."""
     if kv_dtype == "f16":
         return 4 * D
     if kv_dtype == "i8":
         return 2 * D + 8
-    codes = D if kv_dtype == "q8_0" else D // 2
+    codes = {"q8_0": D, "q4_0": D // 2, "q5_0": D // 2 + D // 8}[kv_dtype]
     return 2 * (codes + 2 * (D // 32))
 
 
@@ -190,8 +191,9 @@ class OracleStep:
                 kc, ks = oracle.quantize_rows(w.k[b])
                 vc, vs = oracle.quantize_rows(w.v[b])
                 self.codes[b] = (kc, ks, vc, vs)
-            elif w.kv_dtype in ("q8_0", "q4_0"):
-                qmax = oracle.QMAX_Q8 if w.kv_dtype == "q8_0" else oracle.QMAX_Q4
+            elif w.kv_dtype in ("q8_0", "q4_0", "q5_0"):
+                qmax = {"q8_0": oracle.QMAX_Q8, "q4_0": oracle.QMAX_Q4,
+                        "q5_0": oracle.QMAX_Q5}[w.kv_dtype]
                 kc, ks = oracle.quantize_groups(w.k[b], qmax)
                 vc, vs = oracle.quantize_groups(w.v[b], qmax)
                 self.codes[b] = (kc, ks, vc, vs)
@@ -549,7 +551,7 @@ def measure(w, args, quest: bool, dense: bool, detail: bool = False):
             res["quest"]["warm_us_per_step"] = round(warm, 3)
         if detail:
             res["_roofline"] = (dec_bytes, sel_us, dec_us)
-        grouped = w.kv_dtype in ("q8_0", "q4_0")      # per-head and sparse-V: f16 and int8
+        grouped = w.kv_dtype in ("q8_0", "q4_0", "q5_0")   # per-head and sparse-V: f16, int8
         other_dim = w.D != 128       # the NEXT rows' calls are built for head dim 128
         if not args.no_per_head and not grouped and not other_dim:
             res["quest_per_head"] = measure_per_head(T, skv, torch, w, caches, R, q, seq_len, Lmax,
@@ -815,10 +817,10 @@ def main():
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--mode", choices=("both", "quest", "dense"), default="both",
                     help="which step of the 32K workload to time (profiling runs use one)")
-    ap.add_argument("--workloads", default="1,2,4,5,3@16384,3q8,3q4,3d64,3d256",
+    ap.add_argument("--workloads", default="1,2,4,5,3@16384,3q8,3q4,3q5,3d64,3d256",
                     help="other workloads to time besides the 32K headline ('' = none; "
-                         "3@L = the 32K Quest generator at context L; 3q8 / 3q4 = over a "
-                         "q8_0 / q4_0 cache; 3d64 / 3d256 = at head dim 64 / 256)")
+                         "3@L = the 32K Quest generator at context L; 3q8 / 3q4 / 3q5 = over a "
+                         "q8_0 / q4_0 / q5_0 cache; 3d64 / 3d256 = at head dim 64 / 256)")
     ap.add_argument("--chunk-tokens", type=int, default=4,
                     help="query tokens per chunk for the multi-token measurement (0 = off)")
     ap.add_argument("--no-per-head", action="store_true",
@@ -852,8 +854,9 @@ def main():
             # the 32K generator at another head dim (3d64, 3d256)
             jobs.append((workloads.quest32k_dim(int(tok[2:])), True, True, False))
         elif tok.startswith("3q"):
-            # the 32K generator over a group-wise quantized cache (3q8, 3q4)
-            jobs.append((workloads.quest32k_quant("q8_0" if tok == "3q8" else "q4_0"), True,
+            # the 32K generator over a group-wise quantized cache (3q8, 3q4, 3q5)
+            jobs.append((workloads.quest32k_quant({"3q8": "q8_0", "3q4": "q4_0",
+                                                   "3q5": "q5_0"}[tok]), True,
                          True, False))
         elif int(tok) != 3:
             w = workloads.named(int(tok))

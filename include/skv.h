@@ -74,7 +74,8 @@ typedef enum skv_dtype {
   SKV_F32 = 2,
   SKV_I8 = 3,
   SKV_Q8_0 = 4,   /* group-wise: 32-channel groups, int8 codes, an f16 scale each */
-  SKV_Q4_0 = 5    /* group-wise: 32-channel groups, 4-bit codes, an f16 scale each */
+  SKV_Q4_0 = 5,   /* group-wise: 32-channel groups, 4-bit codes, an f16 scale each */
+  SKV_Q5_0 = 6    /* group-wise: 32-channel groups, 5-bit codes, an f16 scale each */
 } skv_dtype;
 
 /*
@@ -90,18 +91,25 @@ typedef enum skv_dtype {
  *               before quantization (sparse_attn.md, "Method" and
  *               "All-KV-types composition").  Both NULL = no side cache
  *               (dense only; appends then skip the bounds update).
- * Group-wise quantized caches (SKV_Q8_0, SKV_Q4_0; sparse_attn.md, "All-KV-
- * types composition": quantized blocks of 32 values with the side cache
- * filled before quantization):
+ * Group-wise quantized caches (SKV_Q8_0, SKV_Q4_0, SKV_Q5_0; sparse_attn.md,
+ * "All-KV-types composition": quantized blocks of 32 values with the side
+ * cache filled before quantization; "Method: Quest-style min/max block
+ * bounds" names q5_0 and q4_0):
  *   k, v      : [batch][n_kv_heads][max_seq][row] bytes, row = head_dim
  *               (q8_0: int8 codes -127..127) or head_dim / 2 (q4_0: channel
  *               2i in the low nibble of byte i, 2i + 1 in the high nibble,
  *               each code + 8, codes -7..7);
+ *               q5_0 (codes -15..15, each stored as code + 16 in five bits):
+ *               [batch][n_kv_heads][max_seq * 5 head_dim / 8] bytes, each
+ *               (sequence, KV head) holding a plane of max_seq rows of
+ *               head_dim / 2 bytes (bits 0..3, laid out as q4_0) followed by
+ *               a plane of max_seq rows of head_dim / 8 bytes (bit 4 of
+ *               channel c at bit c % 8 of byte c / 8);
  *   k_scale,
  *   v_scale   : f16 bit patterns (uint16_t storage behind the float*
  *               pointers) [batch][n_kv_heads][max_seq][head_dim / 32], the
  *               scale of each group of 32 consecutive channels.
- *   Per group: a = max |x|, scale = f16(a / QMAX) (QMAX 127 or 7), code =
+ *   Per group: a = max |x|, scale = f16(a / QMAX) (QMAX 127, 7 or 15), code =
  *   clamp(rint(x / scale), -QMAX, QMAX) against the stored scale (a scale of
  *   0, or beyond f16's range, gives codes 0); a value is scale * code, and
  *   attention runs on those values with the float32 query.

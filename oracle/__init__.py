@@ -22,7 +22,7 @@ Conventions
 Modules
 -------
 ``quant``      absmax int8 quantization (per row, and per 32-channel group for
-               the q8_0 / q4_0 caches), directed float32 -> float16 rounding
+               the q8_0 / q4_0 / q5_0 caches), directed float32 -> float16 rounding
 ``attention``  dense f16 / int8 (method-exact and dequantized-reference) attention,
                exact int32 logit dots, split-K combine
 ``quest``      per-block kmin/kmax side cache, channel-wise upper bound,
@@ -42,7 +42,7 @@ the reading that forced blocks are excluded from the top-K candidates.
 """
 from . import quant, attention, quest, sparse_v, scan4, multi_token  # noqa: F401
 from .quant import (quantize_rows, f16_round_down, f16_round_up,  # noqa: F401
-                    quantize_groups, dequantize_groups, QMAX_Q8, QMAX_Q4)
+                    quantize_groups, dequantize_groups, QMAX_Q8, QMAX_Q4, QMAX_Q5)
 from .attention import (attend_f16, attend_i8, attend_i8_dequant, attend_grouped,  # noqa: F401
                         int8_logit_dots, combine_partials, softmax_partials)
 from .quest import (block_bounds, upper_bounds, group_scores, select_blocks,  # noqa: F401

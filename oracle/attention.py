@@ -153,7 +153,7 @@ def combine_partials(m: np.ndarray, l: np.ndarray, a: np.ndarray, base: float = 
 
 
 def attend_grouped(q, k_codes, k_scales, v_codes, v_scales, scale, tokens=None):
-    """Attention over a group-wise quantized cache (q8_0 / q4_0): the
+    """Attention over a group-wise quantized cache (q8_0 / q4_0 / q5_0): the
     definition applied to the dequantized values scale * code (exact in
     float64), the query unquantized.  codes [Hkv][L][D] int8, scales
     [Hkv][L][D / 32] float16.  Returns [H][D] float64."""

@@ -66,7 +66,11 @@ def f16_round_up(x: np.ndarray) -> np.ndarray:
 # a row.  Readings taken (the pages name the formats, not their arithmetic):
 # * a group is 32 consecutive channels of one (token, KV head) row;
 # * symmetric absmax per group, the int8 card's rule with QMAX levels each
-#   side: q8_0 QMAX = 127, q4_0 QMAX = 7 (codes -7..7, stored as a nibble);
+#   side: q8_0 QMAX = 127, q4_0 QMAX = 7 (codes -7..7, stored as a nibble),
+#   q5_0 QMAX = 15 (codes -15..15, five bits stored; sparse_attn.md names
+#   q5_0 with q4_0 as the quantized caches the bounds compose with, "Method:
+#   Quest-style min/max block bounds", and gives their block size 32, "Open
+#   questions");
 # * the scale is stored as f16: s = fl16(fl32(a / QMAX)); the codes are taken
 #   against that stored scale, code = clamp(rint(fl32(x / s)), -QMAX, QMAX),
 #   so a value is represented exactly as s * code; s == 0 (a zero group, or
@@ -76,6 +80,7 @@ def f16_round_up(x: np.ndarray) -> np.ndarray:
 GROUP = 32
 QMAX_Q8 = 127
 QMAX_Q4 = 7
+QMAX_Q5 = 15
 
 
 def quantize_groups(x: np.ndarray, qmax: int):

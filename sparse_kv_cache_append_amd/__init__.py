@@ -29,13 +29,15 @@ __all__ = ["load", "Cache", "SkvError", "kv_append", "block_bounds", "select_top
            "select_topk_multi", "select_union_tokens", "decode_attn_multi", "Scan4Index",
            "scan4_build", "scan4_candidates", "scan4_workspace_bytes", "scan4_default_split",
            "decode_step", "decode_step_static", "combine", "workspace_bytes", "status_str", "decode",
-           "SKV_F16", "SKV_F32", "SKV_I8", "SKV_Q8_0", "SKV_Q4_0", "LIB_PATH", "EXPORTS"]
+           "SKV_F16", "SKV_F32", "SKV_I8", "SKV_Q8_0", "SKV_Q4_0", "SKV_Q5_0", "LIB_PATH",
+           "EXPORTS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libskv.so")
 
 SKV_OK, SKV_EINVAL, SKV_ERANGE, SKV_EWORKSPACE, SKV_EUNSUPPORTED, SKV_EDEVICE = 0, -1, -2, -3, -4, -5
-SKV_F16, SKV_F32, SKV_I8, SKV_Q8_0, SKV_Q4_0 = 1, 2, 3, 4, 5
-_KV_CODES = {"f16": SKV_F16, "i8": SKV_I8, "q8_0": SKV_Q8_0, "q4_0": SKV_Q4_0}
+SKV_F16, SKV_F32, SKV_I8, SKV_Q8_0, SKV_Q4_0, SKV_Q5_0 = 1, 2, 3, 4, 5, 6
+_KV_CODES = {"f16": SKV_F16, "i8": SKV_I8, "q8_0": SKV_Q8_0, "q4_0": SKV_Q4_0, "q5_0": SKV_Q5_0}
+_GROUPED = ("q8_0", "q4_0", "q5_0")
 
 EXPORTS = ("skv_max_blocks", "skv_kv_append", "skv_block_bounds", "skv_select_topk",
            "skv_decode_attn", "skv_decode_attn_select", "skv_decode_step",
@@ -214,10 +216,12 @@ class Cache:
     kv_dtype "f16": k, v [batch][n_kv_heads][max_seq][head_dim] float16.
     kv_dtype "i8": k, v int8 codes, same shape; k_scale, v_scale
     [batch][n_kv_heads][max_seq] float32.
-    kv_dtype "q8_0" / "q4_0" (groups of 32 channels): k, v uint8
+    kv_dtype "q8_0" / "q4_0" / "q5_0" (groups of 32 channels): k, v uint8
     [batch][n_kv_heads][max_seq][head_dim] (q8_0 int8 codes) or [...][head_dim
-    / 2] (q4_0 nibbles); k_scale, v_scale float16 [batch][n_kv_heads][max_seq]
-    [head_dim / 32].
+    / 2] (q4_0 nibbles) or [batch][n_kv_heads][max_seq * 5 head_dim / 8]
+    (q5_0: the nibble plane [max_seq][head_dim / 2], then the fifth-bit plane
+    [max_seq][head_dim / 8]; ``q5_planes`` gives both views); k_scale,
+    v_scale float16 [batch][n_kv_heads][max_seq][head_dim / 32].
     kmin, kmax: [batch][n_kv_heads][max_blocks][head_dim] float16 (Quest side
     cache, allocated when ``bounds``)."""
 
@@ -225,12 +229,16 @@ class Cache:
                  kv_dtype: str = "f16", block: int = 64, bounds: bool = True, device="cuda"):
         import torch
         if kv_dtype not in _KV_CODES:
-            raise ValueError("kv_dtype must be 'f16', 'i8', 'q8_0' or 'q4_0'")
+            raise ValueError("kv_dtype must be 'f16', 'i8', 'q8_0', 'q4_0' or 'q5_0'")
         self.batch, self.n_kv_heads, self.max_seq = batch, n_kv_heads, max_seq
         self.head_dim, self.block, self.kv_dtype = head_dim, block, kv_dtype
         self.max_blocks = -(-max_seq // block)
         shape = (batch, n_kv_heads, max_seq, head_dim)
-        if kv_dtype in ("q8_0", "q4_0"):
+        if kv_dtype == "q5_0":
+            per = max_seq * (head_dim // 2 + head_dim // 8)
+            self.k = torch.zeros(shape[:2] + (per,), dtype=torch.uint8, device=device)
+            self.v = torch.zeros(shape[:2] + (per,), dtype=torch.uint8, device=device)
+        elif kv_dtype in ("q8_0", "q4_0"):
             row = head_dim if kv_dtype == "q8_0" else head_dim // 2
             self.k = torch.zeros(shape[:3] + (row,), dtype=torch.uint8, device=device)
             self.v = torch.zeros(shape[:3] + (row,), dtype=torch.uint8, device=device)
@@ -242,7 +250,7 @@ class Cache:
         if kv_dtype == "i8":
             self.k_scale = torch.zeros(shape[:3], dtype=torch.float32, device=device)
             self.v_scale = torch.zeros(shape[:3], dtype=torch.float32, device=device)
-        elif kv_dtype in ("q8_0", "q4_0"):
+        elif kv_dtype in _GROUPED:
             gshape = shape[:3] + (head_dim // 32,)
             self.k_scale = torch.zeros(gshape, dtype=torch.float16, device=device)
             self.v_scale = torch.zeros(gshape, dtype=torch.float16, device=device)
@@ -254,6 +262,15 @@ class Cache:
         self.desc = SkvCacheDesc(batch, n_kv_heads, head_dim, max_seq, block, _KV_CODES[kv_dtype],
                                  _ptr(self.k), _ptr(self.v), _ptr(self.k_scale),
                                  _ptr(self.v_scale), _ptr(self.kmin), _ptr(self.kmax))
+
+    def q5_planes(self, t):
+        """The two planes of a q5_0 code tensor (self.k or self.v): the nibble
+        plane [batch][n_kv_heads][max_seq][head_dim / 2] and the fifth-bit
+        plane [batch][n_kv_heads][max_seq][head_dim / 8] (views)."""
+        n = self.max_seq * (self.head_dim // 2)
+        lo = t[:, :, :n].unflatten(2, (self.max_seq, self.head_dim // 2))
+        hi = t[:, :, n:].unflatten(2, (self.max_seq, self.head_dim // 8))
+        return lo, hi
 
     def src_dtype(self) -> int:
         return SKV_F16 if self.kv_dtype == "f16" else SKV_F32
@@ -663,7 +680,7 @@ def default_split(batch: int, n_kv_heads: int, n_units: int, target_wgs: Optiona
     if target_wgs is None:
         target_wgs = 256
         two = math.ceil(512 / max(1, batch * n_kv_heads))
-        if kv_dtype in ("i8", "q4_0") and not sparse and n_units >= 4 * two:
+        if kv_dtype in ("i8", "q4_0", "q5_0") and not sparse and n_units >= 4 * two:
             target_wgs = 512
     n = max(1, math.ceil(target_wgs / max(1, batch * n_kv_heads)))
     return int(max(1, min(n, n_units, 4096)))

@@ -27,20 +27,42 @@ constexpr int kBoundsThreads = 256;
 constexpr int kLanesPerBlock = 16;
 constexpr int kBlocksPerWG = kBoundsThreads / kLanesPerBlock;  // 16
 
-enum AppendMode { kNoAppend = 0, kAppendF16 = 1, kAppendI8 = 2, kAppendQ8 = 3, kAppendQ4 = 4 };
+enum AppendMode {
+  kNoAppend = 0, kAppendF16 = 1, kAppendI8 = 2, kAppendQ8 = 3, kAppendQ4 = 4, kAppendQ5 = 5
+};
+constexpr bool is_grp_mode(int mode) {
+  return mode == kAppendQ8 || mode == kAppendQ4 || mode == kAppendQ5;
+}
 
-// Group-wise caches (q8_0 / q4_0): 32-channel groups with an f16 scale each,
-// the append kernel's arithmetic (decode_grouped.hip): s = f16(absmax / QMAX),
-// code = clamp(rint(x / s), -QMAX, QMAX) against the stored scale (0 when s is
-// 0 or not finite); q4_0 stores code + 8, channels 2i / 2i + 1 in the low /
-// high nibble of byte i.
+// Group-wise caches (q8_0 / q4_0 / q5_0): 32-channel groups with an f16 scale
+// each, the append kernel's arithmetic (decode_grouped.hip):
+// s = f16(absmax / QMAX), code = clamp(rint(x / s), -QMAX, QMAX) against the
+// stored scale (0 when s is 0 or not finite); q4_0 stores code + 8, channels
+// 2i / 2i + 1 in the low / high nibble of byte i; q5_0 stores code + 16, its
+// low four bits as q4_0 in a nibble plane and bit 4 in a plane of its own
+// (bit c % 8 of byte c / 8), the planes one after the other per (sequence,
+// KV head).
 constexpr int kGrpChannels = 32;
 template <int MODE>
 struct GrpMode {
-  static constexpr bool kQ4 = MODE == kAppendQ4;
-  static constexpr int kQmax = kQ4 ? 7 : 127;
-  static constexpr int kRowBytes = kQ4 ? 64 : 128;
+  static constexpr bool kNib = MODE != kAppendQ8;
+  static constexpr bool kQ5 = MODE == kAppendQ5;
+  static constexpr int kQmax = MODE == kAppendQ8 ? 127 : MODE == kAppendQ4 ? 7 : 15;
+  static constexpr int kBias = kNib ? kQmax + 1 : 0;
+  static constexpr int kRowBytes = kNib ? 64 : 128;
+  static constexpr int kHiBytes = kQ5 ? 16 : 0;
+  static constexpr int kTokBytes = kRowBytes + kHiBytes;
 };
+// byte offsets of token t of row bg: its code / nibble row, its fifth-bit row
+template <int MODE>
+__device__ __forceinline__ int64_t grp_row_b(int64_t bg, int32_t max_seq, int64_t t) {
+  return bg * max_seq * GrpMode<MODE>::kTokBytes + t * GrpMode<MODE>::kRowBytes;
+}
+template <int MODE>
+__device__ __forceinline__ int64_t grp_hi_b(int64_t bg, int32_t max_seq, int64_t t) {
+  return bg * max_seq * GrpMode<MODE>::kTokBytes + int64_t(max_seq) * GrpMode<MODE>::kRowBytes +
+         t * GrpMode<MODE>::kHiBytes;
+}
 __device__ __forceinline__ uint16_t grp_scale_bits_b(float a, int qmax) {
   return __half_as_ushort(__float2half_rn(a / float(qmax)));
 }
@@ -80,7 +102,7 @@ __device__ __forceinline__ void append_one(const AppendOne& ap, uint16_t* __rest
       kmin[bo + d] = bmn;
       kmax[bo + d] = bmx;
     }
-  } else if constexpr (MODE == kAppendQ8 || MODE == kAppendQ4) {
+  } else if constexpr (is_grp_mode(MODE)) {
     // one wavefront per row (K, V): lane l holds channels 2l, 2l + 1, a
     // group is one 16-lane row (the append kernel's layout and order)
     using F = GrpMode<MODE>;
@@ -93,9 +115,24 @@ __device__ __forceinline__ void append_one(const AppendOne& ap, uint16_t* __rest
       const uint16_t sb = grp_scale_bits_b(a, F::kQmax);
       const float sc = h2f(sb);
       const int c0 = grp_code_b(x.x, sc, F::kQmax), c1 = grp_code_b(x.y, sc, F::kQmax);
-      uint8_t* dst = static_cast<uint8_t*>(wave == 0 ? ap.k : ap.v) + row * F::kRowBytes;
-      if constexpr (F::kQ4) {
-        dst[lane] = uint8_t((c0 + 8) | ((c1 + 8) << 4));
+      uint8_t* base = static_cast<uint8_t*>(wave == 0 ? ap.k : ap.v);
+      uint8_t* dst = base + grp_row_b<MODE>(bg, ap.max_seq, p0);
+      if constexpr (F::kNib) {
+        const int u0 = c0 + F::kBias, u1 = c1 + F::kBias;
+        dst[lane] = uint8_t((u0 & 15) | ((u1 & 15) << 4));
+        if constexpr (F::kQ5) {
+          // fifth bits: channel 2l from h0 bit l, 2l + 1 from h1 bit l
+          const uint64_t h0 = __ballot(u0 >> 4), h1 = __ballot(u1 >> 4);
+          if (lane < 4) {
+            const uint32_t e = uint32_t(h0 >> (16 * lane)) & 0xFFFFu;
+            const uint32_t o = uint32_t(h1 >> (16 * lane)) & 0xFFFFu;
+            uint32_t w = 0u;
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+              w |= (((e >> i) & 1u) << (2 * i)) | (((o >> i) & 1u) << (2 * i + 1));
+            reinterpret_cast<uint32_t*>(base + grp_hi_b<MODE>(bg, ap.max_seq, p0))[lane] = w;
+          }
+        }
       } else {
         reinterpret_cast<uint16_t*>(dst)[lane] = uint16_t((c0 & 0xFF) | ((c1 & 0xFF) << 8));
       }
@@ -211,8 +248,9 @@ __device__ __forceinline__ int8_t quant_slot_i8(const float (&kf)[8], const floa
 // Group-wise codes of the new row in the row's first workgroup: slot 0 (the
 // first 16 lanes) quantizes K, slot 1 V, lane c its channels 8c .. 8c + 7; a
 // group is 4 lanes (xor-shuffles 1, 2 give its absmax).  Returns the lane's
-// codes packed as stored (q8_0: 8 bytes, q4_0: 4 bytes) and its group's
-// scale bits.
+// codes packed as stored (q8_0: 8 bytes; q4_0: 4 bytes of nibbles; q5_0: 4
+// bytes of nibbles and, in .y, the byte of fifth bits) and its group's scale
+// bits.
 template <int MODE>
 __device__ __forceinline__ uint2 quant_slot_grp(const float (&kf)[8], const float (&vf)[8],
                                                 uint16_t& sbits) {
@@ -233,10 +271,13 @@ __device__ __forceinline__ uint2 quant_slot_grp(const float (&kf)[8], const floa
 #pragma unroll
   for (int e = 0; e < 8; ++e) c[e] = grp_code_b(x[e], sc, F::kQmax);
   uint2 out = make_uint2(0u, 0u);
-  if constexpr (F::kQ4) {
+  if constexpr (F::kNib) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      out.x |= uint32_t((c[2 * i] + 8) | ((c[2 * i + 1] + 8) << 4)) << (8 * i);
+    for (int i = 0; i < 4; ++i) {
+      const int u0 = c[2 * i] + F::kBias, u1 = c[2 * i + 1] + F::kBias;
+      out.x |= uint32_t((u0 & 15) | ((u1 & 15) << 4)) << (8 * i);
+      out.y |= uint32_t(((u0 >> 4) & 1) | (((u1 >> 4) & 1) << 1)) << (2 * i);
+    }
   } else {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -482,7 +523,7 @@ bounds_kernel(uint16_t* __restrict__ kmin, uint16_t* __restrict__ kmax,
         if constexpr (MODE == kAppendI8) {
           own_wg = tile == 0;
           if (own_wg) code = quant_slot_i8(kf, vf, ks_new, vs_new);
-        } else if constexpr (MODE == kAppendQ8 || MODE == kAppendQ4) {
+        } else if constexpr (is_grp_mode(MODE)) {
           own_wg = tile == 0 && int(threadIdx.x) < 2 * kLanesPerBlock;
           if (own_wg) gcodes = quant_slot_grp<MODE>(kf, vf, gscale);
         }
@@ -585,13 +626,16 @@ scored:
         if (threadIdx.x == 0) ap.ks[arow] = ks_new;
         if (threadIdx.x == 8 * kLanesPerBlock) ap.vs[arow] = vs_new;
       }
-    } else if constexpr (MODE == kAppendQ8 || MODE == kAppendQ4) {
+    } else if constexpr (is_grp_mode(MODE)) {
       if (own_wg) {
         using F = GrpMode<MODE>;
         const bool is_v = int(threadIdx.x) / kLanesPerBlock == 1;
-        uint8_t* dst = static_cast<uint8_t*>(is_v ? ap.v : ap.k) + arow * F::kRowBytes;
-        if constexpr (F::kQ4) reinterpret_cast<uint32_t*>(dst)[c] = gcodes.x;
+        uint8_t* base = static_cast<uint8_t*>(is_v ? ap.v : ap.k);
+        const int64_t bgr = int64_t(b) * Hkv + g;
+        uint8_t* dst = base + grp_row_b<MODE>(bgr, ap.max_seq, p0);
+        if constexpr (F::kNib) reinterpret_cast<uint32_t*>(dst)[c] = gcodes.x;
         else reinterpret_cast<uint2*>(dst)[c] = gcodes;
+        if constexpr (F::kQ5) base[grp_hi_b<MODE>(bgr, ap.max_seq, p0) + c] = uint8_t(gcodes.y);
         if (c % 4 == 0)
           reinterpret_cast<uint16_t*>(is_v ? ap.vs : ap.ks)[arow * (D / kGrpChannels) + c / 4] =
               gscale;
@@ -693,6 +737,8 @@ hipError_t launch_append_bounds(const skv_cache& c, const int32_t* pos0, const v
       return launch_bounds_m<kAppendQ8>(c, q, n_heads, seq_len, max_len, score, ap, stream);
     case SKV_Q4_0:
       return launch_bounds_m<kAppendQ4>(c, q, n_heads, seq_len, max_len, score, ap, stream);
+    case SKV_Q5_0:
+      return launch_bounds_m<kAppendQ5>(c, q, n_heads, seq_len, max_len, score, ap, stream);
     default:
       return hipErrorInvalidValue;
   }

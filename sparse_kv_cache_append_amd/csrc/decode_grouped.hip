@@ -12,8 +12,12 @@
 // Layout: codes [batch][n_kv_heads][max_seq][row] with row = 128 bytes
 // (q8_0, int8 codes -127..127) or 64 bytes (q4_0: channel 2i in the low
 // nibble of byte i, channel 2i + 1 in the high nibble, each code + 8 with
-// codes -7..7); scales [batch][n_kv_heads][max_seq][4] f16, one per group of
-// 32 channels.  Per group: a = max |x|, s = f16(a / QMAX) (QMAX 127 or 7),
+// codes -7..7); q5_0 (codes -15..15, stored as code + 16 in five bits): per
+// (sequence, KV head) a plane of max_seq 64-byte nibble rows (bits 0..3, as
+// q4_0) followed by a plane of max_seq 16-byte rows of the fifth bits (bit
+// c % 8 of byte c / 8 for channel c); scales [batch][n_kv_heads][max_seq][4]
+// f16, one per group of 32 channels.  Per group: a = max |x|,
+// s = f16(a / QMAX) (QMAX 127, 7 or 15),
 // code = clamp(rint(x / s), -QMAX, QMAX) against the stored scale, so a value
 // is exactly s * code (s == 0 or not finite: codes 0).
 //
@@ -46,11 +50,37 @@ namespace {
 constexpr int kGroup = 32;
 constexpr int kGroups = kD / kGroup;        // 4
 
-template <bool Q4>
+enum GrpKind { kQ8 = 0, kQ4 = 1, kQ5 = 2 };
+template <int K>
 struct GrpFmt {
-  static constexpr int kQmax = Q4 ? 7 : 127;
-  static constexpr int kRowBytes = Q4 ? kD / 2 : kD;      // codes per (token, KV head)
+  static constexpr bool kNib = K != kQ8;                   // nibble plane (q4_0, q5_0)
+  static constexpr int kQmax = K == kQ8 ? 127 : K == kQ4 ? 7 : 15;
+  static constexpr int kBias = K == kQ8 ? 0 : kQmax + 1;   // stored = code + bias
+  static constexpr int kRowBytes = kNib ? kD / 2 : kD;     // code / nibble row bytes
+  static constexpr int kHiBytes = K == kQ5 ? kD / 8 : 0;   // fifth-bit row bytes
+  static constexpr int kTokBytes = kRowBytes + kHiBytes;   // per (token, KV head)
 };
+// Byte offsets of token t of row bg (sequence x KV head): its code (or
+// nibble) row and, for q5_0, its fifth-bit row.
+template <int K>
+__device__ __forceinline__ int64_t grp_row_off(int64_t bg, int32_t max_seq, int64_t t) {
+  return bg * max_seq * GrpFmt<K>::kTokBytes + t * GrpFmt<K>::kRowBytes;
+}
+template <int K>
+__device__ __forceinline__ int64_t grp_hi_off(int64_t bg, int32_t max_seq, int64_t t) {
+  return bg * max_seq * GrpFmt<K>::kTokBytes + int64_t(max_seq) * GrpFmt<K>::kRowBytes +
+         t * GrpFmt<K>::kHiBytes;
+}
+// The fifth bits of 32 channels as a 32-bit word (bit i = channel i) from the
+// two ballots of a row (lane l: h0 bit l = channel 2l, h1 bit l = channel
+// 2l + 1), for lanes l < 4 (channels 32 l .. 32 l + 31).
+__device__ __forceinline__ uint32_t q5_hi_word(uint64_t h0, uint64_t h1, int l) {
+  const uint32_t e = uint32_t(h0 >> (16 * l)) & 0xFFFFu, o = uint32_t(h1 >> (16 * l)) & 0xFFFFu;
+  uint32_t w = 0u;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) w |= (((e >> i) & 1u) << (2 * i)) | (((o >> i) & 1u) << (2 * i + 1));
+  return w;
+}
 
 // The group-wise quantizer for one value given its group's absmax (the
 // append's arithmetic): stored f16 scale and code.
@@ -71,7 +101,7 @@ __device__ __forceinline__ int grp_code(float x, float s, int qmax) {
 // cache: the float32 keys' min / max rounded outward to f16.
 constexpr int kAppendThreads = 256;
 
-template <bool Q4>
+template <int K>
 __global__ void __launch_bounds__(kAppendThreads)
 append_grp_kernel(uint8_t* __restrict__ kc, uint8_t* __restrict__ vc,
                   uint16_t* __restrict__ ksc, uint16_t* __restrict__ vsc,
@@ -79,7 +109,7 @@ append_grp_kernel(uint8_t* __restrict__ kc, uint8_t* __restrict__ vc,
                   const float* __restrict__ kn, const float* __restrict__ vn,
                   const int32_t* __restrict__ pos0, int32_t n_new, int32_t Hkv,
                   int32_t max_seq, int32_t block, int32_t max_blocks) {
-  using F = GrpFmt<Q4>;
+  using F = GrpFmt<K>;
   const int32_t g = blockIdx.y, b = blockIdx.z;
   const int32_t p0 = pos0[b];
   if (p0 < 0) return;
@@ -91,7 +121,8 @@ append_grp_kernel(uint8_t* __restrict__ kc, uint8_t* __restrict__ vc,
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   for (int32_t t = t0 + wave; t < t1; t += kAppendThreads / kWave) {
     const int64_t src = ((int64_t(b) * n_new + (t - p0)) * Hkv + g) * kD;
-    const int64_t row = (int64_t(b) * Hkv + g) * max_seq + t;
+    const int64_t bg = int64_t(b) * Hkv + g;
+    const int64_t row = bg * max_seq + t;
 #pragma unroll
     for (int which = 0; which < 2; ++which) {
       const float2 x = reinterpret_cast<const float2*>((which == 0 ? kn : vn) + src)[lane];
@@ -99,9 +130,17 @@ append_grp_kernel(uint8_t* __restrict__ kc, uint8_t* __restrict__ vc,
       const uint16_t sb = grp_scale_bits(a, F::kQmax);
       const float s = h2f(sb);
       const int c0 = grp_code(x.x, s, F::kQmax), c1 = grp_code(x.y, s, F::kQmax);
-      uint8_t* dst = (which == 0 ? kc : vc) + row * F::kRowBytes;
-      if constexpr (Q4) {
-        dst[lane] = uint8_t((c0 + 8) | ((c1 + 8) << 4));
+      uint8_t* base = which == 0 ? kc : vc;
+      uint8_t* dst = base + grp_row_off<K>(bg, max_seq, t);
+      if constexpr (F::kNib) {
+        const int u0 = c0 + F::kBias, u1 = c1 + F::kBias;
+        dst[lane] = uint8_t((u0 & 15) | ((u1 & 15) << 4));
+        if constexpr (K == kQ5) {
+          const uint64_t h0 = __ballot(u0 >> 4), h1 = __ballot(u1 >> 4);
+          if (lane < 4)
+            reinterpret_cast<uint32_t*>(base + grp_hi_off<K>(bg, max_seq, t))[lane] =
+                q5_hi_word(h0, h1, lane);
+        }
       } else {
         reinterpret_cast<uint16_t*>(dst)[lane] = uint16_t((c0 & 0xFF) | ((c1 & 0xFF) << 8));
       }
@@ -146,13 +185,37 @@ __device__ __forceinline__ void unpack_q4(const int4_t& w, int4_t& c0, int4_t& c
   c1 = int4_t{int(o[4]), int(o[5]), int(o[6]), int(o[7])};
 }
 
-// 8 biased q4_0 bytes n = code + 8 to the f16 codes, exactly: each byte goes
-// under a 0x64 high byte (f16 1024 + n), minus 1032.
-__device__ __forceinline__ half8_t widen_q4(int2_t w) {
+// q5_0: the nibbles as for q4_0, plus each channel's fifth bit (hi: bit i =
+// channel i of the 32) as bit 4 of its byte: code + 16, 0..31.  The fifth bits
+// of 4 channels go to bit 0 of 4 bytes by one 24-bit multiply: bit m of n
+// (m < 4) lands at bit 8 m of n * 0x204081 (shifts 0, 7, 14, 21; no two
+// products share a bit, so nothing carries).
+__device__ __forceinline__ uint32_t spread4(uint32_t n) {
+  return (n * 0x204081u) & 0x01010101u;
+}
+__device__ __forceinline__ void unpack_q5(const int4_t& w, uint32_t hi, int4_t& c0, int4_t& c1) {
+  uint32_t o[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t x = uint32_t(w[i]);
+    const uint32_t lo = x & 0x0F0F0F0Fu, hn = (x >> 4) & 0x0F0F0F0Fu;
+    const uint32_t hb = hi >> (8 * i);                    // channels 8 i .. 8 i + 7
+    o[2 * i] = __builtin_amdgcn_perm(hn, lo, 0x05010400u) | (spread4(hb & 15u) << 4);
+    o[2 * i + 1] = __builtin_amdgcn_perm(hn, lo, 0x07030602u) | (spread4((hb >> 4) & 15u) << 4);
+  }
+  c0 = int4_t{int(o[0]), int(o[1]), int(o[2]), int(o[3])};
+  c1 = int4_t{int(o[4]), int(o[5]), int(o[6]), int(o[7])};
+}
+
+// 8 biased bytes n = code + BIAS (q4_0: 8, q5_0: 16) to the f16 codes,
+// exactly: each byte goes under a 0x64 high byte (f16 1024 + n), minus
+// 1024 + BIAS.
+template <int BIAS>
+__device__ __forceinline__ half8_t widen_biased(int2_t w) {
   typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
   constexpr uint32_t kLoSel = 0x04010400u;   // (0x64, x1, 0x64, x0)
   constexpr uint32_t kHiSel = 0x04030402u;   // (0x64, x3, 0x64, x2)
-  const half2_t off = half2_t{(_Float16)1032.0f, (_Float16)1032.0f};
+  const half2_t off = half2_t{(_Float16)(1024.0f + BIAS), (_Float16)(1024.0f + BIAS)};
   half8_t r;
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
@@ -167,10 +230,10 @@ __device__ __forceinline__ half8_t widen_q4(int2_t w) {
   return r;
 }
 
-// The LDS codes of a tile as f16: q4_0 biased bytes or q8_0 int8 codes.
-template <bool Q4>
+// The LDS codes of a tile as f16: q4_0 / q5_0 biased bytes or q8_0 int8 codes.
+template <int K>
 __device__ __forceinline__ half8_t widen_grp(int2_t w) {
-  if constexpr (Q4) return widen_q4(w);
+  if constexpr (GrpFmt<K>::kNib) return widen_biased<GrpFmt<K>::kBias>(w);
   else return widen_codes(w);
 }
 
@@ -178,7 +241,7 @@ constexpr int kPwShiftGrp = 7;
 
 // SELR > 0: the block selection runs in the prologue (fused_walk), as in the
 // f16 and int8 attention kernels.
-template <int G, bool Q4, int SELR = 0>
+template <int G, int K, int SELR = 0>
 __global__ void __launch_bounds__(kMThreads, 2)
 decode_grp_mfma(const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
                 const uint16_t* __restrict__ ksc, const uint16_t* __restrict__ vsc,
@@ -188,13 +251,14 @@ decode_grp_mfma(const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
                 int32_t n_split, int32_t n_rows, int32_t units_per_split, float qscale2,
                 float* __restrict__ ws_m, float* __restrict__ ws_l, float* __restrict__ ws_o,
                 FusedSelect fs) {
-  using F = GrpFmt<Q4>;
+  using F = GrpFmt<K>;
+  constexpr bool Q5 = K == kQ5;
   constexpr int T = 32;
   constexpr int kCodeBytes = T * kRowBytesI8;               // 4096 (int8 codes in LDS)
   constexpr int kScaleOff = 2 * kCodeBytes;                 // K, V scales as float [T][4]
   constexpr int kBufBytes = 2 * kCodeBytes + 2 * T * kGroups * 4;
   constexpr int kTileBytes = T * F::kRowBytes;              // HBM bytes of a code tile
-  constexpr int kLoads = Q4 ? 2 : 4;                        // 16-byte code loads per lane
+  constexpr int kLoads = F::kNib ? 2 : 4;                   // 16-byte code loads per lane
   __shared__ __attribute__((aligned(16))) uint8_t smem[kMWaves][2][kBufBytes];
   const uint32_t slot = xcd_slot(blockIdx.x, gridDim.x);
   const int32_t split = int32_t(slot % uint32_t(n_split));
@@ -240,8 +304,10 @@ decode_grp_mfma(const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
   float4_t O[8];
 #pragma unroll
   for (int n = 0; n < 8; ++n) O[n] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
-  const uint8_t* kbase = kc + bg * int64_t(max_seq) * F::kRowBytes;
-  const uint8_t* vbase = vc + bg * int64_t(max_seq) * F::kRowBytes;
+  const uint8_t* kbase = kc + grp_row_off<K>(bg, max_seq, 0);
+  const uint8_t* vbase = vc + grp_row_off<K>(bg, max_seq, 0);
+  const uint8_t* khbase = kc + grp_hi_off<K>(bg, max_seq, 0);       // q5_0 fifth bits
+  const uint8_t* vhbase = vc + grp_hi_off<K>(bg, max_seq, 0);
   const uint8_t* ksb = reinterpret_cast<const uint8_t*>(ksc + bg * int64_t(max_seq) * kGroups);
   const uint8_t* vsb = reinterpret_cast<const uint8_t*>(vsc + bg * int64_t(max_seq) * kGroups);
   // Lane loads, per code tile: q8_0 row 8 i + lane / 8, 16-byte chunk lane % 8
@@ -249,7 +315,9 @@ decode_grp_mfma(const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
   // (i = 0..1).  Scales: 4 bytes per lane = the two f16 scales of groups
   // 2 (lane % 2), + 1 of token lane / 2.  Buffer resources with the tile's
   // valid bytes: rows past the length read as zeros.
-  struct Frag { int4_t k[kLoads], v[kLoads]; uint32_t ks, vs; int32_t r0, nvalid; };
+  // q5_0 also: the fifth bits of the lane's 32 channels of each of its two
+  // rows (4 bytes at 256 i + 4 lane of the tile's fifth-bit rows)
+  struct Frag { int4_t k[kLoads], v[kLoads]; uint32_t kh[2], vh[2], ks, vs; int32_t r0, nvalid; };
   auto issue = [&](Frag& f) {
     int32_t r0 = 0, nv = 0;
     if (tw.more()) tw.next<T>(r0, nv);
@@ -263,6 +331,18 @@ decode_grp_mfma(const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
     for (int i = 0; i < kLoads; ++i) {
       f.k[i] = tile_load(kr, lo + 1024 * i);
       f.v[i] = tile_load(vr, lo + 1024 * i);
+    }
+    if constexpr (Q5) {
+      const int hbytes = __builtin_amdgcn_readfirstlane(max(nv, 0) * F::kHiBytes);
+      const auto khr = tile_rsrc(khbase + int64_t(r0) * F::kHiBytes, hbytes);
+      const auto vhr = tile_rsrc(vhbase + int64_t(r0) * F::kHiBytes, hbytes);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        f.kh[i] = __builtin_amdgcn_raw_buffer_load_b32(khr, 256u * i + 4u * uint32_t(lane), 0,
+                                                        kAuxNontemporal);
+        f.vh[i] = __builtin_amdgcn_raw_buffer_load_b32(vhr, 256u * i + 4u * uint32_t(lane), 0,
+                                                        kAuxNontemporal);
+      }
     }
     const int sbytes = __builtin_amdgcn_readfirstlane(max(nv, 0) * kGroups * 2);
     const auto ksr = tile_rsrc(ksb + int64_t(r0) * kGroups * 2, sbytes);
@@ -281,15 +361,17 @@ decode_grp_mfma(const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
     uint8_t* vt = kt + kCodeBytes;
     float* stk = reinterpret_cast<float*>(kt + kScaleOff);          // [T][4]
     float* stv = stk + T * kGroups;
-    if constexpr (Q4) {
+    if constexpr (F::kNib) {
 #pragma unroll
       for (int i = 0; i < kLoads; ++i) {
         const int rw = 16 * i + lane / 4, ch = 2 * (lane % 4);
         int4_t a0, a1;
-        unpack_q4(fr.k[i], a0, a1);
+        if constexpr (Q5) unpack_q5(fr.k[i], fr.kh[i], a0, a1);
+        else unpack_q4(fr.k[i], a0, a1);
         *reinterpret_cast<int4_t*>(kt + sw(rw, ch)) = a0;
         *reinterpret_cast<int4_t*>(kt + sw(rw, ch + 1)) = a1;
-        unpack_q4(fr.v[i], a0, a1);
+        if constexpr (Q5) unpack_q5(fr.v[i], fr.vh[i], a0, a1);
+        else unpack_q4(fr.v[i], a0, a1);
         *reinterpret_cast<int4_t*>(vt + sw(rw, ch)) = a0;
         *reinterpret_cast<int4_t*>(vt + sw(rw, ch + 1)) = a1;
       }
@@ -334,7 +416,7 @@ decode_grp_mfma(const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
         const int rw = 16 * s + lc;
         const int2_t raw = *reinterpret_cast<const int2_t*>(kt + sw(rw, 2 * kk + lg / 2) +
                                                             8 * (lg & 1));
-        const half8_t a = widen_grp<Q4>(raw);
+        const half8_t a = widen_grp<K>(raw);
         acc[kk] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
         acc[kk] = mfma_f16_32(a, qhi[kk], acc[kk]);
         acc[kk] = mfma_f16_32(a, qlo[kk], acc[kk]);
@@ -377,7 +459,7 @@ decode_grp_mfma(const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
         const int n = 2 * grp + nn;
         const int off = sw(tr_row, n) + 8 * (lc & 1);
         const int2_t raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32((SKV_LDS int2_t*)(vt + off));
-        const half8_t bv = widen_grp<Q4>(raw);
+        const half8_t bv = widen_grp<K>(raw);
         O[n] = mfma_f16_32(phi, bv, O[n]);
         O[n] = mfma_f16_32(plo, bv, O[n]);
       }
@@ -413,17 +495,18 @@ hipError_t launch_append_grouped(const skv_cache& c, const int32_t* pos0, int32_
   const dim3 grid(n_aff, c.n_kv_heads, c.batch);
   uint16_t* ks = reinterpret_cast<uint16_t*>(c.k_scale);
   uint16_t* vs = reinterpret_cast<uint16_t*>(c.v_scale);
-  if (c.kv_dtype == SKV_Q4_0) {
-    append_grp_kernel<true><<<grid, kAppendThreads, 0, stream>>>(
-        static_cast<uint8_t*>(c.k), static_cast<uint8_t*>(c.v), ks, vs, c.kmin, c.kmax,
-        static_cast<const float*>(k_new), static_cast<const float*>(v_new), pos0, n_new,
-        c.n_kv_heads, c.max_seq, c.block, max_blocks);
-  } else {
-    append_grp_kernel<false><<<grid, kAppendThreads, 0, stream>>>(
-        static_cast<uint8_t*>(c.k), static_cast<uint8_t*>(c.v), ks, vs, c.kmin, c.kmax,
-        static_cast<const float*>(k_new), static_cast<const float*>(v_new), pos0, n_new,
-        c.n_kv_heads, c.max_seq, c.block, max_blocks);
+#define SKV_APP_GRP(KK)                                                                         \
+  append_grp_kernel<KK><<<grid, kAppendThreads, 0, stream>>>(                                   \
+      static_cast<uint8_t*>(c.k), static_cast<uint8_t*>(c.v), ks, vs, c.kmin, c.kmax,          \
+      static_cast<const float*>(k_new), static_cast<const float*>(v_new), pos0, n_new,         \
+      c.n_kv_heads, c.max_seq, c.block, max_blocks)
+  switch (c.kv_dtype) {
+    case SKV_Q8_0: SKV_APP_GRP(kQ8); break;
+    case SKV_Q4_0: SKV_APP_GRP(kQ4); break;
+    case SKV_Q5_0: SKV_APP_GRP(kQ5); break;
+    default: return hipErrorInvalidValue;
   }
+#undef SKV_APP_GRP
   return hipGetLastError();
 }
 
@@ -467,9 +550,10 @@ hipError_t launch_decode_grouped(const DecodeParams& p, hipStream_t stream) {
   else if (fr == 4) SKV_GRP(GG, Q, 4);             \
   else if (fr > 0) SKV_GRP(GG, Q, kFusedSelR);     \
   else SKV_GRP(GG, Q, 0)
-#define SKV_GRP_G(GG)                                \
-  if (c.kv_dtype == SKV_Q4_0) { SKV_GRP_Q(GG, true); } \
-  else { SKV_GRP_Q(GG, false); }
+#define SKV_GRP_G(GG)                                          \
+  if (c.kv_dtype == SKV_Q4_0) { SKV_GRP_Q(GG, kQ4); }            \
+  else if (c.kv_dtype == SKV_Q5_0) { SKV_GRP_Q(GG, kQ5); }       \
+  else { SKV_GRP_Q(GG, kQ8); }
   switch (G) {
     case 1: SKV_GRP_G(1); break;
     case 2: SKV_GRP_G(2); break;

@@ -153,7 +153,9 @@ hipError_t launch_sparse_v(const SparseVParams& p, hipStream_t stream);
 hipError_t launch_append_grouped(const skv_cache& c, const int32_t* pos0, int32_t n_new,
                                  const void* k_new, const void* v_new, hipStream_t stream);
 hipError_t launch_decode_grouped(const DecodeParams& p, hipStream_t stream);
-inline bool is_grouped(int32_t kv_dtype) { return kv_dtype == SKV_Q8_0 || kv_dtype == SKV_Q4_0; }
+inline bool is_grouped(int32_t kv_dtype) {
+  return kv_dtype == SKV_Q8_0 || kv_dtype == SKV_Q4_0 || kv_dtype == SKV_Q5_0;
+}
 
 // The 4-bit key index and its GQA-shared scan (scan4.hip).
 struct Scan4Params {

@@ -83,7 +83,7 @@ def test_partial_last_block_is_clipped():
 
 
 def test_grouped_cache_bytes():
-    """q8_0 / q4_0 (sparse_attn.md, "All-KV-types composition": blocks of 32
+    """q8_0 / q4_0 / q5_0 (sparse_attn.md, "All-KV-types composition": blocks of 32
     values): per (token, KV head) the K and V rows hold D codes of 8 or 4 bits
     and an f16 scale per 32 channels -- 2 x (128 + 8) and 2 x (64 + 8) bytes at
     D = 128, i.e. 34 and 18 bytes per 32 values."""
@@ -91,6 +91,11 @@ def test_grouped_cache_bytes():
     assert bench.kv_bytes_per_token("q4_0", 128) == 144
     assert bench.kv_bytes_per_token("q8_0", 128) / 2 / 4 == 34
     assert bench.kv_bytes_per_token("q4_0", 128) / 2 / 4 == 18
+    # q5_0: five bits per value (a nibble plus a fifth bit) and the f16 scale:
+    # 20 + 2 = 22 bytes per 32 values, 2 x (64 + 16 + 8) per row at D = 128
+    assert bench.kv_bytes_per_token("q5_0", 128) == 176
+    assert bench.kv_bytes_per_token("q5_0", 128) / 2 / 4 == 22
+    assert bench.kv_bytes_per_token("q5_0", 64) == 88
 
 
 def test_scan4_index_bytes_match_the_layout_table():

@@ -1,4 +1,4 @@
-"""Group-wise quantized caches (q8_0, q4_0) on the GPU against the oracle
+"""Group-wise quantized caches (q8_0, q4_0, q5_0) on the GPU against the oracle
 (oracle/quant.py: quantize_groups; oracle/attention.py: attend_grouped):
 the append's codes, f16 scales and side-cache bounds bit-exact (including
 zero groups, scales below and beyond f16's range, round-half-even ties, and
@@ -18,7 +18,8 @@ from oracle import quant
 
 pytestmark = pytest.mark.gpu
 
-QMAX = {"q8_0": quant.QMAX_Q8, "q4_0": quant.QMAX_Q4}
+QMAX = {"q8_0": quant.QMAX_Q8, "q4_0": quant.QMAX_Q4, "q5_0": quant.QMAX_Q5}
+KINDS = ["q8_0", "q4_0", "q5_0"]
 
 
 def _print(*a):
@@ -30,8 +31,12 @@ def host_codes(x, kind):
     codes, s16 = quant.quantize_groups(x, QMAX[kind])
     if kind == "q8_0":
         return codes.view(np.uint8), s16, codes, s16
-    u = (codes.astype(np.int16) + 8).astype(np.uint8)
-    packed = (u[..., 0::2] | (u[..., 1::2] << 4)).astype(np.uint8)
+    u = (codes.astype(np.int16) + QMAX[kind] + 1).astype(np.uint8)
+    packed = ((u[..., 0::2] & 15) | ((u[..., 1::2] & 15) << 4)).astype(np.uint8)
+    if kind == "q5_0":
+        # (nibble plane, fifth-bit plane: bit c % 8 of byte c / 8)
+        hi = np.packbits((u >> 4) & 1, axis=-1, bitorder="little")
+        return (packed, hi), s16, codes, s16
     return packed, s16, codes, s16
 
 
@@ -39,8 +44,13 @@ def check_cache(cache, w, b=0):
     L = w.lens[b]
     for name, src in (("k", w.k[b]), ("v", w.v[b])):
         packed, s16, _, _ = host_codes(src, w.kv_dtype)
-        got = getattr(cache, name).cpu().numpy()[b, :, :L]
-        assert np.array_equal(got, packed), name
+        if w.kv_dtype == "q5_0":
+            lo, hi = cache.q5_planes(getattr(cache, name))
+            assert np.array_equal(lo.cpu().numpy()[b, :, :L], packed[0]), name
+            assert np.array_equal(hi.cpu().numpy()[b, :, :L], packed[1]), name
+        else:
+            got = getattr(cache, name).cpu().numpy()[b, :, :L]
+            assert np.array_equal(got, packed), name
         gs = getattr(cache, name + "_scale").cpu().numpy()[b, :, :L]
         assert np.array_equal(gs.view(np.uint16), s16.view(np.uint16)), name
     kmin, kmax = oracle.block_bounds(w.k[b], L, w.block)
@@ -59,7 +69,7 @@ def reference(w, b, tokens=None, hs=None, g=None):
                                  tokens)
 
 
-@pytest.mark.parametrize("kind", ["q8_0", "q4_0"])
+@pytest.mark.parametrize("kind", KINDS)
 def test_append_codes_scales_bounds_exact(gpu_lib, kind):
     w = workloads.gaussian(901, 2, 16, 4, 128, [300, 129], kind)
     # edge rows: a zero group, a group whose scale underflows f16, one whose
@@ -77,7 +87,7 @@ def test_append_codes_scales_bounds_exact(gpu_lib, kind):
             check_cache(cache, w, b)
 
 
-@pytest.mark.parametrize("kind", ["q8_0", "q4_0"])
+@pytest.mark.parametrize("kind", KINDS)
 @pytest.mark.parametrize("H,Hkv,lens", [(32, 8, [2049, 100]), (8, 8, [513]), (16, 8, [1]),
                                         (32, 4, [4097])])
 def test_dense_decode(gpu_lib, kind, H, Hkv, lens):
@@ -89,7 +99,7 @@ def test_dense_decode(gpu_lib, kind, H, Hkv, lens):
             assert_close(out[b], reference(w, b), 1e-3, kind, b, S)
 
 
-@pytest.mark.parametrize("kind", ["q8_0", "q4_0"])
+@pytest.mark.parametrize("kind", KINDS)
 def test_quest_decode(gpu_lib, kind):
     """Quest over a grouped cache: bounds from the float32 keys, the
     selection, attention over the selected blocks (the step's composition is
@@ -114,8 +124,8 @@ def test_quest_decode(gpu_lib, kind):
             assert_close(out[b, hs], reference(w, b, toks, hs, g), 1e-3, b, g)
 
 
-def test_32k_workload_q8_and_q4(gpu_lib):
-    for kind in ("q8_0", "q4_0"):
+def test_32k_workload_q8_q4_q5(gpu_lib):
+    for kind in KINDS:
         w = workloads.quest32k_quant(kind)
         cache = build_cache(w)
         check_cache(cache, w)

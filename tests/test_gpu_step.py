@@ -48,11 +48,17 @@ def _cache_tensors(c):
 def _poison_rows(cache, pos):
     """Fill the rows the step's append will write with values no correct
     result can depend on (NaN halves; int8 code -128 and NaN scales; q8_0 /
-    q4_0 bytes 0x80 and NaN group scales)."""
+    q4_0 / q5_0 bytes 0x80 (both q5_0 planes) and NaN group scales)."""
     for b, p in enumerate(pos.tolist()):
         if cache.kv_dtype == "f16":
             cache.k[b, :, p] = float("nan")
             cache.v[b, :, p] = float("nan")
+        elif cache.kv_dtype == "q5_0":
+            for t in (cache.k, cache.v):
+                for plane in cache.q5_planes(t):
+                    plane[b, :, p] = 0x80
+            cache.k_scale[b, :, p] = float("nan")
+            cache.v_scale[b, :, p] = float("nan")
         elif cache.kv_dtype in ("q8_0", "q4_0"):
             cache.k[b, :, p] = 0x80
             cache.v[b, :, p] = 0x80
@@ -141,8 +147,9 @@ def _oracle_check(w, out, sel):
             ref = oracle.attend_f16(w.q[0][hs], w.k[0][g:g + 1], w.v[0][g:g + 1],
                                     w.softmax_scale, tokens=toks)
             assert_close(out[0, hs], ref, 1e-3)
-        elif w.kv_dtype in ("q8_0", "q4_0"):
-            qmax = oracle.QMAX_Q8 if w.kv_dtype == "q8_0" else oracle.QMAX_Q4
+        elif w.kv_dtype in ("q8_0", "q4_0", "q5_0"):
+            qmax = {"q8_0": oracle.QMAX_Q8, "q4_0": oracle.QMAX_Q4,
+                    "q5_0": oracle.QMAX_Q5}[w.kv_dtype]
             kc, ksc = oracle.quantize_groups(w.k[0][g:g + 1], qmax)
             vc, vsc = oracle.quantize_groups(w.v[0][g:g + 1], qmax)
             ref = oracle.attend_grouped(w.q[0][hs], kc, ksc, vc, vsc, w.softmax_scale,
@@ -256,6 +263,22 @@ STEP_CASES = [
         544, 2, 32, 8, 128, [65, 2000], "q8_0"), False, True, {"poison": True}),
     ("dense-q4_0 append 5 parts G2", lambda: workloads.gaussian(
         545, 2, 16, 8, 128, [1025, 300], "q4_0"), False, True, {"poison": True, "S": 5}),
+    ("quest-q5_0", lambda: workloads.clustered(
+        [557, 558], 32, 8, 128, [3000, 4097], "q5_0", n_dirs=16, k_sel=[10, 12], n_sink=1,
+        n_recent=2), True, True, {}),
+    ("quest-q5_0 poisoned rows G8", lambda: workloads.clustered(
+        [559], 32, 4, 128, [5001], "q5_0", n_dirs=16, k_sel=[20], n_sink=1, n_recent=4),
+        True, True, {"poison": True}),
+    ("quest-q5_0 NaN channel in the new key", lambda: _with_nan_key(workloads.clustered(
+        [560], 16, 8, 128, [2049], "q5_0", n_dirs=16, k_sel=[9], n_sink=1, n_recent=2)),
+        True, True, {"lag": 1}),
+    ("quest-q5_0 token past the launched tiles", lambda: workloads.clustered(
+        [561], 32, 4, 128, [64 * 16 + 1], "q5_0", n_dirs=16, k_sel=[5], n_sink=1, n_recent=2),
+        True, True, {"lag": 1, "tight": True}),
+    ("dense-q5_0 append poisoned rows", lambda: workloads.gaussian(
+        562, 2, 32, 8, 128, [65, 2000], "q5_0"), False, True, {"poison": True}),
+    ("dense-q5_0 first token of an empty cache", lambda: workloads.gaussian(
+        563, 1, 32, 8, 128, [1], "q5_0"), False, True, {"lag": 1, "tight": True}),
     # part counts whose merge takes 1, 2, 3 and 4 wavefronts per head
     ("quest-f16 8 parts", lambda: workloads.clustered(
         [546, 547], 32, 8, 128, [3000, 4097], "f16", n_dirs=16, k_sel=[10, 12], n_sink=1,
@@ -529,7 +552,8 @@ def test_decode_step_tie_classes(gpu_lib, k_sel):
 
 
 @pytest.mark.parametrize("kv_dtype,L,S", [("f16", 32768, 32), ("i8", 20000, 24), ("f16", 3000, 1),
-                                          ("q8_0", 9000, 16), ("q4_0", 32768, 32)])
+                                          ("q8_0", 9000, 16), ("q4_0", 32768, 32),
+                                          ("q5_0", 32768, 32)])
 def test_decode_attn_select_equals_select_then_decode(gpu_lib, kv_dtype, L, S):
     """skv_decode_attn_select (selection folded into the attention prologue;
     with S = 1 a part spans more than 64 entries and the selection runs as

@@ -1,5 +1,6 @@
 """Pins of the group-wise quantization (oracle/quant.py: quantize_groups;
-sparse_attn.md, "All-KV-types composition": q8_0 / q4_0 blocks of 32 values)
+sparse_attn.md, "All-KV-types composition": q8_0 / q4_0 blocks of 32 values;
+"Method: Quest-style min/max block bounds": q5_0)
 and of attention over such a cache (oracle/attention.py: attend_grouped)."""
 import math
 
@@ -10,7 +11,7 @@ import oracle
 from oracle import quant
 
 
-@pytest.mark.parametrize("qmax", [quant.QMAX_Q8, quant.QMAX_Q4])
+@pytest.mark.parametrize("qmax", [quant.QMAX_Q8, quant.QMAX_Q4, quant.QMAX_Q5])
 def test_group_invariants(qmax):
     rng = np.random.default_rng(qmax)
     x = (rng.standard_normal((3, 50, 128)) * rng.uniform(0.01, 30, (3, 50, 1))).astype(np.float32)
@@ -42,7 +43,7 @@ def test_group_rounding_brute_force():
     to even, clamped."""
     rng = np.random.default_rng(7)
     x = rng.standard_normal((4, 64)).astype(np.float32) * 3
-    for qmax in (127, 7):
+    for qmax in (127, 7, 15):
         codes, s16 = quant.quantize_groups(x, qmax)
         for r in range(4):
             for grp in range(2):

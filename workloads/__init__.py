@@ -184,7 +184,8 @@ def named(cfg: int) -> Workload:
 def quest32k_quant(kv_dtype: str) -> Workload:
     """The 32K Quest workload's generator (H=32, Hkv=8, 64 directions, block
     64, K_SEL=128, sink 1, recent 2, seed 1003) drawn for a group-wise
-    quantized cache ("q8_0" or "q4_0"): the float32 rows that get appended."""
+    quantized cache ("q8_0", "q4_0" or "q5_0"): the float32 rows that get
+    appended."""
     return clustered([1003], 32, 8, 128, [32768], kv_dtype, n_dirs=64,
                      name=f"quest-{kv_dtype} B1 H32/Hkv8 D128 L32768 K_SEL128 sink1 recent2",
                      k_sel=[128], n_sink=1, n_recent=2)
