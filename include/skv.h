@@ -35,11 +35,11 @@
  *     v_new are 16-byte aligned, the int8 scales 4-byte aligned (SKV_EINVAL
  *     otherwise); other buffers need their element's natural alignment.
  *   - Supported in this version: head_dim D = 128 for every call, and
- *     D = 64 or 256 for the f16 and int8 caches' skv_kv_append,
- *     skv_block_bounds, skv_select_topk, skv_decode_attn,
- *     skv_decode_attn_select, skv_combine, skv_decode_step and
- *     skv_decode_step_static (the cpu-attn kernel card, "Requirements and
- *     limits", admits any multiple of 16 up to 1024); GQA group size
+ *     D = 64 or 256 for the f16 and int8 caches' calls except sparse-V and
+ *     the 4-bit scan (append, bounds, selection, attention, combine, the
+ *     step, per-query-head selection and query-token chunks; the cpu-attn
+ *     kernel card, "Requirements and limits", admits any multiple of 16 up to
+ *     1024); GQA group size
  *     G = H / Hkv in {1, 2, 4, 8}; block a multiple of 16.  Other values that
  *     are otherwise valid return SKV_EUNSUPPORTED.
  *   - Launch sizes: batch and n_kv_heads up to 65,535, and at most
@@ -371,7 +371,7 @@ skv_status skv_decode_attn_heads(const skv_cache* c, const float* q, int32_t n_h
  *     -> skv_decode_attn_multi -> skv_combine(ws, batch, T * n_heads, ...)
  * (dense: skv_decode_attn_multi with NULL lists, then skv_combine).
  * q is float32 [batch][T][n_heads][head_dim]; T in {1, 2, 4, 8} with
- * T * G <= 16; head_dim 128.
+ * T * G <= 16; head_dim 64, 128 or 256.
  */
 
 /*

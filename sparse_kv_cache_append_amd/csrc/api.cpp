@@ -13,7 +13,8 @@ constexpr int32_t kMaxSelectBlocks = 16384;
 
 bool valid_head_dim(int32_t d) { return d >= 16 && d <= 1024 && d % 16 == 0; }
 // Head dims built: 128 for every call; 64 and 256 for the f16 and int8
-// caches' append, bounds, attention and step calls (CORE below).
+// caches' append, bounds, selection, attention (per-query-head and
+// token-chunk forms included) and step calls (kDimCore below).
 constexpr int32_t kFullDim = 128;
 bool core_head_dim(int32_t d) { return d == 64 || d == kFullDim || d == 256; }
 bool supported_group(int32_t g) { return g == 1 || g == 2 || g == 4 || g == 8; }
@@ -326,7 +327,7 @@ skv_status skv_decode_attn_select(const skv_cache* c, const float* q, int32_t n_
 skv_status skv_block_bounds_heads(const skv_cache* c, const float* q, int32_t n_heads,
                                   const int32_t* seq_len, int32_t max_len, float* score,
                                   hipStream_t stream) {
-  skv_status st = check_cache(c, true);
+  skv_status st = check_cache(c, true, kDimCore);
   if (st != SKV_OK) return st;
   if (q == nullptr || seq_len == nullptr || score == nullptr || !aligned(q)) return SKV_EINVAL;
   st = check_heads(c, n_heads);
@@ -358,7 +359,7 @@ skv_status skv_decode_attn_heads(const skv_cache* c, const float* q, int32_t n_h
                                  const uint32_t* uni_mask, int32_t max_union,
                                  float softmax_scale, int32_t n_split, void* workspace,
                                  size_t workspace_bytes, hipStream_t stream) {
-  skv_status st = check_cache(c, false);
+  skv_status st = check_cache(c, false, kDimCore);
   if (st != SKV_OK) return st;
   if (q == nullptr || seq_len == nullptr || !aligned(q)) return SKV_EINVAL;
   if (uni_idx == nullptr || uni_cnt == nullptr || uni_mask == nullptr || max_union < 1)
@@ -393,7 +394,7 @@ skv_status skv_decode_attn_heads(const skv_cache* c, const float* q, int32_t n_h
 skv_status skv_block_bounds_multi(const skv_cache* c, const float* q, int32_t n_tokens,
                                   int32_t n_heads, const int32_t* seq_len, int32_t max_len,
                                   float* score, hipStream_t stream) {
-  skv_status st = check_cache(c, true);
+  skv_status st = check_cache(c, true, kDimCore);
   if (st != SKV_OK) return st;
   if (q == nullptr || seq_len == nullptr || score == nullptr || !aligned(q)) return SKV_EINVAL;
   st = check_heads(c, n_heads);
@@ -450,7 +451,7 @@ skv_status skv_decode_attn_multi(const skv_cache* c, const float* q, int32_t n_t
                                  const uint32_t* uni_mask, int32_t max_union,
                                  float softmax_scale, int32_t n_split, void* workspace,
                                  size_t workspace_bytes, hipStream_t stream) {
-  skv_status st = check_cache(c, false);
+  skv_status st = check_cache(c, false, kDimCore);
   if (st != SKV_OK) return st;
   if (q == nullptr || seq_len == nullptr || !aligned(q)) return SKV_EINVAL;
   const bool list = uni_idx != nullptr;

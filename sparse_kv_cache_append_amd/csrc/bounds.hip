@@ -11,8 +11,8 @@
 // D = 128), so it is spread over as many workgroups as there are 16-block
 // tiles: 16 lanes per block, each lane holding D / 16 channels (at D = 128
 // one 16-byte load of kmin and one of kmax), a 16-lane DPP sum per head, then
-// the group max.  Head dims 64 and 256 take the plain pass (no folded append,
-// per-head scores or token chunks, vector scoring).
+// the group max.  Head dims 64 and 256 score on the vector units and take no
+// folded append.
 //
 // A decode step may fold its one-token append into this pass
 // (launch_append_bounds), which saves a launch and a dependent round trip.
@@ -401,13 +401,12 @@ bounds_kernel(uint16_t* __restrict__ kmin, uint16_t* __restrict__ kmax,
               float* __restrict__ score, int32_t Hkv, int32_t max_len, int32_t block,
               int32_t max_blocks, int32_t tiles, int32_t n_rows, AppendOne ap) {
   static_assert(D == 64 || D == 128 || D == 256, "head dims 64, 128, 256");
-  static_assert(D == 128 || (MODE == kNoAppend && !PH && NT == 1),
-                "head dims other than 128: plain bounds only");
+  static_assert(D == 128 || MODE == kNoAppend, "head dims other than 128: no folded append");
   static_assert(NT == 1 || (MODE == kNoAppend && !PH), "token chunks: plain bounds only");
   constexpr int CPL = D / kLanesPerBlock;                      // channels per lane
   constexpr int kQ4 = NT * G * D / 4;                          // 16-byte query loads
   constexpr int kQPer = (kQ4 + kBoundsThreads - 1) / kBoundsThreads;
-  static_assert(kQPer <= 2, "at most 16 query rows");
+  static_assert(kQPer <= 4, "at most 16 query rows of at most 256 channels");
   // 1-D grid of tiles x Hkv x batch, row by row (XCD-aware slots: a row's
   // scores are written on the XCD whose L2 its decode parts read them from)
   const uint32_t slot = xcd_slot(blockIdx.x, gridDim.x);
@@ -662,15 +661,15 @@ hipError_t launch_bounds_g(const skv_cache& c, const float* q, const int32_t* se
   return hipGetLastError();
 }
 
-template <int MODE, int D = 128>
+template <int MODE, int D = 128, bool PH = false>
 hipError_t launch_bounds_m(const skv_cache& c, const float* q, int32_t n_heads,
                            const int32_t* seq_len, int32_t max_len, float* score,
                            const AppendOne& ap, hipStream_t stream) {
   switch (n_heads / c.n_kv_heads) {
-    case 1: return launch_bounds_g<1, MODE, false, 1, D>(c, q, seq_len, max_len, score, ap, stream);
-    case 2: return launch_bounds_g<2, MODE, false, 1, D>(c, q, seq_len, max_len, score, ap, stream);
-    case 4: return launch_bounds_g<4, MODE, false, 1, D>(c, q, seq_len, max_len, score, ap, stream);
-    case 8: return launch_bounds_g<8, MODE, false, 1, D>(c, q, seq_len, max_len, score, ap, stream);
+    case 1: return launch_bounds_g<1, MODE, PH, 1, D>(c, q, seq_len, max_len, score, ap, stream);
+    case 2: return launch_bounds_g<2, MODE, PH, 1, D>(c, q, seq_len, max_len, score, ap, stream);
+    case 4: return launch_bounds_g<4, MODE, PH, 1, D>(c, q, seq_len, max_len, score, ap, stream);
+    case 8: return launch_bounds_g<8, MODE, PH, 1, D>(c, q, seq_len, max_len, score, ap, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -690,15 +689,17 @@ hipError_t launch_bounds(const skv_cache& c, const float* q, int32_t n_heads,
   }
 }
 
-hipError_t launch_bounds_multi(const skv_cache& c, const float* q, int32_t n_tok,
-                               int32_t n_heads, const int32_t* seq_len, int32_t max_len,
-                               float* score, hipStream_t stream) {
-  if (c.head_dim != 128) return hipErrorInvalidValue;
+namespace {
+
+template <int D>
+hipError_t launch_bounds_multi_d(const skv_cache& c, const float* q, int32_t n_tok,
+                                 int32_t n_heads, const int32_t* seq_len, int32_t max_len,
+                                 float* score, hipStream_t stream) {
   const AppendOne ap{};
   const int G = n_heads / c.n_kv_heads;
 #define SKV_BMT(GG, NN)                                                                        \
   if (G == GG && n_tok == NN)                                                                  \
-    return launch_bounds_g<GG, kNoAppend, false, NN>(c, q, seq_len, max_len, score, ap, stream)
+    return launch_bounds_g<GG, kNoAppend, false, NN, D>(c, q, seq_len, max_len, score, ap, stream)
   SKV_BMT(1, 1); SKV_BMT(2, 1); SKV_BMT(4, 1); SKV_BMT(8, 1);
   SKV_BMT(1, 2); SKV_BMT(1, 4); SKV_BMT(1, 8);
   SKV_BMT(2, 2); SKV_BMT(2, 4); SKV_BMT(2, 8);
@@ -708,16 +709,27 @@ hipError_t launch_bounds_multi(const skv_cache& c, const float* q, int32_t n_tok
   return hipErrorInvalidValue;
 }
 
+}  // namespace
+
+hipError_t launch_bounds_multi(const skv_cache& c, const float* q, int32_t n_tok,
+                               int32_t n_heads, const int32_t* seq_len, int32_t max_len,
+                               float* score, hipStream_t stream) {
+  switch (c.head_dim) {
+    case 64: return launch_bounds_multi_d<64>(c, q, n_tok, n_heads, seq_len, max_len, score, stream);
+    case 128: return launch_bounds_multi_d<128>(c, q, n_tok, n_heads, seq_len, max_len, score, stream);
+    case 256: return launch_bounds_multi_d<256>(c, q, n_tok, n_heads, seq_len, max_len, score, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 hipError_t launch_bounds_heads(const skv_cache& c, const float* q, int32_t n_heads,
                                const int32_t* seq_len, int32_t max_len, float* score,
                                hipStream_t stream) {
-  if (c.head_dim != 128) return hipErrorInvalidValue;
   const AppendOne ap{};
-  switch (n_heads / c.n_kv_heads) {
-    case 1: return launch_bounds_g<1, kNoAppend, true>(c, q, seq_len, max_len, score, ap, stream);
-    case 2: return launch_bounds_g<2, kNoAppend, true>(c, q, seq_len, max_len, score, ap, stream);
-    case 4: return launch_bounds_g<4, kNoAppend, true>(c, q, seq_len, max_len, score, ap, stream);
-    case 8: return launch_bounds_g<8, kNoAppend, true>(c, q, seq_len, max_len, score, ap, stream);
+  switch (c.head_dim) {
+    case 64: return launch_bounds_m<kNoAppend, 64, true>(c, q, n_heads, seq_len, max_len, score, ap, stream);
+    case 128: return launch_bounds_m<kNoAppend, 128, true>(c, q, n_heads, seq_len, max_len, score, ap, stream);
+    case 256: return launch_bounds_m<kNoAppend, 256, true>(c, q, n_heads, seq_len, max_len, score, ap, stream);
     default: return hipErrorInvalidValue;
   }
 }

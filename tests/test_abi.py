@@ -74,9 +74,9 @@ def test_cache_descriptor_validation(lib, kw, expect):
 
 @pytest.mark.parametrize("dim", [64, 256])
 def test_head_dims_64_256_core_calls_only(lib, dim):
-    """Head dims 64 and 256 pass the descriptor check of the core calls (the
-    calls below then stop at a later check, before any launch) and are
-    refused by the calls built for head dim 128 only."""
+    """Head dims 64 and 256 pass the descriptor check of the f16 and int8
+    calls (the calls below then stop at a later check, before any launch) and
+    are refused by the calls built for head dim 128 only."""
     d = desc(head_dim=dim)
     q = 0x7000
     # decode_attn: accepted, then the workspace is too small
@@ -92,10 +92,14 @@ def test_head_dims_64_256_core_calls_only(lib, dim):
     assert lib.skv_block_bounds(ctypes.byref(d), q, 32, BAD, 5000, BAD, None) == skv.SKV_ERANGE
     assert lib.skv_kv_append(ctypes.byref(d), BAD, 5000, q, q, skv.SKV_F16, None) == \
         skv.SKV_ERANGE
-    # head dim 128 only: per-head bounds and attention, sparse-V, chunks, the scan
-    assert lib.skv_block_bounds_heads(ctypes.byref(d), q, 32, BAD, 10, BAD, None) == \
-        skv.SKV_EUNSUPPORTED
-    assert lib.skv_block_bounds_multi(ctypes.byref(d), q, 2, 32, BAD, 10, BAD, None) == \
+    # per-head bounds and token chunks: accepted, then a range check fails
+    assert lib.skv_block_bounds_heads(ctypes.byref(d), q, 32, BAD, 5000, BAD, None) == \
+        skv.SKV_ERANGE
+    assert lib.skv_block_bounds_multi(ctypes.byref(d), q, 2, 32, BAD, 5000, BAD, None) == \
+        skv.SKV_ERANGE
+    # head dim 128 only: sparse-V, the scan, group-wise caches
+    g = desc(head_dim=dim, kv_dtype=skv.SKV_Q8_0, k_scale=0x5000, v_scale=0x6000)
+    assert lib.skv_kv_append(ctypes.byref(g), BAD, 1, q, q, skv.SKV_F32, None) == \
         skv.SKV_EUNSUPPORTED
     assert lib.skv_decode_attn_sparse_v(ctypes.byref(d), q, 32, BAD, 10, None, None, 0, 0.1,
                                         1e-3, 0.0, 4, BAD, 1 << 30, BAD, None) == \

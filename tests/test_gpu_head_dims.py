@@ -19,6 +19,11 @@ import oracle
 import workloads
 from gpu_harness import (DEV, assert_close, build_cache, padded_rows, quantized_host, rel_err,
                          run_dense, run_select, run_sparse)
+from test_gpu_multi_token import check_dense as chunk_check_dense
+from test_gpu_multi_token import check_quest as chunk_check_quest
+from test_gpu_multi_token import run_chunk
+from test_gpu_per_head import check as per_head_check
+from test_gpu_per_head import run_per_head
 from test_gpu_step import _oracle_check, _run_case
 
 import sparse_kv_cache_append_amd as skv
@@ -223,9 +228,53 @@ def test_decode_attn_select_equals_select_then_decode(gpu_lib, D, kv):
     assert torch.equal(ws_a, ws_b)
 
 
+@pytest.mark.parametrize("D", DIMS)
+@pytest.mark.parametrize("seeds,H,Hkv,lens,kv,ksel", [([861, 862], 32, 8, [5000, 777], "f16", [20, 4]),
+                                                      ([863], 16, 4, [4100], "i8", [12])])
+def test_per_head_selection(gpu_lib, D, seeds, H, Hkv, lens, kv, ksel):
+    """Per-query-head bounds, selection, union and attention at these head
+    dims (bit-equal group scores, exact selections and unions, outputs
+    element-wise)."""
+    _print("per-head", D, lens, kv)
+    w = workloads.clustered(seeds, H, Hkv, D, lens, kv, n_dirs=16, k_sel=ksel, n_sink=1,
+                            n_recent=2)
+    cache = build_cache(w)
+    r = run_per_head(cache, w)
+    per_head_check(w, r)
+
+
+@pytest.mark.parametrize("D", DIMS)
+@pytest.mark.parametrize("seeds,H,Hkv,lens,kv,T", [([871, 872], 32, 8, [700, 1537], "f16", 4),
+                                                   ([873], 32, 4, [2049], "i8", 2),
+                                                   ([874], 8, 8, [1000], "i8", 8)])
+def test_dense_chunk(gpu_lib, D, seeds, H, Hkv, lens, kv, T):
+    """A chunk of T query tokens (T x G MFMA columns, up to 16), dense."""
+    _print("dense chunk", D, lens, kv, T)
+    w = workloads.clustered(seeds, H, Hkv, D, lens, kv, n_dirs=16)
+    qc = workloads.chunk_queries(w, T, seeds[0] + 50)
+    cache = build_cache(w)
+    r = run_chunk(cache, w, qc, quest=False)
+    chunk_check_dense(w, qc, r)
+
+
+@pytest.mark.parametrize("D", DIMS)
+@pytest.mark.parametrize("seeds,H,Hkv,lens,kv,T,ksel", [([881, 882], 32, 8, [5000, 1800], "f16", 4, [12, 5]),
+                                                        ([883], 32, 4, [6001], "i8", 2, [20])])
+def test_quest_chunk(gpu_lib, D, seeds, H, Hkv, lens, kv, T, ksel):
+    """A chunk of T query tokens, each with its own Quest set."""
+    _print("quest chunk", D, lens, kv, T)
+    w = workloads.clustered(seeds, H, Hkv, D, lens, kv, n_dirs=16, k_sel=ksel, n_sink=1,
+                            n_recent=2)
+    qc = workloads.chunk_queries(w, T, seeds[0] + 60)
+    cache = build_cache(w)
+    r = run_chunk(cache, w, qc, quest=True)
+    chunk_check_quest(w, qc, r)
+
+
 def test_other_head_dims_are_refused(gpu_lib):
-    """Head dim 96 (a multiple of 16, not built) and the calls built for 128
-    only raise SKV_EUNSUPPORTED before any launch."""
+    """Head dim 96 (a multiple of 16, not built), and the calls built for 128
+    only (sparse-V, the 4-bit scan, group-wise caches) at 64, raise
+    SKV_EUNSUPPORTED before any launch."""
     _print("refused")
     c96 = skv.Cache(1, 2, 128, 96, "f16", 64, device=DEV)
     q = torch.zeros((1, 8, 96), dtype=torch.float32, device=DEV)
@@ -235,9 +284,13 @@ def test_other_head_dims_are_refused(gpu_lib):
         skv.block_bounds(c96, q, sl, 10, score)
     assert e.value.status == skv.SKV_EUNSUPPORTED
     c64 = skv.Cache(1, 2, 128, 64, "f16", 64, device=DEV)
-    q = torch.zeros((1, 8, 64), dtype=torch.float32, device=DEV)
-    score = torch.empty((1, 8, c64.max_blocks), dtype=torch.float32, device=DEV)
+    idx = skv.Scan4Index(c64, device=DEV)
     with pytest.raises(skv.SkvError) as e:
-        skv.block_bounds_heads(c64, q, sl, 10, score)
+        skv.scan4_build(c64, idx, torch.zeros(1, dtype=torch.int32, device=DEV), sl, 10)
+    assert e.value.status == skv.SKV_EUNSUPPORTED
+    g64 = skv.Cache(1, 2, 128, 64, "q8_0", 64, device=DEV)
+    k = torch.zeros((1, 1, 2, 64), dtype=torch.float32, device=DEV)
+    with pytest.raises(skv.SkvError) as e:
+        skv.kv_append(g64, torch.zeros(1, dtype=torch.int32, device=DEV), k, k)
     assert e.value.status == skv.SKV_EUNSUPPORTED
     torch.cuda.synchronize()
