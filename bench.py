@@ -41,6 +41,7 @@ import argparse
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -820,7 +821,8 @@ def main():
     ap.add_argument("--workloads", default="1,2,4,5,3@16384,3q8,3q4,3q5,3d64,3d256",
                     help="other workloads to time besides the 32K headline ('' = none; "
                          "3@L = the 32K Quest generator at context L; 3q8 / 3q4 / 3q5 = over a "
-                         "q8_0 / q4_0 / q5_0 cache; 3d64 / 3d256 = at head dim 64 / 256)")
+                         "q8_0 / q4_0 / q5_0 cache; 3d64 / 3d256 = at head dim 64 / 256; both, "
+                         "e.g. 3q4d256)")
     ap.add_argument("--chunk-tokens", type=int, default=4,
                     help="query tokens per chunk for the multi-token measurement (0 = off)")
     ap.add_argument("--no-per-head", action="store_true",
@@ -850,14 +852,13 @@ def main():
         if tok.startswith("3@"):
             # the 32K generator at another length (Quest vs dense from 16K up)
             jobs.append((workloads.quest32k_at(int(tok[2:])), True, True, False))
-        elif tok.startswith("3d"):
-            # the 32K generator at another head dim (3d64, 3d256)
-            jobs.append((workloads.quest32k_dim(int(tok[2:])), True, True, False))
-        elif tok.startswith("3q"):
-            # the 32K generator over a group-wise quantized cache (3q8, 3q4, 3q5)
-            jobs.append((workloads.quest32k_quant({"3q8": "q8_0", "3q4": "q4_0",
-                                                   "3q5": "q5_0"}[tok]), True,
-                         True, False))
+        elif tok != "3" and re.fullmatch(r"3(q[458])?(d\d+)?", tok):
+            # the 32K generator over a group-wise quantized cache (3q8, 3q4,
+            # 3q5) and / or at another head dim (3d64, 3d256, 3q4d256)
+            m = re.fullmatch(r"3(q[458])?(d\d+)?", tok)
+            kv = {None: "f16", "q8": "q8_0", "q4": "q4_0", "q5": "q5_0"}[m.group(1)]
+            D = int(m.group(2)[1:]) if m.group(2) else 128
+            jobs.append((workloads.quest32k_dim(D, kv), True, True, False))
         elif int(tok) != 3:
             w = workloads.named(int(tok))
             jobs.append((w, bool(w.k_sel), True, False))

@@ -12,9 +12,9 @@ constexpr int32_t kMaxSplit = 4096;
 constexpr int32_t kMaxSelectBlocks = 16384;
 
 bool valid_head_dim(int32_t d) { return d >= 16 && d <= 1024 && d % 16 == 0; }
-// Head dims built: 128 for every call; 64 and 256 for the f16 and int8
-// caches' append, bounds, selection, attention (per-query-head and
-// token-chunk forms included) and step calls (kDimCore below).
+// Head dims built: 128 for every call; 64 and 256 for the append, bounds,
+// selection, attention (per-query-head and token-chunk forms included) and
+// step calls of every cache type they take (kDimCore below).
 constexpr int32_t kFullDim = 128;
 bool core_head_dim(int32_t d) { return d == 64 || d == kFullDim || d == 256; }
 bool supported_group(int32_t g) { return g == 1 || g == 2 || g == 4 || g == 8; }
@@ -53,8 +53,7 @@ skv_status check_cache(const skv_cache* c, bool need_bounds, DimUse dims = kDim1
   if (elems > 4.0e18) return SKV_ERANGE;
   if (c->batch > kMaxGridYZ || c->n_kv_heads > kMaxGridYZ) return SKV_ERANGE;
   if (!grid_fits(blocks_of(c->max_seq, c->block), c->n_kv_heads, c->batch)) return SKV_ERANGE;
-  if (c->head_dim != kFullDim &&
-      (dims != kDimCore || !core_head_dim(c->head_dim) || skv::is_grouped(c->kv_dtype)))
+  if (c->head_dim != kFullDim && (dims != kDimCore || !core_head_dim(c->head_dim)))
     return SKV_EUNSUPPORTED;
   return SKV_OK;
 }

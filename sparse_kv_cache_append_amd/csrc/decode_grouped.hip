@@ -1,4 +1,5 @@
-// Group-wise quantized caches (q8_0, q4_0): append and decode attention.
+// Group-wise quantized caches (q8_0, q4_0, q5_0): append and decode
+// attention at head dims D = 64, 128, 256.
 //
 // opencoti-llamafile sparse_attn.md, "All-KV-types composition": the side
 // cache of the block selector is filled from the keys before quantization, so
@@ -9,14 +10,14 @@
 // ("Requirements and limits") contrasts its per-token scale with such
 // group-wise scaling within a row.
 //
-// Layout: codes [batch][n_kv_heads][max_seq][row] with row = 128 bytes
-// (q8_0, int8 codes -127..127) or 64 bytes (q4_0: channel 2i in the low
+// Layout: codes [batch][n_kv_heads][max_seq][row] with row = D bytes
+// (q8_0, int8 codes -127..127) or D / 2 bytes (q4_0: channel 2i in the low
 // nibble of byte i, channel 2i + 1 in the high nibble, each code + 8 with
 // codes -7..7); q5_0 (codes -15..15, stored as code + 16 in five bits): per
-// (sequence, KV head) a plane of max_seq 64-byte nibble rows (bits 0..3, as
-// q4_0) followed by a plane of max_seq 16-byte rows of the fifth bits (bit
-// c % 8 of byte c / 8 for channel c); scales [batch][n_kv_heads][max_seq][4]
-// f16, one per group of 32 channels.  Per group: a = max |x|,
+// (sequence, KV head) a plane of max_seq D / 2-byte nibble rows (bits 0..3,
+// as q4_0) followed by a plane of max_seq D / 8-byte rows of the fifth bits
+// (bit c % 8 of byte c / 8 for channel c); scales
+// [batch][n_kv_heads][max_seq][D / 32] f16, one per group of 32 channels.  Per group: a = max |x|,
 // s = f16(a / QMAX) (QMAX 127, 7 or 15),
 // code = clamp(rint(x / s), -QMAX, QMAX) against the stored scale, so a value
 // is exactly s * code (s == 0 or not finite: codes 0).
@@ -48,28 +49,32 @@ namespace skv {
 namespace {
 
 constexpr int kGroup = 32;
-constexpr int kGroups = kD / kGroup;        // 4
 
 enum GrpKind { kQ8 = 0, kQ4 = 1, kQ5 = 2 };
-template <int K>
+// Format K at head dim D (64, 128 or 256: D / 32 groups per row).
+template <int K, int D = kD>
 struct GrpFmt {
+  static_assert(D == 64 || D == 128 || D == 256, "head dims 64, 128, 256");
   static constexpr bool kNib = K != kQ8;                   // nibble plane (q4_0, q5_0)
   static constexpr int kQmax = K == kQ8 ? 127 : K == kQ4 ? 7 : 15;
   static constexpr int kBias = K == kQ8 ? 0 : kQmax + 1;   // stored = code + bias
-  static constexpr int kRowBytes = kNib ? kD / 2 : kD;     // code / nibble row bytes
-  static constexpr int kHiBytes = K == kQ5 ? kD / 8 : 0;   // fifth-bit row bytes
+  static constexpr int kGroups = D / kGroup;               // 32-channel groups per row
+  static constexpr int kRowBytes = kNib ? D / 2 : D;       // code / nibble row bytes
+  static constexpr int kHiBytes = K == kQ5 ? D / 8 : 0;    // fifth-bit row bytes
   static constexpr int kTokBytes = kRowBytes + kHiBytes;   // per (token, KV head)
+  static constexpr int kOcc = D > 128 ? 1 : 2;             // workgroups per CU (decode)
 };
 // Byte offsets of token t of row bg (sequence x KV head): its code (or
 // nibble) row and, for q5_0, its fifth-bit row.
-template <int K>
+template <int K, int D = kD>
 __device__ __forceinline__ int64_t grp_row_off(int64_t bg, int32_t max_seq, int64_t t) {
-  return bg * max_seq * GrpFmt<K>::kTokBytes + t * GrpFmt<K>::kRowBytes;
+  using F = GrpFmt<K, D>;
+  return bg * max_seq * F::kTokBytes + t * F::kRowBytes;
 }
-template <int K>
+template <int K, int D = kD>
 __device__ __forceinline__ int64_t grp_hi_off(int64_t bg, int32_t max_seq, int64_t t) {
-  return bg * max_seq * GrpFmt<K>::kTokBytes + int64_t(max_seq) * GrpFmt<K>::kRowBytes +
-         t * GrpFmt<K>::kHiBytes;
+  using F = GrpFmt<K, D>;
+  return bg * max_seq * F::kTokBytes + int64_t(max_seq) * F::kRowBytes + t * F::kHiBytes;
 }
 // The fifth bits of 32 channels as a 32-bit word (bit i = channel i) from the
 // two ballots of a row (lane l: h0 bit l = channel 2l, h1 bit l = channel
@@ -96,12 +101,13 @@ __device__ __forceinline__ int grp_code(float x, float s, int qmax) {
 
 // ------------------------------------------------------------------ append
 // One workgroup per (sequence, KV head, block touched by the append); one
-// wavefront per new row: lane l holds channels 2l, 2l + 1, a group is 16 lanes
-// (one DPP row, whose max gives the group's absmax).  Bounds as for the int8
-// cache: the float32 keys' min / max rounded outward to f16.
+// wavefront per new row, a 128-channel slice at a time: lane l holds channels
+// 2l, 2l + 1 of the slice, a group is 16 lanes (one DPP row, whose max gives
+// the group's absmax); at D = 64 lanes 32..63 hold nothing.  Bounds as for
+// the int8 cache: the float32 keys' min / max rounded outward to f16.
 constexpr int kAppendThreads = 256;
 
-template <int K>
+template <int K, int D>
 __global__ void __launch_bounds__(kAppendThreads)
 append_grp_kernel(uint8_t* __restrict__ kc, uint8_t* __restrict__ vc,
                   uint16_t* __restrict__ ksc, uint16_t* __restrict__ vsc,
@@ -109,7 +115,8 @@ append_grp_kernel(uint8_t* __restrict__ kc, uint8_t* __restrict__ vc,
                   const float* __restrict__ kn, const float* __restrict__ vn,
                   const int32_t* __restrict__ pos0, int32_t n_new, int32_t Hkv,
                   int32_t max_seq, int32_t block, int32_t max_blocks) {
-  using F = GrpFmt<K>;
+  using F = GrpFmt<K, D>;
+  constexpr int kSlices = (D + 127) / 128;
   const int32_t g = blockIdx.y, b = blockIdx.z;
   const int32_t p0 = pos0[b];
   if (p0 < 0) return;
@@ -120,44 +127,52 @@ append_grp_kernel(uint8_t* __restrict__ kc, uint8_t* __restrict__ vc,
   const int32_t t0 = int32_t(lo64), t1 = int32_t(hi64);
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   for (int32_t t = t0 + wave; t < t1; t += kAppendThreads / kWave) {
-    const int64_t src = ((int64_t(b) * n_new + (t - p0)) * Hkv + g) * kD;
+    const int64_t src = ((int64_t(b) * n_new + (t - p0)) * Hkv + g) * D;
     const int64_t bg = int64_t(b) * Hkv + g;
     const int64_t row = bg * max_seq + t;
 #pragma unroll
     for (int which = 0; which < 2; ++which) {
-      const float2 x = reinterpret_cast<const float2*>((which == 0 ? kn : vn) + src)[lane];
-      const float a = group16_max(fmaxf(fmaxf(0.0f, fabsf(x.x)), fabsf(x.y)));
-      const uint16_t sb = grp_scale_bits(a, F::kQmax);
-      const float s = h2f(sb);
-      const int c0 = grp_code(x.x, s, F::kQmax), c1 = grp_code(x.y, s, F::kQmax);
-      uint8_t* base = which == 0 ? kc : vc;
-      uint8_t* dst = base + grp_row_off<K>(bg, max_seq, t);
-      if constexpr (F::kNib) {
-        const int u0 = c0 + F::kBias, u1 = c1 + F::kBias;
-        dst[lane] = uint8_t((u0 & 15) | ((u1 & 15) << 4));
-        if constexpr (K == kQ5) {
-          const uint64_t h0 = __ballot(u0 >> 4), h1 = __ballot(u1 >> 4);
-          if (lane < 4)
-            reinterpret_cast<uint32_t*>(base + grp_hi_off<K>(bg, max_seq, t))[lane] =
-                q5_hi_word(h0, h1, lane);
+#pragma unroll
+      for (int sl = 0; sl < kSlices; ++sl) {
+        const bool on = D >= 128 || 2 * lane < D;          // D = 64: lanes 0..31
+        const float2 x = on ? reinterpret_cast<const float2*>((which == 0 ? kn : vn) + src)[64 * sl + lane]
+                            : make_float2(0.0f, 0.0f);
+        const float a = group16_max(fmaxf(fmaxf(0.0f, fabsf(x.x)), fabsf(x.y)));
+        const uint16_t sb = grp_scale_bits(a, F::kQmax);
+        const float s = h2f(sb);
+        const int c0 = grp_code(x.x, s, F::kQmax), c1 = grp_code(x.y, s, F::kQmax);
+        uint8_t* base = which == 0 ? kc : vc;
+        uint8_t* dst = base + grp_row_off<K, D>(bg, max_seq, t);
+        if constexpr (F::kNib) {
+          const int u0 = c0 + F::kBias, u1 = c1 + F::kBias;
+          if (on) dst[64 * sl + lane] = uint8_t((u0 & 15) | ((u1 & 15) << 4));
+          if constexpr (K == kQ5) {
+            const uint64_t h0 = __ballot(u0 >> 4), h1 = __ballot(u1 >> 4);
+            if (lane < 4 && 128 * sl + 32 * lane < D)
+              reinterpret_cast<uint32_t*>(base + grp_hi_off<K, D>(bg, max_seq, t))[4 * sl + lane] =
+                  q5_hi_word(h0, h1, lane);
+          }
+        } else {
+          if (on)
+            reinterpret_cast<uint16_t*>(dst)[64 * sl + lane] =
+                uint16_t((c0 & 0xFF) | ((c1 & 0xFF) << 8));
         }
-      } else {
-        reinterpret_cast<uint16_t*>(dst)[lane] = uint16_t((c0 & 0xFF) | ((c1 & 0xFF) << 8));
+        if (on && lane % 16 == 0)
+          (which == 0 ? ksc : vsc)[row * F::kGroups + 4 * sl + lane / 16] = sb;
       }
-      if (lane % 16 == 0) (which == 0 ? ksc : vsc)[row * kGroups + lane / 16] = sb;
     }
   }
   if (kmin == nullptr) return;
   const bool fresh = int64_t(j) * block >= p0;
-  for (int32_t d = threadIdx.x; d < kD; d += kAppendThreads) {
+  for (int32_t d = threadIdx.x; d < D; d += kAppendThreads) {
     float mn = INFINITY, mx = -INFINITY;
     for (int32_t t = t0; t < t1; ++t) {
-      const float x = kn[((int64_t(b) * n_new + (t - p0)) * Hkv + g) * kD + d];
+      const float x = kn[((int64_t(b) * n_new + (t - p0)) * Hkv + g) * D + d];
       mn = fminf(mn, x);
       mx = fmaxf(mx, x);
     }
     uint16_t bmn = f32_to_f16_down(mn), bmx = f32_to_f16_up(mx);
-    const int64_t o = ((int64_t(b) * Hkv + g) * max_blocks + j) * kD + d;
+    const int64_t o = ((int64_t(b) * Hkv + g) * max_blocks + j) * D + d;
     if (!fresh) {
       bmn = f16_min_bits(kmin[o], bmn);
       bmx = f16_max_bits(kmax[o], bmx);
@@ -241,8 +256,8 @@ constexpr int kPwShiftGrp = 7;
 
 // SELR > 0: the block selection runs in the prologue (fused_walk), as in the
 // f16 and int8 attention kernels.
-template <int G, int K, int SELR = 0>
-__global__ void __launch_bounds__(kMThreads, 2)
+template <int G, int K, int SELR, int D>
+__global__ void __launch_bounds__(kMThreads, (GrpFmt<K, D>::kOcc))
 decode_grp_mfma(const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
                 const uint16_t* __restrict__ ksc, const uint16_t* __restrict__ vsc,
                 const float* __restrict__ q, const int32_t* __restrict__ seq_len,
@@ -251,14 +266,20 @@ decode_grp_mfma(const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
                 int32_t n_split, int32_t n_rows, int32_t units_per_split, float qscale2,
                 float* __restrict__ ws_m, float* __restrict__ ws_l, float* __restrict__ ws_o,
                 FusedSelect fs) {
-  using F = GrpFmt<K>;
+  using F = GrpFmt<K, D>;
   constexpr bool Q5 = K == kQ5;
+  constexpr int KG = F::kGroups;
   constexpr int T = 32;
-  constexpr int kCodeBytes = T * kRowBytesI8;               // 4096 (int8 codes in LDS)
-  constexpr int kScaleOff = 2 * kCodeBytes;                 // K, V scales as float [T][4]
-  constexpr int kBufBytes = 2 * kCodeBytes + 2 * T * kGroups * 4;
+  constexpr int kCpr = D / 16;                              // LDS chunks per code row
+  constexpr int kCodeBytes = T * D;                         // int8 codes in LDS (4 KiB at 128)
+  constexpr int kScaleOff = 2 * kCodeBytes;                 // K, V scales as float [T][KG]
+  constexpr int kBufBytes = 2 * kCodeBytes + 2 * T * KG * 4;
   constexpr int kTileBytes = T * F::kRowBytes;              // HBM bytes of a code tile
-  constexpr int kLoads = F::kNib ? 2 : 4;                   // 16-byte code loads per lane
+  constexpr int kLoads = kTileBytes / 1024;                 // 16-byte code loads per lane
+  constexpr int kHcpr = F::kRowBytes / 16;                  // HBM chunks per code row
+  constexpr int kHrpl = 1024 / F::kRowBytes;                // HBM rows per load instruction
+  constexpr int kSb = KG;                                   // scale bytes per lane and tile
+  static_assert(kLoads >= 1, "a tile is at least one load per lane");
   __shared__ __attribute__((aligned(16))) uint8_t smem[kMWaves][2][kBufBytes];
   const uint32_t slot = xcd_slot(blockIdx.x, gridDim.x);
   const int32_t split = int32_t(slot % uint32_t(n_split));
@@ -275,12 +296,12 @@ decode_grp_mfma(const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
     ls = list_seed(sel_idx, sel_cnt, max_sel, bg, split, units_per_split);
   // query as the B operand of the per-group q.K: column = head lc, k-chunk lg
   // of group kk = channels 32 kk + 8 lg .. + 7; f16 high + low parts
-  half8_t qhi[kGroups], qlo[kGroups];
+  half8_t qhi[KG], qlo[KG];
   {
     const bool hv = lc < G;
-    const float* qp = q + (int64_t(b) * H + g * G + (hv ? lc : 0)) * kD;
+    const float* qp = q + (int64_t(b) * H + g * G + (hv ? lc : 0)) * D;
 #pragma unroll
-    for (int kk = 0; kk < kGroups; ++kk) {
+    for (int kk = 0; kk < KG; ++kk) {
       const float4 a = *reinterpret_cast<const float4*>(qp + 32 * kk + 8 * lg);
       const float4 c = *reinterpret_cast<const float4*>(qp + 32 * kk + 8 * lg + 4);
       const float x[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
@@ -301,23 +322,29 @@ decode_grp_mfma(const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
     tw = make_walk<T>(ls, sel_idx, max_sel, bg, L, block, split, units_per_split);
   tw.init(wave);
   float m_run = -INFINITY, l_run = 0.0f;
-  float4_t O[8];
+  float4_t O[2 * KG];
 #pragma unroll
-  for (int n = 0; n < 8; ++n) O[n] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
-  const uint8_t* kbase = kc + grp_row_off<K>(bg, max_seq, 0);
-  const uint8_t* vbase = vc + grp_row_off<K>(bg, max_seq, 0);
-  const uint8_t* khbase = kc + grp_hi_off<K>(bg, max_seq, 0);       // q5_0 fifth bits
-  const uint8_t* vhbase = vc + grp_hi_off<K>(bg, max_seq, 0);
-  const uint8_t* ksb = reinterpret_cast<const uint8_t*>(ksc + bg * int64_t(max_seq) * kGroups);
-  const uint8_t* vsb = reinterpret_cast<const uint8_t*>(vsc + bg * int64_t(max_seq) * kGroups);
-  // Lane loads, per code tile: q8_0 row 8 i + lane / 8, 16-byte chunk lane % 8
-  // (i = 0..3); q4_0 row 16 i + lane / 4, chunk lane % 4 of the 64-byte row
-  // (i = 0..1).  Scales: 4 bytes per lane = the two f16 scales of groups
-  // 2 (lane % 2), + 1 of token lane / 2.  Buffer resources with the tile's
+  for (int n = 0; n < 2 * KG; ++n) O[n] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  const uint8_t* kbase = kc + grp_row_off<K, D>(bg, max_seq, 0);
+  const uint8_t* vbase = vc + grp_row_off<K, D>(bg, max_seq, 0);
+  const uint8_t* khbase = kc + grp_hi_off<K, D>(bg, max_seq, 0);       // q5_0 fifth bits
+  const uint8_t* vhbase = vc + grp_hi_off<K, D>(bg, max_seq, 0);
+  const uint8_t* ksb = reinterpret_cast<const uint8_t*>(ksc + bg * int64_t(max_seq) * KG);
+  const uint8_t* vsb = reinterpret_cast<const uint8_t*>(vsc + bg * int64_t(max_seq) * KG);
+  // Lane loads, per code tile: 16-byte chunk lane % kHcpr of row
+  // kHrpl i + lane / kHcpr (q8_0 at D = 128: row 8 i + lane / 8; q4_0 / q5_0
+  // at D = 128: row 16 i + lane / 4 of 64-byte nibble rows, 32 channels per
+  // chunk).  Scales: KG bytes per lane = the KG / 2 f16 scales of groups
+  // (lane % 2) KG / 2 .. of token lane / 2.  Buffer resources with the tile's
   // valid bytes: rows past the length read as zeros.
-  // q5_0 also: the fifth bits of the lane's 32 channels of each of its two
-  // rows (4 bytes at 256 i + 4 lane of the tile's fifth-bit rows)
-  struct Frag { int4_t k[kLoads], v[kLoads]; uint32_t kh[2], vh[2], ks, vs; int32_t r0, nvalid; };
+  // q5_0 also: the fifth bits of the lane's 32 channels of each of its rows
+  // (4 bytes at 256 i + 4 lane of the tile's fifth-bit rows, at every D)
+  struct Frag {
+    int4_t k[kLoads], v[kLoads];
+    uint32_t kh[kLoads], vh[kLoads];
+    uint2 ks, vs;
+    int32_t r0, nvalid;
+  };
   auto issue = [&](Frag& f) {
     int32_t r0 = 0, nv = 0;
     if (tw.more()) tw.next<T>(r0, nv);
@@ -337,34 +364,54 @@ decode_grp_mfma(const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
       const auto khr = tile_rsrc(khbase + int64_t(r0) * F::kHiBytes, hbytes);
       const auto vhr = tile_rsrc(vhbase + int64_t(r0) * F::kHiBytes, hbytes);
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
+      for (int i = 0; i < kLoads; ++i) {
         f.kh[i] = __builtin_amdgcn_raw_buffer_load_b32(khr, 256u * i + 4u * uint32_t(lane), 0,
                                                         kAuxNontemporal);
         f.vh[i] = __builtin_amdgcn_raw_buffer_load_b32(vhr, 256u * i + 4u * uint32_t(lane), 0,
                                                         kAuxNontemporal);
       }
     }
-    const int sbytes = __builtin_amdgcn_readfirstlane(max(nv, 0) * kGroups * 2);
-    const auto ksr = tile_rsrc(ksb + int64_t(r0) * kGroups * 2, sbytes);
-    const auto vsr = tile_rsrc(vsb + int64_t(r0) * kGroups * 2, sbytes);
-    f.ks = __builtin_amdgcn_raw_buffer_load_b32(ksr, 4u * uint32_t(lane), 0, kAuxNontemporal);
-    f.vs = __builtin_amdgcn_raw_buffer_load_b32(vsr, 4u * uint32_t(lane), 0, kAuxNontemporal);
+    const int sbytes = __builtin_amdgcn_readfirstlane(max(nv, 0) * KG * 2);
+    const auto ksr = tile_rsrc(ksb + int64_t(r0) * KG * 2, sbytes);
+    const auto vsr = tile_rsrc(vsb + int64_t(r0) * KG * 2, sbytes);
+    if constexpr (kSb == 2) {
+      f.ks = make_uint2(__builtin_amdgcn_raw_buffer_load_b16(ksr, 2u * uint32_t(lane), 0,
+                                                             kAuxNontemporal), 0u);
+      f.vs = make_uint2(__builtin_amdgcn_raw_buffer_load_b16(vsr, 2u * uint32_t(lane), 0,
+                                                             kAuxNontemporal), 0u);
+    } else if constexpr (kSb == 4) {
+      f.ks = make_uint2(__builtin_amdgcn_raw_buffer_load_b32(ksr, 4u * uint32_t(lane), 0,
+                                                             kAuxNontemporal), 0u);
+      f.vs = make_uint2(__builtin_amdgcn_raw_buffer_load_b32(vsr, 4u * uint32_t(lane), 0,
+                                                             kAuxNontemporal), 0u);
+    } else {
+      typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+      const u32x2 a = __builtin_bit_cast(
+          u32x2, __builtin_amdgcn_raw_buffer_load_b64(ksr, 8u * uint32_t(lane), 0, kAuxNontemporal));
+      const u32x2 c = __builtin_bit_cast(
+          u32x2, __builtin_amdgcn_raw_buffer_load_b64(vsr, 8u * uint32_t(lane), 0, kAuxNontemporal));
+      f.ks = make_uint2(a.x, a.y);
+      f.vs = make_uint2(c.x, c.y);
+    }
   };
-  static_assert(kTileBytes <= kTileRsrcBytes, "one buffer resource per tile");
-  auto sw = [](int rw, int chunk) { return rw * kRowBytesI8 + 16 * (chunk ^ (rw & 7)); };
+  static_assert(kLoads * 1024 == kTileBytes, "whole 16-byte loads per lane");
+  constexpr int kSwz = kCpr < 16 ? kCpr : 16;
+  auto sw = [](int rw, int chunk) { return rw * D + 16 * (chunk ^ (rw & (kSwz - 1))); };
   constexpr int kExpUnset = -100000;
   int e_run = kExpUnset;
+  constexpr int SPL = KG / 2;          // scales per lane: groups (lane % 2) SPL .. of token lane / 2
+  typedef float floatS __attribute__((ext_vector_type(SPL)));
 
   auto process = [&](auto bufc, Frag& fr) {
     constexpr int kBuf = decltype(bufc)::value;
     uint8_t* kt = smem[wave][kBuf];
     uint8_t* vt = kt + kCodeBytes;
-    float* stk = reinterpret_cast<float*>(kt + kScaleOff);          // [T][4]
-    float* stv = stk + T * kGroups;
+    float* stk = reinterpret_cast<float*>(kt + kScaleOff);          // [T][KG]
+    float* stv = stk + T * KG;
     if constexpr (F::kNib) {
 #pragma unroll
       for (int i = 0; i < kLoads; ++i) {
-        const int rw = 16 * i + lane / 4, ch = 2 * (lane % 4);
+        const int rw = kHrpl * i + lane / kHcpr, ch = 2 * (lane % kHcpr);
         int4_t a0, a1;
         if constexpr (Q5) unpack_q5(fr.k[i], fr.kh[i], a0, a1);
         else unpack_q4(fr.k[i], a0, a1);
@@ -378,17 +425,24 @@ decode_grp_mfma(const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
     } else {
 #pragma unroll
       for (int i = 0; i < kLoads; ++i) {
-        const int rw = 8 * i + lane / 8;
-        *reinterpret_cast<int4_t*>(kt + sw(rw, lane % 8)) = fr.k[i];
-        *reinterpret_cast<int4_t*>(vt + sw(rw, lane % 8)) = fr.v[i];
+        const int rw = kHrpl * i + lane / kHcpr;
+        *reinterpret_cast<int4_t*>(kt + sw(rw, lane % kHcpr)) = fr.k[i];
+        *reinterpret_cast<int4_t*>(vt + sw(rw, lane % kHcpr)) = fr.v[i];
       }
     }
-    // scales: f16 pairs to float; V scales in the running power-of-two unit
+    // scales: f16 to float; V scales in the running power-of-two unit
     // 2^e_run >= every V scale so far, times 2^kPwShiftGrp
-    const float k0 = h2f_lo(fr.ks), k1 = h2f_hi(fr.ks);
-    const float v0 = h2f_lo(fr.vs), v1 = h2f_hi(fr.vs);
-    const int32_t vbits =
-        __builtin_amdgcn_readfirstlane(__float_as_int(wave_max(fmaxf(v0, v1))));
+    float kv[SPL], vv[SPL];
+#pragma unroll
+    for (int j = 0; j < SPL; ++j) {
+      const uint32_t kw = j < 2 ? fr.ks.x : fr.ks.y, vw = j < 2 ? fr.vs.x : fr.vs.y;
+      kv[j] = (j & 1) ? h2f_hi(kw) : h2f_lo(kw);
+      vv[j] = (j & 1) ? h2f_hi(vw) : h2f_lo(vw);
+    }
+    float vmx = vv[0];
+#pragma unroll
+    for (int j = 1; j < SPL; ++j) vmx = fmaxf(vmx, vv[j]);
+    const int32_t vbits = __builtin_amdgcn_readfirstlane(__float_as_int(wave_max(vmx)));
     float unit = 1.0f;
     if (vbits > 0 && vbits < 0x7F800000) {
       const int32_t ex =
@@ -401,18 +455,25 @@ decode_grp_mfma(const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
       }
     }
     const int e_use = e_run == kExpUnset ? 0 : e_run;
-    reinterpret_cast<float2*>(stk)[lane] = make_float2(k0, k1);
-    reinterpret_cast<float2*>(stv)[lane] =
-        make_float2(ldexpf(v0, kPwShiftGrp - e_use), ldexpf(v1, kPwShiftGrp - e_use));
+    {
+      floatS ks4, vs4;
+#pragma unroll
+      for (int j = 0; j < SPL; ++j) {
+        ks4[j] = kv[j];
+        vs4[j] = ldexpf(vv[j], kPwShiftGrp - e_use);
+      }
+      reinterpret_cast<floatS*>(stk)[lane] = ks4;
+      reinterpret_cast<floatS*>(stv)[lane] = vs4;
+    }
     const int32_t nvalid = fr.nvalid;
     issue(fr);
     // q.K per group: two 16-token halves, one MFMA pair per 32-channel group
     float sc[8];
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      float4_t acc[kGroups];
+      float4_t acc[KG];
 #pragma unroll
-      for (int kk = 0; kk < kGroups; ++kk) {
+      for (int kk = 0; kk < KG; ++kk) {
         const int rw = 16 * s + lc;
         const int2_t raw = *reinterpret_cast<const int2_t*>(kt + sw(rw, 2 * kk + lg / 2) +
                                                             8 * (lg & 1));
@@ -423,9 +484,24 @@ decode_grp_mfma(const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float4 kss = *reinterpret_cast<const float4*>(stk + (16 * s + 4 * lg + r) * kGroups);
-        sc[4 * s + r] = acc[0][r] * kss.x + acc[1][r] * kss.y + acc[2][r] * kss.z +
-                        acc[3][r] * kss.w;
+        const float* kr = stk + (16 * s + 4 * lg + r) * KG;
+        if constexpr (KG == 4) {
+          const float4 kss = *reinterpret_cast<const float4*>(kr);
+          sc[4 * s + r] = acc[0][r] * kss.x + acc[1][r] * kss.y + acc[2][r] * kss.z +
+                          acc[3][r] * kss.w;
+        } else {
+          float kss[KG];
+#pragma unroll
+          for (int kk = 0; kk < KG; kk += 2) {
+            const float2 v2 = *reinterpret_cast<const float2*>(kr + kk);
+            kss[kk] = v2.x;
+            kss[kk + 1] = v2.y;
+          }
+          float a = acc[0][r] * kss[0];
+#pragma unroll
+          for (int kk = 1; kk < KG; ++kk) a += acc[kk][r] * kss[kk];
+          sc[4 * s + r] = a;
+        }
       }
     }
     if (nvalid < T) {
@@ -437,18 +513,28 @@ decode_grp_mfma(const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
     // P.V: per 16-channel block n (group n / 2), A = weight x V scale of
     // (token tok(lg, e), group), f16 high + low; B = V codes of channels
     // 16 n + lc for tokens tok(lg, 0..7) (the int8 kernel's transposing read)
-    float4 vsr[8];
+    float vsr[8][KG];
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-      vsr[e] = *reinterpret_cast<const float4*>(stv + (16 * (e / 4) + 4 * lg + e % 4) * kGroups);
+    for (int e = 0; e < 8; ++e) {
+      const float* vr = stv + (16 * (e / 4) + 4 * lg + e % 4) * KG;
+#pragma unroll
+      for (int kk = 0; kk < KG; kk += 2) {
+        if (KG >= 4 && kk % 4 == 0) {
+          const float4 v4 = *reinterpret_cast<const float4*>(vr + kk);
+          vsr[e][kk] = v4.x; vsr[e][kk + 1] = v4.y; vsr[e][kk + 2] = v4.z; vsr[e][kk + 3] = v4.w;
+        } else if (KG < 4) {
+          const float2 v2 = *reinterpret_cast<const float2*>(vr + kk);
+          vsr[e][kk] = v2.x; vsr[e][kk + 1] = v2.y;
+        }
+      }
+    }
     const int tr_row = 16 * ((lc / 2) / 4) + 4 * lg + (lc / 2) % 4;
 #pragma unroll
-    for (int grp = 0; grp < kGroups; ++grp) {
+    for (int grp = 0; grp < KG; ++grp) {
       half8_t phi, plo;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float vsg = grp == 0 ? vsr[e].x : grp == 1 ? vsr[e].y : grp == 2 ? vsr[e].z
-                                                                                 : vsr[e].w;
+        const float vsg = vsr[e][grp];
         const float pw = sc[e] * vsg;
         const _Float16 h = (_Float16)pw;
         phi[e] = h;
@@ -477,7 +563,7 @@ decode_grp_mfma(const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
   if (n_mine & 1) process(std::integral_constant<int, 0>{}, f0);
   if (e_run != kExpUnset) {
 #pragma unroll
-    for (int n = 0; n < 8; ++n) {
+    for (int n = 0; n < 2 * KG; ++n) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) O[n][r] = ldexpf(O[n][r], e_run - kPwShiftGrp);
     }
@@ -488,15 +574,18 @@ decode_grp_mfma(const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
 
 }  // namespace
 
-hipError_t launch_append_grouped(const skv_cache& c, const int32_t* pos0, int32_t n_new,
-                                 const void* k_new, const void* v_new, hipStream_t stream) {
+namespace {
+
+template <int D>
+hipError_t launch_append_grouped_d(const skv_cache& c, const int32_t* pos0, int32_t n_new,
+                                   const void* k_new, const void* v_new, hipStream_t stream) {
   const int32_t max_blocks = (c.max_seq + c.block - 1) / c.block;
   const int32_t n_aff = (n_new + c.block - 2) / c.block + 1;
   const dim3 grid(n_aff, c.n_kv_heads, c.batch);
   uint16_t* ks = reinterpret_cast<uint16_t*>(c.k_scale);
   uint16_t* vs = reinterpret_cast<uint16_t*>(c.v_scale);
 #define SKV_APP_GRP(KK)                                                                         \
-  append_grp_kernel<KK><<<grid, kAppendThreads, 0, stream>>>(                                   \
+  append_grp_kernel<KK, D><<<grid, kAppendThreads, 0, stream>>>(                                \
       static_cast<uint8_t*>(c.k), static_cast<uint8_t*>(c.v), ks, vs, c.kmin, c.kmax,          \
       static_cast<const float*>(k_new), static_cast<const float*>(v_new), pos0, n_new,         \
       c.n_kv_heads, c.max_seq, c.block, max_blocks)
@@ -510,14 +599,10 @@ hipError_t launch_append_grouped(const skv_cache& c, const int32_t* pos0, int32_
   return hipGetLastError();
 }
 
-hipError_t launch_decode_grouped(const DecodeParams& p, hipStream_t stream) {
+template <int D>
+hipError_t launch_decode_grouped_d(const DecodeParams& p, int G, hipStream_t stream) {
   const skv_cache& c = *p.c;
   const int32_t B = c.batch, H = p.n_heads, S = p.n_split;
-  const int G = H / c.n_kv_heads;
-  if (G != 1 && G != 2 && G != 4 && G != 8) return hipErrorInvalidValue;
-  if (p.app.k_new != nullptr || p.sel_hmask != nullptr || p.dbg_logits != nullptr ||
-      p.n_tok != 1)
-    return hipErrorInvalidValue;
   float* ws_m = p.ws + ws_m_offset(B, H, S);
   float* ws_l = p.ws + ws_l_offset(B, H, S);
   float* ws_o = p.ws + ws_o_offset(B, H, S);
@@ -540,11 +625,9 @@ hipError_t launch_decode_grouped(const DecodeParams& p, hipStream_t stream) {
   const uint16_t* vs = reinterpret_cast<const uint16_t*>(c.v_scale);
   const int fr = p.fused_r;
 #define SKV_GRP(GG, Q, SR)                                                                      \
-  decode_grp_mfma<GG, Q, SR><<<grid, kMThreads, 0, stream>>>(kc, vc, ks, vs, p.q, p.seq_len,   \
-                                                            p.sel_idx, p.sel_cnt, p.max_sel,    \
-                                                            c.n_kv_heads, c.max_seq, c.block,   \
-                                                            p.max_len, S, n_rows, ups, scale2,  \
-                                                            ws_m, ws_l, ws_o, p.fsel)
+  decode_grp_mfma<GG, Q, SR, D><<<grid, kMThreads, 0, stream>>>(                               \
+      kc, vc, ks, vs, p.q, p.seq_len, p.sel_idx, p.sel_cnt, p.max_sel, c.n_kv_heads,           \
+      c.max_seq, c.block, p.max_len, S, n_rows, ups, scale2, ws_m, ws_l, ws_o, p.fsel)
 #define SKV_GRP_Q(GG, Q)                           \
   if (fr == 2) SKV_GRP(GG, Q, 2);                  \
   else if (fr == 4) SKV_GRP(GG, Q, 4);             \
@@ -564,6 +647,33 @@ hipError_t launch_decode_grouped(const DecodeParams& p, hipStream_t stream) {
 #undef SKV_GRP_Q
 #undef SKV_GRP
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_append_grouped(const skv_cache& c, const int32_t* pos0, int32_t n_new,
+                                 const void* k_new, const void* v_new, hipStream_t stream) {
+  switch (c.head_dim) {
+    case 64: return launch_append_grouped_d<64>(c, pos0, n_new, k_new, v_new, stream);
+    case 128: return launch_append_grouped_d<128>(c, pos0, n_new, k_new, v_new, stream);
+    case 256: return launch_append_grouped_d<256>(c, pos0, n_new, k_new, v_new, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_decode_grouped(const DecodeParams& p, hipStream_t stream) {
+  const skv_cache& c = *p.c;
+  const int G = p.n_heads / c.n_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return hipErrorInvalidValue;
+  if (p.app.k_new != nullptr || p.sel_hmask != nullptr || p.dbg_logits != nullptr ||
+      p.n_tok != 1)
+    return hipErrorInvalidValue;
+  switch (c.head_dim) {
+    case 64: return launch_decode_grouped_d<64>(p, G, stream);
+    case 128: return launch_decode_grouped_d<128>(p, G, stream);
+    case 256: return launch_decode_grouped_d<256>(p, G, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace skv

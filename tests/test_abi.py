@@ -52,8 +52,8 @@ BAD = 0x10  # never dereferenced: every call below fails validation first
     (dict(head_dim=2048), skv.SKV_EINVAL),        # above 1024
     (dict(head_dim=96), skv.SKV_EUNSUPPORTED),    # valid, not built
     (dict(head_dim=512), skv.SKV_EUNSUPPORTED),
-    (dict(head_dim=64, kv_dtype=skv.SKV_Q8_0, k_scale=0x5000, v_scale=0x6000),
-     skv.SKV_EUNSUPPORTED),                       # group-wise caches: head dim 128 only
+    (dict(head_dim=96, kv_dtype=skv.SKV_Q8_0, k_scale=0x5000, v_scale=0x6000),
+     skv.SKV_EUNSUPPORTED),                       # group-wise caches: 64, 128, 256
     (dict(block=40), skv.SKV_EINVAL),
     (dict(block=0), skv.SKV_EINVAL),
     (dict(kv_dtype=7), skv.SKV_EINVAL),
@@ -74,8 +74,8 @@ def test_cache_descriptor_validation(lib, kw, expect):
 
 @pytest.mark.parametrize("dim", [64, 256])
 def test_head_dims_64_256_core_calls_only(lib, dim):
-    """Head dims 64 and 256 pass the descriptor check of the f16 and int8
-    calls (the calls below then stop at a later check, before any launch) and
+    """Head dims 64 and 256 pass the descriptor check of the calls built for
+    them (the calls below then stop at a later check, before any launch) and
     are refused by the calls built for head dim 128 only."""
     d = desc(head_dim=dim)
     q = 0x7000
@@ -97,10 +97,11 @@ def test_head_dims_64_256_core_calls_only(lib, dim):
         skv.SKV_ERANGE
     assert lib.skv_block_bounds_multi(ctypes.byref(d), q, 2, 32, BAD, 5000, BAD, None) == \
         skv.SKV_ERANGE
-    # head dim 128 only: sparse-V, the scan, group-wise caches
+    # group-wise caches: accepted, then a range check fails
     g = desc(head_dim=dim, kv_dtype=skv.SKV_Q8_0, k_scale=0x5000, v_scale=0x6000)
-    assert lib.skv_kv_append(ctypes.byref(g), BAD, 1, q, q, skv.SKV_F32, None) == \
-        skv.SKV_EUNSUPPORTED
+    assert lib.skv_kv_append(ctypes.byref(g), BAD, 5000, q, q, skv.SKV_F32, None) == \
+        skv.SKV_ERANGE
+    # head dim 128 only: sparse-V, the scan
     assert lib.skv_decode_attn_sparse_v(ctypes.byref(d), q, 32, BAD, 10, None, None, 0, 0.1,
                                         1e-3, 0.0, 4, BAD, 1 << 30, BAD, None) == \
         skv.SKV_EUNSUPPORTED

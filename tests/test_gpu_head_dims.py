@@ -1,15 +1,15 @@
-"""Head dims 64 and 256: the f16 and int8 caches' append, bounds, selection,
-attention and step calls against the oracle (cpu-attn kernel card,
-"Requirements and limits": the head dimension is any multiple of 16 up to
-1024; these two and 128 are built).
+"""Head dims 64 and 256: the append, bounds, selection, attention and step
+calls of the f16, int8 and group-wise (q8_0, q4_0, q5_0) caches against the
+oracle (cpu-attn kernel card, "Requirements and limits": the head dimension
+is any multiple of 16 up to 1024; these two and 128 are built).
 
 Sizes span several tiles per wavefront, several parts and a ragged tail (the
 f16 tile is 16 tokens, the int8 tile 32; a tile's 16-byte loads cover 8, 4 or
 2 rows per instruction at D = 64, 128, 256).  Bars as at D = 128: appended
 rows, codes, scales and bounds exact; int8 logit dots exact; selected sets
-exact on the kernel's own scores; f16 outputs within 1e-3 and int8 outputs
-within 1e-4 of the method (per head and per element); the step bit-identical
-to the calls it composes.
+exact on the kernel's own scores; f16 and group-wise outputs within 1e-3 and
+int8 outputs within 1e-4 of the method (per head and per element); the step
+bit-identical to the calls it composes.
 """
 import numpy as np
 import pytest
@@ -24,6 +24,8 @@ from test_gpu_multi_token import check_quest as chunk_check_quest
 from test_gpu_multi_token import run_chunk
 from test_gpu_per_head import check as per_head_check
 from test_gpu_per_head import run_per_head
+from test_gpu_grouped import check_cache as grouped_check_cache
+from test_gpu_grouped import reference as grouped_reference
 from test_gpu_step import _oracle_check, _run_case
 
 import sparse_kv_cache_append_amd as skv
@@ -31,6 +33,7 @@ import sparse_kv_cache_append_amd as skv
 pytestmark = pytest.mark.gpu
 
 DIMS = [64, 256]
+GROUPED = ["q8_0", "q4_0", "q5_0"]
 F16_TOL = 1e-3
 I8_TOL = 1e-4
 
@@ -182,7 +185,75 @@ STEP = [
         846, 2, 16, 8, D, [1025, 300], "i8"), False, True, {"poison": True, "S": 5}),
     ("dense-i8 first token of an empty cache", lambda D: workloads.gaussian(
         847, 1, 32, 4, D, [1], "i8"), False, True, {"lag": 1, "tight": True}),
+    ("quest-q8_0", lambda D: workloads.clustered(
+        [848, 849], 32, 8, D, [3000, 4097], "q8_0", n_dirs=16, k_sel=[10, 12], n_sink=1,
+        n_recent=2), True, True, {}),
+    ("quest-q5_0 G8 poisoned rows", lambda D: workloads.clustered(
+        [850], 32, 4, D, [5001], "q5_0", n_dirs=16, k_sel=[20], n_sink=1, n_recent=4),
+        True, True, {"poison": True}),
+    ("dense-q4_0 append poisoned rows", lambda D: workloads.gaussian(
+        851, 2, 32, 8, D, [65, 2000], "q4_0"), False, True, {"poison": True}),
+    ("dense-q5_0 first token of an empty cache", lambda D: workloads.gaussian(
+        852, 1, 32, 4, D, [1], "q5_0"), False, True, {"lag": 1, "tight": True}),
 ]
+
+
+@pytest.mark.parametrize("D", DIMS)
+@pytest.mark.parametrize("kind", GROUPED)
+def test_grouped_append_exact(gpu_lib, D, kind):
+    """Group-wise codes (both q5_0 planes), f16 group scales and block bounds
+    exact, appended whole and in 37-row chunks (blocks straddle the chunk
+    edges), with a zero group and groups whose scale underflows and overflows
+    f16 (the first and last group of a row included)."""
+    _print("grouped append", D, kind)
+    w = workloads.gaussian(890 + D, 2, 16, 4, D, [300, 129], kind)
+    w.k[0][0, 5, :32] = 0.0
+    w.k[0][1, 6, D - 32:] = 1e-9
+    w.v[0][2, 7, 32:64] = 3e9
+    for chunk in (None, 37):
+        cache = build_cache(w, chunk=chunk)
+        for b in range(w.B):
+            grouped_check_cache(cache, w, b)
+
+
+@pytest.mark.parametrize("D", DIMS)
+@pytest.mark.parametrize("kind", GROUPED)
+@pytest.mark.parametrize("H,Hkv,lens", [(32, 8, [2049, 100]), (8, 8, [513]), (16, 8, [1]),
+                                        (32, 4, [4097])])
+def test_grouped_dense(gpu_lib, D, kind, H, Hkv, lens):
+    _print("grouped dense", D, kind, H, Hkv, lens)
+    w = workloads.gaussian(893 + D + H + len(lens), len(lens), H, Hkv, D, lens, kind)
+    cache = build_cache(w)
+    for S in (None, 3):
+        out, _ = run_dense(cache, w, n_split=S)
+        for b in range(w.B):
+            assert_close(out[b], grouped_reference(w, b), F16_TOL, D, kind, b, S)
+
+
+@pytest.mark.parametrize("D", DIMS)
+@pytest.mark.parametrize("kind", GROUPED)
+def test_grouped_quest(gpu_lib, D, kind):
+    """Bounds from the float32 keys, the selection on the kernel's own scores,
+    attention over the selected blocks of a group-wise cache."""
+    _print("grouped quest", D, kind)
+    w = workloads.clustered([896, 897], 32, 8, D, [6000, 2600], kind, n_dirs=16,
+                            k_sel=[20, 9], n_sink=1, n_recent=2)
+    cache = build_cache(w)
+    score, sel, cnt, _ = run_select(cache, w)
+    out = run_sparse(cache, w, sel, cnt)
+    s_h, c_h = sel.cpu().numpy(), cnt.cpu().numpy()
+    for b in range(w.B):
+        nb = w.n_blocks(b)
+        kmin, kmax = oracle.block_bounds(w.k[b], w.lens[b], w.block)
+        ref = oracle.group_scores(oracle.upper_bounds(w.q[b], kmin, kmax), w.Hkv)
+        np.testing.assert_allclose(score[b, :, :nb], ref, rtol=2e-6, atol=1e-4)
+        for g in range(w.Hkv):
+            got = s_h[b, g, :c_h[b, g]]
+            own = oracle.select_blocks(score[b, g], nb, w.k_sel[b], w.n_sink, w.n_recent)
+            assert np.array_equal(got, own["sel"]), (b, g)
+            toks = oracle.selected_tokens(got, w.lens[b], w.block)
+            hs = slice(g * w.G, (g + 1) * w.G)
+            assert_close(out[b, hs], grouped_reference(w, b, toks, hs, g), F16_TOL, b, g)
 
 
 @pytest.mark.parametrize("D", DIMS)
@@ -272,9 +343,8 @@ def test_quest_chunk(gpu_lib, D, seeds, H, Hkv, lens, kv, T, ksel):
 
 
 def test_other_head_dims_are_refused(gpu_lib):
-    """Head dim 96 (a multiple of 16, not built), and the calls built for 128
-    only (sparse-V, the 4-bit scan, group-wise caches) at 64, raise
-    SKV_EUNSUPPORTED before any launch."""
+    """Head dim 96 (a multiple of 16, not built), and a call built for 128
+    only (the 4-bit scan) at 64, raise SKV_EUNSUPPORTED before any launch."""
     _print("refused")
     c96 = skv.Cache(1, 2, 128, 96, "f16", 64, device=DEV)
     q = torch.zeros((1, 8, 96), dtype=torch.float32, device=DEV)
@@ -287,10 +357,5 @@ def test_other_head_dims_are_refused(gpu_lib):
     idx = skv.Scan4Index(c64, device=DEV)
     with pytest.raises(skv.SkvError) as e:
         skv.scan4_build(c64, idx, torch.zeros(1, dtype=torch.int32, device=DEV), sl, 10)
-    assert e.value.status == skv.SKV_EUNSUPPORTED
-    g64 = skv.Cache(1, 2, 128, 64, "q8_0", 64, device=DEV)
-    k = torch.zeros((1, 1, 2, 64), dtype=torch.float32, device=DEV)
-    with pytest.raises(skv.SkvError) as e:
-        skv.kv_append(g64, torch.zeros(1, dtype=torch.int32, device=DEV), k, k)
     assert e.value.status == skv.SKV_EUNSUPPORTED
     torch.cuda.synchronize()

@@ -82,10 +82,11 @@ def test_static_step_matches_the_step_twice_second_smaller(gpu_lib, kv_dtype):
                                                            w.softmax_scale), 1e-3, b)
 
 
-@pytest.mark.parametrize("kv_dtype,D", [("q5_0", 128), ("f16", 256), ("i8", 64)])
+@pytest.mark.parametrize("kv_dtype,D", [("q5_0", 128), ("f16", 256), ("i8", 64),
+                                        ("q4_0", 256)])
 def test_static_step_other_formats_and_head_dims(gpu_lib, kv_dtype, D):
-    """The same pairing for a q5_0 cache and head dims 256 and 64 (where the
-    step runs its append as its own kernel)."""
+    """The same pairing for group-wise caches and head dims 256 and 64 (where
+    the step runs its append as its own kernel)."""
     w = workloads.clustered([605], 32, 8, D, [5000], kv_dtype, n_dirs=16, k_sel=[20], n_sink=1,
                             n_recent=2)
     for quest in (True, False):

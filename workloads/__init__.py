@@ -186,9 +186,7 @@ def quest32k_quant(kv_dtype: str) -> Workload:
     64, K_SEL=128, sink 1, recent 2, seed 1003) drawn for a group-wise
     quantized cache ("q8_0", "q4_0" or "q5_0"): the float32 rows that get
     appended."""
-    return clustered([1003], 32, 8, 128, [32768], kv_dtype, n_dirs=64,
-                     name=f"quest-{kv_dtype} B1 H32/Hkv8 D128 L32768 K_SEL128 sink1 recent2",
-                     k_sel=[128], n_sink=1, n_recent=2)
+    return quest32k_dim(128, kv_dtype)
 
 
 def quest32k_at(L: int) -> Workload:
@@ -201,11 +199,12 @@ def quest32k_at(L: int) -> Workload:
                      k_sel=[nb // 4], n_sink=1, n_recent=2)
 
 
-def quest32k_dim(D: int) -> Workload:
+def quest32k_dim(D: int, kv_dtype: str = "f16") -> Workload:
     """The 32K Quest workload's generator (H=32, Hkv=8, 64 directions, block
-    64, K_SEL=128, sink 1, recent 2, seed 1003, f16) at head dim D."""
-    return clustered([1003], 32, 8, D, [32768], "f16", n_dirs=64,
-                     name=f"quest-f16 B1 H32/Hkv8 D{D} L32768 K_SEL128 sink1 recent2",
+    64, K_SEL=128, sink 1, recent 2, seed 1003) at head dim D over a kv_dtype
+    cache (f16 rows, or the float32 rows a quantized cache is filled from)."""
+    return clustered([1003], 32, 8, D, [32768], kv_dtype, n_dirs=64,
+                     name=f"quest-{kv_dtype} B1 H32/Hkv8 D{D} L32768 K_SEL128 sink1 recent2",
                      k_sel=[128], n_sink=1, n_recent=2)
 
 
