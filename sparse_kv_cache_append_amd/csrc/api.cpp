@@ -12,9 +12,8 @@ constexpr int32_t kMaxSplit = 4096;
 constexpr int32_t kMaxSelectBlocks = 16384;
 
 bool valid_head_dim(int32_t d) { return d >= 16 && d <= 1024 && d % 16 == 0; }
-// Head dims built: 128 for every call; 64 and 256 for the append, bounds,
-// selection, attention (per-query-head and token-chunk forms included) and
-// step calls of every cache type they take (kDimCore below).
+// Head dims built: 128 for every call; 64 and 256 for every call but the
+// 4-bit scan (kDimCore below), over every cache type each call takes.
 constexpr int32_t kFullDim = 128;
 bool core_head_dim(int32_t d) { return d == 64 || d == kFullDim || d == 256; }
 bool supported_group(int32_t g) { return g == 1 || g == 2 || g == 4 || g == 8; }
@@ -562,7 +561,7 @@ skv_status skv_decode_attn_sparse_v(const skv_cache* c, const float* q, int32_t 
                                     int32_t max_sel, float softmax_scale, float tau, float eps,
                                     int32_t n_split, void* workspace, size_t workspace_bytes,
                                     uint32_t* keep_mask, hipStream_t stream) {
-  skv_status st = check_cache(c, false);
+  skv_status st = check_cache(c, false, kDimCore);
   if (st != SKV_OK) return st;
   if (q == nullptr || seq_len == nullptr || !aligned(q)) return SKV_EINVAL;
   st = check_heads(c, n_heads);

@@ -24,9 +24,13 @@
 //     partial state (m = M, l = its own share of L, o = its kept sum), which
 //     skv_combine merges as usual.
 //
-// Bytes per attended (token, KV head): pass A reads the K row (f16 256 B,
-// int8 128 B + a 4-byte scale) and writes G logits; pass B reads the G logits
-// and only the kept V rows (f16 256 B, int8 128 B + 4).
+// Bytes per attended (token, KV head): pass A reads the K row (f16 2 D B,
+// int8 D B + a 4-byte scale) and writes G logits; pass B reads the G logits
+// and only the kept V rows (f16 2 D B, int8 D B + 4).  Head dims D = 64, 128
+// and 256: a tile's 16-byte loads cover 1024 / row-bytes rows per
+// instruction, the XOR swizzle runs over the row's 16-byte chunks (capped at
+// 16), q.K takes D / 32 (f16) or D / 64 (int8) MFMA steps and P.V D / 16
+// channel blocks; at D = 256 one workgroup runs per compute unit.
 #include <type_traits>
 
 #include "decode_core.h"
@@ -42,6 +46,13 @@ constexpr uint32_t kSkipOffset = 0x7FFFFFF0u;
 // Kept weights are at most 1; P.V takes them times 2^15 (exact), so weights
 // down to 2^-18 keep the full precision of the f16 high + low parts.
 constexpr int kPwShiftSvF16 = 15;
+
+// Head dim D: workgroups per CU, and the chunk swizzle of a row of CHUNKS
+// 16-byte chunks (chunk c of row r at c ^ (r % min(CHUNKS, 16))).
+template <int D>
+constexpr int sv_occ() { return D > 128 ? 1 : 2; }
+template <int CHUNKS>
+__device__ __forceinline__ int sv_swz(int row) { return row & ((CHUNKS < 16 ? CHUNKS : 16) - 1); }
 
 // ------------------------------------------------------------ pass A helpers
 // Running logit maximum, denominator and token count of one wavefront.
@@ -169,14 +180,15 @@ __device__ __forceinline__ RowTotals row_totals(const float* stat_m, const float
 // Merge the 4 wavefronts' kept sums (one reference M for all: a plain sum)
 // and write the part's partial state: m = M, l = the part's own pass-A mass
 // relative to M, o = its kept sum.
-template <int G>
-__device__ __forceinline__ void finish_values(const float4_t (&O)[8], float Mh, float* lds,
+template <int G, int N>
+__device__ __forceinline__ void finish_values(const float4_t (&O)[N], float Mh, float* lds,
                                               const float* stat_m, const float* stat_l,
                                               float* ws_m, float* ws_l, float* ws_o,
                                               int64_t head0, int32_t n_split, int32_t split) {
+  constexpr int D = 16 * N;
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   float* lo = lds;                          // [waves][G][D]
-  float* lm = lds + kMWaves * G * kD;       // [G]
+  float* lm = lds + kMWaves * G * D;        // [G]
   __syncthreads();
   const int g4 = 4 * (lane / 16);
 #pragma unroll
@@ -184,18 +196,18 @@ __device__ __forceinline__ void finish_values(const float4_t (&O)[8], float Mh, 
     const int h = g4 + r;
     if (h < G) {
 #pragma unroll
-      for (int n = 0; n < 8; ++n) lo[(wave * G + h) * kD + 16 * n + lane % 16] = O[n][r];
+      for (int n = 0; n < N; ++n) lo[(wave * G + h) * D + 16 * n + lane % 16] = O[n][r];
     }
   }
   if (wave == 0 && lane < G) lm[lane] = Mh;
   __syncthreads();
-  for (int idx = threadIdx.x; idx < G * kD; idx += kMThreads) {
-    const int h = idx / kD, d = idx % kD;
+  for (int idx = threadIdx.x; idx < G * D; idx += kMThreads) {
+    const int h = idx / D, d = idx % D;
     float so = 0.0f;
 #pragma unroll
-    for (int w = 0; w < kMWaves; ++w) so += lo[(w * G + h) * kD + d];
+    for (int w = 0; w < kMWaves; ++w) so += lo[(w * G + h) * D + d];
     const int64_t ps = (head0 + h) * n_split + split;
-    ws_o[ps * kD + d] = so;
+    ws_o[ps * D + d] = so;
     if (d == 0) {
       const float M = lm[h], mi = stat_m[ps];
       ws_m[ps] = M;
@@ -231,8 +243,8 @@ struct SvArgs {
 // ====================================================================== f16
 // Pass A: K tiles of 16 tokens, q.K on the matrix cores (query as f16 high +
 // low parts, as in the dense kernel), logits and stats out.
-template <int G>
-__global__ void __launch_bounds__(kMThreads, 2)
+template <int D, int G>
+__global__ void __launch_bounds__(kMThreads, sv_occ<D>())
 sv_logits_f16(const uint16_t* __restrict__ kc, const float* __restrict__ q,
               const int32_t* __restrict__ seq_len, const int32_t* __restrict__ sel_idx,
               const int32_t* __restrict__ sel_cnt, int32_t max_sel, int32_t Hkv,
@@ -240,7 +252,12 @@ sv_logits_f16(const uint16_t* __restrict__ kc, const float* __restrict__ q,
               int32_t ups, float qscale2, SvArgs sv) {
   constexpr int T = 16;
   const int32_t lstride = sv.lstride;
-  constexpr int kTileBytes = T * kRowBytesF16;              // 4096
+  constexpr int RB = 2 * D;                                 // bytes per row
+  constexpr int kTileBytes = T * RB;                        // 4096 at D = 128
+  constexpr int kLoads = kTileBytes / 1024;                 // 16-byte loads per lane
+  constexpr int kCpr = RB / 16;                             // chunks per row
+  constexpr int kRpl = 1024 / RB;                           // rows per load instruction
+  constexpr int KQ = D / 32;                                // q.K steps
   __shared__ __attribute__((aligned(16))) uint8_t smem[kMWaves][2][kTileBytes];
   const uint32_t slot = xcd_slot(blockIdx.x, gridDim.x);
   const int32_t split = int32_t(slot % uint32_t(n_split));
@@ -253,12 +270,12 @@ sv_logits_f16(const uint16_t* __restrict__ kc, const float* __restrict__ q,
   const int64_t bg = int64_t(b) * Hkv + g;
   const int32_t L_raw = seq_len[b];
   const ListSeed ls = list_seed(sel_idx, sel_cnt, max_sel, bg, split, ups);
-  half8_t qhi[4], qlo[4];
+  half8_t qhi[KQ], qlo[KQ];
   const bool hv = lc < G;
   {
-    const float* qp = q + (int64_t(b) * H + g * G + (hv ? lc : 0)) * kD;
+    const float* qp = q + (int64_t(b) * H + g * G + (hv ? lc : 0)) * D;
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
+    for (int kk = 0; kk < KQ; ++kk) {
       const float4 a = *reinterpret_cast<const float4*>(qp + 32 * kk + 8 * lg);
       const float4 c = *reinterpret_cast<const float4*>(qp + 32 * kk + 8 * lg + 4);
       const float x[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
@@ -275,35 +292,37 @@ sv_logits_f16(const uint16_t* __restrict__ kc, const float* __restrict__ q,
   TileWalk tw = make_walk<T>(ls, sel_idx, max_sel, bg, L, block, split, ups);
   tw.init(wave);
   TileStats ts;
-  const uint8_t* kbase = reinterpret_cast<const uint8_t*>(kc + bg * int64_t(max_seq) * kD);
+  const uint8_t* kbase = reinterpret_cast<const uint8_t*>(kc + bg * int64_t(max_seq) * D);
   float* lrow = sv.logit + (int64_t(b) * H + g * G + (hv ? lc : 0)) * int64_t(lstride);
-  struct Frag { int4_t k[4]; int32_t r0, nvalid; };
+  // lane loads row kRpl i + lane / kCpr of the tile, 16-byte chunk lane % kCpr
+  struct Frag { int4_t k[kLoads]; int32_t r0, nvalid; };
   auto issue = [&](Frag& f) {
     int32_t r0 = 0, nv = 0;
     if (tw.more()) tw.next<T>(r0, nv);
     f.r0 = r0;
     f.nvalid = nv;
     const uint32_t lo = 16u * uint32_t(lane);
-    const int bytes = __builtin_amdgcn_readfirstlane(max(nv, 0) * kRowBytesF16);
-    const auto kr = tile_rsrc(kbase + int64_t(r0) * kRowBytesF16, bytes);
+    const int bytes = __builtin_amdgcn_readfirstlane(max(nv, 0) * RB);
+    const auto kr = tile_rsrc(kbase + int64_t(r0) * RB, bytes);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) f.k[i] = tile_load(kr, lo + 1024 * i);
+    for (int i = 0; i < kLoads; ++i) f.k[i] = tile_load(kr, lo + 1024 * i);
   };
   auto process = [&](auto bufc, Frag& fr) {
     constexpr int kBuf = decltype(bufc)::value;
     uint8_t* kt = smem[wave][kBuf];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int rw = 4 * i + lg;
-      *reinterpret_cast<int4_t*>(kt + rw * kRowBytesF16 + 16 * (lc ^ swz(rw))) = fr.k[i];
+    for (int i = 0; i < kLoads; ++i) {
+      const int rw = kRpl * i + lane / kCpr;
+      *reinterpret_cast<int4_t*>(kt + rw * RB + 16 * ((lane % kCpr) ^ sv_swz<kCpr>(rw))) =
+          fr.k[i];
     }
     const int32_t nvalid = fr.nvalid, r0 = fr.r0;
     issue(fr);
     float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
+    for (int kk = 0; kk < KQ; ++kk) {
       const half8_t a = *reinterpret_cast<const half8_t*>(
-          kt + lc * kRowBytesF16 + 16 * ((lg + 4 * kk) ^ swz(lc)));
+          kt + lc * RB + 16 * ((lg + 4 * kk) ^ sv_swz<kCpr>(lc)));
       acc = mfma_f16_32(a, qhi[kk], acc);
       acc = mfma_f16_32(a, qlo[kk], acc);
     }
@@ -335,15 +354,20 @@ sv_logits_f16(const uint16_t* __restrict__ kc, const float* __restrict__ q,
 }
 
 // Pass B: V tiles of 16 tokens, only the rows some head keeps.
-template <int G>
-__global__ void __launch_bounds__(kMThreads, 2)
+template <int D, int G>
+__global__ void __launch_bounds__(kMThreads, sv_occ<D>())
 sv_values_f16(const uint16_t* __restrict__ vc, const int32_t* __restrict__ seq_len,
               const int32_t* __restrict__ sel_idx, const int32_t* __restrict__ sel_cnt,
               int32_t max_sel, int32_t Hkv, int32_t max_seq, int32_t block, int32_t max_len,
               int32_t n_split, int32_t n_rows, int32_t ups, int32_t keep_words, SvArgs sv) {
   constexpr int T = 16;
   const int32_t lstride = sv.lstride;
-  constexpr int kTileBytes = T * kRowBytesF16;              // 4096
+  constexpr int RB = 2 * D;                                 // bytes per row
+  constexpr int kTileBytes = T * RB;                        // 4096 at D = 128
+  constexpr int kLoads = kTileBytes / 1024;                 // 16-byte loads per lane
+  constexpr int kCpr = RB / 16;                             // chunks per row
+  constexpr int kRpl = 1024 / RB;                           // rows per load instruction
+  constexpr int NB = D / 16;                                // P.V channel blocks
   __shared__ __attribute__((aligned(16))) uint8_t smem[kMWaves][2][kTileBytes];
   __shared__ __attribute__((aligned(16))) uint8_t flags[kMWaves][T];
   const uint32_t slot = xcd_slot(blockIdx.x, gridDim.x);
@@ -367,10 +391,10 @@ sv_values_f16(const uint16_t* __restrict__ vc, const int32_t* __restrict__ seq_l
   const int32_t L = __builtin_amdgcn_readfirstlane(min(max(L_raw, 0), max_len));
   TileWalk tw = make_walk<T>(ls, sel_idx, max_sel, bg, L, block, split, ups);
   tw.init(wave);
-  float4_t O[8];
+  float4_t O[NB];
 #pragma unroll
-  for (int n = 0; n < 8; ++n) O[n] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
-  const uint8_t* vbase = reinterpret_cast<const uint8_t*>(vc + bg * int64_t(max_seq) * kD);
+  for (int n = 0; n < NB; ++n) O[n] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  const uint8_t* vbase = reinterpret_cast<const uint8_t*>(vc + bg * int64_t(max_seq) * D);
   const float* lrow = sv.logit + hrow * int64_t(lstride);
   uint16_t* krow = sv.keep != nullptr
                        ? reinterpret_cast<uint16_t*>(sv.keep + hrow * int64_t(keep_words))
@@ -380,7 +404,7 @@ sv_values_f16(const uint16_t* __restrict__ vc, const int32_t* __restrict__ seq_l
   // two tiles ahead of its value rows; the padding past the buffer's rows
   // keeps the whole float4 in bounds
   struct Lgt { float4 s; int32_t r0, nvalid; };
-  struct Frag { int4_t v[4]; float p[4]; int32_t r0, nvalid; };
+  struct Frag { int4_t v[kLoads]; float p[4]; int32_t r0, nvalid; };
   auto issue_logits = [&](Lgt& lt) {
     int32_t r0 = 0, nv = 0;
     if (tw.more()) tw.next<T>(r0, nv);
@@ -420,11 +444,11 @@ sv_values_f16(const uint16_t* __restrict__ vc, const int32_t* __restrict__ seq_l
       }
     }
     const uint32_t lo = 16u * uint32_t(lane);
-    const int bytes = __builtin_amdgcn_readfirstlane(max(nv, 0) * kRowBytesF16);
-    const auto vr = tile_rsrc(vbase + int64_t(r0) * kRowBytesF16, bytes);
+    const int bytes = __builtin_amdgcn_readfirstlane(max(nv, 0) * RB);
+    const auto vr = tile_rsrc(vbase + int64_t(r0) * RB, bytes);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const bool need = fl[4 * i + lg] != 0;          // row 4 i + lane / 16
+    for (int i = 0; i < kLoads; ++i) {
+      const bool need = fl[kRpl * i + lane / kCpr] != 0;   // row kRpl i + lane / kCpr
       f.v[i] = tile_load(vr, need ? lo + 1024 * i : kSkipOffset);
     }
   };
@@ -432,9 +456,10 @@ sv_values_f16(const uint16_t* __restrict__ vc, const int32_t* __restrict__ seq_l
     constexpr int kBuf = decltype(bufc)::value;
     uint8_t* vt = smem[wave][kBuf];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int rw = 4 * i + lg;
-      *reinterpret_cast<int4_t*>(vt + rw * kRowBytesF16 + 16 * (lc ^ swz(rw))) = fr.v[i];
+    for (int i = 0; i < kLoads; ++i) {
+      const int rw = kRpl * i + lane / kCpr;
+      *reinterpret_cast<int4_t*>(vt + rw * RB + 16 * ((lane % kCpr) ^ sv_swz<kCpr>(rw))) =
+          fr.v[i];
     }
     float pc[4];
 #pragma unroll
@@ -451,9 +476,9 @@ sv_values_f16(const uint16_t* __restrict__ vc, const int32_t* __restrict__ seq_l
     }
     const int tr_row = 4 * lg + (lc >> 2);
 #pragma unroll
-    for (int n = 0; n < 8; ++n) {
+    for (int n = 0; n < NB; ++n) {
       const int chunk = 2 * n + ((lc & 3) >> 1);
-      const int off = tr_row * kRowBytesF16 + 16 * (chunk ^ swz(tr_row)) + 8 * (lc & 1);
+      const int off = tr_row * RB + 16 * (chunk ^ sv_swz<kCpr>(tr_row)) + 8 * (lc & 1);
       const short4_t raw =
           __builtin_amdgcn_ds_read_tr16_b64_v4i16((SKV_LDS short4_t*)(vt + off));
       const half4_t bv = __builtin_bit_cast(half4_t, raw);
@@ -476,7 +501,7 @@ sv_values_f16(const uint16_t* __restrict__ vc, const int32_t* __restrict__ seq_l
   }
   if (n_mine & 1) process(std::integral_constant<int, 0>{}, f0, la);
 #pragma unroll
-  for (int n = 0; n < 8; ++n) {
+  for (int n = 0; n < NB; ++n) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) O[n][r] *= 1.0f / float(1 << kPwShiftSvF16);
   }
@@ -487,8 +512,8 @@ sv_values_f16(const uint16_t* __restrict__ vc, const int32_t* __restrict__ seq_l
 // ===================================================================== int8
 // Tiles of 32 tokens; token order inside a tile as in the dense int8 kernel:
 // lane group lg holds tokens tok(lg, e) = 16 (e / 4) + 4 lg + e % 4.
-template <int G>
-__global__ void __launch_bounds__(kMThreads, 2)
+template <int D, int G>
+__global__ void __launch_bounds__(kMThreads, sv_occ<D>())
 sv_logits_i8(const int8_t* __restrict__ kc, const float* __restrict__ ksc,
              const float* __restrict__ q, const int32_t* __restrict__ seq_len,
              const int32_t* __restrict__ sel_idx, const int32_t* __restrict__ sel_cnt,
@@ -496,7 +521,12 @@ sv_logits_i8(const int8_t* __restrict__ kc, const float* __restrict__ ksc,
              int32_t n_split, int32_t n_rows, int32_t ups, float scale2, SvArgs sv) {
   constexpr int T = 32;
   const int32_t lstride = sv.lstride;
-  constexpr int kTileBytes = T * kRowBytesI8;               // 4096
+  constexpr int RB = D;                                     // bytes per row
+  constexpr int kTileBytes = T * RB;                        // 4096 at D = 128
+  constexpr int kLoads = kTileBytes / 1024;                 // 16-byte loads per lane
+  constexpr int kCpr = RB / 16;                             // chunks per row
+  constexpr int kRpl = 1024 / RB;                           // rows per load instruction
+  constexpr int KK = D / 64;                                // q.K steps
   constexpr int kBufBytes = kTileBytes + T * 4;
   __shared__ __attribute__((aligned(16))) uint8_t smem[kMWaves][2][kBufBytes];
   const uint32_t slot = xcd_slot(blockIdx.x, gridDim.x);
@@ -511,11 +541,11 @@ sv_logits_i8(const int8_t* __restrict__ kc, const float* __restrict__ ksc,
   const int32_t L_raw = seq_len[b];
   const ListSeed ls = list_seed(sel_idx, sel_cnt, max_sel, bg, split, ups);
   const bool hv = lc < G;
-  float x[2][16];
+  float x[KK][16];
   {
-    const float* qp = q + (int64_t(b) * H + g * G + (hv ? lc : 0)) * kD;
+    const float* qp = q + (int64_t(b) * H + g * G + (hv ? lc : 0)) * D;
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
+    for (int kk = 0; kk < KK; ++kk) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float4 v4 = *reinterpret_cast<const float4*>(qp + 64 * kk + 16 * lg + 4 * i);
@@ -524,39 +554,40 @@ sv_logits_i8(const int8_t* __restrict__ kc, const float* __restrict__ ksc,
       }
     }
   }
-  int4_t qb[2];
+  int4_t qb[KK];
   float coef;
   i8_query_operand(x, hv, scale2, qb, coef);
   const int32_t L = __builtin_amdgcn_readfirstlane(min(max(L_raw, 0), max_len));
   TileWalk tw = make_walk<T>(ls, sel_idx, max_sel, bg, L, block, split, ups);
   tw.init(wave);
   TileStats ts;
-  const uint8_t* kbase = reinterpret_cast<const uint8_t*>(kc + bg * int64_t(max_seq) * kD);
+  const uint8_t* kbase = reinterpret_cast<const uint8_t*>(kc + bg * int64_t(max_seq) * D);
   const float* ksb = ksc + bg * int64_t(max_seq);
   const int32_t last = max(L - 1, 0);
   float* lrow = sv.logit + (int64_t(b) * H + g * G + (hv ? lc : 0)) * int64_t(lstride);
-  struct Frag { int4_t k[4]; float sc; int32_t r0, nvalid; };
+  // lane loads row kRpl i + lane / kCpr of the tile, 16-byte chunk lane % kCpr
+  struct Frag { int4_t k[kLoads]; float sc; int32_t r0, nvalid; };
   auto issue = [&](Frag& f) {
     int32_t r0 = 0, nv = 0;
     if (tw.more()) tw.next<T>(r0, nv);
     f.r0 = r0;
     f.nvalid = nv;
     const uint32_t lo = 16u * uint32_t(lane);
-    const int bytes = __builtin_amdgcn_readfirstlane(max(nv, 0) * kRowBytesI8);
-    const auto kr = tile_rsrc(kbase + int64_t(r0) * kRowBytesI8, bytes);
+    const int bytes = __builtin_amdgcn_readfirstlane(max(nv, 0) * RB);
+    const auto kr = tile_rsrc(kbase + int64_t(r0) * RB, bytes);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) f.k[i] = tile_load(kr, lo + 1024 * i);
+    for (int i = 0; i < kLoads; ++i) f.k[i] = tile_load(kr, lo + 1024 * i);
     f.sc = ksb[min(r0 + lane % 32, last)];
   };
-  auto sw = [](int rw, int chunk) { return rw * kRowBytesI8 + 16 * (chunk ^ (rw & 7)); };
+  auto sw = [](int rw, int chunk) { return rw * RB + 16 * (chunk ^ sv_swz<kCpr>(rw)); };
   auto process = [&](auto bufc, Frag& fr) {
     constexpr int kBuf = decltype(bufc)::value;
     uint8_t* kt = smem[wave][kBuf];
     float* st = reinterpret_cast<float*>(kt + kTileBytes);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int rw = 8 * i + lane / 8;
-      *reinterpret_cast<int4_t*>(kt + sw(rw, lane % 8)) = fr.k[i];
+    for (int i = 0; i < kLoads; ++i) {
+      const int rw = kRpl * i + lane / kCpr;
+      *reinterpret_cast<int4_t*>(kt + sw(rw, lane % kCpr)) = fr.k[i];
     }
     if (lane < 32) st[lane] = fr.sc;
     const int32_t nvalid = fr.nvalid, r0 = fr.r0;
@@ -566,7 +597,7 @@ sv_logits_i8(const int8_t* __restrict__ kc, const float* __restrict__ ksc,
     for (int s = 0; s < 2; ++s) {
       acc[s] = int4_t{0, 0, 0, 0};
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
+      for (int kk = 0; kk < KK; ++kk) {
         const int4_t a = *reinterpret_cast<const int4_t*>(kt + sw(16 * s + lc, lg + 4 * kk));
         acc[s] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, qb[kk], acc[s], 0, 0, 0);
       }
@@ -613,8 +644,8 @@ sv_logits_i8(const int8_t* __restrict__ kc, const float* __restrict__ ksc,
 // far, stays below 2^14 in f16.
 constexpr int kPwShiftSvI8 = 14;
 
-template <int G>
-__global__ void __launch_bounds__(kMThreads, 2)
+template <int D, int G>
+__global__ void __launch_bounds__(kMThreads, sv_occ<D>())
 sv_values_i8(const int8_t* __restrict__ vc, const float* __restrict__ vsc,
              const int32_t* __restrict__ seq_len, const int32_t* __restrict__ sel_idx,
              const int32_t* __restrict__ sel_cnt, int32_t max_sel, int32_t Hkv,
@@ -622,7 +653,12 @@ sv_values_i8(const int8_t* __restrict__ vc, const float* __restrict__ vsc,
              int32_t ups, int32_t keep_words, SvArgs sv) {
   constexpr int T = 32;
   const int32_t lstride = sv.lstride;
-  constexpr int kTileBytes = T * kRowBytesI8;               // 4096
+  constexpr int RB = D;                                     // bytes per row
+  constexpr int kTileBytes = T * RB;                        // 4096 at D = 128
+  constexpr int kLoads = kTileBytes / 1024;                 // 16-byte loads per lane
+  constexpr int kCpr = RB / 16;                             // chunks per row
+  constexpr int kRpl = 1024 / RB;                           // rows per load instruction
+  constexpr int NB = D / 16;                                // P.V channel blocks
   constexpr int kBufBytes = kTileBytes + T * 4;
   __shared__ __attribute__((aligned(16))) uint8_t smem[kMWaves][2][kBufBytes];
   __shared__ __attribute__((aligned(16))) uint8_t flags[kMWaves][T];
@@ -647,18 +683,18 @@ sv_values_i8(const int8_t* __restrict__ vc, const float* __restrict__ vsc,
   const int32_t L = __builtin_amdgcn_readfirstlane(min(max(L_raw, 0), max_len));
   TileWalk tw = make_walk<T>(ls, sel_idx, max_sel, bg, L, block, split, ups);
   tw.init(wave);
-  float4_t O[8];
+  float4_t O[NB];
 #pragma unroll
-  for (int n = 0; n < 8; ++n) O[n] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
-  const uint8_t* vbase = reinterpret_cast<const uint8_t*>(vc + bg * int64_t(max_seq) * kD);
+  for (int n = 0; n < NB; ++n) O[n] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  const uint8_t* vbase = reinterpret_cast<const uint8_t*>(vc + bg * int64_t(max_seq) * D);
   const float* vsb = vsc + bg * int64_t(max_seq);
   const float* lrow = sv.logit + hrow * int64_t(lstride);
   uint32_t* krow = sv.keep != nullptr ? sv.keep + hrow * int64_t(keep_words) : nullptr;
   uint8_t* fl = flags[wave];
-  auto sw = [](int rw, int chunk) { return rw * kRowBytesI8 + 16 * (chunk ^ (rw & 7)); };
+  auto sw = [](int rw, int chunk) { return rw * RB + 16 * (chunk ^ sv_swz<kCpr>(rw)); };
   // logits of tokens tok(lg, 0..7): two float4 (tokens 4 lg .. and 16 + 4 lg ..)
   struct Lgt { float4 s0, s1; int32_t r0, nvalid; };
-  struct Frag { int4_t v[4]; float p[8]; float sc; int32_t r0, nvalid; };
+  struct Frag { int4_t v[kLoads]; float p[8]; float sc; int32_t r0, nvalid; };
   auto issue_logits = [&](Lgt& lt) {
     int32_t r0 = 0, nv = 0;
     if (tw.more()) tw.next<T>(r0, nv);
@@ -706,11 +742,11 @@ sv_values_i8(const int8_t* __restrict__ vc, const float* __restrict__ vsc,
       }
     }
     const uint32_t lo = 16u * uint32_t(lane);
-    const int bytes = __builtin_amdgcn_readfirstlane(max(nv, 0) * kRowBytesI8);
-    const auto vr = tile_rsrc(vbase + int64_t(r0) * kRowBytesI8, bytes);
+    const int bytes = __builtin_amdgcn_readfirstlane(max(nv, 0) * RB);
+    const auto vr = tile_rsrc(vbase + int64_t(r0) * RB, bytes);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const bool need = fl[8 * i + lane / 8] != 0;    // row 8 i + lane / 8
+    for (int i = 0; i < kLoads; ++i) {
+      const bool need = fl[kRpl * i + lane / kCpr] != 0;   // row kRpl i + lane / kCpr
       f.v[i] = tile_load(vr, need ? lo + 1024 * i : kSkipOffset);
     }
     // lanes 0..31: the V scale of token lane, when kept
@@ -727,9 +763,9 @@ sv_values_i8(const int8_t* __restrict__ vc, const float* __restrict__ vsc,
     uint8_t* vt = smem[wave][kBuf];
     float* st = reinterpret_cast<float*>(vt + kTileBytes);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int rw = 8 * i + lane / 8;
-      *reinterpret_cast<int4_t*>(vt + sw(rw, lane % 8)) = fr.v[i];
+    for (int i = 0; i < kLoads; ++i) {
+      const int rw = kRpl * i + lane / kCpr;
+      *reinterpret_cast<int4_t*>(vt + sw(rw, lane % kCpr)) = fr.v[i];
     }
     // V-scale unit 2^e_run >= every kept V scale so far (a power of two: the
     // change of unit of O is exact)
@@ -756,7 +792,7 @@ sv_values_i8(const int8_t* __restrict__ vc, const float* __restrict__ vsc,
     issue_logits(lt);
     if (unit != 1.0f) {
 #pragma unroll
-      for (int n = 0; n < 8; ++n) {
+      for (int n = 0; n < NB; ++n) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) O[n][r] *= unit;
       }
@@ -774,7 +810,7 @@ sv_values_i8(const int8_t* __restrict__ vc, const float* __restrict__ vsc,
     }
     const int tr_row = 16 * ((lc / 2) / 4) + 4 * lg + (lc / 2) % 4;
 #pragma unroll
-    for (int n = 0; n < 8; ++n) {
+    for (int n = 0; n < NB; ++n) {
       const int off = sw(tr_row, n) + 8 * (lc & 1);
       const int2_t raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32((SKV_LDS int2_t*)(vt + off));
       const half8_t bv = widen_codes(raw);
@@ -798,7 +834,7 @@ sv_values_i8(const int8_t* __restrict__ vc, const float* __restrict__ vsc,
   if (n_mine & 1) process(std::integral_constant<int, 0>{}, f0, la);
   if (e_run != kExpUnset) {
 #pragma unroll
-    for (int n = 0; n < 8; ++n) {
+    for (int n = 0; n < NB; ++n) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) O[n][r] = ldexpf(O[n][r], e_run - kPwShiftSvI8);
     }
@@ -809,9 +845,63 @@ sv_values_i8(const int8_t* __restrict__ vc, const float* __restrict__ vsc,
 
 }  // namespace
 
+namespace {
+
+template <int D>
+hipError_t launch_sparse_v_d(const SparseVParams& p, int G, const dim3 grid, int32_t n_rows,
+                             int32_t ups, float scale2, const SvArgs& sv, int32_t keep_words,
+                             hipStream_t stream) {
+  const skv_cache& c = *p.c;
+  const int32_t S = p.n_split, Hkv = c.n_kv_heads;
+  if (c.kv_dtype == SKV_F16) {
+    const uint16_t* kc = static_cast<const uint16_t*>(c.k);
+    const uint16_t* vc = static_cast<const uint16_t*>(c.v);
+#define SKV_SV_F16(GG)                                                                          \
+  sv_logits_f16<D, GG><<<grid, kMThreads, 0, stream>>>(kc, p.q, p.seq_len, p.sel_idx,          \
+                                                        p.sel_cnt, p.max_sel, Hkv, c.max_seq,   \
+                                                        c.block, p.max_len, S, n_rows, ups,     \
+                                                        scale2, sv);                            \
+  sv_values_f16<D, GG><<<grid, kMThreads, 0, stream>>>(vc, p.seq_len, p.sel_idx, p.sel_cnt,    \
+                                                        p.max_sel, Hkv, c.max_seq, c.block,     \
+                                                        p.max_len, S, n_rows, ups, keep_words,  \
+                                                        sv)
+    switch (G) {
+      case 1: SKV_SV_F16(1); break;
+      case 2: SKV_SV_F16(2); break;
+      case 4: SKV_SV_F16(4); break;
+      default: SKV_SV_F16(8); break;
+    }
+#undef SKV_SV_F16
+    return hipGetLastError();
+  }
+  if (c.kv_dtype != SKV_I8) return hipErrorInvalidValue;
+  const int8_t* kc = static_cast<const int8_t*>(c.k);
+  const int8_t* vc = static_cast<const int8_t*>(c.v);
+#define SKV_SV_I8(GG)                                                                           \
+  sv_logits_i8<D, GG><<<grid, kMThreads, 0, stream>>>(kc, c.k_scale, p.q, p.seq_len,           \
+                                                       p.sel_idx, p.sel_cnt, p.max_sel, Hkv,    \
+                                                       c.max_seq, c.block, p.max_len, S,        \
+                                                       n_rows, ups, scale2, sv);                \
+  sv_values_i8<D, GG><<<grid, kMThreads, 0, stream>>>(vc, c.v_scale, p.seq_len, p.sel_idx,     \
+                                                       p.sel_cnt, p.max_sel, Hkv, c.max_seq,    \
+                                                       c.block, p.max_len, S, n_rows, ups,      \
+                                                       keep_words, sv)
+  switch (G) {
+    case 1: SKV_SV_I8(1); break;
+    case 2: SKV_SV_I8(2); break;
+    case 4: SKV_SV_I8(4); break;
+    default: SKV_SV_I8(8); break;
+  }
+#undef SKV_SV_I8
+  return hipGetLastError();
+}
+
+}  // namespace
+
 hipError_t launch_sparse_v(const SparseVParams& p, hipStream_t stream) {
   const skv_cache& c = *p.c;
   const int32_t B = c.batch, H = p.n_heads, S = p.n_split, Hkv = c.n_kv_heads;
+  const int32_t D = c.head_dim;
   const int G = H / Hkv;
   if (G != 1 && G != 2 && G != 4 && G != 8) return hipErrorInvalidValue;
   int32_t ups;
@@ -833,7 +923,7 @@ hipError_t launch_sparse_v(const SparseVParams& p, hipStream_t stream) {
   sv.ws_m = ws;
   sv.ws_l = ws + bhs;
   sv.ws_o = ws + 2 * bhs;
-  sv.stat_m = ws + bhs * (2 + kD);
+  sv.stat_m = ws + bhs * (2 + size_t(D));
   sv.stat_l = sv.stat_m + bhs;
   sv.stat_n = reinterpret_cast<int32_t*>(sv.stat_l + bhs);
   sv.logit = reinterpret_cast<float*>(sv.stat_n + size_t(B) * Hkv * S);
@@ -842,45 +932,14 @@ hipError_t launch_sparse_v(const SparseVParams& p, hipStream_t stream) {
   sv.tau = p.tau;
   sv.eps = p.eps;
   const int32_t keep_words = (p.max_len + 31) / 32;
-  if (c.kv_dtype == SKV_F16) {
-    const uint16_t* kc = static_cast<const uint16_t*>(c.k);
-    const uint16_t* vc = static_cast<const uint16_t*>(c.v);
-#define SKV_SV_F16(GG)                                                                          \
-  sv_logits_f16<GG><<<grid, kMThreads, 0, stream>>>(kc, p.q, p.seq_len, p.sel_idx, p.sel_cnt,  \
-                                                     p.max_sel, Hkv, c.max_seq, c.block,        \
-                                                     p.max_len, S, n_rows, ups, scale2, sv);    \
-  sv_values_f16<GG><<<grid, kMThreads, 0, stream>>>(vc, p.seq_len, p.sel_idx, p.sel_cnt,       \
-                                                     p.max_sel, Hkv, c.max_seq, c.block,        \
-                                                     p.max_len, S, n_rows, ups, keep_words, sv)
-    switch (G) {
-      case 1: SKV_SV_F16(1); break;
-      case 2: SKV_SV_F16(2); break;
-      case 4: SKV_SV_F16(4); break;
-      default: SKV_SV_F16(8); break;
-    }
-#undef SKV_SV_F16
-    return hipGetLastError();
+  switch (D) {
+    case 64: return launch_sparse_v_d<64>(p, G, grid, n_rows, ups, scale2, sv, keep_words, stream);
+    case 128:
+      return launch_sparse_v_d<128>(p, G, grid, n_rows, ups, scale2, sv, keep_words, stream);
+    case 256:
+      return launch_sparse_v_d<256>(p, G, grid, n_rows, ups, scale2, sv, keep_words, stream);
+    default: return hipErrorInvalidValue;
   }
-  if (c.kv_dtype != SKV_I8) return hipErrorInvalidValue;
-  const int8_t* kc = static_cast<const int8_t*>(c.k);
-  const int8_t* vc = static_cast<const int8_t*>(c.v);
-#define SKV_SV_I8(GG)                                                                           \
-  sv_logits_i8<GG><<<grid, kMThreads, 0, stream>>>(kc, c.k_scale, p.q, p.seq_len, p.sel_idx,   \
-                                                    p.sel_cnt, p.max_sel, Hkv, c.max_seq,       \
-                                                    c.block, p.max_len, S, n_rows, ups, scale2, \
-                                                    sv);                                        \
-  sv_values_i8<GG><<<grid, kMThreads, 0, stream>>>(vc, c.v_scale, p.seq_len, p.sel_idx,        \
-                                                    p.sel_cnt, p.max_sel, Hkv, c.max_seq,       \
-                                                    c.block, p.max_len, S, n_rows, ups,         \
-                                                    keep_words, sv)
-  switch (G) {
-    case 1: SKV_SV_I8(1); break;
-    case 2: SKV_SV_I8(2); break;
-    case 4: SKV_SV_I8(4); break;
-    default: SKV_SV_I8(8); break;
-  }
-#undef SKV_SV_I8
-  return hipGetLastError();
 }
 
 }  // namespace skv

@@ -101,10 +101,11 @@ def test_head_dims_64_256_core_calls_only(lib, dim):
     g = desc(head_dim=dim, kv_dtype=skv.SKV_Q8_0, k_scale=0x5000, v_scale=0x6000)
     assert lib.skv_kv_append(ctypes.byref(g), BAD, 5000, q, q, skv.SKV_F32, None) == \
         skv.SKV_ERANGE
-    # head dim 128 only: sparse-V, the scan
+    # sparse-V: accepted, then the workspace is too small
     assert lib.skv_decode_attn_sparse_v(ctypes.byref(d), q, 32, BAD, 10, None, None, 0, 0.1,
-                                        1e-3, 0.0, 4, BAD, 1 << 30, BAD, None) == \
-        skv.SKV_EUNSUPPORTED
+                                        1e-3, 0.0, 4, BAD, 16, BAD, None) == \
+        skv.SKV_EWORKSPACE
+    # head dim 128 only: the scan
     assert lib.skv_scan4_build(ctypes.byref(d), BAD, BAD, 10, BAD, BAD, BAD, BAD, None) == \
         skv.SKV_EUNSUPPORTED
 

@@ -1,14 +1,15 @@
-"""Head dims 64 and 256: the append, bounds, selection, attention and step
-calls of the f16, int8 and group-wise (q8_0, q4_0, q5_0) caches against the
-oracle (cpu-attn kernel card, "Requirements and limits": the head dimension
+"""Head dims 64 and 256: the append, bounds, selection, attention, sparse-V and
+step calls of the f16, int8 and group-wise (q8_0, q4_0, q5_0) caches against
+the oracle (cpu-attn kernel card, "Requirements and limits": the head dimension
 is any multiple of 16 up to 1024; these two and 128 are built).
 
 Sizes span several tiles per wavefront, several parts and a ragged tail (the
 f16 tile is 16 tokens, the int8 tile 32; a tile's 16-byte loads cover 8, 4 or
 2 rows per instruction at D = 64, 128, 256).  Bars as at D = 128: appended
 rows, codes, scales and bounds exact; int8 logit dots exact; selected sets
-exact on the kernel's own scores; f16 and group-wise outputs within 1e-3 and
-int8 outputs within 1e-4 of the method (per head and per element); the step
+exact on the kernel's own scores; sparse-V keep decisions exact outside the
+oracle's near-threshold band; f16 and group-wise outputs within 1e-3 and int8
+outputs within 1e-4 of the method (per head and per element); the step
 bit-identical to the calls it composes.
 """
 import numpy as np
@@ -18,7 +19,7 @@ import torch
 import oracle
 import workloads
 from gpu_harness import (DEV, assert_close, build_cache, padded_rows, quantized_host, rel_err,
-                         run_dense, run_select, run_sparse)
+                         run_dense, run_select, run_sparse, sel_tensor_from_lists)
 from test_gpu_multi_token import check_dense as chunk_check_dense
 from test_gpu_multi_token import check_quest as chunk_check_quest
 from test_gpu_multi_token import run_chunk
@@ -26,6 +27,9 @@ from test_gpu_per_head import check as per_head_check
 from test_gpu_per_head import run_per_head
 from test_gpu_grouped import check_cache as grouped_check_cache
 from test_gpu_grouped import reference as grouped_reference
+from test_gpu_sparse_v import check_seq as sv_check_seq
+from test_gpu_sparse_v import keep_bits as sv_keep_bits
+from test_gpu_sparse_v import run_sv
 from test_gpu_step import _oracle_check, _run_case
 
 import sparse_kv_cache_append_amd as skv
@@ -359,3 +363,58 @@ def test_other_head_dims_are_refused(gpu_lib):
         skv.scan4_build(c64, idx, torch.zeros(1, dtype=torch.int32, device=DEV), sl, 10)
     assert e.value.status == skv.SKV_EUNSUPPORTED
     torch.cuda.synchronize()
+
+
+SPARSE_V = [
+    # seed, kv, H, Hkv, lens, tau, eps
+    (881, "f16", 32, 8, [1000, 2500], 1e-3, 0.0),
+    (882, "f16", 16, 8, [4097, 64], 0.0, 0.5),
+    (883, "i8", 32, 4, [3000], 0.0, 1.0),
+    (884, "i8", 16, 8, [2049, 95, 1], 5e-4, 0.0),
+]
+
+
+@pytest.mark.parametrize("D", DIMS)
+@pytest.mark.parametrize("seed,kv,H,Hkv,lens,tau,eps", SPARSE_V)
+def test_sparse_v_dense_walk(gpu_lib, D, seed, kv, H, Hkv, lens, tau, eps):
+    _print("sparse-v", D, seed, kv, H, Hkv, lens, tau, eps)
+    w = workloads.clustered([seed + 10 * b for b in range(len(lens))], H, Hkv, D, lens, kv,
+                            n_dirs=8, amp=5.0)
+    cache = build_cache(w)
+    out, kb = run_sv(cache, w, tau, eps)
+    for b in range(w.B):
+        sv_check_seq(w, b, out, kb, tau, eps)
+
+
+@pytest.mark.parametrize("D", DIMS)
+@pytest.mark.parametrize("kv", ["f16", "i8"])
+def test_sparse_v_given_lists_and_zero_threshold(gpu_lib, D, kv):
+    """Quest lists differing per KV head (a clipped last block) with both
+    rules; and a zero threshold, which keeps every token and equals the dense
+    attention."""
+    _print("sparse-v lists", D, kv)
+    w = workloads.clustered([885, 886], 32, 8, D, [5000, 3333], kv, n_dirs=8, amp=5.0)
+    cache = build_cache(w)
+    rng = np.random.default_rng(7)
+    lists = []
+    for b in range(w.B):
+        nb = w.n_blocks(b)
+        lists.append([np.unique(np.concatenate([[0, nb - 1], rng.choice(nb, 17, replace=False)]))
+                      for _ in range(w.Hkv)])
+    max_sel = max(len(x) for row in lists for x in row)
+    si, sc = sel_tensor_from_lists(lists, w.B, w.Hkv, max_sel)
+    for tau, eps in ((2e-3, 0.0), (0.0, 0.3)):
+        out, kb = run_sv(cache, w, tau, eps, sel=(si, sc))
+        for b in range(w.B):
+            sv_check_seq(w, b, out, kb, tau, eps, lists=lists[b])
+    out, kb = run_sv(cache, w, 0.0, 0.0)
+    for b in range(w.B):
+        if kv == "f16":
+            ref = oracle.attend_f16(w.q[b], w.k[b], w.v[b], w.softmax_scale)
+            assert_close(out[b], ref, F16_TOL, b)
+        else:
+            kc, ks, vc, vs = quantized_host(w, b)
+            assert_close(out[b], oracle.attend_i8(w.q[b], kc, ks, vc, vs, w.softmax_scale),
+                         I8_TOL, b)
+        for h in range(w.H):
+            assert sv_keep_bits(kb[b, h], np.arange(w.lens[b])).all()
