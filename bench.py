@@ -553,11 +553,10 @@ def measure(w, args, quest: bool, dense: bool, detail: bool = False):
         if detail:
             res["_roofline"] = (dec_bytes, sel_us, dec_us)
         grouped = w.kv_dtype in ("q8_0", "q4_0", "q5_0")   # per-head and sparse-V: f16, int8
-        other_dim = w.D != 128       # the 4-bit scan is built for head dim 128
         if not args.no_per_head and not grouped:
             res["quest_per_head"] = measure_per_head(T, skv, torch, w, caches, R, q, seq_len, Lmax,
                                                      new_k, new_v, pos_last, ks, res["quest"])
-        if not args.no_scan4 and w.kv_dtype == "f16" and not other_dim:
+        if not args.no_scan4 and w.kv_dtype == "f16":
             res["scan4"] = measure_scan4(T, skv, torch, w, caches, R, q, seq_len, Lmax,
                                          args.scan4_delta)
         n_chunk = min(args.chunk_tokens, 16 // w.G)

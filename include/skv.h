@@ -34,12 +34,13 @@
  *   - The cache's k, v, kmin, kmax, the queries q and the new rows k_new,
  *     v_new are 16-byte aligned, the int8 scales 4-byte aligned (SKV_EINVAL
  *     otherwise); other buffers need their element's natural alignment.
- *   - Supported in this version: head_dim D = 128 for every call, and
- *     D = 64 or 256 for every call except the 4-bit scan (append, bounds,
- *     selection, attention, combine and the step over f16, int8, q8_0, q4_0
- *     and q5_0 caches; sparse-V, per-query-head selection and query-token
- *     chunks over f16 and int8 caches; the cpu-attn kernel card,
- *     "Requirements and limits", admits any multiple of 16 up to 1024);
+ *   - Supported in this version: head_dim D = 64, 128 or 256 for every call
+ *     (each over the cache types it takes: append, bounds, selection,
+ *     attention, combine and the step over f16, int8, q8_0, q4_0 and q5_0
+ *     caches; sparse-V, per-query-head selection and query-token chunks over
+ *     f16 and int8 caches; the 4-bit scan over f16 caches; the cpu-attn
+ *     kernel card, "Requirements and limits", admits any multiple of 16 up to
+ *     1024);
  *     GQA group size
  *     G = H / Hkv in {1, 2, 4, 8}; block a multiple of 16.  Other values that
  *     are otherwise valid return SKV_EUNSUPPORTED.

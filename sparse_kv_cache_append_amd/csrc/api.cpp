@@ -12,10 +12,10 @@ constexpr int32_t kMaxSplit = 4096;
 constexpr int32_t kMaxSelectBlocks = 16384;
 
 bool valid_head_dim(int32_t d) { return d >= 16 && d <= 1024 && d % 16 == 0; }
-// Head dims built: 128 for every call; 64 and 256 for every call but the
-// 4-bit scan (kDimCore below), over every cache type each call takes.
-constexpr int32_t kFullDim = 128;
-bool core_head_dim(int32_t d) { return d == 64 || d == kFullDim || d == 256; }
+// Head dims built: 64, 128 and 256 for every call, over every cache type
+// each call takes; the folded one-token appends move head dim 128 rows.
+constexpr int32_t kFoldDim = 128;
+bool built_head_dim(int32_t d) { return d == 64 || d == kFoldDim || d == 256; }
 bool supported_group(int32_t g) { return g == 1 || g == 2 || g == 4 || g == 8; }
 bool supported_tokens(int32_t n) { return n == 1 || n == 2 || n == 4 || n == 8; }
 
@@ -32,8 +32,7 @@ bool grid_fits(int64_t a, int64_t b, int64_t c) { return a * b * c <= kMaxGridX;
 // The kernels move cache rows, bounds, queries and new rows in 16-byte vectors.
 bool aligned(const void* p, uintptr_t a = 16) { return reinterpret_cast<uintptr_t>(p) % a == 0; }
 
-enum DimUse { kDim128Only = 0, kDimCore = 1 };
-skv_status check_cache(const skv_cache* c, bool need_bounds, DimUse dims = kDim128Only) {
+skv_status check_cache(const skv_cache* c, bool need_bounds) {
   if (c == nullptr) return SKV_EINVAL;
   if (c->batch < 1 || c->n_kv_heads < 1 || c->max_seq < 1) return SKV_EINVAL;
   if (!valid_head_dim(c->head_dim)) return SKV_EINVAL;
@@ -52,8 +51,7 @@ skv_status check_cache(const skv_cache* c, bool need_bounds, DimUse dims = kDim1
   if (elems > 4.0e18) return SKV_ERANGE;
   if (c->batch > kMaxGridYZ || c->n_kv_heads > kMaxGridYZ) return SKV_ERANGE;
   if (!grid_fits(blocks_of(c->max_seq, c->block), c->n_kv_heads, c->batch)) return SKV_ERANGE;
-  if (c->head_dim != kFullDim && (dims != kDimCore || !core_head_dim(c->head_dim)))
-    return SKV_EUNSUPPORTED;
+  if (!built_head_dim(c->head_dim)) return SKV_EUNSUPPORTED;
   return SKV_OK;
 }
 
@@ -115,7 +113,7 @@ const char* skv_status_str(int32_t s) {
 skv_status skv_kv_append(const skv_cache* c, const int32_t* pos0, int32_t n_new,
                          const void* k_new, const void* v_new, int32_t src_dtype,
                          hipStream_t stream) {
-  skv_status st = check_cache(c, false, kDimCore);
+  skv_status st = check_cache(c, false);
   if (st != SKV_OK) return st;
   if (pos0 == nullptr || k_new == nullptr || v_new == nullptr || n_new < 1) return SKV_EINVAL;
   if (!aligned(k_new) || !aligned(v_new)) return SKV_EINVAL;
@@ -128,7 +126,7 @@ skv_status skv_kv_append(const skv_cache* c, const int32_t* pos0, int32_t n_new,
 skv_status skv_block_bounds(const skv_cache* c, const float* q, int32_t n_heads,
                             const int32_t* seq_len, int32_t max_len, float* score,
                             hipStream_t stream) {
-  skv_status st = check_cache(c, true, kDimCore);
+  skv_status st = check_cache(c, true);
   if (st != SKV_OK) return st;
   if (q == nullptr || seq_len == nullptr || score == nullptr || !aligned(q)) return SKV_EINVAL;
   st = check_heads(c, n_heads);
@@ -161,7 +159,7 @@ skv_status skv_decode_attn(const skv_cache* c, const float* q, int32_t n_heads,
                            float softmax_scale, int32_t n_split,
                            void* workspace, size_t workspace_bytes,
                            int32_t* dbg_logits, hipStream_t stream) {
-  skv_status st = check_cache(c, false, kDimCore);
+  skv_status st = check_cache(c, false);
   if (st != SKV_OK) return st;
   if (q == nullptr || seq_len == nullptr || !aligned(q)) return SKV_EINVAL;
   st = check_heads(c, n_heads);
@@ -199,7 +197,7 @@ skv_status skv_decode_step(const skv_cache* c, const int32_t* pos0, const void* 
                            float softmax_scale, int32_t n_split, void* workspace,
                            size_t workspace_bytes, float* out, hipStream_t stream) {
   const bool quest = k_sel != nullptr;
-  skv_status st = check_cache(c, quest, kDimCore);
+  skv_status st = check_cache(c, quest);
   if (st != SKV_OK) return st;
   if (q == nullptr || seq_len == nullptr || out == nullptr || !aligned(q)) return SKV_EINVAL;
   st = check_heads(c, n_heads);
@@ -240,7 +238,7 @@ skv_status skv_decode_step(const skv_cache* c, const int32_t* pos0, const void* 
   hipError_t e = hipSuccess;
   const bool grouped = skv::is_grouped(c->kv_dtype);
   // the folded appends move head dim 128 rows
-  const bool fold = c->head_dim == kFullDim;
+  const bool fold = c->head_dim == kFoldDim;
   if (k_new != nullptr && ((grouped && !quest) || !fold)) {
     // dense steps over group-wise caches, and every step at another head dim:
     // the append runs as its own kernel (else the Quest step folds it into
@@ -280,7 +278,7 @@ skv_status skv_decode_attn_select(const skv_cache* c, const float* q, int32_t n_
                                   int32_t max_sel, int32_t* sel_idx, int32_t* sel_cnt,
                                   float softmax_scale, int32_t n_split, void* workspace,
                                   size_t workspace_bytes, hipStream_t stream) {
-  skv_status st = check_cache(c, false, kDimCore);
+  skv_status st = check_cache(c, false);
   if (st != SKV_OK) return st;
   if (q == nullptr || seq_len == nullptr || !aligned(q)) return SKV_EINVAL;
   st = check_heads(c, n_heads);
@@ -325,7 +323,7 @@ skv_status skv_decode_attn_select(const skv_cache* c, const float* q, int32_t n_
 skv_status skv_block_bounds_heads(const skv_cache* c, const float* q, int32_t n_heads,
                                   const int32_t* seq_len, int32_t max_len, float* score,
                                   hipStream_t stream) {
-  skv_status st = check_cache(c, true, kDimCore);
+  skv_status st = check_cache(c, true);
   if (st != SKV_OK) return st;
   if (q == nullptr || seq_len == nullptr || score == nullptr || !aligned(q)) return SKV_EINVAL;
   st = check_heads(c, n_heads);
@@ -357,7 +355,7 @@ skv_status skv_decode_attn_heads(const skv_cache* c, const float* q, int32_t n_h
                                  const uint32_t* uni_mask, int32_t max_union,
                                  float softmax_scale, int32_t n_split, void* workspace,
                                  size_t workspace_bytes, hipStream_t stream) {
-  skv_status st = check_cache(c, false, kDimCore);
+  skv_status st = check_cache(c, false);
   if (st != SKV_OK) return st;
   if (q == nullptr || seq_len == nullptr || !aligned(q)) return SKV_EINVAL;
   if (uni_idx == nullptr || uni_cnt == nullptr || uni_mask == nullptr || max_union < 1)
@@ -392,7 +390,7 @@ skv_status skv_decode_attn_heads(const skv_cache* c, const float* q, int32_t n_h
 skv_status skv_block_bounds_multi(const skv_cache* c, const float* q, int32_t n_tokens,
                                   int32_t n_heads, const int32_t* seq_len, int32_t max_len,
                                   float* score, hipStream_t stream) {
-  skv_status st = check_cache(c, true, kDimCore);
+  skv_status st = check_cache(c, true);
   if (st != SKV_OK) return st;
   if (q == nullptr || seq_len == nullptr || score == nullptr || !aligned(q)) return SKV_EINVAL;
   st = check_heads(c, n_heads);
@@ -449,7 +447,7 @@ skv_status skv_decode_attn_multi(const skv_cache* c, const float* q, int32_t n_t
                                  const uint32_t* uni_mask, int32_t max_union,
                                  float softmax_scale, int32_t n_split, void* workspace,
                                  size_t workspace_bytes, hipStream_t stream) {
-  skv_status st = check_cache(c, false, kDimCore);
+  skv_status st = check_cache(c, false);
   if (st != SKV_OK) return st;
   if (q == nullptr || seq_len == nullptr || !aligned(q)) return SKV_EINVAL;
   const bool list = uni_idx != nullptr;
@@ -561,7 +559,7 @@ skv_status skv_decode_attn_sparse_v(const skv_cache* c, const float* q, int32_t 
                                     int32_t max_sel, float softmax_scale, float tau, float eps,
                                     int32_t n_split, void* workspace, size_t workspace_bytes,
                                     uint32_t* keep_mask, hipStream_t stream) {
-  skv_status st = check_cache(c, false, kDimCore);
+  skv_status st = check_cache(c, false);
   if (st != SKV_OK) return st;
   if (q == nullptr || seq_len == nullptr || !aligned(q)) return SKV_EINVAL;
   st = check_heads(c, n_heads);

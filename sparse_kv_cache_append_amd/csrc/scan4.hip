@@ -17,6 +17,9 @@
 //   LB = s~ - r_h <= q.k_t <= UB = s~ + r_h.
 // Candidates of head h for a margin delta: UB_t >= max_u LB_u - delta.
 //
+// Head dims D = 64, 128, 256 (the index rows are D / 2 bytes of nibbles and
+// D floats of lo / step / err per block).
+//
 // Kernels: scan4_build (one workgroup per (block, KV head, sequence));
 // scan4_bounds (pass 1: split-K parts as the decode kernels, the codes of a
 // KV head read once for its G query heads: q.K~ on the matrix cores with the
@@ -35,20 +38,22 @@ namespace {
 
 constexpr int kLevels = 15;
 constexpr int kScanBlockMax = 256;
-constexpr int kRow4 = kD / 2;              // 64 bytes of nibbles per (token, KV head)
 
 // ------------------------------------------------------------------- build
 // The block's keys (up to 64 tokens at a time) are staged in LDS with
-// 16-byte loads, all in flight at once, then thread d < 128 reduces channel d.
+// 16-byte loads, all in flight at once, then thread d < D reduces channel d
+// (head dim D = 64, 128 or 256; a token's row of nibbles is D / 2 bytes).
 constexpr int kBuildChunk = 64;
+template <int D>
 __global__ void __launch_bounds__(256)
 scan4_build(const uint16_t* __restrict__ kc, const int32_t* __restrict__ pos0,
             const int32_t* __restrict__ seq_len, int32_t Hkv, int32_t max_seq, int32_t max_len,
             int32_t block, int32_t max_blocks, uint8_t* __restrict__ codes4,
             float* __restrict__ lo_out, float* __restrict__ step_out,
             float* __restrict__ err_out) {
-  __shared__ uint8_t cs[kScanBlockMax][kD];
-  __shared__ __attribute__((aligned(16))) uint16_t ks[kBuildChunk][kD];
+  constexpr int kRow4 = D / 2;
+  __shared__ uint8_t cs[kScanBlockMax][D];
+  __shared__ __attribute__((aligned(16))) uint16_t ks[kBuildChunk][D];
   const int32_t g = blockIdx.y, b = blockIdx.z;
   const int32_t L = min(max(seq_len[b], 0), max_len);
   const int32_t p0 = pos0[b];
@@ -58,19 +63,19 @@ scan4_build(const uint16_t* __restrict__ kc, const int32_t* __restrict__ pos0,
   const int32_t t0 = j * block, t1 = min(t0 + block, L);
   const int64_t bg = int64_t(b) * Hkv + g;
   const int d = threadIdx.x;
-  const uint4* krow = reinterpret_cast<const uint4*>(kc + (bg * max_seq) * kD);
+  const uint4* krow = reinterpret_cast<const uint4*>(kc + (bg * max_seq) * D);
   // one chunk of rows into LDS: 16 bytes per thread per instruction
   auto stage = [&](int32_t c0, int32_t n) {
     __syncthreads();
-    for (int32_t e = threadIdx.x; e < n * (kD / 8); e += 256)
-      reinterpret_cast<uint4*>(&ks[0][0])[e] = krow[int64_t(c0) * (kD / 8) + e];
+    for (int32_t e = threadIdx.x; e < n * (D / 8); e += 256)
+      reinterpret_cast<uint4*>(&ks[0][0])[e] = krow[int64_t(c0) * (D / 8) + e];
     __syncthreads();
   };
   float mn = INFINITY, mx = -INFINITY;
   for (int32_t c0 = t0; c0 < t1; c0 += kBuildChunk) {
     const int32_t n = min(kBuildChunk, t1 - c0);
     stage(c0, n);
-    if (d < kD) {
+    if (d < D) {
       for (int32_t t = 0; t < n; ++t) {
         const float x = h2f(ks[t][d]);
         mn = fminf(mn, x);
@@ -79,11 +84,11 @@ scan4_build(const uint16_t* __restrict__ kc, const int32_t* __restrict__ pos0,
     }
   }
   float lo = mn, st = 0.0f, err = 0.0f;
-  if (d < kD) st = __fdiv_rn(__fsub_rn(mx, mn), float(kLevels));
+  if (d < D) st = __fdiv_rn(__fsub_rn(mx, mn), float(kLevels));
   for (int32_t c0 = t0; c0 < t1; c0 += kBuildChunk) {
     const int32_t n = min(kBuildChunk, t1 - c0);
     if (block > kBuildChunk) stage(c0, n);           // else the chunk is still staged
-    if (d >= kD) continue;
+    if (d >= D) continue;
     for (int32_t t = c0; t < c0 + n; ++t) {
       const float x = h2f(ks[t - c0][d]);
       float c = 0.0f;
@@ -97,8 +102,8 @@ scan4_build(const uint16_t* __restrict__ kc, const int32_t* __restrict__ pos0,
       cs[t - t0][d] = uint8_t(c);
     }
   }
-  if (d < kD) {
-    const int64_t o = (bg * max_blocks + j) * kD + d;
+  if (d < D) {
+    const int64_t o = (bg * max_blocks + j) * D + d;
     lo_out[o] = lo;
     step_out[o] = st;
     err_out[o] = err;
@@ -134,15 +139,48 @@ __device__ __forceinline__ constexpr int nib_pos(int s) { return (s & 1) ? 4 + (
 
 // T-token tiles (T = 64 when the block is a multiple of 64, else 32), two in
 // flight per wavefront.  The codes go straight from memory into the MFMA
-// operand registers: lane (lg, lc) loads the 16 bytes of token 16 s + lc
-// that hold channels 32 lg .. 32 lg + 31, and MFMA kk takes channels
-// 32 lg + 8 kk .. + 7 as its K index 8 lg .. 8 lg + 7 (the query side uses
-// the same assignment, so the dot is over all 128 channels).  Each tile's
-// refill also requests its block's lo, step and err rows (8 bytes of each per
-// lane, 1.5 KiB per tile), staged through LDS, so no tile waits on a separate
-// round trip for its block's operands.
-template <int G, int T>
-__global__ void __launch_bounds__(kMThreads, 2)
+// operand registers: lane (lg, lc) loads the D / 8 bytes of token 16 s + lc
+// that hold channels CW lg .. CW lg + CW - 1 (CW = D / 4: 16 B, channels
+// 32 lg .. 32 lg + 31 at D = 128), and MFMA kk (kk < D / 32) takes channels
+// CW lg + 8 kk .. + 7 as its K index 8 lg .. 8 lg + 7 (the query side uses
+// the same assignment, so the dot is over all D channels).  Each tile's
+// refill also requests its block's lo, step and err rows (D / 16 bytes of
+// each per lane, 12 D bytes per tile), staged through LDS, so no tile waits
+// on a separate round trip for its block's operands.
+// NW 32-bit words of one lane, as one vector register tuple.
+template <int NW>
+struct LaneWords {
+  typedef unsigned int V __attribute__((ext_vector_type(NW)));
+  V w;
+};
+template <int NW, int AUX>
+__device__ __forceinline__ LaneWords<NW> load_words(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
+  typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  LaneWords<NW> r;
+  if constexpr (NW == 1) {
+    r.w[0] = __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, AUX);
+  } else if constexpr (NW == 2) {
+    r.w = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, AUX));
+  } else if constexpr (NW == 4) {
+    r.w = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, AUX));
+  } else {
+    static_assert(NW == 8, "at most 32 bytes per lane");
+    const u32x4 lo = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, AUX));
+    const u32x4 hi =
+        __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16u, 0, AUX));
+    r.w = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+  return r;
+}
+// NW words to LDS at a 4 NW-byte aligned address, in one store.
+template <int NW>
+__device__ __forceinline__ void store_words(float* dst, const LaneWords<NW>& v) {
+  static_assert(NW == 1 || NW == 2 || NW == 4, "at most 16 bytes per lane");
+  *reinterpret_cast<typename LaneWords<NW>::V*>(dst) = v.w;
+}
+template <int D, int G, int T>
+__global__ void __launch_bounds__(kMThreads, D > 128 ? 1 : 2)
 scan4_bounds(const uint8_t* __restrict__ codes4, const float* __restrict__ lo_in,
              const float* __restrict__ step_in, const float* __restrict__ err_in,
              const float* __restrict__ q, const int32_t* __restrict__ seq_len, int32_t Hkv,
@@ -150,11 +188,16 @@ scan4_bounds(const uint8_t* __restrict__ codes4, const float* __restrict__ lo_in
              int32_t n_split, int32_t n_rows, int32_t ups, float* __restrict__ ub_out,
              float* __restrict__ lbmax, int32_t* __restrict__ cand_cnt) {
   constexpr int kSubs = T / 16;                              // 16-token MFMA row blocks
-  __shared__ __attribute__((aligned(16))) float sprm[kMWaves][2][3][kD];   // lo, step, err
+  constexpr int KS = D / 32;                                 // MFMA steps (per 32 channels)
+  constexpr int CW = D / 4;                                  // channels per lane group
+  constexpr int kCwLog = CW == 16 ? 4 : CW == 32 ? 5 : 6;
+  constexpr int kRow4 = D / 2;                               // nibble bytes per token
+  constexpr int NPW = D / 64;                                // lo / step / err floats per lane
+  __shared__ __attribute__((aligned(16))) float sprm[kMWaves][2][3][D];    // lo, step, err
   // the B operands of the tile's block (f16 high, low) for MFMA lane
   // (lg, lc < G) at entry lg G + lc, and the per-head scalars, written and
   // read by one wavefront
-  __shared__ __attribute__((aligned(16))) uint32_t sbw[kMWaves][2][4][4 * G][4];
+  __shared__ __attribute__((aligned(16))) uint32_t sbw[kMWaves][2][KS][4 * G][4];
   __shared__ float shd[kMWaves][3][16];
   __shared__ float red[kMWaves][16];
   const uint32_t slot = xcd_slot(blockIdx.x, gridDim.x);
@@ -174,16 +217,20 @@ scan4_bounds(const uint8_t* __restrict__ codes4, const float* __restrict__ lo_in
   // (LPH = 64 / G lanes per head, CPL = 2 G channels each), instead of every
   // lane computing its own 32 channels for its MFMA column (of which only G
   // of 16 are heads).
-  constexpr int LPH = kWave / G, CPL = kD / LPH;
+  constexpr int LPH = kWave / G, CPL = D / LPH;
   const int ph = lane / LPH, pc = (lane % LPH) * CPL;
   float qd[CPL];
   {
-    const float* qp = q + (int64_t(b) * H + g * G + ph) * kD + pc;
+    const float* qp = q + (int64_t(b) * H + g * G + ph) * D + pc;
+    if constexpr (CPL == 1) {
+      qd[0] = qp[0];
+    } else {
 #pragma unroll
-    for (int e = 0; e < CPL; e += 2) {
-      const float2 v2 = *reinterpret_cast<const float2*>(qp + e);
-      qd[e] = v2.x;
-      qd[e + 1] = v2.y;
+      for (int e = 0; e < CPL; e += 2) {
+        const float2 v2 = *reinterpret_cast<const float2*>(qp + e);
+        qd[e] = v2.x;
+        qd[e + 1] = v2.y;
+      }
     }
   }
   const int32_t L = __builtin_amdgcn_readfirstlane(min(max(L_raw, 0), max_len));
@@ -191,14 +238,14 @@ scan4_bounds(const uint8_t* __restrict__ codes4, const float* __restrict__ lo_in
   TileWalk tw = make_walk<T>(ls, nullptr, 0, bg, L, block, split, ups);
   tw.init(wave);
   const uint8_t* cbase = codes4 + bg * int64_t(max_seq) * kRow4;
-  const uint8_t* lbase = reinterpret_cast<const uint8_t*>(lo_in + bg * int64_t(max_blocks) * kD);
-  const uint8_t* sbase = reinterpret_cast<const uint8_t*>(step_in + bg * int64_t(max_blocks) * kD);
-  const uint8_t* ebase = reinterpret_cast<const uint8_t*>(err_in + bg * int64_t(max_blocks) * kD);
+  const uint8_t* lbase = reinterpret_cast<const uint8_t*>(lo_in + bg * int64_t(max_blocks) * D);
+  const uint8_t* sbase = reinterpret_cast<const uint8_t*>(step_in + bg * int64_t(max_blocks) * D);
+  const uint8_t* ebase = reinterpret_cast<const uint8_t*>(err_in + bg * int64_t(max_blocks) * D);
   float* urow = ub_out + (int64_t(b) * H + g * G + (hv ? lc : 0)) * int64_t(max_len);
   float lb_run = -INFINITY;
   struct Frag {
-    int4_t c[kSubs];         // token 16 s + lc, channels 32 lg .. 32 lg + 31
-    int2_t p[3];             // channels 2 lane, 2 lane + 1 of lo, step, err
+    LaneWords<KS> c[kSubs];  // token 16 s + lc, channels CW lg .. CW lg + CW - 1
+    LaneWords<NPW> p[3];     // channels NPW lane .. NPW lane + NPW - 1 of lo, step, err
     int32_t r0, nvalid;
   };
   // Every refill issues the same loads, through resources of zero records
@@ -212,23 +259,23 @@ scan4_bounds(const uint8_t* __restrict__ codes4, const float* __restrict__ lo_in
     const auto cr = tile_rsrc(cbase + int64_t(r0) * kRow4, bytes);
 #pragma unroll
     for (int i = 0; i < kSubs; ++i)
-      f.c[i] = tile_load(cr, uint32_t(1024 * i + kRow4 * lc + 16 * lg));
-    const int pbytes = __builtin_amdgcn_readfirstlane(nv > 0 ? kD * 4 : 0);
-    const int64_t po = int64_t(r0 / block) * kD * 4;
+      f.c[i] = load_words<KS, kAuxNontemporal>(
+          cr, uint32_t(16 * kRow4 * i + kRow4 * lc + (D / 8) * lg));
+    const int pbytes = __builtin_amdgcn_readfirstlane(nv > 0 ? D * 4 : 0);
+    const int64_t po = int64_t(r0 / block) * D * 4;
     const uint8_t* bases[3] = {lbase, sbase, ebase};
 #pragma unroll
     for (int a = 0; a < 3; ++a) {
       const auto pr = tile_rsrc(bases[a] + po, pbytes);
-      f.p[a] = __builtin_bit_cast(int2_t, __builtin_amdgcn_raw_buffer_load_b64(
-                                              pr, 8u * uint32_t(lane), 0, 0));
+      f.p[a] = load_words<NPW, 0>(pr, 4u * NPW * uint32_t(lane));
     }
   };
   auto process = [&](auto bufc, Frag& fr) {
     constexpr int kBuf = decltype(bufc)::value;
-    float(*pm)[kD] = sprm[wave][kBuf];
+    float(*pm)[D] = sprm[wave][kBuf];
 #pragma unroll
-    for (int a = 0; a < 3; ++a) *reinterpret_cast<int2_t*>(&pm[a][2 * lane]) = fr.p[a];
-    int4_t cv[kSubs];
+    for (int a = 0; a < 3; ++a) store_words<NPW>(&pm[a][NPW * lane], fr.p[a]);
+    LaneWords<KS> cv[kSubs];
 #pragma unroll
     for (int i = 0; i < kSubs; ++i) cv[i] = fr.c[i];
     const int32_t nvalid = fr.nvalid, r0 = fr.r0;
@@ -242,18 +289,25 @@ scan4_bounds(const uint8_t* __restrict__ codes4, const float* __restrict__ lo_in
     // exactly); a_h = sum q lo, r_h = sum |q| err
     float pa = 0.0f, pr = 0.0f, mw = 0.0f;
     float wv[CPL];
+    if constexpr (CPL == 1) {
+      wv[0] = qd[0] * pm[1][pc];
+      mw = fabsf(wv[0]);
+      pa = qd[0] * pm[0][pc];
+      pr = fabsf(qd[0]) * pm[2][pc];
+    } else {
 #pragma unroll
-    for (int e = 0; e < CPL; e += 2) {
-      const float2 s2 = *reinterpret_cast<const float2*>(&pm[1][pc + e]);
-      const float2 l2 = *reinterpret_cast<const float2*>(&pm[0][pc + e]);
-      const float2 e2 = *reinterpret_cast<const float2*>(&pm[2][pc + e]);
-      const float sv[2] = {s2.x, s2.y}, lv[2] = {l2.x, l2.y}, ev[2] = {e2.x, e2.y};
+      for (int e = 0; e < CPL; e += 2) {
+        const float2 s2 = *reinterpret_cast<const float2*>(&pm[1][pc + e]);
+        const float2 l2 = *reinterpret_cast<const float2*>(&pm[0][pc + e]);
+        const float2 e2 = *reinterpret_cast<const float2*>(&pm[2][pc + e]);
+        const float sv[2] = {s2.x, s2.y}, lv[2] = {l2.x, l2.y}, ev[2] = {e2.x, e2.y};
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        wv[e + i] = qd[e + i] * sv[i];
-        mw = fmaxf(mw, fabsf(wv[e + i]));
-        pa += qd[e + i] * lv[i];
-        pr += fabsf(qd[e + i]) * ev[i];
+        for (int i = 0; i < 2; ++i) {
+          wv[e + i] = qd[e + i] * sv[i];
+          mw = fmaxf(mw, fabsf(wv[e + i]));
+          pa += qd[e + i] * lv[i];
+          pr += fabsf(qd[e + i]) * ev[i];
+        }
       }
     }
     // the head's LPH lanes
@@ -265,7 +319,7 @@ scan4_bounds(const uint8_t* __restrict__ codes4, const float* __restrict__ lo_in
     }
     {
       const int we = mw > 0.0f ? 14 - __builtin_amdgcn_frexp_expf(mw) : 0;
-      // channel c lies in MFMA step (c / 8) % 4 at lane entry G (c / 32) +
+      // channel c lies in MFMA step (c % CW) / 8 at lane entry G (c / CW) +
       // head, position nib_pos(c % 8) of the 8 f16 (the A side's order):
       // channels c, c + 2 (c % 4 < 2) share one 32-bit word
       auto split = [&](float x, uint16_t& h, uint16_t& l) {
@@ -282,7 +336,8 @@ scan4_bounds(const uint8_t* __restrict__ codes4, const float* __restrict__ lo_in
           uint16_t h0, l0, h1, l1;
           split(wv[e], h0, l0);
           split(wv[e + 2], h1, l1);
-          const int kk = (c >> 3) & 3, col = G * (c >> 5) + ph, wd = nib_pos(c & 7) >> 1;
+          const int kk = (c >> 3) & (CW / 8 - 1), col = G * (c >> kCwLog) + ph,
+                    wd = nib_pos(c & 7) >> 1;
           sbw[wave][0][kk][col][wd] = uint32_t(h0) | (uint32_t(h1) << 16);
           sbw[wave][1][kk][col][wd] = uint32_t(l0) | (uint32_t(l1) << 16);
         }
@@ -292,7 +347,8 @@ scan4_bounds(const uint8_t* __restrict__ codes4, const float* __restrict__ lo_in
           const int c = pc + e;
           uint16_t h0, l0;
           split(wv[e], h0, l0);
-          const int kk = (c >> 3) & 3, col = G * (c >> 5) + ph, pos = nib_pos(c & 7);
+          const int kk = (c >> 3) & (CW / 8 - 1), col = G * (c >> kCwLog) + ph,
+                    pos = nib_pos(c & 7);
           reinterpret_cast<uint16_t*>(&sbw[wave][0][kk][col][0])[pos] = h0;
           reinterpret_cast<uint16_t*>(&sbw[wave][1][kk][col][0])[pos] = l0;
         }
@@ -305,9 +361,9 @@ scan4_bounds(const uint8_t* __restrict__ codes4, const float* __restrict__ lo_in
     }
     // the stores above precede these reads (one wavefront, in order)
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    half8_t whi[4], wlo[4];
+    half8_t whi[KS], wlo[KS];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
+    for (int kk = 0; kk < KS; ++kk) {
       whi[kk] = hv ? *reinterpret_cast<const half8_t*>(&sbw[wave][0][kk][G * lg + (hv ? lc : 0)][0]) : half8_t{};
       wlo[kk] = hv ? *reinterpret_cast<const half8_t*>(&sbw[wave][1][kk][G * lg + (hv ? lc : 0)][0]) : half8_t{};
     }
@@ -321,9 +377,9 @@ scan4_bounds(const uint8_t* __restrict__ codes4, const float* __restrict__ lo_in
     for (int s = 0; s < kSubs; ++s) {
       float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        // token 16 s + lc, channels 32 lg + 8 kk .. + 7: 4 bytes of nibbles
-        const half8_t a = nibbles_to_half8(uint32_t(cv[s][kk]));
+      for (int kk = 0; kk < KS; ++kk) {
+        // token 16 s + lc, channels CW lg + 8 kk .. + 7: 4 bytes of nibbles
+        const half8_t a = nibbles_to_half8(cv[s].w[kk]);
         acc = mfma_f16_32(a, whi[kk], acc);
         acc = mfma_f16_32(a, wlo[kk], acc);
       }
@@ -441,9 +497,17 @@ hipError_t launch_scan4_build(const skv_cache& c, const int32_t* pos0, const int
   const int32_t max_blocks = (c.max_seq + c.block - 1) / c.block;
   const int32_t nb = (max_len + c.block - 1) / c.block;
   if (nb == 0) return hipSuccess;
-  scan4_build<<<dim3(nb, c.n_kv_heads, c.batch), 256, 0, stream>>>(
-      static_cast<const uint16_t*>(c.k), pos0, seq_len, c.n_kv_heads, c.max_seq, max_len,
-      c.block, max_blocks, codes4, lo, step, err);
+#define SKV_BUILD(DD)                                                                           \
+  scan4_build<DD><<<dim3(nb, c.n_kv_heads, c.batch), 256, 0, stream>>>(                        \
+      static_cast<const uint16_t*>(c.k), pos0, seq_len, c.n_kv_heads, c.max_seq, max_len,      \
+      c.block, max_blocks, codes4, lo, step, err)
+  switch (c.head_dim) {
+    case 64: SKV_BUILD(64); break;
+    case 128: SKV_BUILD(128); break;
+    case 256: SKV_BUILD(256); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef SKV_BUILD
   return hipGetLastError();
 }
 
@@ -459,19 +523,27 @@ hipError_t launch_scan4(const Scan4Params& p, hipStream_t stream) {
   if (n_wg > 0x7fffffff) return hipErrorInvalidValue;
   float* ub = p.ws;
   float* lbm = p.ws + size_t(B) * H * p.max_len;
-#define SKV_SCAN(GG, TT)                                                                        \
-  scan4_bounds<GG, TT><<<dim3(uint32_t(n_wg)), kMThreads, 0, stream>>>(                        \
+  if (G != 1 && G != 2 && G != 4 && G != 8) return hipErrorInvalidValue;
+  if (c.head_dim != 64 && c.head_dim != 128 && c.head_dim != 256) return hipErrorInvalidValue;
+#define SKV_SCAN(DD, GG, TT)                                                                    \
+  scan4_bounds<DD, GG, TT><<<dim3(uint32_t(n_wg)), kMThreads, 0, stream>>>(                    \
       p.codes4, p.lo, p.step, p.err, p.q, p.seq_len, Hkv, c.max_seq, c.block, max_blocks,     \
       p.max_len, S, Hkv * B, ups, ub, lbm, p.cand_cnt)
-#define SKV_SCAN_T(GG)                                                                          \
-  if (c.block % 64 == 0) SKV_SCAN(GG, 64); else SKV_SCAN(GG, 32);
-  switch (G) {
-    case 1: SKV_SCAN_T(1); break;
-    case 2: SKV_SCAN_T(2); break;
-    case 4: SKV_SCAN_T(4); break;
-    case 8: SKV_SCAN_T(8); break;
-    default: return hipErrorInvalidValue;
+#define SKV_SCAN_T(DD, GG)                                                                      \
+  if (c.block % 64 == 0) SKV_SCAN(DD, GG, 64); else SKV_SCAN(DD, GG, 32);
+#define SKV_SCAN_G(DD)                         \
+  switch (G) {                                 \
+    case 1: SKV_SCAN_T(DD, 1); break;          \
+    case 2: SKV_SCAN_T(DD, 2); break;          \
+    case 4: SKV_SCAN_T(DD, 4); break;          \
+    default: SKV_SCAN_T(DD, 8); break;         \
   }
+  switch (c.head_dim) {
+    case 64: SKV_SCAN_G(64); break;
+    case 128: SKV_SCAN_G(128); break;
+    default: SKV_SCAN_G(256); break;
+  }
+#undef SKV_SCAN_G
 #undef SKV_SCAN_T
 #undef SKV_SCAN
   hipError_t e = hipGetLastError();

@@ -74,9 +74,8 @@ def test_cache_descriptor_validation(lib, kw, expect):
 
 @pytest.mark.parametrize("dim", [64, 256])
 def test_head_dims_64_256_core_calls_only(lib, dim):
-    """Head dims 64 and 256 pass the descriptor check of the calls built for
-    them (the calls below then stop at a later check, before any launch) and
-    are refused by the calls built for head dim 128 only."""
+    """Head dims 64 and 256 pass the descriptor check of every call (the
+    calls below then stop at a later check, before any launch)."""
     d = desc(head_dim=dim)
     q = 0x7000
     # decode_attn: accepted, then the workspace is too small
@@ -105,9 +104,9 @@ def test_head_dims_64_256_core_calls_only(lib, dim):
     assert lib.skv_decode_attn_sparse_v(ctypes.byref(d), q, 32, BAD, 10, None, None, 0, 0.1,
                                         1e-3, 0.0, 4, BAD, 16, BAD, None) == \
         skv.SKV_EWORKSPACE
-    # head dim 128 only: the scan
-    assert lib.skv_scan4_build(ctypes.byref(d), BAD, BAD, 10, BAD, BAD, BAD, BAD, None) == \
-        skv.SKV_EUNSUPPORTED
+    # the scan: accepted, then a range check fails
+    assert lib.skv_scan4_build(ctypes.byref(d), BAD, BAD, 5000, BAD, BAD, BAD, BAD, None) == \
+        skv.SKV_ERANGE
 
 
 def test_decode_argument_validation(lib):

@@ -1,6 +1,6 @@
-"""Head dims 64 and 256: the append, bounds, selection, attention, sparse-V and
-step calls of the f16, int8 and group-wise (q8_0, q4_0, q5_0) caches against
-the oracle (cpu-attn kernel card, "Requirements and limits": the head dimension
+"""Head dims 64 and 256: the append, bounds, selection, attention, sparse-V,
+4-bit scan and step calls of the f16, int8 and group-wise (q8_0, q4_0, q5_0)
+caches against the oracle (cpu-attn kernel card, "Requirements and limits": the head dimension
 is any multiple of 16 up to 1024; these two and 128 are built).
 
 Sizes span several tiles per wavefront, several parts and a ragged tail (the
@@ -8,7 +8,8 @@ f16 tile is 16 tokens, the int8 tile 32; a tile's 16-byte loads cover 8, 4 or
 2 rows per instruction at D = 64, 128, 256).  Bars as at D = 128: appended
 rows, codes, scales and bounds exact; int8 logit dots exact; selected sets
 exact on the kernel's own scores; sparse-V keep decisions exact outside the
-oracle's near-threshold band; f16 and group-wise outputs within 1e-3 and int8
+oracle's near-threshold band; the scan's index bit-exact and its bounds and
+candidates as at head dim 128; f16 and group-wise outputs within 1e-3 and int8
 outputs within 1e-4 of the method (per head and per element); the step
 bit-identical to the calls it composes.
 """
@@ -30,6 +31,10 @@ from test_gpu_grouped import reference as grouped_reference
 from test_gpu_sparse_v import check_seq as sv_check_seq
 from test_gpu_sparse_v import keep_bits as sv_keep_bits
 from test_gpu_sparse_v import run_sv
+from test_gpu_scan4 import build as scan4_index
+from test_gpu_scan4 import check_index as scan4_check_index
+from test_gpu_scan4 import check_scan as scan4_check_scan
+from test_gpu_scan4 import run_scan as scan4_run
 from test_gpu_step import _oracle_check, _run_case
 
 import sparse_kv_cache_append_amd as skv
@@ -347,8 +352,8 @@ def test_quest_chunk(gpu_lib, D, seeds, H, Hkv, lens, kv, T, ksel):
 
 
 def test_other_head_dims_are_refused(gpu_lib):
-    """Head dim 96 (a multiple of 16, not built), and a call built for 128
-    only (the 4-bit scan) at 64, raise SKV_EUNSUPPORTED before any launch."""
+    """Head dim 96 (a multiple of 16, not built) raises SKV_EUNSUPPORTED
+    before any launch."""
     _print("refused")
     c96 = skv.Cache(1, 2, 128, 96, "f16", 64, device=DEV)
     q = torch.zeros((1, 8, 96), dtype=torch.float32, device=DEV)
@@ -357,10 +362,9 @@ def test_other_head_dims_are_refused(gpu_lib):
     with pytest.raises(skv.SkvError) as e:
         skv.block_bounds(c96, q, sl, 10, score)
     assert e.value.status == skv.SKV_EUNSUPPORTED
-    c64 = skv.Cache(1, 2, 128, 64, "f16", 64, device=DEV)
-    idx = skv.Scan4Index(c64, device=DEV)
+    idx = skv.Scan4Index(c96, device=DEV)
     with pytest.raises(skv.SkvError) as e:
-        skv.scan4_build(c64, idx, torch.zeros(1, dtype=torch.int32, device=DEV), sl, 10)
+        skv.scan4_build(c96, idx, torch.zeros(1, dtype=torch.int32, device=DEV), sl, 10)
     assert e.value.status == skv.SKV_EUNSUPPORTED
     torch.cuda.synchronize()
 
@@ -418,3 +422,35 @@ def test_sparse_v_given_lists_and_zero_threshold(gpu_lib, D, kv):
                          I8_TOL, b)
         for h in range(w.H):
             assert sv_keep_bits(kb[b, h], np.arange(w.lens[b])).all()
+
+
+@pytest.mark.parametrize("D", DIMS)
+@pytest.mark.parametrize("H,Hkv,lens,block", [(32, 8, [3000, 777], 64), (8, 8, [1500], 16),
+                                              (16, 8, [1200], 32), (8, 1, [2049, 5], 128)])
+def test_scan4_index_and_candidates(gpu_lib, D, H, Hkv, lens, block):
+    """Every GQA group size (at D = 64 and G = 1 each lane takes one channel
+    of the block's operands), 64- and 32-token tiles, ragged tails."""
+    _print("scan4", D, H, Hkv, lens, block)
+    w = workloads.clustered([970 + D + b for b in range(len(lens))], H, Hkv, D, lens, "f16",
+                            n_dirs=8, amp=4.0, block=block)
+    cache = build_cache(w)
+    idx = scan4_index(cache, w)
+    for delta in (0.0, 8.0):
+        ub, cand, cnt = scan4_run(cache, idx, w, delta)
+        for b in range(w.B):
+            index = scan4_check_index(idx, w, b)
+            scan4_check_scan(w, b, index, ub, cand, cnt, delta)
+
+
+@pytest.mark.parametrize("D", DIMS)
+def test_scan4_rebuild_after_append(gpu_lib, D):
+    w = workloads.gaussian(975 + D, 2, 16, 4, D, [1000, 2049], "f16")
+    cache = build_cache(w)
+    lens_m1 = torch.tensor([L - 1 for L in w.lens], dtype=torch.int32, device=DEV)
+    idx = scan4_index(cache, w, seq=lens_m1)
+    pos = torch.tensor([L - 1 for L in w.lens], dtype=torch.int32, device=DEV)
+    skv.scan4_build(cache, idx, pos, torch.tensor(w.lens, dtype=torch.int32, device=DEV),
+                    max(w.lens))
+    torch.cuda.synchronize()
+    for b in range(w.B):
+        scan4_check_index(idx, w, b)
