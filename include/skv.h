@@ -37,8 +37,8 @@
  *   - Supported in this version: head_dim D = 64, 128 or 256 for every call
  *     (each over the cache types it takes: append, bounds, selection,
  *     attention, combine and the step over f16, int8, q8_0, q4_0 and q5_0
- *     caches; sparse-V, per-query-head selection and query-token chunks over
- *     f16 and int8 caches; the 4-bit scan over f16 caches; the cpu-attn
+ *     caches, per-query-head selection and query-token chunks too; sparse-V
+ *     over f16 and int8 caches; the 4-bit scan over f16 caches; the cpu-attn
  *     kernel card, "Requirements and limits", admits any multiple of 16 up to
  *     1024);
  *     GQA group size
@@ -343,7 +343,8 @@ skv_status skv_select_union(const int32_t* sel_idx, const int32_t* sel_cnt, int3
  * own blocks' tokens (last block clipped at L_b).  Partial states as
  * skv_decode_attn (a part where a head has no block: m = -inf, l = 0, o = 0).
  *   uni_idx, uni_cnt, uni_mask, max_union : from skv_select_union.
- * Other arguments, workspace and errors as skv_decode_attn.
+ * Every cache type (f16, int8, q8_0, q4_0, q5_0).  Other arguments,
+ * workspace and errors as skv_decode_attn.
  */
 skv_status skv_decode_attn_heads(const skv_cache* c, const float* q, int32_t n_heads,
                                  const int32_t* seq_len, int32_t max_len,
@@ -429,8 +430,9 @@ skv_status skv_select_union_tokens(const int32_t* sel_idx, const int32_t* sel_cn
  * skv_workspace_bytes(batch, T * n_heads, head_dim, n_split) bytes, and
  * skv_combine(workspace, batch, T * n_heads, head_dim, n_split, out) gives
  * out float32 [batch][T][n_heads][head_dim].
+ * Every cache type (f16, int8, q8_0, q4_0, q5_0).
  * Errors: as skv_decode_attn; SKV_EUNSUPPORTED for T or T * G outside the
- * supported set, or a q8_0 / q4_0 cache.
+ * supported set.
  */
 skv_status skv_decode_attn_multi(const skv_cache* c, const float* q, int32_t n_tokens,
                                  int32_t n_heads, const int32_t* seq_len, int32_t max_len,

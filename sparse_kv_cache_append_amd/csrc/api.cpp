@@ -362,7 +362,6 @@ skv_status skv_decode_attn_heads(const skv_cache* c, const float* q, int32_t n_h
     return SKV_EINVAL;
   st = check_heads(c, n_heads);
   if (st != SKV_OK) return st;
-  if (skv::is_grouped(c->kv_dtype)) return SKV_EUNSUPPORTED;
   if (n_split < 1 || n_split > kMaxSplit) return SKV_EINVAL;
   if (!grid_fits(n_split, c->n_kv_heads, c->batch)) return SKV_ERANGE;
   if (!(softmax_scale == softmax_scale) || softmax_scale < 0.0f) return SKV_EINVAL;
@@ -383,7 +382,7 @@ skv_status skv_decode_attn_heads(const skv_cache* c, const float* q, int32_t n_h
   p.ws = static_cast<float*>(workspace);
   p.dbg_logits = nullptr;
   p.sel_hmask = uni_mask;
-  return device_status(skv::launch_decode(p, stream));
+  return device_status(decode_any(p, stream));
 }
 
 // ------------------------------------------------------- query-token chunks
@@ -458,7 +457,6 @@ skv_status skv_decode_attn_multi(const skv_cache* c, const float* q, int32_t n_t
   if (n_tokens < 1) return SKV_EINVAL;
   if (!supported_tokens(n_tokens) || (n_heads / c->n_kv_heads) * n_tokens > 16)
     return SKV_EUNSUPPORTED;
-  if (skv::is_grouped(c->kv_dtype)) return SKV_EUNSUPPORTED;
   if (n_split < 1 || n_split > kMaxSplit) return SKV_EINVAL;
   if (!grid_fits(n_split, c->n_kv_heads, c->batch)) return SKV_ERANGE;
   if (!(softmax_scale == softmax_scale) || softmax_scale < 0.0f) return SKV_EINVAL;
@@ -480,7 +478,7 @@ skv_status skv_decode_attn_multi(const skv_cache* c, const float* q, int32_t n_t
   p.dbg_logits = nullptr;
   p.sel_hmask = uni_mask;
   p.n_tok = n_tokens;
-  return device_status(skv::launch_decode(p, stream));
+  return device_status(decode_any(p, stream));
 }
 
 skv_status skv_scan4_build(const skv_cache* c, const int32_t* pos0, const int32_t* seq_len,

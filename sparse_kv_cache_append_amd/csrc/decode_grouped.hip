@@ -255,8 +255,11 @@ __device__ __forceinline__ half8_t widen_grp(int2_t w) {
 constexpr int kPwShiftGrp = 7;
 
 // SELR > 0: the block selection runs in the prologue (fused_walk), as in the
-// f16 and int8 attention kernels.
-template <int G, int K, int SELR, int D>
+// f16 and int8 attention kernels.  HM: per-query-head lists (a head mask per
+// list entry; the heads that did not choose a block leave it out).  The G
+// MFMA columns are ntok query tokens x G / ntok heads (QRows), each token
+// seeing the positions below its causal limit.
+template <int G, int K, int SELR, int D, bool HM = false>
 __global__ void __launch_bounds__(kMThreads, (GrpFmt<K, D>::kOcc))
 decode_grp_mfma(const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
                 const uint16_t* __restrict__ ksc, const uint16_t* __restrict__ vsc,
@@ -265,7 +268,7 @@ decode_grp_mfma(const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
                 int32_t max_sel, int32_t Hkv, int32_t max_seq, int32_t block, int32_t max_len,
                 int32_t n_split, int32_t n_rows, int32_t units_per_split, float qscale2,
                 float* __restrict__ ws_m, float* __restrict__ ws_l, float* __restrict__ ws_o,
-                FusedSelect fs) {
+                FusedSelect fs, const uint32_t* __restrict__ sel_hmask, int32_t ntok) {
   using F = GrpFmt<K, D>;
   constexpr bool Q5 = K == kQ5;
   constexpr int KG = F::kGroups;
@@ -288,18 +291,19 @@ decode_grp_mfma(const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
   const int lane = threadIdx.x % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lg = lane / 16, lc = lane % 16;
-  const int32_t H = Hkv * G;
+  const QRows qr = make_qrows<G>(ntok, Hkv);
   const int64_t bg = int64_t(b) * Hkv + g;
   const int32_t L_raw = seq_len[b];
   ListSeed ls{};
   if constexpr (SELR == 0)
-    ls = list_seed(sel_idx, sel_cnt, max_sel, bg, split, units_per_split);
-  // query as the B operand of the per-group q.K: column = head lc, k-chunk lg
-  // of group kk = channels 32 kk + 8 lg .. + 7; f16 high + low parts
+    ls = list_seed(sel_idx, sel_cnt, max_sel, bg, split, units_per_split,
+                   HM ? sel_hmask : nullptr);
+  // query as the B operand of the per-group q.K: column = query row lc,
+  // k-chunk lg of group kk = channels 32 kk + 8 lg .. + 7; f16 high + low parts
   half8_t qhi[KG], qlo[KG];
   {
     const bool hv = lc < G;
-    const float* qp = q + (int64_t(b) * H + g * G + (hv ? lc : 0)) * D;
+    const float* qp = q + qr.row(b, g, hv ? lc : 0) * D;
 #pragma unroll
     for (int kk = 0; kk < KG; ++kk) {
       const float4 a = *reinterpret_cast<const float4*>(qp + 32 * kk + 8 * lg);
@@ -320,6 +324,7 @@ decode_grp_mfma(const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
     tw = fused_walk<T, SELR>(fs, max_sel, bg, b, L, L_raw, block, split, units_per_split);
   else
     tw = make_walk<T>(ls, sel_idx, max_sel, bg, L, block, split, units_per_split);
+  if constexpr (HM) tw.hsel = sel_hmask + bg * max_sel;
   tw.init(wave);
   float m_run = -INFINITY, l_run = 0.0f;
   float4_t O[2 * KG];
@@ -344,12 +349,15 @@ decode_grp_mfma(const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
     uint32_t kh[kLoads], vh[kLoads];
     uint2 ks, vs;
     int32_t r0, nvalid;
+    uint32_t hm;
   };
   auto issue = [&](Frag& f) {
     int32_t r0 = 0, nv = 0;
-    if (tw.more()) tw.next<T>(r0, nv);
+    uint32_t hm = ~0u;
+    if (tw.more()) tw.next<T, HM>(r0, nv, &hm);
     f.r0 = r0;
     f.nvalid = nv;
+    f.hm = hm;
     const uint32_t lo = 16u * uint32_t(lane);
     const int bytes = __builtin_amdgcn_readfirstlane(max(nv, 0) * F::kRowBytes);
     const auto kr = tile_rsrc(kbase + int64_t(r0) * F::kRowBytes, bytes);
@@ -465,7 +473,8 @@ decode_grp_mfma(const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
       reinterpret_cast<floatS*>(stk)[lane] = ks4;
       reinterpret_cast<floatS*>(stv)[lane] = vs4;
     }
-    const int32_t nvalid = fr.nvalid;
+    const int32_t nvalid = fr.nvalid, r0 = fr.r0;
+    const uint32_t hm = fr.hm;
     issue(fr);
     // q.K per group: two 16-token halves, one MFMA pair per 32-channel group
     float sc[8];
@@ -504,10 +513,20 @@ decode_grp_mfma(const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
         }
       }
     }
-    if (nvalid < T) {
+    if (nvalid < T || (ntok > 1 && r0 + T > L - ntok + 1)) {   // wave-uniform
+      // rows past the row's length; with a chunk of query tokens, column lc
+      // is token lc >> gsh, which sees the positions below
+      // L - (ntok - 1 - token) only
+      const int32_t lim = min(nvalid, L - (ntok - 1 - (lc >> qr.gsh)) - r0);
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        sc[e] = 16 * (e / 4) + 4 * lg + e % 4 < nvalid ? sc[e] : -INFINITY;
+        sc[e] = 16 * (e / 4) + 4 * lg + e % 4 < lim ? sc[e] : -INFINITY;
+    }
+    if constexpr (HM) {
+      // the heads that did not choose this block leave it out
+      const bool off = ((hm >> lc) & 1u) == 0u;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sc[e] = off ? -INFINITY : sc[e];
     }
     tile_softmax<G, 2, true>(sc, m_run, l_run, O, unit);
     // P.V: per 16-channel block n (group n / 2), A = weight x V scale of
@@ -569,7 +588,7 @@ decode_grp_mfma(const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
     }
   }
   finish_mfma<G>(m_run, l_run, O, reinterpret_cast<float*>(&smem[0][0][0]), ws_m, ws_l, ws_o,
-                 make_qrows<G>(1, Hkv), b, g, n_split, split);
+                 qr, b, g, n_split, split);
 }
 
 }  // namespace
@@ -602,10 +621,11 @@ hipError_t launch_append_grouped_d(const skv_cache& c, const int32_t* pos0, int3
 template <int D>
 hipError_t launch_decode_grouped_d(const DecodeParams& p, int G, hipStream_t stream) {
   const skv_cache& c = *p.c;
-  const int32_t B = c.batch, H = p.n_heads, S = p.n_split;
-  float* ws_m = p.ws + ws_m_offset(B, H, S);
-  float* ws_l = p.ws + ws_l_offset(B, H, S);
-  float* ws_o = p.ws + ws_o_offset(B, H, S);
+  const int32_t B = c.batch, S = p.n_split, nt = p.n_tok;
+  const int32_t Hq = p.n_heads * nt;          // query rows: tokens x heads
+  float* ws_m = p.ws + ws_m_offset(B, Hq, S);
+  float* ws_l = p.ws + ws_l_offset(B, Hq, S);
+  float* ws_o = p.ws + ws_o_offset(B, Hq, S);
   int32_t ups;
   if (p.sel_idx != nullptr) {
     ups = (p.max_sel + S - 1) / S;
@@ -624,25 +644,38 @@ hipError_t launch_decode_grouped_d(const DecodeParams& p, int G, hipStream_t str
   const uint16_t* ks = reinterpret_cast<const uint16_t*>(c.k_scale);
   const uint16_t* vs = reinterpret_cast<const uint16_t*>(c.v_scale);
   const int fr = p.fused_r;
-#define SKV_GRP(GG, Q, SR)                                                                      \
-  decode_grp_mfma<GG, Q, SR, D><<<grid, kMThreads, 0, stream>>>(                               \
+  const bool hmk = p.sel_hmask != nullptr;
+#define SKV_GRP(GG, Q, SR, HMK)                                                                 \
+  decode_grp_mfma<GG, Q, SR, D, HMK><<<grid, kMThreads, 0, stream>>>(                          \
       kc, vc, ks, vs, p.q, p.seq_len, p.sel_idx, p.sel_cnt, p.max_sel, c.n_kv_heads,           \
-      c.max_seq, c.block, p.max_len, S, n_rows, ups, scale2, ws_m, ws_l, ws_o, p.fsel)
+      c.max_seq, c.block, p.max_len, S, n_rows, ups, scale2, ws_m, ws_l, ws_o, p.fsel,         \
+      p.sel_hmask, nt)
 #define SKV_GRP_Q(GG, Q)                           \
-  if (fr == 2) SKV_GRP(GG, Q, 2);                  \
-  else if (fr == 4) SKV_GRP(GG, Q, 4);             \
-  else if (fr > 0) SKV_GRP(GG, Q, kFusedSelR);     \
-  else SKV_GRP(GG, Q, 0)
+  if (hmk) SKV_GRP(GG, Q, 0, true);                \
+  else if (fr == 2) SKV_GRP(GG, Q, 2, false);      \
+  else if (fr == 4) SKV_GRP(GG, Q, 4, false);      \
+  else if (fr > 0) SKV_GRP(GG, Q, kFusedSelR, false); \
+  else SKV_GRP(GG, Q, 0, false)
 #define SKV_GRP_G(GG)                                          \
   if (c.kv_dtype == SKV_Q4_0) { SKV_GRP_Q(GG, kQ4); }            \
   else if (c.kv_dtype == SKV_Q5_0) { SKV_GRP_Q(GG, kQ5); }       \
   else { SKV_GRP_Q(GG, kQ8); }
+// 16 columns: query-token chunks only (no fused variants)
+#define SKV_GRP_Q16(Q)                                 \
+  if (hmk) SKV_GRP(16, Q, 0, true);                    \
+  else SKV_GRP(16, Q, 0, false)
   switch (G) {
     case 1: SKV_GRP_G(1); break;
     case 2: SKV_GRP_G(2); break;
     case 4: SKV_GRP_G(4); break;
-    default: SKV_GRP_G(8); break;
+    case 8: SKV_GRP_G(8); break;
+    default:
+      if (c.kv_dtype == SKV_Q4_0) { SKV_GRP_Q16(kQ4); }
+      else if (c.kv_dtype == SKV_Q5_0) { SKV_GRP_Q16(kQ5); }
+      else { SKV_GRP_Q16(kQ8); }
+      break;
   }
+#undef SKV_GRP_Q16
 #undef SKV_GRP_G
 #undef SKV_GRP_Q
 #undef SKV_GRP
@@ -663,10 +696,15 @@ hipError_t launch_append_grouped(const skv_cache& c, const int32_t* pos0, int32_
 
 hipError_t launch_decode_grouped(const DecodeParams& p, hipStream_t stream) {
   const skv_cache& c = *p.c;
-  const int G = p.n_heads / c.n_kv_heads;
-  if (G != 1 && G != 2 && G != 4 && G != 8) return hipErrorInvalidValue;
-  if (p.app.k_new != nullptr || p.sel_hmask != nullptr || p.dbg_logits != nullptr ||
-      p.n_tok != 1)
+  if (c.block % 16 != 0) return hipErrorInvalidValue;
+  // MFMA columns per KV head: n_tok query tokens x the group's heads
+  const int32_t nt = p.n_tok;
+  if (nt != 1 && nt != 2 && nt != 4 && nt != 8) return hipErrorInvalidValue;
+  const int G = (p.n_heads / c.n_kv_heads) * nt;
+  if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16) return hipErrorInvalidValue;
+  if (p.app.k_new != nullptr || p.dbg_logits != nullptr) return hipErrorInvalidValue;
+  if (nt > 1 && p.fused_r > 0) return hipErrorInvalidValue;
+  if (p.sel_hmask != nullptr && (p.sel_idx == nullptr || p.fused_r > 0))
     return hipErrorInvalidValue;
   switch (c.head_dim) {
     case 64: return launch_decode_grouped_d<64>(p, G, stream);

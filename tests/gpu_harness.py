@@ -162,6 +162,16 @@ def sel_tensor_from_lists(lists, B, Hkv, max_sel):
     return torch.from_numpy(idx).to(DEV), torch.from_numpy(cnt).to(DEV)
 
 
+def grouped_host(w, b):
+    """Oracle group-wise quantization of sequence b's float32 rows (codes,
+    f16 scales) for a q8_0 / q4_0 / q5_0 workload."""
+    import oracle
+    qmax = {"q8_0": oracle.QMAX_Q8, "q4_0": oracle.QMAX_Q4, "q5_0": oracle.QMAX_Q5}[w.kv_dtype]
+    kc, ks = oracle.quantize_groups(w.k[b], qmax)
+    vc, vs = oracle.quantize_groups(w.v[b], qmax)
+    return kc, ks, vc, vs
+
+
 def quantized_host(w, b):
     """Oracle quantization of sequence b's float32 rows (codes, scales)."""
     import oracle

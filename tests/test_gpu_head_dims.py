@@ -310,7 +310,8 @@ def test_decode_attn_select_equals_select_then_decode(gpu_lib, D, kv):
 
 @pytest.mark.parametrize("D", DIMS)
 @pytest.mark.parametrize("seeds,H,Hkv,lens,kv,ksel", [([861, 862], 32, 8, [5000, 777], "f16", [20, 4]),
-                                                      ([863], 16, 4, [4100], "i8", [12])])
+                                                      ([863], 16, 4, [4100], "i8", [12]),
+                                                      ([864], 32, 8, [3000], "q4_0", [10])])
 def test_per_head_selection(gpu_lib, D, seeds, H, Hkv, lens, kv, ksel):
     """Per-query-head bounds, selection, union and attention at these head
     dims (bit-equal group scores, exact selections and unions, outputs
@@ -326,7 +327,8 @@ def test_per_head_selection(gpu_lib, D, seeds, H, Hkv, lens, kv, ksel):
 @pytest.mark.parametrize("D", DIMS)
 @pytest.mark.parametrize("seeds,H,Hkv,lens,kv,T", [([871, 872], 32, 8, [700, 1537], "f16", 4),
                                                    ([873], 32, 4, [2049], "i8", 2),
-                                                   ([874], 8, 8, [1000], "i8", 8)])
+                                                   ([874], 8, 8, [1000], "i8", 8),
+                                                   ([875], 32, 8, [900], "q8_0", 4)])
 def test_dense_chunk(gpu_lib, D, seeds, H, Hkv, lens, kv, T):
     """A chunk of T query tokens (T x G MFMA columns, up to 16), dense."""
     _print("dense chunk", D, lens, kv, T)
@@ -339,7 +341,8 @@ def test_dense_chunk(gpu_lib, D, seeds, H, Hkv, lens, kv, T):
 
 @pytest.mark.parametrize("D", DIMS)
 @pytest.mark.parametrize("seeds,H,Hkv,lens,kv,T,ksel", [([881, 882], 32, 8, [5000, 1800], "f16", 4, [12, 5]),
-                                                        ([883], 32, 4, [6001], "i8", 2, [20])])
+                                                        ([883], 32, 4, [6001], "i8", 2, [20]),
+                                                        ([884], 16, 8, [2500], "q5_0", 4, [9])])
 def test_quest_chunk(gpu_lib, D, seeds, H, Hkv, lens, kv, T, ksel):
     """A chunk of T query tokens, each with its own Quest set."""
     _print("quest chunk", D, lens, kv, T)

@@ -4,7 +4,8 @@ skv_combine) against the oracle (oracle/multi_token.py): each token's bounds
 within float32 rounding of the exact-sum bounds over its own blocks, its
 selection bit-exact on the GPU's own scores and equal to the float64 one up
 to reported near-ties, the union and its token masks bit-exact, every output
-element-wise against the token's own causal (dense or Quest) attention; a
+element-wise against the token's own causal (dense or Quest) attention (f16
+and group-wise caches within 1e-3, int8 within 1e-4 of the method); a
 one-token chunk is bit-identical to skv_decode_attn."""
 import numpy as np
 import pytest
@@ -13,7 +14,7 @@ import torch
 import oracle
 import sparse_kv_cache_append_amd as skv
 import workloads
-from gpu_harness import DEV, assert_close, build_cache, quantized_host, rel_err
+from gpu_harness import DEV, assert_close, build_cache, grouped_host, quantized_host, rel_err
 from oracle import multi_token as mt
 
 pytestmark = pytest.mark.gpu
@@ -63,11 +64,17 @@ def run_chunk(cache, w, qc, quest, S=None):
 
 
 def check_dense(w, qc, r, seqs=None, heads=None):
-    tol = 1e-3 if w.kv_dtype == "f16" else 1e-4
+    tol = 1e-4 if w.kv_dtype == "i8" else 1e-3
     for b in (range(w.B) if seqs is None else seqs):
         L = w.lens[b]
         if w.kv_dtype == "f16":
             ref = mt.attend_f16_multi(qc[b], w.k[b], w.v[b], w.softmax_scale, L)
+        elif w.kv_dtype != "i8":
+            kc, ks, vc, vs = grouped_host(w, b)
+            ref = np.stack([oracle.attend_grouped(qc[b, t], kc[:, :Lt], ks[:, :Lt], vc[:, :Lt],
+                                                  vs[:, :Lt], w.softmax_scale)
+                            if Lt > 0 else np.zeros((qc.shape[2], w.D))
+                            for t, Lt in enumerate(mt.token_lengths(L, qc.shape[1]))])
         else:
             kc, ks, vc, vs = quantized_host(w, b)
             ref = mt.attend_i8_multi(qc[b], kc, ks, vc, vs, w.softmax_scale, L)
@@ -90,7 +97,7 @@ def check_dense(w, qc, r, seqs=None, heads=None):
 
 
 def check_quest(w, qc, r, seqs=None):
-    tol = 1e-3 if w.kv_dtype == "f16" else 1e-4
+    tol = 1e-4 if w.kv_dtype == "i8" else 1e-3
     T, G = qc.shape[1], w.G
     near = 0
     for b in (range(w.B) if seqs is None else seqs):
@@ -101,6 +108,8 @@ def check_quest(w, qc, r, seqs=None):
                                         w.n_recent)
         if w.kv_dtype == "i8":
             kc, ks, vc, vs = quantized_host(w, b)
+        elif w.kv_dtype != "f16":
+            kc, ks, vc, vs = grouped_host(w, b)
         for g in range(w.Hkv):
             sets = []
             for t in range(T):
@@ -133,13 +142,16 @@ def check_quest(w, qc, r, seqs=None):
                     assert np.all(got == 0)
                     continue
                 toks = oracle.selected_tokens(sets[t], int(lens[t]), w.block)
+                sl = slice(g, g + 1)
                 if w.kv_dtype == "f16":
                     ref = oracle.attend_f16(qc[b, t, hs], w.k[b][g:g + 1], w.v[b][g:g + 1],
                                             w.softmax_scale, tokens=toks)
-                else:
-                    sl = slice(g, g + 1)
+                elif w.kv_dtype == "i8":
                     ref = oracle.attend_i8(qc[b, t, hs], kc[sl], ks[sl], vc[sl], vs[sl],
                                            w.softmax_scale, tokens=toks)
+                else:
+                    ref = oracle.attend_grouped(qc[b, t, hs], kc[sl], ks[sl], vc[sl], vs[sl],
+                                                w.softmax_scale, tokens=toks)
                 assert_close(got, ref, tol, b, g, t)
     return near
 
@@ -152,6 +164,9 @@ DENSE = [
     ([906], 8, 8, [1000], "i8", 8, 64),                   # G 1
     ([907, 908], 32, 8, [3, 1200], "f16", 4, 64),         # tokens before the first position
     ([909], 16, 8, [513], "i8", 4, 32),                   # 8 columns
+    ([921], 32, 8, [700], "q4_0", 4, 64),                 # group-wise caches: 16 columns
+    ([922, 923], 16, 8, [1537, 40], "q8_0", 2, 64),       # 4 columns
+    ([924], 8, 8, [513], "q5_0", 8, 32),                  # 8 columns, G 1
 ]
 
 
@@ -175,6 +190,9 @@ QUEST = [
     ([914], 16, 8, [1300], "f16", 8, [10], 1, 2, 16),
     ([915, 916], 8, 8, [2200, 5], "i8", 4, [6, 3], 1, 1, 64),
     ([917], 32, 8, [64 * 20 + 2], "f16", 4, [4], 0, 2, 64),   # the chunk crosses a block edge
+    ([925], 32, 8, [5000], "q8_0", 4, [12], 1, 2, 64),        # group-wise caches
+    ([926], 32, 4, [3001], "q5_0", 2, [10], 1, 4, 64),
+    ([927], 16, 8, [1300], "q4_0", 8, [10], 1, 2, 16),
 ]
 
 
