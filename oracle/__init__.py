@@ -47,4 +47,4 @@ from .attention import (attend_f16, attend_i8, attend_i8_dequant, attend_grouped
                         int8_logit_dots, combine_partials, softmax_partials)
 from .quest import (block_bounds, upper_bounds, group_scores, select_blocks,  # noqa: F401
                     selected_tokens)
-from .sparse_v import attend_f16_sparse_v, attend_i8_sparse_v  # noqa: F401
+from .sparse_v import attend_f16_sparse_v, attend_grouped_sparse_v, attend_i8_sparse_v  # noqa: F401

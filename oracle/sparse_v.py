@@ -32,6 +32,7 @@ from __future__ import annotations
 import numpy as np
 
 from .attention import _softmax_weights, int8_logit_dots
+from .quant import dequantize_groups
 
 NEAR_REL = 1e-4
 
@@ -116,3 +117,16 @@ def attend_i8_sparse_v(q, k_codes, k_scale, v_codes, v_scale, scale, tau=0.0, ep
             out[h], keeps[h], nears[h], _ = _sparse_v_rows(
                 s, vd, tau, eps, None if keep is None else keep[h])
     return out, keeps, nears
+
+
+def attend_grouped_sparse_v(q, k_codes, k_scales, v_codes, v_scales, scale, tau=0.0, eps=0.0,
+                            tokens=None, keep=None):
+    """Sparse-V over a group-wise quantized cache (q8_0 / q4_0 / q5_0): the
+    rule above on the dequantized keys and values scale * code (exact in
+    float64), the query unquantized -- the group-wise attention's definition
+    (attention.attend_grouped) with the value rows of negligible weight left
+    out.  codes [Hkv][L][D] int8, scales [Hkv][L][D / 32] float16.  Same
+    returns as attend_f16_sparse_v."""
+    return attend_f16_sparse_v(q, dequantize_groups(k_codes, k_scales),
+                               dequantize_groups(v_codes, v_scales), scale, tau, eps, tokens,
+                               keep)

@@ -57,6 +57,34 @@ def test_zero_threshold_is_the_dense_result_bit_for_bit():
     assert np.array_equal(out, oracle.attend_i8(q, kc, ks, vc, vs, 0.1))
 
 
+@pytest.mark.parametrize("qmax", [oracle.QMAX_Q8, oracle.QMAX_Q4, oracle.QMAX_Q5])
+def test_grouped_caches(qmax):
+    """Group-wise caches: the brute force on the values scale * code, and a
+    zero threshold equal to the dense group-wise oracle bit for bit."""
+    rng = np.random.default_rng(qmax)
+    H, Hkv, L, D = 4, 2, 40, 64
+    q = (2.0 * rng.standard_normal((H, D))).astype(np.float32)
+    kc, ks = oracle.quantize_groups(rng.standard_normal((Hkv, L, D)).astype(np.float32), qmax)
+    vc, vs = oracle.quantize_groups(rng.standard_normal((Hkv, L, D)).astype(np.float32), qmax)
+    G = H // Hkv
+    for tau, eps in ((0.02, 0.0), (0.0, 0.5)):
+        out, keep, _ = oracle.attend_grouped_sparse_v(q, kc, ks, vc, vs, 0.25, tau=tau, eps=eps)
+        assert not keep.all()
+        for h in range(H):
+            g = h // G
+            kd = [[float(ks[g, t, d // 32]) * int(kc[g, t, d]) for d in range(D)]
+                  for t in range(L)]
+            vd = [[float(vs[g, t, d // 32]) * int(vc[g, t, d]) for d in range(D)]
+                  for t in range(L)]
+            np.testing.assert_allclose(out[h], brute(q[h], kd, vd, 0.25, tau, eps),
+                                       rtol=1e-12, atol=1e-14)
+    toks = np.array([0, 3, 4, 39])
+    for t in (None, toks):
+        out, keep, _ = oracle.attend_grouped_sparse_v(q, kc, ks, vc, vs, 0.1, tokens=t)
+        assert keep.all()
+        assert np.array_equal(out, oracle.attend_grouped(q, kc, ks, vc, vs, 0.1, tokens=t))
+
+
 def test_two_tokens_closed_form():
     """Logits ln 9 and 0: weights 0.9 and 0.1.  tau 0.2 keeps only the first
     token, and the normalizer still counts both: out = 0.9 v0 (not v0)."""
