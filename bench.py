@@ -552,7 +552,6 @@ def measure(w, args, quest: bool, dense: bool, detail: bool = False):
             res["quest"]["warm_us_per_step"] = round(warm, 3)
         if detail:
             res["_roofline"] = (dec_bytes, sel_us, dec_us)
-        grouped = w.kv_dtype in ("q8_0", "q4_0", "q5_0")   # sparse-V: f16, int8
         if not args.no_per_head:
             res["quest_per_head"] = measure_per_head(T, skv, torch, w, caches, R, q, seq_len, Lmax,
                                                      new_k, new_v, pos_last, ks, res["quest"])
@@ -563,7 +562,7 @@ def measure(w, args, quest: bool, dense: bool, detail: bool = False):
         if n_chunk > 1:
             res["chunk"] = measure_chunk(T, skv, torch, w, caches, R, seq_len, Lmax, n_chunk,
                                          res.get("dense"), res["quest"])
-        if args.sparse_v_tau > 0 and not grouped:
+        if args.sparse_v_tau > 0:
             res["quest_sparse_v"] = measure_sparse_v(
                 T, skv, torch, w, caches, R, q, seq_len, Lmax, new_k, new_v, pos_last, ks, score,
                 sel, cnt, attended, args.sparse_v_tau, calls_us)

@@ -37,8 +37,8 @@
  *   - Supported in this version: head_dim D = 64, 128 or 256 for every call
  *     (each over the cache types it takes: append, bounds, selection,
  *     attention, combine and the step over f16, int8, q8_0, q4_0 and q5_0
- *     caches, per-query-head selection and query-token chunks too; sparse-V
- *     over f16 and int8 caches; the 4-bit scan over f16 caches; the cpu-attn
+ *     caches, per-query-head selection, query-token chunks and sparse-V
+ *     too; the 4-bit scan over f16 caches; the cpu-attn
  *     kernel card, "Requirements and limits", admits any multiple of 16 up to
  *     1024);
  *     GQA group size
@@ -517,7 +517,10 @@ skv_status skv_scan4_candidates(const skv_cache* c, const uint8_t* codes4, const
  *     out = sum over used t of p_t v_t.
  * tau = eps = 0 uses every row (the dense or Quest result).  The weights and
  * the decision are float32 (a token within about 1e-5 relative of theta may
- * fall either way).  Value rows no head of the group uses are not read.
+ * fall either way).  Value rows no head of the group uses are not read (for
+ * a group-wise cache neither their codes nor their scales).  Every cache
+ * type (f16, int8, q8_0, q4_0, q5_0); the "All-KV-types composition"
+ * section of the same page composes the levers with every cache type.
  * Two launches (the q.K pass, then the value pass over the kept rows); the
  * workspace then holds the standard partial states at its start, so
  *     skv_combine(workspace, batch, n_heads, head_dim, n_split, out)

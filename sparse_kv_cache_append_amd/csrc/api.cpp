@@ -574,7 +574,6 @@ skv_status skv_decode_attn_sparse_v(const skv_cache* c, const float* q, int32_t 
                                                    c->head_dim, n_split, max_len);
   if (workspace == nullptr || workspace_bytes < need) return SKV_EWORKSPACE;
   if (!aligned(workspace)) return SKV_EINVAL;
-  if (skv::is_grouped(c->kv_dtype)) return SKV_EUNSUPPORTED;
   skv::SparseVParams p;
   p.c = c;
   p.q = q;

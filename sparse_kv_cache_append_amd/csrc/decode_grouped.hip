@@ -43,39 +43,12 @@
 #include "decode_core.h"
 #include "device_common.h"
 #include "fused_walk.h"
+#include "grouped_core.h"
 #include "launch.h"
 
 namespace skv {
 namespace {
 
-constexpr int kGroup = 32;
-
-enum GrpKind { kQ8 = 0, kQ4 = 1, kQ5 = 2 };
-// Format K at head dim D (64, 128 or 256: D / 32 groups per row).
-template <int K, int D = kD>
-struct GrpFmt {
-  static_assert(D == 64 || D == 128 || D == 256, "head dims 64, 128, 256");
-  static constexpr bool kNib = K != kQ8;                   // nibble plane (q4_0, q5_0)
-  static constexpr int kQmax = K == kQ8 ? 127 : K == kQ4 ? 7 : 15;
-  static constexpr int kBias = K == kQ8 ? 0 : kQmax + 1;   // stored = code + bias
-  static constexpr int kGroups = D / kGroup;               // 32-channel groups per row
-  static constexpr int kRowBytes = kNib ? D / 2 : D;       // code / nibble row bytes
-  static constexpr int kHiBytes = K == kQ5 ? D / 8 : 0;    // fifth-bit row bytes
-  static constexpr int kTokBytes = kRowBytes + kHiBytes;   // per (token, KV head)
-  static constexpr int kOcc = D > 128 ? 1 : 2;             // workgroups per CU (decode)
-};
-// Byte offsets of token t of row bg (sequence x KV head): its code (or
-// nibble) row and, for q5_0, its fifth-bit row.
-template <int K, int D = kD>
-__device__ __forceinline__ int64_t grp_row_off(int64_t bg, int32_t max_seq, int64_t t) {
-  using F = GrpFmt<K, D>;
-  return bg * max_seq * F::kTokBytes + t * F::kRowBytes;
-}
-template <int K, int D = kD>
-__device__ __forceinline__ int64_t grp_hi_off(int64_t bg, int32_t max_seq, int64_t t) {
-  using F = GrpFmt<K, D>;
-  return bg * max_seq * F::kTokBytes + int64_t(max_seq) * F::kRowBytes + t * F::kHiBytes;
-}
 // The fifth bits of 32 channels as a 32-bit word (bit i = channel i) from the
 // two ballots of a row (lane l: h0 bit l = channel 2l, h1 bit l = channel
 // 2l + 1), for lanes l < 4 (channels 32 l .. 32 l + 31).
@@ -183,75 +156,6 @@ append_grp_kernel(uint8_t* __restrict__ kc, uint8_t* __restrict__ vc,
 }
 
 // ------------------------------------------------------------------ decode
-// 32 nibble codes (16 bytes: byte i = channels 2i, 2i + 1, each code + 8) to
-// 32 bytes in channel order, still biased (code + 8, 0..15): the bias comes
-// off in the widening to f16 (widen_q4), in the same packed subtraction.
-__device__ __forceinline__ void unpack_q4(const int4_t& w, int4_t& c0, int4_t& c1) {
-  uint32_t o[8];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t x = uint32_t(w[i]);
-    const uint32_t lo = x & 0x0F0F0F0Fu, hi = (x >> 4) & 0x0F0F0F0Fu;
-    // (lo0, hi0, lo1, hi1) and (lo2, hi2, lo3, hi3)
-    o[2 * i] = __builtin_amdgcn_perm(hi, lo, 0x05010400u);
-    o[2 * i + 1] = __builtin_amdgcn_perm(hi, lo, 0x07030602u);
-  }
-  c0 = int4_t{int(o[0]), int(o[1]), int(o[2]), int(o[3])};
-  c1 = int4_t{int(o[4]), int(o[5]), int(o[6]), int(o[7])};
-}
-
-// q5_0: the nibbles as for q4_0, plus each channel's fifth bit (hi: bit i =
-// channel i of the 32) as bit 4 of its byte: code + 16, 0..31.  The fifth bits
-// of 4 channels go to bit 0 of 4 bytes by one 24-bit multiply: bit m of n
-// (m < 4) lands at bit 8 m of n * 0x204081 (shifts 0, 7, 14, 21; no two
-// products share a bit, so nothing carries).
-__device__ __forceinline__ uint32_t spread4(uint32_t n) {
-  return (n * 0x204081u) & 0x01010101u;
-}
-__device__ __forceinline__ void unpack_q5(const int4_t& w, uint32_t hi, int4_t& c0, int4_t& c1) {
-  uint32_t o[8];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t x = uint32_t(w[i]);
-    const uint32_t lo = x & 0x0F0F0F0Fu, hn = (x >> 4) & 0x0F0F0F0Fu;
-    const uint32_t hb = hi >> (8 * i);                    // channels 8 i .. 8 i + 7
-    o[2 * i] = __builtin_amdgcn_perm(hn, lo, 0x05010400u) | (spread4(hb & 15u) << 4);
-    o[2 * i + 1] = __builtin_amdgcn_perm(hn, lo, 0x07030602u) | (spread4((hb >> 4) & 15u) << 4);
-  }
-  c0 = int4_t{int(o[0]), int(o[1]), int(o[2]), int(o[3])};
-  c1 = int4_t{int(o[4]), int(o[5]), int(o[6]), int(o[7])};
-}
-
-// 8 biased bytes n = code + BIAS (q4_0: 8, q5_0: 16) to the f16 codes,
-// exactly: each byte goes under a 0x64 high byte (f16 1024 + n), minus
-// 1024 + BIAS.
-template <int BIAS>
-__device__ __forceinline__ half8_t widen_biased(int2_t w) {
-  typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
-  constexpr uint32_t kLoSel = 0x04010400u;   // (0x64, x1, 0x64, x0)
-  constexpr uint32_t kHiSel = 0x04030402u;   // (0x64, x3, 0x64, x2)
-  const half2_t off = half2_t{(_Float16)(1024.0f + BIAS), (_Float16)(1024.0f + BIAS)};
-  half8_t r;
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const uint32_t x = uint32_t(w[k]);
-    const half2_t a = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0x64646464u, x, kLoSel)) - off;
-    const half2_t b = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0x64646464u, x, kHiSel)) - off;
-    r[4 * k + 0] = a[0];
-    r[4 * k + 1] = a[1];
-    r[4 * k + 2] = b[0];
-    r[4 * k + 3] = b[1];
-  }
-  return r;
-}
-
-// The LDS codes of a tile as f16: q4_0 / q5_0 biased bytes or q8_0 int8 codes.
-template <int K>
-__device__ __forceinline__ half8_t widen_grp(int2_t w) {
-  if constexpr (GrpFmt<K>::kNib) return widen_biased<GrpFmt<K>::kBias>(w);
-  else return widen_codes(w);
-}
-
 constexpr int kPwShiftGrp = 7;
 
 // SELR > 0: the block selection runs in the prologue (fused_walk), as in the

@@ -35,6 +35,7 @@
 
 #include "decode_core.h"
 #include "device_common.h"
+#include "grouped_core.h"
 #include "launch.h"
 
 namespace skv {
@@ -843,6 +844,409 @@ sv_values_i8(const int8_t* __restrict__ vc, const float* __restrict__ vsc,
                    sv.ws_m, sv.ws_l, sv.ws_o, int64_t(b) * H + g * G, n_split, split);
 }
 
+// ============================================================== group-wise
+// q8_0 / q4_0 / q5_0 caches: the group-wise attention kernel's tiles (32
+// tokens, codes staged in LDS as one byte per channel, per-(token, group) f16
+// scales as float), split into the two passes.  Pass A: q.K per 32-channel
+// group on the matrix cores (the codes widened to f16 exactly as A, the
+// query as f16 high + low parts as B), each group's dot weighted by its
+// scale in float32.  Pass B: the kept rows' V codes, fifth bits and scales
+// only, P.V per 16-channel block with the weight times the (token, group) V
+// scale in a running power-of-two unit as f16 high + low parts.
+template <int G, int K, int D>
+__global__ void __launch_bounds__(kMThreads, (GrpFmt<K, D>::kOcc))
+sv_logits_grp(const uint8_t* __restrict__ kc, const uint16_t* __restrict__ ksc,
+              const float* __restrict__ q, const int32_t* __restrict__ seq_len,
+              const int32_t* __restrict__ sel_idx, const int32_t* __restrict__ sel_cnt,
+              int32_t max_sel, int32_t Hkv, int32_t max_seq, int32_t block, int32_t max_len,
+              int32_t n_split, int32_t n_rows, int32_t ups, float qscale2, SvArgs sv) {
+  using F = GrpFmt<K, D>;
+  constexpr bool Q5 = K == kQ5;
+  constexpr int KG = F::kGroups;
+  constexpr int T = 32;
+  constexpr int kCpr = D / 16;                              // LDS chunks per code row
+  constexpr int kCodeBytes = T * D;
+  constexpr int kBufBytes = kCodeBytes + T * KG * 4;        // codes, K scales [T][KG]
+  constexpr int kTileBytes = T * F::kRowBytes;
+  constexpr int kLoads = kTileBytes / 1024;
+  constexpr int kHcpr = F::kRowBytes / 16;
+  constexpr int kHrpl = 1024 / F::kRowBytes;
+  constexpr int kSwz = kCpr < 16 ? kCpr : 16;
+  constexpr int SPL = KG / 2;
+  typedef float floatS __attribute__((ext_vector_type(SPL)));
+  const int32_t lstride = sv.lstride;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kMWaves][2][kBufBytes];
+  const uint32_t slot = xcd_slot(blockIdx.x, gridDim.x);
+  const int32_t split = int32_t(slot % uint32_t(n_split));
+  const uint32_t row = xcd_row(slot / uint32_t(n_split), uint32_t(n_rows));
+  const int32_t g = int32_t(row % uint32_t(Hkv)), b = int32_t(row / uint32_t(Hkv));
+  const int lane = threadIdx.x % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int lg = lane / 16, lc = lane % 16;
+  const int32_t H = Hkv * G;
+  const int64_t bg = int64_t(b) * Hkv + g;
+  const int32_t L_raw = seq_len[b];
+  const ListSeed ls = list_seed(sel_idx, sel_cnt, max_sel, bg, split, ups);
+  const bool hv = lc < G;
+  half8_t qhi[KG], qlo[KG];
+  {
+    const float* qp = q + (int64_t(b) * H + g * G + (hv ? lc : 0)) * D;
+#pragma unroll
+    for (int kk = 0; kk < KG; ++kk) {
+      const float4 a = *reinterpret_cast<const float4*>(qp + 32 * kk + 8 * lg);
+      const float4 c = *reinterpret_cast<const float4*>(qp + 32 * kk + 8 * lg + 4);
+      const float x[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float v = hv ? x[e] * qscale2 : 0.0f;
+        const _Float16 h = (_Float16)v;
+        qhi[kk][e] = h;
+        qlo[kk][e] = (_Float16)(v - (float)h);
+      }
+    }
+  }
+  const int32_t L = __builtin_amdgcn_readfirstlane(min(max(L_raw, 0), max_len));
+  TileWalk tw = make_walk<T>(ls, sel_idx, max_sel, bg, L, block, split, ups);
+  tw.init(wave);
+  TileStats ts;
+  const uint8_t* kbase = kc + grp_row_off<K, D>(bg, max_seq, 0);
+  const uint8_t* khbase = kc + grp_hi_off<K, D>(bg, max_seq, 0);
+  const uint8_t* ksb = reinterpret_cast<const uint8_t*>(ksc + bg * int64_t(max_seq) * KG);
+  float* lrow = sv.logit + (int64_t(b) * H + g * G + (hv ? lc : 0)) * int64_t(lstride);
+  // lane loads as in the group-wise attention kernel: 16-byte chunk
+  // lane % kHcpr of row kHrpl i + lane / kHcpr; q5_0 also the fifth bits of
+  // those 32 channels; the KG / 2 scales of groups (lane % 2) KG / 2 .. of
+  // token lane / 2
+  struct Frag {
+    int4_t k[kLoads];
+    uint32_t kh[kLoads];
+    uint2 ks;
+    int32_t r0, nvalid;
+  };
+  auto issue = [&](Frag& f) {
+    int32_t r0 = 0, nv = 0;
+    if (tw.more()) tw.next<T>(r0, nv);
+    f.r0 = r0;
+    f.nvalid = nv;
+    const uint32_t lo = 16u * uint32_t(lane);
+    const int bytes = __builtin_amdgcn_readfirstlane(max(nv, 0) * F::kRowBytes);
+    const auto kr = tile_rsrc(kbase + int64_t(r0) * F::kRowBytes, bytes);
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) f.k[i] = tile_load(kr, lo + 1024 * i);
+    if constexpr (Q5) {
+      const int hbytes = __builtin_amdgcn_readfirstlane(max(nv, 0) * F::kHiBytes);
+      const auto khr = tile_rsrc(khbase + int64_t(r0) * F::kHiBytes, hbytes);
+#pragma unroll
+      for (int i = 0; i < kLoads; ++i)
+        f.kh[i] = __builtin_amdgcn_raw_buffer_load_b32(khr, 256u * i + 4u * uint32_t(lane), 0,
+                                                        kAuxNontemporal);
+    }
+    const int sbytes = __builtin_amdgcn_readfirstlane(max(nv, 0) * KG * 2);
+    const auto ksr = tile_rsrc(ksb + int64_t(r0) * KG * 2, sbytes);
+    f.ks = grp_scale_load<KG>(ksr, uint32_t(KG) * uint32_t(lane));
+  };
+  auto sw = [](int rw, int chunk) { return rw * D + 16 * (chunk ^ (rw & (kSwz - 1))); };
+  auto process = [&](auto bufc, Frag& fr) {
+    constexpr int kBuf = decltype(bufc)::value;
+    uint8_t* kt = smem[wave][kBuf];
+    float* stk = reinterpret_cast<float*>(kt + kCodeBytes);          // [T][KG]
+    grp_stage<K, D>(kt, fr.k, fr.kh);
+    {
+      floatS ks4;
+#pragma unroll
+      for (int j = 0; j < SPL; ++j) {
+        const uint32_t kw = j < 2 ? fr.ks.x : fr.ks.y;
+        ks4[j] = (j & 1) ? h2f_hi(kw) : h2f_lo(kw);
+      }
+      reinterpret_cast<floatS*>(stk)[lane] = ks4;
+    }
+    const int32_t nvalid = fr.nvalid, r0 = fr.r0;
+    issue(fr);
+    float sc[8];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      float4_t acc[KG];
+#pragma unroll
+      for (int kk = 0; kk < KG; ++kk) {
+        const int rw = 16 * s + lc;
+        const int2_t raw = *reinterpret_cast<const int2_t*>(kt + sw(rw, 2 * kk + lg / 2) +
+                                                            8 * (lg & 1));
+        const half8_t a = widen_grp<K>(raw);
+        acc[kk] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        acc[kk] = mfma_f16_32(a, qhi[kk], acc[kk]);
+        acc[kk] = mfma_f16_32(a, qlo[kk], acc[kk]);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float* kr = stk + (16 * s + 4 * lg + r) * KG;
+        float a = acc[0][r] * kr[0];
+#pragma unroll
+        for (int kk = 1; kk < KG; ++kk) a += acc[kk][r] * kr[kk];
+        sc[4 * s + r] = a;
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      sc[e] = 16 * (e / 4) + 4 * lg + e % 4 < nvalid ? sc[e] : -INFINITY;
+    ts.add<2>(sc, nvalid);
+    if (hv && nvalid > 0) {
+      if (nvalid == T) {
+        *reinterpret_cast<float4*>(lrow + r0 + 4 * lg) = make_float4(sc[0], sc[1], sc[2], sc[3]);
+        *reinterpret_cast<float4*>(lrow + r0 + 16 + 4 * lg) =
+            make_float4(sc[4], sc[5], sc[6], sc[7]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int t = 16 * (e / 4) + 4 * lg + e % 4;
+          if (t < nvalid) lrow[r0 + t] = sc[e];
+        }
+      }
+    }
+  };
+  Frag f0, f1;
+  const int32_t n_mine = tw.count();
+  issue(f0);
+  issue(f1);
+  for (int32_t t = 0; t + 1 < n_mine; t += 2) {
+    process(std::integral_constant<int, 0>{}, f0);
+    process(std::integral_constant<int, 1>{}, f1);
+  }
+  if (n_mine & 1) process(std::integral_constant<int, 0>{}, f0);
+  finish_stats<G>(ts, reinterpret_cast<float*>(&smem[0][0][0]), sv.stat_m, sv.stat_l, sv.stat_n,
+                  int64_t(b) * H + g * G, bg, n_split, split);
+}
+
+constexpr int kPwShiftSvGrp = 14;
+
+template <int G, int K, int D>
+__global__ void __launch_bounds__(kMThreads, (GrpFmt<K, D>::kOcc))
+sv_values_grp(const uint8_t* __restrict__ vc, const uint16_t* __restrict__ vsc,
+              const int32_t* __restrict__ seq_len, const int32_t* __restrict__ sel_idx,
+              const int32_t* __restrict__ sel_cnt, int32_t max_sel, int32_t Hkv,
+              int32_t max_seq, int32_t block, int32_t max_len, int32_t n_split, int32_t n_rows,
+              int32_t ups, int32_t keep_words, SvArgs sv) {
+  using F = GrpFmt<K, D>;
+  constexpr bool Q5 = K == kQ5;
+  constexpr int KG = F::kGroups;
+  constexpr int T = 32;
+  constexpr int kCpr = D / 16;
+  constexpr int kCodeBytes = T * D;
+  constexpr int kBufBytes = kCodeBytes + T * KG * 4;        // codes, V scales [T][KG]
+  constexpr int kTileBytes = T * F::kRowBytes;
+  constexpr int kLoads = kTileBytes / 1024;
+  constexpr int kHcpr = F::kRowBytes / 16;
+  constexpr int kHrpl = 1024 / F::kRowBytes;
+  constexpr int kSwz = kCpr < 16 ? kCpr : 16;
+  constexpr int SPL = KG / 2;
+  typedef float floatS __attribute__((ext_vector_type(SPL)));
+  const int32_t lstride = sv.lstride;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kMWaves][2][kBufBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t flags[kMWaves][T];
+  const uint32_t slot = xcd_slot(blockIdx.x, gridDim.x);
+  const int32_t split = int32_t(slot % uint32_t(n_split));
+  const uint32_t row = xcd_row(slot / uint32_t(n_split), uint32_t(n_rows));
+  const int32_t g = int32_t(row % uint32_t(Hkv)), b = int32_t(row / uint32_t(Hkv));
+  const int lane = threadIdx.x % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int lg = lane / 16, lc = lane % 16;
+  const int32_t H = Hkv * G;
+  const int64_t bg = int64_t(b) * Hkv + g;
+  const int32_t L_raw = seq_len[b];
+  const ListSeed ls = list_seed(sel_idx, sel_cnt, max_sel, bg, split, ups);
+  const bool hl = lc < G;
+  const int64_t hrow = int64_t(b) * H + g * G + (hl ? lc : 0);
+  const RowTotals rt = row_totals<G>(sv.stat_m, sv.stat_l, sv.stat_n, int64_t(b) * H + g * G,
+                                     bg, n_split, lc);
+  const float theta = sv.eps > 0.0f ? sv.eps / float(max(rt.n, 1)) : sv.tau;
+  const float thr = theta * rt.L;
+  const bool hv = hl && rt.M != -INFINITY;
+  const int32_t L = __builtin_amdgcn_readfirstlane(min(max(L_raw, 0), max_len));
+  TileWalk tw = make_walk<T>(ls, sel_idx, max_sel, bg, L, block, split, ups);
+  tw.init(wave);
+  float4_t O[2 * KG];
+#pragma unroll
+  for (int n = 0; n < 2 * KG; ++n) O[n] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  const uint8_t* vbase = vc + grp_row_off<K, D>(bg, max_seq, 0);
+  const uint8_t* vhbase = vc + grp_hi_off<K, D>(bg, max_seq, 0);
+  const uint8_t* vsb = reinterpret_cast<const uint8_t*>(vsc + bg * int64_t(max_seq) * KG);
+  const float* lrow = sv.logit + hrow * int64_t(lstride);
+  uint32_t* krow = sv.keep != nullptr ? sv.keep + hrow * int64_t(keep_words) : nullptr;
+  uint8_t* fl = flags[wave];
+  auto sw = [](int rw, int chunk) { return rw * D + 16 * (chunk ^ (rw & (kSwz - 1))); };
+  // logits of tokens tok(lg, 0..7): two float4 (tokens 4 lg .. and 16 + 4 lg ..)
+  struct Lgt { float4 s0, s1; int32_t r0, nvalid; };
+  struct Frag {
+    int4_t v[kLoads];
+    uint32_t vh[kLoads];
+    uint2 vs;
+    float p[8];
+    int32_t r0, nvalid;
+  };
+  auto issue_logits = [&](Lgt& lt) {
+    int32_t r0 = 0, nv = 0;
+    if (tw.more()) tw.next<T>(r0, nv);
+    lt.r0 = r0;
+    lt.nvalid = nv;
+    const float* p = lrow + (nv > 0 ? r0 + 4 * lg : 0);
+    lt.s0 = *reinterpret_cast<const float4*>(p);
+    lt.s1 = *reinterpret_cast<const float4*>(p + 16);
+  };
+  auto fill = [&](Frag& f, const Lgt& lt) {
+    const int32_t r0 = lt.r0, nv = lt.nvalid;
+    f.r0 = r0;
+    f.nvalid = nv;
+    const float s[8] = {lt.s0.x, lt.s0.y, lt.s0.z, lt.s0.w, lt.s1.x, lt.s1.y, lt.s1.z, lt.s1.w};
+    bool keep[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int t = 16 * (e / 4) + 4 * lg + e % 4;
+      const float w = __builtin_amdgcn_exp2f(s[e] - rt.M);
+      keep[e] = hv && t < nv && w >= thr;
+      f.p[e] = keep[e] ? w : 0.0f;
+    }
+    clear_flags<T>(fl);
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (f.p[e] > 0.0f) fl[16 * (e / 4) + 4 * lg + e % 4] = 1;
+    if (krow != nullptr && nv > 0) {
+      uint64_t bal[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) bal[e] = __ballot(int(keep[e]));
+      if (lg == 0 && hl) {
+        uint32_t bits = 0u;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            bits |= uint32_t((bal[e] >> (16 * j + lc)) & 1u) << (16 * (e / 4) + 4 * j + e % 4);
+        }
+        // as two 16-bit halves (a tile may start at an odd half of a word)
+        uint16_t* kh = reinterpret_cast<uint16_t*>(krow);
+        kh[r0 / 16] = uint16_t(bits & 0xFFFFu);
+        if (nv > 16) kh[r0 / 16 + 1] = uint16_t(bits >> 16);
+      }
+    }
+    // the kept rows' codes (and fifth bits), and their scales: rows no head
+    // keeps are requested past their resource's records (zeros, no read)
+    const uint32_t lo = 16u * uint32_t(lane);
+    const int bytes = __builtin_amdgcn_readfirstlane(max(nv, 0) * F::kRowBytes);
+    const auto vr = tile_rsrc(vbase + int64_t(r0) * F::kRowBytes, bytes);
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      const bool need = fl[kHrpl * i + lane / kHcpr] != 0;   // row kHrpl i + lane / kHcpr
+      f.v[i] = tile_load(vr, need ? lo + 1024 * i : kSkipOffset);
+    }
+    if constexpr (Q5) {
+      const int hbytes = __builtin_amdgcn_readfirstlane(max(nv, 0) * F::kHiBytes);
+      const auto vhr = tile_rsrc(vhbase + int64_t(r0) * F::kHiBytes, hbytes);
+#pragma unroll
+      for (int i = 0; i < kLoads; ++i) {
+        const bool need = fl[kHrpl * i + lane / kHcpr] != 0;
+        f.vh[i] = __builtin_amdgcn_raw_buffer_load_b32(
+            vhr, need ? 256u * i + 4u * uint32_t(lane) : kSkipOffset, 0, kAuxNontemporal);
+      }
+    }
+    const int sbytes = __builtin_amdgcn_readfirstlane(max(nv, 0) * KG * 2);
+    const auto vsr = tile_rsrc(vsb + int64_t(r0) * KG * 2, sbytes);
+    f.vs = grp_scale_load<KG>(vsr, fl[lane / 2] != 0 ? uint32_t(KG) * uint32_t(lane)
+                                                     : kSkipOffset);
+  };
+  constexpr int kExpUnset = -100000;
+  int e_run = kExpUnset;
+  auto process = [&](auto bufc, Frag& fr, Lgt& lt) {
+    constexpr int kBuf = decltype(bufc)::value;
+    uint8_t* vt = smem[wave][kBuf];
+    float* stv = reinterpret_cast<float*>(vt + kCodeBytes);          // [T][KG]
+    grp_stage<K, D>(vt, fr.v, fr.vh);
+    // V-scale unit 2^e_run >= every kept V scale so far (a power of two: the
+    // change of unit of O is exact)
+    float vv[SPL];
+#pragma unroll
+    for (int j = 0; j < SPL; ++j) {
+      const uint32_t vw = j < 2 ? fr.vs.x : fr.vs.y;
+      vv[j] = (j & 1) ? h2f_hi(vw) : h2f_lo(vw);
+    }
+    float vmx = vv[0];
+#pragma unroll
+    for (int j = 1; j < SPL; ++j) vmx = fmaxf(vmx, vv[j]);
+    const int32_t vbits = __builtin_amdgcn_readfirstlane(__float_as_int(wave_max(vmx)));
+    float unit = 1.0f;
+    if (vbits > 0 && vbits < 0x7F800000) {
+      const int32_t ex =
+          __builtin_amdgcn_readfirstlane(__builtin_amdgcn_frexp_expf(__int_as_float(vbits)));
+      if (e_run == kExpUnset) {
+        e_run = ex;
+      } else if (ex > e_run) {
+        unit = ldexpf(1.0f, e_run - ex);
+        e_run = ex;
+      }
+    }
+    const int e_use = e_run == kExpUnset ? 0 : e_run;
+    {
+      floatS vs4;
+#pragma unroll
+      for (int j = 0; j < SPL; ++j) vs4[j] = ldexpf(vv[j], kPwShiftSvGrp - e_use);
+      reinterpret_cast<floatS*>(stv)[lane] = vs4;
+    }
+    float pc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pc[e] = fr.p[e];
+    fill(fr, lt);
+    issue_logits(lt);
+    if (unit != 1.0f) {
+#pragma unroll
+      for (int n = 0; n < 2 * KG; ++n) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) O[n][r] *= unit;
+      }
+    }
+    const int tr_row = 16 * ((lc / 2) / 4) + 4 * lg + (lc / 2) % 4;
+#pragma unroll
+    for (int grp = 0; grp < KG; ++grp) {
+      half8_t phi, plo;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float pw = pc[e] * stv[(16 * (e / 4) + 4 * lg + e % 4) * KG + grp];
+        const _Float16 h = (_Float16)pw;
+        phi[e] = h;
+        plo[e] = (_Float16)(pw - (float)h);
+      }
+#pragma unroll
+      for (int nn = 0; nn < 2; ++nn) {
+        const int n = 2 * grp + nn;
+        const int off = sw(tr_row, n) + 8 * (lc & 1);
+        const int2_t raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32((SKV_LDS int2_t*)(vt + off));
+        const half8_t bv = widen_grp<K>(raw);
+        O[n] = mfma_f16_32(phi, bv, O[n]);
+        O[n] = mfma_f16_32(plo, bv, O[n]);
+      }
+    }
+  };
+  Lgt la, lb;
+  Frag f0, f1;
+  const int32_t n_mine = tw.count();
+  issue_logits(la);
+  issue_logits(lb);
+  fill(f0, la);
+  issue_logits(la);
+  fill(f1, lb);
+  issue_logits(lb);
+  for (int32_t t = 0; t + 1 < n_mine; t += 2) {
+    process(std::integral_constant<int, 0>{}, f0, la);
+    process(std::integral_constant<int, 1>{}, f1, lb);
+  }
+  if (n_mine & 1) process(std::integral_constant<int, 0>{}, f0, la);
+  if (e_run != kExpUnset) {
+#pragma unroll
+    for (int n = 0; n < 2 * KG; ++n) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) O[n][r] = ldexpf(O[n][r], e_run - kPwShiftSvGrp);
+    }
+  }
+  finish_values<G>(O, rt.M, reinterpret_cast<float*>(&smem[0][0][0]), sv.stat_m, sv.stat_l,
+                   sv.ws_m, sv.ws_l, sv.ws_o, int64_t(b) * H + g * G, n_split, split);
+}
+
 }  // namespace
 
 namespace {
@@ -872,6 +1276,34 @@ hipError_t launch_sparse_v_d(const SparseVParams& p, int G, const dim3 grid, int
       default: SKV_SV_F16(8); break;
     }
 #undef SKV_SV_F16
+    return hipGetLastError();
+  }
+  if (is_grouped(c.kv_dtype)) {
+    const uint8_t* kc = static_cast<const uint8_t*>(c.k);
+    const uint8_t* vc = static_cast<const uint8_t*>(c.v);
+    const uint16_t* ksc = reinterpret_cast<const uint16_t*>(c.k_scale);
+    const uint16_t* vsc = reinterpret_cast<const uint16_t*>(c.v_scale);
+#define SKV_SV_GRP(GG, Q)                                                                       \
+  sv_logits_grp<GG, Q, D><<<grid, kMThreads, 0, stream>>>(kc, ksc, p.q, p.seq_len, p.sel_idx,  \
+                                                           p.sel_cnt, p.max_sel, Hkv,           \
+                                                           c.max_seq, c.block, p.max_len, S,    \
+                                                           n_rows, ups, scale2, sv);            \
+  sv_values_grp<GG, Q, D><<<grid, kMThreads, 0, stream>>>(vc, vsc, p.seq_len, p.sel_idx,       \
+                                                           p.sel_cnt, p.max_sel, Hkv,           \
+                                                           c.max_seq, c.block, p.max_len, S,    \
+                                                           n_rows, ups, keep_words, sv)
+#define SKV_SV_GRP_G(GG)                                          \
+  if (c.kv_dtype == SKV_Q4_0) { SKV_SV_GRP(GG, kQ4); }             \
+  else if (c.kv_dtype == SKV_Q5_0) { SKV_SV_GRP(GG, kQ5); }        \
+  else { SKV_SV_GRP(GG, kQ8); }
+    switch (G) {
+      case 1: SKV_SV_GRP_G(1); break;
+      case 2: SKV_SV_GRP_G(2); break;
+      case 4: SKV_SV_GRP_G(4); break;
+      default: SKV_SV_GRP_G(8); break;
+    }
+#undef SKV_SV_GRP_G
+#undef SKV_SV_GRP
     return hipGetLastError();
   }
   if (c.kv_dtype != SKV_I8) return hipErrorInvalidValue;

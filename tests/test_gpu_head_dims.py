@@ -378,6 +378,9 @@ SPARSE_V = [
     (882, "f16", 16, 8, [4097, 64], 0.0, 0.5),
     (883, "i8", 32, 4, [3000], 0.0, 1.0),
     (884, "i8", 16, 8, [2049, 95, 1], 5e-4, 0.0),
+    (887, "q4_0", 32, 8, [1500, 300], 1e-3, 0.0),
+    (888, "q5_0", 16, 4, [2000], 0.0, 0.5),
+    (889, "q8_0", 8, 8, [1100], 2e-3, 0.0),
 ]
 
 

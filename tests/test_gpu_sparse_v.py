@@ -5,7 +5,8 @@ The keep decisions are compared bit by bit through the kernel's keep mask:
 they must equal the oracle's except for tokens whose weight lies within the
 oracle's near-threshold band (the kernel decides in float32).  The output is
 compared element-wise with the oracle evaluated on the kernel's own
-decisions (f16 cache 1e-3, int8 cache 1e-4 against the int8 method), and with
+decisions (f16 and group-wise caches 1e-3, int8 cache 1e-4 against the int8
+method), and with
 the oracle's own decisions within the same bar plus the mass of the tokens
 decided differently.  Sizes span several tiles, ragged tails, every GQA group
 size, dense walks and given block lists, and both rules (static tau,
@@ -17,7 +18,8 @@ import torch
 import oracle
 import sparse_kv_cache_append_amd as skv
 import workloads
-from gpu_harness import DEV, assert_close, build_cache, quantized_host, sel_tensor_from_lists
+from gpu_harness import (DEV, assert_close, build_cache, grouped_host, quantized_host,
+                         sel_tensor_from_lists)
 
 pytestmark = pytest.mark.gpu
 
@@ -59,24 +61,30 @@ def keep_bits(words, tokens):
 def check_seq(w, b, out, kb, tau, eps, tokens=None, lists=None):
     """Sequence b: decisions and output against the oracle (per KV head when
     lists give each KV head its own blocks)."""
-    tol = 1e-3 if w.kv_dtype == "f16" else 1e-4
+    tol = 1e-4 if w.kv_dtype == "i8" else 1e-3
     if w.kv_dtype == "i8":
         kc, ks, vc, vs = quantized_host(w, b)
+    elif w.kv_dtype != "f16":
+        kc, ks, vc, vs = grouped_host(w, b)
     n_diff = n_near = 0
     for g in range(w.Hkv):
         hs = slice(g * w.G, (g + 1) * w.G)
         toks = np.arange(w.lens[b]) if lists is None else oracle.selected_tokens(
             lists[g], w.lens[b], w.block)
+        sl = slice(g, g + 1)
         if w.kv_dtype == "f16":
             def ref(keep=None):
                 return oracle.attend_f16_sparse_v(w.q[b][hs], w.k[b][g:g + 1], w.v[b][g:g + 1],
                                                   w.softmax_scale, tau, eps, toks, keep)
-        else:
-            sl = slice(g, g + 1)
-
+        elif w.kv_dtype == "i8":
             def ref(keep=None):
                 return oracle.attend_i8_sparse_v(w.q[b][hs], kc[sl], ks[sl], vc[sl], vs[sl],
                                                  w.softmax_scale, tau, eps, toks, keep)
+        else:
+            def ref(keep=None):
+                return oracle.attend_grouped_sparse_v(w.q[b][hs], kc[sl], ks[sl], vc[sl],
+                                                      vs[sl], w.softmax_scale, tau, eps, toks,
+                                                      keep)
         o_ref, k_ref, near = ref()
         k_gpu = np.stack([keep_bits(kb[b, h], toks) for h in range(g * w.G, (g + 1) * w.G)])
         diff = k_gpu != k_ref
@@ -99,6 +107,11 @@ CASES = [
     (706, "i8", 32, 4, [7000], 0.0, 1.0),
     (707, "i8", 16, 16, [333], 1e-2, 0.0),
     (708, "i8", 16, 8, [2049, 95, 1], 5e-4, 0.0),
+    (741, "q8_0", 32, 8, [1000, 2500], 1e-3, 0.0),       # group-wise caches
+    (742, "q4_0", 16, 8, [4097, 64], 0.0, 0.5),
+    (743, "q5_0", 32, 4, [3001], 0.0, 1.0),
+    (744, "q4_0", 16, 16, [333], 1e-2, 0.0),
+    (745, "q5_0", 8, 8, [2049, 95, 1], 5e-4, 0.0),
 ]
 
 
@@ -114,7 +127,7 @@ def test_sparse_v_dense_walk(gpu_lib, seed, kv, H, Hkv, lens, tau, eps):
         _print("seq", b, "decisions differing (all near the threshold):", nd, "near:", nn)
 
 
-@pytest.mark.parametrize("kv", ["f16", "i8"])
+@pytest.mark.parametrize("kv", ["f16", "i8", "q8_0", "q4_0", "q5_0"])
 def test_sparse_v_given_lists(gpu_lib, kv):
     """Quest lists (host-built, differing per KV head, with a clipped last
     block) and sparse-V inside them."""
@@ -134,7 +147,7 @@ def test_sparse_v_given_lists(gpu_lib, kv):
             check_seq(w, b, out, kb, tau, eps, lists=lists[b])
 
 
-@pytest.mark.parametrize("kv", ["f16", "i8"])
+@pytest.mark.parametrize("kv", ["f16", "i8", "q8_0", "q4_0", "q5_0"])
 def test_sparse_v_zero_threshold_is_dense(gpu_lib, kv):
     w = workloads.gaussian(721, 2, 32, 8, 128, [3000, 777], kv)
     cache = build_cache(w)
@@ -143,6 +156,11 @@ def test_sparse_v_zero_threshold_is_dense(gpu_lib, kv):
         if kv == "f16":
             ref = oracle.attend_f16(w.q[b], w.k[b], w.v[b], w.softmax_scale)
             assert_close(out[b], ref, 1e-3, b)
+        elif kv != "i8":
+            kc, ks, vc, vs = grouped_host(w, b)
+            assert_close(out[b], oracle.attend_grouped(q=w.q[b], k_codes=kc, k_scales=ks,
+                                                       v_codes=vc, v_scales=vs,
+                                                       scale=w.softmax_scale), 1e-3, b)
         else:
             kc, ks, vc, vs = quantized_host(w, b)
             assert_close(out[b], oracle.attend_i8(w.q[b], kc, ks, vc, vs, w.softmax_scale),
