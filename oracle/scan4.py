@@ -22,6 +22,11 @@ Readings taken where the page leaves a step open:
   float32 steps are single IEEE operations (no fused multiply-add).
 * For a query q and token t of block b: s~ = sum_d q_d recon_td, r = sum_d
   |q_d| err_bd, LB = s~ - r <= q.k_t <= UB = s~ + r.
+* For an int8 or group-wise (q8_0 / q4_0 / q5_0) cache the index is built
+  from the keys the cache holds, code x scale, each one float32 product
+  (``cache_keys``): exact for the group-wise formats (a code of at most 8
+  bits times an f16 scale fits in float32), correctly rounded for int8 (a
+  float32 scale).
 * Candidates of a query head for a margin delta >= 0 (in q.k units): every
   token whose exact q.k could be within delta of the largest,
   C = {t : UB_t >= max_u LB_u - delta}.  It contains {t : q.k_t >= max_u q.k_u
@@ -35,6 +40,20 @@ import numpy as np
 
 LEVELS = 15
 NEAR_REL = 1e-5
+
+
+def cache_keys(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """The keys a quantized cache holds, as float32: codes int8 [..., L, D];
+    scales float32 [..., L] (int8, one per token) or float16 [..., L, D / 32]
+    (group-wise, one per 32 channels).  Each value is one float32 product
+    code * scale."""
+    c = np.asarray(codes).astype(np.float32)
+    sc = np.asarray(scales)
+    if sc.ndim == c.ndim - 1:
+        s = sc.astype(np.float32)[..., None]
+    else:
+        s = np.repeat(sc.astype(np.float32), 32, axis=-1)
+    return (c * s).astype(np.float32)
 
 
 def build_index(keys: np.ndarray, L: int, block: int):

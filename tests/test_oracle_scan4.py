@@ -5,6 +5,7 @@ import math
 import numpy as np
 import pytest
 
+import oracle
 from oracle import scan4
 
 
@@ -116,3 +117,19 @@ def test_float64_bounds_agree_with_the_exact_sums():
     lb2, ub2 = scan4.scan_bounds_f64(q, *idx, 64)
     np.testing.assert_allclose(lb2, lb, rtol=1e-12, atol=1e-12)
     np.testing.assert_allclose(ub2, ub, rtol=1e-12, atol=1e-12)
+
+
+def test_cache_keys_are_the_dequantized_values():
+    """int8: the float32 product of code and scale (correctly rounded);
+    group-wise: scale * code exactly (the float64 dequantization)."""
+    rng = np.random.default_rng(44)
+    x = rng.standard_normal((2, 50, 64)).astype(np.float32)
+    kc, ks = oracle.quantize_rows(x)
+    got = scan4.cache_keys(kc, ks)
+    assert got.dtype == np.float32
+    ref = (kc.astype(np.float64) * ks.astype(np.float64)[..., None]).astype(np.float32)
+    assert np.array_equal(got, ref)                 # one rounding of the exact product
+    for qmax in (oracle.QMAX_Q8, oracle.QMAX_Q4, oracle.QMAX_Q5):
+        gc, gs = oracle.quantize_groups(x, qmax)
+        got = scan4.cache_keys(gc, gs)
+        assert np.array_equal(got.astype(np.float64), oracle.dequantize_groups(gc, gs))
