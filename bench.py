@@ -555,7 +555,7 @@ def measure(w, args, quest: bool, dense: bool, detail: bool = False):
         if not args.no_per_head:
             res["quest_per_head"] = measure_per_head(T, skv, torch, w, caches, R, q, seq_len, Lmax,
                                                      new_k, new_v, pos_last, ks, res["quest"])
-        if not args.no_scan4 and w.kv_dtype == "f16":
+        if not args.no_scan4:
             res["scan4"] = measure_scan4(T, skv, torch, w, caches, R, q, seq_len, Lmax,
                                          args.scan4_delta)
         n_chunk = min(args.chunk_tokens, 16 // w.G)

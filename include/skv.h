@@ -34,11 +34,8 @@
  *   - The cache's k, v, kmin, kmax, the queries q and the new rows k_new,
  *     v_new are 16-byte aligned, the int8 scales 4-byte aligned (SKV_EINVAL
  *     otherwise); other buffers need their element's natural alignment.
- *   - Supported in this version: head_dim D = 64, 128 or 256 for every call
- *     (each over the cache types it takes: append, bounds, selection,
- *     attention, combine and the step over f16, int8, q8_0, q4_0 and q5_0
- *     caches, per-query-head selection, query-token chunks and sparse-V
- *     too; the 4-bit scan over f16 caches; the cpu-attn
+ *   - Supported in this version: head_dim D = 64, 128 or 256 for every call,
+ *     over every cache type (f16, int8, q8_0, q4_0, q5_0) (the cpu-attn
  *     kernel card, "Requirements and limits", admits any multiple of 16 up to
  *     1024);
  *     GQA group size
@@ -448,7 +445,9 @@ skv_status skv_decode_attn_multi(const skv_cache* c, const float* q, int32_t n_t
  * reads every key; the appendix layout table -- 4-bit codes of 64 B per token
  * at D = 128, per-block per-channel float32 lo and step).  A token-level
  * candidate generator; the certificate, perturbation and sampling layers of
- * that method are not part of this library.  f16 caches, block <= 256.
+ * that method are not part of this library.  Every cache type, block <= 256:
+ * the keys k are the cache's (f16 values; for an int8 or group-wise cache
+ * code x scale, one float32 product).
  *
  * Index, per block of `block` tokens and channel d: lo = min k, step =
  * fl32(fl32(max k - lo) / 15), code = clamp(rint(fl32(fl32(k - lo) / step)),
@@ -466,8 +465,8 @@ skv_status skv_decode_attn_multi(const skv_cache* c, const float* q, int32_t n_t
  *   codes4 : device uint8 [batch][n_kv_heads][max_seq][head_dim / 2]: channel
  *            2i in the low nibble of byte i, 2i + 1 in the high nibble.
  *   lo, step, err : device float32 [batch][n_kv_heads][max_blocks][head_dim].
- * Errors: SKV_EINVAL, SKV_ERANGE (max_len), SKV_EUNSUPPORTED (not f16, block
- * > 256), SKV_EDEVICE.
+ * Errors: SKV_EINVAL, SKV_ERANGE (max_len), SKV_EUNSUPPORTED (block > 256),
+ * SKV_EDEVICE.
  */
 skv_status skv_scan4_build(const skv_cache* c, const int32_t* pos0, const int32_t* seq_len,
                            int32_t max_len, uint8_t* codes4, float* lo, float* step, float* err,

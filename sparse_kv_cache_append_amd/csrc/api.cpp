@@ -489,7 +489,7 @@ skv_status skv_scan4_build(const skv_cache* c, const int32_t* pos0, const int32_
   if (pos0 == nullptr || seq_len == nullptr || codes4 == nullptr || lo == nullptr ||
       step == nullptr || err == nullptr)
     return SKV_EINVAL;
-  if (c->kv_dtype != SKV_F16 || c->block > 256) return SKV_EUNSUPPORTED;
+  if (c->block > 256) return SKV_EUNSUPPORTED;
   if (!aligned(lo) || !aligned(step) || !aligned(err)) return SKV_EINVAL;
   if (max_len < 0 || max_len > c->max_seq) return SKV_ERANGE;
   return device_status(skv::launch_scan4_build(*c, pos0, seq_len, max_len, codes4, lo, step, err,
@@ -516,7 +516,7 @@ skv_status skv_scan4_candidates(const skv_cache* c, const uint8_t* codes4, const
   if (!aligned(codes4) || !aligned(lo) || !aligned(step) || !aligned(err)) return SKV_EINVAL;
   st = check_heads(c, n_heads);
   if (st != SKV_OK) return st;
-  if (c->kv_dtype != SKV_F16 || c->block > 256) return SKV_EUNSUPPORTED;
+  if (c->block > 256) return SKV_EUNSUPPORTED;
   if (!(delta >= 0.0f && delta <= 3.4e38f)) return SKV_EINVAL;
   if (n_split < 1 || n_split > kMaxSplit) return SKV_EINVAL;
   if (!grid_fits(n_split, c->n_kv_heads, c->batch)) return SKV_ERANGE;

@@ -31,6 +31,7 @@
 
 #include "decode_core.h"
 #include "device_common.h"
+#include "grouped_core.h"
 #include "launch.h"
 
 namespace skv {
@@ -110,6 +111,93 @@ scan4_build(const uint16_t* __restrict__ kc, const int32_t* __restrict__ pos0,
   }
   __syncthreads();
   // pack: byte i of a token's row = channel 2i (low nibble), 2i + 1 (high)
+  const int32_t n = (t1 - t0) * kRow4;
+  uint8_t* dst = codes4 + (bg * max_seq + t0) * kRow4;
+  for (int32_t e = threadIdx.x; e < n; e += 256) {
+    const int32_t t = e / kRow4, i = e % kRow4;
+    dst[e] = uint8_t(cs[t][2 * i] | (cs[t][2 * i + 1] << 4));
+  }
+}
+
+// The key an int8 or group-wise cache holds at token t, channel d of row bg
+// (sequence x KV head): code x scale as one float32 product (no fused
+// multiply-add with what follows).
+template <int D, int KV>
+__device__ __forceinline__ float cache_key(const uint8_t* __restrict__ kc,
+                                           const void* __restrict__ ks, int64_t bg,
+                                           int32_t max_seq, int32_t t, int d) {
+  if constexpr (KV == SKV_I8) {
+    const int code = int(reinterpret_cast<const int8_t*>(kc)[(bg * max_seq + t) * D + d]);
+    const float s = static_cast<const float*>(ks)[bg * max_seq + t];
+    return __fmul_rn(float(code), s);
+  } else {
+    constexpr int K = KV == SKV_Q8_0 ? kQ8 : KV == SKV_Q4_0 ? kQ4 : kQ5;
+    using F = GrpFmt<K, D>;
+    const uint8_t* row = kc + grp_row_off<K, D>(bg, max_seq, t);
+    int code;
+    if constexpr (K == kQ8) {
+      code = int(int8_t(row[d]));
+    } else {
+      const uint32_t by = row[d / 2];
+      uint32_t n = (d & 1) ? (by >> 4) : (by & 15u);
+      if constexpr (K == kQ5) {
+        const uint8_t* hi = kc + grp_hi_off<K, D>(bg, max_seq, t);
+        n |= ((uint32_t(hi[d / 8]) >> (d % 8)) & 1u) << 4;
+      }
+      code = int(n) - F::kBias;
+    }
+    const float s =
+        h2f(static_cast<const uint16_t*>(ks)[(bg * max_seq + t) * F::kGroups + d / kGroup]);
+    return __fmul_rn(float(code), s);
+  }
+}
+
+// The index of an int8 or group-wise cache: as scan4_build, each key read
+// as the cache holds it (cache_key), channel d by thread d < D.
+template <int D, int KV>
+__global__ void __launch_bounds__(256)
+scan4_build_q(const uint8_t* __restrict__ kc, const void* __restrict__ ks,
+              const int32_t* __restrict__ pos0, const int32_t* __restrict__ seq_len, int32_t Hkv,
+              int32_t max_seq, int32_t max_len, int32_t block, int32_t max_blocks,
+              uint8_t* __restrict__ codes4, float* __restrict__ lo_out,
+              float* __restrict__ step_out, float* __restrict__ err_out) {
+  constexpr int kRow4 = D / 2;
+  __shared__ uint8_t cs[kScanBlockMax][D];
+  const int32_t g = blockIdx.y, b = blockIdx.z;
+  const int32_t L = min(max(seq_len[b], 0), max_len);
+  const int32_t p0 = pos0[b];
+  const int32_t j = int32_t(blockIdx.x);
+  const int32_t nb = (L + block - 1) / block;
+  if (p0 < 0 || j < p0 / block || j >= nb) return;
+  const int32_t t0 = j * block, t1 = min(t0 + block, L);
+  const int64_t bg = int64_t(b) * Hkv + g;
+  const int d = threadIdx.x;
+  float lo = 0.0f, st = 0.0f, err = 0.0f;
+  if (d < D) {
+    float mn = INFINITY, mx = -INFINITY;
+    for (int32_t t = t0; t < t1; ++t) {
+      const float x = cache_key<D, KV>(kc, ks, bg, max_seq, t, d);
+      mn = fminf(mn, x);
+      mx = fmaxf(mx, x);
+    }
+    lo = mn;
+    st = __fdiv_rn(__fsub_rn(mx, mn), float(kLevels));
+    for (int32_t t = t0; t < t1; ++t) {
+      const float x = cache_key<D, KV>(kc, ks, bg, max_seq, t, d);
+      float c = 0.0f;
+      if (st > 0.0f) c = fminf(fmaxf(rintf(__fdiv_rn(__fsub_rn(x, lo), st)), 0.0f), float(kLevels));
+      float prod = st * c;
+      asm volatile("" : "+v"(prod));
+      const float rec = lo + prod;
+      err = fmaxf(err, fabsf(__fsub_rn(x, rec)));
+      cs[t - t0][d] = uint8_t(c);
+    }
+    const int64_t o = (bg * max_blocks + j) * D + d;
+    lo_out[o] = lo;
+    step_out[o] = st;
+    err_out[o] = err;
+  }
+  __syncthreads();
   const int32_t n = (t1 - t0) * kRow4;
   uint8_t* dst = codes4 + (bg * max_seq + t0) * kRow4;
   for (int32_t e = threadIdx.x; e < n; e += 256) {
@@ -493,21 +581,46 @@ scan4_select(const float* __restrict__ ub, const float* __restrict__ lbmax,
 hipError_t launch_scan4_build(const skv_cache& c, const int32_t* pos0, const int32_t* seq_len,
                               int32_t max_len, uint8_t* codes4, float* lo, float* step,
                               float* err, hipStream_t stream) {
-  if (c.kv_dtype != SKV_F16 || c.block > kScanBlockMax) return hipErrorInvalidValue;
+  if (c.block > kScanBlockMax) return hipErrorInvalidValue;
   const int32_t max_blocks = (c.max_seq + c.block - 1) / c.block;
   const int32_t nb = (max_len + c.block - 1) / c.block;
   if (nb == 0) return hipSuccess;
+  const dim3 grid(nb, c.n_kv_heads, c.batch);
+  if (c.kv_dtype == SKV_F16) {
 #define SKV_BUILD(DD)                                                                           \
-  scan4_build<DD><<<dim3(nb, c.n_kv_heads, c.batch), 256, 0, stream>>>(                        \
-      static_cast<const uint16_t*>(c.k), pos0, seq_len, c.n_kv_heads, c.max_seq, max_len,      \
-      c.block, max_blocks, codes4, lo, step, err)
-  switch (c.head_dim) {
-    case 64: SKV_BUILD(64); break;
-    case 128: SKV_BUILD(128); break;
-    case 256: SKV_BUILD(256); break;
+  scan4_build<DD><<<grid, 256, 0, stream>>>(static_cast<const uint16_t*>(c.k), pos0, seq_len,   \
+                                           c.n_kv_heads, c.max_seq, max_len, c.block,           \
+                                           max_blocks, codes4, lo, step, err)
+    switch (c.head_dim) {
+      case 64: SKV_BUILD(64); break;
+      case 128: SKV_BUILD(128); break;
+      case 256: SKV_BUILD(256); break;
+      default: return hipErrorInvalidValue;
+    }
+#undef SKV_BUILD
+    return hipGetLastError();
+  }
+#define SKV_BUILD_Q(DD, KV)                                                                     \
+  scan4_build_q<DD, KV><<<grid, 256, 0, stream>>>(static_cast<const uint8_t*>(c.k), c.k_scale,  \
+                                                 pos0, seq_len, c.n_kv_heads, c.max_seq,        \
+                                                 max_len, c.block, max_blocks, codes4, lo,      \
+                                                 step, err)
+#define SKV_BUILD_QD(KV)                       \
+  switch (c.head_dim) {                        \
+    case 64: SKV_BUILD_Q(64, KV); break;       \
+    case 128: SKV_BUILD_Q(128, KV); break;     \
+    case 256: SKV_BUILD_Q(256, KV); break;     \
+    default: return hipErrorInvalidValue;      \
+  }
+  switch (c.kv_dtype) {
+    case SKV_I8: SKV_BUILD_QD(SKV_I8); break;
+    case SKV_Q8_0: SKV_BUILD_QD(SKV_Q8_0); break;
+    case SKV_Q4_0: SKV_BUILD_QD(SKV_Q4_0); break;
+    case SKV_Q5_0: SKV_BUILD_QD(SKV_Q5_0); break;
     default: return hipErrorInvalidValue;
   }
-#undef SKV_BUILD
+#undef SKV_BUILD_QD
+#undef SKV_BUILD_Q
   return hipGetLastError();
 }
 

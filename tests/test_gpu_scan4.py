@@ -4,7 +4,9 @@ lo, step, err) bit-exact, rebuilding from an append position equal to a full
 build, the upper bounds within float32 rounding of the exact ones, the
 candidate sets equal up to tokens within rounding of the threshold, and
 every token within delta of the best exact score among the GPU's candidates
-(up to the same band)."""
+(up to the same band).  Over int8 and group-wise caches the keys are the
+cache's (code x scale, one float32 product: oracle scan4.cache_keys)."""
+import copy
 import math
 
 import numpy as np
@@ -13,7 +15,7 @@ import torch
 
 import sparse_kv_cache_append_amd as skv
 import workloads
-from gpu_harness import DEV, build_cache, device_inputs
+from gpu_harness import DEV, build_cache, device_inputs, grouped_host, quantized_host
 from oracle import scan4
 
 pytestmark = pytest.mark.gpu
@@ -132,3 +134,23 @@ def test_32k_workload_scan(gpu_lib):
     index = check_index(idx, w, 0)
     nb = check_scan(w, 0, index, ub, cand, cnt, 8.0)
     _print("32K delta 8: candidates per head", cnt[0].tolist(), "band differences", nb)
+
+
+@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("kv", ["i8", "q8_0", "q4_0", "q5_0"])
+def test_quantized_caches(gpu_lib, kv, D):
+    """The index built from the keys the cache holds, bit-exact; bounds and
+    candidates against those keys."""
+    w = workloads.clustered([990 + D, 991 + D], 32, 8, D, [3000, 777], kv, n_dirs=8, amp=4.0,
+                            block=64)
+    cache = build_cache(w)
+    idx = build(cache, w)
+    wk = copy.copy(w)
+    host = quantized_host if kv == "i8" else grouped_host
+    wk.k = [scan4.cache_keys(*host(w, b)[:2]) for b in range(w.B)]
+    for delta in (0.0, 8.0):
+        ub, cand, cnt = run_scan(cache, idx, w, delta)
+        for b in range(w.B):
+            index = check_index(idx, wk, b)
+            nb = check_scan(wk, b, index, ub, cand, cnt, delta)
+            _print(kv, D, "delta", delta, "seq", b, "band differences", nb)
