@@ -188,6 +188,8 @@ decode_grp_mfma(const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
   constexpr int kSb = KG;                                   // scale bytes per lane and tile
   static_assert(kLoads >= 1, "a tile is at least one load per lane");
   __shared__ __attribute__((aligned(16))) uint8_t smem[kMWaves][2][kBufBytes];
+  static_assert(SELR == 0 || sizeof(smem) >= sizeof(SelectShared),
+                "the prologue's selection runs in the tile buffers");
   const uint32_t slot = xcd_slot(blockIdx.x, gridDim.x);
   const int32_t split = int32_t(slot % uint32_t(n_split));
   const uint32_t row = xcd_row(slot / uint32_t(n_split), uint32_t(n_rows));
@@ -225,7 +227,8 @@ decode_grp_mfma(const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
   const int32_t L = __builtin_amdgcn_readfirstlane(min(max(L_raw, 0), max_len));
   TileWalk tw;
   if constexpr (SELR > 0)
-    tw = fused_walk<T, SELR>(fs, max_sel, bg, b, L, L_raw, block, split, units_per_split);
+    tw = fused_walk<T, SELR>(fs, max_sel, bg, b, L, L_raw, block, split, units_per_split,
+                            smem);
   else
     tw = make_walk<T>(ls, sel_idx, max_sel, bg, L, block, split, units_per_split);
   if constexpr (HM) tw.hsel = sel_hmask + bg * max_sel;

@@ -179,6 +179,8 @@ decode_f16_mfma(const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc
   constexpr int KQ = D / 32;                                // q.K steps
   constexpr int NB = HeadDim<D>::kNB;
   __shared__ __attribute__((aligned(16))) uint8_t smem[kMWaves][2][2 * kTileBytes];
+  static_assert(SELR == 0 || sizeof(smem) >= sizeof(SelectShared),
+                "the prologue's selection runs in the tile buffers");
   // 1-D grid of n_split x Hkv x batch parts, row by row (XCD-aware slots)
   const uint32_t slot = xcd_slot(blockIdx.x, gridDim.x);
   const int32_t split = int32_t(slot % uint32_t(n_split));
@@ -226,7 +228,8 @@ decode_f16_mfma(const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc
   const int32_t L = __builtin_amdgcn_readfirstlane(min(max(L_raw, 0), max_len));
   TileWalk tw;
   if constexpr (SELR > 0)
-    tw = fused_walk<T, SELR>(fs, max_sel, bg, b, L, L_raw, block, split, units_per_split);
+    tw = fused_walk<T, SELR>(fs, max_sel, bg, b, L, L_raw, block, split, units_per_split,
+                            smem);
   else
     tw = make_walk<T>(ls, sel_idx, max_sel, bg, L, block, split, units_per_split);
   if constexpr (HM) tw.hsel = sel_hmask + bg * max_sel;
@@ -430,6 +433,8 @@ decode_i8_mfma(const int8_t* __restrict__ kc, const int8_t* __restrict__ vc,
   constexpr int kScaleOff = 2 * kTileBytes;                 // 32 K scales, 32 V scales
   constexpr int kBufBytes = 2 * kTileBytes + 2 * T * 4;
   __shared__ __attribute__((aligned(16))) uint8_t smem[kMWaves][2][kBufBytes];
+  static_assert(SELR == 0 || sizeof(smem) >= sizeof(SelectShared),
+                "the prologue's selection runs in the tile buffers");
   // 1-D grid of n_split x Hkv x batch parts, row by row (XCD-aware slots)
   const uint32_t slot = xcd_slot(blockIdx.x, gridDim.x);
   const int32_t split = int32_t(slot % uint32_t(n_split));
@@ -476,7 +481,8 @@ decode_i8_mfma(const int8_t* __restrict__ kc, const int8_t* __restrict__ vc,
   const int32_t L = __builtin_amdgcn_readfirstlane(min(max(L_raw, 0), max_len));
   TileWalk tw;
   if constexpr (SELR > 0)
-    tw = fused_walk<T, SELR>(fs, max_sel, bg, b, L, L_raw, block, split, units_per_split);
+    tw = fused_walk<T, SELR>(fs, max_sel, bg, b, L, L_raw, block, split, units_per_split,
+                            smem);
   else
     tw = make_walk<T>(ls, sel_idx, max_sel, bg, L, block, split, units_per_split);
   if constexpr (HM) tw.hsel = sel_hmask + bg * max_sel;

@@ -24,11 +24,16 @@ static_assert(kMThreads == kSelThreads, "the selection prologue runs on the whol
 // ceil(max_sel / n_split)); split 0 also publishes the count.
 // (The scores are requested here, after the query has arrived; requesting
 // them at kernel entry instead measured no faster.)
+// sel_lds: workgroup memory of at least sizeof(SelectShared) bytes, 16-byte
+// aligned, that nothing else uses until this returns (the kernel's tile
+// buffers: no tile is staged before the walk starts, and after the final
+// barrier here only plist, a buffer of its own, is read).
 template <int T, int SELR>
 __device__ __forceinline__ TileWalk fused_walk(const FusedSelect& fs, int32_t max_sel, int64_t bg,
                                                int32_t b, int32_t L, int32_t L_raw, int32_t block,
-                                               int32_t split, int32_t units_per_split) {
-  __shared__ SelectShared ssh;
+                                               int32_t split, int32_t units_per_split,
+                                               void* sel_lds) {
+  SelectShared& ssh = *reinterpret_cast<SelectShared*>(sel_lds);
   __shared__ int32_t plist[kWave + kSelThreads];   // the slice, then one spare entry per thread
   const int tid = threadIdx.x;
   // The candidates start at n_sink whenever there are any, so their scores
@@ -75,19 +80,34 @@ __device__ __forceinline__ TileWalk fused_walk(const FusedSelect& fs, int32_t ma
     kk.set_count(n_cand);
     const uint64_t cut = sel_cut(kk, K, ssh);
     const uint64_t taken = sel_taken_mask(kk, cut);
-    const int R = (n_cand + kSelThreads - 1) / kSelThreads;
-    const SelOrder o = sel_order_prepare<SELR>(taken, R, ssh);
-    // the taken candidates whose positions fall in this part's slice go to
-    // plist; every thread writes once per chunk, the others to a spare entry
-    // of their own, so the chunks carry no branch and overlap (chunks past R
-    // have no taken bit)
+    if constexpr (SELR >= 16) {
+      // this thread's taken candidates SELR tid + j, ascending from position
+      // cs + base: the ones in this part's slice go to plist
+      const SelRank rk = sel_rank_prepare<SELR>(taken, ssh);
+      int32_t pos = cs + rk.base;
+      if (pos < u0 + ups && pos + __popcll(rk.bits) > u0) {
+        uint64_t bits = rk.bits;
+        while (bits != 0u) {
+          if (pos >= u0 && pos < u0 + ups) plist[pos - u0] = cs + SELR * tid + __builtin_ctzll(bits);
+          ++pos;
+          bits &= bits - 1u;
+        }
+      }
+    } else {
+      const int R = (n_cand + kSelThreads - 1) / kSelThreads;
+      const SelOrder o = sel_order_prepare<SELR>(taken, R, ssh);
+      // the taken candidates whose positions fall in this part's slice go to
+      // plist; every thread writes once per chunk, the others to a spare
+      // entry of their own, so the chunks carry no branch and overlap (chunks
+      // past R have no taken bit)
 #pragma unroll
-    for (int r = 0; r < SELR; ++r) {
-      const bool t = (taken >> r) & 1u;
-      const uint64_t bal = __ballot(int(t));
-      const int32_t pos = cs + __builtin_amdgcn_readlane(o.pre, r) + lanes_below(bal);
-      const bool hit = t && pos >= u0 && pos < u0 + ups;
-      plist[hit ? pos - u0 : kWave + tid] = cs + kk.index(r);
+      for (int r = 0; r < SELR; ++r) {
+        const bool t = (taken >> r) & 1u;
+        const uint64_t bal = __ballot(int(t));
+        const int32_t pos = cs + __builtin_amdgcn_readlane(o.pre, r) + lanes_below(bal);
+        const bool hit = t && pos >= u0 && pos < u0 + ups;
+        plist[hit ? pos - u0 : kWave + tid] = cs + kk.index(r);
+      }
     }
   }
   __syncthreads();

@@ -71,13 +71,24 @@ select_kernel(const float* __restrict__ score, const int32_t* __restrict__ seq_l
     kk.set_count(n_cand);
     const uint64_t cut = sel_cut(kk, K, sh);
     const uint64_t taken = sel_taken_mask(kk, cut);
-    const int R = (n_cand + kSelThreads - 1) / kSelThreads;
-    const SelOrder o = sel_order_prepare<RMAX>(taken, R, sh);
+    if constexpr (RMAX >= 16) {
+      // this thread's taken candidates RMAX tid + j, in ascending order
+      const SelRank rk = sel_rank_prepare<RMAX>(taken, sh);
+      uint64_t bits = rk.bits;
+      int32_t pos = cs + rk.base;
+      while (bits != 0u) {
+        emit(pos++, cs + RMAX * tid + __builtin_ctzll(bits));
+        bits &= bits - 1u;
+      }
+    } else {
+      const int R = (n_cand + kSelThreads - 1) / kSelThreads;
+      const SelOrder o = sel_order_prepare<RMAX>(taken, R, sh);
 #pragma unroll
-    for (int r = 0; r < RMAX; ++r) {
-      if (r < R) {
-        const int pos = sel_order_pos(o, taken, r);
-        if ((taken >> r) & 1u) emit(cs + pos, cs + kk.index(r));
+      for (int r = 0; r < RMAX; ++r) {
+        if (r < R) {
+          const int pos = sel_order_pos(o, taken, r);
+          if ((taken >> r) & 1u) emit(cs + pos, cs + kk.index(r));
+        }
       }
     }
   }
