@@ -425,6 +425,9 @@ SELECT_CASES = [
     ("distinct", 16384, [4096, 16000], 1, 4),
     ("few-values", 300, [150, 1], 1, 1),
     ("distinct", 5, [1, 2], 1, 1),
+    ("all-equal", 4000, [1200, 3], 1, 2),          # 16 keys per thread, cut among equal keys
+    ("few-values", 4096, [640, 5], 1, 4),
+    ("shared-exponent", 1024, [300, 30], 1, 2),    # 4 keys per thread, first pass narrower
 ]
 
 
@@ -446,6 +449,54 @@ def test_select_topk_on_given_scores(gpu_lib, kind, nb, k_sel, ns, nr):
     sel = torch.empty((B, Hkv, max_sel), dtype=torch.int32, device=DEV)
     cnt = torch.empty((B, Hkv), dtype=torch.int32, device=DEV)
     skv.select_topk(st, seq_len, blk, ks, ns, nr, sel, cnt)
+    torch.cuda.synchronize()
+    sel, cnt = sel.cpu().numpy(), cnt.cpu().numpy()
+    for b in range(B):
+        n_blocks = -(-lens[b] // blk)
+        for g in range(Hkv):
+            ref = oracle.select_blocks(score[b, g], n_blocks, k_sel[b], ns, nr)["sel"]
+            assert cnt[b, g] == len(ref), (b, g)
+            assert np.array_equal(sel[b, g, :cnt[b, g]], ref), (b, g)
+            assert np.all(sel[b, g, cnt[b, g]:] == -1)
+
+
+FUSED_SELECT_CASES = [
+    # (pattern, n_blocks, k_sel per sequence, n_sink, n_recent, n_split): rows of
+    # 2, 4 and 16 keys per thread in the attention kernel's prologue
+    ("distinct", 500, [120, 37], 1, 2, 8),
+    ("few-values", 1000, [250, 3], 1, 2, 8),
+    ("shared-exponent", 4000, [512, 100], 1, 4, 16),
+    ("few-values", 4000, [900, 17], 1, 4, 32),
+    ("all-equal", 4096, [511, 1000], 1, 4, 32),
+    ("near-ties", 3500, [600, 64], 2, 3, 16),
+    ("signed-zeros", 4096, [700, 1], 1, 2, 16),
+]
+
+
+@pytest.mark.parametrize("kind,nb,k_sel,ns,nr,S", FUSED_SELECT_CASES)
+def test_fused_select_on_given_scores(gpu_lib, kind, nb, k_sel, ns, nr, S):
+    """The selection in the attention kernel's prologue (decode_attn_select:
+    every part recomputes the row's top-K and publishes its slice of the list)
+    on host-made tie patterns equals the oracle's rule bit for bit, at 2, 4 and
+    16 candidate keys per thread."""
+    _print("fused select on given scores", kind, nb, k_sel, S)
+    rng = np.random.default_rng(nb * 17 + len(kind))
+    B, H, Hkv, D, blk = 2, 4, 2, 128, 16
+    score = np.stack([np.stack([_score_pattern(kind, nb, rng) for _ in range(Hkv)])
+                      for _ in range(B)])
+    lens = [nb * blk, nb * blk - blk // 2]
+    cache = skv.Cache(B, Hkv, nb * blk, D, "f16", blk, device=DEV)
+    max_sel = max(k_sel) + ns + nr
+    assert -(-max_sel // S) <= 64, "each part's slice fits the prologue's list"
+    q = torch.zeros((B, H, D), dtype=torch.float32, device=DEV)
+    st = torch.from_numpy(score).to(DEV)
+    seq_len = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    ks = torch.tensor(k_sel, dtype=torch.int32, device=DEV)
+    sel = torch.full((B, Hkv, max_sel), -7, dtype=torch.int32, device=DEV)
+    cnt = torch.full((B, Hkv), -7, dtype=torch.int32, device=DEV)
+    ws = torch.empty(skv.workspace_bytes(B, H, D, S), dtype=torch.uint8, device=DEV)
+    skv.decode_attn_select(cache, q, seq_len, max(lens), 1.0 / math.sqrt(D), S, ws, st, ks, ns,
+                           nr, sel, cnt)
     torch.cuda.synchronize()
     sel, cnt = sel.cpu().numpy(), cnt.cpu().numpy()
     for b in range(B):
