@@ -404,6 +404,9 @@ def _score_pattern(kind, nb, rng):
         x[rng.random(nb) < 0.05] = np.inf
         x[rng.random(nb) < 0.05] = -np.inf
         return x
+    if kind == "ulp-band":                 # keys differ in their last 9 bits only
+        base = np.float32(3.0).view(np.uint32)
+        return (base + rng.integers(0, 400, nb).astype(np.uint32)).view(np.float32)
     if kind == "near-ties":                # neighbours one ulp apart
         base = np.float32(7.25)
         steps = rng.integers(-300, 300, nb)
@@ -428,6 +431,8 @@ SELECT_CASES = [
     ("all-equal", 4000, [1200, 3], 1, 2),          # 16 keys per thread, cut among equal keys
     ("few-values", 4096, [640, 5], 1, 4),
     ("shared-exponent", 1024, [300, 30], 1, 2),    # 4 keys per thread, first pass narrower
+    ("ulp-band", 4096, [512, 4000], 1, 4),         # fewer than 10 free bits for the first pass
+    ("ulp-band", 700, [90, 600], 1, 2),
 ]
 
 
@@ -470,6 +475,8 @@ FUSED_SELECT_CASES = [
     ("all-equal", 4096, [511, 1000], 1, 4, 32),
     ("near-ties", 3500, [600, 64], 2, 3, 16),
     ("signed-zeros", 4096, [700, 1], 1, 2, 16),
+    ("ulp-band", 4096, [512, 40], 1, 4, 16),
+    ("ulp-band", 509, [128, 2], 1, 2, 8),
 ]
 
 
